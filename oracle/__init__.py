@@ -1,0 +1,172 @@
+"""CPU oracle for GGUF block-quantized matmul with q8_1 activations -- TEST INFRASTRUCTURE.
+
+Only tests/, the smoke check and bench.py's cpu_baseline leg may import this package.  The
+product library (block_quantized_matmul_quantize_amd) never imports, links or falls back to it.
+
+Thin ctypes marshalling over qmm_oracle.c; every step of the arithmetic lives in that C file,
+which states the readings of the pages it follows.  numpy arrays in, numpy arrays out.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+Q8_0 = 8
+Q4_K = 12
+Q6_K = 14
+
+BLOCK_VALUES = {Q8_0: 32, Q4_K: 256, Q6_K: 256}
+BLOCK_BYTES = {Q8_0: 34, Q4_K: 144, Q6_K: 210}
+Q8_1_BYTES = 36
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        path = _build.LIB
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_build.SRC):
+            _build.build()
+        L = ctypes.CDLL(path)
+        i64, i32, u16 = ctypes.c_int64, ctypes.c_int, ctypes.c_uint16
+        vp = ctypes.c_void_p
+        L.oracle_half_to_double.argtypes = [u16]
+        L.oracle_half_to_double.restype = ctypes.c_double
+        L.oracle_float_to_half.argtypes = [ctypes.c_float]
+        L.oracle_float_to_half.restype = u16
+        L.oracle_quantize_q8_1.argtypes = [vp, i64, i64, vp]
+        L.oracle_quantize_q8_1.restype = None
+        L.oracle_row_bytes.argtypes = [i32, i64]
+        L.oracle_row_bytes.restype = i64
+        L.oracle_subdots_per_row.argtypes = [i32, i64]
+        L.oracle_subdots_per_row.restype = i64
+        L.oracle_dequantize.argtypes = [i32, vp, i64, i64, vp]
+        L.oracle_dequantize.restype = i32
+        L.oracle_dequantize_q8_1.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.oracle_dequantize_q8_1.restype = None
+        L.oracle_matmul_q8_1.argtypes = [i32, vp, i64, i64, vp, i64, vp]
+        L.oracle_matmul_q8_1.restype = i32
+        L.oracle_matmul_q8_1_at.argtypes = [i32, vp, i64, i64, vp, i64, vp, vp, i64, vp]
+        L.oracle_matmul_q8_1_at.restype = i32
+        L.oracle_subdots.argtypes = [i32, vp, i64, i64, vp, i64, vp]
+        L.oracle_subdots.restype = i32
+        L.oracle_matmul.argtypes = [i32, vp, i64, i64, vp, i64, vp]
+        L.oracle_matmul.restype = i32
+        L.oracle_matmul_id.argtypes = [i32, vp, i64, i64, i64, vp, i64, vp, i64, i64, vp, vp]
+        L.oracle_matmul_id.restype = i32
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def row_bytes(qtype, k):
+    return int(lib().oracle_row_bytes(qtype, k))
+
+
+def half_to_double(bits):
+    return float(lib().oracle_half_to_double(int(bits) & 0xFFFF))
+
+
+def float_to_half(x):
+    return int(lib().oracle_float_to_half(float(np.float32(x))))
+
+
+def quantize_q8_1(x):
+    """fp32 [n, k] -> uint8 [n, k/32*36] canonical q8_1 blocks."""
+    x = _c(x, np.float32)
+    n, k = x.shape
+    assert k % 32 == 0
+    y = np.zeros((n, k // 32 * Q8_1_BYTES), dtype=np.uint8)
+    lib().oracle_quantize_q8_1(_ptr(x), n, k, _ptr(y))
+    return y
+
+
+def dequantize(qtype, w, rows, k):
+    w = _c(w, np.uint8)
+    out = np.zeros((rows, k), dtype=np.float64)
+    rc = lib().oracle_dequantize(qtype, _ptr(w), rows, k, _ptr(out))
+    if rc:
+        raise ValueError("oracle_dequantize: bad arguments")
+    return out
+
+
+def dequantize_q8_1(xq, n, k):
+    """q8_1 blocks -> (values d*q fp64 [n,k], d [n,k/32], s [n,k/32])."""
+    xq = _c(xq, np.uint8)
+    out = np.zeros((n, k), dtype=np.float64)
+    d = np.zeros((n, k // 32), dtype=np.float64)
+    s = np.zeros((n, k // 32), dtype=np.float64)
+    lib().oracle_dequantize_q8_1(_ptr(xq), n, k, _ptr(out), _ptr(d), _ptr(s))
+    return out, d, s
+
+
+def matmul_q8_1(qtype, w, rows, k, xq, n):
+    w = _c(w, np.uint8)
+    xq = _c(xq, np.uint8)
+    y = np.zeros((n, rows), dtype=np.float32)
+    rc = lib().oracle_matmul_q8_1(qtype, _ptr(w), rows, k, _ptr(xq), n, _ptr(y))
+    if rc:
+        raise ValueError("oracle_matmul_q8_1: bad arguments")
+    return y
+
+
+def matmul_q8_1_at(qtype, w, rows, k, xq, n, cols, rws):
+    w = _c(w, np.uint8)
+    xq = _c(xq, np.uint8)
+    cols = _c(cols, np.int64)
+    rws = _c(rws, np.int64)
+    out = np.zeros(cols.shape[0], dtype=np.float32)
+    rc = lib().oracle_matmul_q8_1_at(qtype, _ptr(w), rows, k, _ptr(xq), n, _ptr(cols), _ptr(rws),
+                                     cols.shape[0], _ptr(out))
+    if rc:
+        raise ValueError("oracle_matmul_q8_1_at: bad arguments")
+    return out
+
+
+def subdots(qtype, w, rows, k, xq, n):
+    """Integer sub-block dots, int32 [n, rows, k/32] (Q6_K: [n, rows, k/16])."""
+    w = _c(w, np.uint8)
+    xq = _c(xq, np.uint8)
+    per = int(lib().oracle_subdots_per_row(qtype, k))
+    D = np.zeros((n, rows, per), dtype=np.int32)
+    rc = lib().oracle_subdots(qtype, _ptr(w), rows, k, _ptr(xq), n, _ptr(D))
+    if rc:
+        raise ValueError("oracle_subdots: bad arguments")
+    return D
+
+
+def matmul(qtype, w, rows, k, x):
+    w = _c(w, np.uint8)
+    x = _c(x, np.float32)
+    n = x.shape[0]
+    y = np.zeros((n, rows), dtype=np.float32)
+    rc = lib().oracle_matmul(qtype, _ptr(w), rows, k, _ptr(x), n, _ptr(y))
+    if rc:
+        raise ValueError("oracle_matmul: bad arguments")
+    return y
+
+
+def matmul_id(qtype, w, n_exp, rows, k, x, x_per_tok, ids, fill=np.nan):
+    """Expert-indexed product; returns (y [n_tok, top_k, rows], n_invalid).  Rows of y whose id is
+    out of range keep `fill`."""
+    w = _c(w, np.uint8)
+    x = _c(x, np.float32)
+    ids = _c(ids, np.int32)
+    n_tok, top_k = ids.shape
+    y = np.full((n_tok, top_k, rows), fill, dtype=np.float32)
+    bad = ctypes.c_int64(0)
+    rc = lib().oracle_matmul_id(qtype, _ptr(w), n_exp, rows, k, _ptr(x), x_per_tok, _ptr(ids), n_tok,
+                                top_k, _ptr(y), ctypes.byref(bad))
+    if rc:
+        raise ValueError("oracle_matmul_id: bad arguments")
+    return y, int(bad.value)

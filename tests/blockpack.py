@@ -1,0 +1,138 @@
+"""Test-side block ENCODERS: integer fields -> block bytes, in the GGUF layouts.
+
+These go the opposite way from the oracle's decoders and share nothing with them, so a probe
+built here pins where each field lands.  Layouts (GGUF block definitions; the MMQ page gives the
+Q4_K size (144 B per 256 values), the half2 (d, dmin), the low/high nibble split per pair of
+sub-blocks, and the Q6_K ql/qh bit composition):
+
+  q4_K: d f16 @0, dmin f16 @2, 12 bytes of packed 6-bit (sc, m) @4, qs[128] @16
+  q6_K: ql[128] @0, qh[64] @128, int8 scales[16] @192, d f16 @208
+  q8_0: d f16 @0, int8 qs[32] @2
+"""
+import numpy as np
+
+
+def f16_bits(x):
+    return int(np.array([x], dtype=np.float32).astype(np.float16).view(np.uint16)[0])
+
+
+def _put16(buf, off, bits):
+    buf[off] = bits & 0xFF
+    buf[off + 1] = (bits >> 8) & 0xFF
+
+
+def pack_q4_K(d, dmin, sc, m, q):
+    """sc, m: 8 ints in [0,63]; q: 256 ints in [0,15] (value index order).  Returns 144 bytes."""
+    sc = [int(v) for v in sc]
+    m = [int(v) for v in m]
+    q = [int(v) for v in q]
+    assert len(sc) == 8 and len(m) == 8 and len(q) == 256
+    assert all(0 <= v < 64 for v in sc + m) and all(0 <= v < 16 for v in q)
+    b = np.zeros(144, dtype=np.uint8)
+    _put16(b, 0, f16_bits(d))
+    _put16(b, 2, f16_bits(dmin))
+    s = [0] * 12
+    for j in range(4):
+        # sub-blocks 0..3 keep their low 6 bits in bytes 0..3 (scale) and 4..7 (min)
+        s[j] |= sc[j] & 63
+        s[j + 4] |= m[j] & 63
+    for j in range(4, 8):
+        # sub-blocks 4..7: low 4 bits in bytes 8..11 (scale low nibble, min high nibble),
+        # top 2 bits in the spare top bits of bytes j-4 (scale) and j (min)
+        s[j + 4] |= (sc[j] & 15) | ((m[j] & 15) << 4)
+        s[j - 4] |= (sc[j] >> 4) << 6
+        s[j] |= (m[j] >> 4) << 6
+    b[4:16] = s
+    for chunk in range(4):                      # 64 values per 32 bytes
+        for l in range(32):
+            lo = q[64 * chunk + l]              # first sub-block of the pair -> low nibble
+            hi = q[64 * chunk + 32 + l]         # second sub-block -> high nibble
+            b[16 + 32 * chunk + l] = lo | (hi << 4)
+    return b
+
+
+def pack_q6_K(d, sc, q):
+    """sc: 16 ints in [-128,127]; q: 256 ints in [0,63] (stored 6-bit values, value index order)."""
+    q = [int(v) for v in q]
+    assert len(q) == 256 and all(0 <= v < 64 for v in q)
+    b = np.zeros(210, dtype=np.uint8)
+    for half in range(2):                       # 128 values per half
+        for l in range(32):
+            v0 = q[128 * half + l]
+            v1 = q[128 * half + 32 + l]
+            v2 = q[128 * half + 64 + l]
+            v3 = q[128 * half + 96 + l]
+            b[64 * half + l] = (v0 & 15) | ((v2 & 15) << 4)
+            b[64 * half + 32 + l] = (v1 & 15) | ((v3 & 15) << 4)
+            b[128 + 32 * half + l] = (v0 >> 4) | ((v1 >> 4) << 2) | ((v2 >> 4) << 4) | ((v3 >> 4) << 6)
+    b[192:208] = np.array(sc, dtype=np.int8).view(np.uint8)
+    _put16(b, 208, f16_bits(d))
+    return b
+
+
+def pack_q8_0(d, q):
+    b = np.zeros(34, dtype=np.uint8)
+    _put16(b, 0, f16_bits(d))
+    b[2:34] = np.array(q, dtype=np.int8).view(np.uint8)
+    return b
+
+
+def f16_value(x):
+    return float(np.float32(x).astype(np.float16))
+
+
+def random_q4_K_row(rng, k):
+    """Returns (bytes, fields) for one row of k values."""
+    blocks, fields = [], []
+    for _ in range(k // 256):
+        d = f16_value(rng.uniform(0.001, 0.02))
+        dmin = f16_value(rng.uniform(0.001, 0.02))
+        sc = rng.integers(0, 64, 8)
+        m = rng.integers(0, 64, 8)
+        q = rng.integers(0, 16, 256)
+        blocks.append(pack_q4_K(d, dmin, sc, m, q))
+        fields.append((d, dmin, sc, m, q))
+    return np.concatenate(blocks), fields
+
+
+def random_q6_K_row(rng, k):
+    blocks, fields = [], []
+    for _ in range(k // 256):
+        d = f16_value(rng.uniform(0.001, 0.02))
+        sc = rng.integers(-32, 32, 16)
+        q = rng.integers(0, 64, 256)
+        blocks.append(pack_q6_K(d, sc, q))
+        fields.append((d, sc, q))
+    return np.concatenate(blocks), fields
+
+
+def random_q8_0_row(rng, k):
+    blocks, fields = [], []
+    for _ in range(k // 32):
+        d = f16_value(rng.uniform(0.001, 0.02))
+        q = rng.integers(-127, 128, 32)
+        blocks.append(pack_q8_0(d, q))
+        fields.append((d, q))
+    return np.concatenate(blocks), fields
+
+
+def weight_codes(qtype, fields):
+    """Integer weight codes per value (Q4_K: [0,15]; Q6_K: q-32; Q8_0: int8) for one row."""
+    if qtype == 12:
+        return np.concatenate([f[4] for f in fields]).astype(np.int64)
+    if qtype == 14:
+        return np.concatenate([f[2] for f in fields]).astype(np.int64) - 32
+    return np.concatenate([f[1] for f in fields]).astype(np.int64)
+
+
+def q8_1_codes(xq_row):
+    """int8 codes of one canonical q8_1 row (36-byte blocks: d, s, 32 codes)."""
+    blk = np.asarray(xq_row, dtype=np.uint8).reshape(-1, 36)
+    return blk[:, 4:36].view(np.int8).reshape(-1).astype(np.int64)
+
+
+def q8_1_scales(xq_row):
+    blk = np.ascontiguousarray(np.asarray(xq_row, dtype=np.uint8).reshape(-1, 36))
+    d = blk[:, 0:2].copy().view(np.float16).reshape(-1).astype(np.float64)
+    s = blk[:, 2:4].copy().view(np.float16).reshape(-1).astype(np.float64)
+    return d, s
