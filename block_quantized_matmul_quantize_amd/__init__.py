@@ -1,0 +1,248 @@
+"""Python binding of libqmm: GGUF block-quantized (Q4_K / Q6_K / Q8_0) x q8_1 matmul on MI355X.
+
+Thin ctypes marshalling over the C ABI declared in include/qmm.h; every computation runs in the
+library's HIP kernels.  Function names follow the C entry points without the ``qmm_`` prefix.
+Tensors are torch tensors on a ROCm device; calls are enqueued on torch's current stream.
+There is no CPU fallback: if libqmm.so is missing, importing this package raises.
+"""
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqmm.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "qmm.h")
+
+Q8_0 = 8
+Q4_K = 12
+Q6_K = 14
+BLOCK_VALUES = {Q8_0: 32, Q4_K: 256, Q6_K: 256}
+BLOCK_BYTES = {Q8_0: 34, Q4_K: 144, Q6_K: 210}
+Q8_1_BYTES = 36
+
+OVR_PATH, OVR_STREAMK, OVR_TILE_J = 1, 2, 3
+PATH_AUTO, PATH_MATVEC, PATH_TILED = 0, 1, 2
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m block_quantized_matmul_quantize_amd.build`")
+
+# torch ships its own HIP runtime with the same soname as the system one; loading torch first
+# makes libqmm bind to that already-loaded runtime, so one HIP runtime owns the device.
+import torch  # noqa: E402,F401
+
+_L = ctypes.CDLL(LIB_PATH)
+_i64, _i32, _vp, _sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("regime", ctypes.c_int32), ("tile_i", ctypes.c_int32), ("tile_j", ctypes.c_int32),
+                ("ntiles", ctypes.c_int64), ("efficiency_pct", ctypes.c_int32), ("stream_k", ctypes.c_int32),
+                ("k_iters", ctypes.c_int64), ("units", ctypes.c_int64), ("fixup", ctypes.c_int32)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+def _sig(name, res, *args):
+    fn = getattr(_L, name)
+    fn.restype = res
+    fn.argtypes = list(args)
+    return fn
+
+
+_sig("qmm_last_error", ctypes.c_char_p)
+_sig("qmm_version", ctypes.c_char_p)
+_sig("qmm_quantize_q8_1", _i32, _vp, _i64, _i64, _vp, _vp)
+_sig("qmm_matmul_workspace", _sz, _i32, _i64, _i64, _i64)
+_sig("qmm_matmul", _i32, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _sz, _vp)
+_sig("qmm_matmul_q8_1_workspace", _sz, _i32, _i64, _i64, _i64)
+_sig("qmm_matmul_q8_1", _i32, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _sz, _vp)
+_sig("qmm_matmul_id_workspace", _sz, _i32, _i64, _i64, _i64, _i64, _i64, _i64)
+_sig("qmm_matmul_id", _i32, _i32, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _sz, _vp)
+_sig("qmm_matmul_id_invalid_count", _i32, _vp, ctypes.POINTER(_i64), _vp)
+_sig("qmm_debug_subdots", _i32, _i32, _vp, _i64, _i64, _vp, _i64, _i32, _vp, _vp)
+_sig("qmm_set_override", _i32, _i32, _i32)
+_sig("qmm_plan_dense", _i32, _i32, _i64, _i64, _i64, ctypes.c_int32, ctypes.POINTER(Plan))
+_sig("qmm_tile_efficiency", ctypes.c_int32, _i64, ctypes.c_int32)
+_sig("qmm_select_tile_j", ctypes.c_int32, _i64)
+_sig("qmm_streamk_unit_start", _i64, _i64, _i64, _i64, _i64)
+
+
+class QmmError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"qmm status {status}: {msg}")
+        self.status = status
+
+
+def _check(st):
+    if st != 0:
+        raise QmmError(st, _L.qmm_last_error().decode())
+
+
+def lib():
+    return _L
+
+
+def header_symbols():
+    """Entry points declared in include/qmm.h."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(qmm_[a-z0-9_]+)\s*\(", text)))
+
+
+def version():
+    return _L.qmm_version().decode()
+
+
+# --------------------------------------------------------------------------------------------
+# Host-side planner (no GPU needed)
+# --------------------------------------------------------------------------------------------
+def set_override(key, value):
+    _check(_L.qmm_set_override(key, value))
+
+
+def plan_dense(qtype, rows, k, n, nsm=256):
+    p = Plan()
+    _check(_L.qmm_plan_dense(qtype, rows, k, n, nsm, ctypes.byref(p)))
+    return p.as_dict()
+
+
+def tile_efficiency(ntiles, nsm):
+    return int(_L.qmm_tile_efficiency(ntiles, nsm))
+
+
+def select_tile_j(ncols):
+    return int(_L.qmm_select_tile_j(ncols))
+
+
+def streamk_unit_start(u, units, ntiles, k_iters):
+    return int(_L.qmm_streamk_unit_start(u, units, ntiles, k_iters))
+
+
+def matmul_workspace(qtype, rows, k, n):
+    return int(_L.qmm_matmul_workspace(qtype, rows, k, n))
+
+
+def matmul_q8_1_workspace(qtype, rows, k, n):
+    return int(_L.qmm_matmul_q8_1_workspace(qtype, rows, k, n))
+
+
+def matmul_id_workspace(qtype, n_exp, rows, k, n_tok, top_k, x_per_tok):
+    return int(_L.qmm_matmul_id_workspace(qtype, n_exp, rows, k, n_tok, top_k, x_per_tok))
+
+
+# --------------------------------------------------------------------------------------------
+# Device entry points (torch tensors)
+# --------------------------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _stream():
+    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def _need(t, dtype, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _workspace(nbytes, device):
+    torch = _torch()
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def quantize_q8_1(x, out=None):
+    """fp32 [n, k] -> uint8 [n, k/32*36] q8_1 blocks."""
+    torch = _torch()
+    px = _need(x, torch.float32, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [n, k]")
+    n, k = x.shape
+    if out is None:
+        out = torch.empty((n, (k // 32) * Q8_1_BYTES), dtype=torch.uint8, device=x.device)
+    py = _need(out, torch.uint8, "out")
+    _check(_L.qmm_quantize_q8_1(px, n, k, py, _stream()))
+    return out
+
+
+def matmul(w, qtype, rows, k, x, out=None, ws=None):
+    """Y[n, rows] = W[rows, k] . X[n, k]^T with X quantized to q8_1 on the way."""
+    torch = _torch()
+    pw = _need(w, torch.uint8, "w")
+    px = _need(x, torch.float32, "x")
+    if x.dim() != 2 or x.shape[1] != k:
+        raise ValueError(f"x must be [n, {k}]")
+    n = x.shape[0]
+    if out is None:
+        out = torch.empty((n, rows), dtype=torch.float32, device=x.device)
+    py = _need(out, torch.float32, "out")
+    nbytes = matmul_workspace(qtype, rows, k, n)
+    if ws is None:
+        ws = _workspace(nbytes, x.device)
+    _check(_L.qmm_matmul(qtype, pw, rows, k, px, n, py, ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream()))
+    return out
+
+
+def matmul_q8_1(w, qtype, rows, k, xq, n, out=None, ws=None):
+    """Same product from q8_1 activations (uint8 [n, k/32*36])."""
+    torch = _torch()
+    pw = _need(w, torch.uint8, "w")
+    px = _need(xq, torch.uint8, "xq")
+    if xq.numel() != n * (k // 32) * Q8_1_BYTES:
+        raise ValueError("xq has the wrong number of bytes")
+    if out is None:
+        out = torch.empty((n, rows), dtype=torch.float32, device=xq.device)
+    py = _need(out, torch.float32, "out")
+    nbytes = matmul_q8_1_workspace(qtype, rows, k, n)
+    if ws is None:
+        ws = _workspace(nbytes, xq.device)
+    _check(_L.qmm_matmul_q8_1(qtype, pw, rows, k, px, n, py, ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream()))
+    return out
+
+
+def matmul_id(w, qtype, n_exp, rows, k, x, ids, x_per_tok=1, out=None, ws=None):
+    """Expert-indexed product.  x: fp32 [n_tok*x_per_tok, k]; ids: int32 [n_tok, top_k];
+    returns y fp32 [n_tok, top_k, rows] (rows with an invalid id are left as they were in `out`)."""
+    torch = _torch()
+    pw = _need(w, torch.uint8, "w")
+    px = _need(x, torch.float32, "x")
+    pi = _need(ids, torch.int32, "ids")
+    n_tok, top_k = ids.shape
+    if x.shape != (n_tok * x_per_tok, k):
+        raise ValueError(f"x must be [{n_tok * x_per_tok}, {k}]")
+    if out is None:
+        out = torch.zeros((n_tok, top_k, rows), dtype=torch.float32, device=x.device)
+    py = _need(out, torch.float32, "out")
+    nbytes = matmul_id_workspace(qtype, n_exp, rows, k, n_tok, top_k, x_per_tok)
+    if ws is None:
+        ws = _workspace(nbytes, x.device)
+    _check(_L.qmm_matmul_id(qtype, pw, n_exp, rows, k, px, x_per_tok, pi, n_tok, top_k, py,
+                            ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream()))
+    return out, ws
+
+
+def matmul_id_invalid_count(ws):
+    v = _i64(0)
+    _check(_L.qmm_matmul_id_invalid_count(ctypes.c_void_p(ws.data_ptr()), ctypes.byref(v), _stream()))
+    return int(v.value)
+
+
+def debug_subdots(w, qtype, rows, k, xq, n, path):
+    """Integer sub-block dots from the chosen production kernel: int32 [n, rows, per]."""
+    torch = _torch()
+    pw = _need(w, torch.uint8, "w")
+    px = _need(xq, torch.uint8, "xq")
+    per = k // 16 if (qtype == Q6_K and path == PATH_MATVEC) else k // 32
+    out = torch.zeros((n, rows, per), dtype=torch.int32, device=xq.device)
+    _check(_L.qmm_debug_subdots(qtype, pw, rows, k, px, n, path, ctypes.c_void_p(out.data_ptr()), _stream()))
+    return out

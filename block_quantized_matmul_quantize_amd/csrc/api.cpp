@@ -1,0 +1,442 @@
+// C ABI of libqmm: argument validation, workspace layout, the host planner and the launches.
+// Declarations and the contract of every entry point are in include/qmm.h.
+#include "../../include/qmm.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <atomic>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_err;
+
+qmm_status fail(qmm_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+qmm_status fail(qmm_status st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+qmm_status hip_fail(hipError_t e, const char *what) {
+    return fail(QMM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+std::atomic<int> g_ovr_path{0}, g_ovr_streamk{0}, g_ovr_tile_j{0};
+
+constexpr int64_t kMaxK = 1 << 20;
+constexpr int64_t kMvMaxK = 32768;     // matrix-vector kernel stages k/32 scales in LDS
+constexpr int kTI = 128;
+constexpr int kSmallMax = 8;           // experts with <= 8 columns use the matrix-vector kernel
+
+int block_values(int type) {
+    switch (type) {
+        case QMM_Q4_K: case QMM_Q6_K: return 256;
+        case QMM_Q8_0: return 32;
+        default: return 0;
+    }
+}
+int block_bytes(int type) {
+    switch (type) {
+        case QMM_Q4_K: return 144;
+        case QMM_Q6_K: return 210;
+        case QMM_Q8_0: return 34;
+        default: return 0;
+    }
+}
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int g_nsm_cache[64];
+std::mutex g_nsm_mu;
+int device_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    std::lock_guard<std::mutex> lk(g_nsm_mu);
+    if (g_nsm_cache[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+        g_nsm_cache[dev] = v;
+    }
+    return g_nsm_cache[dev];
+}
+
+qmm_status check_common(int type, int64_t rows, int64_t k, int64_t n) {
+    const int qk = block_values(type);
+    if (qk == 0) return fail(QMM_ERR_TYPE, "unsupported weight type %d (supported: Q8_0=8, Q4_K=12, Q6_K=14)", type);
+    if (rows <= 0) return fail(QMM_ERR_ARG, "rows must be >= 1 (got %lld)", (long long)rows);
+    if (n < 0) return fail(QMM_ERR_ARG, "n must be >= 0 (got %lld)", (long long)n);
+    if (k <= 0 || k % qk != 0) return fail(QMM_ERR_SHAPE, "k=%lld is not a positive multiple of the block size %d", (long long)k, qk);
+    if (k > kMaxK) return fail(QMM_ERR_SHAPE, "k=%lld exceeds the supported maximum %lld", (long long)k, (long long)kMaxK);
+    if (rows > (1ll << 31) || n > (1ll << 31)) return fail(QMM_ERR_SHAPE, "rows/n too large");
+    return QMM_OK;
+}
+
+// Shared-memory footprint of the tiled kernel, for its occupancy estimate.
+int mmq_smem(int type, int J) {
+    const int nw = type == QMM_Q6_K ? 2 : 1;
+    return nw * kTI * 272 + J * 272 + 2 * 8 * kTI * 4 + 8 * J * 8;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *qmm_last_error(void) { return g_err.c_str(); }
+const char *qmm_version(void) { return "qmm 0.1 (gfx950)"; }
+
+int32_t qmm_tile_efficiency(int64_t ntiles, int32_t nsm) {
+    if (ntiles <= 0 || nsm <= 0) return 0;
+    const int64_t waves = (ntiles + nsm - 1) / nsm;
+    return (int32_t)(100 * ntiles / (nsm * waves));
+}
+
+int32_t qmm_select_tile_j(int64_t ncols) {
+    static const int32_t cand[] = {32, 64, 128};
+    int32_t best = cand[0];
+    int64_t best_tiles = INT64_MAX;
+    for (int32_t J : cand) {
+        const int64_t t = (ncols + J - 1) / J;
+        if (t < best_tiles) { best_tiles = t; best = J; }
+        if (best_tiles <= 1) break;
+    }
+    return best;
+}
+
+int64_t qmm_streamk_unit_start(int64_t u, int64_t units, int64_t ntiles, int64_t k_iters) {
+    if (units <= 0 || u < 0) return 0;
+    if (u > units) u = units;
+    const int64_t W = ntiles * k_iters;
+    return (u * W) / units;
+}
+
+qmm_status qmm_set_override(int key, int value) {
+    switch (key) {
+        case QMM_OVR_PATH:
+            if (value < 0 || value > 2) return fail(QMM_ERR_ARG, "path override must be 0, 1 or 2");
+            g_ovr_path = value; return QMM_OK;
+        case QMM_OVR_STREAMK:
+            if (value < 0 || value > 2) return fail(QMM_ERR_ARG, "stream-K override must be 0, 1 or 2");
+            g_ovr_streamk = value; return QMM_OK;
+        case QMM_OVR_TILE_J:
+            if (value != 0 && value != 32 && value != 64 && value != 128)
+                return fail(QMM_ERR_ARG, "tile width override must be 0, 32, 64 or 128");
+            g_ovr_tile_j = value; return QMM_OK;
+        default:
+            return fail(QMM_ERR_ARG, "unknown override key %d", key);
+    }
+}
+
+qmm_status qmm_plan_dense(int type, int64_t rows, int64_t k, int64_t n, int32_t nsm, qmm_plan *out) {
+    qmm_status st = check_common(type, rows, k, n);
+    if (st) return st;
+    if (!out || nsm <= 0) return fail(QMM_ERR_ARG, "null plan pointer or nsm <= 0");
+    qmm_plan p{};
+    const int path = g_ovr_path.load();
+    const bool mv = (path == 1) ? (n <= 8 && k <= kMvMaxK) : (path == 2 ? false : (n <= 8 && k <= kMvMaxK));
+    if (path == 1 && !mv) return fail(QMM_ERR_ARG, "matrix-vector path forced but n=%lld > 8 or k > %lld", (long long)n, (long long)kMvMaxK);
+    p.k_iters = (k + 255) / 256;
+    if (mv) {
+        p.regime = 1;
+        p.tile_i = 16;
+        p.tile_j = 8;
+        p.ntiles = (rows + 15) / 16;
+        p.efficiency_pct = qmm_tile_efficiency(p.ntiles, nsm);
+        p.units = p.ntiles;
+        out[0] = p;
+        return QMM_OK;
+    }
+    p.regime = 2;
+    p.tile_i = kTI;
+    p.tile_j = g_ovr_tile_j.load() ? g_ovr_tile_j.load() : qmm_select_tile_j(n);
+    const int64_t n_ct = (n + p.tile_j - 1) / p.tile_j;
+    p.ntiles = ((rows + kTI - 1) / kTI) * n_ct;
+    const int occ = std::max(1, std::min(2, (160 * 1024) / mmq_smem(type, p.tile_j)));
+    const int32_t slots = nsm * occ;
+    p.efficiency_pct = qmm_tile_efficiency(p.ntiles, slots);
+    const int sk = g_ovr_streamk.load();
+    bool use_sk = p.efficiency_pct < 90 && p.k_iters > 1;
+    if (sk == 1) use_sk = false;
+    if (sk == 2) use_sk = p.k_iters > 1 || p.ntiles > 1;
+    p.stream_k = use_sk ? 1 : 0;
+    const int64_t nwork = p.ntiles * p.k_iters;
+    p.units = use_sk ? std::min<int64_t>(slots, nwork) : p.ntiles;
+    p.fixup = use_sk && (p.ntiles % p.units != 0) ? 1 : 0;
+    out[0] = p;
+    return QMM_OK;
+}
+
+// ----------------------------------------------------------------------------------------------
+// Dense product
+// ----------------------------------------------------------------------------------------------
+namespace {
+
+struct DenseWs {
+    size_t xq_off, tab_off, part_off, total;
+};
+
+DenseWs dense_layout(int type, int64_t rows, int64_t k, int64_t n, bool with_xq) {
+    DenseWs L{};
+    const int64_t nb = k / 32;
+    size_t off = 0;
+    L.xq_off = off;
+    if (with_xq) off = align_up(off + (size_t)(n * nb * 36), 256);
+    L.tab_off = off;
+    off = align_up(off + (size_t)(nb * std::max<int64_t>(n, 1) * 8), 256);
+    L.part_off = off;
+    if (n > 8 || g_ovr_path.load() == 2) {
+        // stream-K partial slots: at most (compute units x 2 resident) units x 2 slots x 128 x 128
+        const int64_t nsm = device_cus();
+        const int64_t ntiles_max = ((rows + kTI - 1) / kTI) * ((n + 31) / 32);
+        const int64_t units = std::min<int64_t>(2 * nsm, ntiles_max * ((k + 255) / 256));
+        off = align_up(off + (size_t)(units * 2 * kTI * 128 * 4), 256);
+    }
+    L.total = off;
+    return L;
+}
+
+qmm_status run_dense(int type, const void *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y,
+                     uint8_t *ws, const DenseWs &L, int32_t *dbg, int dbg_path, hipStream_t s) {
+    const int64_t nb = k / 32;
+    float2 *tab = (float2 *)(ws + L.tab_off);
+    hipError_t e;
+    if (!dbg) {
+        e = qmm::launch_q8_1_scale_table(xq, n, k, tab, n, s);
+        if (e != hipSuccess) return hip_fail(e, "scale table launch");
+    }
+    qmm_plan p{};
+    qmm_status st;
+    if (dbg) {
+        // debug export: the chosen kernel, no stream-K
+        const int save_path = g_ovr_path.load(), save_sk = g_ovr_streamk.load();
+        g_ovr_path = dbg_path;
+        g_ovr_streamk = 1;
+        st = qmm_plan_dense(type, rows, k, n, device_cus(), &p);
+        g_ovr_path = save_path;
+        g_ovr_streamk = save_sk;
+    } else {
+        st = qmm_plan_dense(type, rows, k, n, device_cus(), &p);
+    }
+    if (st) return st;
+    (void)nb;
+    if (p.regime == 1) {
+        e = qmm::launch_mmvq(type, (const uint8_t *)w, rows, k, xq, tab, n, n, y, dbg, nullptr, 0, s);
+        if (e != hipSuccess) return hip_fail(e, "matrix-vector kernel launch");
+        return QMM_OK;
+    }
+    qmm::MmqLaunch ml{};
+    ml.tile_j = p.tile_j;
+    ml.ntiles = p.ntiles;
+    ml.n_ct = (n + p.tile_j - 1) / p.tile_j;
+    ml.k_iters = p.k_iters;
+    ml.units = p.units;
+    ml.stream_k = p.stream_k != 0;
+    ml.partials = (float *)(ws + L.part_off);
+    if (ml.stream_k && (size_t)(L.part_off + (size_t)ml.units * 2 * kTI * p.tile_j * 4) > L.total)
+        return fail(QMM_ERR_WORKSPACE, "internal: stream-K partials exceed the workspace");
+    e = qmm::launch_mmq(type, (const uint8_t *)w, rows, k, xq, tab, n, n, y, dbg, ml, s);
+    if (e != hipSuccess) return hip_fail(e, "tiled kernel launch");
+    return QMM_OK;
+}
+
+qmm_status check_ptrs_dense(const void *w, const void *x, const float *y, int64_t n) {
+    if (n == 0) return QMM_OK;
+    if (!w || !x || !y) return fail(QMM_ERR_ARG, "null w, x or y");
+    if (((uintptr_t)w) & 1) return fail(QMM_ERR_ARG, "w must be 2-byte aligned");
+    if (((uintptr_t)y) & 3) return fail(QMM_ERR_ARG, "y must be 4-byte aligned");
+    return QMM_OK;
+}
+
+}  // namespace
+
+qmm_status qmm_quantize_q8_1(const float *x, int64_t n_rows, int64_t k, void *y, void *stream) {
+    if (n_rows < 0) return fail(QMM_ERR_ARG, "n_rows must be >= 0");
+    if (k <= 0 || k % 32 != 0) return fail(QMM_ERR_SHAPE, "k=%lld is not a positive multiple of 32", (long long)k);
+    if (k > kMaxK) return fail(QMM_ERR_SHAPE, "k too large");
+    if (n_rows == 0) return QMM_OK;
+    if (!x || !y) return fail(QMM_ERR_ARG, "null x or y");
+    if (((uintptr_t)x) & 15) return fail(QMM_ERR_ARG, "x must be 16-byte aligned");
+    if (((uintptr_t)y) & 3) return fail(QMM_ERR_ARG, "y must be 4-byte aligned");
+    hipError_t e = qmm::launch_quantize_q8_1(x, n_rows, k, (uint8_t *)y, nullptr, 0, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "quantize launch");
+    return QMM_OK;
+}
+
+size_t qmm_matmul_workspace(int type, int64_t rows, int64_t k, int64_t n) {
+    if (check_common(type, rows, k, n)) return 0;
+    return dense_layout(type, rows, k, n, true).total;
+}
+
+size_t qmm_matmul_q8_1_workspace(int type, int64_t rows, int64_t k, int64_t n) {
+    if (check_common(type, rows, k, n)) return 0;
+    return dense_layout(type, rows, k, n, false).total;
+}
+
+qmm_status qmm_matmul(int type, const void *w, int64_t rows, int64_t k, const float *x, int64_t n, float *y,
+                      void *ws, size_t ws_bytes, void *stream) {
+    qmm_status st = check_common(type, rows, k, n);
+    if (st) return st;
+    if ((st = check_ptrs_dense(w, x, y, n))) return st;
+    if (n == 0) return QMM_OK;
+    if (((uintptr_t)x) & 15) return fail(QMM_ERR_ARG, "x must be 16-byte aligned");
+    const DenseWs L = dense_layout(type, rows, k, n, true);
+    if (!ws || ws_bytes < L.total)
+        return fail(QMM_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", ws_bytes, L.total);
+    if (((uintptr_t)ws) & 255) return fail(QMM_ERR_ARG, "workspace must be 256-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    uint8_t *wsb = (uint8_t *)ws;
+    hipError_t e = qmm::launch_quantize_q8_1(x, n, k, wsb + L.xq_off, nullptr, 0, s);
+    if (e != hipSuccess) return hip_fail(e, "quantize launch");
+    return run_dense(type, w, rows, k, wsb + L.xq_off, n, y, wsb, L, nullptr, 0, s);
+}
+
+qmm_status qmm_matmul_q8_1(int type, const void *w, int64_t rows, int64_t k, const void *xq, int64_t n, float *y,
+                           void *ws, size_t ws_bytes, void *stream) {
+    qmm_status st = check_common(type, rows, k, n);
+    if (st) return st;
+    if ((st = check_ptrs_dense(w, xq, y, n))) return st;
+    if (n == 0) return QMM_OK;
+    if (((uintptr_t)xq) & 3) return fail(QMM_ERR_ARG, "xq must be 4-byte aligned");
+    const DenseWs L = dense_layout(type, rows, k, n, false);
+    if (!ws || ws_bytes < L.total)
+        return fail(QMM_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", ws_bytes, L.total);
+    if (((uintptr_t)ws) & 255) return fail(QMM_ERR_ARG, "workspace must be 256-byte aligned");
+    return run_dense(type, w, rows, k, (const uint8_t *)xq, n, y, (uint8_t *)ws, L, nullptr, 0, (hipStream_t)stream);
+}
+
+qmm_status qmm_debug_subdots(int type, const void *w, int64_t rows, int64_t k, const void *xq, int64_t n, int path,
+                             int32_t *d_out, void *stream) {
+    qmm_status st = check_common(type, rows, k, n);
+    if (st) return st;
+    if (path != 1 && path != 2) return fail(QMM_ERR_ARG, "path must be 1 (matrix-vector) or 2 (tiled)");
+    if (path == 1 && (n > 8 || k > kMvMaxK)) return fail(QMM_ERR_ARG, "matrix-vector debug export needs n <= 8");
+    if (n == 0) return QMM_OK;
+    if (!w || !xq || !d_out) return fail(QMM_ERR_ARG, "null pointer");
+    DenseWs L{};
+    return run_dense(type, w, rows, k, (const uint8_t *)xq, n, nullptr, nullptr, L, d_out, path, (hipStream_t)stream);
+}
+
+// ----------------------------------------------------------------------------------------------
+// Expert-indexed product
+// ----------------------------------------------------------------------------------------------
+namespace {
+
+struct IdWs {
+    size_t invalid_off, xq_off, tab_off, sorted_off, bounds_off, tstart_off, small_off, total;
+};
+
+IdWs id_layout(int64_t n_exp, int64_t k, int64_t n_tok, int64_t top_k, int64_t x_per_tok) {
+    IdWs L{};
+    const int64_t nb = k / 32;
+    const int64_t nx = n_tok * x_per_tok;
+    const int64_t pairs = n_tok * top_k;
+    size_t off = 0;
+    L.invalid_off = off; off = align_up(off + 4, 256);   // first, so the count is found from ws alone
+    L.xq_off = off; off = align_up(off + (size_t)(nx * nb * 36), 256);
+    L.tab_off = off; off = align_up(off + (size_t)(nb * std::max<int64_t>(nx, 1) * 8), 256);
+    L.sorted_off = off; off = align_up(off + (size_t)(std::max<int64_t>(pairs, 1) * 4), 256);
+    L.bounds_off = off; off = align_up(off + (size_t)((n_exp + 1) * 4), 256);
+    L.tstart_off = off; off = align_up(off + (size_t)((n_exp + 1) * 4), 256);
+    L.small_off = off; off = align_up(off + (size_t)(n_exp * 4), 256);
+    L.total = off;
+    return L;
+}
+
+int id_tile_j(int64_t pairs, int64_t n_exp) {
+    const int ov = g_ovr_tile_j.load();
+    if (ov) return ov;
+    // all columns of the call, as the MMQ page's default "ncols_opt" for expert mode
+    (void)n_exp;
+    return qmm_select_tile_j(pairs);
+}
+
+}  // namespace
+
+size_t qmm_matmul_id_workspace(int type, int64_t n_exp, int64_t rows, int64_t k, int64_t n_tok, int64_t top_k,
+                               int64_t x_per_tok) {
+    if (check_common(type, rows, k, n_tok)) return 0;
+    if (n_exp <= 0 || top_k <= 0 || (x_per_tok != 1 && x_per_tok != top_k)) return 0;
+    return id_layout(n_exp, k, n_tok, top_k, x_per_tok).total;
+}
+
+qmm_status qmm_matmul_id(int type, const void *w, int64_t n_exp, int64_t rows, int64_t k, const float *x,
+                         int64_t x_per_tok, const int32_t *ids, int64_t n_tok, int64_t top_k, float *y, void *ws,
+                         size_t ws_bytes, void *stream) {
+    qmm_status st = check_common(type, rows, k, n_tok);
+    if (st) return st;
+    if (n_exp <= 0 || n_exp > 32768) return fail(QMM_ERR_ARG, "n_exp must be in [1, 32768]");
+    if (top_k <= 0) return fail(QMM_ERR_ARG, "top_k must be >= 1");
+    if (x_per_tok != 1 && x_per_tok != top_k) return fail(QMM_ERR_ARG, "x_per_tok must be 1 or top_k");
+    if (n_tok * top_k > (1ll << 30)) return fail(QMM_ERR_SHAPE, "too many (token, slot) pairs");
+    const IdWs L = id_layout(n_exp, k, n_tok, top_k, x_per_tok);
+    if (!ws || ws_bytes < L.total)
+        return fail(QMM_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", ws_bytes, L.total);
+    if (((uintptr_t)ws) & 255) return fail(QMM_ERR_ARG, "workspace must be 256-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    uint8_t *wsb = (uint8_t *)ws;
+    int32_t *invalid = (int32_t *)(wsb + L.invalid_off);
+    if (n_tok == 0) {
+        hipError_t e = qmm::launch_fill_u32((uint32_t *)invalid, 1, 0u, s);
+        return e == hipSuccess ? QMM_OK : hip_fail(e, "fill launch");
+    }
+    if (!w || !x || !ids || !y) return fail(QMM_ERR_ARG, "null w, x, ids or y");
+    if (((uintptr_t)w) & 1) return fail(QMM_ERR_ARG, "w must be 2-byte aligned");
+    if (((uintptr_t)x) & 15) return fail(QMM_ERR_ARG, "x must be 16-byte aligned");
+    if (((uintptr_t)y) & 3 || ((uintptr_t)ids) & 3) return fail(QMM_ERR_ARG, "y and ids must be 4-byte aligned");
+
+    const int64_t nx = n_tok * x_per_tok;
+    const int64_t pairs = n_tok * top_k;
+    uint8_t *xq = wsb + L.xq_off;
+    float2 *tab = (float2 *)(wsb + L.tab_off);
+    hipError_t e = qmm::launch_quantize_q8_1(x, nx, k, xq, tab, nx, s);
+    if (e != hipSuccess) return hip_fail(e, "quantize launch");
+    const int tile_j = id_tile_j(pairs, n_exp);
+    qmm::ColMap cm{};
+    cm.sorted = (const int32_t *)(wsb + L.sorted_off);
+    cm.bounds = (const int32_t *)(wsb + L.bounds_off);
+    cm.tile_start = (const int32_t *)(wsb + L.tstart_off);
+    cm.small = (const int32_t *)(wsb + L.small_off);
+    cm.top_k = (int32_t)top_k;
+    cm.x_per_tok = (int32_t)x_per_tok;
+    cm.n_exp = (int32_t)n_exp;
+    cm.w_expert_stride = rows * (k / block_values(type)) * block_bytes(type);
+    const int small_max = k <= kMvMaxK ? kSmallMax : 0;
+    e = qmm::launch_moe_group(ids, pairs, (int32_t)n_exp, tile_j, small_max, (int32_t *)cm.sorted,
+                              (int32_t *)cm.bounds, (int32_t *)cm.tile_start, (int32_t *)cm.small, invalid, s);
+    if (e != hipSuccess) return hip_fail(e, "grouping launch");
+    // experts with <= 8 columns: matrix-vector kernel, one workgroup row per listed expert
+    if (k <= kMvMaxK) {
+        e = qmm::launch_mmvq(type, (const uint8_t *)w, rows, k, xq, tab, nx, 0, y, nullptr, &cm, n_exp, s);
+        if (e != hipSuccess) return hip_fail(e, "expert matrix-vector launch");
+    }
+    // the rest: tiled kernel over the device-built column-tile list
+    const int64_t mmq_experts = std::min<int64_t>(n_exp, pairs / (small_max + 1));
+    const int64_t max_ct = (pairs + tile_j - 1) / tile_j + mmq_experts;
+    e = qmm::launch_mmq_id(type, (const uint8_t *)w, rows, k, xq, tab, nx, y, cm, tile_j, max_ct, s);
+    if (e != hipSuccess) return hip_fail(e, "expert tiled launch");
+    return QMM_OK;
+}
+
+qmm_status qmm_matmul_id_invalid_count(const void *ws, int64_t *out, void *stream) {
+    if (!ws || !out) return fail(QMM_ERR_ARG, "null ws or out");
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+    int32_t v = 0;
+    e = hipMemcpy(&v, ws, sizeof v, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "copy of the invalid-id count");
+    *out = v;
+    return QMM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,64 @@
+// Shared device/host definitions for libqmm (gfx950 / CDNA4, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace qmm {
+
+constexpr int kQ8_0 = 8;
+constexpr int kQ4_K = 12;
+constexpr int kQ6_K = 14;
+
+// GGUF block geometry.
+template <int T> struct Fmt;
+template <> struct Fmt<kQ4_K> { static constexpr int QK = 256, BYTES = 144; };
+template <> struct Fmt<kQ6_K> { static constexpr int QK = 256, BYTES = 210; };
+template <> struct Fmt<kQ8_0> { static constexpr int QK = 32, BYTES = 34; };
+
+constexpr int kQ8_1Bytes = 36;       // {fp16 d, fp16 s, int8 q[32]}
+constexpr int kSuper = 256;          // K values per planning step (one K-quant super-block)
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+// 16-byte vector with only 2-byte alignment guaranteed: Q6_K (210 B) and Q8_0 (34 B) blocks
+// and the q8_1 code arrays sit at 2- or 4-byte offsets.  gfx950 global loads accept these.
+typedef u32x4 __attribute__((aligned(2))) u32x4_a2;
+typedef uint32_t __attribute__((aligned(2))) u32_a2;
+
+__device__ __forceinline__ u32x4 ld16(const uint8_t *p) { return *(const u32x4_a2 *)p; }
+__device__ __forceinline__ uint32_t ld4(const uint8_t *p) { return *(const u32_a2 *)p; }
+__device__ __forceinline__ uint16_t ld2(const uint8_t *p) { return *(const uint16_t *)p; }
+
+__device__ __forceinline__ float h2f(uint16_t bits) {
+    return __half2float(__ushort_as_half(bits));
+}
+
+// MFMA wrappers.  16x16x64: A lane l holds row l%16, B lane l column l%16, each 16 int8 of the
+// K slots owned by lane group l/16; C lane l holds C[4*(l/16)+e][l%16], e = 0..3.
+__device__ __forceinline__ i32x4 mfma16x16x64(u32x4 a, u32x4 b, i32x4 c) {
+    return __builtin_amdgcn_mfma_i32_16x16x64_i8((i32x4)a, (i32x4)b, c, 0, 0, 0);
+}
+// 32x32x32: A lane l holds row l%32, B lane l column l%32, 16 int8 each of the K slots owned by
+// lane group l/32; C lane l holds C[8*(e/4) + 4*(l/32) + e%4][l%32], e = 0..15.
+__device__ __forceinline__ i32x16 mfma32x32x32(u32x4 a, u32x4 b, i32x16 c) {
+    return __builtin_amdgcn_mfma_i32_32x32x32_i8((i32x4)a, (i32x4)b, c, 0, 0, 0);
+}
+
+// Per-byte x - 32 for bytes in [0, 63] (no borrow crosses a byte: each byte first gets its top
+// bit set, and the top bit is flipped back afterwards).
+__device__ __forceinline__ uint32_t sub32_bytes(uint32_t x) {
+    return ((x | 0x80808080u) - 0x20202020u) ^ 0x80808080u;
+}
+
+// Workgroup index -> work index such that each XCD (workgroups are dealt round-robin over the
+// 8 XCDs) gets one contiguous range of work, keeping neighbouring tiles in one L2.
+__device__ __forceinline__ int64_t xcd_remap(int64_t b, int64_t n) {
+    const int64_t q = n / 8, r = n % 8;
+    const int64_t x = b % 8, i = b / 8;
+    return x * q + (x < r ? x : r) + i;
+}
+
+}  // namespace qmm

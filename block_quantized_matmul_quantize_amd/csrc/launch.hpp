@@ -1,0 +1,57 @@
+// Host-side launch functions implemented by the kernel translation units.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmm {
+
+hipError_t launch_quantize_q8_1(const float *x, int64_t n_rows, int64_t k, uint8_t *y, float2 *tab,
+                                int64_t tab_ld, hipStream_t s);
+hipError_t launch_q8_1_scale_table(const uint8_t *xq, int64_t n_rows, int64_t k, float2 *tab, int64_t tab_ld,
+                                   hipStream_t s);
+hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t s);
+
+// Column map for the matrix-vector and tiled kernels.  Dense: column j reads activation row j
+// and writes output row j.  Expert mode: columns are the expert's (token, slot) pairs taken from
+// the device-side sorted list.
+struct ColMap {
+    // expert mode only (all null / zero for dense)
+    const int32_t *sorted;     // [pairs] pair index (t*top_k + slot), grouped by expert
+    const int32_t *bounds;     // [n_exp + 1] segment starts in `sorted`
+    const int32_t *tile_start; // [n_exp + 1] prefix of tiled-kernel column tiles per expert
+    const int32_t *small;      // [n_exp] experts handled by the matrix-vector kernel, then -1
+    int32_t top_k;
+    int32_t x_per_tok;
+    int32_t n_exp;
+    int64_t w_expert_stride;   // bytes between expert matrices
+};
+
+// Matrix-vector kernel: n <= 8 columns (dense) or the small experts (expert mode, grid.y = n_exp).
+hipError_t launch_mmvq(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq,
+                       const float2 *tab, int64_t tab_ld, int64_t n, float *y, int32_t *dbg,
+                       const ColMap *cm, int64_t n_exp, hipStream_t s);
+
+// Tiled int8-MFMA kernel plan.
+struct MmqLaunch {
+    int tile_j;          // 32, 64 or 128
+    int64_t ntiles;      // row tiles x column tiles (dense)
+    int64_t n_ct;        // column tiles
+    int64_t k_iters;     // K steps of 256 values
+    int64_t units;       // workgroups (== ntiles unless stream-K)
+    bool stream_k;
+    float *partials;     // [units][2][128*tile_j] when stream_k
+};
+hipError_t launch_mmq(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq,
+                      const float2 *tab, int64_t tab_ld, int64_t n, float *y, int32_t *dbg,
+                      const MmqLaunch &plan, hipStream_t s);
+// Expert mode: grid over (row tiles, max column tiles); experts with > 8 columns.
+hipError_t launch_mmq_id(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq,
+                         const float2 *tab, int64_t tab_ld, float *y, const ColMap &cm,
+                         int tile_j, int64_t max_col_tiles, hipStream_t s);
+
+// Expert grouping: counts, bounds, stable sorted pair list, column-tile prefix, small-expert list.
+hipError_t launch_moe_group(const int32_t *ids, int64_t pairs, int32_t n_exp, int32_t tile_j,
+                            int32_t small_max, int32_t *sorted, int32_t *bounds, int32_t *tile_start,
+                            int32_t *small, int32_t *invalid, hipStream_t s);
+
+}  // namespace qmm

@@ -1,0 +1,168 @@
+/*
+ * qmm.h -- C ABI of libqmm: GGUF block-quantized weights (Q4_K, Q6_K, Q8_0) times fp32
+ * activations quantized to q8_1, on AMD Instinct MI355X (gfx950).
+ *
+ * Sources (the web pages this library implements):
+ *  [MMQ]   "llama.cpp source walkthrough (15): quantized GEMM -- MMQ" (pinghaoyang.com.cn)
+ *  [GP100] "Patch 0007: an fp16 matrix-vector path for GP100"
+ *  [QMM]   "QTensor and QMatMul" (candle-core 0.11.0 documentation)
+ *
+ * Conventions shared by every entry point
+ *  - Pointers named w, x, xq, y, ids, ws, d_out are DEVICE pointers owned by the caller.  The
+ *    library never frees them and keeps no reference after the call returns.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL means the default stream).
+ *    Arguments are validated on the host before anything is launched; a non-zero status means
+ *    nothing was launched, except QMM_ERR_HIP (a launch failed part-way).
+ *  - Weights are a row-major [rows][k] matrix stored as raw GGUF blocks: each row is k/QK blocks
+ *    back to back, rows back to back ([QMM] "QTensor": the last dimension must be a multiple of
+ *    the block size and a block never spans rows).  QK = 256 for Q4_K/Q6_K, 32 for Q8_0.  Block
+ *    bytes: Q4_K 144 {fp16 d, fp16 dmin, 12 B packed 6-bit scales/mins, 128 B nibbles};
+ *    Q6_K 210 {128 B ql, 64 B qh, 16 int8 scales, fp16 d}; Q8_0 34 {fp16 d, 32 int8}.  Only
+ *    2-byte alignment of w is required.
+ *  - Activations x are fp32 row-major [n][k] (token-major, [QMM] "QMatMul": input [..., k]),
+ *    4-byte aligned.  Outputs y are fp32 row-major [n][rows] (output [..., n]).
+ *  - q8_1 blocks (36 B): {fp16 d, fp16 s, int8 q[32]}, one per 32 activation values; [MMQ]
+ *    introduction and "dp4a path Q4_K" section (the activation half2 (d, s), s = d * sum(q)).
+ *    Quantization: amax = max|x|; d32 = amax/127 (fp32); q = round-half-away(x / d32);
+ *    d = fp16(d32); s = fp16(d32 * sum(q)); an all-zero block gives d = s = q = 0.
+ *  - Result ([MMQ] "dp4a path Q4_K", "Q6_K dot", "write-back"): per 32-value block b an exact
+ *    integer dot D_b of weight codes and q8_1 codes, then fp32 scale fixups:
+ *      Q4_K  y += d*sc_b*d_b*D_b - dmin*m_b*s_b
+ *      Q6_K  y += d*d_b*(sc_{2b}*D_{2b} + sc_{2b+1}*D_{2b+1})   (16-value sub-blocks)
+ *      Q8_0  y += dw_b*d_b*D_b
+ *    summed in fp32 in an order that depends on the chosen kernel (several fp32 results are
+ *    correct; see qmm_set_override).  For a fixed plan the result is bitwise reproducible.
+ *  - Errors: a status code; qmm_last_error() returns a message for the calling thread.
+ */
+#ifndef QMM_H
+#define QMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QMM_OK = 0,
+    QMM_ERR_ARG = -1,        /* null pointer, negative size, bad x_per_tok, ... */
+    QMM_ERR_TYPE = -2,       /* weight type not supported */
+    QMM_ERR_SHAPE = -3,      /* k not a multiple of the block size, or too large */
+    QMM_ERR_WORKSPACE = -4,  /* workspace pointer null or smaller than the *_workspace size */
+    QMM_ERR_HIP = -5         /* a HIP call failed (message in qmm_last_error) */
+} qmm_status;
+
+typedef enum { QMM_Q8_0 = 8, QMM_Q4_K = 12, QMM_Q6_K = 14 } qmm_type; /* GGUF type ids */
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char *qmm_last_error(void);
+
+/* Library version string. */
+const char *qmm_version(void);
+
+/* ---------------------------------------------------------------------------------------------
+ * a1: activation quantization ([MMQ] introduction; "dp4a path Q4_K": s = d * sum(q)).
+ * x: fp32 [n_rows][k], k % 32 == 0.  y: n_rows * (k/32) q8_1 blocks of 36 bytes, row-major,
+ * 4-byte aligned.  n_rows == 0 is a no-op.
+ * ------------------------------------------------------------------------------------------- */
+qmm_status qmm_quantize_q8_1(const float *x, int64_t n_rows, int64_t k, void *y, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Dense product Y[n][rows] = W[rows][k] . X[n][k]^T with q8_1 activations.
+ * Regimes ([MMQ] "shape criteria" and the MMVQ-vs-MMQ table): n <= 8 uses the matrix-vector
+ * kernel (weights streamed once, all columns per pass); n > 8 uses the tiled int8-MFMA GEMM with
+ * a tile-width selector and a stream-K split when the tiles underfill the GPU ([MMQ] "J runtime
+ * selection", "tile efficiency", "stream-K", "fixup").
+ *
+ * qmm_matmul_workspace: bytes of device workspace qmm_matmul needs (>= 0; 256-byte aligned
+ *   pointer expected).  Returns 0 for invalid arguments.
+ * qmm_matmul: quantizes x to q8_1 into the workspace, then multiplies.
+ * qmm_matmul_q8_1: the same product from already-quantized activations xq (n * k/32 q8_1
+ *   blocks, as written by qmm_quantize_q8_1), so one quantization can serve several weights
+ *   ([GP100] "How": the activation-conversion cache).  Uses qmm_matmul_q8_1_workspace bytes.
+ * n == 0 is a no-op.  rows >= 1, k >= QK, k % QK == 0, k <= 1<<20.
+ * ------------------------------------------------------------------------------------------- */
+size_t qmm_matmul_workspace(int type, int64_t rows, int64_t k, int64_t n);
+qmm_status qmm_matmul(int type, const void *w, int64_t rows, int64_t k, const float *x, int64_t n,
+                      float *y, void *ws, size_t ws_bytes, void *stream);
+size_t qmm_matmul_q8_1_workspace(int type, int64_t rows, int64_t k, int64_t n);
+qmm_status qmm_matmul_q8_1(int type, const void *w, int64_t rows, int64_t k, const void *xq,
+                           int64_t n, float *y, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Expert-indexed product (MoE mul_mat_id; [MMQ] "MoE dispatch", "expert bounds", "MoE skew").
+ * w: n_exp weight matrices [rows][k] back to back (ggml [k, rows, n_exp]).
+ * ids: int32 [n_tok][top_k] expert ids (ggml [n_expert_used, n_tokens]).
+ * x: fp32 [n_tok][x_per_tok][k]; x_per_tok == 1 (one row shared by every slot, gate/up) or
+ *    x_per_tok == top_k (one row per slot, down projection).
+ * y: fp32 [n_tok][top_k][rows]: row (t, j) = W[ids[t][j]] . x[t][j or 0], written back in the
+ *    original (token, slot) order.
+ * Grouping by expert, per-expert column counts, tile enumeration and the per-expert choice of
+ * matrix-vector vs tiled kernel all happen on the device; nothing is read back to the host.
+ * An id outside [0, n_exp) is skipped: its output row is left untouched and a counter in the
+ * workspace is incremented (qmm_matmul_id_invalid_count reads it after the stream completes).
+ * ------------------------------------------------------------------------------------------- */
+size_t qmm_matmul_id_workspace(int type, int64_t n_exp, int64_t rows, int64_t k, int64_t n_tok,
+                               int64_t top_k, int64_t x_per_tok);
+qmm_status qmm_matmul_id(int type, const void *w, int64_t n_exp, int64_t rows, int64_t k,
+                         const float *x, int64_t x_per_tok, const int32_t *ids, int64_t n_tok,
+                         int64_t top_k, float *y, void *ws, size_t ws_bytes, void *stream);
+/* Host pointer out receives the invalid-id count of the last qmm_matmul_id that used `ws`
+ * (synchronizes `stream` first). */
+qmm_status qmm_matmul_id_invalid_count(const void *ws, int64_t *out, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Test hook: the integer sub-block dots from the production kernels' own integer accumulators
+ * ([MMQ] "write-back": the integer part is exact).  path: 1 = matrix-vector kernel,
+ * 2 = tiled MFMA kernel.  d_out: int32 [n][rows][per] with
+ *   per = k/32 for Q4_K and Q8_0 (D_b),
+ *   Q6_K path 1: per = k/16 (D per 16-value sub-block),
+ *   Q6_K path 2: per = k/32, the scale-folded integer sc_{2b}*D_{2b} + sc_{2b+1}*D_{2b+1}.
+ * Path 1 requires n <= 8.
+ * ------------------------------------------------------------------------------------------- */
+qmm_status qmm_debug_subdots(int type, const void *w, int64_t rows, int64_t k, const void *xq,
+                             int64_t n, int path, int32_t *d_out, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Plan overrides for tests and tuning (process-wide; 0 = automatic).
+ *   QMM_OVR_PATH:     1 force matrix-vector (only when n <= 8), 2 force tiled MFMA.
+ *   QMM_OVR_STREAMK:  1 force off, 2 force on (tiled path).
+ *   QMM_OVR_TILE_J:   tile width in columns (32, 64 or 128).
+ * Returns QMM_ERR_ARG for an unknown key or value.
+ * ------------------------------------------------------------------------------------------- */
+enum { QMM_OVR_PATH = 1, QMM_OVR_STREAMK = 2, QMM_OVR_TILE_J = 3 };
+qmm_status qmm_set_override(int key, int value);
+
+/* ---------------------------------------------------------------------------------------------
+ * Host-side planner, exposed so its arithmetic can be tested without a GPU.
+ * ([MMQ] "J runtime selection": smallest J with the fewest column tiles; "tile efficiency":
+ * eff = floor(100 * ntiles / (nsm * ceil(ntiles / nsm))); "when not to use stream-K" and
+ * "stream-K": nwork = ntiles * ceil(k_iters), units = min(nsm * occupancy, nwork), and unit u
+ * owns the flattened (tile, k-iteration) range [u*W/units, (u+1)*W/units).)
+ * ------------------------------------------------------------------------------------------- */
+typedef struct {
+    int32_t regime;          /* 1 matrix-vector, 2 tiled */
+    int32_t tile_i;          /* rows per tile */
+    int32_t tile_j;          /* columns per tile */
+    int64_t ntiles;          /* output tiles */
+    int32_t efficiency_pct;  /* tile efficiency on nsm compute units */
+    int32_t stream_k;        /* 1 if the stream-K split is used */
+    int64_t k_iters;         /* K steps per tile (one super-block of 256 values per step) */
+    int64_t units;           /* stream-K work units launched (== ntiles without stream-K) */
+    int32_t fixup;           /* 1 if a fixup pass is needed */
+} qmm_plan;
+
+qmm_status qmm_plan_dense(int type, int64_t rows, int64_t k, int64_t n, int32_t nsm, qmm_plan *out);
+/* Tile efficiency percentage for ntiles tiles on nsm units. */
+int32_t qmm_tile_efficiency(int64_t ntiles, int32_t nsm);
+/* Column tile width minimising ceil(ncols / J) over the candidate widths (ties -> smaller J). */
+int32_t qmm_select_tile_j(int64_t ncols);
+/* Stream-K partition: first flattened work item of unit u, aligned down to a tile boundary's
+ * K step; returns the start index in [0, nwork]. */
+int64_t qmm_streamk_unit_start(int64_t u, int64_t units, int64_t ntiles, int64_t k_iters);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QMM_H */

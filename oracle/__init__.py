@@ -53,6 +53,8 @@ def lib():
         L.oracle_matmul_q8_1_at.restype = i32
         L.oracle_subdots.argtypes = [i32, vp, i64, i64, vp, i64, vp]
         L.oracle_subdots.restype = i32
+        L.oracle_subdots_q6_K_folded.argtypes = [vp, i64, i64, vp, i64, vp]
+        L.oracle_subdots_q6_K_folded.restype = i32
         L.oracle_matmul.argtypes = [i32, vp, i64, i64, vp, i64, vp]
         L.oracle_matmul.restype = i32
         L.oracle_matmul_id.argtypes = [i32, vp, i64, i64, i64, vp, i64, vp, i64, i64, vp, vp]
@@ -143,6 +145,17 @@ def subdots(qtype, w, rows, k, xq, n):
     if rc:
         raise ValueError("oracle_subdots: bad arguments")
     return D
+
+
+def subdots_q6_K_folded(w, rows, k, xq, n):
+    """Q6_K: sc0*D0 + sc1*D1 per 32-value block, int32 [n, rows, k/32]."""
+    w = _c(w, np.uint8)
+    xq = _c(xq, np.uint8)
+    F = np.zeros((n, rows, k // 32), dtype=np.int32)
+    rc = lib().oracle_subdots_q6_K_folded(_ptr(w), rows, k, _ptr(xq), n, _ptr(F))
+    if rc:
+        raise ValueError("oracle_subdots_q6_K_folded: bad arguments")
+    return F
 
 
 def matmul(qtype, w, rows, k, x):

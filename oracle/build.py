@@ -1,6 +1,6 @@
 """Build the CPU oracle (test infrastructure) into oracle/liboracle.so with gcc.
 
-Plain C99, -O2, no intrinsics, OpenMP over output elements.  Run as a script or via build().
+Plain C99, -O2, no intrinsics, no floating-point contraction, OpenMP over output elements.  Run as a script or via build().
 """
 import os
 import subprocess
@@ -11,7 +11,7 @@ LIB = os.path.join(HERE, "liboracle.so")
 
 
 def build(verbose: bool = False) -> str:
-    cmd = ["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-fopenmp", "-fPIC", "-shared",
+    cmd = ["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-Wall", "-Wextra", "-fopenmp", "-fPIC", "-shared",
            SRC, "-o", LIB + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd))

@@ -411,6 +411,32 @@ int oracle_subdots(int type, const uint8_t *w, int64_t rows, int64_t k, const ui
     return ORC_OK;
 }
 
+/* Q6_K only: the scale-folded integer per 32-value q8_1 block, sc[2b]*D[2b] + sc[2b+1]*D[2b+1]
+ * (the MMQ page's "Q6_K dot": two 16-value sub-blocks share one activation block).
+ * Output int32 [n][rows][k/32]. */
+int oracle_subdots_q6_K_folded(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n,
+                               int32_t *F) {
+    if (check_args(ORC_Q6_K, rows, k, n)) return ORC_ERR;
+    int64_t rb = oracle_row_bytes(ORC_Q6_K, k);
+    int64_t nb = k / 32;
+    int32_t *D = (int32_t *)malloc(sizeof(int32_t) * (size_t)(k / 16) + 4);
+    act_t a;
+    if (act_decode(&a, xq, n, k)) { act_free(&a); free(D); return ORC_ERR; }
+    for (int64_t c = 0; c < n; ++c)
+        for (int64_t r = 0; r < rows; ++r) {
+            const uint8_t *wrow = w + r * rb;
+            (void)dot_row_col(ORC_Q6_K, wrow, k, &a, c, D);
+            for (int64_t b = 0; b < nb; ++b) {
+                const int8_t *sc = (const int8_t *)(wrow + (b / 8) * 210 + 192);
+                int j = (int)(b % 8);
+                F[(c * rows + r) * nb + b] = sc[2 * j] * D[2 * b] + sc[2 * j + 1] * D[2 * b + 1];
+            }
+        }
+    act_free(&a);
+    free(D);
+    return ORC_OK;
+}
+
 /* fp32 activations -> q8_1 -> Y. */
 int oracle_matmul(int type, const uint8_t *w, int64_t rows, int64_t k, const float *x, int64_t n,
                   float *y) {

@@ -1,0 +1,146 @@
+"""C-ABI library loading, exported symbols and host-side planner logic (CPU only, no GPU calls).
+
+Planner numbers are the MMQ page's printed arithmetic: "tile efficiency" section (100 tiles on
+108 SMs -> 92 %, 120 tiles -> 55 %), "worked example: 8K prefill" (11008 rows x 8192 columns at
+I = J = 128 -> 86 x 64 = 5504 tiles; 64 experts, 8192 tokens, top-2 -> 256 tokens per expert),
+"J runtime selection" (fewest column tiles, ties to the smaller J) and "stream-K" (unit u owns
+[u*W/units, (u+1)*W/units) of the flattened (tile, K-step) items).
+"""
+import ctypes
+import subprocess
+
+import pytest
+
+import block_quantized_matmul_quantize_amd as qmm
+
+
+def test_library_exports_every_header_symbol():
+    declared = qmm.header_symbols()
+    assert len(declared) >= 15
+    out = subprocess.run(["nm", "-D", "--defined-only", qmm.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    missing = [s for s in declared if s not in exported]
+    assert not missing, missing
+    for s in declared:
+        assert hasattr(qmm.lib(), s)
+
+
+def test_version_string():
+    assert "gfx950" in qmm.version()
+
+
+@pytest.mark.parametrize("ntiles,nsm,pct", [(100, 108, 92), (120, 108, 55), (108, 108, 100), (216, 108, 100),
+                                            (217, 108, 66), (448, 256, 87), (128, 256, 50), (1, 256, 0)])
+def test_tile_efficiency(ntiles, nsm, pct):
+    assert qmm.tile_efficiency(ntiles, nsm) == pct
+
+
+def test_worked_example_tile_count():
+    # 11008 rows, 8192 columns, I = J = 128
+    assert qmm.select_tile_j(8192) == 128
+    rows_tiles = (11008 + 127) // 128
+    col_tiles = (8192 + qmm.select_tile_j(8192) - 1) // qmm.select_tile_j(8192)
+    assert (rows_tiles, col_tiles, rows_tiles * col_tiles) == (86, 64, 5504)
+    p = qmm.plan_dense(qmm.Q4_K, 11008, 4096, 8192, nsm=108)
+    assert p["regime"] == 2 and p["tile_j"] == 128 and p["ntiles"] == 5504
+    # 5504 tiles is about 25.5 waves on 108 units (two resident per unit here): efficiency well
+    # above the stream-K threshold, so one workgroup per tile
+    assert p["stream_k"] == 0 and p["units"] == 5504
+    # MoE average: 8192 tokens x top-2 over 64 experts
+    assert 8192 * 2 // 64 == 256
+
+
+@pytest.mark.parametrize("ncols,J", [(1, 32), (16, 32), (32, 32), (33, 64), (64, 64), (65, 128), (100, 128),
+                                     (128, 128), (129, 128), (512, 128), (2048, 128)])
+def test_select_tile_j(ncols, J):
+    assert qmm.select_tile_j(ncols) == J
+
+
+def test_plan_regimes():
+    assert qmm.plan_dense(qmm.Q4_K, 4096, 4096, 1)["regime"] == 1
+    assert qmm.plan_dense(qmm.Q4_K, 4096, 4096, 8)["regime"] == 1
+    assert qmm.plan_dense(qmm.Q4_K, 4096, 4096, 9)["regime"] == 2
+    p = qmm.plan_dense(qmm.Q4_K, 512, 1024, 16)
+    assert p["regime"] == 2 and p["tile_j"] == 32 and p["ntiles"] == 4
+    # prefill down projection: 32 x 4 tiles underfill 256 units -> stream-K over 256 units
+    p = qmm.plan_dense(qmm.Q6_K, 4096, 14336, 512)
+    assert p["ntiles"] == 128 and p["stream_k"] == 1 and p["units"] == 256 and p["k_iters"] == 56
+
+
+def test_overrides_and_restore():
+    try:
+        qmm.set_override(qmm.OVR_PATH, qmm.PATH_TILED)
+        assert qmm.plan_dense(qmm.Q4_K, 4096, 4096, 4)["regime"] == 2
+        qmm.set_override(qmm.OVR_STREAMK, 1)
+        assert qmm.plan_dense(qmm.Q6_K, 4096, 14336, 512)["stream_k"] == 0
+        qmm.set_override(qmm.OVR_TILE_J, 64)
+        assert qmm.plan_dense(qmm.Q4_K, 4096, 4096, 512)["tile_j"] == 64
+        with pytest.raises(qmm.QmmError):
+            qmm.set_override(qmm.OVR_TILE_J, 48)
+        with pytest.raises(qmm.QmmError):
+            qmm.set_override(99, 1)
+    finally:
+        for key in (qmm.OVR_PATH, qmm.OVR_STREAMK, qmm.OVR_TILE_J):
+            qmm.set_override(key, 0)
+
+
+@pytest.mark.parametrize("ntiles,k_iters,units", [(128, 56, 256), (448, 16, 256), (5, 7, 3), (1, 16, 16),
+                                                  (7, 1, 7), (9, 13, 256)])
+def test_streamk_partition_covers_every_item_once(ntiles, k_iters, units):
+    units = min(units, ntiles * k_iters)
+    W = ntiles * k_iters
+    starts = [qmm.streamk_unit_start(u, units, ntiles, k_iters) for u in range(units + 1)]
+    assert starts[0] == 0 and starts[-1] == W
+    assert all(b > a for a, b in zip(starts, starts[1:]))          # every unit has work
+    sizes = [b - a for a, b in zip(starts, starts[1:])]
+    assert max(sizes) - min(sizes) <= 1                              # balanced
+    covered = [0] * W
+    for a, b in zip(starts, starts[1:]):
+        for i in range(a, b):
+            covered[i] += 1
+    assert covered == [1] * W
+    # a unit touches at most two partial tiles (its first and its last)
+    for a, b in zip(starts, starts[1:]):
+        tiles = range(a // k_iters, (b - 1) // k_iters + 1)
+        partial = [t for t in tiles if max(a, t * k_iters) > t * k_iters or min(b, (t + 1) * k_iters) < (t + 1) * k_iters]
+        assert len(partial) <= 2
+        assert all(t in (tiles[0], tiles[-1]) for t in partial)
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def test_argument_validation_without_gpu():
+    L = qmm.lib()
+    null = ctypes.c_void_p(0)
+    # unsupported type
+    assert L.qmm_matmul(13, null, 16, 256, null, 1, null, null, 0, null) == -2
+    assert b"unsupported" in L.qmm_last_error()
+    # k not a multiple of the block size
+    assert L.qmm_matmul(qmm.Q4_K, null, 16, 100, null, 1, null, null, 0, null) == -3
+    assert L.qmm_matmul(qmm.Q8_0, null, 16, 48, null, 1, null, null, 0, null) == -3
+    assert L.qmm_quantize_q8_1(null, 1, 33, null, null) == -3
+    # negative sizes, null pointers
+    assert L.qmm_matmul(qmm.Q4_K, null, 0, 256, null, 1, null, null, 0, null) == -1
+    assert L.qmm_matmul(qmm.Q4_K, null, 16, 256, null, -1, null, null, 0, null) == -1
+    assert L.qmm_matmul(qmm.Q4_K, null, 16, 256, null, 1, null, null, 0, null) == -1
+    # n == 0 is a no-op
+    assert L.qmm_matmul(qmm.Q4_K, null, 16, 256, null, 0, null, null, 0, null) == 0
+    assert L.qmm_quantize_q8_1(null, 0, 32, null, null) == 0
+    # bad x_per_tok / top_k
+    assert L.qmm_matmul_id(qmm.Q4_K, null, 4, 16, 256, null, 3, null, 8, 2, null, null, 0, null) == -1
+    assert L.qmm_matmul_id(qmm.Q4_K, null, 4, 16, 256, null, 1, null, 8, 0, null, null, 0, null) == -1
+    # debug export: bad path
+    assert L.qmm_debug_subdots(qmm.Q4_K, null, 16, 256, null, 1, 3, null, null) == -1
+    assert L.qmm_debug_subdots(qmm.Q4_K, null, 16, 256, null, 9, 1, null, null) == -1
+
+
+def test_workspace_sizes_monotone():
+    a = qmm.matmul_q8_1_workspace(qmm.Q4_K, 4096, 4096, 1)
+    b = qmm.matmul_workspace(qmm.Q4_K, 4096, 4096, 1)
+    assert 0 < a < b
+    assert qmm.matmul_workspace(13, 16, 256, 1) == 0
+    assert qmm.matmul_id_workspace(qmm.Q4_K, 8, 14336, 4096, 512, 2, 1) > 512 * 128 * 36
+    assert qmm.matmul_id_workspace(qmm.Q4_K, 8, 14336, 4096, 512, 2, 3) == 0

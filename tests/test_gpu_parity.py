@@ -1,0 +1,324 @@
+"""GPU parity: the HIP kernels, called through the C ABI, against the CPU oracle on identical
+seeded inputs.
+
+Bars (both sides take every integer decision in the same precision):
+  * q8_1 bytes (codes, fp16 d and s): bit-exact.
+  * integer sub-block dots from the production kernels' own accumulators: bit-exact.
+  * fp32 outputs: |Y_gpu - Y_oracle| <= 1e-4 * ||w_r|| * ||x_n|| (gpu_util.assert_close).
+Full-size workloads are checked on sampled outputs the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_quantized_matmul_quantize_amd as qmm
+import oracle
+import synth
+from gpu_util import DEV, assert_close, col_norms, row_norms, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TYPES = [qmm.Q4_K, qmm.Q6_K, qmm.Q8_0]
+TNAME = {qmm.Q4_K: "q4_K", qmm.Q6_K: "q6_K", qmm.Q8_0: "q8_0"}
+
+
+def _reset_overrides():
+    for key in (qmm.OVR_PATH, qmm.OVR_STREAMK, qmm.OVR_TILE_J):
+        qmm.set_override(key, 0)
+
+
+@pytest.fixture(autouse=True)
+def _clean_overrides():
+    _reset_overrides()
+    yield
+    _reset_overrides()
+
+
+def _case(qtype, rows, k, n, seed):
+    g_w, g_x = synth.rngs(seed, 2)
+    return synth.gen_weights(qtype, rows, k, g_w), synth.gen_activations(n, k, g_x)
+
+
+# ---------------------------------------------------------------------------------------------
+# a1: q8_1 quantization, bit-exact
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("n,k", [(1, 32), (3, 256), (17, 4096), (64, 14336), (512, 4096)])
+def test_quantize_bit_exact_random(n, k):
+    rng = np.random.default_rng(100 + n)
+    x = (rng.standard_normal((n, k)) * rng.uniform(1e-3, 1e3, (n, 1))).astype(np.float32)
+    got = qmm.quantize_q8_1(to_dev(x)).cpu().numpy()
+    exp = oracle.quantize_q8_1(x)
+    assert np.array_equal(got, exp), np.argwhere(got != exp)[:5]
+
+
+def test_quantize_bit_exact_special_blocks():
+    rows = []
+    rows.append(np.zeros(32))                                         # zero block
+    t = np.zeros(32); t[:6] = [15.875, 0.3125, -0.3125, 0.0625, -0.0625, 1.5625]
+    rows.append(t)                                                    # exact rounding ties
+    s = np.zeros(32); s[7] = -3.0
+    rows.append(s)                                                    # single spike
+    rows.append(np.full(32, 0.7))                                     # constant
+    rows.append(np.linspace(-1e-38, 1e-38, 32))                       # fp32-subnormal scale
+    rows.append(np.linspace(-6e4, 6.5e4, 32))                         # d near fp16 range
+    rows.append(np.array([1e30] + [1.0] * 31))                        # d overflows fp16 -> inf
+    d = np.zeros(32); d[:2] = [127.031005859375, 100.51]
+    rows.append(d)                                                    # unrounded-divisor case
+    x = np.stack(rows).astype(np.float32)
+    got = qmm.quantize_q8_1(to_dev(x)).cpu().numpy()
+    exp = oracle.quantize_q8_1(x)
+    assert np.array_equal(got, exp), np.argwhere(got != exp)[:5]
+
+
+# ---------------------------------------------------------------------------------------------
+# a5: integer sub-block dots from the production kernels, bit-exact
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
+@pytest.mark.parametrize("n", [1, 5, 8])
+def test_subdots_matvec_bit_exact(qtype, n):
+    k = 96 if qtype == qmm.Q8_0 else 512          # Q8_0: a ragged last 256-value step
+    rows = 40                                      # not a multiple of the 16-row group
+    w, x = _case(qtype, rows, k, n, 200 + n)
+    xq = oracle.quantize_q8_1(x)
+    got = qmm.debug_subdots(to_dev(w), qtype, rows, k, to_dev(xq), n, qmm.PATH_MATVEC).cpu().numpy()
+    exp = oracle.subdots(qtype, w, rows, k, xq, n)
+    assert np.array_equal(got, exp), np.argwhere(got != exp)[:5]
+
+
+@pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
+@pytest.mark.parametrize("n", [3, 40])
+def test_subdots_tiled_bit_exact(qtype, n):
+    k = 352 if qtype == qmm.Q8_0 else 512
+    rows = 200                                     # not a multiple of the 128-row tile
+    w, x = _case(qtype, rows, k, n, 300 + n)
+    xq = oracle.quantize_q8_1(x)
+    got = qmm.debug_subdots(to_dev(w), qtype, rows, k, to_dev(xq), n, qmm.PATH_TILED).cpu().numpy()
+    if qtype == qmm.Q6_K:
+        exp = oracle.subdots_q6_K_folded(w, rows, k, xq, n)
+    else:
+        exp = oracle.subdots(qtype, w, rows, k, xq, n)
+    assert np.array_equal(got, exp), np.argwhere(got != exp)[:5]
+
+
+# ---------------------------------------------------------------------------------------------
+# fp32 outputs, full comparison at sizes the oracle finishes quickly
+# ---------------------------------------------------------------------------------------------
+def _full_check(qtype, rows, k, n, seed, what):
+    w, x = _case(qtype, rows, k, n, seed)
+    y = qmm.matmul(to_dev(w), qtype, rows, k, to_dev(x)).cpu().numpy()
+    xq = oracle.quantize_q8_1(x)
+    ref = oracle.matmul_q8_1(qtype, w, rows, k, xq, n)
+    return assert_close(y, ref, row_norms(qtype, w, rows, k), col_norms(xq, n, k), what=what)
+
+
+def test_dense_small_workload():
+    """Q4_K 512 x 1024 weight times 16 tokens (the small dense workload)."""
+    c = synth.DENSE_SMALL
+    w, x = synth.make_dense(c)
+    y = qmm.matmul(to_dev(w), c["qtype"], c["rows"], c["k"], to_dev(x)).cpu().numpy()
+    assert y.shape == (16, 512)
+    xq = oracle.quantize_q8_1(x)
+    ref = oracle.matmul_q8_1(c["qtype"], w, c["rows"], c["k"], xq, c["n"])
+    assert_close(y, ref, row_norms(c["qtype"], w, c["rows"], c["k"]), col_norms(xq, c["n"], c["k"]))
+
+
+@pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 8, 9, 16, 17, 33, 130])
+def test_dense_ragged(qtype, n):
+    k = 160 if qtype == qmm.Q8_0 else 768
+    _full_check(qtype, 300, k, n, 400 + n, f"{TNAME[qtype]} 300x{k} n={n}")
+
+
+@pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
+def test_dense_single_block_k(qtype):
+    k = 32 if qtype == qmm.Q8_0 else 256
+    for n in (1, 12):
+        _full_check(qtype, 129, k, n, 450 + n, f"{TNAME[qtype]} k={k} n={n}")
+
+
+@pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
+@pytest.mark.parametrize("n", [1, 2, 5, 8])
+def test_matvec_workload_full(qtype, n):
+    """The matrix-vector workload at full size: 4096 x 4096, every output compared."""
+    _full_check(qtype, 4096, 4096, n, 500 + n, f"{TNAME[qtype]} 4096^2 n={n}")
+
+
+def test_matmul_q8_1_entry_matches_matmul():
+    qtype, rows, k, n = qmm.Q4_K, 1000, 2048, 24
+    w, x = _case(qtype, rows, k, n, 600)
+    wd, xd = to_dev(w), to_dev(x)
+    y1 = qmm.matmul(wd, qtype, rows, k, xd)
+    xq = qmm.quantize_q8_1(xd)
+    y2 = qmm.matmul_q8_1(wd, qtype, rows, k, xq, n)
+    assert torch.equal(y1, y2)
+
+
+def test_empty_n_is_noop():
+    w, _ = _case(qmm.Q4_K, 64, 256, 1, 610)
+    out = torch.full((0, 64), 7.0, device=DEV)
+    y = qmm.matmul(to_dev(w), qmm.Q4_K, 64, 256, torch.empty((0, 256), device=DEV), out=out)
+    assert y.shape == (0, 64)
+
+
+def test_wrong_dtype_rejected():
+    w, x = _case(qmm.Q4_K, 64, 256, 2, 620)
+    with pytest.raises(TypeError):
+        qmm.matmul(to_dev(w), qmm.Q4_K, 64, 256, to_dev(x).half())
+    with pytest.raises(TypeError):
+        qmm.quantize_q8_1(to_dev(x).double())
+
+
+# ---------------------------------------------------------------------------------------------
+# Full-size prefill shapes: sampled outputs
+# ---------------------------------------------------------------------------------------------
+def _sampled_check(y, qtype, w, rows, k, xq, n, rng, count=1536, what=""):
+    cols = rng.integers(0, n, count)
+    rws = rng.integers(0, rows, count)
+    ref = oracle.matmul_q8_1_at(qtype, w, rows, k, xq, n, cols, rws)
+    got = y[cols, rws]
+    rb = oracle.row_bytes(qtype, k)
+    w2 = w.reshape(rows, rb)
+    wn = np.linalg.norm(oracle.dequantize(qtype, w2[rws], count, k), axis=1)
+    X, _, _ = oracle.dequantize_q8_1(xq[cols], count, k)
+    xn = np.linalg.norm(X, axis=1)
+    err = np.abs(got.astype(np.float64) - ref) / (wn * xn)
+    assert np.all(np.isfinite(got))
+    assert err.max() <= 1e-4, f"{what}: max normalised error {err.max():.3e}"
+    return float(err.max())
+
+
+@pytest.mark.parametrize("case", synth.PREFILL_CASES, ids=lambda c: c["name"])
+def test_prefill_workloads_sampled(case):
+    w, x = synth.make_dense(case)
+    qtype, rows, k, n = case["qtype"], case["rows"], case["k"], case["n"]
+    y = qmm.matmul(to_dev(w), qtype, rows, k, to_dev(x)).cpu().numpy()
+    xq = oracle.quantize_q8_1(x)
+    _sampled_check(y, qtype, w, rows, k, xq, n, np.random.default_rng(7), what=case["name"])
+
+
+def test_streamk_on_off_agree_and_rerun_is_bitwise():
+    qtype, rows, k, n = qmm.Q6_K, 1024, 14336, 160       # 8 x 2 tiles: stream-K splits every tile
+    w, x = _case(qtype, rows, k, n, 700)
+    wd, xd = to_dev(w), to_dev(x)
+    p = qmm.plan_dense(qtype, rows, k, n)
+    assert p["stream_k"] == 1 and p["units"] > p["ntiles"]
+    y_sk = qmm.matmul(wd, qtype, rows, k, xd)
+    y_sk2 = qmm.matmul(wd, qtype, rows, k, xd)
+    assert torch.equal(y_sk, y_sk2)
+    qmm.set_override(qmm.OVR_STREAMK, 1)
+    y_dp = qmm.matmul(wd, qtype, rows, k, xd)
+    xq = oracle.quantize_q8_1(x)
+    wn, xn = row_norms(qtype, w, rows, k), col_norms(xq, n, k)
+    assert_close(y_sk.cpu().numpy(), y_dp.cpu().numpy(), wn, xn, what="stream-K vs whole tiles")
+    ref = oracle.matmul_q8_1(qtype, w, rows, k, xq, n)
+    assert_close(y_sk.cpu().numpy(), ref, wn, xn, what="stream-K vs oracle")
+
+
+@pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
+def test_forced_regimes_agree(qtype):
+    rows, k, n = 520, 1024, 6
+    w, x = _case(qtype, rows, k, n, 800)
+    wd, xd = to_dev(w), to_dev(x)
+    qmm.set_override(qmm.OVR_PATH, qmm.PATH_MATVEC)
+    y_mv = qmm.matmul(wd, qtype, rows, k, xd).cpu().numpy()
+    qmm.set_override(qmm.OVR_PATH, qmm.PATH_TILED)
+    y_mq = qmm.matmul(wd, qtype, rows, k, xd).cpu().numpy()
+    xq = oracle.quantize_q8_1(x)
+    wn, xn = row_norms(qtype, w, rows, k), col_norms(xq, n, k)
+    ref = oracle.matmul_q8_1(qtype, w, rows, k, xq, n)
+    assert_close(y_mv, ref, wn, xn, what="matrix-vector")
+    assert_close(y_mq, ref, wn, xn, what="tiled")
+
+
+@pytest.mark.parametrize("J", [32, 64, 128])
+def test_tile_widths(J):
+    qtype, rows, k, n = qmm.Q4_K, 384, 1024, 100
+    qmm.set_override(qmm.OVR_TILE_J, J)
+    _full_check(qtype, rows, k, n, 900 + J, f"J={J}")
+
+
+# ---------------------------------------------------------------------------------------------
+# Expert-indexed product
+# ---------------------------------------------------------------------------------------------
+def _moe_ref_sampled(case, w, x, ids, y, rng, count=1024):
+    qtype, rows, k, n_exp = case["qtype"], case["rows"], case["k"], case["n_exp"]
+    n_tok, top_k = ids.shape
+    xpt = case["x_per_tok"]
+    rb = oracle.row_bytes(qtype, k)
+    wm = w.reshape(n_exp, rows * rb)
+    xq = oracle.quantize_q8_1(x)
+    pairs = rng.integers(0, n_tok * top_k, count)
+    rws = rng.integers(0, rows, count)
+    worst = 0.0
+    for e in np.unique(ids.reshape(-1)[pairs]):
+        sel = np.nonzero(ids.reshape(-1)[pairs] == e)[0]
+        p = pairs[sel]
+        arow = (p // top_k) * xpt + (p % top_k if xpt > 1 else 0)
+        ref = oracle.matmul_q8_1_at(qtype, wm[e], rows, k, xq, xq.shape[0], arow, rws[sel])
+        got = y.reshape(n_tok * top_k, rows)[p, rws[sel]]
+        wn = np.linalg.norm(oracle.dequantize(qtype, wm[e].reshape(rows, rb)[rws[sel]], len(sel), k), axis=1)
+        X, _, _ = oracle.dequantize_q8_1(xq[arow], len(sel), k)
+        err = np.abs(got.astype(np.float64) - ref) / (wn * np.linalg.norm(X, axis=1))
+        worst = max(worst, float(err.max()))
+    assert worst <= 1e-4, f"max normalised error {worst:.3e}"
+    return worst
+
+
+@pytest.mark.parametrize("case", synth.MOE_CASES, ids=lambda c: c["name"])
+def test_moe_workloads(case):
+    w, x, ids = synth.make_moe(case)
+    qtype, n_exp, rows, k = case["qtype"], case["n_exp"], case["rows"], case["k"]
+    y, ws = qmm.matmul_id(to_dev(w), qtype, n_exp, rows, k, to_dev(x), to_dev(ids), x_per_tok=case["x_per_tok"])
+    assert qmm.matmul_id_invalid_count(ws) == 0
+    y = y.cpu().numpy()
+    if case["n_tok"] <= 64:
+        ref, bad = oracle.matmul_id(qtype, w, n_exp, rows, k, x, case["x_per_tok"], ids)
+        assert bad == 0
+        xq = oracle.quantize_q8_1(x)
+        wn_all = row_norms(qtype, w, n_exp * rows, k).reshape(n_exp, rows)
+        xn_all = col_norms(xq, xq.shape[0], k)
+        n_tok, top_k = ids.shape
+        for t in range(n_tok):
+            for s in range(top_k):
+                a = t * case["x_per_tok"] + (s if case["x_per_tok"] > 1 else 0)
+                assert_close(y[t, s][None], ref[t, s][None], wn_all[ids[t, s]], xn_all[a:a + 1], what=f"pair {t},{s}")
+    else:
+        _moe_ref_sampled(case, w, x, ids, y, np.random.default_rng(11))
+
+
+def test_moe_invalid_ids_and_per_slot_activations():
+    rng = np.random.default_rng(1000)
+    n_exp, rows, k, n_tok, top_k = 6, 200, 512, 40, 3
+    qtype = qmm.Q4_K
+    w = synth.gen_weights(qtype, n_exp * rows, k, rng)
+    x = rng.standard_normal((n_tok * top_k, k)).astype(np.float32)
+    ids = np.stack([rng.choice(n_exp, top_k, replace=False) for _ in range(n_tok)]).astype(np.int32)
+    ids[0, 0] = n_exp
+    ids[5, 2] = -7
+    ids[39, 1] = 1000
+    out = torch.full((n_tok, top_k, rows), 12345.0, device=DEV)
+    y, ws = qmm.matmul_id(to_dev(w), qtype, n_exp, rows, k, to_dev(x), to_dev(ids), x_per_tok=top_k, out=out)
+    assert qmm.matmul_id_invalid_count(ws) == 3
+    y = y.cpu().numpy()
+    ref, bad = oracle.matmul_id(qtype, w, n_exp, rows, k, x, top_k, ids, fill=12345.0)
+    assert bad == 3
+    for t, s in [(0, 0), (5, 2), (39, 1)]:
+        assert np.all(y[t, s] == 12345.0)
+    xq = oracle.quantize_q8_1(x)
+    wn_all = row_norms(qtype, w, n_exp * rows, k).reshape(n_exp, rows)
+    xn_all = col_norms(xq, n_tok * top_k, k)
+    for t in range(n_tok):
+        for s in range(top_k):
+            e = ids[t, s]
+            if 0 <= e < n_exp:
+                a = t * top_k + s
+                assert_close(y[t, s][None], ref[t, s][None], wn_all[e], xn_all[a:a + 1], what=f"pair {t},{s}")
+
+
+def test_moe_rerun_is_bitwise():
+    case = synth.MOE_CASES[3]
+    w, x, ids = synth.make_moe(case)
+    args = (to_dev(w), case["qtype"], case["n_exp"], case["rows"], case["k"], to_dev(x), to_dev(ids))
+    y1, _ = qmm.matmul_id(*args, x_per_tok=case["x_per_tok"])
+    y2, _ = qmm.matmul_id(*args, x_per_tok=case["x_per_tok"])
+    assert torch.equal(y1, y2)

@@ -157,3 +157,20 @@ def test_matmul_id_is_loop_of_dense(x_per_tok):
             xr = x[t * x_per_tok + (s if x_per_tok > 1 else 0)][None, :]
             ref = oracle.matmul(oracle.Q6_K, wm[e], rows, k, xr)[0]
             assert np.array_equal(y[t, s], ref)
+
+
+def test_q6_K_folded_subdots_brute_force():
+    """sc[2b]*D[2b] + sc[2b+1]*D[2b+1] per q8_1 block, from the encoder's own scales and codes."""
+    rng = np.random.default_rng(70)
+    rows, k, n = 4, 512, 2
+    w, fields = _rows(oracle.Q6_K, rows, k, rng)
+    xq = oracle.quantize_q8_1(rng.standard_normal((n, k)).astype(np.float32))
+    F = oracle.subdots_q6_K_folded(w, rows, k, xq, n)
+    for c in range(n):
+        qa = q8_1_codes(xq[c])
+        for r in range(rows):
+            qw = weight_codes(oracle.Q6_K, fields[r])
+            sc = np.concatenate([f[1] for f in fields[r]])
+            for b in range(k // 32):
+                expect = sum(int(sc[v // 16]) * int(qw[v]) * int(qa[v]) for v in range(32 * b, 32 * b + 32))
+                assert F[c, r, b] == expect
