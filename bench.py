@@ -1,0 +1,289 @@
+"""Benchmark of the block-quantized matmul hot path on one MI355X.
+
+Headline workload (one "step"): the matrix-vector regime -- Q4_K, Q6_K and Q8_0 weights of
+4096 x 4096, each times N = 1, 2, 5 and 8 columns of N(0,1) fp32 activations, i.e. 12 calls of
+quantize-to-q8_1 + matmul.  value = effective GB/s of the whole step:
+    algorithmic bytes = weight blocks + q8_1 activation blocks + fp32 outputs, per call,
+divided by the step time.  Weights rotate over several distinct copies (> 512 MB in all) so the
+256 MB Infinity Cache cannot serve them; the cache-warm rate is reported separately.
+
+Also in the same JSON line:
+  roofline      for the dominant kernel (the matrix-vector kernel): per case, a HIP graph of
+                back-to-back launches over the weight rotations is replayed between two HIP
+                events on the launch stream; peak = 8 TB/s HBM.  traffic comes from the committed
+                rocprofv3 FETCH_SIZE/WRITE_SIZE summary when it matches the current sources.
+  cpu_baseline  the oracle (plain C, all host threads) on whole steps of the same workload.
+  secondary     int8 TOPS and % of the 5.0 POP/s int8 MFMA peak for the prefill and MoE shapes.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-secondary]
+"""
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+INT8_PEAK_TOPS = 5000.0
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "block_quantized_matmul_quantize_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algo_bytes(qtype, rows, k, n, block_bytes, block_values):
+    return rows * (k // block_values[qtype]) * block_bytes[qtype] + n * (k // 32) * 36 + n * rows * 4
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--rotations", type=int, default=4)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run one 256 MiB device copy (known bytes) to scale profiler counters")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the sharded "
+              "design is described in DESIGN.md, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_quantized_matmul_quantize_amd as qmm
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.calib_copy:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    BB, BV = qmm.BLOCK_BYTES, qmm.BLOCK_VALUES
+    cases = synth.MMVQ_CASES
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+
+    # ---------------------------------------------------------------- inputs (resident in HBM)
+    R = max(1, args.rotations)
+    W = [[None] * len(cases) for _ in range(R)]
+    X, XQ, Y = [], [], []
+    for i, c in enumerate(cases):
+        for r in range(R):
+            g = synth.rngs(1000 * r + i, 1)[0]
+            W[r][i] = torch.from_numpy(synth.gen_weights(c["qtype"], c["rows"], c["k"], g)).to(dev)
+        x = torch.from_numpy(synth.gen_activations(c["n"], c["k"], synth.rngs(7 + i, 1)[0])).to(dev)
+        X.append(x)
+        XQ.append(qmm.quantize_q8_1(x))
+        Y.append(torch.empty((c["n"], c["rows"]), dtype=torch.float32, device=dev))
+    WS = [qmm._workspace(qmm.matmul_workspace(c["qtype"], c["rows"], c["k"], c["n"]), dev) for c in cases]
+    step_bytes = sum(algo_bytes(c["qtype"], c["rows"], c["k"], c["n"], BB, BV) for c in cases)
+    weight_total = sum(w.numel() for row in W for w in row)
+    log(f"[bench] {len(cases)} calls per step, {step_bytes / 1e6:.1f} MB algorithmic per step, "
+        f"{R} weight rotations ({weight_total / 1e6:.0f} MB of weights)")
+
+    def step(r):
+        for i, c in enumerate(cases):
+            qmm.matmul(W[r][i], c["qtype"], c["rows"], c["k"], X[i], out=Y[i], ws=WS[i])
+
+    def capture(fn):
+        """One HIP graph of fn() (kernel launches only; every buffer is preallocated)."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g
+
+    # One graph per weight rotation: a step is 12 x (quantize + matmul) = 24 kernels, replayed
+    # without host launch overhead (the eager rate is reported as well).
+    graphs = [capture(lambda r=r: step(r)) for r in range(R)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+
+    def run(nsteps, fn):
+        torch.cuda.synchronize()
+        t0.record()
+        for s in range(nsteps):
+            fn(s)
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / nsteps
+
+    # ---------------------------------------------------------------- timed region
+    for s in range(args.warmup):
+        graphs[s % R].replay()
+    wall0 = time.perf_counter()
+    ms_per_step = run(args.steps, lambda s: graphs[s % R].replay())
+    wall = time.perf_counter() - wall0
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    log(f"[bench] timed {args.steps} steps (graph replay): {ms_per_step:.4f} ms/step, {value:.1f} GB/s "
+        f"(wall {wall:.2f} s)")
+    eager_ms = run(args.steps, lambda s: step(s % R))
+    eager_gbps = step_bytes / (eager_ms * 1e-3) / 1e9
+    log(f"[bench] eager launches: {eager_ms:.4f} ms/step, {eager_gbps:.1f} GB/s")
+    # cache-warm rate (same weights every step), reported separately
+    warm_ms = run(args.steps, lambda s: graphs[0].replay())
+    warm_gbps = step_bytes / (warm_ms * 1e-3) / 1e9
+
+    # ---------------------------------------------------------------- per-launch kernel timing
+    # The matrix-vector kernel alone: qmm_matmul_q8_1 on pre-quantized activations is exactly one
+    # launch of it.  Per case, a graph of back-to-back launches over the R weight rotations is
+    # replayed between two HIP events on the launch stream; duration = elapsed / launches.
+    per_case = []
+    tot_bytes = tot_us = 0.0
+    nrep = max(4, args.steps // 10)
+    for i, c in enumerate(cases):
+        g = capture(lambda i=i, c=c: [qmm.matmul_q8_1(W[r][i], c["qtype"], c["rows"], c["k"], XQ[i], c["n"],
+                                                      out=Y[i]) for _ in range(4) for r in range(R)])
+        g.replay()
+        us = run(nrep, lambda s: g.replay()) * 1e3 / (4 * R)
+        b = algo_bytes(c["qtype"], c["rows"], c["k"], c["n"], BB, BV)
+        per_case.append({"case": c["name"], "us": round(us, 3), "GBps": round(b / us / 1e3, 1),
+                         "frac": round(b / us / 1e3 / HBM_PEAK_GBPS, 4)})
+        tot_bytes += b
+        tot_us += us
+    achieved = tot_bytes / tot_us / 1e3
+    for pc in per_case:
+        log(f"[bench]   {pc['case']:24s} {pc['us']:8.3f} us  {pc['GBps']:8.1f} GB/s")
+
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", "mmvq_traffic.json")
+    if os.path.exists(tpath):
+        with open(tpath) as f:
+            tj = json.load(f)
+        if tj.get("source_hash") == source_hash():
+            traffic = tj.get("bytes_per_launch_avg")
+
+    roofline = {"kernel": "mmvq_kernel (matrix-vector, all 12 calls)", "bound": "hbm",
+                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "algorithmic_bytes_per_launch_avg": round(tot_bytes / len(cases), 1),
+                "avg_launch_us": round(tot_us / len(cases), 3), "per_case": per_case}
+
+    # ---------------------------------------------------------------- secondary: prefill / MoE
+    secondary = None
+    if not args.no_secondary:
+        secondary = run_secondary(torch, np, qmm, synth, dev, log)
+
+    # ---------------------------------------------------------------- CPU baseline (oracle)
+    cpu = None
+    if not args.no_cpu:
+        cpu = run_cpu_baseline(np, synth, cases, BB, BV, args.cpu_seconds, log)
+
+    out = {
+        "metric": "Q4_K x q8_1 qmatmul effective GB/s (N<=8) & int8 TOPS (prefill/MoE), % roofline",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int8 (q8_1 x Q4_K/Q6_K/Q8_0 codes), fp32 fixups", "data": "synthetic",
+        "config": {"workload": "matrix-vector regime: Q4_K, Q6_K, Q8_0 4096x4096 x N in {1,2,5,8} "
+                               "N(0,1) fp32 activations (12 quantize+matmul calls per step, replayed "
+                               "as one HIP graph per weight rotation)",
+                   "weight_rotations": R, "algorithmic_bytes_per_step": step_bytes},
+        "warm_cache_GBps": round(warm_gbps, 1),
+        "eager_launch_GBps": round(eager_gbps, 1),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def run_secondary(torch, np, qmm, synth, dev, log):
+    """Prefill and MoE shapes: int8 TOPS = 2*rows*k*columns / kernel-sequence time."""
+    res = []
+    reps, warm = 6, 2
+
+    def timed(fn):
+        for _ in range(warm):
+            fn(0)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for r in range(reps):
+            fn(r)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e3   # us
+
+    for c in synth.PREFILL_CASES:
+        w, x = synth.make_dense(c)
+        nrot = max(1, int(np.ceil(512e6 / w.nbytes)))
+        ws_ = [torch.from_numpy(w).to(dev)] + [torch.roll(torch.from_numpy(w).to(dev), 1, 0) for _ in range(min(nrot, 8) - 1)]
+        xd = torch.from_numpy(x).to(dev)
+        y = torch.empty((c["n"], c["rows"]), dtype=torch.float32, device=dev)
+        wsb = qmm._workspace(qmm.matmul_workspace(c["qtype"], c["rows"], c["k"], c["n"]), dev)
+        us = timed(lambda r: qmm.matmul(ws_[r % len(ws_)], c["qtype"], c["rows"], c["k"], xd, out=y, ws=wsb))
+        ops = 2.0 * c["rows"] * c["k"] * c["n"]
+        tops = ops / us / 1e6
+        res.append({"case": c["name"], "us": round(us, 1), "TOPS": round(tops, 1),
+                    "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4)})
+        log(f"[bench] {c['name']:36s} {us:9.1f} us {tops:8.1f} TOPS")
+        del ws_
+    for c in synth.MOE_CASES[:3]:
+        w, x, ids = synth.make_moe(c)
+        wd = torch.from_numpy(w).to(dev)
+        xd, idd = torch.from_numpy(x).to(dev), torch.from_numpy(ids).to(dev)
+        out = torch.empty((c["n_tok"], c["top_k"], c["rows"]), dtype=torch.float32, device=dev)
+        wsb = qmm._workspace(qmm.matmul_id_workspace(c["qtype"], c["n_exp"], c["rows"], c["k"], c["n_tok"],
+                                                     c["top_k"], c["x_per_tok"]), dev)
+        us = timed(lambda r: qmm.matmul_id(wd, c["qtype"], c["n_exp"], c["rows"], c["k"], xd, idd,
+                                           x_per_tok=c["x_per_tok"], out=out, ws=wsb))
+        ops = 2.0 * c["rows"] * c["k"] * c["n_tok"] * c["top_k"]
+        tops = ops / us / 1e6
+        res.append({"case": c["name"], "us": round(us, 1), "TOPS": round(tops, 1),
+                    "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4), "cache": "weights resident (warm)"})
+        log(f"[bench] {c['name']:36s} {us:9.1f} us {tops:8.1f} TOPS")
+        del wd
+    return res
+
+
+def run_cpu_baseline(np, synth, cases, BB, BV, seconds, log):
+    import oracle
+    data = []
+    for i, c in enumerate(cases):
+        g = synth.rngs(1000 * 0 + i, 1)[0]
+        w = synth.gen_weights(c["qtype"], c["rows"], c["k"], g)
+        x = synth.gen_activations(c["n"], c["k"], synth.rngs(7 + i, 1)[0])
+        data.append((c, w, x))
+    step_bytes = sum(algo_bytes(c["qtype"], c["rows"], c["k"], c["n"], BB, BV) for c in cases)
+    t0 = time.perf_counter()
+    nsteps = 0
+    while True:
+        for c, w, x in data:
+            oracle.matmul(c["qtype"], w, c["rows"], c["k"], x)
+        nsteps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    gbps = step_bytes * nsteps / dt / 1e9
+    log(f"[bench] cpu oracle: {nsteps} steps in {dt:.2f} s -> {gbps:.3f} GB/s on {cores} threads")
+    return {"value": round(gbps, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{nsteps} whole steps of the same 12-call workload ({dt:.1f} s), weights from rotation 0",
+            "ms_per_step": round(dt / nsteps * 1e3, 2)}
+
+
+if __name__ == "__main__":
+    main()

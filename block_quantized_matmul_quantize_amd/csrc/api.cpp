@@ -183,7 +183,7 @@ qmm_status qmm_plan_dense(int type, int64_t rows, int64_t k, int64_t n, int32_t 
 namespace {
 
 struct DenseWs {
-    size_t xq_off, tab_off, part_off, total;
+    size_t xq_off, part_off, total;
 };
 
 DenseWs dense_layout(int type, int64_t rows, int64_t k, int64_t n, bool with_xq) {
@@ -192,8 +192,6 @@ DenseWs dense_layout(int type, int64_t rows, int64_t k, int64_t n, bool with_xq)
     size_t off = 0;
     L.xq_off = off;
     if (with_xq) off = align_up(off + (size_t)(n * nb * 36), 256);
-    L.tab_off = off;
-    off = align_up(off + (size_t)(nb * std::max<int64_t>(n, 1) * 8), 256);
     L.part_off = off;
     if (n > 8 || g_ovr_path.load() == 2) {
         // stream-K partial slots: at most (compute units x 2 resident) units x 2 slots x 128 x 128
@@ -208,13 +206,7 @@ DenseWs dense_layout(int type, int64_t rows, int64_t k, int64_t n, bool with_xq)
 
 qmm_status run_dense(int type, const void *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y,
                      uint8_t *ws, const DenseWs &L, int32_t *dbg, int dbg_path, hipStream_t s) {
-    const int64_t nb = k / 32;
-    float2 *tab = (float2 *)(ws + L.tab_off);
     hipError_t e;
-    if (!dbg) {
-        e = qmm::launch_q8_1_scale_table(xq, n, k, tab, n, s);
-        if (e != hipSuccess) return hip_fail(e, "scale table launch");
-    }
     qmm_plan p{};
     qmm_status st;
     if (dbg) {
@@ -229,9 +221,8 @@ qmm_status run_dense(int type, const void *w, int64_t rows, int64_t k, const uin
         st = qmm_plan_dense(type, rows, k, n, device_cus(), &p);
     }
     if (st) return st;
-    (void)nb;
     if (p.regime == 1) {
-        e = qmm::launch_mmvq(type, (const uint8_t *)w, rows, k, xq, tab, n, n, y, dbg, nullptr, 0, s);
+        e = qmm::launch_mmvq(type, (const uint8_t *)w, rows, k, xq, n, y, dbg, nullptr, 0, s);
         if (e != hipSuccess) return hip_fail(e, "matrix-vector kernel launch");
         return QMM_OK;
     }
@@ -245,7 +236,7 @@ qmm_status run_dense(int type, const void *w, int64_t rows, int64_t k, const uin
     ml.partials = (float *)(ws + L.part_off);
     if (ml.stream_k && (size_t)(L.part_off + (size_t)ml.units * 2 * kTI * p.tile_j * 4) > L.total)
         return fail(QMM_ERR_WORKSPACE, "internal: stream-K partials exceed the workspace");
-    e = qmm::launch_mmq(type, (const uint8_t *)w, rows, k, xq, tab, n, n, y, dbg, ml, s);
+    e = qmm::launch_mmq(type, (const uint8_t *)w, rows, k, xq, n, y, dbg, ml, s);
     if (e != hipSuccess) return hip_fail(e, "tiled kernel launch");
     return QMM_OK;
 }
@@ -268,7 +259,7 @@ qmm_status qmm_quantize_q8_1(const float *x, int64_t n_rows, int64_t k, void *y,
     if (!x || !y) return fail(QMM_ERR_ARG, "null x or y");
     if (((uintptr_t)x) & 15) return fail(QMM_ERR_ARG, "x must be 16-byte aligned");
     if (((uintptr_t)y) & 3) return fail(QMM_ERR_ARG, "y must be 4-byte aligned");
-    hipError_t e = qmm::launch_quantize_q8_1(x, n_rows, k, (uint8_t *)y, nullptr, 0, (hipStream_t)stream);
+    hipError_t e = qmm::launch_quantize_q8_1(x, n_rows, k, (uint8_t *)y, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "quantize launch");
     return QMM_OK;
 }
@@ -291,12 +282,12 @@ qmm_status qmm_matmul(int type, const void *w, int64_t rows, int64_t k, const fl
     if (n == 0) return QMM_OK;
     if (((uintptr_t)x) & 15) return fail(QMM_ERR_ARG, "x must be 16-byte aligned");
     const DenseWs L = dense_layout(type, rows, k, n, true);
-    if (!ws || ws_bytes < L.total)
+    if (L.total > 0 && (!ws || ws_bytes < L.total))
         return fail(QMM_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", ws_bytes, L.total);
     if (((uintptr_t)ws) & 255) return fail(QMM_ERR_ARG, "workspace must be 256-byte aligned");
     hipStream_t s = (hipStream_t)stream;
     uint8_t *wsb = (uint8_t *)ws;
-    hipError_t e = qmm::launch_quantize_q8_1(x, n, k, wsb + L.xq_off, nullptr, 0, s);
+    hipError_t e = qmm::launch_quantize_q8_1(x, n, k, wsb + L.xq_off, s);
     if (e != hipSuccess) return hip_fail(e, "quantize launch");
     return run_dense(type, w, rows, k, wsb + L.xq_off, n, y, wsb, L, nullptr, 0, s);
 }
@@ -309,7 +300,7 @@ qmm_status qmm_matmul_q8_1(int type, const void *w, int64_t rows, int64_t k, con
     if (n == 0) return QMM_OK;
     if (((uintptr_t)xq) & 3) return fail(QMM_ERR_ARG, "xq must be 4-byte aligned");
     const DenseWs L = dense_layout(type, rows, k, n, false);
-    if (!ws || ws_bytes < L.total)
+    if (L.total > 0 && (!ws || ws_bytes < L.total))
         return fail(QMM_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", ws_bytes, L.total);
     if (((uintptr_t)ws) & 255) return fail(QMM_ERR_ARG, "workspace must be 256-byte aligned");
     return run_dense(type, w, rows, k, (const uint8_t *)xq, n, y, (uint8_t *)ws, L, nullptr, 0, (hipStream_t)stream);
@@ -333,7 +324,7 @@ qmm_status qmm_debug_subdots(int type, const void *w, int64_t rows, int64_t k, c
 namespace {
 
 struct IdWs {
-    size_t invalid_off, xq_off, tab_off, sorted_off, bounds_off, tstart_off, small_off, total;
+    size_t invalid_off, xq_off, sorted_off, bounds_off, tstart_off, small_off, total;
 };
 
 IdWs id_layout(int64_t n_exp, int64_t k, int64_t n_tok, int64_t top_k, int64_t x_per_tok) {
@@ -344,7 +335,6 @@ IdWs id_layout(int64_t n_exp, int64_t k, int64_t n_tok, int64_t top_k, int64_t x
     size_t off = 0;
     L.invalid_off = off; off = align_up(off + 4, 256);   // first, so the count is found from ws alone
     L.xq_off = off; off = align_up(off + (size_t)(nx * nb * 36), 256);
-    L.tab_off = off; off = align_up(off + (size_t)(nb * std::max<int64_t>(nx, 1) * 8), 256);
     L.sorted_off = off; off = align_up(off + (size_t)(std::max<int64_t>(pairs, 1) * 4), 256);
     L.bounds_off = off; off = align_up(off + (size_t)((n_exp + 1) * 4), 256);
     L.tstart_off = off; off = align_up(off + (size_t)((n_exp + 1) * 4), 256);
@@ -380,7 +370,7 @@ qmm_status qmm_matmul_id(int type, const void *w, int64_t n_exp, int64_t rows, i
     if (x_per_tok != 1 && x_per_tok != top_k) return fail(QMM_ERR_ARG, "x_per_tok must be 1 or top_k");
     if (n_tok * top_k > (1ll << 30)) return fail(QMM_ERR_SHAPE, "too many (token, slot) pairs");
     const IdWs L = id_layout(n_exp, k, n_tok, top_k, x_per_tok);
-    if (!ws || ws_bytes < L.total)
+    if (L.total > 0 && (!ws || ws_bytes < L.total))
         return fail(QMM_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", ws_bytes, L.total);
     if (((uintptr_t)ws) & 255) return fail(QMM_ERR_ARG, "workspace must be 256-byte aligned");
     hipStream_t s = (hipStream_t)stream;
@@ -398,8 +388,7 @@ qmm_status qmm_matmul_id(int type, const void *w, int64_t n_exp, int64_t rows, i
     const int64_t nx = n_tok * x_per_tok;
     const int64_t pairs = n_tok * top_k;
     uint8_t *xq = wsb + L.xq_off;
-    float2 *tab = (float2 *)(wsb + L.tab_off);
-    hipError_t e = qmm::launch_quantize_q8_1(x, nx, k, xq, tab, nx, s);
+    hipError_t e = qmm::launch_quantize_q8_1(x, nx, k, xq, s);
     if (e != hipSuccess) return hip_fail(e, "quantize launch");
     const int tile_j = id_tile_j(pairs, n_exp);
     qmm::ColMap cm{};
@@ -417,13 +406,13 @@ qmm_status qmm_matmul_id(int type, const void *w, int64_t n_exp, int64_t rows, i
     if (e != hipSuccess) return hip_fail(e, "grouping launch");
     // experts with <= 8 columns: matrix-vector kernel, one workgroup row per listed expert
     if (k <= kMvMaxK) {
-        e = qmm::launch_mmvq(type, (const uint8_t *)w, rows, k, xq, tab, nx, 0, y, nullptr, &cm, n_exp, s);
+        e = qmm::launch_mmvq(type, (const uint8_t *)w, rows, k, xq, 0, y, nullptr, &cm, n_exp, s);
         if (e != hipSuccess) return hip_fail(e, "expert matrix-vector launch");
     }
     // the rest: tiled kernel over the device-built column-tile list
     const int64_t mmq_experts = std::min<int64_t>(n_exp, pairs / (small_max + 1));
     const int64_t max_ct = (pairs + tile_j - 1) / tile_j + mmq_experts;
-    e = qmm::launch_mmq_id(type, (const uint8_t *)w, rows, k, xq, tab, nx, y, cm, tile_j, max_ct, s);
+    e = qmm::launch_mmq_id(type, (const uint8_t *)w, rows, k, xq, y, cm, tile_j, max_ct, s);
     if (e != hipSuccess) return hip_fail(e, "expert tiled launch");
     return QMM_OK;
 }

@@ -5,10 +5,7 @@
 
 namespace qmm {
 
-hipError_t launch_quantize_q8_1(const float *x, int64_t n_rows, int64_t k, uint8_t *y, float2 *tab,
-                                int64_t tab_ld, hipStream_t s);
-hipError_t launch_q8_1_scale_table(const uint8_t *xq, int64_t n_rows, int64_t k, float2 *tab, int64_t tab_ld,
-                                   hipStream_t s);
+hipError_t launch_quantize_q8_1(const float *x, int64_t n_rows, int64_t k, uint8_t *y, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t s);
 
 // Column map for the matrix-vector and tiled kernels.  Dense: column j reads activation row j
@@ -27,9 +24,8 @@ struct ColMap {
 };
 
 // Matrix-vector kernel: n <= 8 columns (dense) or the small experts (expert mode, grid.y = n_exp).
-hipError_t launch_mmvq(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq,
-                       const float2 *tab, int64_t tab_ld, int64_t n, float *y, int32_t *dbg,
-                       const ColMap *cm, int64_t n_exp, hipStream_t s);
+hipError_t launch_mmvq(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n,
+                       float *y, int32_t *dbg, const ColMap *cm, int64_t n_exp, hipStream_t s);
 
 // Tiled int8-MFMA kernel plan.
 struct MmqLaunch {
@@ -41,13 +37,11 @@ struct MmqLaunch {
     bool stream_k;
     float *partials;     // [units][2][128*tile_j] when stream_k
 };
-hipError_t launch_mmq(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq,
-                      const float2 *tab, int64_t tab_ld, int64_t n, float *y, int32_t *dbg,
-                      const MmqLaunch &plan, hipStream_t s);
+hipError_t launch_mmq(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n,
+                      float *y, int32_t *dbg, const MmqLaunch &plan, hipStream_t s);
 // Expert mode: grid over (row tiles, max column tiles); experts with > 8 columns.
-hipError_t launch_mmq_id(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq,
-                         const float2 *tab, int64_t tab_ld, float *y, const ColMap &cm,
-                         int tile_j, int64_t max_col_tiles, hipStream_t s);
+hipError_t launch_mmq_id(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, float *y,
+                         const ColMap &cm, int tile_j, int64_t max_col_tiles, hipStream_t s);
 
 // Expert grouping: counts, bounds, stable sorted pair list, column-tile prefix, small-expert list.
 hipError_t launch_moe_group(const int32_t *ids, int64_t pairs, int32_t n_exp, int32_t tile_j,

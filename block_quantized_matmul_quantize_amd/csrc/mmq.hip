@@ -175,9 +175,8 @@ __device__ __forceinline__ void stage_weights_q6_k(uint8_t *sm, const uint8_t *w
 // acol[] holds this thread's activation rows (or -1 for columns beyond the tile's range).
 // ---------------------------------------------------------------------------------------------
 template <int T, int J>
-__device__ __forceinline__ void stage_acts(uint8_t *sm, const uint8_t *xq, const float2 *tab, int64_t tab_ld,
-                                           int64_t nb32, int64_t kb, const int64_t (&acol)[J / 16],
-                                           const int64_t (&tcol)[J / 32]) {
+__device__ __forceinline__ void stage_acts(uint8_t *sm, const uint8_t *xq, int64_t nb32, int64_t kb,
+                                           const int64_t (&acol)[J / 16], const int64_t (&tcol)[J / 32]) {
     const int tid = threadIdx.x;
     int8_t *sA = (int8_t *)(sm + Smem<T, J>::A_OFF);
     float2 *sX = (float2 *)(sm + Smem<T, J>::X_OFF);
@@ -196,7 +195,10 @@ __device__ __forceinline__ void stage_acts(uint8_t *sm, const uint8_t *xq, const
         const int j = i / J, c = i % J;
         const int64_t b = kb * 8 + j;
         float2 v = make_float2(0.f, 0.f);
-        if (tcol[it] >= 0 && b < nb32) v = tab[b * tab_ld + tcol[it]];
+        if (tcol[it] >= 0 && b < nb32) {
+            const uint32_t ds = *(const uint32_t *)(xq + (tcol[it] * nb32 + b) * kQ8_1Bytes);
+            v = make_float2(h2f((uint16_t)(ds & 0xFFFF)), h2f((uint16_t)(ds >> 16)));
+        }
         sX[j * J + c] = v;
     }
 }
@@ -276,13 +278,12 @@ __device__ __forceinline__ void tile_step(const uint8_t *sm, float (&acc)[J / 32
 template <int T, int J>
 __device__ __forceinline__ void stage_step(uint8_t *sm, const uint8_t *wbase, int64_t row_bytes, int64_t r0,
                                            int64_t rows, int64_t kb, int64_t nb32, const uint8_t *xq,
-                                           const float2 *tab, int64_t tab_ld, const int64_t (&acol)[J / 16],
-                                           const int64_t (&tcol)[J / 32]) {
+                                           const int64_t (&acol)[J / 16], const int64_t (&tcol)[J / 32]) {
     if constexpr (T == kQ4_K) stage_weights_q4_k(sm, wbase, row_bytes, r0, rows, kb);
     else if constexpr (T == kQ8_0) stage_weights_q8_0<J>(sm, wbase, row_bytes, r0, rows, kb, nb32);
     else stage_weights_q6_k(sm, wbase, row_bytes, r0, rows, kb);
     stage_weight_scales<T, J>(sm, wbase, row_bytes, r0, rows, kb, nb32);
-    stage_acts<T, J>(sm, xq, tab, tab_ld, nb32, kb, acol, tcol);
+    stage_acts<T, J>(sm, xq, nb32, kb, acol, tcol);
 }
 
 // Accumulator (lane, e) -> tile coordinates.
@@ -296,8 +297,7 @@ __device__ __forceinline__ int acc_row(int e) {
 // ---------------------------------------------------------------------------------------------
 template <int T, int J, bool DBG>
 __global__ __launch_bounds__(256) void mmq_kernel(const uint8_t *__restrict__ w, int64_t rows, int64_t k,
-                                                  const uint8_t *__restrict__ xq, const float2 *__restrict__ tab,
-                                                  int64_t tab_ld, int64_t n, float *__restrict__ y,
+                                                  const uint8_t *__restrict__ xq, int64_t n, float *__restrict__ y,
                                                   int32_t *__restrict__ dbg, MmqArgs args) {
     extern __shared__ __align__(16) uint8_t sm[];
     const int64_t nb32 = k / 32;
@@ -335,7 +335,7 @@ __global__ __launch_bounds__(256) void mmq_kernel(const uint8_t *__restrict__ w,
 
         for (int64_t kb = kb0; kb < kb1; ++kb) {
             __syncthreads();
-            stage_step<T, J>(sm, w, row_bytes, r0, rows, kb, nb32, xq, tab, tab_ld, acol, tcol);
+            stage_step<T, J>(sm, w, row_bytes, r0, rows, kb, nb32, xq, acol, tcol);
             __syncthreads();
             tile_step<T, J, DBG>(sm, acc, kb, nb32, dbg, rows, n, r0, c0);
         }
@@ -404,9 +404,8 @@ __global__ __launch_bounds__(256) void streamk_fixup_kernel(float *__restrict__ 
 // ---------------------------------------------------------------------------------------------
 template <int T, int J>
 __global__ __launch_bounds__(256) void mmq_id_kernel(const uint8_t *__restrict__ w, int64_t rows, int64_t k,
-                                                     const uint8_t *__restrict__ xq,
-                                                     const float2 *__restrict__ tab, int64_t tab_ld,
-                                                     float *__restrict__ y, ColMap cm, int32_t n_exp) {
+                                                     const uint8_t *__restrict__ xq, float *__restrict__ y,
+                                                     ColMap cm, int32_t n_exp) {
     extern __shared__ __align__(16) uint8_t sm[];
     const int64_t ct = blockIdx.y;
     if (ct >= cm.tile_start[n_exp]) return;
@@ -452,7 +451,7 @@ __global__ __launch_bounds__(256) void mmq_id_kernel(const uint8_t *__restrict__
     const int64_t k_iters = (k + kSuper - 1) / kSuper;
     for (int64_t kb = 0; kb < k_iters; ++kb) {
         __syncthreads();
-        stage_step<T, J>(sm, wbase, row_bytes, r0, rows, kb, nb32, xq, tab, tab_ld, acol, tcol);
+        stage_step<T, J>(sm, wbase, row_bytes, r0, rows, kb, nb32, xq, acol, tcol);
         __syncthreads();
         tile_step<T, J, false>(sm, acc, kb, nb32, nullptr, rows, cnt, r0, c0);
     }
@@ -473,9 +472,8 @@ __global__ __launch_bounds__(256) void mmq_id_kernel(const uint8_t *__restrict__
 // Launchers
 // ---------------------------------------------------------------------------------------------
 template <int T, int J, bool DBG>
-static hipError_t launch_mmq_t(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, const float2 *tab,
-                               int64_t tab_ld, int64_t n, float *y, int32_t *dbg, const MmqLaunch &p,
-                               hipStream_t s) {
+static hipError_t launch_mmq_t(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y,
+                               int32_t *dbg, const MmqLaunch &p, hipStream_t s) {
     MmqArgs a{p.ntiles, p.n_ct, p.k_iters, p.units, p.partials, p.stream_k ? 1 : 0};
     constexpr int smem = Smem<T, J>::BYTES;
     auto kern = mmq_kernel<T, J, DBG>;
@@ -485,7 +483,7 @@ static hipError_t launch_mmq_t(const uint8_t *w, int64_t rows, int64_t k, const 
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)p.units), dim3(256), smem, s, w, rows, k, xq, tab, tab_ld, n, y, dbg, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)p.units), dim3(256), smem, s, w, rows, k, xq, n, y, dbg, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || DBG || !p.stream_k) return e;
     hipLaunchKernelGGL(streamk_fixup_kernel<J>, dim3((unsigned)p.ntiles), dim3(256), 0, s, y, rows, n, a);
@@ -493,21 +491,20 @@ static hipError_t launch_mmq_t(const uint8_t *w, int64_t rows, int64_t k, const 
 }
 
 template <int T, bool DBG>
-static hipError_t launch_mmq_j(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, const float2 *tab,
-                               int64_t tab_ld, int64_t n, float *y, int32_t *dbg, const MmqLaunch &p,
-                               hipStream_t s) {
-    if (p.tile_j == 32) return launch_mmq_t<T, 32, DBG>(w, rows, k, xq, tab, tab_ld, n, y, dbg, p, s);
-    if (p.tile_j == 64) return launch_mmq_t<T, 64, DBG>(w, rows, k, xq, tab, tab_ld, n, y, dbg, p, s);
-    if (p.tile_j == 128) return launch_mmq_t<T, 128, DBG>(w, rows, k, xq, tab, tab_ld, n, y, dbg, p, s);
+static hipError_t launch_mmq_j(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y,
+                               int32_t *dbg, const MmqLaunch &p, hipStream_t s) {
+    if (p.tile_j == 32) return launch_mmq_t<T, 32, DBG>(w, rows, k, xq, n, y, dbg, p, s);
+    if (p.tile_j == 64) return launch_mmq_t<T, 64, DBG>(w, rows, k, xq, n, y, dbg, p, s);
+    if (p.tile_j == 128) return launch_mmq_t<T, 128, DBG>(w, rows, k, xq, n, y, dbg, p, s);
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_mmq(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, const float2 *tab,
-                      int64_t tab_ld, int64_t n, float *y, int32_t *dbg, const MmqLaunch &p, hipStream_t s) {
+hipError_t launch_mmq(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y,
+                      int32_t *dbg, const MmqLaunch &p, hipStream_t s) {
     const bool d = dbg != nullptr;
 #define QMM_MQ(TT)                                                                                    \
-    if (type == TT) return d ? launch_mmq_j<TT, true>(w, rows, k, xq, tab, tab_ld, n, y, dbg, p, s)    \
-                             : launch_mmq_j<TT, false>(w, rows, k, xq, tab, tab_ld, n, y, dbg, p, s);
+    if (type == TT) return d ? launch_mmq_j<TT, true>(w, rows, k, xq, n, y, dbg, p, s)    \
+                             : launch_mmq_j<TT, false>(w, rows, k, xq, n, y, dbg, p, s);
     QMM_MQ(kQ4_K)
     QMM_MQ(kQ6_K)
     QMM_MQ(kQ8_0)
@@ -516,9 +513,8 @@ hipError_t launch_mmq(int type, const uint8_t *w, int64_t rows, int64_t k, const
 }
 
 template <int T, int J>
-static hipError_t launch_mmq_id_t(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, const float2 *tab,
-                                  int64_t tab_ld, float *y, const ColMap &cm, int32_t n_exp, int64_t max_ct,
-                                  hipStream_t s) {
+static hipError_t launch_mmq_id_t(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, float *y,
+                                  const ColMap &cm, int32_t n_exp, int64_t max_ct, hipStream_t s) {
     constexpr int smem = Smem<T, J>::BYTES;
     auto kern = mmq_id_kernel<T, J>;
     static bool attr_set = false;
@@ -529,18 +525,17 @@ static hipError_t launch_mmq_id_t(const uint8_t *w, int64_t rows, int64_t k, con
     }
     if (max_ct <= 0) return hipSuccess;
     dim3 grid((unsigned)((rows + kTI - 1) / kTI), (unsigned)max_ct);
-    hipLaunchKernelGGL(kern, grid, dim3(256), smem, s, w, rows, k, xq, tab, tab_ld, y, cm, n_exp);
+    hipLaunchKernelGGL(kern, grid, dim3(256), smem, s, w, rows, k, xq, y, cm, n_exp);
     return hipGetLastError();
 }
 
-hipError_t launch_mmq_id(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, const float2 *tab,
-                         int64_t tab_ld, float *y, const ColMap &cm, int tile_j, int64_t max_col_tiles,
-                         hipStream_t s) {
+hipError_t launch_mmq_id(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, float *y,
+                         const ColMap &cm, int tile_j, int64_t max_col_tiles, hipStream_t s) {
 #define QMM_MQI(TT)                                                                                   \
     if (type == TT) {                                                                                 \
-        if (tile_j == 32) return launch_mmq_id_t<TT, 32>(w, rows, k, xq, tab, tab_ld, y, cm, cm.n_exp, max_col_tiles, s); \
-        if (tile_j == 64) return launch_mmq_id_t<TT, 64>(w, rows, k, xq, tab, tab_ld, y, cm, cm.n_exp, max_col_tiles, s); \
-        if (tile_j == 128) return launch_mmq_id_t<TT, 128>(w, rows, k, xq, tab, tab_ld, y, cm, cm.n_exp, max_col_tiles, s); \
+        if (tile_j == 32) return launch_mmq_id_t<TT, 32>(w, rows, k, xq, y, cm, cm.n_exp, max_col_tiles, s); \
+        if (tile_j == 64) return launch_mmq_id_t<TT, 64>(w, rows, k, xq, y, cm, cm.n_exp, max_col_tiles, s); \
+        if (tile_j == 128) return launch_mmq_id_t<TT, 128>(w, rows, k, xq, y, cm, cm.n_exp, max_col_tiles, s); \
     }
     QMM_MQI(kQ4_K)
     QMM_MQI(kQ6_K)

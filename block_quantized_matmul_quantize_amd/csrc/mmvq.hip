@@ -26,7 +26,8 @@
 namespace qmm {
 
 constexpr int kMvRows = 16;
-constexpr int kMvMaxWaves = 8;
+constexpr int kMvMaxWaves1 = 16;     // one step per wave up to K = 4096
+constexpr int kMvMaxWaves2 = 8;      // longer K: 8 waves, two register buffers each
 constexpr int kMvMaxBlocks = 1024;   // K <= 32768 (the activation scale table is staged in LDS)
 
 template <int T> struct MvStep;
@@ -263,13 +264,14 @@ __device__ __forceinline__ bool mv_resolve(MvCols &mc, const uint8_t *w, int64_t
     return true;
 }
 
-template <int T, bool DBG, bool EXPERT>
-__global__ __launch_bounds__(512) void mmvq_kernel(const uint8_t *__restrict__ w, int64_t rows, int64_t k,
-                                                    const uint8_t *__restrict__ xq, const float2 *__restrict__ tab,
-                                                    int64_t tab_ld, int64_t n, float *__restrict__ y,
-                                                    int32_t *__restrict__ dbg, ColMap cm) {
-    __shared__ __align__(16) float2 sTab[kMvMaxBlocks * 8];
-    __shared__ float sRed[kMvMaxWaves][64][8];
+// NB = 1: every wave owns at most one 256-value step (up to 16 waves), so all of a workgroup's
+// weight loads are in flight at once.  NB = 2: 8 waves walk K with two explicitly unrolled
+// register buffers, the loads of step s + 2*nwaves issued right after step s is consumed.
+template <int T, bool DBG, bool EXPERT, int NB>
+__global__ __launch_bounds__(NB == 1 ? 1024 : 512) void mmvq_kernel(
+    const uint8_t *__restrict__ w, int64_t rows, int64_t k, const uint8_t *__restrict__ xq, int64_t n,
+    float *__restrict__ y, int32_t *__restrict__ dbg, ColMap cm) {
+    extern __shared__ __align__(16) uint8_t mv_smem[];
     using S = MvStep<T>;
     constexpr int NCG = S::NCG;
 
@@ -288,6 +290,8 @@ __global__ __launch_bounds__(512) void mmvq_kernel(const uint8_t *__restrict__ w
     const int64_t row_bytes = (k / Fmt<T>::QK) * Fmt<T>::BYTES;
     const uint8_t *wrow = mc.wbase + (row_ok ? row : 0) * row_bytes;
     const int64_t nsteps = (k + kSuper - 1) / kSuper;
+    float2 *sTab = (float2 *)mv_smem;                          // [nb][8] (d, s)
+    float *sRed = (float *)(mv_smem + nb * 8 * sizeof(float2)); // [nwaves][128]
 
     // This lane's A-operand column (one per column group).
     const int m = r16;
@@ -300,13 +304,29 @@ __global__ __launch_bounds__(512) void mmvq_kernel(const uint8_t *__restrict__ w
     const uint8_t *arow0 = xq + (a_ok0 ? mc.arow(acol0) : 0) * nb * kQ8_1Bytes;
     const uint8_t *arow1 = xq + (a_ok1 ? mc.arow(acol1) : 0) * nb * kQ8_1Bytes;
 
-    // Stage the (d, s) scale table of the workgroup's columns: sTab[block][column].
+    auto do_load = [&](S &st, int64_t s) {
+        if constexpr (T == kQ6_K) st.load(wrow, row_ok, s, g, arow0, arow1, a_ok0, a_ok1);
+        else if constexpr (T == kQ8_0) st.load(wrow, row_ok, s, g, nb, arow0, a_ok0, asel);
+        else st.load(wrow, row_ok, s, g, arow0, a_ok0, asel);
+    };
+    // Weight and code loads first: nothing below waits on them until the first compute.
+    S b0, b1;
+    const int64_t s0 = wave, s1 = wave + nwaves;
+    if (s0 < nsteps) do_load(b0, s0);
+    if (NB == 2 && s1 < nsteps) do_load(b1, s1);
+
+    // Stage the fp32 (d, s) of the workgroup's columns from their q8_1 blocks: sTab[block][column].
     if (!DBG) {
         const int c = threadIdx.x & 7;
-        const int64_t ar = c < ncols ? mc.arow(c) : 0;
+        const uint8_t *xrow = xq + (c < ncols ? mc.arow(c) : 0) * nb * kQ8_1Bytes;
         for (int64_t i = threadIdx.x; i < nb * 8; i += blockDim.x) {
             const int64_t b = i >> 3;     // blockDim.x is a multiple of 8: column c is fixed
-            sTab[i] = c < ncols ? tab[b * tab_ld + ar] : make_float2(0.f, 0.f);
+            float2 v = make_float2(0.f, 0.f);
+            if (c < ncols) {
+                const uint32_t ds = *(const uint32_t *)(xrow + b * kQ8_1Bytes);
+                v = make_float2(h2f((uint16_t)(ds & 0xFFFF)), h2f((uint16_t)(ds >> 16)));
+            }
+            sTab[i] = v;
         }
     }
 
@@ -323,23 +343,22 @@ __global__ __launch_bounds__(512) void mmvq_kernel(const uint8_t *__restrict__ w
         dbg_ld = (int)(rows * per);
         dbg_row = dbg + row * per;
     }
-
-    // Steps of this wave: wave, wave + nwaves, ... (interleaved so neighbouring waves read
-    // neighbouring super-blocks).
-    S cur, nxt;
-    int64_t step = wave;
-    auto do_load = [&](S &st, int64_t s) {
-        if constexpr (T == kQ6_K) st.load(wrow, row_ok, s, g, arow0, arow1, a_ok0, a_ok1);
-        else if constexpr (T == kQ8_0) st.load(wrow, row_ok, s, g, nb, arow0, a_ok0, asel);
-        else st.load(wrow, row_ok, s, g, arow0, a_ok0, asel);
+    auto do_compute = [&](const S &st, int64_t s) {
+        if constexpr (T == kQ8_0) st.template compute<DBG>(s, g, sTab, acc, dbg_row, dbg_ld, ncols, nb);
+        else st.template compute<DBG>(s, g, sTab, acc, dbg_row, dbg_ld, ncols);
     };
-    if (step < nsteps) do_load(nxt, step);
     __syncthreads();
-    for (; step < nsteps; step += nwaves) {
-        cur = nxt;
-        if (step + nwaves < nsteps) do_load(nxt, step + nwaves);
-        if constexpr (T == kQ8_0) cur.template compute<DBG>(step, g, sTab, acc, dbg_row, dbg_ld, ncols, nb);
-        else cur.template compute<DBG>(step, g, sTab, acc, dbg_row, dbg_ld, ncols);
+    if (NB == 1) {
+        if (s0 < nsteps) do_compute(b0, s0);
+    } else {
+        for (int64_t s = s0; s < nsteps; s += 2 * nwaves) {
+            do_compute(b0, s);
+            if (s + 2 * nwaves < nsteps) do_load(b0, s + 2 * nwaves);
+            if (s + nwaves < nsteps) {
+                do_compute(b1, s + nwaves);
+                if (s + 3 * nwaves < nsteps) do_load(b1, s + 3 * nwaves);
+            }
+        }
     }
     if (DBG) return;
 
@@ -354,51 +373,72 @@ __global__ __launch_bounds__(512) void mmvq_kernel(const uint8_t *__restrict__ w
             v += __shfl_xor(v, 32);
             acc[cg][e] = v;
         }
-    // Lanes holding final per-wave values: Q4_K/Q8_0 g in {0,1} (columns 4g..4g+3),
-    // Q6_K g == 0 (columns 4cg..4cg+3).
-#pragma unroll
-    for (int cg = 0; cg < NCG; ++cg)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sRed[wave][lane][cg * 4 + e] = acc[cg][e];
-    __syncthreads();
-    if (wave != 0) return;
+    // Lanes holding the wave's values: Q4_K/Q8_0 g in {0,1} (columns 4g..4g+3), Q6_K g == 0
+    // (columns 4cg..4cg+3); 128 floats per wave.
     const bool holder = (T == kQ6_K) ? (g == 0) : (g < 2);
-    if (!holder || !row_ok) return;
+    if (holder) {
+#pragma unroll
+        for (int cg = 0; cg < NCG; ++cg)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sRed[wave * 128 + lane * (4 * NCG) + cg * 4 + e] = acc[cg][e];
+    }
+    __syncthreads();
+    if (wave != 0 || !holder || !row_ok) return;
 #pragma unroll
     for (int cg = 0; cg < NCG; ++cg)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float v = 0.f;
-            for (int wv = 0; wv < nwaves; ++wv) v += sRed[wv][lane][cg * 4 + e];
+            for (int wv = 0; wv < nwaves; ++wv) v += sRed[wv * 128 + lane * (4 * NCG) + cg * 4 + e];
             const int c = (T == kQ6_K) ? 4 * cg + e : 4 * g + e;
             if (c < ncols) y[mc.pair(c) * rows + row] = v;
         }
 }
 
 template <int T, bool DBG, bool EXPERT>
-static hipError_t launch_mmvq_t(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, const float2 *tab,
-                                int64_t tab_ld, int64_t n, float *y, int32_t *dbg, const ColMap *cm,
-                                int64_t n_exp, hipStream_t s) {
+static hipError_t launch_mmvq_t(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y,
+                                int32_t *dbg, const ColMap *cm, int64_t n_exp, hipStream_t s) {
     const int64_t nsteps = (k + kSuper - 1) / kSuper;
-    int nw = (int)(nsteps < kMvMaxWaves ? nsteps : kMvMaxWaves);
-    if (nw < 1) nw = 1;
     ColMap c = cm ? *cm : ColMap{};
     dim3 grid((unsigned)((rows + kMvRows - 1) / kMvRows), EXPERT ? (unsigned)n_exp : 1u);
-    hipLaunchKernelGGL((mmvq_kernel<T, DBG, EXPERT>), grid, dim3(64 * nw), 0, s, w, rows, k, xq, tab, tab_ld, n, y,
-                       dbg, c);
+    const size_t smem_tab = (size_t)(k / 32) * 8 * sizeof(float2);
+    if (nsteps <= kMvMaxWaves1) {
+        const int nw = (int)nsteps;
+        const size_t smem = smem_tab + (size_t)nw * 128 * sizeof(float);
+        static bool attr1 = false;
+        if (!attr1) {
+            hipError_t e = hipFuncSetAttribute((const void *)mmvq_kernel<T, DBG, EXPERT, 1>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+            if (e != hipSuccess) return e;
+            attr1 = true;
+        }
+        hipLaunchKernelGGL((mmvq_kernel<T, DBG, EXPERT, 1>), grid, dim3(64 * nw), smem, s, w, rows, k, xq, n, y,
+                           dbg, c);
+    } else {
+        const int nw = kMvMaxWaves2;
+        const size_t smem = smem_tab + (size_t)nw * 128 * sizeof(float);
+        static bool attr2 = false;
+        if (!attr2) {
+            hipError_t e = hipFuncSetAttribute((const void *)mmvq_kernel<T, DBG, EXPERT, 2>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+            if (e != hipSuccess) return e;
+            attr2 = true;
+        }
+        hipLaunchKernelGGL((mmvq_kernel<T, DBG, EXPERT, 2>), grid, dim3(64 * nw), smem, s, w, rows, k, xq, n, y,
+                           dbg, c);
+    }
     return hipGetLastError();
 }
 
-hipError_t launch_mmvq(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, const float2 *tab,
-                       int64_t tab_ld, int64_t n, float *y, int32_t *dbg, const ColMap *cm, int64_t n_exp,
-                       hipStream_t s) {
+hipError_t launch_mmvq(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y,
+                       int32_t *dbg, const ColMap *cm, int64_t n_exp, hipStream_t s) {
     const bool expert = cm != nullptr;
     const bool d = dbg != nullptr;
 #define QMM_MV(TT)                                                                                       \
     if (type == TT) {                                                                                  \
-        if (d) return launch_mmvq_t<TT, true, false>(w, rows, k, xq, tab, tab_ld, n, y, dbg, cm, n_exp, s); \
-        if (expert) return launch_mmvq_t<TT, false, true>(w, rows, k, xq, tab, tab_ld, n, y, dbg, cm, n_exp, s); \
-        return launch_mmvq_t<TT, false, false>(w, rows, k, xq, tab, tab_ld, n, y, dbg, cm, n_exp, s);   \
+        if (d) return launch_mmvq_t<TT, true, false>(w, rows, k, xq, n, y, dbg, cm, n_exp, s); \
+        if (expert) return launch_mmvq_t<TT, false, true>(w, rows, k, xq, n, y, dbg, cm, n_exp, s); \
+        return launch_mmvq_t<TT, false, false>(w, rows, k, xq, n, y, dbg, cm, n_exp, s);   \
     }
     QMM_MV(kQ4_K)
     QMM_MV(kQ6_K)

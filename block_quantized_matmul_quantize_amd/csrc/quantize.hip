@@ -14,8 +14,7 @@
 namespace qmm {
 
 __global__ __launch_bounds__(256) void quantize_q8_1_kernel(const float *__restrict__ x, int64_t n_rows,
-                                                            int64_t k, uint8_t *__restrict__ y,
-                                                            float2 *__restrict__ tab, int64_t tab_ld) {
+                                                            int64_t k, uint8_t *__restrict__ y) {
     const int64_t nb = k / 32;
     const int64_t total = n_rows * nb;
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -59,20 +58,7 @@ __global__ __launch_bounds__(256) void quantize_q8_1_kernel(const float *__restr
         asm volatile("" : "+v"(s32));
         const __half hs = __float2half_rn(s32);
         *(uint32_t *)yb = (uint32_t)__half_as_ushort(hd) | ((uint32_t)__half_as_ushort(hs) << 16);
-        if (tab) tab[b * tab_ld + row] = make_float2(__half2float(hd), __half2float(hs));
     }
-}
-
-// (d, s) of existing q8_1 blocks -> fp32 table [k/32][tab_ld] (columns beyond n_rows untouched).
-__global__ __launch_bounds__(256) void q8_1_scale_table_kernel(const uint8_t *__restrict__ xq, int64_t n_rows,
-                                                               int64_t k, float2 *__restrict__ tab,
-                                                               int64_t tab_ld) {
-    const int64_t nb = k / 32;
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n_rows * nb) return;
-    const int64_t row = i / nb, b = i - row * nb;
-    const uint32_t ds = *(const uint32_t *)(xq + i * kQ8_1Bytes);
-    tab[b * tab_ld + row] = make_float2(h2f((uint16_t)(ds & 0xFFFF)), h2f((uint16_t)(ds >> 16)));
 }
 
 // Plain fill kernel (used instead of a memset so that the call sequence stays capturable).
@@ -82,22 +68,11 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t *__restrict__ p,
     for (int64_t j = i; j < n; j += stride) p[j] = v;
 }
 
-hipError_t launch_quantize_q8_1(const float *x, int64_t n_rows, int64_t k, uint8_t *y, float2 *tab,
-                                int64_t tab_ld, hipStream_t s) {
+hipError_t launch_quantize_q8_1(const float *x, int64_t n_rows, int64_t k, uint8_t *y, hipStream_t s) {
     const int64_t threads = n_rows * (k / 32) * 8;
     if (threads == 0) return hipSuccess;
     const int64_t blocks = (threads + 255) / 256;
-    hipLaunchKernelGGL(quantize_q8_1_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, n_rows, k, y, tab,
-                       tab_ld);
-    return hipGetLastError();
-}
-
-hipError_t launch_q8_1_scale_table(const uint8_t *xq, int64_t n_rows, int64_t k, float2 *tab, int64_t tab_ld,
-                                   hipStream_t s) {
-    const int64_t items = n_rows * (k / 32);
-    if (items == 0) return hipSuccess;
-    hipLaunchKernelGGL(q8_1_scale_table_kernel, dim3((unsigned)((items + 255) / 256)), dim3(256), 0, s, xq,
-                       n_rows, k, tab, tab_ld);
+    hipLaunchKernelGGL(quantize_q8_1_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, n_rows, k, y);
     return hipGetLastError();
 }
 

@@ -75,8 +75,9 @@ qmm_status qmm_quantize_q8_1(const float *x, int64_t n_rows, int64_t k, void *y,
  * a tile-width selector and a stream-K split when the tiles underfill the GPU ([MMQ] "J runtime
  * selection", "tile efficiency", "stream-K", "fixup").
  *
- * qmm_matmul_workspace: bytes of device workspace qmm_matmul needs (>= 0; 256-byte aligned
- *   pointer expected).  Returns 0 for invalid arguments.
+ * qmm_matmul_workspace: bytes of device workspace qmm_matmul needs (256-byte aligned pointer
+ *   expected).  A size of 0 means no workspace is needed (ws may be NULL); invalid arguments also
+ *   give 0, and the call itself then reports the error.
  * qmm_matmul: quantizes x to q8_1 into the workspace, then multiplies.
  * qmm_matmul_q8_1: the same product from already-quantized activations xq (n * k/32 q8_1
  *   blocks, as written by qmm_quantize_q8_1), so one quantization can serve several weights
