@@ -133,6 +133,10 @@ qmm_status qmm_set_override(int key, int value) {
             if (value != 0 && value != 32 && value != 64 && value != 128)
                 return fail(QMM_ERR_ARG, "tile width override must be 0, 32, 64 or 128");
             g_ovr_tile_j = value; return QMM_OK;
+        case QMM_OVR_MV_STEPS:
+            if (value != 0 && value != 1 && value != 2 && value != 4)
+                return fail(QMM_ERR_ARG, "steps-per-wave override must be 0, 1, 2 or 4");
+            qmm::set_mmvq_steps_per_wave(value); return QMM_OK;
         default:
             return fail(QMM_ERR_ARG, "unknown override key %d", key);
     }

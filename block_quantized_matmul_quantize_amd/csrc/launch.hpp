@@ -27,6 +27,9 @@ struct ColMap {
 hipError_t launch_mmvq(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n,
                        float *y, int32_t *dbg, const ColMap *cm, int64_t n_exp, hipStream_t s);
 
+// Tuning: 256-value steps per wave of the matrix-vector kernel (0 = automatic).
+void set_mmvq_steps_per_wave(int spw);
+
 // Tiled int8-MFMA kernel plan.
 struct MmqLaunch {
     int tile_j;          // 32, 64 or 128

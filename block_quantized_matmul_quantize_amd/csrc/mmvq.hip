@@ -3,86 +3,116 @@
 // weight byte is read once and serves all columns; GP100 patch page, "Coverage": multi-column
 // kernels unpack each weight once and reuse it for every column).
 //
-// CDNA4 design.  A workgroup owns 16 weight rows; its waves split K (one 256-value step per wave
-// per iteration, the next step's weight and code loads are issued before the current step's
-// math).  Each 64-value slice of K is one v_mfma_i32_16x16x64_i8 whose B operand is 16 weight
-// rows and whose A operand is block-diagonal over activation (column, sub-block) pairs, so every
-// one of the 16 result columns is useful:
-//   Q4_K, Q8_0: A row m = (column m%8, sub-block m/8); K slots 0-31 hold sub-block 2p, slots
-//               32-63 sub-block 2p+1; the off-diagonal halves are zero.  -> 8 columns.
-//   Q6_K:       A row m = (column m%4, 16-value sub-block m/4), four diagonal 16-slot blocks,
-//               because Q6_K scales change every 16 values ("Q6_K dot" section).  -> 4 columns
-//               per MFMA, two MFMAs for 5..8 columns.
-// The int32 result of each lane is then one exact sub-block dot D for one (row, column,
-// sub-block), and the fp32 fixup ("dp4a path Q4_K" section) is applied per lane:
+// CDNA4 design.  A workgroup owns 16 weight rows and W waves; wave w handles the 256-value
+// steps w, w+W, ... (SPW of them per pass), issuing every load of the pass before any math so
+// the math of early steps overlaps the arrival of later ones.  Each 64-value slice of K is one
+// v_mfma_i32_16x16x64_i8: B = 16 weight rows (4 lanes per row), A = activations arranged
+// block-diagonally over (column, sub-block) so that all 16 result columns are useful and every
+// int32 result is one exact sub-block dot D:
+//   Q4_K, Q8_0: 8 columns x 2 sub-blocks of 32 values per MFMA;
+//   Q6_K:       4 columns x 4 sub-blocks of 16 values per MFMA (its scale changes every 16
+//               values, "Q6_K dot" section); 5..8 columns use a second MFMA.
+// Weight loads: per load instruction the 4 lanes of a row read one contiguous 64-byte run; the
+// K-slot assignment of each MFMA follows whatever bytes a lane holds (any consistent slot order
+// gives the same contraction).  Off-diagonal activation lanes read a 16-byte zero block, and
+// row indices are clamped, so the loop has no per-lane branches.
+// fp32 fixups per lane ("dp4a path Q4_K" section):
 //   Q4_K  acc += D * (d*sc) * d_a - (dmin*m) * s_a
-//   Q6_K  acc += D * (d*sc) * d_a
+//   Q6_K  acc += D * (d*sc) * d_a      with D = sum q6*q_a - 32*sum q_a (a second MFMA against a
+//                                       constant -32 operand, chained through the accumulator)
 //   Q8_0  acc += D * d_w * d_a
-// Partial sums over sub-blocks are combined with lane shuffles, then across waves in LDS in a
-// fixed order (bitwise reproducible).
+// Partial sums are combined with lane shuffles, then across waves in LDS in a fixed order.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace qmm {
 
 constexpr int kMvRows = 16;
-constexpr int kMvMaxWaves1 = 16;     // one step per wave up to K = 4096
-constexpr int kMvMaxWaves2 = 8;      // longer K: 8 waves, two register buffers each
 constexpr int kMvMaxBlocks = 1024;   // K <= 32768 (the activation scale table is staged in LDS)
+
+// 16 zero bytes: the A operand of lanes outside the block diagonal or beyond the live columns.
+__device__ __attribute__((aligned(16))) uint8_t mv_zero16[16];
+
+__device__ __forceinline__ uint32_t nib_lo(uint32_t v) { return v & 0x0F0F0F0Fu; }
+__device__ __forceinline__ uint32_t nib_hi(uint32_t v) { return (v >> 4) & 0x0F0F0F0Fu; }
+__device__ __forceinline__ u32x4 nib_lo4(u32x4 v) { return u32x4{nib_lo(v.x), nib_lo(v.y), nib_lo(v.z), nib_lo(v.w)}; }
+__device__ __forceinline__ u32x4 nib_hi4(u32x4 v) { return u32x4{nib_hi(v.x), nib_hi(v.y), nib_hi(v.z), nib_hi(v.w)}; }
+__device__ __forceinline__ u32x4 sel4(bool c, u32x4 a, u32x4 b) { return c ? a : b; }
+
+// Per-lane constants shared by every step.
+struct MvLane {
+    int g, r16;                 // K-slot group (lane / 16) and row within the 16-row group
+    uint32_t wrow_off;          // byte offset of this lane's (clamped) row from the group base
+    const uint8_t *abase[2];    // activation row of this lane's A column (or the zero block)
+    int64_t astride[2];         // bytes per 256-value step of that row (0 for the zero block)
+    uint32_t aoff[2][4];        // byte offset, within a step, of this lane's A piece per MFMA
+};
 
 template <int T> struct MvStep;
 
 // ------------------------------------------------------------------------------------------
-// Q4_K: one step = one 144-byte super-block per row = 4 MFMAs (sub-block pairs 2p, 2p+1).
+// Q4_K: 144-byte super-block = {d, dmin, 12 scale bytes, qs[128]}; piece p = bytes 16p..16p+15.
+// Lane g of a row loads pieces g and 4+g (two 64-byte runs per row), the last piece and the
+// header (same address for the row's 4 lanes).  32 qs bytes serve 64 values: low nibbles the
+// first sub-block of the pair, high nibbles the second.  MFMA j covers sub-blocks
+//   j=0: {0, 2} (low nibbles of src1), j=1: {1, 3} (high, src1),
+//   j=2: {4, 6} (low, src2),           j=3: {5, 7} (high, src2),
+// src1 = g==0 ? piece 4 : piece g, src2 = g==0 ? piece 8 : piece 4+g; lanes g = 1, 2 carry the
+// first sub-block of the pair (values 0-15 / 16-31) and g = 3, 0 the second.
 // ------------------------------------------------------------------------------------------
 template <> struct MvStep<kQ4_K> {
     static constexpr int NCG = 1;
-    u32x4 hdr;
-    u32x4 q[4];
-    u32x4 a[4][1];
+    static constexpr int BYTES = 144;
+    u32x4 pa, pb, pc, hdr;
+    u32x4 a[4];
 
-    __device__ __forceinline__ void load(const uint8_t *wrow, bool row_ok, int64_t step, int g,
-                                         const uint8_t *arow, bool a_ok, int asel) {
-        const uint8_t *blk = wrow + step * 144;
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        hdr = row_ok ? ld16(blk) : z;
+    // K-slot group of lane g for the block diagonal: 0 for g in {1,2}, 1 for g in {3,0}; the half
+    // of the sub-block it carries: values 0-15 for g in {1,3}, 16-31 for g in {0,2}.
+    __device__ static int group(int g) { return (g == 1 || g == 2) ? 0 : 1; }
+    __device__ static int half(int g) { return (g & 1) ? 0 : 1; }
+    // sub-block of MFMA j for diagonal half sel
+    __device__ static int subblock(int j, int sel) {
+        const int base = (j >> 1) * 4 + (j & 1);
+        return base + 2 * sel;
+    }
+    __device__ static void lane_setup(MvLane &L, int m) {
+        const int sel = m >> 3;
+        for (int j = 0; j < 4; ++j)
+            L.aoff[0][j] = (uint32_t)(subblock(j, sel) * kQ8_1Bytes + 4 + 16 * half(L.g));
+    }
+    __device__ static bool a_diag(int g, int m) { return group(g) == (m >> 3); }
+    __device__ static int a_col(int m, int) { return m & 7; }
+
+    __device__ __forceinline__ void load(const uint8_t *wg, const MvLane &L, int64_t step) {
+        const uint8_t *blk = wg + L.wrow_off + step * BYTES;
+        pa = ld16(blk + 16 * L.g);
+        pb = ld16(blk + 64 + 16 * L.g);
+        pc = ld16(blk + 128);
+        hdr = ld16(blk);
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            q[p] = row_ok ? ld16(blk + 16 + 32 * p + 16 * (g & 1)) : z;
-            a[p][0] = a_ok ? ld16(arow + (step * 8 + 2 * p + asel) * kQ8_1Bytes + 4 + 16 * (g & 1)) : z;
-        }
+        for (int j = 0; j < 4; ++j) a[j] = ld16(L.abase[0] + step * L.astride[0] + L.aoff[0][j]);
     }
 
     template <bool DBG>
-    __device__ __forceinline__ void compute(int64_t step, int g, const float2 *sTab, float acc[NCG][4],
-                                           int32_t *dbg_row, int dbg_ld, int ncols) const {
-        const int sel = g >> 1;
+    __device__ __forceinline__ void compute(int64_t step, const MvLane &L, const float2 *sTab, float (&acc)[NCG][4],
+                                            int32_t *dbg_row, int64_t dbg_ld, int ncols) const {
+        const int g = L.g, sel = g >> 1;
         const float d = h2f((uint16_t)(hdr.x & 0xFFFF));
         const float dmin = h2f((uint16_t)(hdr.x >> 16));
-        // 6-bit scales/mins of sub-blocks 0..7 as bytes: j<4 in the low 6 bits of bytes j / j+4,
-        // j>=4 split over the low/high nibble of byte j+4 and the top bits of bytes j-4 / j.
-        uint32_t sc_lo = hdr.y & 0x3F3F3F3Fu;
-        uint32_t m_lo = hdr.z & 0x3F3F3F3Fu;
-        uint32_t sc_hi = (hdr.w & 0x0F0F0F0Fu) | ((hdr.y >> 2) & 0x30303030u);
-        uint32_t m_hi = ((hdr.w >> 4) & 0x0F0F0F0Fu) | ((hdr.z >> 2) & 0x30303030u);
-        // this lane's sub-blocks are 2p + sel: shift so that byte 2*(p%2) is the one needed
-        sc_lo >>= 8 * sel; m_lo >>= 8 * sel; sc_hi >>= 8 * sel; m_hi >>= 8 * sel;
-        const int shift = 4 * sel;   // low nibbles: first sub-block of the pair
+        // 6-bit scales/mins as bytes: j<4 in the low 6 bits of bytes j / j+4, j>=4 split over the
+        // low/high nibble of byte j+4 and the top bits of bytes j-4 / j.
+        const uint32_t sc_lo = (hdr.y & 0x3F3F3F3Fu) >> (16 * sel);
+        const uint32_t m_lo = (hdr.z & 0x3F3F3F3Fu) >> (16 * sel);
+        const uint32_t sc_hi = ((hdr.w & 0x0F0F0F0Fu) | ((hdr.y >> 2) & 0x30303030u)) >> (16 * sel);
+        const uint32_t m_hi = (((hdr.w >> 4) & 0x0F0F0F0Fu) | ((hdr.z >> 2) & 0x30303030u)) >> (16 * sel);
+        const u32x4 src1 = sel4(g == 0, pb, pa), src2 = sel4(g == 0, pc, pb);
+        const u32x4 bop[4] = {nib_lo4(src1), nib_hi4(src1), nib_lo4(src2), nib_hi4(src2)};
+        const i32x4 zero = {0, 0, 0, 0};
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const uint32_t scw = p < 2 ? sc_lo : sc_hi;
-            const uint32_t mw = p < 2 ? m_lo : m_hi;
-            const int bsh = 16 * (p & 1);
-            const float ws = d * (float)((scw >> bsh) & 0xFF);
-            const float wm = dmin * (float)((mw >> bsh) & 0xFF);
-            u32x4 b;
-            b.x = (q[p].x >> shift) & 0x0F0F0F0Fu;
-            b.y = (q[p].y >> shift) & 0x0F0F0F0Fu;
-            b.z = (q[p].z >> shift) & 0x0F0F0F0Fu;
-            b.w = (q[p].w >> shift) & 0x0F0F0F0Fu;
-            const i32x4 zero = {0, 0, 0, 0};
-            const i32x4 D = mfma16x16x64(a[p][0], b, zero);
-            const int64_t blk = step * 8 + 2 * p + sel;
+        for (int j = 0; j < 4; ++j) {
+            const i32x4 D = mfma16x16x64(a[j], bop[j], zero);
+            const int sb = subblock(j, sel);
+            const int64_t blk = step * 8 + sb;
             if (DBG) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -90,6 +120,9 @@ template <> struct MvStep<kQ4_K> {
                     if (dbg_row && c < ncols) dbg_row[(int64_t)c * dbg_ld + blk] = D[e];
                 }
             } else {
+                const uint32_t scw = j < 2 ? sc_lo : sc_hi, mw = j < 2 ? m_lo : m_hi;
+                const float ws = d * (float)((scw >> (8 * (j & 1))) & 0xFF);
+                const float wm = dmin * (float)((mw >> (8 * (j & 1))) & 0xFF);
                 const f32x4 t0 = *(const f32x4 *)(sTab + blk * 8 + 4 * (g & 1));
                 const f32x4 t1 = *(const f32x4 *)(sTab + blk * 8 + 4 * (g & 1) + 2);
                 acc[0][0] += (float)D[0] * (ws * t0.x) - wm * t0.y;
@@ -102,60 +135,80 @@ template <> struct MvStep<kQ4_K> {
 };
 
 // ------------------------------------------------------------------------------------------
-// Q6_K: one step = one 210-byte super-block per row = 4 MFMAs per 4-column group.
-// Value v of a super-block: half h = v/128, u = v%128, quarter g = u/32, l = u%32; the low 4 bits
-// are nibble (g<2 ? low : high) of ql[64h + 32(g&1) + l], the top 2 bits are bits 2g..2g+1 of
-// qh[32h + l], and the code is that 6-bit value minus 32 (the MMQ page's Q6_K load pairs ql word
-// txi with qh word 8*(txi/16) + txi%8 shifted by (txi&8)>>2, which this mapping reproduces).
+// Q6_K: 210-byte super-block = {ql[128], qh[64], int8 scales[16], d}.  Value v: half h = v/128,
+// u = v%128, quarter q = u/32, l = u%32; low 4 bits = nibble (q<2 ? low : high) of
+// ql[64h + 32(q&1) + l], top 2 bits = bits 2q..2q+1 of qh[32h + l]; code = 6-bit value - 32
+// (the MMQ page's Q6_K load pairs ql word txi with qh word 8*(txi/16) + txi%8 shifted by
+// (txi&8)>>2, which this mapping reproduces).  Lane g of a row loads ql[16g..] and
+// ql[64+16g..] and qh[16g..] (64-byte runs); MFMA p covers values 64p..64p+63, lane g the
+// 16-value sub-block 4p+g, whose qh bytes sit in lane 2*(p/2) + (g&1) -- this lane or its
+// xor-32 partner.
 // ------------------------------------------------------------------------------------------
 template <> struct MvStep<kQ6_K> {
     static constexpr int NCG = 2;
-    u32x4 scv;
+    static constexpr int BYTES = 210;
+    u32x4 ql0, ql1, qh, scv;
     uint32_t dbits;
-    u32x4 ql[2], qh[2];     // per 128-value half: ql serves two quarters (low/high nibble)
-    u32x4 a[4][2];
+    u32x4 a[2][4];
 
-    __device__ __forceinline__ void load(const uint8_t *wrow, bool row_ok, int64_t step, int g,
-                                         const uint8_t *arow0, const uint8_t *arow1, bool a_ok0, bool a_ok1) {
-        const uint8_t *blk = wrow + step * 210;
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        scv = row_ok ? ld16(blk + 192) : z;
-        dbits = row_ok ? (uint32_t)ld2(blk + 208) : 0u;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            ql[h] = row_ok ? ld16(blk + 64 * h + 16 * g) : z;
-            qh[h] = row_ok ? ld16(blk + 128 + 32 * h + 16 * (g & 1)) : z;
-        }
-#pragma unroll
+    __device__ static void lane_setup(MvLane &L, int m) {
+        const int grp = m >> 2;                  // the 16-value sub-block this A row covers
         for (int p = 0; p < 4; ++p) {
-            const int64_t off = (step * 8 + 2 * p + (g >> 1)) * kQ8_1Bytes + 4 + 16 * (g & 1);
-            a[p][0] = a_ok0 ? ld16(arow0 + off) : z;
-            a[p][1] = a_ok1 ? ld16(arow1 + off) : z;
+            const uint32_t off = (uint32_t)((2 * p + (grp >> 1)) * kQ8_1Bytes + 4 + 16 * (grp & 1));
+            L.aoff[0][p] = off;
+            L.aoff[1][p] = off;
         }
+    }
+    __device__ static bool a_diag(int g, int m) { return g == (m >> 2); }
+    __device__ static int a_col(int m, int cg) { return (m & 3) + 4 * cg; }
+
+    __device__ __forceinline__ void load(const uint8_t *wg, const MvLane &L, int64_t step) {
+        const uint8_t *blk = wg + L.wrow_off + step * BYTES;
+        ql0 = ld16(blk + 16 * L.g);
+        ql1 = ld16(blk + 64 + 16 * L.g);
+        qh = ld16(blk + 128 + 16 * L.g);
+        scv = ld16(blk + 192);
+        dbits = ld2(blk + 208);
+#pragma unroll
+        for (int cg = 0; cg < 2; ++cg)
+#pragma unroll
+            for (int p = 0; p < 4; ++p) a[cg][p] = ld16(L.abase[cg] + step * L.astride[cg] + L.aoff[cg][p]);
     }
 
     template <bool DBG>
-    __device__ __forceinline__ void compute(int64_t step, int g, const float2 *sTab, float acc[NCG][4],
-                                            int32_t *dbg_row, int dbg_ld, int ncols) const {
+    __device__ __forceinline__ void compute(int64_t step, const MvLane &L, const float2 *sTab, float (&acc)[NCG][4],
+                                            int32_t *dbg_row, int64_t dbg_ld, int ncols) const {
+        const int g = L.g;
         const float d = h2f((uint16_t)dbits);
+        // qh bytes of half h live in lanes 2h + (g&1): fetch the partner's (xor 32) copy.
+        u32x4 qh_x;
+        qh_x.x = (uint32_t)__shfl_xor((int)qh.x, 32);
+        qh_x.y = (uint32_t)__shfl_xor((int)qh.y, 32);
+        qh_x.z = (uint32_t)__shfl_xor((int)qh.z, 32);
+        qh_x.w = (uint32_t)__shfl_xor((int)qh.w, 32);
+        const u32x4 qh_h0 = (g >> 1) == 0 ? qh : qh_x;     // qh[16(g&1)..] of half 0
+        const u32x4 qh_h1 = (g >> 1) == 1 ? qh : qh_x;     // qh[32 + 16(g&1)..] of half 1
+        const u32x4 neg32 = {0xE0E0E0E0u, 0xE0E0E0E0u, 0xE0E0E0E0u, 0xE0E0E0E0u};
+        const i32x4 zero = {0, 0, 0, 0};
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const int odd = p & 1;
-            const uint32_t scw = p == 0 ? scv.x : p == 1 ? scv.y : p == 2 ? scv.z : scv.w;
-            const float ws = d * (float)((int32_t)(scw << (24 - 8 * g)) >> 24);   // scale of 16-value block 4p+g
+            const u32x4 L4 = (p >> 1) ? ql1 : ql0;
+            const u32x4 H4 = (p >> 1) ? qh_h1 : qh_h0;
             const int tsh = 4 * odd + 2 * (g >> 1);
-            u32x4 b;
-            const u32x4 L = ql[p >> 1], H = qh[p >> 1];
-            b.x = sub32_bytes(((L.x >> (4 * odd)) & 0x0F0F0F0Fu) | (((H.x >> tsh) & 0x03030303u) << 4));
-            b.y = sub32_bytes(((L.y >> (4 * odd)) & 0x0F0F0F0Fu) | (((H.y >> tsh) & 0x03030303u) << 4));
-            b.z = sub32_bytes(((L.z >> (4 * odd)) & 0x0F0F0F0Fu) | (((H.z >> tsh) & 0x03030303u) << 4));
-            b.w = sub32_bytes(((L.w >> (4 * odd)) & 0x0F0F0F0Fu) | (((H.w >> tsh) & 0x03030303u) << 4));
+            u32x4 b;   // stored 6-bit values (0..63)
+            b.x = ((L4.x >> (4 * odd)) & 0x0F0F0F0Fu) | (((H4.x >> tsh) << 4) & 0x30303030u);
+            b.y = ((L4.y >> (4 * odd)) & 0x0F0F0F0Fu) | (((H4.y >> tsh) << 4) & 0x30303030u);
+            b.z = ((L4.z >> (4 * odd)) & 0x0F0F0F0Fu) | (((H4.z >> tsh) << 4) & 0x30303030u);
+            b.w = ((L4.w >> (4 * odd)) & 0x0F0F0F0Fu) | (((H4.w >> tsh) << 4) & 0x30303030u);
+            const uint32_t scw = p == 0 ? scv.x : p == 1 ? scv.y : p == 2 ? scv.z : scv.w;
+            const float ws = d * (float)((int32_t)(scw << (24 - 8 * g)) >> 24);   // scale of sub-block 4p+g
             const int64_t blk = step * 8 + 2 * p + (g >> 1);   // q8_1 block of this lane's sub-block
 #pragma unroll
             for (int cg = 0; cg < NCG; ++cg) {
                 if (cg * 4 >= ncols) break;
-                const i32x4 zero = {0, 0, 0, 0};
-                const i32x4 D = mfma16x16x64(a[p][cg], b, zero);
+                i32x4 D = mfma16x16x64(a[cg][p], b, zero);
+                D = mfma16x16x64(a[cg][p], neg32, D);          // - 32 * sum(q_a) over the sub-block
                 if (DBG) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -176,39 +229,52 @@ template <> struct MvStep<kQ6_K> {
 };
 
 // ------------------------------------------------------------------------------------------
-// Q8_0: one step = 8 blocks of 34 bytes (256 values) = 4 MFMAs; a final partial step masks the
-// blocks beyond k/32.
+// Q8_0: 34-byte blocks {d, int8 q[32]}; a step is 8 blocks (256 values), MFMA p covers blocks
+// 2p (lanes g = 0, 1) and 2p+1 (lanes g = 2, 3); lane g loads 16 codes of its block, so the
+// 4 lanes of a row read the 64 code bytes of two adjacent blocks.  The last step of a row may be
+// partial (k/32 blocks): blocks beyond it are clamped to the last block and their results dropped.
 // ------------------------------------------------------------------------------------------
 template <> struct MvStep<kQ8_0> {
     static constexpr int NCG = 1;
+    static constexpr int BYTES = 272;
     uint32_t dbits[4];
     u32x4 q[4];
-    u32x4 a[4][1];
+    u32x4 a[4];
 
-    __device__ __forceinline__ void load(const uint8_t *wrow, bool row_ok, int64_t step, int g, int64_t nb,
-                                         const uint8_t *arow, bool a_ok, int asel) {
-        const u32x4 z = {0u, 0u, 0u, 0u};
+    // aoff[0][p] holds the block index 2p + sel within the step; the byte offset is formed in
+    // load() after clamping to the row's last block (astride is 8 for a live lane, 0 otherwise).
+    __device__ static void lane_setup(MvLane &L, int m) {
+        const int sel = m >> 3;
+        for (int p = 0; p < 4; ++p) L.aoff[0][p] = (uint32_t)(2 * p + sel);
+    }
+    __device__ static bool a_diag(int g, int m) { return (g >> 1) == (m >> 3); }
+    __device__ static int a_col(int m, int) { return m & 7; }
+
+    __device__ __forceinline__ void load(const uint8_t *wg, const MvLane &L, int64_t step, int64_t nb) {
+        const int64_t live = L.astride[0] != 0 ? 1 : 0;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            const int64_t bw = step * 8 + 2 * p + (g >> 1);    // this lane's weight block
-            const bool ok = row_ok && bw < nb;
-            const uint8_t *blk = wrow + bw * 34;
-            dbits[p] = ok ? (uint32_t)ld2(blk) : 0u;
-            q[p] = ok ? ld16(blk + 2 + 16 * (g & 1)) : z;
-            const int64_t ba = step * 8 + 2 * p + asel;        // this lane's activation block
-            a[p][0] = (a_ok && ba < nb) ? ld16(arow + ba * kQ8_1Bytes + 4 + 16 * (g & 1)) : z;
+            int64_t bw = step * 8 + 2 * p + (L.g >> 1);
+            bw = bw < nb ? bw : nb - 1;
+            const uint8_t *blk = wg + L.wrow_off + bw * 34;
+            dbits[p] = ld2(blk);
+            q[p] = ld16(blk + 2 + 16 * (L.g & 1));
+            int64_t ba = step * 8 + L.aoff[0][p];
+            ba = ba < nb ? ba : nb - 1;
+            a[p] = ld16(L.abase[0] + live * (ba * kQ8_1Bytes + 4 + 16 * (L.g & 1)));
         }
     }
 
     template <bool DBG>
-    __device__ __forceinline__ void compute(int64_t step, int g, const float2 *sTab, float acc[NCG][4],
-                                            int32_t *dbg_row, int dbg_ld, int ncols, int64_t nb) const {
+    __device__ __forceinline__ void compute(int64_t step, const MvLane &L, const float2 *sTab, float (&acc)[NCG][4],
+                                            int32_t *dbg_row, int64_t dbg_ld, int ncols, int64_t nb) const {
+        const int g = L.g;
+        const i32x4 zero = {0, 0, 0, 0};
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            const int64_t blk = step * 8 + 2 * p + (g >> 1);
             if (step * 8 + 2 * p >= nb) break;   // wave-uniform
-            const i32x4 zero = {0, 0, 0, 0};
-            const i32x4 D = mfma16x16x64(a[p][0], q[p], zero);
+            const i32x4 D = mfma16x16x64(a[p], q[p], zero);
+            const int64_t blk = step * 8 + 2 * p + (g >> 1);
             if (blk >= nb) continue;
             if (DBG) {
 #pragma unroll
@@ -264,13 +330,12 @@ __device__ __forceinline__ bool mv_resolve(MvCols &mc, const uint8_t *w, int64_t
     return true;
 }
 
-// NB = 1: every wave owns at most one 256-value step (up to 16 waves), so all of a workgroup's
-// weight loads are in flight at once.  NB = 2: 8 waves walk K with two explicitly unrolled
-// register buffers, the loads of step s + 2*nwaves issued right after step s is consumed.
-template <int T, bool DBG, bool EXPERT, int NB>
-__global__ __launch_bounds__(NB == 1 ? 1024 : 512) void mmvq_kernel(
-    const uint8_t *__restrict__ w, int64_t rows, int64_t k, const uint8_t *__restrict__ xq, int64_t n,
-    float *__restrict__ y, int32_t *__restrict__ dbg, ColMap cm) {
+constexpr int mv_max_waves(int spw) { return spw == 1 ? 16 : spw == 2 ? 8 : 4; }
+
+template <int T, int SPW, bool DBG, bool EXPERT>
+__global__ __launch_bounds__(64 * mv_max_waves(SPW)) void mmvq_kernel(const uint8_t *__restrict__ w, int64_t rows, int64_t k,
+                                                    const uint8_t *__restrict__ xq, int64_t n, float *__restrict__ y,
+                                                    int32_t *__restrict__ dbg, ColMap cm) {
     extern __shared__ __align__(16) uint8_t mv_smem[];
     using S = MvStep<T>;
     constexpr int NCG = S::NCG;
@@ -282,38 +347,31 @@ __global__ __launch_bounds__(NB == 1 ? 1024 : 512) void mmvq_kernel(
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int nwaves = blockDim.x >> 6;
-    const int g = lane >> 4;
-    const int r16 = lane & 15;
-    const int64_t row = (int64_t)blockIdx.x * kMvRows + r16;
-    const bool row_ok = row < rows;
     const int64_t nb = k / 32;                         // q8_1 blocks per activation row
     const int64_t row_bytes = (k / Fmt<T>::QK) * Fmt<T>::BYTES;
-    const uint8_t *wrow = mc.wbase + (row_ok ? row : 0) * row_bytes;
     const int64_t nsteps = (k + kSuper - 1) / kSuper;
+    const int64_t row0 = (int64_t)blockIdx.x * kMvRows;
+    const uint8_t *wg = mc.wbase + row0 * row_bytes;   // uniform base of the 16-row group
     float2 *sTab = (float2 *)mv_smem;                          // [nb][8] (d, s)
     float *sRed = (float *)(mv_smem + nb * 8 * sizeof(float2)); // [nwaves][128]
 
-    // This lane's A-operand column (one per column group).
-    const int m = r16;
-    int acol0, acol1, asel;
-    if (T == kQ6_K) { acol0 = m & 3; acol1 = 4 + (m & 3); asel = m >> 2; }
-    else { acol0 = m & 7; acol1 = 0; asel = m >> 3; }
-    const bool a_diag = (T == kQ6_K) ? (g == asel) : ((g >> 1) == asel);
-    const bool a_ok0 = a_diag && acol0 < ncols;
-    const bool a_ok1 = a_diag && acol1 < ncols;
-    const uint8_t *arow0 = xq + (a_ok0 ? mc.arow(acol0) : 0) * nb * kQ8_1Bytes;
-    const uint8_t *arow1 = xq + (a_ok1 ? mc.arow(acol1) : 0) * nb * kQ8_1Bytes;
-
-    auto do_load = [&](S &st, int64_t s) {
-        if constexpr (T == kQ6_K) st.load(wrow, row_ok, s, g, arow0, arow1, a_ok0, a_ok1);
-        else if constexpr (T == kQ8_0) st.load(wrow, row_ok, s, g, nb, arow0, a_ok0, asel);
-        else st.load(wrow, row_ok, s, g, arow0, a_ok0, asel);
-    };
-    // Weight and code loads first: nothing below waits on them until the first compute.
-    S b0, b1;
-    const int64_t s0 = wave, s1 = wave + nwaves;
-    if (s0 < nsteps) do_load(b0, s0);
-    if (NB == 2 && s1 < nsteps) do_load(b1, s1);
+    MvLane L;
+    L.g = lane >> 4;
+    L.r16 = lane & 15;
+    const int64_t row = row0 + L.r16;
+    const int64_t rclamp = row < rows ? row : rows - 1;
+    L.wrow_off = (uint32_t)((rclamp - row0) * row_bytes);
+    const int m = L.r16;
+    S::lane_setup(L, m);
+#pragma unroll
+    for (int cg = 0; cg < 2; ++cg) {
+        const int c = S::a_col(m, cg);
+        const bool on = (cg < NCG) && S::a_diag(L.g, m) && c < ncols;
+        L.abase[cg] = on ? xq + mc.arow(c) * nb * kQ8_1Bytes : (const uint8_t *)mv_zero16;
+        L.astride[cg] = on ? 8 * kQ8_1Bytes : 0;
+        if (!on)
+            for (int j = 0; j < 4; ++j) L.aoff[cg][j] = 0;
+    }
 
     // Stage the fp32 (d, s) of the workgroup's columns from their q8_1 blocks: sTab[block][column].
     if (!DBG) {
@@ -337,33 +395,39 @@ __global__ __launch_bounds__(NB == 1 ? 1024 : 512) void mmvq_kernel(
         for (int e = 0; e < 4; ++e) acc[cg][e] = 0.f;
 
     int32_t *dbg_row = nullptr;
-    int dbg_ld = 0;
-    if (DBG && row_ok) {
-        const int per = (T == kQ6_K) ? (int)(k / 16) : (int)nb;
-        dbg_ld = (int)(rows * per);
+    int64_t dbg_ld = 0;
+    if (DBG && row < rows) {
+        const int64_t per = (T == kQ6_K) ? k / 16 : nb;
+        dbg_ld = rows * per;
         dbg_row = dbg + row * per;
     }
-    auto do_compute = [&](const S &st, int64_t s) {
-        if constexpr (T == kQ8_0) st.template compute<DBG>(s, g, sTab, acc, dbg_row, dbg_ld, ncols, nb);
-        else st.template compute<DBG>(s, g, sTab, acc, dbg_row, dbg_ld, ncols);
-    };
-    __syncthreads();
-    if (NB == 1) {
-        if (s0 < nsteps) do_compute(b0, s0);
-    } else {
-        for (int64_t s = s0; s < nsteps; s += 2 * nwaves) {
-            do_compute(b0, s);
-            if (s + 2 * nwaves < nsteps) do_load(b0, s + 2 * nwaves);
-            if (s + nwaves < nsteps) {
-                do_compute(b1, s + nwaves);
-                if (s + 3 * nwaves < nsteps) do_load(b1, s + 3 * nwaves);
+
+    // Passes of SPW steps per wave; within a pass every load is issued before the first math.
+    bool synced = false;
+    for (int64_t base = 0; base < nsteps; base += (int64_t)SPW * nwaves) {
+        S st[SPW];
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            const int64_t s = base + wave + (int64_t)i * nwaves;
+            if (s < nsteps) {
+                if constexpr (T == kQ8_0) st[i].load(wg, L, s, nb);
+                else st[i].load(wg, L, s);
+            }
+        }
+        if (!synced) { __syncthreads(); synced = true; }   // scale table ready
+#pragma unroll
+        for (int i = 0; i < SPW; ++i) {
+            const int64_t s = base + wave + (int64_t)i * nwaves;
+            if (s < nsteps) {
+                if constexpr (T == kQ8_0) st[i].template compute<DBG>(s, L, sTab, acc, dbg_row, dbg_ld, ncols, nb);
+                else st[i].template compute<DBG>(s, L, sTab, acc, dbg_row, dbg_ld, ncols);
             }
         }
     }
     if (DBG) return;
 
-    // Combine the sub-block slots held by lane groups: Q4_K/Q8_0 lanes g and g^2 (sub-blocks
-    // 2p and 2p+1), Q6_K lanes g = 0..3 (the four 16-value sub-blocks).
+    // Combine the sub-block slots held by lane groups: Q4_K/Q8_0 lanes g and g^2 (the two halves
+    // of the block diagonal), Q6_K lanes g = 0..3 (the four 16-value sub-blocks).
 #pragma unroll
     for (int cg = 0; cg < NCG; ++cg)
 #pragma unroll
@@ -375,7 +439,7 @@ __global__ __launch_bounds__(NB == 1 ? 1024 : 512) void mmvq_kernel(
         }
     // Lanes holding the wave's values: Q4_K/Q8_0 g in {0,1} (columns 4g..4g+3), Q6_K g == 0
     // (columns 4cg..4cg+3); 128 floats per wave.
-    const bool holder = (T == kQ6_K) ? (g == 0) : (g < 2);
+    const bool holder = (T == kQ6_K) ? (L.g == 0) : (L.g < 2);
     if (holder) {
 #pragma unroll
         for (int cg = 0; cg < NCG; ++cg)
@@ -383,52 +447,53 @@ __global__ __launch_bounds__(NB == 1 ? 1024 : 512) void mmvq_kernel(
             for (int e = 0; e < 4; ++e) sRed[wave * 128 + lane * (4 * NCG) + cg * 4 + e] = acc[cg][e];
     }
     __syncthreads();
-    if (wave != 0 || !holder || !row_ok) return;
+    if (wave != 0 || !holder || row >= rows) return;
 #pragma unroll
     for (int cg = 0; cg < NCG; ++cg)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float v = 0.f;
             for (int wv = 0; wv < nwaves; ++wv) v += sRed[wv * 128 + lane * (4 * NCG) + cg * 4 + e];
-            const int c = (T == kQ6_K) ? 4 * cg + e : 4 * g + e;
+            const int c = (T == kQ6_K) ? 4 * cg + e : 4 * L.g + e;
             if (c < ncols) y[mc.pair(c) * rows + row] = v;
         }
+}
+
+static int g_mv_spw = 0;   // 0: automatic
+
+template <int T, int SPW, bool DBG, bool EXPERT>
+static hipError_t launch_mmvq_spw(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y,
+                                  int32_t *dbg, const ColMap &c, int64_t n_exp, hipStream_t s) {
+    const int64_t nsteps = (k + kSuper - 1) / kSuper;
+    int64_t nw = (nsteps + SPW - 1) / SPW;
+    if (nw > mv_max_waves(SPW)) nw = mv_max_waves(SPW);
+    if (nw < 1) nw = 1;
+    dim3 grid((unsigned)((rows + kMvRows - 1) / kMvRows), EXPERT ? (unsigned)n_exp : 1u);
+    const size_t smem = (size_t)(k / 32) * 8 * sizeof(float2) + (size_t)nw * 128 * sizeof(float);
+    static bool attr = false;
+    if (!attr) {
+        hipError_t e = hipFuncSetAttribute((const void *)mmvq_kernel<T, SPW, DBG, EXPERT>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (e != hipSuccess) return e;
+        attr = true;
+    }
+    hipLaunchKernelGGL((mmvq_kernel<T, SPW, DBG, EXPERT>), grid, dim3(64 * (unsigned)nw), smem, s, w, rows, k, xq, n,
+                       y, dbg, c);
+    return hipGetLastError();
 }
 
 template <int T, bool DBG, bool EXPERT>
 static hipError_t launch_mmvq_t(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y,
                                 int32_t *dbg, const ColMap *cm, int64_t n_exp, hipStream_t s) {
-    const int64_t nsteps = (k + kSuper - 1) / kSuper;
     ColMap c = cm ? *cm : ColMap{};
-    dim3 grid((unsigned)((rows + kMvRows - 1) / kMvRows), EXPERT ? (unsigned)n_exp : 1u);
-    const size_t smem_tab = (size_t)(k / 32) * 8 * sizeof(float2);
-    if (nsteps <= kMvMaxWaves1) {
-        const int nw = (int)nsteps;
-        const size_t smem = smem_tab + (size_t)nw * 128 * sizeof(float);
-        static bool attr1 = false;
-        if (!attr1) {
-            hipError_t e = hipFuncSetAttribute((const void *)mmvq_kernel<T, DBG, EXPERT, 1>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-            if (e != hipSuccess) return e;
-            attr1 = true;
-        }
-        hipLaunchKernelGGL((mmvq_kernel<T, DBG, EXPERT, 1>), grid, dim3(64 * nw), smem, s, w, rows, k, xq, n, y,
-                           dbg, c);
-    } else {
-        const int nw = kMvMaxWaves2;
-        const size_t smem = smem_tab + (size_t)nw * 128 * sizeof(float);
-        static bool attr2 = false;
-        if (!attr2) {
-            hipError_t e = hipFuncSetAttribute((const void *)mmvq_kernel<T, DBG, EXPERT, 2>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-            if (e != hipSuccess) return e;
-            attr2 = true;
-        }
-        hipLaunchKernelGGL((mmvq_kernel<T, DBG, EXPERT, 2>), grid, dim3(64 * nw), smem, s, w, rows, k, xq, n, y,
-                           dbg, c);
-    }
-    return hipGetLastError();
+    int spw = g_mv_spw;
+    if (spw == 0) spw = 2;
+    if (spw == 1) return launch_mmvq_spw<T, 1, DBG, EXPERT>(w, rows, k, xq, n, y, dbg, c, n_exp, s);
+    if (spw == 4) return launch_mmvq_spw<T, 4, DBG, EXPERT>(w, rows, k, xq, n, y, dbg, c, n_exp, s);
+    return launch_mmvq_spw<T, 2, DBG, EXPERT>(w, rows, k, xq, n, y, dbg, c, n_exp, s);
 }
+
+void set_mmvq_steps_per_wave(int spw) { g_mv_spw = spw; }
 
 hipError_t launch_mmvq(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y,
                        int32_t *dbg, const ColMap *cm, int64_t n_exp, hipStream_t s) {

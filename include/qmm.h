@@ -130,9 +130,10 @@ qmm_status qmm_debug_subdots(int type, const void *w, int64_t rows, int64_t k, c
  *   QMM_OVR_PATH:     1 force matrix-vector (only when n <= 8), 2 force tiled MFMA.
  *   QMM_OVR_STREAMK:  1 force off, 2 force on (tiled path).
  *   QMM_OVR_TILE_J:   tile width in columns (32, 64 or 128).
+ *   QMM_OVR_MV_STEPS: 256-value steps per wave in the matrix-vector kernel (1, 2 or 4).
  * Returns QMM_ERR_ARG for an unknown key or value.
  * ------------------------------------------------------------------------------------------- */
-enum { QMM_OVR_PATH = 1, QMM_OVR_STREAMK = 2, QMM_OVR_TILE_J = 3 };
+enum { QMM_OVR_PATH = 1, QMM_OVR_STREAMK = 2, QMM_OVR_TILE_J = 3, QMM_OVR_MV_STEPS = 4 };
 qmm_status qmm_set_override(int key, int value);
 
 /* ---------------------------------------------------------------------------------------------

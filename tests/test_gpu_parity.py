@@ -23,7 +23,7 @@ TNAME = {qmm.Q4_K: "q4_K", qmm.Q6_K: "q6_K", qmm.Q8_0: "q8_0"}
 
 
 def _reset_overrides():
-    for key in (qmm.OVR_PATH, qmm.OVR_STREAMK, qmm.OVR_TILE_J):
+    for key in (qmm.OVR_PATH, qmm.OVR_STREAMK, qmm.OVR_TILE_J, qmm.OVR_MV_STEPS):
         qmm.set_override(key, 0)
 
 
@@ -141,6 +141,21 @@ def test_dense_single_block_k(qtype):
 def test_matvec_workload_full(qtype, n):
     """The matrix-vector workload at full size: 4096 x 4096, every output compared."""
     _full_check(qtype, 4096, 4096, n, 500 + n, f"{TNAME[qtype]} 4096^2 n={n}")
+
+
+@pytest.mark.parametrize("spw", [1, 2, 4])
+@pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
+def test_matvec_steps_per_wave(qtype, spw):
+    """Every steps-per-wave variant of the matrix-vector kernel, on a K that leaves a partial
+    pass (several passes for one step per wave) and ragged rows, against the oracle."""
+    qmm.set_override(qmm.OVR_MV_STEPS, spw)
+    k = 2080 if qmm.Q8_0 == qtype else 4352
+    for n in (1, 6):
+        _full_check(qtype, 77, k, n, 470 + spw + n, f"{TNAME[qtype]} spw={spw} n={n}")
+    w, x = _case(qtype, 77, k, 5, 480 + spw)
+    xq = oracle.quantize_q8_1(x)
+    got = qmm.debug_subdots(to_dev(w), qtype, 77, k, to_dev(xq), 5, qmm.PATH_MATVEC).cpu().numpy()
+    assert np.array_equal(got, oracle.subdots(qtype, w, 77, k, xq, 5))
 
 
 def test_matmul_q8_1_entry_matches_matmul():
