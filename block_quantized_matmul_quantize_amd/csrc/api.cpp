@@ -137,6 +137,9 @@ qmm_status qmm_set_override(int key, int value) {
             if (value != 0 && value != 1 && value != 2 && value != 4)
                 return fail(QMM_ERR_ARG, "steps-per-wave override must be 0, 1, 2 or 4");
             qmm::set_mmvq_steps_per_wave(value); return QMM_OK;
+        case QMM_OVR_MV_KERNEL:
+            if (value < 0 || value > 3) return fail(QMM_ERR_ARG, "matrix-vector kernel override must be 0..3");
+            qmm::set_mmvq_kernel(value); return QMM_OK;
         default:
             return fail(QMM_ERR_ARG, "unknown override key %d", key);
     }

@@ -27,8 +27,23 @@ struct ColMap {
 hipError_t launch_mmvq(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n,
                        float *y, int32_t *dbg, const ColMap *cm, int64_t n_exp, hipStream_t s);
 
-// Tuning: 256-value steps per wave of the matrix-vector kernel (0 = automatic).
+// Tuning: 256-value steps per wave of the register-streamed matrix-vector kernel (0 = automatic).
 void set_mmvq_steps_per_wave(int spw);
+// Matrix-vector kernel choice: 0 automatic (dot4 for few columns, else LDS-staged MFMA, where
+// supported), 1 register-streamed, 2 LDS-staged MFMA only, 3 dot4 only (launch_mmvq fails where
+// the forced kernel is unsupported).
+void set_mmvq_kernel(int which);
+// LDS-streamed matrix-vector kernel (mmvq_stream.hip): 16-byte aligned weights, activations and
+// rows, K a multiple of 256.
+bool mmvq_stream_supported(int type, const void *w, int64_t k, const void *xq, const ColMap *cm);
+hipError_t launch_mmvq_stream(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n,
+                              float *y, int32_t *dbg, const ColMap *cm, int64_t n_exp, hipStream_t s);
+// dot4 matrix-vector kernel (mmvq_dot4.hip) for 1..mmvq_dot4_max_cols() dense columns: Q4_K and
+// Q8_0, K a multiple of 256.
+int mmvq_dot4_max_cols();
+bool mmvq_dot4_supported(int type, const void *w, int64_t k, const void *xq, const ColMap *cm);
+hipError_t launch_mmvq_dot4(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n,
+                            float *y, int32_t *dbg, const ColMap *cm, int64_t n_exp, int max_cols, hipStream_t s);
 
 // Tiled int8-MFMA kernel plan.
 struct MmqLaunch {

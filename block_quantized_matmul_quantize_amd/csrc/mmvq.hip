@@ -24,6 +24,7 @@
 // Partial sums are combined with lane shuffles, then across waves in LDS in a fixed order.
 #include "common.hpp"
 #include "launch.hpp"
+#include "mv_cols.hpp"
 
 namespace qmm {
 
@@ -295,41 +296,6 @@ template <> struct MvStep<kQ8_0> {
     }
 };
 
-// Resolve the workgroup's columns: dense -> column c is activation row c and output row c;
-// expert mode -> expert small[blockIdx.y], columns are its (token, slot) pairs.
-struct MvCols {
-    int ncols;
-    int lo;
-    const uint8_t *wbase;
-    bool expert;
-    ColMap cm;
-    __device__ __forceinline__ int64_t pair(int c) const { return expert ? cm.sorted[lo + c] : c; }
-    __device__ __forceinline__ int64_t arow(int c) const {
-        if (!expert) return c;
-        const int64_t pr = cm.sorted[lo + c];
-        const int64_t t = pr / cm.top_k, s = pr - t * cm.top_k;
-        return t * cm.x_per_tok + (cm.x_per_tok > 1 ? s : 0);
-    }
-};
-
-__device__ __forceinline__ bool mv_resolve(MvCols &mc, const uint8_t *w, int64_t n, const ColMap &cm,
-                                           bool expert) {
-    mc.wbase = w;
-    mc.expert = expert;
-    mc.cm = cm;
-    mc.lo = 0;
-    if (!expert) {
-        mc.ncols = (int)n;
-        return true;
-    }
-    const int e = cm.small[blockIdx.y];
-    if (e < 0) return false;
-    mc.lo = cm.bounds[e];
-    mc.ncols = cm.bounds[e + 1] - mc.lo;
-    mc.wbase = w + (int64_t)e * cm.w_expert_stride;
-    return true;
-}
-
 constexpr int mv_max_waves(int spw) { return spw == 1 ? 16 : spw == 2 ? 8 : 4; }
 
 template <int T, int SPW, bool DBG, bool EXPERT>
@@ -495,8 +461,26 @@ static hipError_t launch_mmvq_t(const uint8_t *w, int64_t rows, int64_t k, const
 
 void set_mmvq_steps_per_wave(int spw) { g_mv_spw = spw; }
 
+// 0: automatic, 1: this file's register-streamed kernel, 2: LDS-staged MFMA kernel, 3: dot4 kernel
+static int g_mv_kernel = 0;
+
+void set_mmvq_kernel(int which) { g_mv_kernel = which; }
+
+// Largest column count the automatic choice sends to the dot4 kernel, per type.
+static int dot4_auto_cols(int type) { return type == kQ4_K ? 2 : type == kQ8_0 ? 3 : 0; }
+
 hipError_t launch_mmvq(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y,
                        int32_t *dbg, const ColMap *cm, int64_t n_exp, hipStream_t s) {
+    const int kc = g_mv_kernel;
+    if (kc == 3 || kc == 0) {
+        const int lim = kc == 3 ? mmvq_dot4_max_cols() : dot4_auto_cols(type);
+        if (!cm && n <= lim && mmvq_dot4_supported(type, w, k, xq, cm))
+            return launch_mmvq_dot4(type, w, rows, k, xq, n, y, dbg, cm, n_exp, (int)n, s);
+        if (kc == 3) return hipErrorInvalidValue;
+    }
+    if (kc != 1 && mmvq_stream_supported(type, w, k, xq, cm))
+        return launch_mmvq_stream(type, w, rows, k, xq, n, y, dbg, cm, n_exp, s);
+    if (kc == 2) return hipErrorInvalidValue;
     const bool expert = cm != nullptr;
     const bool d = dbg != nullptr;
 #define QMM_MV(TT)                                                                                       \

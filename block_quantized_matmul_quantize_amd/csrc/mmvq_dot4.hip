@@ -1,0 +1,296 @@
+// Matrix-vector product for 1..3 activation columns with v_dot4_i32_i8 (the MMVQ regime of the
+// MMQ page: "shape criteria" and the MMVQ-vs-MMQ table; "dp4a path Q4_K" section for the per
+// sub-block dot and its d*sc / dmin*m*s fixup).
+//
+// With one to three columns a block-diagonal MFMA would spend most of its per-result fp32 fixups
+// on empty columns, so this kernel works on the vector ALU and does exactly the useful work.
+// A workgroup owns 16 weight rows; wave w takes the 256-value steps w, w+W, ... (up to 16 waves).
+// Lane 4r+g holds row r and the quarter g of the step: values 64g..64g+63, i.e. the two 32-value
+// sub-blocks 2g and 2g+1 -- for Q4_K the 32 qs bytes 32g..32g+31 (low nibbles sub-block 2g, high
+// nibbles 2g+1), for Q8_0 the two 34-byte blocks.  Consecutive lanes of a row read consecutive
+// bytes, so each quarter-wave load touches one or two cache lines.  The columns' q8_1 codes and
+// fp32 (d, s) are staged once per workgroup in LDS; every lane with the same quarter reads the
+// same LDS words (a broadcast).  Next step's weights load while this step computes.
+//   Q4_K  acc += D(2g)*(d*sc)*d_a - (dmin*m)*s_a   (+ the same for sub-block 2g+1)
+//   Q8_0  acc += D*d_w*d_a                         (both blocks)
+// The four quarters of a row are summed with lane shuffles, the waves in LDS in a fixed order.
+// Requirements (checked by the host): K a multiple of 256; Q4_K weights and rows 16-byte
+// aligned, Q8_0 4-byte aligned; activations 4-byte aligned.
+#include "common.hpp"
+#include "launch.hpp"
+#include "mv_cols.hpp"
+
+namespace qmm {
+
+namespace {
+
+constexpr int kRows = 16;
+typedef u32x4 __attribute__((aligned(4))) u32x4_a4;
+
+struct D4Args {
+    int64_t rows;
+    uint32_t row_bytes;   // weight bytes per row
+    uint32_t nb;          // q8_1 blocks per activation row (k / 32)
+    int32_t nsteps;       // 256-value steps (k / 256)
+    int32_t q, r;         // steps per wave: q, plus one for waves < r
+    int32_t n;            // dense column count
+};
+
+__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int c) {
+    return __builtin_amdgcn_sdot4((int)a, (int)b, c, false);
+}
+
+// Per-lane weight registers of one step.
+template <int T> struct W4;
+template <> struct W4<kQ4_K> {
+    u32x4 h, q0, q1;   // header (d, dmin, scales) and qs bytes 32g..32g+31
+    __device__ __forceinline__ void load(const uint8_t *base, uint32_t off, int g) {
+        h = *(const u32x4 *)(base + off);
+        q0 = *(const u32x4 *)(base + off + 16 + 32 * g);
+        q1 = *(const u32x4 *)(base + off + 32 + 32 * g);
+    }
+};
+template <> struct W4<kQ8_0> {
+    u32x4 v0, v1, v2, v3;   // bytes 68g..68g+63 of the step: {d0, q0[32], d1, q1[0..29]}
+    uint32_t v4;            // bytes 68g+64..68g+67: q1[30..31] ... (the last 4 bytes)
+    __device__ __forceinline__ void load(const uint8_t *base, uint32_t off, int g) {
+        const uint8_t *p = base + off + 68 * g;
+        v0 = *(const u32x4_a4 *)(p);
+        v1 = *(const u32x4_a4 *)(p + 16);
+        v2 = *(const u32x4_a4 *)(p + 32);
+        v3 = *(const u32x4_a4 *)(p + 48);
+        v4 = *(const uint32_t *)(p + 64);
+    }
+};
+template <int T> struct StepBytes;
+template <> struct StepBytes<kQ4_K> { static constexpr int V = 144; };
+template <> struct StepBytes<kQ8_0> { static constexpr int V = 272; };
+
+template <int T, int NC, bool DBG, bool EXPERT>
+__global__ __launch_bounds__(1024) void mmvq_dot4_kernel(const uint8_t *__restrict__ w, const uint8_t *__restrict__ xq,
+                                                        float *__restrict__ y, int32_t *__restrict__ dbg, D4Args P,
+                                                        ColMap cm) {
+    extern __shared__ __align__(16) uint8_t smem[];
+    MvCols mc;
+    if (!mv_resolve(mc, w, P.n, cm, EXPERT)) return;   // workgroup-uniform
+    const int ncols = mc.ncols;                           // 1..NC
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int nwaves = blockDim.x >> 6;
+    const int r = lane >> 2, g = lane & 3;
+    const int64_t rows = P.rows;
+    const uint32_t nb = P.nb;
+    const int64_t row0 = (int64_t)blockIdx.x * kRows;
+    const int rmax = (int)((rows - row0) < kRows ? (rows - row0) : kRows) - 1;
+    const uint8_t *wg = mc.wbase + row0 * (int64_t)P.row_bytes;
+    const uint32_t woff = (uint32_t)(r < rmax ? r : rmax) * P.row_bytes;   // rows past the end re-read the last
+    const int my_steps = P.q + (wave < P.r ? 1 : 0);
+
+    W4<T> cur;
+    if (my_steps > 0) cur.load(wg + wave * StepBytes<T>::V, woff, g);
+
+    // Stage the columns' q8_1 codes ([NC][nb][32 B]) and fp32 (d, s) ([NC][nb]) in LDS.
+    uint8_t *acodes = smem;
+    float2 *aft = (float2 *)(smem + (size_t)NC * nb * 32);
+    float *red = (float *)(smem + (size_t)NC * nb * 40);   // [nwaves][16 * NC]
+    for (int c = 0; c < ncols; ++c) {
+        const uint8_t *xrow = xq + mc.arow(c) * (int64_t)nb * kQ8_1Bytes;
+        for (uint32_t b = threadIdx.x; b < nb; b += blockDim.x) {
+            const uint8_t *src = xrow + (size_t)b * kQ8_1Bytes;
+            const uint32_t ds = *(const uint32_t *)src;
+            const u32x4 c0 = *(const u32x4_a4 *)(src + 4);
+            const u32x4 c1 = *(const u32x4_a4 *)(src + 20);
+            uint8_t *dst = acodes + ((size_t)c * nb + b) * 32;
+            *(u32x4 *)dst = c0;
+            *(u32x4 *)(dst + 16) = c1;
+            aft[(size_t)c * nb + b] = make_float2(h2f((uint16_t)(ds & 0xFFFF)), h2f((uint16_t)(ds >> 16)));
+        }
+    }
+    __syncthreads();
+
+    float acc[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[c] = 0.f;
+    int32_t *dbg_row = nullptr;
+    int64_t dbg_ld = 0;
+    if (DBG && row0 + r < rows) {
+        dbg_ld = rows * (int64_t)nb;
+        dbg_row = dbg + (row0 + r) * (int64_t)nb;
+    }
+
+    for (int it = 0; it < my_steps; ++it) {
+        const int s = wave + it * nwaves;
+        const W4<T> x = cur;
+        if (it + 1 < my_steps) cur.load(wg + (s + nwaves) * StepBytes<T>::V, woff, g);   // next step in flight
+        const uint32_t b0 = 8 * s + 2 * g;   // q8_1 block of sub-block 2g
+
+        if constexpr (T == kQ4_K) {
+            const float d = h2f((uint16_t)(x.h.x & 0xFFFF));
+            const float dmin = h2f((uint16_t)(x.h.x >> 16));
+            // 6-bit scale / min of sub-blocks 2g, 2g+1 in bytes 0, 1: sub-blocks 0-3 sit in the low
+            // 6 bits of scale bytes 0-3 / 4-7, sub-blocks 4-7 in the nibbles of bytes 8-11 with
+            // their top 2 bits in the top bits of bytes 0-3 / 4-7.
+            const uint32_t sc_a = x.h.y & 0x3F3F3F3Fu, m_a = x.h.z & 0x3F3F3F3Fu;
+            const uint32_t sc_b = (x.h.w & 0x0F0F0F0Fu) | ((x.h.y >> 2) & 0x30303030u);
+            const uint32_t m_b = ((x.h.w >> 4) & 0x0F0F0F0Fu) | ((x.h.z >> 2) & 0x30303030u);
+            const int sh = 16 * (g & 1);
+            const uint32_t scp = (g < 2 ? sc_a : sc_b) >> sh, mp = (g < 2 ? m_a : m_b) >> sh;
+            const float ws0 = d * (float)(scp & 0xFF), ws1 = d * (float)((scp >> 8) & 0xFF);
+            const float wm0 = dmin * (float)(mp & 0xFF), wm1 = dmin * (float)((mp >> 8) & 0xFF);
+            const uint32_t qv[8] = {x.q0.x, x.q0.y, x.q0.z, x.q0.w, x.q1.x, x.q1.y, x.q1.z, x.q1.w};
+            uint32_t lo[8], hi[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                lo[i] = qv[i] & 0x0F0F0F0Fu;
+                hi[i] = (qv[i] >> 4) & 0x0F0F0F0Fu;
+            }
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                if (c >= ncols) break;
+                const uint8_t *ab = acodes + ((size_t)c * nb + b0) * 32;
+                const u32x4 a0 = *(const u32x4 *)ab, a1 = *(const u32x4 *)(ab + 16);
+                const u32x4 a2 = *(const u32x4 *)(ab + 32), a3 = *(const u32x4 *)(ab + 48);
+                int D0 = 0, D1 = 0;
+                D0 = dot4(lo[0], a0.x, D0); D0 = dot4(lo[1], a0.y, D0); D0 = dot4(lo[2], a0.z, D0); D0 = dot4(lo[3], a0.w, D0);
+                D0 = dot4(lo[4], a1.x, D0); D0 = dot4(lo[5], a1.y, D0); D0 = dot4(lo[6], a1.z, D0); D0 = dot4(lo[7], a1.w, D0);
+                D1 = dot4(hi[0], a2.x, D1); D1 = dot4(hi[1], a2.y, D1); D1 = dot4(hi[2], a2.z, D1); D1 = dot4(hi[3], a2.w, D1);
+                D1 = dot4(hi[4], a3.x, D1); D1 = dot4(hi[5], a3.y, D1); D1 = dot4(hi[6], a3.z, D1); D1 = dot4(hi[7], a3.w, D1);
+                if (DBG) {
+                    if (dbg_row) {
+                        dbg_row[(int64_t)c * dbg_ld + b0] = D0;
+                        dbg_row[(int64_t)c * dbg_ld + b0 + 1] = D1;
+                    }
+                } else {
+                    const f32x4 f = *(const f32x4 *)(aft + (size_t)c * nb + b0);   // d0, s0, d1, s1
+                    float a = acc[c];
+                    a = fmaf((float)D0, ws0 * f.x, a);
+                    a = fmaf(-wm0, f.y, a);
+                    a = fmaf((float)D1, ws1 * f.z, a);
+                    a = fmaf(-wm1, f.w, a);
+                    acc[c] = a;
+                }
+            }
+        } else {
+            // bytes 0-1: d0; 2-33: q0; 34-35: d1; 36-67: q1 -> q0 realigned by two bytes
+            const uint32_t v[17] = {x.v0.x, x.v0.y, x.v0.z, x.v0.w, x.v1.x, x.v1.y, x.v1.z, x.v1.w,
+                                    x.v2.x, x.v2.y, x.v2.z, x.v2.w, x.v3.x, x.v3.y, x.v3.z, x.v3.w, x.v4};
+            uint32_t q0[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) q0[i] = __builtin_amdgcn_alignbyte(v[i + 1], v[i], 2);
+            const float dw0 = h2f((uint16_t)(v[0] & 0xFFFF)), dw1 = h2f((uint16_t)(v[8] >> 16));
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                if (c >= ncols) break;
+                const uint8_t *ab = acodes + ((size_t)c * nb + b0) * 32;
+                const u32x4 a0 = *(const u32x4 *)ab, a1 = *(const u32x4 *)(ab + 16);
+                const u32x4 a2 = *(const u32x4 *)(ab + 32), a3 = *(const u32x4 *)(ab + 48);
+                int D0 = 0, D1 = 0;
+                D0 = dot4(q0[0], a0.x, D0); D0 = dot4(q0[1], a0.y, D0); D0 = dot4(q0[2], a0.z, D0); D0 = dot4(q0[3], a0.w, D0);
+                D0 = dot4(q0[4], a1.x, D0); D0 = dot4(q0[5], a1.y, D0); D0 = dot4(q0[6], a1.z, D0); D0 = dot4(q0[7], a1.w, D0);
+                D1 = dot4(v[9], a2.x, D1); D1 = dot4(v[10], a2.y, D1); D1 = dot4(v[11], a2.z, D1); D1 = dot4(v[12], a2.w, D1);
+                D1 = dot4(v[13], a3.x, D1); D1 = dot4(v[14], a3.y, D1); D1 = dot4(v[15], a3.z, D1); D1 = dot4(v[16], a3.w, D1);
+                if (DBG) {
+                    if (dbg_row) {
+                        dbg_row[(int64_t)c * dbg_ld + b0] = D0;
+                        dbg_row[(int64_t)c * dbg_ld + b0 + 1] = D1;
+                    }
+                } else {
+                    const f32x4 f = *(const f32x4 *)(aft + (size_t)c * nb + b0);   // d0, s0, d1, s1
+                    float a = acc[c];
+                    a = fmaf((float)D0, dw0 * f.x, a);
+                    a = fmaf((float)D1, dw1 * f.z, a);
+                    acc[c] = a;
+                }
+            }
+        }
+    }
+    if (DBG) return;
+
+    // Sum the four quarters of each row (lanes 4r..4r+3), then the waves.
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        float v = acc[c];
+        v += __shfl_xor(v, 1);
+        v += __shfl_xor(v, 2);
+        acc[c] = v;
+    }
+    if (g == 0) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) red[wave * (16 * NC) + r * NC + c] = acc[c];
+    }
+    __syncthreads();
+    const int t = threadIdx.x;
+    if (t >= 16 * NC) return;
+    float v = 0.f;
+    for (int wv = 0; wv < nwaves; ++wv) v += red[wv * (16 * NC) + t];
+    const int rr = t / NC, c = t - rr * NC;
+    if (c < ncols && row0 + rr < rows) y[mc.pair(c) * rows + row0 + rr] = v;
+}
+
+template <int T, int NC, bool DBG, bool EXPERT>
+hipError_t launch_nc(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y, int32_t *dbg,
+                     const ColMap &cm, int64_t n_exp, hipStream_t s) {
+    const int64_t nsteps = k / kSuper;
+    const int nw = (int)(nsteps < 16 ? nsteps : 16);
+    D4Args a;
+    a.rows = rows;
+    a.row_bytes = (uint32_t)((k / Fmt<T>::QK) * Fmt<T>::BYTES);
+    a.nb = (uint32_t)(k / 32);
+    a.nsteps = (int32_t)nsteps;
+    a.q = (int32_t)(nsteps / nw);
+    a.r = (int32_t)(nsteps % nw);
+    a.n = (int32_t)n;
+    const size_t smem = (size_t)NC * a.nb * 40 + (size_t)nw * 16 * NC * sizeof(float);
+    static bool attr = false;
+    if (!attr) {
+        hipError_t e = hipFuncSetAttribute((const void *)mmvq_dot4_kernel<T, NC, DBG, EXPERT>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (e != hipSuccess) return e;
+        attr = true;
+    }
+    dim3 grid((unsigned)((rows + kRows - 1) / kRows), EXPERT ? (unsigned)n_exp : 1u);
+    hipLaunchKernelGGL((mmvq_dot4_kernel<T, NC, DBG, EXPERT>), grid, dim3(64 * (unsigned)nw), smem, s, w, xq, y, dbg, a,
+                       cm);
+    return hipGetLastError();
+}
+
+template <int T, int NC>
+hipError_t dispatch_nc(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y, int32_t *dbg,
+                       const ColMap *cm, int64_t n_exp, hipStream_t s) {
+    const ColMap c = cm ? *cm : ColMap{};
+    if (dbg) return launch_nc<T, NC, true, false>(w, rows, k, xq, n, y, dbg, c, n_exp, s);
+    if (cm) return launch_nc<T, NC, false, true>(w, rows, k, xq, n, y, dbg, c, n_exp, s);
+    return launch_nc<T, NC, false, false>(w, rows, k, xq, n, y, dbg, c, n_exp, s);
+}
+
+template <int T>
+hipError_t dispatch(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y, int32_t *dbg,
+                    const ColMap *cm, int64_t n_exp, int max_cols, hipStream_t s) {
+    if (max_cols <= 1) return dispatch_nc<T, 1>(w, rows, k, xq, n, y, dbg, cm, n_exp, s);
+    if (max_cols == 2) return dispatch_nc<T, 2>(w, rows, k, xq, n, y, dbg, cm, n_exp, s);
+    return dispatch_nc<T, 3>(w, rows, k, xq, n, y, dbg, cm, n_exp, s);
+}
+
+}  // namespace
+
+int mmvq_dot4_max_cols() { return 3; }
+
+bool mmvq_dot4_supported(int type, const void *w, int64_t k, const void *xq, const ColMap *cm) {
+    if (type != kQ4_K && type != kQ8_0) return false;
+    if (k % kSuper != 0 || k < kSuper || k > 32768) return false;
+    const int64_t row_bytes = type == kQ8_0 ? k / 32 * 34 : k / 256 * 144;
+    const int align = type == kQ4_K ? 16 : 4;
+    if (row_bytes % align != 0 || (uintptr_t)w % align != 0) return false;
+    if ((uintptr_t)xq % 4 != 0) return false;
+    if (cm && cm->w_expert_stride % align != 0) return false;
+    return true;
+}
+
+hipError_t launch_mmvq_dot4(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n,
+                            float *y, int32_t *dbg, const ColMap *cm, int64_t n_exp, int max_cols, hipStream_t s) {
+    if (type == kQ4_K) return dispatch<kQ4_K>(w, rows, k, xq, n, y, dbg, cm, n_exp, max_cols, s);
+    if (type == kQ8_0) return dispatch<kQ8_0>(w, rows, k, xq, n, y, dbg, cm, n_exp, max_cols, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace qmm

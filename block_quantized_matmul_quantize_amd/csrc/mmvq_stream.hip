@@ -1,0 +1,425 @@
+// Matrix-vector product for 1..8 activation columns, streamed through LDS (the MMVQ regime of
+// the MMQ page: "shape criteria" and the MMVQ-vs-MMQ table -- decode is bound by how fast the
+// weights stream, every weight byte is read once and serves all columns).
+//
+// CDNA4 design.  A workgroup owns 16 weight rows; wave w takes the 256-value steps w, w+W, ...
+// (up to 16 waves, so a 4096-wide K gives every wave one step and a CU 16 waves to hide HBM
+// latency with).  For each step the wave loads the 16 rows' bytes of that step, and the step's
+// q8_1 blocks of every column, with coalesced 16-byte loads (consecutive lanes fetch consecutive
+// pieces of one contiguous run, so a quarter-wave touches one cache line), parks them in its own
+// LDS stage, and loads the next step while it computes.  No workgroup barrier in the loop.
+// Operands are then read from LDS in the MFMA lane layout: one v_mfma_i32_16x16x64_i8 per
+// 64-value slice, B = 16 weight rows, A = activations placed block-diagonally over
+// (column, sub-block) so every int32 result is one exact sub-block dot D (the same contraction
+// as the register-streamed kernel in mmvq.hip, which serves the shapes this one does not).
+// Fixups per D in fp32 ("dp4a path Q4_K" section of the MMQ page):
+//   Q4_K  acc += D * (d*sc) * d_a - (dmin*m) * s_a
+//   Q6_K  acc += D * (d*sc) * d_a      (D includes -32 * sum q_a via a second MFMA)
+//   Q8_0  acc += D * d_w * d_a
+// Requirements (checked by the host): weights, activations and every row 16-byte aligned, and
+// K a multiple of 256, so each step's pieces are whole 16-byte units inside the row.
+#include "common.hpp"
+#include "launch.hpp"
+#include "mv_cols.hpp"
+
+namespace qmm {
+
+namespace {
+
+constexpr int kRows = 16;
+constexpr int kActStep = 8 * kQ8_1Bytes;   // one column's q8_1 bytes per 256-value step (288)
+
+// Per-type step geometry: PPR 16-byte pieces per row per step (Q6_K: the 16-byte-aligned window
+// around a 210-byte super-block that starts at an even offset -- always 14 pieces), STEP bytes
+// per row per step, RSTR the LDS row stride (16 rows read in one MFMA operand fetch fall in
+// distinct banks).
+template <int T> struct Geo;
+template <> struct Geo<kQ4_K> { static constexpr int PPR = 9, STEP = 144, RSTR = 144; };
+template <> struct Geo<kQ6_K> { static constexpr int PPR = 14, STEP = 210, RSTR = 240; };
+template <> struct Geo<kQ8_0> { static constexpr int PPR = 17, STEP = 272, RSTR = 272; };
+
+template <int T> struct Stage {
+    static constexpr int WB = kRows * Geo<T>::RSTR;   // weights: [row][RSTR]
+    static constexpr int AB = 8 * kActStep;           // activations: [column][288]
+    static constexpr int FB = 64 * 8;                 // fp32 (d, s): [block 0..7][column 0..7]
+    static constexpr int BYTES = WB + AB + FB;
+};
+
+__device__ __forceinline__ uint32_t nib_lo(uint32_t v) { return v & 0x0F0F0F0Fu; }
+__device__ __forceinline__ uint32_t nib_hi(uint32_t v) { return (v >> 4) & 0x0F0F0F0Fu; }
+__device__ __forceinline__ u32x4 nib_lo4(u32x4 v) { return u32x4{nib_lo(v.x), nib_lo(v.y), nib_lo(v.z), nib_lo(v.w)}; }
+__device__ __forceinline__ u32x4 nib_hi4(u32x4 v) { return u32x4{nib_hi(v.x), nib_hi(v.y), nib_hi(v.z), nib_hi(v.w)}; }
+__device__ __forceinline__ u32x4 lds16(const uint8_t *p) { return *(const u32x4_a2 *)p; }
+
+// Q4_K block diagonal (as in mmvq.hip): MFMA j covers sub-blocks {(j>>1)*4 + (j&1) + 2*sel};
+// lanes g in {1,2} carry diagonal half 0, g in {3,0} half 1; g odd holds values 0-15 of its
+// sub-block, g even values 16-31.
+__device__ __forceinline__ int q4_group(int g) { return (g == 1 || g == 2) ? 0 : 1; }
+__device__ __forceinline__ int q4_half(int g) { return (g & 1) ? 0 : 1; }
+__device__ __forceinline__ int q4_sub(int j, int sel) { return (j >> 1) * 4 + (j & 1) + 2 * sel; }
+
+// Launch constants computed on the host (no 64-bit or variable-divisor arithmetic on the GPU).
+struct MvArgs {
+    int64_t rows;
+    uint32_t row_bytes;   // weight bytes per row
+    uint32_t col_bytes;   // q8_1 bytes per activation row (k/32 blocks)
+    int32_t nsteps;       // 256-value steps (k / 256)
+    int32_t q, r;         // steps per wave: q, plus one for waves < r
+    int32_t n;            // dense column count
+};
+
+template <int T, bool DBG, bool EXPERT>
+__global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__restrict__ w, const uint8_t *__restrict__ xq,
+                                                          float *__restrict__ y, int32_t *__restrict__ dbg,
+                                                          MvArgs P, ColMap cm) {
+    using S = Stage<T>;
+    constexpr int PPR = Geo<T>::PPR, RSTR = Geo<T>::RSTR, WB = S::WB, SB = S::BYTES;
+    constexpr int NCG = (T == kQ6_K) ? 2 : 1;
+    extern __shared__ __align__(16) uint8_t smem[];
+
+    MvCols mc;
+    if (!mv_resolve(mc, w, P.n, cm, EXPERT)) return;   // workgroup-uniform
+    const int ncols = mc.ncols;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int nwaves = blockDim.x >> 6;
+    const int64_t rows = P.rows;
+    const uint32_t row_bytes = P.row_bytes, col_bytes = P.col_bytes;
+    const int64_t row0 = (int64_t)blockIdx.x * kRows;
+    const int rmax = (int)((rows - row0) < kRows ? (rows - row0) : kRows) - 1;   // last live row of the group
+    const uint8_t *wg = mc.wbase + row0 * (int64_t)row_bytes;
+    uint8_t *zero = smem + (size_t)wave * (16 + SB);   // 16 zero bytes (off-diagonal A lanes)
+    uint8_t *st = zero + 16;                            // this wave's stage
+    const int my_steps = P.q + (wave < P.r ? 1 : 0);
+
+    // Weight loads: instruction i covers rows 4i..4i+3, 16 lanes per row, lane piece j = lane % 16
+    // (j < PPR); Q8_0's 17th piece of every row comes from a fifth instruction (lanes 0..15).  The
+    // lane's byte offset is the same for every instruction and step; the rest is uniform.
+    constexpr int NIW = PPR > 16 ? 5 : 4;
+    const int rq = lane >> 4, jq = lane & 15;
+    const uint32_t wl = (uint32_t)rq * row_bytes + 16u * jq;
+    const uint32_t pl = (uint32_t)rq * RSTR + 16u * jq;
+    const uint32_t wl16 = (uint32_t)jq * row_bytes + 256u;   // fifth instruction (Q8_0)
+    const uint32_t pl16 = (uint32_t)jq * RSTR + 256u;
+    bool wlive[NIW];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wlive[i] = jq < (PPR < 16 ? PPR : 16) && 4 * i + rq <= rmax;
+    if (NIW == 5) wlive[NIW - 1] = lane < 16 && jq <= rmax;
+
+    u32x4 wv[NIW], av[4];
+    auto load_w = [&](int s) {
+        const uint8_t *wstep = wg + ((uint32_t)(s * Geo<T>::STEP) & ~15u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (wlive[i]) wv[i] = *(const u32x4 *)(wstep + (size_t)(4 * i) * row_bytes + wl);
+        if (NIW == 5 && wlive[NIW - 1]) wv[NIW - 1] = *(const u32x4 *)(wstep + wl16);
+    };
+    if (my_steps > 0) load_w(wave);
+
+    // Activation loads: instruction i covers columns 2i, 2i+1, 32 lanes per column, lane piece
+    // j = lane % 32 (j < 18: a column's 288 bytes of the step).
+    const int cq = lane >> 5, ja = lane & 31;
+    const int nia = (ncols + 1) >> 1;
+    int64_t aoff[4];
+    bool alive[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int c = 2 * i + cq;
+        alive[i] = ja < 18 && c < ncols;
+        aoff[i] = EXPERT ? (alive[i] ? mc.arow(c) * (int64_t)col_bytes : 0) + 16 * ja
+                         : (int64_t)c * col_bytes + 16 * ja;
+    }
+    const uint32_t pa = (uint32_t)cq * kActStep + 16u * ja;
+    auto load_a = [&](int s) {
+        const uint8_t *astep = xq + (uint32_t)(s * kActStep);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (i < nia && alive[i]) av[i] = *(const u32x4 *)(astep + aoff[i]);
+    };
+    if (my_steps > 0) load_a(wave);
+
+    auto park = [&]() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (wlive[i]) *(u32x4 *)(st + 4 * i * RSTR + pl) = wv[i];
+        if (NIW == 5 && wlive[NIW - 1]) *(u32x4 *)(st + pl16) = wv[NIW - 1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (i < nia && alive[i]) *(u32x4 *)(st + WB + 2 * i * kActStep + pa) = av[i];
+    };
+    if (lane < 4) ((uint32_t *)zero)[lane] = 0u;       // read only by this wave
+
+    // Per-lane operand addresses (offsets within a stage).
+    const int g = lane >> 4, r16 = lane & 15;
+    const int m = r16;   // this lane's A row
+    const int wrow = r16 * RSTR;
+    uint32_t a_off[NCG][4];   // activation operand offsets, 0xFFFFFFFF = zero block
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            int c, blk, half;
+            bool on;
+            if (T == kQ4_K) {
+                const int sel = m >> 3;
+                c = m & 7;
+                on = q4_group(g) == sel;
+                blk = q4_sub(j, sel);
+                half = q4_half(g);
+            } else if (T == kQ6_K) {
+                const int grp = m >> 2;
+                c = (m & 3) + 4 * cg;
+                on = g == grp;
+                blk = 2 * j + (grp >> 1);
+                half = grp & 1;
+            } else {
+                const int sel = m >> 3;
+                c = m & 7;
+                on = (g >> 1) == sel;
+                blk = 2 * j + sel;
+                half = g & 1;
+            }
+            on = on && c < ncols;
+            a_off[cg][j] = on ? (uint32_t)(WB + c * kActStep + blk * kQ8_1Bytes + 4 + 16 * half) : 0xFFFFFFFFu;
+        }
+
+    float acc[NCG][4];
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[cg][e] = 0.f;
+
+    int32_t *dbg_row = nullptr;
+    int64_t dbg_ld = 0;
+    const int64_t row = row0 + r16;
+    if (DBG && row < rows) {
+        const int64_t per = (T == kQ6_K) ? (int64_t)P.nsteps * 16 : (int64_t)P.nsteps * 8;
+        dbg_ld = rows * per;
+        dbg_row = dbg + row * per;
+    }
+    const i32x4 zero4 = {0, 0, 0, 0};
+
+    for (int it = 0; it < my_steps; ++it) {
+        const int s = wave + it * nwaves;
+        park();
+        if (it + 1 < my_steps) {   // the next step's loads fly during this step's math
+            load_w(s + nwaves);
+            load_a(s + nwaves);
+        }
+
+        const float2 *ftab = (const float2 *)(st + WB + S::AB);
+        if (!DBG) {
+            // fp32 (d, s) of the step's 8 blocks x 8 columns; columns past ncols read as zero.
+            const int b = lane >> 3, c = lane & 7;
+            float2 v = make_float2(0.f, 0.f);
+            if (c < ncols) {
+                const uint32_t ds = *(const uint32_t *)(st + WB + c * kActStep + b * kQ8_1Bytes);
+                v = make_float2(h2f((uint16_t)(ds & 0xFFFF)), h2f((uint16_t)(ds >> 16)));
+            }
+            ((float2 *)(st + WB + S::AB))[lane] = v;
+        }
+        auto aop = [&](int cg, int j) -> u32x4 {
+            const uint32_t o = a_off[cg][j];
+            return lds16(o == 0xFFFFFFFFu ? zero : st + o);
+        };
+        if constexpr (T == kQ4_K) {
+            const uint8_t *wr = st + wrow;
+            const u32x4 hdr = lds16(wr);
+            const u32x4 src1 = lds16(wr + 16 * (g ? g : 4));
+            const u32x4 src2 = lds16(wr + 16 * (g ? 4 + g : 8));
+            const int sel = g >> 1;
+            const float d = h2f((uint16_t)(hdr.x & 0xFFFF));
+            const float dmin = h2f((uint16_t)(hdr.x >> 16));
+            const uint32_t sc_lo = (hdr.y & 0x3F3F3F3Fu) >> (16 * sel);
+            const uint32_t m_lo = (hdr.z & 0x3F3F3F3Fu) >> (16 * sel);
+            const uint32_t sc_hi = ((hdr.w & 0x0F0F0F0Fu) | ((hdr.y >> 2) & 0x30303030u)) >> (16 * sel);
+            const uint32_t m_hi = (((hdr.w >> 4) & 0x0F0F0F0Fu) | ((hdr.z >> 2) & 0x30303030u)) >> (16 * sel);
+            const u32x4 bop[4] = {nib_lo4(src1), nib_hi4(src1), nib_lo4(src2), nib_hi4(src2)};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const i32x4 D = mfma16x16x64(aop(0, j), bop[j], zero4);
+                const int sb = q4_sub(j, sel);
+                if (DBG) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int c = 4 * (g & 1) + e;
+                        if (dbg_row && c < ncols) dbg_row[(int64_t)c * dbg_ld + s * 8 + sb] = D[e];
+                    }
+                } else {
+                    const uint32_t scw = j < 2 ? sc_lo : sc_hi, mw = j < 2 ? m_lo : m_hi;
+                    const float ws = d * (float)((scw >> (8 * (j & 1))) & 0xFF);
+                    const float wm = dmin * (float)((mw >> (8 * (j & 1))) & 0xFF);
+                    const f32x4 t0 = *(const f32x4 *)(ftab + sb * 8 + 4 * (g & 1));
+                    const f32x4 t1 = *(const f32x4 *)(ftab + sb * 8 + 4 * (g & 1) + 2);
+                    acc[0][0] = fmaf(-wm, t0.y, fmaf((float)D[0], ws * t0.x, acc[0][0]));
+                    acc[0][1] = fmaf(-wm, t0.w, fmaf((float)D[1], ws * t0.z, acc[0][1]));
+                    acc[0][2] = fmaf(-wm, t1.y, fmaf((float)D[2], ws * t1.x, acc[0][2]));
+                    acc[0][3] = fmaf(-wm, t1.w, fmaf((float)D[3], ws * t1.z, acc[0][3]));
+                }
+            }
+        } else if constexpr (T == kQ6_K) {
+            const int a6 = (s * 210) & 15;
+            const uint8_t *wr = st + wrow + a6;
+            const u32x4 ql0 = lds16(wr + 16 * g);
+            const u32x4 ql1 = lds16(wr + 64 + 16 * g);
+            const u32x4 qh0 = lds16(wr + 128 + 16 * (g & 1));   // qh of half 0 for this lane's l range
+            const u32x4 qh1 = lds16(wr + 160 + 16 * (g & 1));   // half 1
+            const u32x4 scv = lds16(wr + 192);
+            const float d = h2f(*(const uint16_t *)(wr + 208));
+            const u32x4 neg32 = {0xE0E0E0E0u, 0xE0E0E0E0u, 0xE0E0E0E0u, 0xE0E0E0E0u};
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int odd = p & 1;
+                const u32x4 L4 = (p >> 1) ? ql1 : ql0;
+                const u32x4 H4 = (p >> 1) ? qh1 : qh0;
+                const int tsh = 4 * odd + 2 * (g >> 1);
+                u32x4 b;
+                b.x = ((L4.x >> (4 * odd)) & 0x0F0F0F0Fu) | (((H4.x >> tsh) << 4) & 0x30303030u);
+                b.y = ((L4.y >> (4 * odd)) & 0x0F0F0F0Fu) | (((H4.y >> tsh) << 4) & 0x30303030u);
+                b.z = ((L4.z >> (4 * odd)) & 0x0F0F0F0Fu) | (((H4.z >> tsh) << 4) & 0x30303030u);
+                b.w = ((L4.w >> (4 * odd)) & 0x0F0F0F0Fu) | (((H4.w >> tsh) << 4) & 0x30303030u);
+                const uint32_t scw = p == 0 ? scv.x : p == 1 ? scv.y : p == 2 ? scv.z : scv.w;
+                const float ws = d * (float)((int32_t)(scw << (24 - 8 * g)) >> 24);
+                const int blk = 2 * p + (g >> 1);
+#pragma unroll
+                for (int cg = 0; cg < NCG; ++cg) {
+                    if (cg * 4 >= ncols) break;
+                    const u32x4 a = aop(cg, p);
+                    i32x4 D = mfma16x16x64(a, b, zero4);
+                    D = mfma16x16x64(a, neg32, D);
+                    if (DBG) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int c = 4 * cg + e;
+                            if (dbg_row && c < ncols) dbg_row[(int64_t)c * dbg_ld + s * 16 + 4 * p + g] = D[e];
+                        }
+                    } else {
+                        const f32x4 t0 = *(const f32x4 *)(ftab + blk * 8 + 4 * cg);
+                        const f32x4 t1 = *(const f32x4 *)(ftab + blk * 8 + 4 * cg + 2);
+                        acc[cg][0] = fmaf((float)D[0], ws * t0.x, acc[cg][0]);
+                        acc[cg][1] = fmaf((float)D[1], ws * t0.z, acc[cg][1]);
+                        acc[cg][2] = fmaf((float)D[2], ws * t1.x, acc[cg][2]);
+                        acc[cg][3] = fmaf((float)D[3], ws * t1.z, acc[cg][3]);
+                    }
+                }
+            }
+        } else {
+            const uint8_t *wr = st + wrow;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int blk = 2 * p + (g >> 1);
+                const uint8_t *bp = wr + blk * 34;
+                const u32x4 q = lds16(bp + 2 + 16 * (g & 1));
+                const i32x4 D = mfma16x16x64(aop(0, p), q, zero4);
+                if (DBG) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int c = 4 * (g & 1) + e;
+                        if (dbg_row && c < ncols) dbg_row[(int64_t)c * dbg_ld + s * 8 + blk] = D[e];
+                    }
+                } else {
+                    const float ws = h2f(*(const uint16_t *)bp);
+                    const f32x4 t0 = *(const f32x4 *)(ftab + blk * 8 + 4 * (g & 1));
+                    const f32x4 t1 = *(const f32x4 *)(ftab + blk * 8 + 4 * (g & 1) + 2);
+                    acc[0][0] = fmaf((float)D[0], ws * t0.x, acc[0][0]);
+                    acc[0][1] = fmaf((float)D[1], ws * t0.z, acc[0][1]);
+                    acc[0][2] = fmaf((float)D[2], ws * t1.x, acc[0][2]);
+                    acc[0][3] = fmaf((float)D[3], ws * t1.z, acc[0][3]);
+                }
+            }
+        }
+
+    }
+    if (DBG) return;
+
+    // Combine the sub-block slots held by lane groups: Q4_K/Q8_0 lanes g and g^2 (the two halves
+    // of the block diagonal), Q6_K lanes g = 0..3 (the four 16-value sub-blocks).
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            float v = acc[cg][e];
+            if (T == kQ6_K) v += __shfl_xor(v, 16);
+            v += __shfl_xor(v, 32);
+            acc[cg][e] = v;
+        }
+    // Each wave leaves its 16 rows x 8 columns (128 floats) at the start of its own stage:
+    // Q4_K/Q8_0 lanes g < 2 hold columns 4g..4g+3 of row r16 (index 4*lane + e), Q6_K lanes
+    // g == 0 hold columns 4cg + e (index 8*lane + 4cg + e).
+    const bool holder = (T == kQ6_K) ? (g == 0) : (g < 2);
+    float *red = (float *)st;
+    if (holder) {
+#pragma unroll
+        for (int cg = 0; cg < NCG; ++cg)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) red[lane * (4 * NCG) + cg * 4 + e] = acc[cg][e];
+    }
+    __syncthreads();
+    // 128 threads each sum one (row, column) over the waves, all loads in flight at once.
+    const int t = threadIdx.x;
+    if (t >= 128) return;
+    float v = 0.f;
+    for (int wv = 0; wv < nwaves; ++wv) v += ((const float *)(smem + (size_t)wv * (16 + SB) + 16))[t];
+    int rr, c;
+    if (T == kQ6_K) { rr = t >> 3; c = t & 7; }
+    else { rr = (t >> 2) & 15; c = 4 * (t >> 6) + (t & 3); }
+    if (c < ncols && row0 + rr < rows) y[mc.pair(c) * rows + row0 + rr] = v;
+}
+
+template <int T, bool DBG, bool EXPERT>
+hipError_t launch_t(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y,
+                    int32_t *dbg, const ColMap &c, int64_t n_exp, hipStream_t s) {
+    const int64_t nsteps = k / kSuper;
+    const int nw = (int)(nsteps < 16 ? nsteps : 16);
+    const size_t smem = (size_t)nw * (16 + Stage<T>::BYTES);
+    MvArgs a;
+    a.rows = rows;
+    a.row_bytes = (uint32_t)((k / Fmt<T>::QK) * Fmt<T>::BYTES);
+    a.col_bytes = (uint32_t)(k / 32 * kQ8_1Bytes);
+    a.nsteps = (int32_t)nsteps;
+    a.q = (int32_t)(nsteps / nw);
+    a.r = (int32_t)(nsteps % nw);
+    a.n = (int32_t)n;
+    static bool attr = false;
+    if (!attr) {
+        hipError_t e = hipFuncSetAttribute((const void *)mmvq_stream_kernel<T, DBG, EXPERT>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        if (e != hipSuccess) return e;
+        attr = true;
+    }
+    dim3 grid((unsigned)((rows + kRows - 1) / kRows), EXPERT ? (unsigned)n_exp : 1u);
+    hipLaunchKernelGGL((mmvq_stream_kernel<T, DBG, EXPERT>), grid, dim3(64 * (unsigned)nw), smem, s, w, xq, y, dbg,
+                       a, c);
+    return hipGetLastError();
+}
+
+template <int T>
+hipError_t dispatch(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y, int32_t *dbg,
+                    const ColMap *cm, int64_t n_exp, hipStream_t s) {
+    const ColMap c = cm ? *cm : ColMap{};
+    if (dbg) return launch_t<T, true, false>(w, rows, k, xq, n, y, dbg, c, n_exp, s);
+    if (cm) return launch_t<T, false, true>(w, rows, k, xq, n, y, dbg, c, n_exp, s);
+    return launch_t<T, false, false>(w, rows, k, xq, n, y, dbg, c, n_exp, s);
+}
+
+}  // namespace
+
+bool mmvq_stream_supported(int type, const void *w, int64_t k, const void *xq, const ColMap *cm) {
+    if (type != kQ4_K && type != kQ6_K && type != kQ8_0) return false;
+    if (k % kSuper != 0 || k < kSuper) return false;
+    const int64_t row_bytes = type == kQ8_0 ? k / 32 * 34 : k / 256 * (type == kQ4_K ? 144 : 210);
+    if (row_bytes % 16 != 0) return false;
+    if ((uintptr_t)w % 16 != 0 || (uintptr_t)xq % 16 != 0) return false;
+    if (cm && cm->w_expert_stride % 16 != 0) return false;
+    return true;
+}
+
+hipError_t launch_mmvq_stream(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n,
+                              float *y, int32_t *dbg, const ColMap *cm, int64_t n_exp, hipStream_t s) {
+    if (type == kQ4_K) return dispatch<kQ4_K>(w, rows, k, xq, n, y, dbg, cm, n_exp, s);
+    if (type == kQ6_K) return dispatch<kQ6_K>(w, rows, k, xq, n, y, dbg, cm, n_exp, s);
+    if (type == kQ8_0) return dispatch<kQ8_0>(w, rows, k, xq, n, y, dbg, cm, n_exp, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace qmm

@@ -130,10 +130,17 @@ qmm_status qmm_debug_subdots(int type, const void *w, int64_t rows, int64_t k, c
  *   QMM_OVR_PATH:     1 force matrix-vector (only when n <= 8), 2 force tiled MFMA.
  *   QMM_OVR_STREAMK:  1 force off, 2 force on (tiled path).
  *   QMM_OVR_TILE_J:   tile width in columns (32, 64 or 128).
- *   QMM_OVR_MV_STEPS: 256-value steps per wave in the matrix-vector kernel (1, 2 or 4).
+ *   QMM_OVR_MV_STEPS: 256-value steps per wave in the register-streamed matrix-vector kernel
+ *                     (1, 2 or 4).
+ *   QMM_OVR_MV_KERNEL: matrix-vector kernel: 1 register-streamed (any input), 2 LDS-staged
+ *                     MFMA only, 3 dot4 only (up to 3 columns, Q4_K and Q8_0); calls the forced
+ *                     kernel cannot serve fail with QMM_ERR_HIP.  The automatic choice takes the
+ *                     dot4 kernel for Q4_K with n <= 2 and Q8_0 with n <= 3, else the LDS-staged
+ *                     kernel, when weights, activations and rows are aligned (16 bytes; Q8_0 dot4:
+ *                     4) and K is a multiple of 256; otherwise the register-streamed kernel.
  * Returns QMM_ERR_ARG for an unknown key or value.
  * ------------------------------------------------------------------------------------------- */
-enum { QMM_OVR_PATH = 1, QMM_OVR_STREAMK = 2, QMM_OVR_TILE_J = 3, QMM_OVR_MV_STEPS = 4 };
+enum { QMM_OVR_PATH = 1, QMM_OVR_STREAMK = 2, QMM_OVR_TILE_J = 3, QMM_OVR_MV_STEPS = 4, QMM_OVR_MV_KERNEL = 5 };
 qmm_status qmm_set_override(int key, int value);
 
 /* ---------------------------------------------------------------------------------------------

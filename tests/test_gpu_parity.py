@@ -23,7 +23,7 @@ TNAME = {qmm.Q4_K: "q4_K", qmm.Q6_K: "q6_K", qmm.Q8_0: "q8_0"}
 
 
 def _reset_overrides():
-    for key in (qmm.OVR_PATH, qmm.OVR_STREAMK, qmm.OVR_TILE_J, qmm.OVR_MV_STEPS):
+    for key in (qmm.OVR_PATH, qmm.OVR_STREAMK, qmm.OVR_TILE_J, qmm.OVR_MV_STEPS, qmm.OVR_MV_KERNEL):
         qmm.set_override(key, 0)
 
 
@@ -156,6 +156,41 @@ def test_matvec_steps_per_wave(qtype, spw):
     xq = oracle.quantize_q8_1(x)
     got = qmm.debug_subdots(to_dev(w), qtype, 77, k, to_dev(xq), 5, qmm.PATH_MATVEC).cpu().numpy()
     assert np.array_equal(got, oracle.subdots(qtype, w, 77, k, xq, 5))
+
+
+MV_KERNELS = [1, 2, 3]     # register-streamed, LDS-staged MFMA, dot4
+MV_KNAME = {1: "regs", 2: "lds", 3: "dot4"}
+
+
+@pytest.mark.parametrize("kernel", MV_KERNELS, ids=MV_KNAME.get)
+@pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
+def test_matvec_kernel_variants(qtype, kernel):
+    """Every matrix-vector kernel on shapes it serves (aligned rows, K a multiple of 256): ragged
+    rows, more 256-value steps than waves so some waves take two, every column-count class the
+    kernel handles; fp32 outputs and the integer sub-block dots."""
+    if kernel == 3 and qtype == qmm.Q6_K:
+        pytest.skip("the dot4 kernel serves Q4_K and Q8_0")
+    qmm.set_override(qmm.OVR_MV_KERNEL, kernel)
+    k = 6144 if qtype == qmm.Q6_K else 4352
+    ns = (1, 2, 3) if kernel == 3 else (1, 3, 4, 5, 8)
+    for n in ns:
+        _full_check(qtype, 77, k, n, 520 + n, f"{TNAME[qtype]} {MV_KNAME[kernel]} n={n}")
+    nd = 3 if kernel == 3 else 7
+    w, x = _case(qtype, 77, k, nd, 530)
+    xq = oracle.quantize_q8_1(x)
+    got = qmm.debug_subdots(to_dev(w), qtype, 77, k, to_dev(xq), nd, qmm.PATH_MATVEC).cpu().numpy()
+    assert np.array_equal(got, oracle.subdots(qtype, w, 77, k, xq, nd))
+
+
+@pytest.mark.parametrize("kernel,qtype,k,n", [(2, qmm.Q6_K, 768, 1),    # 630-byte rows: not 16-byte aligned
+                                              (3, qmm.Q6_K, 4096, 1),   # dot4 serves Q4_K / Q8_0 only
+                                              (3, qmm.Q4_K, 4096, 4)])  # dot4 takes at most 3 columns
+def test_forced_matvec_kernel_refuses_unsupported_call(kernel, qtype, k, n):
+    qmm.set_override(qmm.OVR_MV_KERNEL, kernel)
+    w, x = _case(qtype, 32, k, n, 540)
+    with pytest.raises(qmm.QmmError):
+        qmm.matmul(to_dev(w), qtype, 32, k, to_dev(x))
+        torch.cuda.synchronize()
 
 
 def test_matmul_q8_1_entry_matches_matmul():
@@ -328,6 +363,31 @@ def test_moe_invalid_ids_and_per_slot_activations():
             if 0 <= e < n_exp:
                 a = t * top_k + s
                 assert_close(y[t, s][None], ref[t, s][None], wn_all[e], xn_all[a:a + 1], what=f"pair {t},{s}")
+
+
+@pytest.mark.parametrize("kernel", [1, 2], ids=MV_KNAME.get)
+@pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
+def test_moe_small_experts_both_kernels(qtype, kernel):
+    """Experts with at most 8 columns go to the matrix-vector kernel in expert mode; both kernels,
+    ragged rows, per-slot activations, every output against the oracle."""
+    qmm.set_override(qmm.OVR_MV_KERNEL, kernel)
+    rng = np.random.default_rng(1100 + qtype)
+    n_exp, rows, k, n_tok, top_k = 6, 77, 2048, 20, 2
+    w = synth.gen_weights(qtype, n_exp * rows, k, rng)
+    x = rng.standard_normal((n_tok * top_k, k)).astype(np.float32)
+    ids = np.stack([rng.choice(n_exp, top_k, replace=False) for _ in range(n_tok)]).astype(np.int32)
+    y, ws = qmm.matmul_id(to_dev(w), qtype, n_exp, rows, k, to_dev(x), to_dev(ids), x_per_tok=top_k)
+    assert qmm.matmul_id_invalid_count(ws) == 0
+    y = y.cpu().numpy()
+    ref, bad = oracle.matmul_id(qtype, w, n_exp, rows, k, x, top_k, ids)
+    assert bad == 0
+    xq = oracle.quantize_q8_1(x)
+    wn_all = row_norms(qtype, w, n_exp * rows, k).reshape(n_exp, rows)
+    xn_all = col_norms(xq, n_tok * top_k, k)
+    for t in range(n_tok):
+        for s in range(top_k):
+            a = t * top_k + s
+            assert_close(y[t, s][None], ref[t, s][None], wn_all[ids[t, s]], xn_all[a:a + 1], what=f"pair {t},{s}")
 
 
 def test_moe_rerun_is_bitwise():
