@@ -294,6 +294,14 @@ qmm_status qmm_matmul(int type, const void *w, int64_t rows, int64_t k, const fl
     if (((uintptr_t)ws) & 255) return fail(QMM_ERR_ARG, "workspace must be 256-byte aligned");
     hipStream_t s = (hipStream_t)stream;
     uint8_t *wsb = (uint8_t *)ws;
+    qmm_plan p{};
+    if ((st = qmm_plan_dense(type, rows, k, n, device_cus(), &p))) return st;
+    if (p.regime == 1 && qmm::mmvq_fused_applies(type, w, k, x, n)) {
+        // few columns: the dot4 kernel quantizes the activations itself (same bytes as below)
+        hipError_t e = qmm::launch_mmvq_fused(type, (const uint8_t *)w, rows, k, x, n, y, s);
+        if (e != hipSuccess) return hip_fail(e, "fused matrix-vector kernel launch");
+        return QMM_OK;
+    }
     hipError_t e = qmm::launch_quantize_q8_1(x, n, k, wsb + L.xq_off, s);
     if (e != hipSuccess) return hip_fail(e, "quantize launch");
     return run_dense(type, w, rows, k, wsb + L.xq_off, n, y, wsb, L, nullptr, 0, s);

@@ -469,6 +469,19 @@ void set_mmvq_kernel(int which) { g_mv_kernel = which; }
 // Largest column count the automatic choice sends to the dot4 kernel, per type.
 static int dot4_auto_cols(int type) { return type == kQ4_K ? 2 : type == kQ8_0 ? 3 : 0; }
 
+bool mmvq_fused_applies(int type, const void *w, int64_t k, const float *x, int64_t n) {
+    const int kc = g_mv_kernel;
+    if (kc != 0 && kc != 3) return false;
+    const int lim = kc == 3 ? mmvq_dot4_max_cols() : dot4_auto_cols(type);
+    return n >= 1 && n <= lim && (uintptr_t)x % 16 == 0 && mmvq_dot4_supported(type, w, k, x, nullptr);
+}
+
+hipError_t launch_mmvq_fused(int type, const uint8_t *w, int64_t rows, int64_t k, const float *x, int64_t n, float *y,
+                             hipStream_t s) {
+    if (!mmvq_fused_applies(type, w, k, x, n)) return hipErrorInvalidValue;
+    return launch_mmvq_dot4_f32(type, w, rows, k, x, n, y, s);
+}
+
 hipError_t launch_mmvq(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y,
                        int32_t *dbg, const ColMap *cm, int64_t n_exp, hipStream_t s) {
     const int kc = g_mv_kernel;

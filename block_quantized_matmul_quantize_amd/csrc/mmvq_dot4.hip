@@ -9,8 +9,10 @@
 // sub-blocks 2g and 2g+1 -- for Q4_K the 32 qs bytes 32g..32g+31 (low nibbles sub-block 2g, high
 // nibbles 2g+1), for Q8_0 the two 34-byte blocks.  Consecutive lanes of a row read consecutive
 // bytes, so each quarter-wave load touches one or two cache lines.  The columns' q8_1 codes and
-// fp32 (d, s) are staged once per workgroup in LDS; every lane with the same quarter reads the
-// same LDS words (a broadcast).  Next step's weights load while this step computes.
+// fp32 (d, s) are staged once per workgroup in LDS -- read from q8_1 blocks, or, for fp32 input,
+// quantized on the spot with the same arithmetic as the standalone quantize kernel (q8_1.hpp),
+// which saves that kernel's launch; every lane with the same quarter reads the same LDS words (a
+// broadcast).  Next step's weights load while this step computes.
 //   Q4_K  acc += D(2g)*(d*sc)*d_a - (dmin*m)*s_a   (+ the same for sub-block 2g+1)
 //   Q8_0  acc += D*d_w*d_a                         (both blocks)
 // The four quarters of a row are summed with lane shuffles, the waves in LDS in a fixed order.
@@ -19,6 +21,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "mv_cols.hpp"
+#include "q8_1.hpp"
 
 namespace qmm {
 
@@ -66,8 +69,8 @@ template <int T> struct StepBytes;
 template <> struct StepBytes<kQ4_K> { static constexpr int V = 144; };
 template <> struct StepBytes<kQ8_0> { static constexpr int V = 272; };
 
-template <int T, int NC, bool DBG, bool EXPERT>
-__global__ __launch_bounds__(1024) void mmvq_dot4_kernel(const uint8_t *__restrict__ w, const uint8_t *__restrict__ xq,
+template <int T, int NC, bool DBG, bool EXPERT, bool F32>
+__global__ __launch_bounds__(1024) void mmvq_dot4_kernel(const uint8_t *__restrict__ w, const void *__restrict__ xin,
                                                         float *__restrict__ y, int32_t *__restrict__ dbg, D4Args P,
                                                         ColMap cm) {
     extern __shared__ __align__(16) uint8_t smem[];
@@ -93,17 +96,33 @@ __global__ __launch_bounds__(1024) void mmvq_dot4_kernel(const uint8_t *__restri
     uint8_t *acodes = smem;
     float2 *aft = (float2 *)(smem + (size_t)NC * nb * 32);
     float *red = (float *)(smem + (size_t)NC * nb * 40);   // [nwaves][16 * NC]
-    for (int c = 0; c < ncols; ++c) {
-        const uint8_t *xrow = xq + mc.arow(c) * (int64_t)nb * kQ8_1Bytes;
-        for (uint32_t b = threadIdx.x; b < nb; b += blockDim.x) {
-            const uint8_t *src = xrow + (size_t)b * kQ8_1Bytes;
-            const uint32_t ds = *(const uint32_t *)src;
-            const u32x4 c0 = *(const u32x4_a4 *)(src + 4);
-            const u32x4 c1 = *(const u32x4_a4 *)(src + 20);
-            uint8_t *dst = acodes + ((size_t)c * nb + b) * 32;
-            *(u32x4 *)dst = c0;
-            *(u32x4 *)(dst + 16) = c1;
-            aft[(size_t)c * nb + b] = make_float2(h2f((uint16_t)(ds & 0xFFFF)), h2f((uint16_t)(ds >> 16)));
+    if constexpr (F32) {
+        // fp32 rows (dense): 8 consecutive threads quantize one block; nb*8 and the block size
+        // are multiples of 8, so the 8 lanes of a block are active together.
+        for (int c = 0; c < ncols; ++c) {
+            const float *xrow = (const float *)xin + (size_t)c * nb * 32;
+            for (uint32_t t = threadIdx.x; t < nb * 8; t += blockDim.x) {
+                const uint32_t b = t >> 3, sub = t & 7;
+                const Q81Lane q = quantize_q8_1_lane(*(const float4 *)(xrow + b * 32 + 4 * sub));
+                *(uint32_t *)(acodes + ((size_t)c * nb + b) * 32 + 4 * sub) = q.codes;
+                if (sub == 0)
+                    aft[(size_t)c * nb + b] = make_float2(h2f((uint16_t)(q.ds & 0xFFFF)), h2f((uint16_t)(q.ds >> 16)));
+            }
+        }
+    } else {
+        const uint8_t *xq = (const uint8_t *)xin;
+        for (int c = 0; c < ncols; ++c) {
+            const uint8_t *xrow = xq + mc.arow(c) * (int64_t)nb * kQ8_1Bytes;
+            for (uint32_t b = threadIdx.x; b < nb; b += blockDim.x) {
+                const uint8_t *src = xrow + (size_t)b * kQ8_1Bytes;
+                const uint32_t ds = *(const uint32_t *)src;
+                const u32x4 c0 = *(const u32x4_a4 *)(src + 4);
+                const u32x4 c1 = *(const u32x4_a4 *)(src + 20);
+                uint8_t *dst = acodes + ((size_t)c * nb + b) * 32;
+                *(u32x4 *)dst = c0;
+                *(u32x4 *)(dst + 16) = c1;
+                aft[(size_t)c * nb + b] = make_float2(h2f((uint16_t)(ds & 0xFFFF)), h2f((uint16_t)(ds >> 16)));
+            }
         }
     }
     __syncthreads();
@@ -227,8 +246,8 @@ __global__ __launch_bounds__(1024) void mmvq_dot4_kernel(const uint8_t *__restri
     if (c < ncols && row0 + rr < rows) y[mc.pair(c) * rows + row0 + rr] = v;
 }
 
-template <int T, int NC, bool DBG, bool EXPERT>
-hipError_t launch_nc(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y, int32_t *dbg,
+template <int T, int NC, bool DBG, bool EXPERT, bool F32 = false>
+hipError_t launch_nc(const uint8_t *w, int64_t rows, int64_t k, const void *xq, int64_t n, float *y, int32_t *dbg,
                      const ColMap &cm, int64_t n_exp, hipStream_t s) {
     const int64_t nsteps = k / kSuper;
     const int nw = (int)(nsteps < 16 ? nsteps : 16);
@@ -243,13 +262,13 @@ hipError_t launch_nc(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *x
     const size_t smem = (size_t)NC * a.nb * 40 + (size_t)nw * 16 * NC * sizeof(float);
     static bool attr = false;
     if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void *)mmvq_dot4_kernel<T, NC, DBG, EXPERT>,
+        hipError_t e = hipFuncSetAttribute((const void *)mmvq_dot4_kernel<T, NC, DBG, EXPERT, F32>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
         attr = true;
     }
     dim3 grid((unsigned)((rows + kRows - 1) / kRows), EXPERT ? (unsigned)n_exp : 1u);
-    hipLaunchKernelGGL((mmvq_dot4_kernel<T, NC, DBG, EXPERT>), grid, dim3(64 * (unsigned)nw), smem, s, w, xq, y, dbg, a,
+    hipLaunchKernelGGL((mmvq_dot4_kernel<T, NC, DBG, EXPERT, F32>), grid, dim3(64 * (unsigned)nw), smem, s, w, xq, y, dbg, a,
                        cm);
     return hipGetLastError();
 }
@@ -290,6 +309,21 @@ hipError_t launch_mmvq_dot4(int type, const uint8_t *w, int64_t rows, int64_t k,
                             float *y, int32_t *dbg, const ColMap *cm, int64_t n_exp, int max_cols, hipStream_t s) {
     if (type == kQ4_K) return dispatch<kQ4_K>(w, rows, k, xq, n, y, dbg, cm, n_exp, max_cols, s);
     if (type == kQ8_0) return dispatch<kQ8_0>(w, rows, k, xq, n, y, dbg, cm, n_exp, max_cols, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_mmvq_dot4_f32(int type, const uint8_t *w, int64_t rows, int64_t k, const float *x, int64_t n,
+                                float *y, hipStream_t s) {
+    const ColMap c{};
+#define QMM_D4F(TT)                                                                                            \
+    if (type == TT) {                                                                                         \
+        if (n <= 1) return launch_nc<TT, 1, false, false, true>(w, rows, k, x, n, y, nullptr, c, 0, s);     \
+        if (n == 2) return launch_nc<TT, 2, false, false, true>(w, rows, k, x, n, y, nullptr, c, 0, s);     \
+        return launch_nc<TT, 3, false, false, true>(w, rows, k, x, n, y, nullptr, c, 0, s);                  \
+    }
+    QMM_D4F(kQ4_K)
+    QMM_D4F(kQ8_0)
+#undef QMM_D4F
     return hipErrorInvalidValue;
 }
 

@@ -193,6 +193,44 @@ def test_forced_matvec_kernel_refuses_unsupported_call(kernel, qtype, k, n):
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("qtype,n", [(qmm.Q4_K, 1), (qmm.Q4_K, 2), (qmm.Q8_0, 1), (qmm.Q8_0, 2), (qmm.Q8_0, 3)])
+def test_fused_quantize_matches_separate_quantize_bitwise(qtype, n):
+    """fp32 input with few columns: the dot4 kernel quantizes the activations itself; its output
+    equals quantize_q8_1 followed by the q8_1-input product bit for bit, and the oracle's."""
+    w, x = _case(qtype, 77, 4352, n, 560 + n)
+    wd, xd = to_dev(w), to_dev(x)
+    fused = qmm.matmul(wd, qtype, 77, 4352, xd)
+    separate = qmm.matmul_q8_1(wd, qtype, 77, 4352, qmm.quantize_q8_1(xd), n)
+    assert torch.equal(fused, separate)
+    xq = oracle.quantize_q8_1(x)
+    ref = oracle.matmul_q8_1(qtype, w, 77, 4352, xq, n)
+    assert_close(fused.cpu().numpy(), ref, row_norms(qtype, w, 77, 4352), col_norms(xq, n, 4352))
+
+
+def test_fused_quantize_special_blocks():
+    """Zero blocks, exact rounding ties, a lone spike, a constant block, a subnormal-range scale and
+    a scale near the fp16 limit inside the fused kernel's activation rows."""
+    blocks = [np.zeros(32), np.concatenate([[15.875, 0.3125, -0.3125, 0.0625, -0.0625, 1.5625], np.zeros(26)]),
+              np.where(np.arange(32) == 7, -3.0, 0.0), np.full(32, 0.7), np.linspace(-1e-38, 1e-38, 32),
+              np.linspace(-6e4, 6.5e4, 32) * 1e-3, np.concatenate([[127.031005859375, 100.51], np.zeros(30)]),
+              np.random.default_rng(570).standard_normal(32)]
+    row = np.concatenate(blocks)
+    x = np.stack([row, row[::-1].copy(), np.roll(row, 64)]).astype(np.float32)   # k = 256
+    for qtype in (qmm.Q4_K, qmm.Q8_0):
+        w = synth.gen_weights(qtype, 40, 256, np.random.default_rng(571))
+        for n in (1, 2, 3):
+            if qtype == qmm.Q4_K and n == 3:
+                continue
+            xs = np.ascontiguousarray(x[:n])
+            wd, xd = to_dev(w), to_dev(xs)
+            fused = qmm.matmul(wd, qtype, 40, 256, xd)
+            separate = qmm.matmul_q8_1(wd, qtype, 40, 256, qmm.quantize_q8_1(xd), n)
+            assert torch.equal(fused, separate), (qtype, n)
+            xq = oracle.quantize_q8_1(xs)
+            ref = oracle.matmul_q8_1(qtype, w, 40, 256, xq, n)
+            assert_close(fused.cpu().numpy(), ref, row_norms(qtype, w, 40, 256), col_norms(xq, n, 256))
+
+
 def test_matmul_q8_1_entry_matches_matmul():
     qtype, rows, k, n = qmm.Q4_K, 1000, 2048, 24
     w, x = _case(qtype, rows, k, n, 600)
