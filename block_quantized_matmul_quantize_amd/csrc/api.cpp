@@ -84,9 +84,21 @@ qmm_status check_common(int type, int64_t rows, int64_t k, int64_t n) {
 }
 
 // Shared-memory footprint of the tiled kernel, for its occupancy estimate.
+// LDS bytes of one tiled-kernel workgroup (the Smem layout in mmq.hip): weight tile, fp32 row
+// scales (and Q4_K mins), activation codes, fp32 (d, s).
 int mmq_smem(int type, int J) {
-    const int nw = type == QMM_Q6_K ? 2 : 1;
-    return nw * kTI * 272 + J * 272 + 2 * 8 * kTI * 4 + 8 * J * 8;
+    const int wt = type == QMM_Q4_K ? kTI * 144 : (type == QMM_Q6_K ? 2 * kTI * 272 : kTI * 272);
+    const int wm = type == QMM_Q4_K ? 8 * kTI * 4 : 0;
+    return wt + 8 * kTI * 4 + wm + J * 272 + 8 * J * 8;
+}
+
+// Tiled-kernel workgroups resident per compute unit: the kernels keep about 200 registers per
+// lane, so two waves per SIMD (8 per CU): two 4-wave groups for J <= 64, one 8-wave group for
+// J = 128; fewer if LDS runs out.
+int mmq_resident(int type, int J) {
+    const int by_waves = J == 128 ? 1 : 2;
+    const int by_lds = (160 * 1024) / mmq_smem(type, J);
+    return std::max(1, std::min(by_waves, by_lds));
 }
 
 }  // namespace
@@ -169,11 +181,13 @@ qmm_status qmm_plan_dense(int type, int64_t rows, int64_t k, int64_t n, int32_t 
     p.tile_j = g_ovr_tile_j.load() ? g_ovr_tile_j.load() : qmm_select_tile_j(n);
     const int64_t n_ct = (n + p.tile_j - 1) / p.tile_j;
     p.ntiles = ((rows + kTI - 1) / kTI) * n_ct;
-    const int occ = std::max(1, std::min(2, (160 * 1024) / mmq_smem(type, p.tile_j)));
+    const int occ = mmq_resident(type, p.tile_j);
     const int32_t slots = nsm * occ;
     p.efficiency_pct = qmm_tile_efficiency(p.ntiles, slots);
     const int sk = g_ovr_streamk.load();
-    bool use_sk = p.efficiency_pct < 90 && p.k_iters > 1;
+    // stream-K pays a partial-tile round trip and a fixup pass: worth it once a quarter of the
+    // last round of tiles would idle (efficiency below 75 %)
+    bool use_sk = p.efficiency_pct < 75 && p.k_iters > 1;
     if (sk == 1) use_sk = false;
     if (sk == 2) use_sk = p.k_iters > 1 || p.ntiles > 1;
     p.stream_k = use_sk ? 1 : 0;

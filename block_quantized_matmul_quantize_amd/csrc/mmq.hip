@@ -2,15 +2,19 @@
 // "J runtime selection", "tile efficiency", "stream-K", "fixup", "expert bounds").
 //
 // CDNA4 design.  A 256-thread workgroup owns a 128-row x J-column output tile (J = 32/64/128)
-// and walks K in 256-value steps.  Each step stages the weight tile into LDS already unpacked to
-// int8 codes (the MMQ page's "why not dequantize": stay quantized, unpack once per tile and
-// reuse it for J columns) together with fp32 per-row scales, and the activation tile (int8 codes
-// plus fp32 (d, s) per 32-value block).  Each wave owns 32 rows; per 32-value block it runs one
-// v_mfma_i32_32x32x32_i8 per 32 columns -- K = 32 is exactly one q8_1 block, so every int32
-// result is one exact sub-block dot D -- and applies the fp32 fixup to its 16 accumulators:
-//   Q4_K  acc += D * (d*sc) * d_a - (dmin*m) * s_a
-//   Q8_0  acc += D * d_w * d_a
-//   Q6_K  acc += (sc0*D0 + sc1*D1) * d * d_a
+// and walks K in 256-value steps.  Each step's weight tile and activation tile are fetched from
+// HBM into registers while the previous step computes (software pipelining: the loads of step
+// kb+1 are issued right after step kb is parked in LDS), then parked in LDS: Q4_K as packed qs
+// bytes plus fp32 per-(row, sub-block) scales d*sc and mins -dmin*m, Q8_0 as int8 codes plus
+// fp32 d, Q6_K unpacked (below); activations as int8 codes plus fp32 (d, s) per 32-value block
+// (the MMQ page's "why not dequantize": stay quantized and reuse each unpacked tile for J
+// columns).  Each wave owns 32 rows; per 32-value block it runs one v_mfma_i32_32x32x32_i8 per
+// 32 columns -- K = 32 is exactly one q8_1 block, so every int32 result is one exact sub-block
+// dot D -- and folds it into its fp32 accumulators with one multiply-add:
+//   Q4_K  acc += D * (d*sc * d_a);  the min term -(dmin*m) * s_a is a rank-8 product per step,
+//         done as four v_mfma_f32_32x32x2_f32 into the same accumulators
+//   Q8_0  acc += D * (d_w * d_a)
+//   Q6_K  acc += (sc0*D0 + sc1*D1) * (d * d_a)
 // Q6_K changes scale every 16 values, so its int8 scale is folded into the codes at unpack time:
 // v = sc*(q-32) lies in [-4064, 4096] and is split as v = 128*hi + lo with lo in [0,127] and hi
 // in [-32, 32]; two MFMAs give D_hi and D_lo and sc0*D0 + sc1*D1 = 128*D_hi + D_lo exactly.
@@ -26,7 +30,8 @@
 namespace qmm {
 
 constexpr int kTI = 128;        // rows per tile
-constexpr int kLd = 272;        // LDS bytes per 256-value row (+16 to spread banks)
+constexpr int kLd = 272;        // LDS bytes per 256-value row of int8 codes (+16 to spread banks)
+constexpr int kLd4 = 144;       // LDS bytes per row of packed Q4_K qs (128 + 16)
 
 struct MmqArgs {
     int64_t ntiles, n_ct, k_iters, units;
@@ -34,53 +39,101 @@ struct MmqArgs {
     int32_t write_partials;     // stream-K active
 };
 
+// Threads per tile: 4 row waves (32 rows each) times J/64 column waves (J = 128: two 64-column
+// halves, so every wave keeps at most 64 columns of accumulators and two waves fit per SIMD).
+template <int J> struct Cfg {
+    static constexpr int NWC = J == 128 ? 2 : 1;   // column waves
+    static constexpr int NT = 256 * NWC;            // threads
+    static constexpr int JW = J / NWC;              // columns per wave
+    static constexpr int NCB = JW / 32;             // 32-column MFMA blocks per wave
+};
+
+// LDS layout of one step.
 template <int T, int J> struct Smem {
-    static constexpr int NW = (T == kQ6_K) ? 2 : 1;               // weight planes
+    static constexpr int W_BYTES = T == kQ4_K ? kTI * kLd4 : (T == kQ6_K ? 2 * kTI * kLd : kTI * kLd);
     static constexpr int W_OFF = 0;
-    static constexpr int A_OFF = W_OFF + NW * kTI * kLd;
-    static constexpr int WS_OFF = A_OFF + J * kLd;                 // float [8][128]
-    static constexpr int WM_OFF = WS_OFF + 8 * kTI * 4;            // float [8][128]
-    static constexpr int X_OFF = WM_OFF + 8 * kTI * 4;             // float2 [8][J]
+    static constexpr int WS_OFF = W_OFF + W_BYTES;                               // float [8][128]
+    static constexpr int WM_OFF = WS_OFF + 8 * kTI * 4;                          // float [8][128] (Q4_K)
+    static constexpr int A_OFF = WM_OFF + (T == kQ4_K ? 8 * kTI * 4 : 0);      // int8 [J][kLd]
+    static constexpr int X_OFF = A_OFF + J * kLd;                                // float2 [8][J]
     static constexpr int BYTES = X_OFF + 8 * J * 8;
 };
 
 // ---------------------------------------------------------------------------------------------
-// Weight tile staging: rows [r0, r0+128) of the step's 256 values -> int8 codes + fp32 scales.
+// Activation tile: J columns of the step's 8 q8_1 blocks.  Thread tid owns (column, block) pairs
+// i = tid + NT*it: column i/8, block i%8 (8 consecutive threads read one column's 288 bytes).
 // ---------------------------------------------------------------------------------------------
-__device__ __forceinline__ void stage_weights_q4_k(uint8_t *sm, const uint8_t *wbase, int64_t row_bytes,
-                                                   int64_t r0, int64_t rows, int64_t kb) {
-    const int tid = threadIdx.x;
-    int8_t *sW = (int8_t *)sm;
+template <int J> struct ActFetch {
+    static constexpr int NT = Cfg<J>::NT, N = J * 8 / NT;
+    uint32_t ds[N];
+    u32x4 c0[N], c1[N];
+    __device__ __forceinline__ void fetch(const uint8_t *xq, int64_t nb32, int64_t kb, const int64_t (&acol)[N]) {
+        const int tid = threadIdx.x;
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int i = tid + 256 * it;              // (row, 16-byte piece of qs): 128 x 8
-        const int r = i >> 3, piece = i & 7;
-        const int64_t row = r0 + r;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (row < rows) v = ld16(wbase + row * row_bytes + kb * 144 + 16 + 16 * piece);
-        // 32 qs bytes serve 64 values: low nibbles the first sub-block of the pair, high the second
-        const int c = piece >> 1, l0 = 16 * (piece & 1);
-        u32x4 lo, hi;
-        lo.x = v.x & 0x0F0F0F0Fu; hi.x = (v.x >> 4) & 0x0F0F0F0Fu;
-        lo.y = v.y & 0x0F0F0F0Fu; hi.y = (v.y >> 4) & 0x0F0F0F0Fu;
-        lo.z = v.z & 0x0F0F0F0Fu; hi.z = (v.z >> 4) & 0x0F0F0F0Fu;
-        lo.w = v.w & 0x0F0F0F0Fu; hi.w = (v.w >> 4) & 0x0F0F0F0Fu;
-        *(u32x4 *)(sW + r * kLd + 64 * c + l0) = lo;
-        *(u32x4 *)(sW + r * kLd + 64 * c + 32 + l0) = hi;
+        for (int it = 0; it < N; ++it) {
+            const int blk = (tid + NT * it) & 7;
+            const int64_t b = kb * 8 + blk;
+            ds[it] = 0u;
+            c0[it] = u32x4{0u, 0u, 0u, 0u};
+            c1[it] = c0[it];
+            if (acol[it] >= 0 && b < nb32) {
+                const uint8_t *src = xq + (acol[it] * nb32 + b) * kQ8_1Bytes;
+                ds[it] = *(const uint32_t *)src;
+                c0[it] = ld16(src + 4);
+                c1[it] = ld16(src + 20);
+            }
+        }
     }
-}
+    template <int T>
+    __device__ __forceinline__ void store(uint8_t *sm) const {
+        const int tid = threadIdx.x;
+        int8_t *sA = (int8_t *)(sm + Smem<T, J>::A_OFF);
+        float2 *sX = (float2 *)(sm + Smem<T, J>::X_OFF);
+#pragma unroll
+        for (int it = 0; it < N; ++it) {
+            const int i = tid + NT * it;
+            const int col = i >> 3, blk = i & 7;
+            *(u32x4 *)(sA + col * kLd + 32 * blk) = c0[it];
+            *(u32x4 *)(sA + col * kLd + 32 * blk + 16) = c1[it];
+            sX[blk * J + col] = make_float2(h2f((uint16_t)(ds[it] & 0xFFFF)), h2f((uint16_t)(ds[it] >> 16)));
+        }
+    }
+};
 
-template <int T, int J>
-__device__ __forceinline__ void stage_weight_scales(uint8_t *sm, const uint8_t *wbase, int64_t row_bytes,
-                                                    int64_t r0, int64_t rows, int64_t kb, int64_t nb32) {
-    const int tid = threadIdx.x;
-    float *sWs = (float *)(sm + Smem<T, J>::WS_OFF);
-    float *sWm = (float *)(sm + Smem<T, J>::WM_OFF);
-    if constexpr (T == kQ4_K) {
+// ---------------------------------------------------------------------------------------------
+// Weight tile fetch / park, rows [r0, r0+128) of step kb.
+// ---------------------------------------------------------------------------------------------
+template <int T, int NT> struct WFetch;
+
+// Q4_K: qs pieces (row i/8, 16-byte piece i%8 of the 128 qs bytes) and the row headers.
+template <int NT> struct WFetch<kQ4_K, NT> {
+    static constexpr int N = 1024 / NT;
+    u32x4 q[N], h;
+    __device__ __forceinline__ void fetch(const uint8_t *wbase, int64_t row_bytes, int64_t r0, int64_t rows,
+                                          int64_t kb, int64_t) {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int it = 0; it < N; ++it) {
+            const int i = tid + NT * it;
+            const int64_t row = r0 + (i >> 3);
+            q[it] = row < rows ? ld16(wbase + row * row_bytes + kb * 144 + 16 + 16 * (i & 7)) : u32x4{0u, 0u, 0u, 0u};
+        }
+        h = u32x4{0u, 0u, 0u, 0u};
+        if (tid < kTI && r0 + tid < rows) h = ld16(wbase + (r0 + tid) * row_bytes + kb * 144);
+    }
+    template <int J>
+    __device__ __forceinline__ void store(uint8_t *sm, const uint8_t *, int64_t, int64_t, int64_t, int64_t,
+                                          int64_t) const {
+        const int tid = threadIdx.x;
+        uint8_t *sW = sm + Smem<kQ4_K, J>::W_OFF;
+#pragma unroll
+        for (int it = 0; it < N; ++it) {
+            const int i = tid + NT * it;
+            *(u32x4 *)(sW + (i >> 3) * kLd4 + 16 * (i & 7)) = q[it];
+        }
         if (tid < kTI) {
-            const int64_t row = r0 + tid;
-            u32x4 h = {0u, 0u, 0u, 0u};
-            if (row < rows) h = ld16(wbase + row * row_bytes + kb * 144);
+            float *sWs = (float *)(sm + Smem<kQ4_K, J>::WS_OFF);
+            float *sWm = (float *)(sm + Smem<kQ4_K, J>::WM_OFF);
             const float d = h2f((uint16_t)(h.x & 0xFFFF)), dmin = h2f((uint16_t)(h.x >> 16));
             const uint32_t sc_lo = h.y & 0x3F3F3F3Fu, m_lo = h.z & 0x3F3F3F3Fu;
             const uint32_t sc_hi = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
@@ -90,216 +143,279 @@ __device__ __forceinline__ void stage_weight_scales(uint8_t *sm, const uint8_t *
                 const uint32_t scw = j < 4 ? sc_lo : sc_hi, mw = j < 4 ? m_lo : m_hi;
                 const int sh = 8 * (j & 3);
                 sWs[j * kTI + tid] = d * (float)((scw >> sh) & 0xFF);
-                sWm[j * kTI + tid] = dmin * (float)((mw >> sh) & 0xFF);
+                sWm[j * kTI + tid] = -(dmin * (float)((mw >> sh) & 0xFF));
+            }
+        }
+    }
+};
+
+// Q8_0: 16 code bytes per (row, block, half) and the fp16 d per (row, block); blocks past the end
+// of a ragged last step read as zero.
+template <int NT> struct WFetch<kQ8_0, NT> {
+    static constexpr int NQ = 2048 / NT, ND = 1024 / NT;
+    u32x4 q[NQ];
+    uint16_t d[ND];
+    __device__ __forceinline__ void fetch(const uint8_t *wbase, int64_t row_bytes, int64_t r0, int64_t rows,
+                                          int64_t kb, int64_t nb32) {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int it = 0; it < NQ; ++it) {
+            const int i = tid + NT * it;
+            const int64_t row = r0 + (i >> 4), b = kb * 8 + ((i >> 1) & 7);
+            q[it] = (row < rows && b < nb32) ? ld16(wbase + row * row_bytes + b * 34 + 2 + 16 * (i & 1))
+                                             : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int it = 0; it < ND; ++it) {
+            const int i = tid + NT * it;
+            const int64_t row = r0 + (i >> 3), b = kb * 8 + (i & 7);
+            d[it] = (row < rows && b < nb32) ? ld2(wbase + row * row_bytes + b * 34) : (uint16_t)0;
+        }
+    }
+    template <int J>
+    __device__ __forceinline__ void store(uint8_t *sm, const uint8_t *, int64_t, int64_t, int64_t, int64_t,
+                                          int64_t) const {
+        const int tid = threadIdx.x;
+        uint8_t *sW = sm + Smem<kQ8_0, J>::W_OFF;
+        float *sWs = (float *)(sm + Smem<kQ8_0, J>::WS_OFF);
+#pragma unroll
+        for (int it = 0; it < NQ; ++it) {
+            const int i = tid + NT * it;
+            *(u32x4 *)(sW + (i >> 4) * kLd + 32 * ((i >> 1) & 7) + 16 * (i & 1)) = q[it];
+        }
+#pragma unroll
+        for (int it = 0; it < ND; ++it) {
+            const int i = tid + NT * it;
+            sWs[(i & 7) * kTI + (i >> 3)] = h2f(d[it]);
+        }
+    }
+};
+
+// Q6_K: unpacked straight from HBM into the two planes at park time (no register prefetch).
+template <int NT> struct WFetch<kQ6_K, NT> {
+    __device__ __forceinline__ void fetch(const uint8_t *, int64_t, int64_t, int64_t, int64_t, int64_t) {}
+    template <int J>
+    __device__ __forceinline__ void store(uint8_t *sm, const uint8_t *wbase, int64_t row_bytes, int64_t r0,
+                                          int64_t rows, int64_t kb, int64_t) const {
+        const int tid = threadIdx.x;
+        int8_t *sLo = (int8_t *)(sm + Smem<kQ6_K, J>::W_OFF);
+        int8_t *sHi = sLo + kTI * kLd;
+#pragma unroll 2
+        for (int it = 0; it < 2048 / NT; ++it) {
+            const int i = tid + NT * it;               // (row, 16-value group G): 128 x 16
+            const int r = i >> 4, G = i & 15;
+            const int64_t row = r0 + r;
+            uint32_t lo_w[4] = {0u, 0u, 0u, 0u}, hi_w[4] = {0u, 0u, 0u, 0u};
+            if (row < rows) {
+                const uint8_t *blk = wbase + row * row_bytes + kb * 210;
+                const int hh = G >> 3, gq = (G & 7) >> 1, l0 = 16 * (G & 1);
+                const u32x4 ql = ld16(blk + 64 * hh + 32 * (gq & 1) + l0);
+                const u32x4 qh = ld16(blk + 128 + 32 * hh + l0);
+                const int sc = (int)(int8_t)blk[192 + G];
+                const int nsh = gq < 2 ? 0 : 4, tsh = 2 * gq;
+                const uint32_t qlw[4] = {ql.x, ql.y, ql.z, ql.w}, qhw[4] = {qh.x, qh.y, qh.z, qh.w};
+#pragma unroll
+                for (int dd = 0; dd < 4; ++dd) {
+                    const uint32_t code6 = ((qlw[dd] >> nsh) & 0x0F0F0F0Fu) | (((qhw[dd] >> tsh) & 0x03030303u) << 4);
+                    uint32_t lo = 0, hi = 0;
+#pragma unroll
+                    for (int bi = 0; bi < 4; ++bi) {
+                        const int v = sc * ((int)((code6 >> (8 * bi)) & 0xFF) - 32);
+                        lo |= (uint32_t)(v & 127) << (8 * bi);
+                        hi |= (uint32_t)((v >> 7) & 0xFF) << (8 * bi);
+                    }
+                    lo_w[dd] = lo;
+                    hi_w[dd] = hi;
+                }
+            }
+            *(u32x4 *)(sLo + r * kLd + 16 * G) = u32x4{lo_w[0], lo_w[1], lo_w[2], lo_w[3]};
+            *(u32x4 *)(sHi + r * kLd + 16 * G) = u32x4{hi_w[0], hi_w[1], hi_w[2], hi_w[3]};
+        }
+        if (tid < kTI) {
+            float *sWs = (float *)(sm + Smem<kQ6_K, J>::WS_OFF);
+            const int64_t row = r0 + tid;
+            sWs[tid] = row < rows ? h2f(ld2(wbase + row * row_bytes + kb * 210 + 208)) : 0.f;
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------------------------
+// One 256-value step of MFMAs + fixups for this wave's 32 rows x JW columns.  Wave wid: row wave
+// rw = wid % 4 (rows 32*rw..), column wave cw = wid / 4 (columns JW*cw..).  Accumulator block cb,
+// element e of lane l: row 32*rw + 8*(e/4) + 4*(l/32) + e%4, column JW*cw + 32*cb + l%32.
+// The per-element scale w_scale[row] * d_a[col] of a 32x32 block is their outer product, made
+// on the matrix pipe, so the vector ALU does two operations per result: int->float and a
+// multiply-add.
+// ---------------------------------------------------------------------------------------------
+template <int T, int J, bool DBG>
+__device__ __forceinline__ void tile_step(const uint8_t *sm, f32x16 (&acc)[Cfg<J>::NCB], int64_t kb, int64_t nb32,
+                                          int32_t *dbg, int64_t rows, int64_t n, int64_t r0, int64_t c0) {
+    using L = Smem<T, J>;
+    constexpr int NCB = Cfg<J>::NCB, JW = Cfg<J>::JW;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int rw = wid & 3, cw = wid >> 2;
+    const int8_t *sA = (const int8_t *)(sm + L::A_OFF);
+    const float *sWs = (const float *)(sm + L::WS_OFF);
+    const float2 *sX = (const float2 *)(sm + L::X_OFF);
+    const int arow = 32 * rw + (lane & 31);
+    const int h = lane >> 5, koff = 16 * h;
+    const int colw = JW * cw + (lane & 31);   // + 32*cb
+    const i32x16 zero = {};
+    const f32x16 fzero = {};
+
+    // Per-element scales of sub-block sb: the outer product of this wave's 32 row scales and its
+    // columns' d_a.  Two 32-column blocks come from one two-block v_mfma_f32_32x32x1_f32 (block b
+    // takes rows from lanes 32b.. and columns from lanes 32b..: here the same rows, the block's
+    // columns); a single block from v_mfma_f32_32x32x2_f32 with the second K slot zero.
+    auto scales = [&](int sb, float wsr, f32x16 (&S)[NCB]) {
+        if constexpr (NCB == 2) {
+            const float da = sX[sb * J + JW * cw + 32 * h + (lane & 31)].x;
+            const f32x32 S2 = __builtin_amdgcn_mfma_f32_32x32x1f32(wsr, da, f32x32{}, 0, 0, 0);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                S[0][e] = S2[e];
+                S[1][e] = S2[16 + e];
+            }
+        } else {
+            const float da = h ? 0.f : sX[sb * J + colw].x;
+            S[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(h ? 0.f : wsr, da, fzero, 0, 0, 0);
+        }
+    };
+    // D of block (sb, cb) folded into the accumulators with its scales (or exported raw)
+    auto fix = [&](int cb, int sb, const i32x16 &D, const f32x16 &S) {
+        const int bcol = colw + 32 * cb;
+        if (DBG) {
+            const int64_t col = c0 + bcol;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int64_t row = r0 + 32 * rw + 4 * h + 8 * (e >> 2) + (e & 3);
+                if (row < rows && col < n) dbg[(col * rows + row) * nb32 + kb * 8 + sb] = D[e];
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[cb][e] = fmaf((float)D[e], S[e], acc[cb][e]);
+        }
+    };
+
+    if constexpr (T == kQ4_K) {
+        const uint8_t *sW = sm + L::W_OFF;
+#pragma unroll 1
+        for (int sb = 0; sb < 8; ++sb) {
+            // qs bytes 32*(sb/2)+16h .. +15: low nibbles = values 16h.. of the even sub-block of
+            // the pair, high nibbles = of the odd one
+            const u32x4 q = *(const u32x4 *)(sW + arow * kLd4 + 32 * (sb >> 1) + koff);
+            const int sh = 4 * (sb & 1);
+            const u32x4 aop = {(q.x >> sh) & 0x0F0F0F0Fu, (q.y >> sh) & 0x0F0F0F0Fu, (q.z >> sh) & 0x0F0F0F0Fu,
+                               (q.w >> sh) & 0x0F0F0F0Fu};
+            f32x16 S[NCB];
+            if (!DBG) scales(sb, sWs[sb * kTI + arow], S);
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                const u32x4 b = *(const u32x4 *)(sA + (colw + 32 * cb) * kLd + 32 * sb + koff);
+                fix(cb, sb, mfma32x32x32(aop, b, zero), S[cb]);
+            }
+        }
+        if (!DBG) {
+            // min term: acc += sum over the 8 sub-blocks of (-dmin*m)[row] * s_a[col], as four
+            // K=2 fp32 MFMAs (k = lane/32 selects sub-block 2i+k)
+            const float *sWm = (const float *)(sm + L::WM_OFF);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int sb = 2 * i + h;
+                const float am = sWm[sb * kTI + arow];
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(am, sX[sb * J + colw + 32 * cb].y, acc[cb], 0, 0, 0);
             }
         }
     } else if constexpr (T == kQ8_0) {
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int i = tid + 256 * it;          // (row, block) pairs: 128 x 8
-            const int r = i >> 3, j = i & 7;
-            const int64_t row = r0 + r, b = kb * 8 + j;
-            float d = 0.f;
-            if (row < rows && b < nb32) d = h2f(ld2(wbase + row * row_bytes + b * 34));
-            sWs[j * kTI + r] = d;
-        }
-    } else {   // Q6_K: the per-row super-block scale d
-        if (tid < kTI) {
-            const int64_t row = r0 + tid;
-            float d = 0.f;
-            if (row < rows) d = h2f(ld2(wbase + row * row_bytes + kb * 210 + 208));
-            sWs[tid] = d;
-        }
-    }
-}
-
-template <int J>
-__device__ __forceinline__ void stage_weights_q8_0(uint8_t *sm, const uint8_t *wbase, int64_t row_bytes,
-                                                   int64_t r0, int64_t rows, int64_t kb, int64_t nb32) {
-    const int tid = threadIdx.x;
-    int8_t *sW = (int8_t *)sm;
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-        const int i = tid + 256 * it;              // (row, block, half): 128 x 8 x 2
-        const int r = i >> 4, j = (i >> 1) & 7, half = i & 1;
-        const int64_t row = r0 + r, b = kb * 8 + j;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (row < rows && b < nb32) v = ld16(wbase + row * row_bytes + b * 34 + 2 + 16 * half);
-        *(u32x4 *)(sW + r * kLd + 32 * j + 16 * half) = v;
-    }
-}
-
-// Q6_K: codes folded with their int8 scale, split into lo (plane 0) and hi (plane 1).
-__device__ __forceinline__ void stage_weights_q6_k(uint8_t *sm, const uint8_t *wbase, int64_t row_bytes,
-                                                   int64_t r0, int64_t rows, int64_t kb) {
-    const int tid = threadIdx.x;
-    int8_t *sLo = (int8_t *)sm;
-    int8_t *sHi = (int8_t *)sm + kTI * kLd;
-#pragma unroll 2
-    for (int it = 0; it < 8; ++it) {
-        const int i = tid + 256 * it;              // (row, 16-value group G): 128 x 16
-        const int r = i >> 4, G = i & 15;
-        const int64_t row = r0 + r;
-        uint32_t lo_w[4] = {0u, 0u, 0u, 0u}, hi_w[4] = {0u, 0u, 0u, 0u};
-        if (row < rows) {
-            const uint8_t *blk = wbase + row * row_bytes + kb * 210;
-            const int h = G >> 3, gq = (G & 7) >> 1, l0 = 16 * (G & 1);
-            const u32x4 ql = ld16(blk + 64 * h + 32 * (gq & 1) + l0);
-            const u32x4 qh = ld16(blk + 128 + 32 * h + l0);
-            const int sc = (int)(int8_t)blk[192 + G];
-            const int nsh = gq < 2 ? 0 : 4, tsh = 2 * gq;
-            const uint32_t qlw[4] = {ql.x, ql.y, ql.z, ql.w}, qhw[4] = {qh.x, qh.y, qh.z, qh.w};
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                const uint32_t code6 = ((qlw[d] >> nsh) & 0x0F0F0F0Fu) | (((qhw[d] >> tsh) & 0x03030303u) << 4);
-                uint32_t lo = 0, hi = 0;
-#pragma unroll
-                for (int bi = 0; bi < 4; ++bi) {
-                    const int v = sc * ((int)((code6 >> (8 * bi)) & 0xFF) - 32);
-                    lo |= (uint32_t)(v & 127) << (8 * bi);
-                    hi |= (uint32_t)((v >> 7) & 0xFF) << (8 * bi);
-                }
-                lo_w[d] = lo;
-                hi_w[d] = hi;
-            }
-        }
-        const u32x4 lo4 = {lo_w[0], lo_w[1], lo_w[2], lo_w[3]};
-        const u32x4 hi4 = {hi_w[0], hi_w[1], hi_w[2], hi_w[3]};
-        *(u32x4 *)(sLo + r * kLd + 16 * G) = lo4;
-        *(u32x4 *)(sHi + r * kLd + 16 * G) = hi4;
-    }
-}
-
-// ---------------------------------------------------------------------------------------------
-// Activation tile staging: J columns of the step's 8 q8_1 blocks -> int8 codes + fp32 (d, s).
-// acol[] holds this thread's activation rows (or -1 for columns beyond the tile's range).
-// ---------------------------------------------------------------------------------------------
-template <int T, int J>
-__device__ __forceinline__ void stage_acts(uint8_t *sm, const uint8_t *xq, int64_t nb32, int64_t kb,
-                                           const int64_t (&acol)[J / 16], const int64_t (&tcol)[J / 32]) {
-    const int tid = threadIdx.x;
-    int8_t *sA = (int8_t *)(sm + Smem<T, J>::A_OFF);
-    float2 *sX = (float2 *)(sm + Smem<T, J>::X_OFF);
-#pragma unroll
-    for (int it = 0; it < J / 16; ++it) {
-        const int i = tid + 256 * it;              // (column, block, half): J x 8 x 2
-        const int c = i >> 4, j = (i >> 1) & 7, half = i & 1;
-        const int64_t b = kb * 8 + j;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (acol[it] >= 0 && b < nb32) v = ld16(xq + (acol[it] * nb32 + b) * kQ8_1Bytes + 4 + 16 * half);
-        *(u32x4 *)(sA + c * kLd + 32 * j + 16 * half) = v;
-    }
-#pragma unroll
-    for (int it = 0; it < J / 32; ++it) {
-        const int i = tid + 256 * it;              // (block, column): 8 x J
-        const int j = i / J, c = i % J;
-        const int64_t b = kb * 8 + j;
-        float2 v = make_float2(0.f, 0.f);
-        if (tcol[it] >= 0 && b < nb32) {
-            const uint32_t ds = *(const uint32_t *)(xq + (tcol[it] * nb32 + b) * kQ8_1Bytes);
-            v = make_float2(h2f((uint16_t)(ds & 0xFFFF)), h2f((uint16_t)(ds >> 16)));
-        }
-        sX[j * J + c] = v;
-    }
-}
-
-// ---------------------------------------------------------------------------------------------
-// One 256-value step of MFMAs + fixups for this wave's 32 rows and all J columns.
-// ---------------------------------------------------------------------------------------------
-template <int T, int J, bool DBG>
-__device__ __forceinline__ void tile_step(const uint8_t *sm, float (&acc)[J / 32][16], int64_t kb, int64_t nb32,
-                                          int32_t *dbg, int64_t rows, int64_t n, int64_t r0, int64_t c0) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int8_t *sW = (const int8_t *)sm;
-    const int8_t *sA = (const int8_t *)(sm + Smem<T, J>::A_OFF);
-    const float *sWs = (const float *)(sm + Smem<T, J>::WS_OFF);
-    const float *sWm = (const float *)(sm + Smem<T, J>::WM_OFF);
-    const float2 *sX = (const float2 *)(sm + Smem<T, J>::X_OFF);
-    const int arow = 32 * wave + (lane & 31);
-    const int koff = 16 * (lane >> 5);
-    const int rbase = 32 * wave + 4 * (lane >> 5);   // + 8*(e/4) + e%4
-    float d6[16];
-    if constexpr (T == kQ6_K) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const f32x4 v = *(const f32x4 *)(sWs + rbase + 8 * q);
-            d6[4 * q] = v.x; d6[4 * q + 1] = v.y; d6[4 * q + 2] = v.z; d6[4 * q + 3] = v.w;
-        }
-    }
+        const int8_t *sW = (const int8_t *)(sm + L::W_OFF);
 #pragma unroll 1
-    for (int j = 0; j < 8; ++j) {
-        if (kb * 8 + j >= nb32) break;   // Q8_0 ragged last step (workgroup-uniform)
-        const u32x4 a = *(const u32x4 *)(sW + arow * kLd + 32 * j + koff);
-        u32x4 a_hi;
-        if constexpr (T == kQ6_K) a_hi = *(const u32x4 *)(sW + kTI * kLd + arow * kLd + 32 * j + koff);
-        float ws[16], wm[16];
-        if constexpr (T != kQ6_K) {
+        for (int j = 0; j < 8; ++j) {
+            if (kb * 8 + j >= nb32) break;   // ragged last step (workgroup-uniform)
+            const u32x4 a = *(const u32x4 *)(sW + arow * kLd + 32 * j + koff);
+            f32x16 S[NCB];
+            if (!DBG) scales(j, sWs[j * kTI + arow], S);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const f32x4 v = *(const f32x4 *)(sWs + j * kTI + rbase + 8 * q);
-                ws[4 * q] = v.x; ws[4 * q + 1] = v.y; ws[4 * q + 2] = v.z; ws[4 * q + 3] = v.w;
-                if constexpr (T == kQ4_K) {
-                    const f32x4 u = *(const f32x4 *)(sWm + j * kTI + rbase + 8 * q);
-                    wm[4 * q] = u.x; wm[4 * q + 1] = u.y; wm[4 * q + 2] = u.z; wm[4 * q + 3] = u.w;
-                }
+            for (int cb = 0; cb < NCB; ++cb) {
+                const u32x4 b = *(const u32x4 *)(sA + (colw + 32 * cb) * kLd + 32 * j + koff);
+                fix(cb, j, mfma32x32x32(a, b, zero), S[cb]);
             }
         }
+    } else {
+        const int8_t *sW = (const int8_t *)(sm + L::W_OFF);
+        const float d6 = sWs[arow];
+#pragma unroll 1
+        for (int j = 0; j < 8; ++j) {
+            const u32x4 a = *(const u32x4 *)(sW + arow * kLd + 32 * j + koff);
+            const u32x4 a_hi = *(const u32x4 *)(sW + kTI * kLd + arow * kLd + 32 * j + koff);
+            f32x16 S[NCB];
+            if (!DBG) scales(j, d6, S);
 #pragma unroll
-        for (int cb = 0; cb < J / 32; ++cb) {
-            const int bcol = 32 * cb + (lane & 31);
-            const u32x4 b = *(const u32x4 *)(sA + bcol * kLd + 32 * j + koff);
-            const i32x16 zero = {};
-            i32x16 D = mfma32x32x32(a, b, zero);
-            if constexpr (T == kQ6_K) {
+            for (int cb = 0; cb < NCB; ++cb) {
+                const u32x4 b = *(const u32x4 *)(sA + (colw + 32 * cb) * kLd + 32 * j + koff);
+                i32x16 D = mfma32x32x32(a, b, zero);
                 const i32x16 Dh = mfma32x32x32(a_hi, b, zero);
 #pragma unroll
                 for (int e = 0; e < 16; ++e) D[e] = (Dh[e] << 7) + D[e];
-            }
-            if (DBG) {
-                const int64_t col = c0 + bcol;
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int64_t row = r0 + rbase + 8 * (e >> 2) + (e & 3);
-                    if (row < rows && col < n) dbg[(col * rows + row) * nb32 + kb * 8 + j] = D[e];
-                }
-            } else {
-                const float2 x = sX[j * J + bcol];
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    if constexpr (T == kQ4_K) acc[cb][e] += (float)D[e] * (ws[e] * x.x) - wm[e] * x.y;
-                    else if constexpr (T == kQ8_0) acc[cb][e] += (float)D[e] * (ws[e] * x.x);
-                    else acc[cb][e] += (float)D[e] * (d6[e] * x.x);
-                }
+                fix(cb, j, D, S[cb]);
             }
         }
     }
 }
 
-template <int T, int J>
-__device__ __forceinline__ void stage_step(uint8_t *sm, const uint8_t *wbase, int64_t row_bytes, int64_t r0,
-                                           int64_t rows, int64_t kb, int64_t nb32, const uint8_t *xq,
-                                           const int64_t (&acol)[J / 16], const int64_t (&tcol)[J / 32]) {
-    if constexpr (T == kQ4_K) stage_weights_q4_k(sm, wbase, row_bytes, r0, rows, kb);
-    else if constexpr (T == kQ8_0) stage_weights_q8_0<J>(sm, wbase, row_bytes, r0, rows, kb, nb32);
-    else stage_weights_q6_k(sm, wbase, row_bytes, r0, rows, kb);
-    stage_weight_scales<T, J>(sm, wbase, row_bytes, r0, rows, kb, nb32);
-    stage_acts<T, J>(sm, xq, nb32, kb, acol, tcol);
+// One tile's steps [kb0, kb1): fetch step kb+1 into registers while step kb computes.
+template <int T, int J, bool DBG>
+__device__ __forceinline__ void run_tile(uint8_t *sm, f32x16 (&acc)[Cfg<J>::NCB], const uint8_t *wbase,
+                                         int64_t row_bytes, int64_t r0, int64_t rows, int64_t kb0, int64_t kb1,
+                                         int64_t nb32, const uint8_t *xq, const int64_t (&acol)[ActFetch<J>::N],
+                                         int32_t *dbg, int64_t n, int64_t c0) {
+    WFetch<T, Cfg<J>::NT> wf;
+    ActFetch<J> af;
+    wf.fetch(wbase, row_bytes, r0, rows, kb0, nb32);
+    af.fetch(xq, nb32, kb0, acol);
+    for (int64_t kb = kb0; kb < kb1; ++kb) {
+        __syncthreads();   // the previous step's LDS reads are done
+        wf.template store<J>(sm, wbase, row_bytes, r0, rows, kb, nb32);
+        af.template store<T>(sm);
+        __syncthreads();
+        if (kb + 1 < kb1) {
+            wf.fetch(wbase, row_bytes, r0, rows, kb + 1, nb32);
+            af.fetch(xq, nb32, kb + 1, acol);
+        }
+        tile_step<T, J, DBG>(sm, acc, kb, nb32, dbg, rows, n, r0, c0);
+    }
 }
 
-// Accumulator (lane, e) -> tile coordinates.
-__device__ __forceinline__ int acc_row(int e) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    return 32 * wave + 4 * (lane >> 5) + 8 * (e >> 2) + (e & 3);
+// Writes a tile's accumulators to dst (column-major with leading dimension ld), rows < rlim and
+// columns < clim.
+template <int J>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[Cfg<J>::NCB], float *dst, int64_t ld, int64_t rlim,
+                                           int64_t clim) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int rw = wid & 3, cw = wid >> 2;
+#pragma unroll
+    for (int cb = 0; cb < Cfg<J>::NCB; ++cb) {
+        const int col = Cfg<J>::JW * cw + 32 * cb + (lane & 31);
+        if (col >= clim) continue;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int r = 32 * rw + 4 * (lane >> 5) + 8 * (e >> 2) + (e & 3);
+            if (r < rlim) dst[(int64_t)col * ld + r] = acc[cb][e];
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------------------------
 // Dense kernel: persistent over the unit's (tile, step) range.
 // ---------------------------------------------------------------------------------------------
 template <int T, int J, bool DBG>
-__global__ __launch_bounds__(256) void mmq_kernel(const uint8_t *__restrict__ w, int64_t rows, int64_t k,
-                                                  const uint8_t *__restrict__ xq, int64_t n, float *__restrict__ y,
-                                                  int32_t *__restrict__ dbg, MmqArgs args) {
+__global__ __launch_bounds__(Cfg<J>::NT, 2) void mmq_kernel(const uint8_t *__restrict__ w, int64_t rows, int64_t k,
+                                                         const uint8_t *__restrict__ xq, int64_t n,
+                                                         float *__restrict__ y, int32_t *__restrict__ dbg,
+                                                         MmqArgs args) {
     extern __shared__ __align__(16) uint8_t sm[];
+    constexpr int NA = ActFetch<J>::N, NT = Cfg<J>::NT;
     const int64_t nb32 = k / 32;
     const int64_t row_bytes = (k / Fmt<T>::QK) * Fmt<T>::BYTES;
     const int64_t u = xcd_remap(blockIdx.x, args.units);
@@ -307,7 +423,7 @@ __global__ __launch_bounds__(256) void mmq_kernel(const uint8_t *__restrict__ w,
     int64_t pos = (u * W) / args.units;
     const int64_t end = ((u + 1) * W) / args.units;
     const int64_t first = pos;
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x;
 
     while (pos < end) {
         const int64_t t = pos / args.k_iters;
@@ -316,49 +432,25 @@ __global__ __launch_bounds__(256) void mmq_kernel(const uint8_t *__restrict__ w,
         const int64_t rt = t / args.n_ct, ct = t - rt * args.n_ct;
         const int64_t r0 = rt * kTI, c0 = ct * J;
 
-        int64_t acol[J / 16], tcol[J / 32];
+        int64_t acol[NA];
 #pragma unroll
-        for (int it = 0; it < J / 16; ++it) {
-            const int64_t c = c0 + ((tid + 256 * it) >> 4);
+        for (int it = 0; it < NA; ++it) {
+            const int64_t c = c0 + ((tid + NT * it) >> 3);
             acol[it] = c < n ? c : -1;
         }
+        f32x16 acc[Cfg<J>::NCB];
 #pragma unroll
-        for (int it = 0; it < J / 32; ++it) {
-            const int64_t c = c0 + (tid + 256 * it) % J;
-            tcol[it] = (c < n && !DBG) ? c : -1;   // the debug export needs no scales
-        }
-        float acc[J / 32][16];
-#pragma unroll
-        for (int cb = 0; cb < J / 32; ++cb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[cb][e] = 0.f;
+        for (int cb = 0; cb < Cfg<J>::NCB; ++cb) acc[cb] = f32x16{};
 
-        for (int64_t kb = kb0; kb < kb1; ++kb) {
-            __syncthreads();
-            stage_step<T, J>(sm, w, row_bytes, r0, rows, kb, nb32, xq, acol, tcol);
-            __syncthreads();
-            tile_step<T, J, DBG>(sm, acc, kb, nb32, dbg, rows, n, r0, c0);
-        }
+        run_tile<T, J, DBG>(sm, acc, w, row_bytes, r0, rows, kb0, kb1, nb32, xq, acol, dbg, n, c0);
 
         if (!DBG) {
             const bool whole = kb0 == 0 && kb1 == args.k_iters;
-            float *dst;
-            int64_t ld, rlim, clim;
             if (whole || !args.write_partials) {
-                dst = y + c0 * rows + r0; ld = rows; rlim = rows - r0; clim = n - c0;
+                store_tile<J>(acc, y + c0 * rows + r0, rows, rows - r0, n - c0);
             } else {
                 const int64_t slot = 2 * u + (pos == first ? 0 : 1);
-                dst = args.partials + slot * (int64_t)kTI * J; ld = kTI; rlim = kTI; clim = J;
-            }
-#pragma unroll
-            for (int cb = 0; cb < J / 32; ++cb) {
-                const int col = 32 * cb + (lane & 31);
-                if (col >= clim) continue;
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int r = acc_row(e);
-                    if (r < rlim) dst[(int64_t)col * ld + r] = acc[cb][e];
-                }
+                store_tile<J>(acc, args.partials + slot * (int64_t)kTI * J, kTI, kTI, J);
             }
         }
         pos += kb1 - kb0;
@@ -403,10 +495,11 @@ __global__ __launch_bounds__(256) void streamk_fixup_kernel(float *__restrict__ 
 // Expert kernel: one tile per workgroup, full K; grid (row tiles, column-tile slots).
 // ---------------------------------------------------------------------------------------------
 template <int T, int J>
-__global__ __launch_bounds__(256) void mmq_id_kernel(const uint8_t *__restrict__ w, int64_t rows, int64_t k,
-                                                     const uint8_t *__restrict__ xq, float *__restrict__ y,
-                                                     ColMap cm, int32_t n_exp) {
+__global__ __launch_bounds__(Cfg<J>::NT, 2) void mmq_id_kernel(const uint8_t *__restrict__ w, int64_t rows, int64_t k,
+                                                            const uint8_t *__restrict__ xq, float *__restrict__ y,
+                                                            ColMap cm, int32_t n_exp) {
     extern __shared__ __align__(16) uint8_t sm[];
+    constexpr int NA = ActFetch<J>::N, NT = Cfg<J>::NT;
     const int64_t ct = blockIdx.y;
     if (ct >= cm.tile_start[n_exp]) return;
     // expert owning column tile ct: largest e with tile_start[e] <= ct
@@ -424,45 +517,34 @@ __global__ __launch_bounds__(256) void mmq_id_kernel(const uint8_t *__restrict__
     const uint8_t *wbase = w + (int64_t)e * cm.w_expert_stride;
     const int64_t r0 = (int64_t)blockIdx.x * kTI;
     const int64_t c0 = jt * J;
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
 
     auto arow_of = [&](int64_t c) -> int64_t {
         const int64_t pr = cm.sorted[seg + c];
         const int64_t t = pr / cm.top_k, s = pr - t * cm.top_k;
         return t * cm.x_per_tok + (cm.x_per_tok > 1 ? s : 0);
     };
-    int64_t acol[J / 16], tcol[J / 32];
+    int64_t acol[NA];
 #pragma unroll
-    for (int it = 0; it < J / 16; ++it) {
-        const int64_t c = c0 + ((tid + 256 * it) >> 4);
+    for (int it = 0; it < NA; ++it) {
+        const int64_t c = c0 + ((tid + NT * it) >> 3);
         acol[it] = c < cnt ? arow_of(c) : -1;
     }
+    f32x16 acc[Cfg<J>::NCB];
 #pragma unroll
-    for (int it = 0; it < J / 32; ++it) {
-        const int64_t c = c0 + (tid + 256 * it) % J;
-        tcol[it] = c < cnt ? arow_of(c) : -1;
-    }
-    float acc[J / 32][16];
-#pragma unroll
-    for (int cb = 0; cb < J / 32; ++cb)
-#pragma unroll
-        for (int e2 = 0; e2 < 16; ++e2) acc[cb][e2] = 0.f;
+    for (int cb = 0; cb < Cfg<J>::NCB; ++cb) acc[cb] = f32x16{};
 
     const int64_t k_iters = (k + kSuper - 1) / kSuper;
-    for (int64_t kb = 0; kb < k_iters; ++kb) {
-        __syncthreads();
-        stage_step<T, J>(sm, wbase, row_bytes, r0, rows, kb, nb32, xq, acol, tcol);
-        __syncthreads();
-        tile_step<T, J, false>(sm, acc, kb, nb32, nullptr, rows, cnt, r0, c0);
-    }
+    run_tile<T, J, false>(sm, acc, wbase, row_bytes, r0, rows, 0, k_iters, nb32, xq, acol, nullptr, cnt, c0);
+    const int rw = wid & 3, cw = wid >> 2;
 #pragma unroll
-    for (int cb = 0; cb < J / 32; ++cb) {
-        const int64_t c = c0 + 32 * cb + (lane & 31);
+    for (int cb = 0; cb < Cfg<J>::NCB; ++cb) {
+        const int64_t c = c0 + Cfg<J>::JW * cw + 32 * cb + (lane & 31);
         if (c >= cnt) continue;
         const int64_t orow = cm.sorted[seg + c];
 #pragma unroll
         for (int e2 = 0; e2 < 16; ++e2) {
-            const int64_t r = r0 + acc_row(e2);
+            const int64_t r = r0 + 32 * rw + 4 * (lane >> 5) + 8 * (e2 >> 2) + (e2 & 3);
             if (r < rows) y[orow * rows + r] = acc[cb][e2];
         }
     }
@@ -483,7 +565,7 @@ static hipError_t launch_mmq_t(const uint8_t *w, int64_t rows, int64_t k, const 
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL(kern, dim3((unsigned)p.units), dim3(256), smem, s, w, rows, k, xq, n, y, dbg, a);
+    hipLaunchKernelGGL(kern, dim3((unsigned)p.units), dim3(Cfg<J>::NT), smem, s, w, rows, k, xq, n, y, dbg, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || DBG || !p.stream_k) return e;
     hipLaunchKernelGGL(streamk_fixup_kernel<J>, dim3((unsigned)p.ntiles), dim3(256), 0, s, y, rows, n, a);
@@ -525,7 +607,7 @@ static hipError_t launch_mmq_id_t(const uint8_t *w, int64_t rows, int64_t k, con
     }
     if (max_ct <= 0) return hipSuccess;
     dim3 grid((unsigned)((rows + kTI - 1) / kTI), (unsigned)max_ct);
-    hipLaunchKernelGGL(kern, grid, dim3(256), smem, s, w, rows, k, xq, y, cm, n_exp);
+    hipLaunchKernelGGL(kern, grid, dim3(Cfg<J>::NT), smem, s, w, rows, k, xq, y, cm, n_exp);
     return hipGetLastError();
 }
 

@@ -44,8 +44,8 @@ def test_worked_example_tile_count():
     assert (rows_tiles, col_tiles, rows_tiles * col_tiles) == (86, 64, 5504)
     p = qmm.plan_dense(qmm.Q4_K, 11008, 4096, 8192, nsm=108)
     assert p["regime"] == 2 and p["tile_j"] == 128 and p["ntiles"] == 5504
-    # 5504 tiles is about 25.5 waves on 108 units (two resident per unit here): efficiency well
-    # above the stream-K threshold, so one workgroup per tile
+    # 5504 tiles is about 51 rounds on 108 units (one 128-column tile resident per unit):
+    # efficiency well above the stream-K threshold, so one workgroup per tile
     assert p["stream_k"] == 0 and p["units"] == 5504
     # MoE average: 8192 tokens x top-2 over 64 experts
     assert 8192 * 2 // 64 == 256
