@@ -27,13 +27,15 @@ struct ColMap {
 hipError_t launch_mmvq(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n,
                        float *y, int32_t *dbg, const ColMap *cm, int64_t n_exp, hipStream_t s);
 
-// fp32-input matrix-vector product with the q8_1 quantization done inside the dot4 kernel (no
-// separate quantize launch): applies to the calls the dot4 kernel would take (dense, few columns).
+// fp32-input matrix-vector product with the q8_1 quantization done inside the dot4 or the
+// LDS-staged kernel (no separate quantize launch): dense calls either kernel would take.
 bool mmvq_fused_applies(int type, const void *w, int64_t k, const float *x, int64_t n);
 hipError_t launch_mmvq_fused(int type, const uint8_t *w, int64_t rows, int64_t k, const float *x, int64_t n, float *y,
                              hipStream_t s);
 hipError_t launch_mmvq_dot4_f32(int type, const uint8_t *w, int64_t rows, int64_t k, const float *x, int64_t n,
                                 float *y, hipStream_t s);
+hipError_t launch_mmvq_stream_f32(int type, const uint8_t *w, int64_t rows, int64_t k, const float *x, int64_t n,
+                                  float *y, hipStream_t s);
 
 // Tuning: 256-value steps per wave of the register-streamed matrix-vector kernel (0 = automatic).
 void set_mmvq_steps_per_wave(int spw);

@@ -469,17 +469,33 @@ void set_mmvq_kernel(int which) { g_mv_kernel = which; }
 // Largest column count the automatic choice sends to the dot4 kernel, per type.
 static int dot4_auto_cols(int type) { return type == kQ4_K ? 2 : type == kQ8_0 ? 3 : 0; }
 
-bool mmvq_fused_applies(int type, const void *w, int64_t k, const float *x, int64_t n) {
+// Which fused kernel serves an fp32-input call: 3 dot4, 2 LDS-staged MFMA, 0 none.
+static int fused_kernel(int type, const void *w, int64_t k, const float *x, int64_t n) {
     const int kc = g_mv_kernel;
-    if (kc != 0 && kc != 3) return false;
-    const int lim = kc == 3 ? mmvq_dot4_max_cols() : dot4_auto_cols(type);
-    return n >= 1 && n <= lim && (uintptr_t)x % 16 == 0 && mmvq_dot4_supported(type, w, k, x, nullptr);
+    if (n < 1 || (uintptr_t)x % 16 != 0) return 0;
+    if (kc == 0 || kc == 3) {
+        const int lim = kc == 3 ? mmvq_dot4_max_cols() : dot4_auto_cols(type);
+        if (n <= lim && mmvq_dot4_supported(type, w, k, x, nullptr)) return 3;
+        if (kc == 3) return 0;
+    }
+    // The LDS-staged kernel quantizes a step's blocks with 8 lanes per block; measured against a
+    // separate quantize launch that pays off up to 3 columns (4096 x 4096: 1-2 us saved per call
+    // at n <= 3, 0.5-3 us lost at n = 5..8).
+    if ((kc == 0 || kc == 2) && n <= 3 && mmvq_stream_supported(type, w, k, x, nullptr)) return 2;
+    return 0;
+}
+
+bool mmvq_fused_applies(int type, const void *w, int64_t k, const float *x, int64_t n) {
+    return fused_kernel(type, w, k, x, n) != 0;
 }
 
 hipError_t launch_mmvq_fused(int type, const uint8_t *w, int64_t rows, int64_t k, const float *x, int64_t n, float *y,
                              hipStream_t s) {
-    if (!mmvq_fused_applies(type, w, k, x, n)) return hipErrorInvalidValue;
-    return launch_mmvq_dot4_f32(type, w, rows, k, x, n, y, s);
+    switch (fused_kernel(type, w, k, x, n)) {
+        case 3: return launch_mmvq_dot4_f32(type, w, rows, k, x, n, y, s);
+        case 2: return launch_mmvq_stream_f32(type, w, rows, k, x, n, y, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_mmvq(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y,

@@ -16,11 +16,15 @@
 //   Q4_K  acc += D * (d*sc) * d_a - (dmin*m) * s_a
 //   Q6_K  acc += D * (d*sc) * d_a      (D includes -32 * sum q_a via a second MFMA)
 //   Q8_0  acc += D * d_w * d_a
+// For fp32 activations (dense) the wave quantizes its step's blocks itself, 8 lanes per block with
+// the arithmetic of the standalone quantize kernel (q8_1.hpp), and parks the q8_1 bytes in the
+// same place -- one launch instead of two.
 // Requirements (checked by the host): weights, activations and every row 16-byte aligned, and
 // K a multiple of 256, so each step's pieces are whole 16-byte units inside the row.
 #include "common.hpp"
 #include "launch.hpp"
 #include "mv_cols.hpp"
+#include "q8_1.hpp"
 
 namespace qmm {
 
@@ -68,8 +72,8 @@ struct MvArgs {
     int32_t n;            // dense column count
 };
 
-template <int T, bool DBG, bool EXPERT>
-__global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__restrict__ w, const uint8_t *__restrict__ xq,
+template <int T, bool DBG, bool EXPERT, bool F32>
+__global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__restrict__ w, const void *__restrict__ xin,
                                                           float *__restrict__ y, int32_t *__restrict__ dbg,
                                                           MvArgs P, ColMap cm) {
     using S = Stage<T>;
@@ -130,22 +134,48 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
                          : (int64_t)c * col_bytes + 16 * ja;
     }
     const uint32_t pa = (uint32_t)cq * kActStep + 16u * ja;
+    // fp32 input: columns 0..3 of a step are fetched ahead (registers), 4..7 at park time
+    float4 xv[4];
+    const float *xf = (const float *)xin + 4 * lane;
+    const size_t xstride = (size_t)P.nsteps * kSuper;
     auto load_a = [&](int s) {
-        const uint8_t *astep = xq + (uint32_t)(s * kActStep);
+        if constexpr (F32) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (i < nia && alive[i]) av[i] = *(const u32x4 *)(astep + aoff[i]);
+            for (int c = 0; c < 4; ++c)
+                if (c < ncols) xv[c] = *(const float4 *)(xf + s * kSuper + c * xstride);
+        } else {
+            const uint8_t *astep = (const uint8_t *)xin + (uint32_t)(s * kActStep);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (i < nia && alive[i]) av[i] = *(const u32x4 *)(astep + aoff[i]);
+        }
     };
     if (my_steps > 0) load_a(wave);
 
-    auto park = [&]() {
+    auto park = [&](int s) {
+        if constexpr (F32) {
+            // fp32 input: column c's step values, lane = (block lane/8, values 4*(lane%8)..); done
+            // before the weights are parked so late loads overlap the weights' arrival
+            const int b = lane >> 3, sub = lane & 7;
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                if (c < ncols) {
+                    const float4 v = c < 4 ? xv[c & 3] : *(const float4 *)(xf + s * kSuper + c * xstride);
+                    const Q81Lane q = quantize_q8_1_lane(v);
+                    uint8_t *blk = st + WB + c * kActStep + b * kQ8_1Bytes;
+                    *(uint32_t *)(blk + 4 + 4 * sub) = q.codes;
+                    if (sub == 0) *(uint32_t *)blk = q.ds;
+                }
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             if (wlive[i]) *(u32x4 *)(st + 4 * i * RSTR + pl) = wv[i];
         if (NIW == 5 && wlive[NIW - 1]) *(u32x4 *)(st + pl16) = wv[NIW - 1];
+        if constexpr (!F32) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (i < nia && alive[i]) *(u32x4 *)(st + WB + 2 * i * kActStep + pa) = av[i];
+            for (int i = 0; i < 4; ++i)
+                if (i < nia && alive[i]) *(u32x4 *)(st + WB + 2 * i * kActStep + pa) = av[i];
+        }
     };
     if (lane < 4) ((uint32_t *)zero)[lane] = 0u;       // read only by this wave
 
@@ -201,7 +231,7 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
 
     for (int it = 0; it < my_steps; ++it) {
         const int s = wave + it * nwaves;
-        park();
+        park(s);
         if (it + 1 < my_steps) {   // the next step's loads fly during this step's math
             load_w(s + nwaves);
             load_a(s + nwaves);
@@ -366,8 +396,8 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
     if (c < ncols && row0 + rr < rows) y[mc.pair(c) * rows + row0 + rr] = v;
 }
 
-template <int T, bool DBG, bool EXPERT>
-hipError_t launch_t(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y,
+template <int T, bool DBG, bool EXPERT, bool F32 = false>
+hipError_t launch_t(const uint8_t *w, int64_t rows, int64_t k, const void *xq, int64_t n, float *y,
                     int32_t *dbg, const ColMap &c, int64_t n_exp, hipStream_t s) {
     const int64_t nsteps = k / kSuper;
     const int nw = (int)(nsteps < 16 ? nsteps : 16);
@@ -382,13 +412,13 @@ hipError_t launch_t(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq
     a.n = (int32_t)n;
     static bool attr = false;
     if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void *)mmvq_stream_kernel<T, DBG, EXPERT>,
+        hipError_t e = hipFuncSetAttribute((const void *)mmvq_stream_kernel<T, DBG, EXPERT, F32>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
         attr = true;
     }
     dim3 grid((unsigned)((rows + kRows - 1) / kRows), EXPERT ? (unsigned)n_exp : 1u);
-    hipLaunchKernelGGL((mmvq_stream_kernel<T, DBG, EXPERT>), grid, dim3(64 * (unsigned)nw), smem, s, w, xq, y, dbg,
+    hipLaunchKernelGGL((mmvq_stream_kernel<T, DBG, EXPERT, F32>), grid, dim3(64 * (unsigned)nw), smem, s, w, xq, y, dbg,
                        a, c);
     return hipGetLastError();
 }
@@ -412,6 +442,15 @@ bool mmvq_stream_supported(int type, const void *w, int64_t k, const void *xq, c
     if ((uintptr_t)w % 16 != 0 || (uintptr_t)xq % 16 != 0) return false;
     if (cm && cm->w_expert_stride % 16 != 0) return false;
     return true;
+}
+
+hipError_t launch_mmvq_stream_f32(int type, const uint8_t *w, int64_t rows, int64_t k, const float *x, int64_t n,
+                                  float *y, hipStream_t s) {
+    const ColMap c{};
+    if (type == kQ4_K) return launch_t<kQ4_K, false, false, true>(w, rows, k, x, n, y, nullptr, c, 0, s);
+    if (type == kQ6_K) return launch_t<kQ6_K, false, false, true>(w, rows, k, x, n, y, nullptr, c, 0, s);
+    if (type == kQ8_0) return launch_t<kQ8_0, false, false, true>(w, rows, k, x, n, y, nullptr, c, 0, s);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_mmvq_stream(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n,

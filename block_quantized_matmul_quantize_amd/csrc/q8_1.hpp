@@ -18,6 +18,15 @@ struct Q81Lane {
 
 // One block of 32 values held by 8 consecutive lanes (lane l of the group owns values 4l..4l+3);
 // max and sum reduce over the group with xor shuffles, so all 8 lanes must call it together.
+//
+// q = round-half-away(RN(x / d32)).  Fast path: t = x * rcp(d32) (hardware reciprocal, 1 ulp)
+// is within 2^-15 + 2^-17 of x / d32 for |x| <= amax, and q = trunc(t + copysign(0.5, t)) equals
+// the exact answer unless x / d32 lies within a few ulps of a half-integer -- which the
+// |fract(|t|) - 0.5| < 2^-13 test catches (it also covers the rounding of t + 0.5).  Those values,
+// and blocks whose d32 is outside [2^-100, 2^100] (or not finite), take the IEEE division, so the
+// codes are always those of the plain definition.
+__device__ __forceinline__ int q81_round_div(float x, float d32) { return (int)roundf(x / d32); }
+
 __device__ __forceinline__ Q81Lane quantize_q8_1_lane(float4 v) {
     float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
     amax = fmaxf(amax, __shfl_xor(amax, 1, 8));
@@ -26,10 +35,26 @@ __device__ __forceinline__ Q81Lane quantize_q8_1_lane(float4 v) {
     const float d32 = amax / 127.0f;
     int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
     if (amax != 0.0f) {
-        q0 = (int)roundf(v.x / d32);
-        q1 = (int)roundf(v.y / d32);
-        q2 = (int)roundf(v.z / d32);
-        q3 = (int)roundf(v.w / d32);
+        bool slow = !(d32 >= 0x1p-100f && d32 <= 0x1p100f);
+        if (!slow) {
+            const float r = __builtin_amdgcn_rcpf(d32);
+            const float t0 = v.x * r, t1 = v.y * r, t2 = v.z * r, t3 = v.w * r;
+            const float m = 0x1p-13f;
+            slow = fabsf(__builtin_amdgcn_fractf(fabsf(t0)) - 0.5f) < m ||
+                   fabsf(__builtin_amdgcn_fractf(fabsf(t1)) - 0.5f) < m ||
+                   fabsf(__builtin_amdgcn_fractf(fabsf(t2)) - 0.5f) < m ||
+                   fabsf(__builtin_amdgcn_fractf(fabsf(t3)) - 0.5f) < m;
+            q0 = (int)(t0 + copysignf(0.5f, t0));
+            q1 = (int)(t1 + copysignf(0.5f, t1));
+            q2 = (int)(t2 + copysignf(0.5f, t2));
+            q3 = (int)(t3 + copysignf(0.5f, t3));
+        }
+        if (slow) {
+            q0 = q81_round_div(v.x, d32);
+            q1 = q81_round_div(v.y, d32);
+            q2 = q81_round_div(v.z, d32);
+            q3 = q81_round_div(v.w, d32);
+        }
     }
     int sum = q0 + q1 + q2 + q3;
     sum += __shfl_xor(sum, 1, 8);

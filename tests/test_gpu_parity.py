@@ -70,6 +70,32 @@ def test_quantize_bit_exact_special_blocks():
     assert np.array_equal(got, exp), np.argwhere(got != exp)[:5]
 
 
+def _near_boundary_rows(rng, nrows):
+    """Blocks whose values sit on, just below and just above half-integer multiples of the block
+    scale d32 = amax/127 (fp32), where the code depends on the last bit of x/d32."""
+    rows = []
+    for _ in range(nrows):
+        blocks = []
+        for _ in range(8):
+            amax = np.float32(rng.uniform(0.01, 100.0))
+            d32 = np.float32(amax / np.float32(127.0))
+            ks = rng.integers(-126, 126, 31)
+            x = (ks.astype(np.float32) + np.float32(0.5)) * d32
+            step = rng.integers(-2, 3, 31)
+            x = np.where(step < 0, np.nextafter(x, np.float32(-np.inf)), np.where(step > 0, np.nextafter(x, np.float32(np.inf)), x))
+            x = np.clip(x, -amax, amax).astype(np.float32)
+            blocks.append(np.concatenate([[amax if rng.random() < 0.5 else -amax], x]).astype(np.float32))
+        rows.append(np.concatenate(blocks))
+    return np.stack(rows).astype(np.float32)
+
+
+def test_quantize_bit_exact_near_rounding_boundaries():
+    x = _near_boundary_rows(np.random.default_rng(123), 64)     # 64 rows x 256 values
+    got = qmm.quantize_q8_1(to_dev(x)).cpu().numpy()
+    exp = oracle.quantize_q8_1(x)
+    assert np.array_equal(got, exp), np.argwhere(got != exp)[:5]
+
+
 # ---------------------------------------------------------------------------------------------
 # a5: integer sub-block dots from the production kernels, bit-exact
 # ---------------------------------------------------------------------------------------------
@@ -193,18 +219,38 @@ def test_forced_matvec_kernel_refuses_unsupported_call(kernel, qtype, k, n):
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("qtype,n", [(qmm.Q4_K, 1), (qmm.Q4_K, 2), (qmm.Q8_0, 1), (qmm.Q8_0, 2), (qmm.Q8_0, 3)])
-def test_fused_quantize_matches_separate_quantize_bitwise(qtype, n):
-    """fp32 input with few columns: the dot4 kernel quantizes the activations itself; its output
-    equals quantize_q8_1 followed by the q8_1-input product bit for bit, and the oracle's."""
-    w, x = _case(qtype, 77, 4352, n, 560 + n)
+@pytest.mark.parametrize("kernel", [0, 2], ids=["auto", "lds"])
+@pytest.mark.parametrize("qtype,n", [(qmm.Q4_K, 1), (qmm.Q4_K, 2), (qmm.Q8_0, 1), (qmm.Q8_0, 2), (qmm.Q8_0, 3),
+                                     (qmm.Q4_K, 3), (qmm.Q4_K, 5), (qmm.Q4_K, 8), (qmm.Q8_0, 4), (qmm.Q8_0, 8),
+                                     (qmm.Q6_K, 1), (qmm.Q6_K, 2), (qmm.Q6_K, 3), (qmm.Q6_K, 8)])
+def test_fused_quantize_matches_separate_quantize_bitwise(qtype, n, kernel):
+    """fp32 input to the matrix-vector path: for up to 3 columns the dot4 or LDS-staged kernel
+    quantizes the activations itself (beyond that a quantize launch precedes it); the output equals
+    quantize_q8_1 followed by the q8_1-input product bit for bit, and the oracle's.  More 256-value
+    steps than waves, so some waves quantize two steps."""
+    qmm.set_override(qmm.OVR_MV_KERNEL, kernel)
+    k = 6144 if qtype == qmm.Q6_K else 4352
+    w, x = _case(qtype, 77, k, n, 560 + n)
     wd, xd = to_dev(w), to_dev(x)
-    fused = qmm.matmul(wd, qtype, 77, 4352, xd)
-    separate = qmm.matmul_q8_1(wd, qtype, 77, 4352, qmm.quantize_q8_1(xd), n)
+    fused = qmm.matmul(wd, qtype, 77, k, xd)
+    separate = qmm.matmul_q8_1(wd, qtype, 77, k, qmm.quantize_q8_1(xd), n)
     assert torch.equal(fused, separate)
     xq = oracle.quantize_q8_1(x)
-    ref = oracle.matmul_q8_1(qtype, w, 77, 4352, xq, n)
-    assert_close(fused.cpu().numpy(), ref, row_norms(qtype, w, 77, 4352), col_norms(xq, n, 4352))
+    ref = oracle.matmul_q8_1(qtype, w, 77, k, xq, n)
+    assert_close(fused.cpu().numpy(), ref, row_norms(qtype, w, 77, k), col_norms(xq, n, k))
+
+
+@pytest.mark.parametrize("qtype,n", [(qmm.Q4_K, 2), (qmm.Q8_0, 3), (qmm.Q4_K, 6), (qmm.Q6_K, 3)])
+def test_fused_quantize_near_rounding_boundaries(qtype, n):
+    k = 2048
+    x = _near_boundary_rows(np.random.default_rng(124), n)
+    x = np.ascontiguousarray(np.tile(x, (1, k // 256)))
+    w = synth.gen_weights(qtype, 48, k, np.random.default_rng(125))
+    wd, xd = to_dev(w), to_dev(x)
+    fused = qmm.matmul(wd, qtype, 48, k, xd)
+    xq_dev = qmm.quantize_q8_1(xd)
+    assert np.array_equal(xq_dev.cpu().numpy(), oracle.quantize_q8_1(x))
+    assert torch.equal(fused, qmm.matmul_q8_1(wd, qtype, 48, k, xq_dev, n))
 
 
 def test_fused_quantize_special_blocks():
