@@ -20,7 +20,7 @@ BLOCK_VALUES = {Q8_0: 32, Q4_K: 256, Q6_K: 256}
 BLOCK_BYTES = {Q8_0: 34, Q4_K: 144, Q6_K: 210}
 Q8_1_BYTES = 36
 
-OVR_PATH, OVR_STREAMK, OVR_TILE_J, OVR_MV_STEPS, OVR_MV_KERNEL = 1, 2, 3, 4, 5
+OVR_PATH, OVR_STREAMK, OVR_TILE_J, OVR_MV_STEPS, OVR_MV_KERNEL, OVR_FUSE_COLS = 1, 2, 3, 4, 5, 6
 PATH_AUTO, PATH_MATVEC, PATH_TILED = 0, 1, 2
 
 if not os.path.exists(LIB_PATH):

@@ -152,6 +152,9 @@ qmm_status qmm_set_override(int key, int value) {
         case QMM_OVR_MV_KERNEL:
             if (value < 0 || value > 3) return fail(QMM_ERR_ARG, "matrix-vector kernel override must be 0..3");
             qmm::set_mmvq_kernel(value); return QMM_OK;
+        case QMM_OVR_FUSE_COLS:
+            if (value < 0 || value > 8) return fail(QMM_ERR_ARG, "fused-quantize column override must be 0..8");
+            qmm::set_mmvq_fuse_cols(value); return QMM_OK;
         default:
             return fail(QMM_ERR_ARG, "unknown override key %d", key);
     }

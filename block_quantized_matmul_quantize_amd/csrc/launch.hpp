@@ -30,6 +30,8 @@ hipError_t launch_mmvq(int type, const uint8_t *w, int64_t rows, int64_t k, cons
 // fp32-input matrix-vector product with the q8_1 quantization done inside the dot4 or the
 // LDS-staged kernel (no separate quantize launch): dense calls either kernel would take.
 bool mmvq_fused_applies(int type, const void *w, int64_t k, const float *x, int64_t n);
+// Tuning: most columns the LDS-staged kernel quantizes itself (0 = automatic).
+void set_mmvq_fuse_cols(int cols);
 hipError_t launch_mmvq_fused(int type, const uint8_t *w, int64_t rows, int64_t k, const float *x, int64_t n, float *y,
                              hipStream_t s);
 hipError_t launch_mmvq_dot4_f32(int type, const uint8_t *w, int64_t rows, int64_t k, const float *x, int64_t n,

@@ -469,6 +469,10 @@ void set_mmvq_kernel(int which) { g_mv_kernel = which; }
 // Largest column count the automatic choice sends to the dot4 kernel, per type.
 static int dot4_auto_cols(int type) { return type == kQ4_K ? 2 : type == kQ8_0 ? 3 : 0; }
 
+static int g_fuse_cols = 0;   // 0: automatic (5)
+
+void set_mmvq_fuse_cols(int cols) { g_fuse_cols = cols; }
+
 // Which fused kernel serves an fp32-input call: 3 dot4, 2 LDS-staged MFMA, 0 none.
 static int fused_kernel(int type, const void *w, int64_t k, const float *x, int64_t n) {
     const int kc = g_mv_kernel;
@@ -479,9 +483,10 @@ static int fused_kernel(int type, const void *w, int64_t k, const float *x, int6
         if (kc == 3) return 0;
     }
     // The LDS-staged kernel quantizes a step's blocks with 8 lanes per block; measured against a
-    // separate quantize launch that pays off up to 3 columns (4096 x 4096: 1-2 us saved per call
-    // at n <= 3, 0.5-3 us lost at n = 5..8).
-    if ((kc == 0 || kc == 2) && n <= 3 && mmvq_stream_supported(type, w, k, x, nullptr)) return 2;
+    // separate quantize launch that pays off up to 5 columns (4096 x 4096: 0.7-2.3 us saved per
+    // call at n <= 5, 0.9-1.3 us lost at n = 8).
+    const int lim = g_fuse_cols > 0 ? g_fuse_cols : 5;
+    if ((kc == 0 || kc == 2) && n <= lim && mmvq_stream_supported(type, w, k, x, nullptr)) return 2;
     return 0;
 }
 

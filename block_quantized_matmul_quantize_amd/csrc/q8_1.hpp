@@ -16,8 +16,21 @@ struct Q81Lane {
     uint32_t ds;      // fp16 d | fp16 s << 16 of the whole block (same on all 8 lanes)
 };
 
-// One block of 32 values held by 8 consecutive lanes (lane l of the group owns values 4l..4l+3);
-// max and sum reduce over the group with xor shuffles, so all 8 lanes must call it together.
+// Lane exchange within aligned groups of 8 lanes by DPP (a modifier on a vector ALU operation,
+// no LDS round trip): quad_perm [1,0,3,2] (xor 1), quad_perm [2,3,0,1] (xor 2), row_half_mirror
+// (lane i of the group <-> lane 7-i, which pairs the two quads).  After the three steps every
+// lane of the group holds the max / sum of all eight.
+template <int CTRL> __device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL> __device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141;
+
+// One block of 32 values held by 8 consecutive lanes (lane l of the group owns values 4l..4l+3,
+// the group starts at a lane index divisible by 8); max and sum reduce over the group, so all 8
+// lanes must call it together.
 //
 // q = round-half-away(RN(x / d32)).  Fast path: t = x * rcp(d32) (hardware reciprocal, 1 ulp)
 // is within 2^-15 + 2^-17 of x / d32 for |x| <= amax, and q = trunc(t + copysign(0.5, t)) equals
@@ -29,9 +42,9 @@ __device__ __forceinline__ int q81_round_div(float x, float d32) { return (int)r
 
 __device__ __forceinline__ Q81Lane quantize_q8_1_lane(float4 v) {
     float amax = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
-    amax = fmaxf(amax, __shfl_xor(amax, 1, 8));
-    amax = fmaxf(amax, __shfl_xor(amax, 2, 8));
-    amax = fmaxf(amax, __shfl_xor(amax, 4, 8));
+    amax = fmaxf(amax, dpp_f<kDppXor1>(amax));
+    amax = fmaxf(amax, dpp_f<kDppXor2>(amax));
+    amax = fmaxf(amax, dpp_f<kDppHalfMirror>(amax));
     const float d32 = amax / 127.0f;
     int q0 = 0, q1 = 0, q2 = 0, q3 = 0;
     if (amax != 0.0f) {
@@ -57,9 +70,9 @@ __device__ __forceinline__ Q81Lane quantize_q8_1_lane(float4 v) {
         }
     }
     int sum = q0 + q1 + q2 + q3;
-    sum += __shfl_xor(sum, 1, 8);
-    sum += __shfl_xor(sum, 2, 8);
-    sum += __shfl_xor(sum, 4, 8);
+    sum += dpp_i<kDppXor1>(sum);
+    sum += dpp_i<kDppXor2>(sum);
+    sum += dpp_i<kDppHalfMirror>(sum);
     Q81Lane out;
     out.codes = (uint32_t)(q0 & 0xFF) | ((uint32_t)(q1 & 0xFF) << 8) | ((uint32_t)(q2 & 0xFF) << 16) |
                 ((uint32_t)(q3 & 0xFF) << 24);

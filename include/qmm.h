@@ -138,9 +138,13 @@ qmm_status qmm_debug_subdots(int type, const void *w, int64_t rows, int64_t k, c
  *                     dot4 kernel for Q4_K with n <= 2 and Q8_0 with n <= 3, else the LDS-staged
  *                     kernel, when weights, activations and rows are aligned (16 bytes; Q8_0 dot4:
  *                     4) and K is a multiple of 256; otherwise the register-streamed kernel.
+ *   QMM_OVR_FUSE_COLS: qmm_matmul only: most columns (1..8) for which the LDS-staged kernel
+ *                     quantizes the fp32 activations itself instead of a separate quantize
+ *                     launch (automatic: 5).
  * Returns QMM_ERR_ARG for an unknown key or value.
  * ------------------------------------------------------------------------------------------- */
-enum { QMM_OVR_PATH = 1, QMM_OVR_STREAMK = 2, QMM_OVR_TILE_J = 3, QMM_OVR_MV_STEPS = 4, QMM_OVR_MV_KERNEL = 5 };
+enum { QMM_OVR_PATH = 1, QMM_OVR_STREAMK = 2, QMM_OVR_TILE_J = 3, QMM_OVR_MV_STEPS = 4, QMM_OVR_MV_KERNEL = 5,
+       QMM_OVR_FUSE_COLS = 6 };
 qmm_status qmm_set_override(int key, int value);
 
 /* ---------------------------------------------------------------------------------------------

@@ -23,7 +23,7 @@ TNAME = {qmm.Q4_K: "q4_K", qmm.Q6_K: "q6_K", qmm.Q8_0: "q8_0"}
 
 
 def _reset_overrides():
-    for key in (qmm.OVR_PATH, qmm.OVR_STREAMK, qmm.OVR_TILE_J, qmm.OVR_MV_STEPS, qmm.OVR_MV_KERNEL):
+    for key in (qmm.OVR_PATH, qmm.OVR_STREAMK, qmm.OVR_TILE_J, qmm.OVR_MV_STEPS, qmm.OVR_MV_KERNEL, qmm.OVR_FUSE_COLS):
         qmm.set_override(key, 0)
 
 
@@ -224,11 +224,12 @@ def test_forced_matvec_kernel_refuses_unsupported_call(kernel, qtype, k, n):
                                      (qmm.Q4_K, 3), (qmm.Q4_K, 5), (qmm.Q4_K, 8), (qmm.Q8_0, 4), (qmm.Q8_0, 8),
                                      (qmm.Q6_K, 1), (qmm.Q6_K, 2), (qmm.Q6_K, 3), (qmm.Q6_K, 8)])
 def test_fused_quantize_matches_separate_quantize_bitwise(qtype, n, kernel):
-    """fp32 input to the matrix-vector path: for up to 3 columns the dot4 or LDS-staged kernel
-    quantizes the activations itself (beyond that a quantize launch precedes it); the output equals
+    """fp32 input to the matrix-vector path with fusion forced for every column count: the dot4 or
+    LDS-staged kernel quantizes the activations itself; the output equals
     quantize_q8_1 followed by the q8_1-input product bit for bit, and the oracle's.  More 256-value
     steps than waves, so some waves quantize two steps."""
     qmm.set_override(qmm.OVR_MV_KERNEL, kernel)
+    qmm.set_override(qmm.OVR_FUSE_COLS, 8)                    # every column count fused here
     k = 6144 if qtype == qmm.Q6_K else 4352
     w, x = _case(qtype, 77, k, n, 560 + n)
     wd, xd = to_dev(w), to_dev(x)
