@@ -29,6 +29,8 @@ typedef float f32x32 __attribute__((ext_vector_type(32)));
 // and the q8_1 code arrays sit at 2- or 4-byte offsets.  gfx950 global loads accept these.
 typedef u32x4 __attribute__((aligned(2))) u32x4_a2;
 typedef uint32_t __attribute__((aligned(2))) u32_a2;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef u32x2 __attribute__((aligned(4))) u32x2_a4;   // 8 bytes at a 4-byte offset (q8_1 codes)
 
 __device__ __forceinline__ u32x4 ld16(const uint8_t *p) { return *(const u32x4_a2 *)p; }
 __device__ __forceinline__ uint32_t ld4(const uint8_t *p) { return *(const u32_a2 *)p; }

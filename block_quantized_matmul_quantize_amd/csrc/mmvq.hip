@@ -29,7 +29,6 @@
 namespace qmm {
 
 constexpr int kMvRows = 16;
-constexpr int kMvMaxBlocks = 1024;   // K <= 32768 (the activation scale table is staged in LDS)
 
 // 16 zero bytes: the A operand of lanes outside the block diagonal or beyond the live columns.
 __device__ __attribute__((aligned(16))) uint8_t mv_zero16[16];
@@ -482,10 +481,10 @@ static int fused_kernel(int type, const void *w, int64_t k, const float *x, int6
         if (n <= lim && mmvq_dot4_supported(type, w, k, x, nullptr)) return 3;
         if (kc == 3) return 0;
     }
-    // The LDS-staged kernel quantizes a step's blocks with 8 lanes per block; measured against a
-    // separate quantize launch that pays off up to 5 columns (4096 x 4096: 0.7-2.3 us saved per
-    // call at n <= 5, 0.9-1.3 us lost at n = 8).
-    const int lim = g_fuse_cols > 0 ? g_fuse_cols : 5;
+    // The LDS-staged kernel quantizes a step's blocks with 4 lanes per block; measured against a
+    // separate quantize launch at 4096 x 4096 it saves 0.4-2.4 us per call for Q6_K and Q8_0 at
+    // every n <= 8, and for Q4_K up to n = 5 (0.4 us lost at n = 8).
+    const int lim = g_fuse_cols > 0 ? g_fuse_cols : (type == kQ4_K ? 5 : 8);
     if ((kc == 0 || kc == 2) && n <= lim && mmvq_stream_supported(type, w, k, x, nullptr)) return 2;
     return 0;
 }

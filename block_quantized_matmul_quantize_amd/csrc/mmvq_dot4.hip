@@ -97,14 +97,15 @@ __global__ __launch_bounds__(1024) void mmvq_dot4_kernel(const uint8_t *__restri
     float2 *aft = (float2 *)(smem + (size_t)NC * nb * 32);
     float *red = (float *)(smem + (size_t)NC * nb * 40);   // [nwaves][16 * NC]
     if constexpr (F32) {
-        // fp32 rows (dense): 8 consecutive threads quantize one block; nb*8 and the block size
-        // are multiples of 8, so the 8 lanes of a block are active together.
+        // fp32 rows (dense): 4 consecutive threads quantize one block, 8 values each; nb*4 and the
+        // block size are multiples of 4, so the 4 lanes of a block are active together.
         for (int c = 0; c < ncols; ++c) {
             const float *xrow = (const float *)xin + (size_t)c * nb * 32;
-            for (uint32_t t = threadIdx.x; t < nb * 8; t += blockDim.x) {
-                const uint32_t b = t >> 3, sub = t & 7;
-                const Q81Lane q = quantize_q8_1_lane(*(const float4 *)(xrow + b * 32 + 4 * sub));
-                *(uint32_t *)(acodes + ((size_t)c * nb + b) * 32 + 4 * sub) = q.codes;
+            for (uint32_t t = threadIdx.x; t < nb * 4; t += blockDim.x) {
+                const uint32_t b = t >> 2, sub = t & 3;
+                const float *src = xrow + b * 32 + 8 * sub;
+                const Q81Lane4 q = quantize_q8_1_lane4(*(const float4 *)src, *(const float4 *)(src + 4));
+                *(u32x2 *)(acodes + ((size_t)c * nb + b) * 32 + 8 * sub) = u32x2{q.c0, q.c1};
                 if (sub == 0)
                     aft[(size_t)c * nb + b] = make_float2(h2f((uint16_t)(q.ds & 0xFFFF)), h2f((uint16_t)(q.ds >> 16)));
             }

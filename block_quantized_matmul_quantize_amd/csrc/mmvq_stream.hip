@@ -16,7 +16,7 @@
 //   Q4_K  acc += D * (d*sc) * d_a - (dmin*m) * s_a
 //   Q6_K  acc += D * (d*sc) * d_a      (D includes -32 * sum q_a via a second MFMA)
 //   Q8_0  acc += D * d_w * d_a
-// For fp32 activations (dense) the wave quantizes its step's blocks itself, 8 lanes per block with
+// For fp32 activations (dense) the wave quantizes its step's blocks itself, 4 lanes per block with
 // the arithmetic of the standalone quantize kernel (q8_1.hpp), and parks the q8_1 bytes in the
 // same place -- one launch instead of two.
 // Requirements (checked by the host): weights, activations and every row 16-byte aligned, and
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
     if (NIW == 5) wlive[NIW - 1] = lane < 16 && jq <= rmax;
 
     u32x4 wv[NIW], av[4];
-    auto load_w = [&](int s) {
+    auto load_w = [&](int s) __attribute__((always_inline)) {
         const uint8_t *wstep = wg + ((uint32_t)(s * Geo<T>::STEP) & ~15u);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -134,15 +134,26 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
                          : (int64_t)c * col_bytes + 16 * ja;
     }
     const uint32_t pa = (uint32_t)cq * kActStep + 16u * ja;
-    // fp32 input: columns 0..3 of a step are fetched ahead (registers), 4..7 at park time
-    float4 xv[4];
-    const float *xf = (const float *)xin + 4 * lane;
+    // fp32 input: a column's 256 step values are 8 blocks of 4 lanes, 8 values per lane, so a
+    // pass covers columns 2i + lane/32; the first NPF passes are fetched ahead into registers
+    // (one for Q6_K, whose unpacking needs the registers), the rest at park time.
+    constexpr int NPF = T == kQ6_K ? 1 : 2;
     const size_t xstride = (size_t)P.nsteps * kSuper;
-    auto load_a = [&](int s) {
+    const float *xf = (const float *)xin + (size_t)cq * xstride + 8 * ja;
+    const float4 fz = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 x0a = fz, x0b = fz, x1a = fz, x1b = fz;   // passes 0 and 1 (named: kept in registers)
+    auto load8 = [&](int s, int i, float4 &a, float4 &b) __attribute__((always_inline)) {
+        const float *src = xf + s * kSuper + 2 * i * xstride;
+        a = b = fz;
+        if (2 * i + cq < ncols) {
+            a = *(const float4 *)src;
+            b = *(const float4 *)(src + 4);
+        }
+    };
+    auto load_a = [&](int s) __attribute__((always_inline)) {
         if constexpr (F32) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-                if (c < ncols) xv[c] = *(const float4 *)(xf + s * kSuper + c * xstride);
+            load8(s, 0, x0a, x0b);
+            if (NPF > 1 && ncols > 2) load8(s, 1, x1a, x1b);
         } else {
             const uint8_t *astep = (const uint8_t *)xin + (uint32_t)(s * kActStep);
 #pragma unroll
@@ -152,19 +163,30 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
     };
     if (my_steps > 0) load_a(wave);
 
-    auto park = [&](int s) {
+    auto park = [&](int s) __attribute__((always_inline)) {
         if constexpr (F32) {
-            // fp32 input: column c's step values, lane = (block lane/8, values 4*(lane%8)..); done
-            // before the weights are parked so late loads overlap the weights' arrival
-            const int b = lane >> 3, sub = lane & 7;
+            // quantized before the weights are parked so late loads overlap the weights' arrival
+            const int b = (lane >> 2) & 7, sub = lane & 3;
 #pragma unroll
-            for (int c = 0; c < 8; ++c)
-                if (c < ncols) {
-                    const float4 v = c < 4 ? xv[c & 3] : *(const float4 *)(xf + s * kSuper + c * xstride);
-                    const Q81Lane q = quantize_q8_1_lane(v);
-                    uint8_t *blk = st + WB + c * kActStep + b * kQ8_1Bytes;
-                    *(uint32_t *)(blk + 4 + 4 * sub) = q.codes;
-                    if (sub == 0) *(uint32_t *)blk = q.ds;
+            for (int i = 0; i < 4; ++i)
+                if (2 * i < ncols) {   // wave-uniform; the lanes of a missing odd column quantize zeros
+                    const int c = 2 * i + cq;
+                    float4 a, bv;
+                    if (i == 0) {
+                        a = x0a;
+                        bv = x0b;
+                    } else if (i == 1 && NPF > 1) {
+                        a = x1a;
+                        bv = x1b;
+                    } else {
+                        load8(s, i, a, bv);
+                    }
+                    const Q81Lane4 q = quantize_q8_1_lane4(a, bv);
+                    if (c < ncols) {
+                        uint8_t *blk = st + WB + c * kActStep + b * kQ8_1Bytes;
+                        *(u32x2_a4 *)(blk + 4 + 8 * sub) = u32x2{q.c0, q.c1};
+                        if (sub == 0) *(uint32_t *)blk = q.ds;
+                    }
                 }
         }
 #pragma unroll

@@ -1,5 +1,5 @@
-// q8_1 activation quantization kernel: one block of 32 values per 8 consecutive lanes, each lane
-// owning 4 values (one 16-byte load, one 4-byte store of codes); the arithmetic and its readings
+// q8_1 activation quantization kernel: one block of 32 values per 4 consecutive lanes, each lane
+// owning 8 values (two 16-byte loads, one 8-byte store of codes); the arithmetic and its readings
 // are in q8_1.hpp.
 #include "common.hpp"
 #include "launch.hpp"
@@ -12,20 +12,20 @@ __global__ __launch_bounds__(256) void quantize_q8_1_kernel(const float *__restr
     const int64_t nb = k / 32;
     const int64_t total = n_rows * nb;
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t blk = gid >> 3;
-    const int sub = (int)(gid & 7);
-    const bool live = blk < total;   // the whole 8-lane group shares this predicate
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    int64_t row = 0, b = 0;
+    const int64_t blk = gid >> 2;
+    const int sub = (int)(gid & 3);
+    const bool live = blk < total;   // the whole 4-lane group shares this predicate
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
     if (live) {
-        row = blk / nb;
-        b = blk - row * nb;
-        v = *(const float4 *)(x + row * k + b * 32 + 4 * sub);
+        const int64_t row = blk / nb;
+        const float *src = x + row * k + (blk - row * nb) * 32 + 8 * sub;
+        a = *(const float4 *)src;
+        b = *(const float4 *)(src + 4);
     }
-    const Q81Lane q = quantize_q8_1_lane(v);
+    const Q81Lane4 q = quantize_q8_1_lane4(a, b);
     if (!live) return;
     uint8_t *yb = y + blk * kQ8_1Bytes;
-    *(uint32_t *)(yb + 4 + 4 * sub) = q.codes;
+    *(u32x2_a4 *)(yb + 4 + 8 * sub) = u32x2{q.c0, q.c1};
     if (sub == 0) *(uint32_t *)yb = q.ds;
 }
 
@@ -37,7 +37,7 @@ __global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t *__restrict__ p,
 }
 
 hipError_t launch_quantize_q8_1(const float *x, int64_t n_rows, int64_t k, uint8_t *y, hipStream_t s) {
-    const int64_t threads = n_rows * (k / 32) * 8;
+    const int64_t threads = n_rows * (k / 32) * 4;
     if (threads == 0) return hipSuccess;
     const int64_t blocks = (threads + 255) / 256;
     hipLaunchKernelGGL(quantize_q8_1_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, n_rows, k, y);

@@ -20,7 +20,8 @@
  *    Q6_K 210 {128 B ql, 64 B qh, 16 int8 scales, fp16 d}; Q8_0 34 {fp16 d, 32 int8}.  Only
  *    2-byte alignment of w is required.
  *  - Activations x are fp32 row-major [n][k] (token-major, [QMM] "QMatMul": input [..., k]),
- *    4-byte aligned.  Outputs y are fp32 row-major [n][rows] (output [..., n]).
+ *    16-byte aligned (the kernels read 8 values per lane as two 16-byte loads); QMM_ERR_ARG
+ *    otherwise.  Outputs y are fp32 row-major [n][rows] (output [..., n]), 4-byte aligned.
  *  - q8_1 blocks (36 B): {fp16 d, fp16 s, int8 q[32]}, one per 32 activation values; [MMQ]
  *    introduction and "dp4a path Q4_K" section (the activation half2 (d, s), s = d * sum(q)).
  *    Quantization: amax = max|x|; d32 = amax/127 (fp32); q = round-half-away(x / d32);
@@ -63,7 +64,7 @@ const char *qmm_version(void);
 
 /* ---------------------------------------------------------------------------------------------
  * a1: activation quantization ([MMQ] introduction; "dp4a path Q4_K": s = d * sum(q)).
- * x: fp32 [n_rows][k], k % 32 == 0.  y: n_rows * (k/32) q8_1 blocks of 36 bytes, row-major,
+ * x: fp32 [n_rows][k], k % 32 == 0, 16-byte aligned.  y: n_rows * (k/32) q8_1 blocks of 36 bytes, row-major,
  * 4-byte aligned.  n_rows == 0 is a no-op.
  * ------------------------------------------------------------------------------------------- */
 qmm_status qmm_quantize_q8_1(const float *x, int64_t n_rows, int64_t k, void *y, void *stream);
@@ -140,7 +141,7 @@ qmm_status qmm_debug_subdots(int type, const void *w, int64_t rows, int64_t k, c
  *                     4) and K is a multiple of 256; otherwise the register-streamed kernel.
  *   QMM_OVR_FUSE_COLS: qmm_matmul only: most columns (1..8) for which the LDS-staged kernel
  *                     quantizes the fp32 activations itself instead of a separate quantize
- *                     launch (automatic: 5).
+ *                     launch (automatic: 5 for Q4_K, 8 for Q6_K and Q8_0).
  * Returns QMM_ERR_ARG for an unknown key or value.
  * ------------------------------------------------------------------------------------------- */
 enum { QMM_OVR_PATH = 1, QMM_OVR_STREAMK = 2, QMM_OVR_TILE_J = 3, QMM_OVR_MV_STEPS = 4, QMM_OVR_MV_KERNEL = 5,
