@@ -16,6 +16,14 @@ Also in the same JSON line:
   secondary     int8 TOPS and % of the 5.0 POP/s int8 MFMA peak for the prefill and MoE shapes.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-secondary]
+
+Profile summaries (no GPU; read the SQLite databases rocprofv3 writes under -d DIR):
+  python bench.py --summarize-trace DIR          per-kernel durations of a --kernel-trace run
+  python bench.py --summarize-pmc FDIR WDIR [--write-traffic]
+                 per-kernel FETCH_SIZE / WRITE_SIZE of two --pmc runs of `bench.py --calib-copy`,
+                 scaled to bytes by the 256 MiB device copy; --write-traffic stores the
+                 matrix-vector kernels' average in profiles/mmvq_traffic.json (with a hash of
+                 the kernel sources, so the figure is dropped once they change).
 """
 import argparse
 import glob
@@ -42,7 +50,16 @@ def source_hash():
 
 
 def algo_bytes(qtype, rows, k, n, block_bytes, block_values):
+    """Bytes one call must move: weight blocks + q8_1 activation blocks + fp32 outputs."""
     return rows * (k // block_values[qtype]) * block_bytes[qtype] + n * (k // 32) * 36 + n * rows * 4
+
+
+def launch_bytes(qtype, rows, k, n, block_bytes, block_values, fp32_in):
+    """Bytes one matrix-vector launch must move: as algo_bytes, with fp32 activations (4 B per
+    value) in place of q8_1 blocks when the kernel quantizes its input itself."""
+    if not fp32_in:
+        return algo_bytes(qtype, rows, k, n, block_bytes, block_values)
+    return rows * (k // block_values[qtype]) * block_bytes[qtype] + n * k * 4 + n * rows * 4
 
 
 def main():
@@ -56,7 +73,16 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 256 MiB device copy (known bytes) to scale profiler counters")
+    ap.add_argument("--summarize-trace", metavar="DIR")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--write-traffic", action="store_true")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, write=args.write_traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the sharded "
               "design is described in DESIGN.md, not built)", file=sys.stderr)
@@ -148,25 +174,34 @@ def main():
     warm_gbps = step_bytes / (warm_ms * 1e-3) / 1e9
 
     # ---------------------------------------------------------------- per-launch kernel timing
-    # The matrix-vector kernel alone: qmm_matmul_q8_1 on pre-quantized activations is exactly one
-    # launch of it.  Per case, a graph of back-to-back launches over the R weight rotations is
-    # replayed between two HIP events on the launch stream; duration = elapsed / launches.
+    # The matrix-vector kernel as the step launches it.  qmm.matvec_kernel names it per case and
+    # says whether it quantizes the fp32 input itself: then qmm.matmul is exactly one launch of it
+    # (reading fp32 activations); otherwise qmm.matmul_q8_1 on the pre-quantized activations is
+    # one launch of it (the step adds one quantize launch).  Per case, a graph of back-to-back
+    # launches over the R weight rotations is replayed between two HIP events on the stream the
+    # graph runs on; duration = elapsed / launches.
     per_case = []
     tot_bytes = tot_us = 0.0
     nrep = max(4, args.steps // 10)
     for i, c in enumerate(cases):
-        g = capture(lambda i=i, c=c: [qmm.matmul_q8_1(W[r][i], c["qtype"], c["rows"], c["k"], XQ[i], c["n"],
-                                                      out=Y[i]) for _ in range(4) for r in range(R)])
+        kid, fused = qmm.matvec_kernel(c["qtype"], W[0][i], c["k"], X[i], c["n"], x_fp32=True)
+        if fused:
+            call = lambda r, i=i, c=c: qmm.matmul(W[r][i], c["qtype"], c["rows"], c["k"], X[i], out=Y[i], ws=WS[i])
+        else:
+            call = lambda r, i=i, c=c: qmm.matmul_q8_1(W[r][i], c["qtype"], c["rows"], c["k"], XQ[i], c["n"],
+                                                       out=Y[i])
+        g = capture(lambda: [call(r) for _ in range(4) for r in range(R)])
         g.replay()
         us = run(nrep, lambda s: g.replay()) * 1e3 / (4 * R)
-        b = algo_bytes(c["qtype"], c["rows"], c["k"], c["n"], BB, BV)
-        per_case.append({"case": c["name"], "us": round(us, 3), "GBps": round(b / us / 1e3, 1),
+        b = launch_bytes(c["qtype"], c["rows"], c["k"], c["n"], BB, BV, fused)
+        per_case.append({"case": c["name"], "kernel": qmm.MV_KERNEL_NAMES.get(kid, "?") + (" (fp32 in)" if fused else ""),
+                         "us": round(us, 3), "bytes": b, "GBps": round(b / us / 1e3, 1),
                          "frac": round(b / us / 1e3 / HBM_PEAK_GBPS, 4)})
         tot_bytes += b
         tot_us += us
     achieved = tot_bytes / tot_us / 1e3
     for pc in per_case:
-        log(f"[bench]   {pc['case']:24s} {pc['us']:8.3f} us  {pc['GBps']:8.1f} GB/s")
+        log(f"[bench]   {pc['case']:24s} {pc['kernel']:30s} {pc['us']:8.3f} us  {pc['GBps']:8.1f} GB/s")
 
     traffic = None
     tpath = os.path.join(ROOT, "profiles", "mmvq_traffic.json")
@@ -176,7 +211,8 @@ def main():
         if tj.get("source_hash") == source_hash():
             traffic = tj.get("bytes_per_launch_avg")
 
-    roofline = {"kernel": "mmvq_kernel (matrix-vector, all 12 calls)", "bound": "hbm",
+    roofline = {"kernel": "matrix-vector kernels as the step launches them (mmvq_dot4_kernel, "
+                          "mmvq_stream_kernel), 12 cases", "bound": "hbm",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "algorithmic_bytes_per_launch_avg": round(tot_bytes / len(cases), 1),
@@ -208,6 +244,77 @@ def main():
         "secondary": secondary,
     }
     print(json.dumps(out), flush=True)
+
+
+# -------------------------------------------------------------------- profile summaries (host only)
+COPY_BYTES = 256 << 20   # the --calib-copy device copy
+
+
+def _rocpd(d):
+    import sqlite3
+    dbs = sorted(glob.glob(os.path.join(d, "**", "*.db"), recursive=True))
+    if not dbs:
+        raise SystemExit(f"no rocprofv3 database under {d}")
+    return sqlite3.connect(dbs[0])
+
+
+def _short(name):
+    import re
+    name = name.replace("(anonymous namespace)::", "")
+    return re.sub(r"^void ", "", name.split("(")[0])
+
+
+def summarize_trace(d):
+    import statistics
+    con = _rocpd(d)
+    by = {}
+    for name, start, end in con.execute("select name, start, end from kernels"):
+        by.setdefault(_short(name), []).append((end - start) / 1000.0)
+    print(f"{'kernel':66s} {'count':>6s} {'avg_us':>9s} {'med_us':>9s} {'min_us':>9s} {'max_us':>9s} {'total_ms':>9s}")
+    for n, ds in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        print(f"{n[:66]:66s} {len(ds):6d} {sum(ds) / len(ds):9.3f} {statistics.median(ds):9.3f} "
+              f"{min(ds):9.3f} {max(ds):9.3f} {sum(ds) / 1e3:9.3f}")
+
+
+def summarize_pmc(fdir, wdir, write=False):
+    import statistics
+
+    def load(d):
+        by = {}
+        for name, value in _rocpd(d).execute("select kernel_name, value from counters_collection"):
+            by.setdefault(_short(name), []).append(value)
+        return by
+
+    F, Wr = load(fdir), load(wdir)
+    copy = [k for k in F if "copyBuffer" in k or "copy" in k.lower()]
+    if not copy:
+        raise SystemExit("no device-copy dispatch found: run bench.py with --calib-copy")
+    fs = COPY_BYTES / (max(max(F[k]) for k in copy) * 1024)
+    ws = COPY_BYTES / (max(max(Wr[k]) for k in copy if k in Wr) * 1024)
+    print(f"calibration: {COPY_BYTES >> 20} MiB device copy -> FETCH_SIZE x{fs:.3f}, WRITE_SIZE x{ws:.3f}")
+    print("| kernel | dispatches | FETCH_SIZE KiB/dispatch (raw) | WRITE_SIZE KiB/dispatch (raw) | HBM bytes/dispatch (scaled) |")
+    print("|---|---|---|---|---|")
+    mv_tot = mv_cnt = 0
+    for k in sorted(F, key=lambda k: -statistics.mean(F[k])):
+        f = statistics.mean(F[k])
+        w = statistics.mean(Wr.get(k, [0.0]))
+        b = f * 1024 * fs + w * 1024 * ws
+        print(f"| `{k}` | {len(F[k])} | {f:.1f} | {w:.1f} | {b / 1e6:.3f} MB |")
+        if "mmvq" in k:
+            mv_tot += b * len(F[k])
+            mv_cnt += len(F[k])
+    if not mv_cnt:
+        raise SystemExit("no matrix-vector kernel dispatches in the counter runs")
+    avg = mv_tot / mv_cnt
+    print(f"matrix-vector kernels: {mv_cnt} dispatches, average HBM bytes per dispatch {avg / 1e6:.3f} MB")
+    if write:
+        with open(os.path.join(ROOT, "profiles", "mmvq_traffic.json"), "w") as f:
+            json.dump({"kernel": "matrix-vector kernels as the step launches them (12 cases)",
+                       "bytes_per_launch_avg": round(avg), "fetch_scale": fs, "write_scale": ws,
+                       "source_hash": source_hash(),
+                       "command": "rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -- python3 bench.py --no-cpu "
+                                  "--no-secondary --calib-copy --steps 20 --warmup 2"}, f, indent=1)
+            f.write("\n")
 
 
 def run_secondary(torch, np, qmm, synth, dev, log):

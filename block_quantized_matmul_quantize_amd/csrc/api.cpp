@@ -314,7 +314,8 @@ qmm_status qmm_matmul(int type, const void *w, int64_t rows, int64_t k, const fl
     qmm_plan p{};
     if ((st = qmm_plan_dense(type, rows, k, n, device_cus(), &p))) return st;
     if (p.regime == 1 && qmm::mmvq_fused_applies(type, w, k, x, n)) {
-        // few columns: the dot4 kernel quantizes the activations itself (same bytes as below)
+        // few columns: the dot4 or LDS-staged kernel quantizes the activations itself (the same
+        // q8_1 bytes as the quantize kernel below), one launch instead of two
         hipError_t e = qmm::launch_mmvq_fused(type, (const uint8_t *)w, rows, k, x, n, y, s);
         if (e != hipSuccess) return hip_fail(e, "fused matrix-vector kernel launch");
         return QMM_OK;
@@ -322,6 +323,29 @@ qmm_status qmm_matmul(int type, const void *w, int64_t rows, int64_t k, const fl
     hipError_t e = qmm::launch_quantize_q8_1(x, n, k, wsb + L.xq_off, s);
     if (e != hipSuccess) return hip_fail(e, "quantize launch");
     return run_dense(type, w, rows, k, wsb + L.xq_off, n, y, wsb, L, nullptr, 0, s);
+}
+
+qmm_status qmm_matvec_kernel(int type, const void *w, int64_t k, const void *x, int64_t n, int32_t x_fp32,
+                             int32_t *out) {
+    qmm_status st = check_common(type, 1, k, n);
+    if (st) return st;
+    if (!out) return fail(QMM_ERR_ARG, "null out");
+    const int path = g_ovr_path.load();
+    if (n < 1 || n > 8 || k > kMvMaxK || path == 2) {
+        *out = 0;
+        return QMM_OK;
+    }
+    if (x_fp32) {
+        if (((uintptr_t)x) & 15) return fail(QMM_ERR_ARG, "x must be 16-byte aligned");
+        const int f = qmm::mmvq_fused_choice(type, w, k, (const float *)x, n);
+        if (f) {
+            *out = f + 16;
+            return QMM_OK;
+        }
+        x = (const void *)(uintptr_t)256;   // the q8_1 copy sits at the 256-byte aligned workspace start
+    }
+    *out = qmm::mmvq_kernel_choice(type, w, k, x, n, nullptr);
+    return QMM_OK;
 }
 
 qmm_status qmm_matmul_q8_1(int type, const void *w, int64_t rows, int64_t k, const void *xq, int64_t n, float *y,

@@ -30,6 +30,11 @@ hipError_t launch_mmvq(int type, const uint8_t *w, int64_t rows, int64_t k, cons
 // fp32-input matrix-vector product with the q8_1 quantization done inside the dot4 or the
 // LDS-staged kernel (no separate quantize launch): dense calls either kernel would take.
 bool mmvq_fused_applies(int type, const void *w, int64_t k, const float *x, int64_t n);
+// Kernel launch_mmvq takes for q8_1 input: 3 dot4, 2 LDS-staged MFMA, 1 register-streamed, 0 none
+// (a forced kernel that cannot serve the call); host logic only.
+int mmvq_kernel_choice(int type, const void *w, int64_t k, const void *xq, int64_t n, const ColMap *cm);
+// Kernel launch_mmvq_fused takes for fp32 input: 3 dot4, 2 LDS-staged MFMA, 0 not fused.
+int mmvq_fused_choice(int type, const void *w, int64_t k, const float *x, int64_t n);
 // Tuning: most columns the LDS-staged kernel quantizes itself (0 = automatic).
 void set_mmvq_fuse_cols(int cols);
 hipError_t launch_mmvq_fused(int type, const uint8_t *w, int64_t rows, int64_t k, const float *x, int64_t n, float *y,

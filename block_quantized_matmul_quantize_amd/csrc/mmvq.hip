@@ -502,18 +502,30 @@ hipError_t launch_mmvq_fused(int type, const uint8_t *w, int64_t rows, int64_t k
     }
 }
 
-hipError_t launch_mmvq(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y,
-                       int32_t *dbg, const ColMap *cm, int64_t n_exp, hipStream_t s) {
+int mmvq_kernel_choice(int type, const void *w, int64_t k, const void *xq, int64_t n, const ColMap *cm) {
     const int kc = g_mv_kernel;
     if (kc == 3 || kc == 0) {
         const int lim = kc == 3 ? mmvq_dot4_max_cols() : dot4_auto_cols(type);
-        if (!cm && n <= lim && mmvq_dot4_supported(type, w, k, xq, cm))
-            return launch_mmvq_dot4(type, w, rows, k, xq, n, y, dbg, cm, n_exp, (int)n, s);
-        if (kc == 3) return hipErrorInvalidValue;
+        if (!cm && n <= lim && mmvq_dot4_supported(type, w, k, xq, cm)) return 3;
+        if (kc == 3) return 0;
     }
-    if (kc != 1 && mmvq_stream_supported(type, w, k, xq, cm))
-        return launch_mmvq_stream(type, w, rows, k, xq, n, y, dbg, cm, n_exp, s);
-    if (kc == 2) return hipErrorInvalidValue;
+    if (kc != 1 && mmvq_stream_supported(type, w, k, xq, cm)) return 2;
+    if (kc == 2) return 0;
+    return 1;
+}
+
+int mmvq_fused_choice(int type, const void *w, int64_t k, const float *x, int64_t n) {
+    return fused_kernel(type, w, k, x, n);
+}
+
+hipError_t launch_mmvq(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y,
+                       int32_t *dbg, const ColMap *cm, int64_t n_exp, hipStream_t s) {
+    switch (mmvq_kernel_choice(type, w, k, xq, n, cm)) {
+        case 3: return launch_mmvq_dot4(type, w, rows, k, xq, n, y, dbg, cm, n_exp, (int)n, s);
+        case 2: return launch_mmvq_stream(type, w, rows, k, xq, n, y, dbg, cm, n_exp, s);
+        case 1: break;
+        default: return hipErrorInvalidValue;
+    }
     const bool expert = cm != nullptr;
     const bool d = dbg != nullptr;
 #define QMM_MV(TT)                                                                                       \

@@ -146,3 +146,54 @@ def test_workspace_sizes_monotone():
     assert qmm.matmul_workspace(13, 16, 256, 1) == 0
     assert qmm.matmul_id_workspace(qmm.Q4_K, 8, 14336, 4096, 512, 2, 1) > 512 * 128 * 36
     assert qmm.matmul_id_workspace(qmm.Q4_K, 8, 14336, 4096, 512, 2, 3) == 0
+
+
+MV_AUTO = [
+    # (type, n, expected (kernel, fused)) for aligned weights and fp32 activations, K = 4096:
+    # dot4 for Q4_K n <= 2 and Q8_0 n <= 3, else the LDS-staged kernel; it quantizes the fp32
+    # input itself up to 5 columns for Q4_K and 8 for Q6_K / Q8_0.
+    *[(qmm.Q4_K, n, (3, True)) for n in (1, 2)],
+    *[(qmm.Q4_K, n, (2, True)) for n in (3, 4, 5)],
+    *[(qmm.Q4_K, n, (2, False)) for n in (6, 7, 8)],
+    *[(qmm.Q6_K, n, (2, True)) for n in range(1, 9)],
+    *[(qmm.Q8_0, n, (3, True)) for n in (1, 2, 3)],
+    *[(qmm.Q8_0, n, (2, True)) for n in range(4, 9)],
+    *[(t, 9, (0, False)) for t in (qmm.Q4_K, qmm.Q6_K, qmm.Q8_0)],
+]
+
+
+@pytest.mark.parametrize("qtype,n,expect", MV_AUTO)
+def test_matvec_kernel_automatic_choice(qtype, n, expect):
+    assert qmm.matvec_kernel(qtype, 0x10000, 4096, 0x20000, n, x_fp32=True) == expect
+
+
+def test_matvec_kernel_choice_follows_alignment_and_overrides():
+    mk = qmm.matvec_kernel
+    # q8_1 input 4-byte aligned: dot4 still serves Q4_K n = 1, the LDS-staged kernel needs 16 bytes
+    assert mk(qmm.Q4_K, 0x10000, 4096, 0x20004, 1, x_fp32=False) == (3, False)
+    assert mk(qmm.Q4_K, 0x10000, 4096, 0x20004, 5, x_fp32=False) == (1, False)
+    assert mk(qmm.Q4_K, 0x10000, 4096, 0x20000, 5, x_fp32=False) == (2, False)
+    # weights only 2-byte aligned: the register-streamed kernel, on the quantized copy
+    assert mk(qmm.Q4_K, 0x10002, 4096, 0x20000, 1, x_fp32=True) == (1, False)
+    assert mk(qmm.Q6_K, 0x10002, 4096, 0x20000, 4, x_fp32=True) == (1, False)
+    # Q8_0 weights 4-byte aligned: dot4 (needs 4) but not the LDS-staged kernel (needs 16)
+    assert mk(qmm.Q8_0, 0x10004, 4096, 0x20000, 2, x_fp32=True) == (3, True)
+    assert mk(qmm.Q8_0, 0x10004, 4096, 0x20000, 6, x_fp32=True) == (1, False)
+    # K not a multiple of 256 (Q8_0 allows multiples of 32): register-streamed
+    assert mk(qmm.Q8_0, 0x10000, 4128, 0x20000, 2, x_fp32=True) == (1, False)
+    with pytest.raises(qmm.QmmError):
+        mk(qmm.Q4_K, 0x10000, 4096, 0x20004, 1, x_fp32=True)   # fp32 x must be 16-byte aligned
+    try:
+        qmm.set_override(qmm.OVR_MV_KERNEL, 1)
+        assert mk(qmm.Q4_K, 0x10000, 4096, 0x20000, 1) == (1, False)
+        qmm.set_override(qmm.OVR_MV_KERNEL, 2)
+        assert mk(qmm.Q4_K, 0x10000, 4096, 0x20000, 1) == (2, True)
+        qmm.set_override(qmm.OVR_MV_KERNEL, 0)
+        qmm.set_override(qmm.OVR_FUSE_COLS, 2)
+        assert mk(qmm.Q6_K, 0x10000, 4096, 0x20000, 3) == (2, False)
+        qmm.set_override(qmm.OVR_FUSE_COLS, 0)
+        qmm.set_override(qmm.OVR_PATH, 2)
+        assert mk(qmm.Q4_K, 0x10000, 4096, 0x20000, 1) == (0, False)
+    finally:
+        for key in (qmm.OVR_MV_KERNEL, qmm.OVR_FUSE_COLS, qmm.OVR_PATH):
+            qmm.set_override(key, 0)
