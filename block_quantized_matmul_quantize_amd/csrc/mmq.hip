@@ -1,10 +1,10 @@
 // Tiled product for many activation columns (the MMQ regime of the MMQ page: "tiling skeleton",
 // "J runtime selection", "tile efficiency", "stream-K", "fixup", "expert bounds").
 //
-// CDNA4 design.  A 256-thread workgroup owns a 128-row x J-column output tile (J = 32/64/128)
-// and walks K in 256-value steps.  Each step's weight tile and activation tile are fetched from
-// HBM into registers while the previous step computes (software pipelining: the loads of step
-// kb+1 are issued right after step kb is parked in LDS), then parked in LDS: Q4_K as packed qs
+// CDNA4 design.  A workgroup of 4 waves (8 for J = 128) owns a 128-row x J-column output tile
+// (J = 32/64/128) and walks K in 256-value steps.  Each step's weight and activation tiles are
+// fetched from HBM into registers while the previous step computes (software pipelining: the
+// loads of step kb+1 are issued right after step kb is parked in LDS), then parked in LDS: Q4_K as packed qs
 // bytes plus fp32 per-(row, sub-block) scales d*sc and mins -dmin*m, Q8_0 as int8 codes plus
 // fp32 d, Q6_K unpacked (below); activations as int8 codes plus fp32 (d, s) per 32-value block
 // (the MMQ page's "why not dequantize": stay quantized and reuse each unpacked tile for J
