@@ -32,6 +32,10 @@ namespace {
 
 constexpr int kRows = 16;
 constexpr int kActStep = 8 * kQ8_1Bytes;   // one column's q8_1 bytes per 256-value step (288)
+// Per-wave LDS head before its stage: 16 zero bytes (the off-diagonal A operand) and a 48-byte
+// sink that lanes with nothing to park write to, so every load and store is unconditional (no
+// divergent branches around memory operations).
+constexpr int kHead = 64;
 
 // Per-type step geometry: PPR 16-byte pieces per row per step (Q6_K: the 16-byte-aligned window
 // around a 210-byte super-block that starts at an even offset -- always 14 pieces), STEP bytes
@@ -92,63 +96,76 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
     const int64_t row0 = (int64_t)blockIdx.x * kRows;
     const int rmax = (int)((rows - row0) < kRows ? (rows - row0) : kRows) - 1;   // last live row of the group
     const uint8_t *wg = mc.wbase + row0 * (int64_t)row_bytes;
-    uint8_t *zero = smem + (size_t)wave * (16 + SB);   // 16 zero bytes (off-diagonal A lanes)
-    uint8_t *st = zero + 16;                            // this wave's stage
+    uint8_t *zero = smem + (size_t)wave * (kHead + SB);   // 16 zero bytes (off-diagonal A lanes)
+    uint8_t *st = zero + kHead;                            // this wave's stage
+    constexpr int kSink = 16 - kHead;                      // sink offset relative to st
     const int my_steps = P.q + (wave < P.r ? 1 : 0);
 
     // Weight loads: instruction i covers rows 4i..4i+3, 16 lanes per row, lane piece j = lane % 16
     // (j < PPR); Q8_0's 17th piece of every row comes from a fifth instruction (lanes 0..15).  The
-    // lane's byte offset is the same for every instruction and step; the rest is uniform.
+    // lane's byte offsets are the same for every step.  Lanes past PPR re-read piece 0 and rows
+    // past the end re-read the last row (valid addresses, no predicate); their copies go to the
+    // sink (pieces) or to rows whose outputs are never written.
     constexpr int NIW = PPR > 16 ? 5 : 4;
+    constexpr int PM = PPR < 16 ? PPR : 16;
     const int rq = lane >> 4, jq = lane & 15;
-    const uint32_t wl = (uint32_t)rq * row_bytes + 16u * jq;
-    const uint32_t pl = (uint32_t)rq * RSTR + 16u * jq;
-    const uint32_t wl16 = (uint32_t)jq * row_bytes + 256u;   // fifth instruction (Q8_0)
-    const uint32_t pl16 = (uint32_t)jq * RSTR + 256u;
-    bool wlive[NIW];
+    uint32_t wofs[NIW];
+    int32_t pofs[NIW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wlive[i] = jq < (PPR < 16 ? PPR : 16) && 4 * i + rq <= rmax;
-    if (NIW == 5) wlive[NIW - 1] = lane < 16 && jq <= rmax;
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * i + rq;
+        wofs[i] = (uint32_t)(r < rmax ? r : rmax) * row_bytes + 16u * (jq < PM ? jq : 0);
+        pofs[i] = jq < PM ? r * RSTR + 16 * jq : kSink;
+    }
+    if (NIW == 5) {
+        wofs[NIW - 1] = (uint32_t)(jq < rmax ? jq : rmax) * row_bytes + 256u;
+        pofs[NIW - 1] = lane < 16 ? jq * RSTR + 256 : kSink;
+    }
 
     u32x4 wv[NIW], av[4];
     auto load_w = [&](int s) __attribute__((always_inline)) {
         const uint8_t *wstep = wg + ((uint32_t)(s * Geo<T>::STEP) & ~15u);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (wlive[i]) wv[i] = *(const u32x4 *)(wstep + (size_t)(4 * i) * row_bytes + wl);
-        if (NIW == 5 && wlive[NIW - 1]) wv[NIW - 1] = *(const u32x4 *)(wstep + wl16);
+        for (int i = 0; i < NIW; ++i) wv[i] = *(const u32x4 *)(wstep + wofs[i]);
     };
     if (my_steps > 0) load_w(wave);
 
     // Activation loads: instruction i covers columns 2i, 2i+1, 32 lanes per column, lane piece
-    // j = lane % 32 (j < 18: a column's 288 bytes of the step).
+    // j = lane % 32 (j < 18: a column's 288 bytes of the step).  Lanes without a piece re-read
+    // the last column's piece 0 and park it in the sink.
     const int cq = lane >> 5, ja = lane & 31;
     const int nia = (ncols + 1) >> 1;
     int64_t aoff[4];
-    bool alive[4];
+    int32_t aofs[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int c = 2 * i + cq;
-        alive[i] = ja < 18 && c < ncols;
-        aoff[i] = EXPERT ? (alive[i] ? mc.arow(c) * (int64_t)col_bytes : 0) + 16 * ja
-                         : (int64_t)c * col_bytes + 16 * ja;
+        const bool live = ja < 18 && c < ncols;
+        const int ce = c < ncols ? c : ncols - 1;
+        aoff[i] = (EXPERT ? mc.arow(ce) : (int64_t)ce) * (int64_t)col_bytes + 16 * (ja < 18 ? ja : 0);
+        aofs[i] = live ? WB + c * kActStep + 16 * ja : kSink;
     }
-    const uint32_t pa = (uint32_t)cq * kActStep + 16u * ja;
     // fp32 input: a column's 256 step values are 8 blocks of 4 lanes, 8 values per lane, so a
     // pass covers columns 2i + lane/32; the first NPF passes are fetched ahead into registers
-    // (one for Q6_K, whose unpacking needs the registers), the rest at park time.
+    // (one for Q6_K, whose unpacking needs the registers), the rest at park time.  Lanes of a
+    // missing odd column quantize a copy of the last column and park it in the sink.
     constexpr int NPF = T == kQ6_K ? 1 : 2;
     const size_t xstride = (size_t)P.nsteps * kSuper;
-    const float *xf = (const float *)xin + (size_t)cq * xstride + 8 * ja;
-    const float4 fz = make_float4(0.f, 0.f, 0.f, 0.f);
-    float4 x0a = fz, x0b = fz, x1a = fz, x1b = fz;   // passes 0 and 1 (named: kept in registers)
+    const float *xf = (const float *)xin + 8 * ja;
+    size_t xcol[4];
+    int32_t xdst[4];
+    const int qb = (lane >> 2) & 7, qsub = lane & 3;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int c = 2 * i + cq;
+        xcol[i] = (size_t)(c < ncols ? c : ncols - 1) * xstride;
+        xdst[i] = c < ncols ? WB + c * kActStep + qb * kQ8_1Bytes : kSink;
+    }
+    float4 x0a, x0b, x1a, x1b;   // passes 0 and 1 (named: kept in registers)
     auto load8 = [&](int s, int i, float4 &a, float4 &b) __attribute__((always_inline)) {
-        const float *src = xf + s * kSuper + 2 * i * xstride;
-        a = b = fz;
-        if (2 * i + cq < ncols) {
-            a = *(const float4 *)src;
-            b = *(const float4 *)(src + 4);
-        }
+        const float *src = xf + xcol[i] + s * kSuper;
+        a = *(const float4 *)src;
+        b = *(const float4 *)(src + 4);
     };
     auto load_a = [&](int s) __attribute__((always_inline)) {
         if constexpr (F32) {
@@ -158,7 +175,7 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
             const uint8_t *astep = (const uint8_t *)xin + (uint32_t)(s * kActStep);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                if (i < nia && alive[i]) av[i] = *(const u32x4 *)(astep + aoff[i]);
+                if (i < nia) av[i] = *(const u32x4 *)(astep + aoff[i]);   // wave-uniform test
         }
     };
     if (my_steps > 0) load_a(wave);
@@ -166,11 +183,9 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
     auto park = [&](int s) __attribute__((always_inline)) {
         if constexpr (F32) {
             // quantized before the weights are parked so late loads overlap the weights' arrival
-            const int b = (lane >> 2) & 7, sub = lane & 3;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                if (2 * i < ncols) {   // wave-uniform; the lanes of a missing odd column quantize zeros
-                    const int c = 2 * i + cq;
+                if (2 * i < ncols) {   // wave-uniform
                     float4 a, bv;
                     if (i == 0) {
                         a = x0a;
@@ -182,21 +197,17 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
                         load8(s, i, a, bv);
                     }
                     const Q81Lane4 q = quantize_q8_1_lane4(a, bv);
-                    if (c < ncols) {
-                        uint8_t *blk = st + WB + c * kActStep + b * kQ8_1Bytes;
-                        *(u32x2_a4 *)(blk + 4 + 8 * sub) = u32x2{q.c0, q.c1};
-                        if (sub == 0) *(uint32_t *)blk = q.ds;
-                    }
+                    uint8_t *blk = st + xdst[i];
+                    *(u32x2_a4 *)(blk + 4 + 8 * qsub) = u32x2{q.c0, q.c1};
+                    *(uint32_t *)(qsub == 0 ? blk : st + kSink) = q.ds;
                 }
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (wlive[i]) *(u32x4 *)(st + 4 * i * RSTR + pl) = wv[i];
-        if (NIW == 5 && wlive[NIW - 1]) *(u32x4 *)(st + pl16) = wv[NIW - 1];
+        for (int i = 0; i < NIW; ++i) *(u32x4 *)(st + pofs[i]) = wv[i];
         if constexpr (!F32) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                if (i < nia && alive[i]) *(u32x4 *)(st + WB + 2 * i * kActStep + pa) = av[i];
+                if (i < nia) *(u32x4 *)(st + aofs[i]) = av[i];
         }
     };
     if (lane < 4) ((uint32_t *)zero)[lane] = 0u;       // read only by this wave
@@ -263,11 +274,9 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
         if (!DBG) {
             // fp32 (d, s) of the step's 8 blocks x 8 columns; columns past ncols read as zero.
             const int b = lane >> 3, c = lane & 7;
-            float2 v = make_float2(0.f, 0.f);
-            if (c < ncols) {
-                const uint32_t ds = *(const uint32_t *)(st + WB + c * kActStep + b * kQ8_1Bytes);
-                v = make_float2(h2f((uint16_t)(ds & 0xFFFF)), h2f((uint16_t)(ds >> 16)));
-            }
+            const uint32_t ds = *(const uint32_t *)(st + WB + (c < ncols ? c : 0) * kActStep + b * kQ8_1Bytes);
+            const float2 v = c < ncols ? make_float2(h2f((uint16_t)(ds & 0xFFFF)), h2f((uint16_t)(ds >> 16)))
+                                       : make_float2(0.f, 0.f);
             ((float2 *)(st + WB + S::AB))[lane] = v;
         }
         auto aop = [&](int cg, int j) -> u32x4 {
@@ -411,7 +420,7 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
     const int t = threadIdx.x;
     if (t >= 128) return;
     float v = 0.f;
-    for (int wv = 0; wv < nwaves; ++wv) v += ((const float *)(smem + (size_t)wv * (16 + SB) + 16))[t];
+    for (int wv = 0; wv < nwaves; ++wv) v += ((const float *)(smem + (size_t)wv * (kHead + SB) + kHead))[t];
     int rr, c;
     if (T == kQ6_K) { rr = t >> 3; c = t & 7; }
     else { rr = (t >> 2) & 15; c = 4 * (t >> 6) + (t & 3); }
@@ -423,7 +432,7 @@ hipError_t launch_t(const uint8_t *w, int64_t rows, int64_t k, const void *xq, i
                     int32_t *dbg, const ColMap &c, int64_t n_exp, hipStream_t s) {
     const int64_t nsteps = k / kSuper;
     const int nw = (int)(nsteps < 16 ? nsteps : 16);
-    const size_t smem = (size_t)nw * (16 + Stage<T>::BYTES);
+    const size_t smem = (size_t)nw * (kHead + Stage<T>::BYTES);
     MvArgs a;
     a.rows = rows;
     a.row_bytes = (uint32_t)((k / Fmt<T>::QK) * Fmt<T>::BYTES);
