@@ -4,23 +4,26 @@
 //
 // CDNA4 design.  A workgroup owns 16 weight rows; wave w takes the 256-value steps w, w+W, ...
 // (up to 16 waves, so a 4096-wide K gives every wave one step and a CU 16 waves to hide HBM
-// latency with).  For each step the wave loads the 16 rows' bytes of that step, and the step's
-// q8_1 blocks of every column, with coalesced 16-byte loads (consecutive lanes fetch consecutive
-// pieces of one contiguous run, so a quarter-wave touches one cache line), parks them in its own
-// LDS stage, and loads the next step while it computes.  No workgroup barrier in the loop.
-// Operands are then read from LDS in the MFMA lane layout: one v_mfma_i32_16x16x64_i8 per
-// 64-value slice, B = 16 weight rows, A = activations placed block-diagonally over
-// (column, sub-block) so every int32 result is one exact sub-block dot D (the same contraction
-// as the register-streamed kernel in mmvq.hip, which serves the shapes this one does not).
-// Fixups per D in fp32 ("dp4a path Q4_K" section of the MMQ page):
+// latency with).  For each step the wave loads the 16 rows' bytes of that step and the step's
+// activations with coalesced loads, parks them in its own LDS stage, and loads the next step
+// while it computes.  No workgroup barrier in the loop.  Operands are then read from LDS in the
+// MFMA lane layout: one v_mfma_i32_16x16x64_i8 per 64-value slice, B = 16 weight rows, A =
+// activations placed block-diagonally over (column, sub-block) so every int32 result is one exact
+// sub-block dot D (the same contraction as the register-streamed kernel in mmvq.hip, which serves
+// the shapes this one does not).  Fixups per D in fp32 ("dp4a path Q4_K" section of the MMQ page):
 //   Q4_K  acc += D * (d*sc) * d_a - (dmin*m) * s_a
 //   Q6_K  acc += D * (d*sc) * d_a      (D includes -32 * sum q_a via a second MFMA)
 //   Q8_0  acc += D * d_w * d_a
-// For fp32 activations (dense) the wave quantizes its step's blocks itself, 4 lanes per block with
-// the arithmetic of the standalone quantize kernel (q8_1.hpp), and parks the q8_1 bytes in the
-// same place -- one launch instead of two.
-// Requirements (checked by the host): weights, activations and every row 16-byte aligned, and
-// K a multiple of 256, so each step's pieces are whole 16-byte units inside the row.
+// Every 16-byte LDS operand sits at a 16-byte aligned address (a misaligned ds_read_b128 runs at
+// a quarter to an eighth of the aligned rate), so parking reshapes what the loads return: q8_1
+// blocks (36 bytes) are split into 32 aligned code bytes per block and an fp32 (d, s) table; a Q6_K
+// super-block (210 bytes, at an even offset) is shifted into place with a lane exchange and
+// v_alignbyte; Q8_0 blocks (34 bytes) are loaded two at a time (68 bytes, 4-byte aligned) and
+// split into aligned codes and fp32 scales.  For fp32 activations (dense) the wave quantizes its
+// step's blocks itself, 4 lanes per block with the arithmetic of the standalone quantize kernel
+// (q8_1.hpp) -- one launch instead of two.
+// Requirements (checked by the host): K a multiple of 256; Q4_K and Q6_K weights and rows 16-byte
+// aligned, Q8_0 weights 4-byte aligned; q8_1 activations 4-byte aligned (fp32: 16-byte).
 #include "common.hpp"
 #include "launch.hpp"
 #include "mv_cols.hpp"
@@ -37,19 +40,22 @@ constexpr int kActStep = 8 * kQ8_1Bytes;   // one column's q8_1 bytes per 256-va
 // divergent branches around memory operations).
 constexpr int kHead = 64;
 
-// Per-type step geometry: PPR 16-byte pieces per row per step (Q6_K: the 16-byte-aligned window
-// around a 210-byte super-block that starts at an even offset -- always 14 pieces), STEP bytes
-// per row per step, RSTR the LDS row stride (16 rows read in one MFMA operand fetch fall in
-// distinct banks).
+typedef u32x4 __attribute__((aligned(4))) u32x4_a4;
+
+// Per-type step geometry.  Q4_K / Q6_K: PPR 16-byte pieces per row per step (Q6_K: the
+// 16-byte-aligned window around a 210-byte super-block that starts at an even offset -- always
+// 14 pieces), STEP bytes per row per step.  RSTR is the LDS row stride (16 rows read in one MFMA
+// operand fetch fall in distinct banks); Q8_0 rows hold 8 blocks x 32 aligned code bytes, WD its
+// fp32 block scales [16 rows][8 blocks].
 template <int T> struct Geo;
-template <> struct Geo<kQ4_K> { static constexpr int PPR = 9, STEP = 144, RSTR = 144; };
-template <> struct Geo<kQ6_K> { static constexpr int PPR = 14, STEP = 210, RSTR = 240; };
-template <> struct Geo<kQ8_0> { static constexpr int PPR = 17, STEP = 272, RSTR = 272; };
+template <> struct Geo<kQ4_K> { static constexpr int PPR = 9, STEP = 144, RSTR = 144, WD = 0; };
+template <> struct Geo<kQ6_K> { static constexpr int PPR = 14, STEP = 210, RSTR = 240, WD = 0; };
+template <> struct Geo<kQ8_0> { static constexpr int PPR = 0, STEP = 272, RSTR = 272, WD = 16 * 8 * 4; };
 
 template <int T> struct Stage {
-    static constexpr int WB = kRows * Geo<T>::RSTR;   // weights: [row][RSTR]
-    static constexpr int AB = 8 * kActStep;           // activations: [column][288]
-    static constexpr int FB = 64 * 8;                 // fp32 (d, s): [block 0..7][column 0..7]
+    static constexpr int WB = kRows * Geo<T>::RSTR + Geo<T>::WD;   // weights (+ Q8_0 scales)
+    static constexpr int AB = 8 * 256;                             // activation codes: [column][block][32]
+    static constexpr int FB = 64 * 8;                              // fp32 (d, s): [block][column]
     static constexpr int BYTES = WB + AB + FB;
 };
 
@@ -57,7 +63,24 @@ __device__ __forceinline__ uint32_t nib_lo(uint32_t v) { return v & 0x0F0F0F0Fu;
 __device__ __forceinline__ uint32_t nib_hi(uint32_t v) { return (v >> 4) & 0x0F0F0F0Fu; }
 __device__ __forceinline__ u32x4 nib_lo4(u32x4 v) { return u32x4{nib_lo(v.x), nib_lo(v.y), nib_lo(v.z), nib_lo(v.w)}; }
 __device__ __forceinline__ u32x4 nib_hi4(u32x4 v) { return u32x4{nib_hi(v.x), nib_hi(v.y), nib_hi(v.z), nib_hi(v.w)}; }
-__device__ __forceinline__ u32x4 lds16(const uint8_t *p) { return *(const u32x4_a2 *)p; }
+__device__ __forceinline__ u32x4 lds16(const uint8_t *p) { return *(const u32x4 *)p; }   // 16-byte aligned
+__device__ __forceinline__ uint32_t abyte(uint32_t hi, uint32_t lo, uint32_t sh) {
+    return __builtin_amdgcn_alignbyte(hi, lo, sh);
+}
+
+// The same register of the next lane within a row of 16 lanes (DPP row_shl:1; the last lane of a
+// row keeps its own value, which no caller uses).
+__device__ __forceinline__ uint32_t from_next_lane(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x101, 0xF, 0xF, false);
+}
+
+// Bytes [16j + 4Q + r, +16) of a row whose 16-byte pieces j (this lane) and j+1 are c and n.
+template <int Q> __device__ __forceinline__ u32x4 shift_piece(u32x4 c, u32x4 n, uint32_t r) {
+    const uint32_t D[8] = {c.x, c.y, c.z, c.w, n.x, n.y, n.z, n.w};
+    return u32x4{abyte(D[Q + 1], D[Q], r), abyte(D[Q + 2], D[Q + 1], r), abyte(D[Q + 3], D[Q + 2], r),
+                 abyte(D[Q + 4], D[Q + 3], r)};
+}
+template <int V> struct IC { static constexpr int value = V; };
 
 // Q4_K block diagonal (as in mmvq.hip): MFMA j covers sub-blocks {(j>>1)*4 + (j&1) + 2*sel};
 // lanes g in {1,2} carry diagonal half 0, g in {3,0} half 1; g odd holds values 0-15 of its
@@ -82,12 +105,13 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
                                                           MvArgs P, ColMap cm) {
     using S = Stage<T>;
     constexpr int PPR = Geo<T>::PPR, RSTR = Geo<T>::RSTR, WB = S::WB, SB = S::BYTES;
+    constexpr int A0 = WB, F0 = WB + S::AB;   // activation codes and (d, s) table within a stage
     constexpr int NCG = (T == kQ6_K) ? 2 : 1;
     extern __shared__ __align__(16) uint8_t smem[];
 
     MvCols mc;
     if (!mv_resolve(mc, w, P.n, cm, EXPERT)) return;   // workgroup-uniform
-    const int ncols = mc.ncols;
+    const int ncols = mc.ncols;                           // >= 1
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int nwaves = blockDim.x >> 6;
@@ -101,65 +125,82 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
     constexpr int kSink = 16 - kHead;                      // sink offset relative to st
     const int my_steps = P.q + (wave < P.r ? 1 : 0);
 
-    // Weight loads: instruction i covers rows 4i..4i+3, 16 lanes per row, lane piece j = lane % 16
-    // (j < PPR); Q8_0's 17th piece of every row comes from a fifth instruction (lanes 0..15).  The
-    // lane's byte offsets are the same for every step.  Lanes past PPR re-read piece 0 and rows
+    // Weight loads.  Q4_K / Q6_K: instruction i covers rows 4i..4i+3, 16 lanes per row, lane piece
+    // j = lane % 16 (j < PPR) of the step's aligned window.  Q8_0: lane (row lane/4, pair lane%4)
+    // reads the 68 bytes of blocks 2p, 2p+1 of the step.  Lanes past PPR re-read piece 0 and rows
     // past the end re-read the last row (valid addresses, no predicate); their copies go to the
     // sink (pieces) or to rows whose outputs are never written.
-    constexpr int NIW = PPR > 16 ? 5 : 4;
     constexpr int PM = PPR < 16 ? PPR : 16;
     const int rq = lane >> 4, jq = lane & 15;
-    uint32_t wofs[NIW];
-    int32_t pofs[NIW];
+    const int r8 = lane >> 2, p8 = lane & 3;   // Q8_0 lane roles
+    uint32_t wofs[4];
+    int32_t pofs[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = 4 * i + rq;
         wofs[i] = (uint32_t)(r < rmax ? r : rmax) * row_bytes + 16u * (jq < PM ? jq : 0);
         pofs[i] = jq < PM ? r * RSTR + 16 * jq : kSink;
     }
-    if (NIW == 5) {
-        wofs[NIW - 1] = (uint32_t)(jq < rmax ? jq : rmax) * row_bytes + 256u;
-        pofs[NIW - 1] = lane < 16 ? jq * RSTR + 256 : kSink;
-    }
+    const uint32_t wofs8 = (uint32_t)(r8 < rmax ? r8 : rmax) * row_bytes + 68u * p8;
 
-    u32x4 wv[NIW], av[4];
+    u32x4 wv[4];
+    uint32_t wv4 = 0;
     auto load_w = [&](int s) __attribute__((always_inline)) {
-        const uint8_t *wstep = wg + ((uint32_t)(s * Geo<T>::STEP) & ~15u);
+        if constexpr (T == kQ8_0) {
+            const uint8_t *src = wg + (uint32_t)(s * 272) + wofs8;
 #pragma unroll
-        for (int i = 0; i < NIW; ++i) wv[i] = *(const u32x4 *)(wstep + wofs[i]);
+            for (int i = 0; i < 4; ++i) wv[i] = *(const u32x4_a4 *)(src + 16 * i);
+            wv4 = *(const uint32_t *)(src + 64);
+        } else {
+            const uint8_t *wstep = wg + ((uint32_t)(s * Geo<T>::STEP) & ~15u);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wv[i] = *(const u32x4 *)(wstep + wofs[i]);
+        }
     };
     if (my_steps > 0) load_w(wave);
 
-    // Activation loads: instruction i covers columns 2i, 2i+1, 32 lanes per column, lane piece
-    // j = lane % 32 (j < 18: a column's 288 bytes of the step).  Lanes without a piece re-read
-    // the last column's piece 0 and park it in the sink.
-    const int cq = lane >> 5, ja = lane & 31;
-    const int nia = (ncols + 1) >> 1;
-    int64_t aoff[4];
-    int32_t aofs[4];
+    // q8_1 activation loads.  Codes: instruction i covers columns 4i..4i+3, lane (column 4i +
+    // lane/16, block (lane/2)%8, half lane%2) reads 16 code bytes; scales: lane (column lane/8,
+    // block lane%8) reads the block's (d, s).  Missing columns re-read the last column and park
+    // in the sink.
+    const int nic = (ncols + 3) >> 2;
+    int64_t acoff[2];
+    int32_t acdst[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int c = 2 * i + cq;
-        const bool live = ja < 18 && c < ncols;
+    for (int i = 0; i < 2; ++i) {
+        const int c = 4 * i + (lane >> 4), b = (lane >> 1) & 7, h = lane & 1;
         const int ce = c < ncols ? c : ncols - 1;
-        aoff[i] = (EXPERT ? mc.arow(ce) : (int64_t)ce) * (int64_t)col_bytes + 16 * (ja < 18 ? ja : 0);
-        aofs[i] = live ? WB + c * kActStep + 16 * ja : kSink;
+        acoff[i] = (EXPERT ? mc.arow(ce) : (int64_t)ce) * (int64_t)col_bytes + 36 * b + 4 + 16 * h;
+        acdst[i] = c < ncols ? A0 + c * 256 + 32 * b + 16 * h : kSink;
     }
+    int64_t asoff;
+    int32_t asdst;
+    {
+        const int c = lane >> 3, b = lane & 7;
+        const int ce = c < ncols ? c : ncols - 1;
+        asoff = (EXPERT ? mc.arow(ce) : (int64_t)ce) * (int64_t)col_bytes + 36 * b;
+        asdst = c < ncols ? F0 + 8 * (8 * b + c) : kSink;
+    }
+    u32x4 av[2];
+    uint32_t ads = 0;
+
     // fp32 input: a column's 256 step values are 8 blocks of 4 lanes, 8 values per lane, so a
     // pass covers columns 2i + lane/32; the first NPF passes are fetched ahead into registers
     // (one for Q6_K, whose unpacking needs the registers), the rest at park time.  Lanes of a
     // missing odd column quantize a copy of the last column and park it in the sink.
     constexpr int NPF = T == kQ6_K ? 1 : 2;
+    const int cq = lane >> 5, ja = lane & 31;
     const size_t xstride = (size_t)P.nsteps * kSuper;
     const float *xf = (const float *)xin + 8 * ja;
     size_t xcol[4];
-    int32_t xdst[4];
+    int32_t xdst[4], xfd[4];
     const int qb = (lane >> 2) & 7, qsub = lane & 3;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int c = 2 * i + cq;
         xcol[i] = (size_t)(c < ncols ? c : ncols - 1) * xstride;
-        xdst[i] = c < ncols ? WB + c * kActStep + qb * kQ8_1Bytes : kSink;
+        xdst[i] = c < ncols ? A0 + c * 256 + 32 * qb + 8 * qsub : kSink;
+        xfd[i] = c < ncols && qsub == 0 ? F0 + 8 * (8 * qb + c) : kSink;
     }
     float4 x0a, x0b, x1a, x1b;   // passes 0 and 1 (named: kept in registers)
     auto load8 = [&](int s, int i, float4 &a, float4 &b) __attribute__((always_inline)) {
@@ -174,8 +215,9 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
         } else {
             const uint8_t *astep = (const uint8_t *)xin + (uint32_t)(s * kActStep);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (i < nia) av[i] = *(const u32x4 *)(astep + aoff[i]);   // wave-uniform test
+            for (int i = 0; i < 2; ++i)
+                if (i < nic) av[i] = *(const u32x4_a4 *)(astep + acoff[i]);   // wave-uniform test
+            ads = *(const uint32_t *)(astep + asoff);
         }
     };
     if (my_steps > 0) load_a(wave);
@@ -197,20 +239,54 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
                         load8(s, i, a, bv);
                     }
                     const Q81Lane4 q = quantize_q8_1_lane4(a, bv);
-                    uint8_t *blk = st + xdst[i];
-                    *(u32x2_a4 *)(blk + 4 + 8 * qsub) = u32x2{q.c0, q.c1};
-                    *(uint32_t *)(qsub == 0 ? blk : st + kSink) = q.ds;
+                    *(u32x2 *)(st + xdst[i]) = u32x2{q.c0, q.c1};
+                    *(float2 *)(st + xfd[i]) = make_float2(h2f((uint16_t)(q.ds & 0xFFFF)), h2f((uint16_t)(q.ds >> 16)));
                 }
-        }
+        } else {
 #pragma unroll
-        for (int i = 0; i < NIW; ++i) *(u32x4 *)(st + pofs[i]) = wv[i];
-        if constexpr (!F32) {
+            for (int i = 0; i < 2; ++i)
+                if (i < nic) *(u32x4 *)(st + acdst[i]) = av[i];
+            *(float2 *)(st + asdst) = make_float2(h2f((uint16_t)(ads & 0xFFFF)), h2f((uint16_t)(ads >> 16)));
+        }
+        if constexpr (T == kQ4_K) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) *(u32x4 *)(st + pofs[i]) = wv[i];
+        } else if constexpr (T == kQ6_K) {
+            // the super-block starts a6 bytes into the aligned window: shift every piece by a6
+            // (wave-uniform) so that LDS row r holds super-block bytes 0..209 at offset 0
+            const uint32_t a6 = (uint32_t)(s * 210) & 15u;
+            u32x4 nx[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                if (i < nia) *(u32x4 *)(st + aofs[i]) = av[i];
+                nx[i] = u32x4{from_next_lane(wv[i].x), from_next_lane(wv[i].y), from_next_lane(wv[i].z),
+                              from_next_lane(wv[i].w)};
+            auto put = [&](auto QC) __attribute__((always_inline)) {
+                constexpr int Q = decltype(QC)::value;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) *(u32x4 *)(st + pofs[i]) = shift_piece<Q>(wv[i], nx[i], a6 & 3u);
+            };
+            switch (a6 >> 2) {
+                case 0: put(IC<0>{}); break;
+                case 1: put(IC<1>{}); break;
+                case 2: put(IC<2>{}); break;
+                default: put(IC<3>{}); break;
+            }
+        } else {
+            // Q8_0: bytes 0..67 of blocks 2p, 2p+1 = {d0, q0[32], d1, q1[32]}; q0 sits 2 bytes off
+            // a dword boundary, q1 on one
+            const uint32_t D[17] = {wv[0].x, wv[0].y, wv[0].z, wv[0].w, wv[1].x, wv[1].y, wv[1].z, wv[1].w,
+                                    wv[2].x, wv[2].y, wv[2].z, wv[2].w, wv[3].x, wv[3].y, wv[3].z, wv[3].w, wv4};
+            uint8_t *dst = st + r8 * RSTR + 64 * p8;
+            *(u32x4 *)dst = u32x4{abyte(D[1], D[0], 2), abyte(D[2], D[1], 2), abyte(D[3], D[2], 2), abyte(D[4], D[3], 2)};
+            *(u32x4 *)(dst + 16) = u32x4{abyte(D[5], D[4], 2), abyte(D[6], D[5], 2), abyte(D[7], D[6], 2), abyte(D[8], D[7], 2)};
+            *(u32x4 *)(dst + 32) = u32x4{D[9], D[10], D[11], D[12]};
+            *(u32x4 *)(dst + 48) = u32x4{D[13], D[14], D[15], D[16]};
+            *(float2 *)(st + kRows * RSTR + 4 * (8 * r8 + 2 * p8)) =
+                make_float2(h2f((uint16_t)(D[0] & 0xFFFF)), h2f((uint16_t)(D[8] >> 16)));
         }
     };
-    if (lane < 4) ((uint32_t *)zero)[lane] = 0u;       // read only by this wave
+    if (lane < 4) ((uint32_t *)zero)[lane] = 0u;                  // read only by this wave
+    ((float2 *)(st + F0))[lane] = make_float2(0.f, 0.f);          // columns past ncols stay zero
 
     // Per-lane operand addresses (offsets within a stage).
     const int g = lane >> 4, r16 = lane & 15;
@@ -243,7 +319,7 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
                 half = g & 1;
             }
             on = on && c < ncols;
-            a_off[cg][j] = on ? (uint32_t)(WB + c * kActStep + blk * kQ8_1Bytes + 4 + 16 * half) : 0xFFFFFFFFu;
+            a_off[cg][j] = on ? (uint32_t)(A0 + c * 256 + blk * 32 + 16 * half) : 0xFFFFFFFFu;
         }
 
     float acc[NCG][4];
@@ -261,6 +337,7 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
         dbg_row = dbg + row * per;
     }
     const i32x4 zero4 = {0, 0, 0, 0};
+    const float2 *ftab = (const float2 *)(st + F0);
 
     for (int it = 0; it < my_steps; ++it) {
         const int s = wave + it * nwaves;
@@ -270,15 +347,6 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
             load_a(s + nwaves);
         }
 
-        const float2 *ftab = (const float2 *)(st + WB + S::AB);
-        if (!DBG) {
-            // fp32 (d, s) of the step's 8 blocks x 8 columns; columns past ncols read as zero.
-            const int b = lane >> 3, c = lane & 7;
-            const uint32_t ds = *(const uint32_t *)(st + WB + (c < ncols ? c : 0) * kActStep + b * kQ8_1Bytes);
-            const float2 v = c < ncols ? make_float2(h2f((uint16_t)(ds & 0xFFFF)), h2f((uint16_t)(ds >> 16)))
-                                       : make_float2(0.f, 0.f);
-            ((float2 *)(st + WB + S::AB))[lane] = v;
-        }
         auto aop = [&](int cg, int j) -> u32x4 {
             const uint32_t o = a_off[cg][j];
             return lds16(o == 0xFFFFFFFFu ? zero : st + o);
@@ -319,8 +387,7 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
                 }
             }
         } else if constexpr (T == kQ6_K) {
-            const int a6 = (s * 210) & 15;
-            const uint8_t *wr = st + wrow + a6;
+            const uint8_t *wr = st + wrow;
             const u32x4 ql0 = lds16(wr + 16 * g);
             const u32x4 ql1 = lds16(wr + 64 + 16 * g);
             const u32x4 qh0 = lds16(wr + 128 + 16 * (g & 1));   // qh of half 0 for this lane's l range
@@ -366,11 +433,11 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
             }
         } else {
             const uint8_t *wr = st + wrow;
+            const float *wd = (const float *)(st + kRows * RSTR) + 8 * r16;
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
                 const int blk = 2 * p + (g >> 1);
-                const uint8_t *bp = wr + blk * 34;
-                const u32x4 q = lds16(bp + 2 + 16 * (g & 1));
+                const u32x4 q = lds16(wr + 64 * p + 16 * g);
                 const i32x4 D = mfma16x16x64(aop(0, p), q, zero4);
                 if (DBG) {
 #pragma unroll
@@ -379,7 +446,7 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
                         if (dbg_row && c < ncols) dbg_row[(int64_t)c * dbg_ld + s * 8 + blk] = D[e];
                     }
                 } else {
-                    const float ws = h2f(*(const uint16_t *)bp);
+                    const float ws = wd[blk];
                     const f32x4 t0 = *(const f32x4 *)(ftab + blk * 8 + 4 * (g & 1));
                     const f32x4 t1 = *(const f32x4 *)(ftab + blk * 8 + 4 * (g & 1) + 2);
                     acc[0][0] = fmaf((float)D[0], ws * t0.x, acc[0][0]);
@@ -469,9 +536,10 @@ bool mmvq_stream_supported(int type, const void *w, int64_t k, const void *xq, c
     if (type != kQ4_K && type != kQ6_K && type != kQ8_0) return false;
     if (k % kSuper != 0 || k < kSuper) return false;
     const int64_t row_bytes = type == kQ8_0 ? k / 32 * 34 : k / 256 * (type == kQ4_K ? 144 : 210);
-    if (row_bytes % 16 != 0) return false;
-    if ((uintptr_t)w % 16 != 0 || (uintptr_t)xq % 16 != 0) return false;
-    if (cm && cm->w_expert_stride % 16 != 0) return false;
+    const int64_t walign = type == kQ8_0 ? 4 : 16;   // Q8_0: 68-byte block pairs; else aligned windows
+    if (row_bytes % walign != 0 || (uintptr_t)w % walign != 0) return false;
+    if ((uintptr_t)xq % 4 != 0) return false;
+    if (cm && cm->w_expert_stride % walign != 0) return false;
     return true;
 }
 

@@ -169,16 +169,19 @@ def test_matvec_kernel_automatic_choice(qtype, n, expect):
 
 def test_matvec_kernel_choice_follows_alignment_and_overrides():
     mk = qmm.matvec_kernel
-    # q8_1 input 4-byte aligned: dot4 still serves Q4_K n = 1, the LDS-staged kernel needs 16 bytes
+    # q8_1 input: 4-byte alignment serves both dot4 and the LDS-staged kernel, 2-byte neither
     assert mk(qmm.Q4_K, 0x10000, 4096, 0x20004, 1, x_fp32=False) == (3, False)
-    assert mk(qmm.Q4_K, 0x10000, 4096, 0x20004, 5, x_fp32=False) == (1, False)
-    assert mk(qmm.Q4_K, 0x10000, 4096, 0x20000, 5, x_fp32=False) == (2, False)
+    assert mk(qmm.Q4_K, 0x10000, 4096, 0x20004, 5, x_fp32=False) == (2, False)
+    assert mk(qmm.Q4_K, 0x10000, 4096, 0x20002, 1, x_fp32=False) == (1, False)
+    assert mk(qmm.Q6_K, 0x10000, 4096, 0x20002, 5, x_fp32=False) == (1, False)
     # weights only 2-byte aligned: the register-streamed kernel, on the quantized copy
     assert mk(qmm.Q4_K, 0x10002, 4096, 0x20000, 1, x_fp32=True) == (1, False)
     assert mk(qmm.Q6_K, 0x10002, 4096, 0x20000, 4, x_fp32=True) == (1, False)
-    # Q8_0 weights 4-byte aligned: dot4 (needs 4) but not the LDS-staged kernel (needs 16)
+    # Q8_0 weights need 4-byte alignment in both kernels (Q4_K / Q6_K: 16 in the LDS-staged one)
     assert mk(qmm.Q8_0, 0x10004, 4096, 0x20000, 2, x_fp32=True) == (3, True)
-    assert mk(qmm.Q8_0, 0x10004, 4096, 0x20000, 6, x_fp32=True) == (1, False)
+    assert mk(qmm.Q8_0, 0x10004, 4096, 0x20000, 6, x_fp32=True) == (2, True)
+    assert mk(qmm.Q8_0, 0x10002, 4096, 0x20000, 6, x_fp32=True) == (1, False)
+    assert mk(qmm.Q6_K, 0x10004, 4096, 0x20000, 6, x_fp32=True) == (1, False)
     # K not a multiple of 256 (Q8_0 allows multiples of 32): register-streamed
     assert mk(qmm.Q8_0, 0x10000, 4128, 0x20000, 2, x_fp32=True) == (1, False)
     with pytest.raises(qmm.QmmError):

@@ -208,6 +208,35 @@ def test_matvec_kernel_variants(qtype, kernel):
     assert np.array_equal(got, oracle.subdots(qtype, w, 77, k, xq, nd))
 
 
+def _at_offset(a, off):
+    """Device copy of numpy bytes whose data pointer sits `off` bytes past a 256-byte boundary."""
+    buf = torch.zeros(a.nbytes + 512, dtype=torch.uint8, device=DEV)
+    base = (-buf.data_ptr()) % 256
+    view = buf[base + off: base + off + a.nbytes]
+    view.copy_(torch.from_numpy(np.ascontiguousarray(a).view(np.uint8).reshape(-1)))
+    assert view.data_ptr() % 256 == off
+    return view
+
+
+@pytest.mark.parametrize("qtype,woff", [(qmm.Q4_K, 16), (qmm.Q6_K, 16), (qmm.Q8_0, 4), (qmm.Q8_0, 36)],
+                         ids=["q4_K", "q6_K", "q8_0_w4", "q8_0_w36"])
+def test_matvec_lds_kernel_at_minimum_alignment(qtype, woff):
+    """The LDS-staged kernel at the least alignment it accepts: q8_1 activations 4 bytes past a
+    16-byte boundary (the 36-byte blocks are re-laid at park time), Q8_0 weights 4 bytes off."""
+    rows, k = 77, 4352 if qtype != qmm.Q6_K else 6144
+    qmm.set_override(qmm.OVR_MV_KERNEL, 2)
+    for n in (1, 3, 8):
+        w, x = _case(qtype, rows, k, n, 560 + n)
+        xq = oracle.quantize_q8_1(x)
+        wd, xd = _at_offset(w, woff), _at_offset(xq, 4)
+        assert qmm.matvec_kernel(qtype, wd, k, xd, n, x_fp32=False) == (2, False)
+        y = qmm.matmul_q8_1(wd, qtype, rows, k, xd, n).cpu().numpy()
+        ref = oracle.matmul_q8_1(qtype, w, rows, k, xq, n)
+        assert_close(y, ref, row_norms(qtype, w, rows, k), col_norms(xq, n, k), what=f"{TNAME[qtype]} n={n}")
+        got = qmm.debug_subdots(wd, qtype, rows, k, xd, n, qmm.PATH_MATVEC).cpu().numpy()
+        assert np.array_equal(got, oracle.subdots(qtype, w, rows, k, xq, n))
+
+
 @pytest.mark.parametrize("kernel,qtype,k,n", [(2, qmm.Q6_K, 768, 1),    # 630-byte rows: not 16-byte aligned
                                               (3, qmm.Q6_K, 4096, 1),   # dot4 serves Q4_K / Q8_0 only
                                               (3, qmm.Q4_K, 4096, 4)])  # dot4 takes at most 3 columns
