@@ -465,8 +465,10 @@ static int g_mv_kernel = 0;
 
 void set_mmvq_kernel(int which) { g_mv_kernel = which; }
 
-// Largest column count the automatic choice sends to the dot4 kernel, per type.
-static int dot4_auto_cols(int type) { return type == kQ4_K ? 2 : type == kQ8_0 ? 3 : 0; }
+// Largest column count the automatic choice sends to the dot4 kernel, per type: measured at
+// 4096 x 4096 (fp32 input, graph-replayed calls), dot4 is ~0.1 us faster than the LDS-staged
+// kernel at one column and 0.8-1.4 us slower at two or three.
+static int dot4_auto_cols(int type) { return type == kQ4_K || type == kQ8_0 ? 1 : 0; }
 
 static int g_fuse_cols = 0;   // 0: automatic (5)
 
@@ -481,10 +483,12 @@ static int fused_kernel(int type, const void *w, int64_t k, const float *x, int6
         if (n <= lim && mmvq_dot4_supported(type, w, k, x, nullptr)) return 3;
         if (kc == 3) return 0;
     }
-    // The LDS-staged kernel quantizes a step's blocks with 4 lanes per block; measured against a
-    // separate quantize launch at 4096 x 4096 it saves 0.4-2.4 us per call for Q6_K and Q8_0 at
-    // every n <= 8, and for Q4_K up to n = 5 (0.4 us lost at n = 8).
-    const int lim = g_fuse_cols > 0 ? g_fuse_cols : (type == kQ4_K ? 5 : 8);
+    // The LDS-staged kernel quantizes a step's blocks with 4 lanes per block; every workgroup
+    // quantizes all of x, so the cost grows with n while a separate quantize launch costs a
+    // fixed ~3 us.  Measured at 4096 x 4096: fused wins up to n = 3 for Q4_K (0.9 us at n = 3,
+    // 0.2 us lost at n = 5) and up to n = 5 for Q6_K and Q8_0 (0.3-0.5 us at n = 5, 0.3-0.5 us
+    // lost at n = 8).
+    const int lim = g_fuse_cols > 0 ? g_fuse_cols : (type == kQ4_K ? 4 : 5);
     if ((kc == 0 || kc == 2) && n <= lim && mmvq_stream_supported(type, w, k, x, nullptr)) return 2;
     return 0;
 }

@@ -35,10 +35,12 @@ namespace {
 
 constexpr int kRows = 16;
 constexpr int kActStep = 8 * kQ8_1Bytes;   // one column's q8_1 bytes per 256-value step (288)
-// Per-wave LDS head before its stage: 16 zero bytes (the off-diagonal A operand) and a 48-byte
-// sink that lanes with nothing to park write to, so every load and store is unconditional (no
-// divergent branches around memory operations).
-constexpr int kHead = 64;
+// Per-wave LDS head before its stage: 208 zero bytes (the off-diagonal A operand: a lane's
+// operand pointer for slice j is its base plus a fixed offset of at most 192, and lanes off the
+// diagonal take the zero block as base) and a 48-byte sink that lanes with nothing to park write
+// to, so every load and store is unconditional (no divergent branches around memory operations).
+constexpr int kHead = 256;
+constexpr int kZeroBytes = 208;
 
 typedef u32x4 __attribute__((aligned(4))) u32x4_a4;
 
@@ -120,9 +122,9 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
     const int64_t row0 = (int64_t)blockIdx.x * kRows;
     const int rmax = (int)((rows - row0) < kRows ? (rows - row0) : kRows) - 1;   // last live row of the group
     const uint8_t *wg = mc.wbase + row0 * (int64_t)row_bytes;
-    uint8_t *zero = smem + (size_t)wave * (kHead + SB);   // 16 zero bytes (off-diagonal A lanes)
+    uint8_t *zero = smem + (size_t)wave * (kHead + SB);   // zero block (off-diagonal A lanes)
     uint8_t *st = zero + kHead;                            // this wave's stage
-    constexpr int kSink = 16 - kHead;                      // sink offset relative to st
+    constexpr int kSink = kZeroBytes - kHead;              // sink offset relative to st
     const int my_steps = P.q + (wave < P.r ? 1 : 0);
 
     // Weight loads.  Q4_K / Q6_K: instruction i covers rows 4i..4i+3, 16 lanes per row, lane piece
@@ -157,7 +159,6 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
             for (int i = 0; i < 4; ++i) wv[i] = *(const u32x4 *)(wstep + wofs[i]);
         }
     };
-    if (my_steps > 0) load_w(wave);
 
     // q8_1 activation loads.  Codes: instruction i covers columns 4i..4i+3, lane (column 4i +
     // lane/16, block (lane/2)%8, half lane%2) reads 16 code bytes; scales: lane (column lane/8,
@@ -186,9 +187,9 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
 
     // fp32 input: a column's 256 step values are 8 blocks of 4 lanes, 8 values per lane, so a
     // pass covers columns 2i + lane/32; the first NPF passes are fetched ahead into registers
-    // (one for Q6_K, whose unpacking needs the registers), the rest at park time.  Lanes of a
+    // (one for Q6_K, whose unpacking needs registers), the rest at park time.  Lanes of a
     // missing odd column quantize a copy of the last column and park it in the sink.
-    constexpr int NPF = T == kQ6_K ? 1 : 2;
+    constexpr int NPF = T == kQ6_K ? 1 : 4;
     const int cq = lane >> 5, ja = lane & 31;
     const size_t xstride = (size_t)P.nsteps * kSuper;
     const float *xf = (const float *)xin + 8 * ja;
@@ -202,7 +203,7 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
         xdst[i] = c < ncols ? A0 + c * 256 + 32 * qb + 8 * qsub : kSink;
         xfd[i] = c < ncols && qsub == 0 ? F0 + 8 * (8 * qb + c) : kSink;
     }
-    float4 x0a, x0b, x1a, x1b;   // passes 0 and 1 (named: kept in registers)
+    float4 xa[4], xb[4];   // prefetched passes (constant indices only: kept in registers)
     auto load8 = [&](int s, int i, float4 &a, float4 &b) __attribute__((always_inline)) {
         const float *src = xf + xcol[i] + s * kSuper;
         a = *(const float4 *)src;
@@ -210,8 +211,9 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
     };
     auto load_a = [&](int s) __attribute__((always_inline)) {
         if constexpr (F32) {
-            load8(s, 0, x0a, x0b);
-            if (NPF > 1 && ncols > 2) load8(s, 1, x1a, x1b);
+#pragma unroll
+            for (int i = 0; i < NPF; ++i)
+                if (2 * i < ncols) load8(s, i, xa[i], xb[i]);   // wave-uniform test
         } else {
             const uint8_t *astep = (const uint8_t *)xin + (uint32_t)(s * kActStep);
 #pragma unroll
@@ -220,7 +222,12 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
             ads = *(const uint32_t *)(astep + asoff);
         }
     };
-    if (my_steps > 0) load_a(wave);
+    // Activations first: they come from L2, so their wait (loads retire in order) does not wait
+    // for the weights, and quantizing or re-laying them overlaps the weights' flight.
+    if (my_steps > 0) {
+        load_a(wave);
+        load_w(wave);
+    }
 
     auto park = [&](int s) __attribute__((always_inline)) {
         if constexpr (F32) {
@@ -229,12 +236,9 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
             for (int i = 0; i < 4; ++i)
                 if (2 * i < ncols) {   // wave-uniform
                     float4 a, bv;
-                    if (i == 0) {
-                        a = x0a;
-                        bv = x0b;
-                    } else if (i == 1 && NPF > 1) {
-                        a = x1a;
-                        bv = x1b;
+                    if (i < NPF) {
+                        a = xa[i];
+                        bv = xb[i];
                     } else {
                         load8(s, i, a, bv);
                     }
@@ -285,42 +289,45 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
                 make_float2(h2f((uint16_t)(D[0] & 0xFFFF)), h2f((uint16_t)(D[8] >> 16)));
         }
     };
-    if (lane < 4) ((uint32_t *)zero)[lane] = 0u;                  // read only by this wave
+    if (lane < kZeroBytes / 4) ((uint32_t *)zero)[lane] = 0u;     // read only by this wave
     ((float2 *)(st + F0))[lane] = make_float2(0.f, 0.f);          // columns past ncols stay zero
 
     // Per-lane operand addresses (offsets within a stage).
     const int g = lane >> 4, r16 = lane & 15;
     const int m = r16;   // this lane's A row
     const int wrow = r16 * RSTR;
-    uint32_t a_off[NCG][4];   // activation operand offsets, 0xFFFFFFFF = zero block
+    // A operand of slice j for column group cg: abase[cg] + aoffj(j); abase is the zero block
+    // for lanes off the diagonal or past the last column.
+    const uint8_t *abase[NCG];
 #pragma unroll
-    for (int cg = 0; cg < NCG; ++cg)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            int c, blk, half;
-            bool on;
-            if (T == kQ4_K) {
-                const int sel = m >> 3;
-                c = m & 7;
-                on = q4_group(g) == sel;
-                blk = q4_sub(j, sel);
-                half = q4_half(g);
-            } else if (T == kQ6_K) {
-                const int grp = m >> 2;
-                c = (m & 3) + 4 * cg;
-                on = g == grp;
-                blk = 2 * j + (grp >> 1);
-                half = grp & 1;
-            } else {
-                const int sel = m >> 3;
-                c = m & 7;
-                on = (g >> 1) == sel;
-                blk = 2 * j + sel;
-                half = g & 1;
-            }
-            on = on && c < ncols;
-            a_off[cg][j] = on ? (uint32_t)(A0 + c * 256 + blk * 32 + 16 * half) : 0xFFFFFFFFu;
+    for (int cg = 0; cg < NCG; ++cg) {
+        int c, blk0, half;
+        bool on;
+        if (T == kQ4_K) {
+            const int sel = m >> 3;
+            c = m & 7;
+            on = q4_group(g) == sel;
+            blk0 = q4_sub(0, sel);
+            half = q4_half(g);
+        } else if (T == kQ6_K) {
+            const int grp = m >> 2;
+            c = (m & 3) + 4 * cg;
+            on = g == grp;
+            blk0 = grp >> 1;
+            half = grp & 1;
+        } else {
+            const int sel = m >> 3;
+            c = m & 7;
+            on = (g >> 1) == sel;
+            blk0 = sel;
+            half = g & 1;
         }
+        abase[cg] = on && c < ncols ? st + A0 + c * 256 + blk0 * 32 + 16 * half : zero;
+    }
+    // Q4_K: slice j covers sub-blocks (j>>1)*4 + (j&1) + 2*sel; Q6_K / Q8_0: blocks 2j + ...
+    auto aoffj = [](int j) { return T == kQ4_K ? 32 * ((j >> 1) * 4 + (j & 1)) : 64 * j; };
+    static_assert(T != kQ4_K || 32 * 5 + 16 <= kZeroBytes, "zero block too small");
+    static_assert(64 * 3 + 16 <= kZeroBytes, "zero block too small");
 
     float acc[NCG][4];
 #pragma unroll
@@ -343,14 +350,11 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
         const int s = wave + it * nwaves;
         park(s);
         if (it + 1 < my_steps) {   // the next step's loads fly during this step's math
-            load_w(s + nwaves);
             load_a(s + nwaves);
+            load_w(s + nwaves);
         }
 
-        auto aop = [&](int cg, int j) -> u32x4 {
-            const uint32_t o = a_off[cg][j];
-            return lds16(o == 0xFFFFFFFFu ? zero : st + o);
-        };
+        auto aop = [&](int cg, int j) -> u32x4 { return lds16(abase[cg] + aoffj(j)); };
         if constexpr (T == kQ4_K) {
             const uint8_t *wr = st + wrow;
             const u32x4 hdr = lds16(wr);

@@ -149,13 +149,13 @@ qmm_status qmm_matvec_kernel(int type, const void *w, int64_t k, const void *x, 
  *   QMM_OVR_MV_KERNEL: matrix-vector kernel: 1 register-streamed (any input), 2 LDS-staged
  *                     MFMA only, 3 dot4 only (up to 3 columns, Q4_K and Q8_0); calls the forced
  *                     kernel cannot serve fail with QMM_ERR_HIP.  The automatic choice takes the
- *                     dot4 kernel for Q4_K with n <= 2 and Q8_0 with n <= 3, else the LDS-staged
- *                     kernel, when K is a multiple of 256 and the weights are aligned (Q4_K, Q6_K:
- *                     16 bytes, rows too; Q8_0: 4) and q8_1 activations 4-byte aligned; otherwise
- *                     the register-streamed kernel.
+ *                     dot4 kernel for Q4_K and Q8_0 with n = 1, else the LDS-staged kernel, when
+ *                     K is a multiple of 256 and the weights are aligned (Q4_K, Q6_K: 16 bytes,
+ *                     rows too; Q8_0: 4) and q8_1 activations 4-byte aligned; otherwise the
+ *                     register-streamed kernel.
  *   QMM_OVR_FUSE_COLS: qmm_matmul only: most columns (1..8) for which the LDS-staged kernel
  *                     quantizes the fp32 activations itself instead of a separate quantize
- *                     launch (automatic: 5 for Q4_K, 8 for Q6_K and Q8_0).
+ *                     launch (automatic: 4 for Q4_K, 5 for Q6_K and Q8_0).
  * Returns QMM_ERR_ARG for an unknown key or value.
  * ------------------------------------------------------------------------------------------- */
 enum { QMM_OVR_PATH = 1, QMM_OVR_STREAMK = 2, QMM_OVR_TILE_J = 3, QMM_OVR_MV_STEPS = 4, QMM_OVR_MV_KERNEL = 5,

@@ -150,14 +150,16 @@ def test_workspace_sizes_monotone():
 
 MV_AUTO = [
     # (type, n, expected (kernel, fused)) for aligned weights and fp32 activations, K = 4096:
-    # dot4 for Q4_K n <= 2 and Q8_0 n <= 3, else the LDS-staged kernel; it quantizes the fp32
-    # input itself up to 5 columns for Q4_K and 8 for Q6_K / Q8_0.
-    *[(qmm.Q4_K, n, (3, True)) for n in (1, 2)],
-    *[(qmm.Q4_K, n, (2, True)) for n in (3, 4, 5)],
-    *[(qmm.Q4_K, n, (2, False)) for n in (6, 7, 8)],
-    *[(qmm.Q6_K, n, (2, True)) for n in range(1, 9)],
-    *[(qmm.Q8_0, n, (3, True)) for n in (1, 2, 3)],
-    *[(qmm.Q8_0, n, (2, True)) for n in range(4, 9)],
+    # dot4 for Q4_K and Q8_0 at n = 1, else the LDS-staged kernel; it quantizes the fp32 input
+    # itself up to 4 columns for Q4_K and 5 for Q6_K / Q8_0.
+    (qmm.Q4_K, 1, (3, True)),
+    *[(qmm.Q4_K, n, (2, True)) for n in (2, 3, 4)],
+    *[(qmm.Q4_K, n, (2, False)) for n in (5, 6, 7, 8)],
+    *[(qmm.Q6_K, n, (2, True)) for n in range(1, 6)],
+    *[(qmm.Q6_K, n, (2, False)) for n in (6, 7, 8)],
+    (qmm.Q8_0, 1, (3, True)),
+    *[(qmm.Q8_0, n, (2, True)) for n in range(2, 6)],
+    *[(qmm.Q8_0, n, (2, False)) for n in (6, 7, 8)],
     *[(t, 9, (0, False)) for t in (qmm.Q4_K, qmm.Q6_K, qmm.Q8_0)],
 ]
 
@@ -178,8 +180,8 @@ def test_matvec_kernel_choice_follows_alignment_and_overrides():
     assert mk(qmm.Q4_K, 0x10002, 4096, 0x20000, 1, x_fp32=True) == (1, False)
     assert mk(qmm.Q6_K, 0x10002, 4096, 0x20000, 4, x_fp32=True) == (1, False)
     # Q8_0 weights need 4-byte alignment in both kernels (Q4_K / Q6_K: 16 in the LDS-staged one)
-    assert mk(qmm.Q8_0, 0x10004, 4096, 0x20000, 2, x_fp32=True) == (3, True)
-    assert mk(qmm.Q8_0, 0x10004, 4096, 0x20000, 6, x_fp32=True) == (2, True)
+    assert mk(qmm.Q8_0, 0x10004, 4096, 0x20000, 1, x_fp32=True) == (3, True)
+    assert mk(qmm.Q8_0, 0x10004, 4096, 0x20000, 5, x_fp32=True) == (2, True)
     assert mk(qmm.Q8_0, 0x10002, 4096, 0x20000, 6, x_fp32=True) == (1, False)
     assert mk(qmm.Q6_K, 0x10004, 4096, 0x20000, 6, x_fp32=True) == (1, False)
     # K not a multiple of 256 (Q8_0 allows multiples of 32): register-streamed
