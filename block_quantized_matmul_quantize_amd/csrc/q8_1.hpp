@@ -46,15 +46,20 @@ struct Q81Lane4 {
 
 __device__ __forceinline__ Q81Lane4 quantize_q8_1_lane4(float4 a, float4 b) {
     const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    float amax = fabsf(v[0]);
-#pragma unroll
-    for (int i = 1; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    float amax = fmaxf(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))),
+                       fmaxf(fmaxf(fabsf(v[4]), fabsf(v[5])), fmaxf(fabsf(v[6]), fabsf(v[7]))));
     amax = fmaxf(amax, dpp_f<kDppXor1>(amax));
     amax = fmaxf(amax, dpp_f<kDppXor2>(amax));
-    const float d32 = amax / 127.0f;
-    int q[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    // d32 = amax / 127 by one multiply and an fma correction: with c = RN(1/127), the corrected
+    // quotient equals the IEEE quotient for every amax whose quotient lies in [2^-101, 2^101]
+    // (checked exhaustively over all such floats); outside that range the division below runs.
+    const float c127 = 1.0f / 127.0f;
+    const float q1 = amax * c127;
+    float d32 = fmaf(fmaf(-q1, 127.0f, amax), c127, q1);
+    uint32_t c0 = 0u, c1 = 0u;
     if (amax != 0.0f) {
         bool slow = !(d32 >= 0x1p-100f && d32 <= 0x1p100f);
+        int q[8];
         if (!slow) {
             const float r = __builtin_amdgcn_rcpf(d32);
 #pragma unroll
@@ -66,16 +71,22 @@ __device__ __forceinline__ Q81Lane4 quantize_q8_1_lane4(float4 a, float4 b) {
             }
         }
         if (slow) {
+            d32 = amax / 127.0f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) q[i] = q81_round_div(v[i], d32);
         }
+        c0 = pack4(q[0], q[1], q[2], q[3]);
+        c1 = pack4(q[4], q[5], q[6], q[7]);
+    } else {
+        d32 = 0.0f;
     }
-    int sum = ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
+    // sum of the 8 codes by two byte dot products with ones, then over the 4 lanes
+    int sum = __builtin_amdgcn_sdot4((int)c1, 0x01010101, __builtin_amdgcn_sdot4((int)c0, 0x01010101, 0, false), false);
     sum += dpp_i<kDppXor1>(sum);
     sum += dpp_i<kDppXor2>(sum);
     Q81Lane4 out;
-    out.c0 = pack4(q[0], q[1], q[2], q[3]);
-    out.c1 = pack4(q[4], q[5], q[6], q[7]);
+    out.c0 = c0;
+    out.c1 = c1;
     const __half hd = __float2half_rn(d32);
     // s is the fp32 product d32 * sum(q) rounded to fp16.  The empty asm pins the fp32 product in a
     // register so it cannot be fused into a single-rounding multiply-to-fp16 (v_fma_mixlo_f16),
