@@ -89,7 +89,8 @@ qmm_status check_common(int type, int64_t rows, int64_t k, int64_t n) {
 int mmq_smem(int type, int J) {
     const int wt = type == QMM_Q4_K ? kTI * 144 : (type == QMM_Q6_K ? 2 * kTI * 272 : kTI * 272);
     const int wm = type == QMM_Q4_K ? 8 * kTI * 4 : 0;
-    return wt + 8 * kTI * 4 + wm + J * 272 + 8 * J * 8;
+    const int stg = type == QMM_Q6_K && J == 128 ? kTI * 224 : 0;   // raw super-block staging
+    return wt + 8 * kTI * 4 + wm + J * 272 + 8 * J * 8 + stg;
 }
 
 // Tiled-kernel workgroups resident per compute unit: the kernels keep about 200 registers per

@@ -24,6 +24,8 @@
 // goes to the unit's slot (0: its first tile, 1: its last) and the fixup kernel adds the slots
 // of a split tile in ascending unit order (deterministic, no atomics).  Without stream-K,
 // units == ntiles and every unit is exactly one tile.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -56,7 +58,9 @@ template <int T, int J> struct Smem {
     static constexpr int WM_OFF = WS_OFF + 8 * kTI * 4;                          // float [8][128] (Q4_K)
     static constexpr int A_OFF = WM_OFF + (T == kQ4_K ? 8 * kTI * 4 : 0);      // int8 [J][kLd]
     static constexpr int X_OFF = A_OFF + J * kLd;                                // float2 [8][J]
-    static constexpr int BYTES = X_OFF + 8 * J * 8;
+    static constexpr int STG_OFF = X_OFF + 8 * J * 8;                            // Q6_K raw [128][224]
+    static constexpr int STG_BYTES = (T == kQ6_K && Cfg<J>::NT >= 512) ? kTI * 224 : 0;
+    static constexpr int BYTES = STG_OFF + STG_BYTES;
 };
 
 // ---------------------------------------------------------------------------------------------
@@ -191,9 +195,11 @@ template <int NT> struct WFetch<kQ8_0, NT> {
     }
 };
 
-// Q6_K: unpacked straight from HBM into the two planes at park time (no register prefetch).
-template <int NT> struct WFetch<kQ6_K, NT> {
+// Q6_K with 4-wave tiles (J <= 64): unpacked straight from HBM into the two planes at park time
+// (no register prefetch: the registers are taken by the accumulators).
+template <int NT> struct WFetchQ6Direct {
     __device__ __forceinline__ void fetch(const uint8_t *, int64_t, int64_t, int64_t, int64_t, int64_t) {}
+    template <int J> __device__ __forceinline__ void unpack(uint8_t *, int64_t, int64_t) const {}
     template <int J>
     __device__ __forceinline__ void store(uint8_t *sm, const uint8_t *wbase, int64_t row_bytes, int64_t r0,
                                           int64_t rows, int64_t kb, int64_t) const {
@@ -238,6 +244,84 @@ template <int NT> struct WFetch<kQ6_K, NT> {
         }
     }
 };
+
+// Q6_K with 8-wave tiles (J = 128): the step's 210-byte super-blocks of the 128 rows are
+// prefetched into registers as 14 pieces per row (13 of 16 bytes, the 14th ends at the fp16 d),
+// parked raw in a staging area, and unpacked from there into the two planes after a barrier
+// (the unpack needs ql, qh and the scale of a 16-value group, which different pieces hold).
+template <int NT> struct WFetchQ6Staged {
+    static constexpr int NP = kTI * 14, N = (NP + NT - 1) / NT;
+    u32x4 q[N];
+    __device__ __forceinline__ void fetch(const uint8_t *wbase, int64_t row_bytes, int64_t r0, int64_t rows,
+                                          int64_t kb, int64_t) {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int it = 0; it < N; ++it) {
+            const int i = (tid + NT * it) < NP ? tid + NT * it : NP - 1;   // idle lanes re-read a valid piece
+            const int r = i / 14, j = i - 14 * r;
+            const int64_t row = r0 + r < rows ? r0 + r : rows - 1;       // ragged tile: re-read the last row
+            q[it] = ld16(wbase + row * row_bytes + kb * 210 + (j < 13 ? 16 * j : 194));
+        }
+    }
+    template <int J>
+    __device__ __forceinline__ void store(uint8_t *sm, const uint8_t *, int64_t, int64_t, int64_t, int64_t,
+                                          int64_t) const {
+        const int tid = threadIdx.x;
+        uint8_t *stg = sm + Smem<kQ6_K, J>::STG_OFF;
+        static_assert(Smem<kQ6_K, J>::STG_BYTES > 0, "staging area missing");
+#pragma unroll
+        for (int it = 0; it < N; ++it) {
+            const int i = tid + NT * it;
+            if (NT * it + NT <= NP || i < NP) {
+                const int r = i / 14, j = i - 14 * r;
+                if (j < 13) *(u32x4 *)(stg + r * 224 + 16 * j) = q[it];
+                else *(uint16_t *)(stg + r * 224 + 208) = (uint16_t)(q[it].w >> 16);   // bytes 208..209: d
+            }
+        }
+    }
+    // staging -> planes: item (row, 16-value group G); v = sc * (q - 32) = 128 * hi + lo
+    template <int J>
+    __device__ __forceinline__ void unpack(uint8_t *sm, int64_t r0, int64_t rows) const {
+        const int tid = threadIdx.x;
+        const uint8_t *stg = sm + Smem<kQ6_K, J>::STG_OFF;
+        int8_t *sLo = (int8_t *)(sm + Smem<kQ6_K, J>::W_OFF);
+        int8_t *sHi = sLo + kTI * kLd;
+#pragma unroll 2
+        for (int it = 0; it < 2048 / NT; ++it) {
+            const int i = tid + NT * it;               // (row, 16-value group G): 128 x 16
+            const int r = i >> 4, G = i & 15;
+            const uint8_t *blk = stg + r * 224;
+            const int hh = G >> 3, gq = (G & 7) >> 1, l0 = 16 * (G & 1);
+            const u32x4 ql = *(const u32x4 *)(blk + 64 * hh + 32 * (gq & 1) + l0);
+            const u32x4 qh = *(const u32x4 *)(blk + 128 + 32 * hh + l0);
+            const int sc = (int)(int8_t)blk[192 + G];
+            const int nsh = gq < 2 ? 0 : 4, tsh = 2 * gq;
+            const uint32_t qlw[4] = {ql.x, ql.y, ql.z, ql.w}, qhw[4] = {qh.x, qh.y, qh.z, qh.w};
+            uint32_t lo_w[4], hi_w[4];
+#pragma unroll
+            for (int dd = 0; dd < 4; ++dd) {
+                const uint32_t code6 = ((qlw[dd] >> nsh) & 0x0F0F0F0Fu) | (((qhw[dd] >> tsh) & 0x03030303u) << 4);
+                uint32_t lo = 0, hi = 0;
+#pragma unroll
+                for (int bi = 0; bi < 4; ++bi) {
+                    const int v = sc * ((int)((code6 >> (8 * bi)) & 0xFF) - 32);
+                    lo |= (uint32_t)(v & 127) << (8 * bi);
+                    hi |= (uint32_t)((v >> 7) & 0xFF) << (8 * bi);
+                }
+                lo_w[dd] = lo;
+                hi_w[dd] = hi;
+            }
+            *(u32x4 *)(sLo + r * kLd + 16 * G) = u32x4{lo_w[0], lo_w[1], lo_w[2], lo_w[3]};
+            *(u32x4 *)(sHi + r * kLd + 16 * G) = u32x4{hi_w[0], hi_w[1], hi_w[2], hi_w[3]};
+        }
+        if (tid < kTI) {
+            float *sWs = (float *)(sm + Smem<kQ6_K, J>::WS_OFF);
+            sWs[tid] = r0 + tid < rows ? h2f(*(const uint16_t *)(stg + tid * 224 + 208)) : 0.f;
+        }
+    }
+};
+
+template <int NT> struct WFetch<kQ6_K, NT> : std::conditional<(NT >= 512), WFetchQ6Staged<NT>, WFetchQ6Direct<NT>>::type {};
 
 // ---------------------------------------------------------------------------------------------
 // One 256-value step of MFMAs + fixups for this wave's 32 rows x JW columns.  Wave wid: row wave
@@ -379,6 +463,10 @@ __device__ __forceinline__ void run_tile(uint8_t *sm, f32x16 (&acc)[Cfg<J>::NCB]
         wf.template store<J>(sm, wbase, row_bytes, r0, rows, kb, nb32);
         af.template store<T>(sm);
         __syncthreads();
+        if constexpr (Smem<T, J>::STG_BYTES > 0) {   // Q6_K staged: raw bytes -> planes
+            wf.template unpack<J>(sm, r0, rows);
+            __syncthreads();
+        }
         if (kb + 1 < kb1) {
             wf.fetch(wbase, row_bytes, r0, rows, kb + 1, nb32);
             af.fetch(xq, nb32, kb + 1, acol);
