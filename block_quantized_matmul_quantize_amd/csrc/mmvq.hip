@@ -485,10 +485,9 @@ static int fused_kernel(int type, const void *w, int64_t k, const float *x, int6
     }
     // The LDS-staged kernel quantizes a step's blocks with 4 lanes per block; every workgroup
     // quantizes all of x, so the cost grows with n while a separate quantize launch costs a
-    // fixed ~3 us.  Measured at 4096 x 4096: fused wins up to n = 3 for Q4_K (0.9 us at n = 3,
-    // 0.2 us lost at n = 5) and up to n = 5 for Q6_K and Q8_0 (0.3-0.5 us at n = 5, 0.3-0.5 us
-    // lost at n = 8).
-    const int lim = g_fuse_cols > 0 ? g_fuse_cols : (type == kQ4_K ? 4 : 5);
+    // fixed ~2-3 us.  Measured at 4096 x 4096 (graph-replayed calls), fused is faster for every
+    // n <= 8 and type: 1.9-2.4 us at n = 1, 0.3-0.7 us at n = 8.
+    const int lim = g_fuse_cols > 0 ? g_fuse_cols : 8;
     if ((kc == 0 || kc == 2) && n <= lim && mmvq_stream_supported(type, w, k, x, nullptr)) return 2;
     return 0;
 }

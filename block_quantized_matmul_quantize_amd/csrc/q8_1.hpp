@@ -46,10 +46,15 @@ struct Q81Lane4 {
 
 __device__ __forceinline__ Q81Lane4 quantize_q8_1_lane4(float4 a, float4 b) {
     const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    float amax = fmaxf(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))),
-                       fmaxf(fmaxf(fabsf(v[4]), fabsf(v[5])), fmaxf(fabsf(v[6]), fabsf(v[7]))));
-    amax = fmaxf(amax, dpp_f<kDppXor1>(amax));
-    amax = fmaxf(amax, dpp_f<kDppXor2>(amax));
+    // max |v| over the lane (three v_max3 with |.| operand modifiers), then over the quad with the
+    // DPP exchange as an operand modifier (finite inputs: no NaN canonicalisation is needed)
+    float m0, m1, amax;
+    asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(m0) : "v"(v[0]), "v"(v[1]), "v"(v[2]));
+    asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(m1) : "v"(v[3]), "v"(v[4]), "v"(v[5]));
+    asm("v_max_f32 %0, %1, %2" : "=v"(amax) : "v"(m0), "v"(m1));
+    asm("v_max3_f32 %0, |%1|, |%2|, %3" : "=v"(amax) : "v"(v[6]), "v"(v[7]), "v"(amax));
+    asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 quad_perm:[1,0,3,2] row_mask:0xf bank_mask:0xf" : "=v"(m0) : "v"(amax));
+    asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 quad_perm:[2,3,0,1] row_mask:0xf bank_mask:0xf" : "=v"(amax) : "v"(m0));
     // d32 = amax / 127 by one multiply and an fma correction: with c = RN(1/127), the corrected
     // quotient equals the IEEE quotient for every amax whose quotient lies in [2^-101, 2^101]
     // (checked exhaustively over all such floats); outside that range the division below runs.
@@ -59,24 +64,28 @@ __device__ __forceinline__ Q81Lane4 quantize_q8_1_lane4(float4 a, float4 b) {
     uint32_t c0 = 0u, c1 = 0u;
     if (amax != 0.0f) {
         bool slow = !(d32 >= 0x1p-100f && d32 <= 0x1p100f);
-        int q[8];
         if (!slow) {
             const float r = __builtin_amdgcn_rcpf(d32);
+            int q[8];
+            float dev = 0.0f;   // largest distance of a quotient from its nearest integer
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const float t = v[i] * r;
                 const float rt = rintf(t);
-                slow |= fabsf(t - rt) > 0.5f - 0x1p-13f;
+                dev = fmaxf(dev, fabsf(t - rt));
                 q[i] = (int)rt;
             }
+            slow = dev > 0.5f - 0x1p-13f;
+            c0 = pack4(q[0], q[1], q[2], q[3]);
+            c1 = pack4(q[4], q[5], q[6], q[7]);
         }
         if (slow) {
             d32 = amax / 127.0f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) q[i] = q81_round_div(v[i], d32);
+            c0 = pack4(q81_round_div(v[0], d32), q81_round_div(v[1], d32), q81_round_div(v[2], d32),
+                       q81_round_div(v[3], d32));
+            c1 = pack4(q81_round_div(v[4], d32), q81_round_div(v[5], d32), q81_round_div(v[6], d32),
+                       q81_round_div(v[7], d32));
         }
-        c0 = pack4(q[0], q[1], q[2], q[3]);
-        c1 = pack4(q[4], q[5], q[6], q[7]);
     } else {
         d32 = 0.0f;
     }

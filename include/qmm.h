@@ -155,7 +155,7 @@ qmm_status qmm_matvec_kernel(int type, const void *w, int64_t k, const void *x, 
  *                     register-streamed kernel.
  *   QMM_OVR_FUSE_COLS: qmm_matmul only: most columns (1..8) for which the LDS-staged kernel
  *                     quantizes the fp32 activations itself instead of a separate quantize
- *                     launch (automatic: 4 for Q4_K, 5 for Q6_K and Q8_0).
+ *                     launch (automatic: 8).
  * Returns QMM_ERR_ARG for an unknown key or value.
  * ------------------------------------------------------------------------------------------- */
 enum { QMM_OVR_PATH = 1, QMM_OVR_STREAMK = 2, QMM_OVR_TILE_J = 3, QMM_OVR_MV_STEPS = 4, QMM_OVR_MV_KERNEL = 5,

@@ -150,16 +150,13 @@ def test_workspace_sizes_monotone():
 
 MV_AUTO = [
     # (type, n, expected (kernel, fused)) for aligned weights and fp32 activations, K = 4096:
-    # dot4 for Q4_K and Q8_0 at n = 1, else the LDS-staged kernel; it quantizes the fp32 input
-    # itself up to 4 columns for Q4_K and 5 for Q6_K / Q8_0.
+    # dot4 for Q4_K and Q8_0 at n = 1, else the LDS-staged kernel; both quantize the fp32 input
+    # themselves at every n <= 8.
     (qmm.Q4_K, 1, (3, True)),
-    *[(qmm.Q4_K, n, (2, True)) for n in (2, 3, 4)],
-    *[(qmm.Q4_K, n, (2, False)) for n in (5, 6, 7, 8)],
-    *[(qmm.Q6_K, n, (2, True)) for n in range(1, 6)],
-    *[(qmm.Q6_K, n, (2, False)) for n in (6, 7, 8)],
+    *[(qmm.Q4_K, n, (2, True)) for n in range(2, 9)],
+    *[(qmm.Q6_K, n, (2, True)) for n in range(1, 9)],
     (qmm.Q8_0, 1, (3, True)),
-    *[(qmm.Q8_0, n, (2, True)) for n in range(2, 6)],
-    *[(qmm.Q8_0, n, (2, False)) for n in (6, 7, 8)],
+    *[(qmm.Q8_0, n, (2, True)) for n in range(2, 9)],
     *[(t, 9, (0, False)) for t in (qmm.Q4_K, qmm.Q6_K, qmm.Q8_0)],
 ]
 
