@@ -63,6 +63,11 @@ template <int T, int J> struct Smem {
     static constexpr int BYTES = STG_OFF + STG_BYTES;
 };
 
+// Two LDS step buffers where they fit beside the occupancy the tile runs at: Q4_K 8-wave tiles
+// (one workgroup per CU either way, 2 x 68 KB).
+template <int T, int J> constexpr bool kDoubleBuffer = T == kQ4_K && J == 128;
+template <int T, int J> constexpr int kSmemBytes = (kDoubleBuffer<T, J> ? 2 : 1) * Smem<T, J>::BYTES;
+
 // ---------------------------------------------------------------------------------------------
 // Activation tile: J columns of the step's 8 q8_1 blocks.  Thread tid owns (column, block) pairs
 // i = tid + NT*it: column i/8, block i%8 (8 consecutive threads read one column's 288 bytes).
@@ -458,6 +463,33 @@ __device__ __forceinline__ void run_tile(uint8_t *sm, f32x16 (&acc)[Cfg<J>::NCB]
     ActFetch<J> af;
     wf.fetch(wbase, row_bytes, r0, rows, kb0, nb32);
     af.fetch(xq, nb32, kb0, acol);
+    if constexpr (kDoubleBuffer<T, J>) {
+        // Two LDS buffers: step kb computes from one while step kb+1 is parked in the other, so a
+        // step needs one barrier (it publishes the parked step and retires the buffer computed
+        // before), and the fetch of step kb+2 flies during step kb.
+        uint8_t *buf0 = sm, *buf1 = sm + Smem<T, J>::BYTES;
+        __syncthreads();   // the previous tile's reads of both buffers are done
+        wf.template store<J>(buf0, wbase, row_bytes, r0, rows, kb0, nb32);
+        af.template store<T>(buf0);
+        if (kb0 + 1 < kb1) {
+            wf.fetch(wbase, row_bytes, r0, rows, kb0 + 1, nb32);
+            af.fetch(xq, nb32, kb0 + 1, acol);
+        }
+        for (int64_t kb = kb0; kb < kb1; ++kb) {
+            uint8_t *cur = ((kb - kb0) & 1) ? buf1 : buf0, *nxt = ((kb - kb0) & 1) ? buf0 : buf1;
+            __syncthreads();
+            if (kb + 1 < kb1) {
+                wf.template store<J>(nxt, wbase, row_bytes, r0, rows, kb + 1, nb32);
+                af.template store<T>(nxt);
+                if (kb + 2 < kb1) {
+                    wf.fetch(wbase, row_bytes, r0, rows, kb + 2, nb32);
+                    af.fetch(xq, nb32, kb + 2, acol);
+                }
+            }
+            tile_step<T, J, DBG>(cur, acc, kb, nb32, dbg, rows, n, r0, c0);
+        }
+        return;
+    }
     for (int64_t kb = kb0; kb < kb1; ++kb) {
         __syncthreads();   // the previous step's LDS reads are done
         wf.template store<J>(sm, wbase, row_bytes, r0, rows, kb, nb32);
@@ -645,7 +677,7 @@ template <int T, int J, bool DBG>
 static hipError_t launch_mmq_t(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y,
                                int32_t *dbg, const MmqLaunch &p, hipStream_t s) {
     MmqArgs a{p.ntiles, p.n_ct, p.k_iters, p.units, p.partials, p.stream_k ? 1 : 0};
-    constexpr int smem = Smem<T, J>::BYTES;
+    constexpr int smem = kSmemBytes<T, J>;
     auto kern = mmq_kernel<T, J, DBG>;
     static bool attr_set = false;
     if (!attr_set) {
@@ -685,7 +717,7 @@ hipError_t launch_mmq(int type, const uint8_t *w, int64_t rows, int64_t k, const
 template <int T, int J>
 static hipError_t launch_mmq_id_t(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, float *y,
                                   const ColMap &cm, int32_t n_exp, int64_t max_ct, hipStream_t s) {
-    constexpr int smem = Smem<T, J>::BYTES;
+    constexpr int smem = kSmemBytes<T, J>;
     auto kern = mmq_id_kernel<T, J>;
     static bool attr_set = false;
     if (!attr_set) {
