@@ -209,17 +209,23 @@ qmm_status qmm_plan_dense(int type, int64_t rows, int64_t k, int64_t n, int32_t 
 namespace {
 
 struct DenseWs {
-    size_t xq_off, part_off, total;
+    size_t xq_off, tiled_off, part_off, total;
 };
 
+// Workspace of a dense call: canonical q8_1 blocks for fp32 input on the matrix-vector path (used
+// only where the kernel does not quantize itself), the tiled-kernel activation layout and the
+// stream-K partial slots on the tiled path.
 DenseWs dense_layout(int type, int64_t rows, int64_t k, int64_t n, bool with_xq) {
     DenseWs L{};
     const int64_t nb = k / 32;
+    const bool tiled = n > 8 || k > kMvMaxK || g_ovr_path.load() == 2;   // as qmm_plan_dense decides
     size_t off = 0;
     L.xq_off = off;
-    if (with_xq) off = align_up(off + (size_t)(n * nb * 36), 256);
+    if (with_xq && !tiled) off = align_up(off + (size_t)(n * nb * 36), 256);
+    L.tiled_off = off;
+    if (tiled) off = align_up(off + qmm::q8_1_tiled_bytes(n, k), 256);
     L.part_off = off;
-    if (n > 8 || g_ovr_path.load() == 2) {
+    if (tiled) {
         // stream-K partial slots: at most (compute units x 2 resident) units x 2 slots x 128 x 128
         const int64_t nsm = device_cus();
         const int64_t ntiles_max = ((rows + kTI - 1) / kTI) * ((n + 31) / 32);
@@ -230,8 +236,9 @@ DenseWs dense_layout(int type, int64_t rows, int64_t k, int64_t n, bool with_xq)
     return L;
 }
 
+// xq: canonical q8_1 blocks, or (x_tiled) activations already in the tiled layout.
 qmm_status run_dense(int type, const void *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y,
-                     uint8_t *ws, const DenseWs &L, int32_t *dbg, int dbg_path, hipStream_t s) {
+                     uint8_t *ws, const DenseWs &L, int32_t *dbg, int dbg_path, hipStream_t s, bool x_tiled = false) {
     hipError_t e;
     qmm_plan p{};
     qmm_status st;
@@ -248,6 +255,7 @@ qmm_status run_dense(int type, const void *w, int64_t rows, int64_t k, const uin
     }
     if (st) return st;
     if (p.regime == 1) {
+        if (x_tiled) return fail(QMM_ERR_ARG, "internal: tiled activations on the matrix-vector path");
         e = qmm::launch_mmvq(type, (const uint8_t *)w, rows, k, xq, n, y, dbg, nullptr, 0, s);
         if (e != hipSuccess) return hip_fail(e, "matrix-vector kernel launch");
         return QMM_OK;
@@ -262,7 +270,14 @@ qmm_status run_dense(int type, const void *w, int64_t rows, int64_t k, const uin
     ml.partials = (float *)(ws + L.part_off);
     if (ml.stream_k && (size_t)(L.part_off + (size_t)ml.units * 2 * kTI * p.tile_j * 4) > L.total)
         return fail(QMM_ERR_WORKSPACE, "internal: stream-K partials exceed the workspace");
-    e = qmm::launch_mmq(type, (const uint8_t *)w, rows, k, xq, n, y, dbg, ml, s);
+    // the production tiled kernel reads the tiled layout, the debug export canonical blocks
+    const uint8_t *xa = xq;
+    if (!dbg && !x_tiled) {
+        e = qmm::launch_relayout_q8_1_tiled(xq, n, k, ws + L.tiled_off, s);
+        if (e != hipSuccess) return hip_fail(e, "relayout launch");
+        xa = ws + L.tiled_off;
+    }
+    e = qmm::launch_mmq(type, (const uint8_t *)w, rows, k, xa, n, y, dbg, ml, s);
     if (e != hipSuccess) return hip_fail(e, "tiled kernel launch");
     return QMM_OK;
 }
@@ -321,6 +336,12 @@ qmm_status qmm_matmul(int type, const void *w, int64_t rows, int64_t k, const fl
         hipError_t e = qmm::launch_mmvq_fused(type, (const uint8_t *)w, rows, k, x, n, y, s);
         if (e != hipSuccess) return hip_fail(e, "fused matrix-vector kernel launch");
         return QMM_OK;
+    }
+    if (p.regime == 2) {
+        // tiled path: quantize straight into the tiled kernel's layout
+        hipError_t e = qmm::launch_quantize_q8_1_tiled(x, n, k, wsb + L.tiled_off, nullptr, s);
+        if (e != hipSuccess) return hip_fail(e, "quantize launch");
+        return run_dense(type, w, rows, k, wsb + L.tiled_off, n, y, wsb, L, nullptr, 0, s, true);
     }
     hipError_t e = qmm::launch_quantize_q8_1(x, n, k, wsb + L.xq_off, s);
     if (e != hipSuccess) return hip_fail(e, "quantize launch");
@@ -382,7 +403,7 @@ qmm_status qmm_debug_subdots(int type, const void *w, int64_t rows, int64_t k, c
 namespace {
 
 struct IdWs {
-    size_t invalid_off, xq_off, sorted_off, bounds_off, tstart_off, small_off, total;
+    size_t invalid_off, xq_off, tiled_off, sorted_off, bounds_off, tstart_off, small_off, total;
 };
 
 IdWs id_layout(int64_t n_exp, int64_t k, int64_t n_tok, int64_t top_k, int64_t x_per_tok) {
@@ -392,7 +413,8 @@ IdWs id_layout(int64_t n_exp, int64_t k, int64_t n_tok, int64_t top_k, int64_t x
     const int64_t pairs = n_tok * top_k;
     size_t off = 0;
     L.invalid_off = off; off = align_up(off + 4, 256);   // first, so the count is found from ws alone
-    L.xq_off = off; off = align_up(off + (size_t)(nx * nb * 36), 256);
+    L.xq_off = off; off = align_up(off + (size_t)(nx * nb * 36), 256);           // small experts
+    L.tiled_off = off; off = align_up(off + qmm::q8_1_tiled_bytes(nx, k), 256);   // tiled experts
     L.sorted_off = off; off = align_up(off + (size_t)(std::max<int64_t>(pairs, 1) * 4), 256);
     L.bounds_off = off; off = align_up(off + (size_t)((n_exp + 1) * 4), 256);
     L.tstart_off = off; off = align_up(off + (size_t)((n_exp + 1) * 4), 256);
@@ -445,8 +467,8 @@ qmm_status qmm_matmul_id(int type, const void *w, int64_t n_exp, int64_t rows, i
 
     const int64_t nx = n_tok * x_per_tok;
     const int64_t pairs = n_tok * top_k;
-    uint8_t *xq = wsb + L.xq_off;
-    hipError_t e = qmm::launch_quantize_q8_1(x, nx, k, xq, s);
+    uint8_t *xq = wsb + L.xq_off, *xt = wsb + L.tiled_off;
+    hipError_t e = qmm::launch_quantize_q8_1_tiled(x, nx, k, xt, xq, s);   // both layouts, one launch
     if (e != hipSuccess) return hip_fail(e, "quantize launch");
     const int tile_j = id_tile_j(pairs, n_exp);
     qmm::ColMap cm{};
@@ -458,6 +480,7 @@ qmm_status qmm_matmul_id(int type, const void *w, int64_t n_exp, int64_t rows, i
     cm.x_per_tok = (int32_t)x_per_tok;
     cm.n_exp = (int32_t)n_exp;
     cm.w_expert_stride = rows * (k / block_values(type)) * block_bytes(type);
+    cm.act_rows = nx;
     const int small_max = k <= kMvMaxK ? kSmallMax : 0;
     e = qmm::launch_moe_group(ids, pairs, (int32_t)n_exp, tile_j, small_max, (int32_t *)cm.sorted,
                               (int32_t *)cm.bounds, (int32_t *)cm.tile_start, (int32_t *)cm.small, invalid, s);
@@ -470,7 +493,7 @@ qmm_status qmm_matmul_id(int type, const void *w, int64_t n_exp, int64_t rows, i
     // the rest: tiled kernel over the device-built column-tile list
     const int64_t mmq_experts = std::min<int64_t>(n_exp, pairs / (small_max + 1));
     const int64_t max_ct = (pairs + tile_j - 1) / tile_j + mmq_experts;
-    e = qmm::launch_mmq_id(type, (const uint8_t *)w, rows, k, xq, y, cm, tile_j, max_ct, s);
+    e = qmm::launch_mmq_id(type, (const uint8_t *)w, rows, k, xt, y, cm, tile_j, max_ct, s);
     if (e != hipSuccess) return hip_fail(e, "expert tiled launch");
     return QMM_OK;
 }

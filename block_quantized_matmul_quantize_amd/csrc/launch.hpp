@@ -6,6 +6,16 @@
 namespace qmm {
 
 hipError_t launch_quantize_q8_1(const float *x, int64_t n_rows, int64_t k, uint8_t *y, hipStream_t s);
+
+// Tiled-kernel activation layout: for each 256-value step kb and activation row r, the 8 blocks'
+// codes as 256 contiguous bytes at (kb * n_rows + r) * 256, then (after all steps' codes) the 8
+// blocks' fp16 (d, s) pairs at (kb * n_rows + r) * 32 -- every load of the tiled kernel aligned.
+inline size_t q8_1_tiled_bytes(int64_t n_rows, int64_t k) { return (size_t)((k / 32 + 7) / 8) * n_rows * 288; }
+// fp32 rows -> tiled layout (and, if canon is not null, the canonical q8_1 blocks as well)
+hipError_t launch_quantize_q8_1_tiled(const float *x, int64_t n_rows, int64_t k, uint8_t *tiled, uint8_t *canon,
+                                      hipStream_t s);
+// canonical q8_1 blocks -> tiled layout
+hipError_t launch_relayout_q8_1_tiled(const uint8_t *xq, int64_t n_rows, int64_t k, uint8_t *tiled, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t s);
 
 // Column map for the matrix-vector and tiled kernels.  Dense: column j reads activation row j
@@ -21,6 +31,7 @@ struct ColMap {
     int32_t x_per_tok;
     int32_t n_exp;
     int64_t w_expert_stride;   // bytes between expert matrices
+    int64_t act_rows;          // activation rows (n_tok * x_per_tok): row count of the tiled layout
 };
 
 // Matrix-vector kernel: n <= 8 columns (dense) or the small experts (expert mode, grid.y = n_exp).

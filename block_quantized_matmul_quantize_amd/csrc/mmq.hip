@@ -70,13 +70,16 @@ template <int T, int J> constexpr int kSmemBytes = (kDoubleBuffer<T, J> ? 2 : 1)
 
 // ---------------------------------------------------------------------------------------------
 // Activation tile: J columns of the step's 8 q8_1 blocks.  Thread tid owns (column, block) pairs
-// i = tid + NT*it: column i/8, block i%8 (8 consecutive threads read one column's 288 bytes).
+// i = tid + NT*it: column i/8, block i%8.  TILED: the tiled layout (launch.hpp), where the 8
+// consecutive threads of a column read its 256 code bytes and 8 (d, s) pairs with aligned loads;
+// otherwise canonical 36-byte blocks (the debug export reads those).
 // ---------------------------------------------------------------------------------------------
-template <int J> struct ActFetch {
+template <int J, bool TILED> struct ActFetch {
     static constexpr int NT = Cfg<J>::NT, N = J * 8 / NT;
-    uint32_t ds[N];
+    uint32_t ds[N];   // fp16 d | fp16 s << 16
     u32x4 c0[N], c1[N];
-    __device__ __forceinline__ void fetch(const uint8_t *xq, int64_t nb32, int64_t kb, const int64_t (&acol)[N]) {
+    __device__ __forceinline__ void fetch(const uint8_t *xq, int64_t nb32, int64_t kb, const int64_t (&acol)[N],
+                                          int64_t act_rows) {
         const int tid = threadIdx.x;
 #pragma unroll
         for (int it = 0; it < N; ++it) {
@@ -86,10 +89,18 @@ template <int J> struct ActFetch {
             c0[it] = u32x4{0u, 0u, 0u, 0u};
             c1[it] = c0[it];
             if (acol[it] >= 0 && b < nb32) {
-                const uint8_t *src = xq + (acol[it] * nb32 + b) * kQ8_1Bytes;
-                ds[it] = *(const uint32_t *)src;
-                c0[it] = ld16(src + 4);
-                c1[it] = ld16(src + 20);
+                if constexpr (TILED) {
+                    const int64_t slot = kb * act_rows + acol[it];
+                    const uint8_t *src = xq + slot * 256 + 32 * blk;
+                    c0[it] = *(const u32x4 *)src;
+                    c1[it] = *(const u32x4 *)(src + 16);
+                    ds[it] = ((const uint32_t *)(xq + ((nb32 + 7) / 8) * act_rows * 256))[slot * 8 + blk];
+                } else {
+                    const uint8_t *src = xq + (acol[it] * nb32 + b) * kQ8_1Bytes;
+                    ds[it] = *(const uint32_t *)src;
+                    c0[it] = ld16(src + 4);
+                    c1[it] = ld16(src + 20);
+                }
             }
         }
     }
@@ -457,12 +468,12 @@ __device__ __forceinline__ void tile_step(const uint8_t *sm, f32x16 (&acc)[Cfg<J
 template <int T, int J, bool DBG>
 __device__ __forceinline__ void run_tile(uint8_t *sm, f32x16 (&acc)[Cfg<J>::NCB], const uint8_t *wbase,
                                          int64_t row_bytes, int64_t r0, int64_t rows, int64_t kb0, int64_t kb1,
-                                         int64_t nb32, const uint8_t *xq, const int64_t (&acol)[ActFetch<J>::N],
-                                         int32_t *dbg, int64_t n, int64_t c0) {
+                                         int64_t nb32, const uint8_t *xq, const int64_t (&acol)[J * 8 / Cfg<J>::NT],
+                                         int32_t *dbg, int64_t n, int64_t c0, int64_t act_rows) {
     WFetch<T, Cfg<J>::NT> wf;
-    ActFetch<J> af;
+    ActFetch<J, !DBG> af;
     wf.fetch(wbase, row_bytes, r0, rows, kb0, nb32);
-    af.fetch(xq, nb32, kb0, acol);
+    af.fetch(xq, nb32, kb0, acol, act_rows);
     if constexpr (kDoubleBuffer<T, J>) {
         // Two LDS buffers: step kb computes from one while step kb+1 is parked in the other, so a
         // step needs one barrier (it publishes the parked step and retires the buffer computed
@@ -473,7 +484,7 @@ __device__ __forceinline__ void run_tile(uint8_t *sm, f32x16 (&acc)[Cfg<J>::NCB]
         af.template store<T>(buf0);
         if (kb0 + 1 < kb1) {
             wf.fetch(wbase, row_bytes, r0, rows, kb0 + 1, nb32);
-            af.fetch(xq, nb32, kb0 + 1, acol);
+            af.fetch(xq, nb32, kb0 + 1, acol, act_rows);
         }
         for (int64_t kb = kb0; kb < kb1; ++kb) {
             uint8_t *cur = ((kb - kb0) & 1) ? buf1 : buf0, *nxt = ((kb - kb0) & 1) ? buf0 : buf1;
@@ -483,7 +494,7 @@ __device__ __forceinline__ void run_tile(uint8_t *sm, f32x16 (&acc)[Cfg<J>::NCB]
                 af.template store<T>(nxt);
                 if (kb + 2 < kb1) {
                     wf.fetch(wbase, row_bytes, r0, rows, kb + 2, nb32);
-                    af.fetch(xq, nb32, kb + 2, acol);
+                    af.fetch(xq, nb32, kb + 2, acol, act_rows);
                 }
             }
             tile_step<T, J, DBG>(cur, acc, kb, nb32, dbg, rows, n, r0, c0);
@@ -501,7 +512,7 @@ __device__ __forceinline__ void run_tile(uint8_t *sm, f32x16 (&acc)[Cfg<J>::NCB]
         }
         if (kb + 1 < kb1) {
             wf.fetch(wbase, row_bytes, r0, rows, kb + 1, nb32);
-            af.fetch(xq, nb32, kb + 1, acol);
+            af.fetch(xq, nb32, kb + 1, acol, act_rows);
         }
         tile_step<T, J, DBG>(sm, acc, kb, nb32, dbg, rows, n, r0, c0);
     }
@@ -535,7 +546,7 @@ __global__ __launch_bounds__(Cfg<J>::NT, 2) void mmq_kernel(const uint8_t *__res
                                                          float *__restrict__ y, int32_t *__restrict__ dbg,
                                                          MmqArgs args) {
     extern __shared__ __align__(16) uint8_t sm[];
-    constexpr int NA = ActFetch<J>::N, NT = Cfg<J>::NT;
+    constexpr int NA = J * 8 / Cfg<J>::NT, NT = Cfg<J>::NT;
     const int64_t nb32 = k / 32;
     const int64_t row_bytes = (k / Fmt<T>::QK) * Fmt<T>::BYTES;
     const int64_t u = xcd_remap(blockIdx.x, args.units);
@@ -562,7 +573,7 @@ __global__ __launch_bounds__(Cfg<J>::NT, 2) void mmq_kernel(const uint8_t *__res
 #pragma unroll
         for (int cb = 0; cb < Cfg<J>::NCB; ++cb) acc[cb] = f32x16{};
 
-        run_tile<T, J, DBG>(sm, acc, w, row_bytes, r0, rows, kb0, kb1, nb32, xq, acol, dbg, n, c0);
+        run_tile<T, J, DBG>(sm, acc, w, row_bytes, r0, rows, kb0, kb1, nb32, xq, acol, dbg, n, c0, n);
 
         if (!DBG) {
             const bool whole = kb0 == 0 && kb1 == args.k_iters;
@@ -619,7 +630,7 @@ __global__ __launch_bounds__(Cfg<J>::NT, 2) void mmq_id_kernel(const uint8_t *__
                                                             const uint8_t *__restrict__ xq, float *__restrict__ y,
                                                             ColMap cm, int32_t n_exp) {
     extern __shared__ __align__(16) uint8_t sm[];
-    constexpr int NA = ActFetch<J>::N, NT = Cfg<J>::NT;
+    constexpr int NA = J * 8 / Cfg<J>::NT, NT = Cfg<J>::NT;
     const int64_t ct = blockIdx.y;
     if (ct >= cm.tile_start[n_exp]) return;
     // expert owning column tile ct: largest e with tile_start[e] <= ct
@@ -655,7 +666,8 @@ __global__ __launch_bounds__(Cfg<J>::NT, 2) void mmq_id_kernel(const uint8_t *__
     for (int cb = 0; cb < Cfg<J>::NCB; ++cb) acc[cb] = f32x16{};
 
     const int64_t k_iters = (k + kSuper - 1) / kSuper;
-    run_tile<T, J, false>(sm, acc, wbase, row_bytes, r0, rows, 0, k_iters, nb32, xq, acol, nullptr, cnt, c0);
+    run_tile<T, J, false>(sm, acc, wbase, row_bytes, r0, rows, 0, k_iters, nb32, xq, acol, nullptr, cnt, c0,
+                          cm.act_rows);
     const int rw = wid & 3, cw = wid >> 2;
 #pragma unroll
     for (int cb = 0; cb < Cfg<J>::NCB; ++cb) {
