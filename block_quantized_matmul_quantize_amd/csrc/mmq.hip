@@ -211,6 +211,22 @@ template <int NT> struct WFetch<kQ8_0, NT> {
     }
 };
 
+// Q6_K scale folding for four codes c (the bytes of c6, each in [0, 63]) of one 16-value group:
+// v = sc * (c - 32) in [-4064, 4096], split as v = 128 * hi + lo with lo in [0, 127] and hi in
+// [-32, 32], returned as the byte vectors lo and hi.  Two codes per 32-bit lane pair: packed
+// 16-bit integer multiply-add and arithmetic shift, then v_perm gathers the bytes.
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void q6_split4(uint32_t c6, s16x2 sc2, s16x2 off2, uint32_t &lo, uint32_t &hi) {
+    const uint32_t ce = c6 & 0x00FF00FFu;                          // codes 0, 2
+    const uint32_t co = __builtin_amdgcn_perm(0u, c6, 0x0c030c01u);  // codes 1, 3
+    const s16x2 ve = __builtin_bit_cast(s16x2, ce) * sc2 + off2;   // sc * c - 32 * sc
+    const s16x2 vo = __builtin_bit_cast(s16x2, co) * sc2 + off2;
+    const uint32_t ue = __builtin_bit_cast(uint32_t, ve), uo = __builtin_bit_cast(uint32_t, vo);
+    lo = __builtin_amdgcn_perm(uo, ue, 0x06020400u) & 0x7F7F7F7Fu;
+    const uint32_t he = __builtin_bit_cast(uint32_t, ve >> (short)7), ho = __builtin_bit_cast(uint32_t, vo >> (short)7);
+    hi = __builtin_amdgcn_perm(ho, he, 0x06020400u);
+}
+
 // Q6_K with 4-wave tiles (J <= 64): unpacked straight from HBM into the two planes at park time
 // (no register prefetch: the registers are taken by the accumulators).
 template <int NT> struct WFetchQ6Direct {
@@ -234,20 +250,13 @@ template <int NT> struct WFetchQ6Direct {
                 const u32x4 ql = ld16(blk + 64 * hh + 32 * (gq & 1) + l0);
                 const u32x4 qh = ld16(blk + 128 + 32 * hh + l0);
                 const int sc = (int)(int8_t)blk[192 + G];
+                const s16x2 sc2 = {(short)sc, (short)sc}, off2 = {(short)(-32 * sc), (short)(-32 * sc)};
                 const int nsh = gq < 2 ? 0 : 4, tsh = 2 * gq;
                 const uint32_t qlw[4] = {ql.x, ql.y, ql.z, ql.w}, qhw[4] = {qh.x, qh.y, qh.z, qh.w};
 #pragma unroll
                 for (int dd = 0; dd < 4; ++dd) {
                     const uint32_t code6 = ((qlw[dd] >> nsh) & 0x0F0F0F0Fu) | (((qhw[dd] >> tsh) & 0x03030303u) << 4);
-                    uint32_t lo = 0, hi = 0;
-#pragma unroll
-                    for (int bi = 0; bi < 4; ++bi) {
-                        const int v = sc * ((int)((code6 >> (8 * bi)) & 0xFF) - 32);
-                        lo |= (uint32_t)(v & 127) << (8 * bi);
-                        hi |= (uint32_t)((v >> 7) & 0xFF) << (8 * bi);
-                    }
-                    lo_w[dd] = lo;
-                    hi_w[dd] = hi;
+                    q6_split4(code6, sc2, off2, lo_w[dd], hi_w[dd]);
                 }
             }
             *(u32x4 *)(sLo + r * kLd + 16 * G) = u32x4{lo_w[0], lo_w[1], lo_w[2], lo_w[3]};
@@ -311,21 +320,14 @@ template <int NT> struct WFetchQ6Staged {
             const u32x4 ql = *(const u32x4 *)(blk + 64 * hh + 32 * (gq & 1) + l0);
             const u32x4 qh = *(const u32x4 *)(blk + 128 + 32 * hh + l0);
             const int sc = (int)(int8_t)blk[192 + G];
+            const s16x2 sc2 = {(short)sc, (short)sc}, off2 = {(short)(-32 * sc), (short)(-32 * sc)};
             const int nsh = gq < 2 ? 0 : 4, tsh = 2 * gq;
             const uint32_t qlw[4] = {ql.x, ql.y, ql.z, ql.w}, qhw[4] = {qh.x, qh.y, qh.z, qh.w};
             uint32_t lo_w[4], hi_w[4];
 #pragma unroll
             for (int dd = 0; dd < 4; ++dd) {
                 const uint32_t code6 = ((qlw[dd] >> nsh) & 0x0F0F0F0Fu) | (((qhw[dd] >> tsh) & 0x03030303u) << 4);
-                uint32_t lo = 0, hi = 0;
-#pragma unroll
-                for (int bi = 0; bi < 4; ++bi) {
-                    const int v = sc * ((int)((code6 >> (8 * bi)) & 0xFF) - 32);
-                    lo |= (uint32_t)(v & 127) << (8 * bi);
-                    hi |= (uint32_t)((v >> 7) & 0xFF) << (8 * bi);
-                }
-                lo_w[dd] = lo;
-                hi_w[dd] = hi;
+                q6_split4(code6, sc2, off2, lo_w[dd], hi_w[dd]);
             }
             *(u32x4 *)(sLo + r * kLd + 16 * G) = u32x4{lo_w[0], lo_w[1], lo_w[2], lo_w[3]};
             *(u32x4 *)(sHi + r * kLd + 16 * G) = u32x4{hi_w[0], hi_w[1], hi_w[2], hi_w[3]};
