@@ -60,6 +60,7 @@ _sig("qmm_matmul_q8_1", _i32, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _sz, _
 _sig("qmm_matmul_id_workspace", _sz, _i32, _i64, _i64, _i64, _i64, _i64, _i64)
 _sig("qmm_matmul_id", _i32, _i32, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _sz, _vp)
 _sig("qmm_matmul_id_invalid_count", _i32, _vp, ctypes.POINTER(_i64), _vp)
+_sig("qmm_matmul_id_grouping_layout", _i32, _i64, _i64, _i64, _i64, _i64, ctypes.POINTER(_i64))
 _sig("qmm_debug_subdots", _i32, _i32, _vp, _i64, _i64, _vp, _i64, _i32, _vp, _vp)
 _sig("qmm_set_override", _i32, _i32, _i32)
 _sig("qmm_plan_dense", _i32, _i32, _i64, _i64, _i64, ctypes.c_int32, ctypes.POINTER(Plan))
@@ -250,6 +251,23 @@ def matmul_id_invalid_count(ws):
     v = _i64(0)
     _check(_L.qmm_matmul_id_invalid_count(ctypes.c_void_p(ws.data_ptr()), ctypes.byref(v), _stream()))
     return int(v.value)
+
+
+def matmul_id_grouping(ws, n_exp, k, n_tok, top_k, x_per_tok=1):
+    """Expert grouping the last matmul_id with workspace `ws` built (synchronizes the stream):
+    dict of int32 CPU tensors sorted, bounds, tile_start, small, plus tile_j and small_max."""
+    torch = _torch()
+    out = (_i64 * 6)()
+    _check(_L.qmm_matmul_id_grouping_layout(n_exp, k, n_tok, top_k, x_per_tok, out))
+    torch.cuda.current_stream().synchronize()
+    pairs = n_tok * top_k
+    raw = ws.view(torch.uint8)
+
+    def take(off, count):
+        return raw[off:off + 4 * count].view(torch.int32).cpu()
+
+    return {"sorted": take(out[0], pairs), "bounds": take(out[1], n_exp + 1), "tile_start": take(out[2], n_exp + 1),
+            "small": take(out[3], n_exp), "tile_j": int(out[4]), "small_max": int(out[5])}
 
 
 def debug_subdots(w, qtype, rows, k, xq, n, path):

@@ -498,6 +498,21 @@ qmm_status qmm_matmul_id(int type, const void *w, int64_t n_exp, int64_t rows, i
     return QMM_OK;
 }
 
+qmm_status qmm_matmul_id_grouping_layout(int64_t n_exp, int64_t k, int64_t n_tok, int64_t top_k, int64_t x_per_tok,
+                                         int64_t *out) {
+    if (!out) return fail(QMM_ERR_ARG, "null out");
+    if (n_exp <= 0 || n_exp > 32768 || top_k <= 0 || n_tok < 0 || k <= 0 || (x_per_tok != 1 && x_per_tok != top_k))
+        return fail(QMM_ERR_ARG, "bad expert-product shape");
+    const IdWs L = id_layout(n_exp, k, n_tok, top_k, x_per_tok);
+    out[0] = (int64_t)L.sorted_off;
+    out[1] = (int64_t)L.bounds_off;
+    out[2] = (int64_t)L.tstart_off;
+    out[3] = (int64_t)L.small_off;
+    out[4] = id_tile_j(n_tok * top_k, n_exp);
+    out[5] = k <= kMvMaxK ? kSmallMax : 0;
+    return QMM_OK;
+}
+
 qmm_status qmm_matmul_id_invalid_count(const void *ws, int64_t *out, void *stream) {
     if (!ws || !out) return fail(QMM_ERR_ARG, "null ws or out");
     hipError_t e = hipStreamSynchronize((hipStream_t)stream);

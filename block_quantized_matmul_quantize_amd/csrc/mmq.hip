@@ -611,16 +611,25 @@ __global__ __launch_bounds__(256) void streamk_fixup_kernel(float *__restrict__ 
     if (u0 == u1) return;                         // one unit covered the whole tile
     const int64_t rt = t / args.n_ct, ct = t - rt * args.n_ct;
     const int64_t r0 = rt * kTI, c0 = ct * J;
-    for (int i = threadIdx.x; i < kTI * J; i += blockDim.x) {
-        const int c = i / kTI, r = i - c * kTI;
-        if (r0 + r >= rows || c0 + c >= n) continue;
-        float v = 0.f;
-        for (int64_t u = u0; u <= u1; ++u) {
+    // partial-slot offsets of the covering units, computed once (kSlots at a time)
+    constexpr int kSlots = 256;
+    __shared__ int64_t slot_off[kSlots];
+    for (int64_t ub = u0; ub <= u1; ub += kSlots) {
+        const int64_t m = u1 - ub + 1 < kSlots ? u1 - ub + 1 : kSlots;
+        __syncthreads();
+        if (threadIdx.x < m) {
+            const int64_t u = ub + threadIdx.x;
             const int64_t first_tile = ((u * W) / args.units) / args.k_iters;
-            const int64_t slot = 2 * u + (first_tile == t ? 0 : 1);
-            v += args.partials[slot * (int64_t)kTI * J + (int64_t)c * kTI + r];
+            slot_off[threadIdx.x] = (2 * u + (first_tile == t ? 0 : 1)) * (int64_t)kTI * J;
         }
-        y[(c0 + c) * rows + r0 + r] = v;
+        __syncthreads();
+        for (int i = threadIdx.x; i < kTI * J; i += blockDim.x) {
+            const int c = i / kTI, r = i - c * kTI;
+            if (r0 + r >= rows || c0 + c >= n) continue;
+            float v = ub == u0 ? 0.f : y[(c0 + c) * rows + r0 + r];
+            for (int64_t j = 0; j < m; ++j) v += args.partials[slot_off[j] + (int64_t)c * kTI + r];
+            y[(c0 + c) * rows + r0 + r] = v;
+        }
     }
 }
 

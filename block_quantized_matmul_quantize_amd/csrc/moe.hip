@@ -3,9 +3,11 @@
 // sorting by expert makes each expert's columns contiguous).
 //
 // One workgroup runs a stable counting sort of the (token, slot) pairs by expert id:
-//   1. thread t counts its contiguous chunk of pairs per expert into an LDS table cnt[e][t];
-//   2. an exclusive scan of the table in (expert, thread) order gives each (e, t) its first
-//      output position, and expert e's segment start bounds[e];
+//   1. thread t counts its contiguous chunk of pairs per expert into an LDS table cnt[e][t]
+//      (ids read in batches of independent loads);
+//   2. per expert row e, the wave that owns it sums cnt[e][*] into bounds[e]; a scan over the
+//      experts turns these into the segment starts; the row is then scanned in thread order, so
+//      that (e, t) holds the first output position of thread t's pairs of expert e;
 //   3. each thread walks its chunk again and writes pair indices to their positions, so the
 //      order inside an expert is ascending pair index (token-major, then slot).
 // It also emits the per-expert dispatch: experts with 1..small_max columns go to the
@@ -18,6 +20,24 @@ namespace qmm {
 
 constexpr int kGroupThreads = 256;
 constexpr int kGroupTableInts = 32768;   // LDS table: n_exp * threads_used <= 32768
+constexpr int kGroupBatch = 16;          // ids in flight per thread
+
+__device__ __forceinline__ int32_t wave_sum(int32_t v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// inclusive prefix sum over the 64 lanes of a wave
+__device__ __forceinline__ int32_t wave_incl_scan(int32_t v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int32_t u = __shfl_up(v, o);
+        if (lane >= o) v += u;
+    }
+    return v;
+}
 
 __global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(const int32_t *__restrict__ ids, int64_t pairs,
                                                                   int32_t n_exp, int32_t nthr, int32_t tile_j,
@@ -29,63 +49,92 @@ __global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(const int32_t 
     __shared__ int32_t tab[kGroupTableInts];
     __shared__ int32_t part[kGroupThreads];
     __shared__ int32_t bad_sh[kGroupThreads];
-    __shared__ int32_t total_sh;
-    const int t = threadIdx.x;
+    const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+    constexpr int NW = kGroupThreads / 64;
     const bool active = t < nthr;
     const int64_t chunk = (pairs + nthr - 1) / nthr;
     const int64_t lo = active ? (int64_t)t * chunk : 0;
     const int64_t hi = active ? (lo + chunk < pairs ? lo + chunk : pairs) : 0;
 
-    if (active)
-        for (int e = 0; e < n_exp; ++e) tab[e * nthr + t] = 0;
+    for (int i = t; i < n_exp * nthr; i += kGroupThreads) tab[i] = 0;
+    __syncthreads();
     int bad = 0;
-    for (int64_t p = lo; p < hi; ++p) {
-        const int32_t e = ids[p];
-        if (e >= 0 && e < n_exp) tab[e * nthr + t] += 1;
-        else bad++;
+    for (int64_t p0 = lo; p0 < hi; p0 += kGroupBatch) {
+        int32_t ev[kGroupBatch];
+#pragma unroll
+        for (int j = 0; j < kGroupBatch; ++j) ev[j] = p0 + j < hi ? ids[p0 + j] : -1;
+#pragma unroll
+        for (int j = 0; j < kGroupBatch; ++j) {
+            if (p0 + j >= hi) break;
+            const int32_t e = ev[j];
+            if (e >= 0 && e < n_exp) tab[e * nthr + t] += 1;
+            else bad++;
+        }
     }
     bad_sh[t] = bad;
     __syncthreads();
 
-    // Exclusive scan over tab in linear (expert-major) order: thread t owns entries
-    // [t*n_exp, (t+1)*n_exp) of the nthr*n_exp table.
-    int32_t s = 0;
-    if (active)
-        for (int i = 0; i < n_exp; ++i) s += tab[t * n_exp + i];
-    part[t] = active ? s : 0;
-    __syncthreads();
-    if (t == 0) {
-        int32_t run = 0, nbad = 0;
-        for (int i = 0; i < nthr; ++i) {
-            const int32_t v = part[i];
-            part[i] = run;
-            run += v;
-        }
-        for (int i = 0; i < kGroupThreads; ++i) nbad += bad_sh[i];
-        bounds[n_exp] = run;
-        total_sh = run;
-        invalid[0] = nbad;
+    // per-expert totals into bounds[e] (expert rows e = wid, wid + NW, ...; lanes stride the row)
+    for (int e = wid; e < n_exp; e += NW) {
+        int32_t v = 0;
+        for (int i = lane; i < nthr; i += 64) v += tab[e * nthr + i];
+        v = wave_sum(v);
+        if (lane == 0) bounds[e] = v;
     }
     __syncthreads();
-    if (active) {
+    // exclusive scan of the totals over the experts: thread t takes experts [t*ce, t*ce + ce)
+    {
+        const int ce = (n_exp + kGroupThreads - 1) / kGroupThreads;
+        const int e0 = t * ce, e1 = e0 + ce < n_exp ? e0 + ce : n_exp;
+        int32_t sum = 0;
+        for (int e = e0; e < e1; ++e) sum += bounds[e];
+        part[t] = sum;
+        __syncthreads();
+        if (t == 0) {
+            int32_t run = 0, nbad = 0;
+            for (int i = 0; i < kGroupThreads; ++i) {
+                const int32_t v = part[i];
+                part[i] = run;
+                run += v;
+                nbad += bad_sh[i];
+            }
+            bounds[n_exp] = run;
+            invalid[0] = nbad;
+        }
+        __syncthreads();
         int32_t run = part[t];
-        for (int i = 0; i < n_exp; ++i) {
-            const int32_t v = tab[t * n_exp + i];
-            tab[t * n_exp + i] = run;
+        for (int e = e0; e < e1; ++e) {
+            const int32_t v = bounds[e];
+            bounds[e] = run;
             run += v;
         }
     }
     __syncthreads();
-    // Segment starts and the per-expert dispatch, read from the scanned table before the
-    // scatter advances it.
-    for (int e = t; e < n_exp; e += blockDim.x) bounds[e] = tab[e * nthr];
+    // each expert row scanned in thread order: lane l takes threads [l*q, l*q + q), q = nthr/64
+    // (nthr >= 64) or one thread per lane for l < nthr (nthr < 64)
+    for (int e = wid; e < n_exp; e += NW) {
+        const int q = nthr >= 64 ? nthr / 64 : 1;
+        const int t0 = lane * q;
+        int32_t loc[4];
+        int32_t sum = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            loc[j] = (j < q && t0 + j < nthr) ? tab[e * nthr + t0 + j] : 0;
+            sum += loc[j];
+        }
+        int32_t run = wave_incl_scan(sum) - sum + bounds[e];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (j < q && t0 + j < nthr) tab[e * nthr + t0 + j] = run;
+            run += loc[j];
+        }
+    }
+    __syncthreads();
+    // the per-expert dispatch, from the segment starts
     if (t == 0) {
-        const int32_t total = total_sh;
         int32_t tiles = 0, ns = 0;
         for (int e = 0; e < n_exp; ++e) {
-            const int32_t start = tab[e * nthr];
-            const int32_t stop = (e + 1 < n_exp) ? tab[(e + 1) * nthr] : total;
-            const int32_t c = stop - start;
+            const int32_t c = bounds[e + 1] - bounds[e];
             tile_start[e] = tiles;
             if (c > small_max) tiles += (c + tile_j - 1) / tile_j;
             else if (c > 0) small[ns++] = e;
@@ -93,13 +142,19 @@ __global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(const int32_t 
         tile_start[n_exp] = tiles;
         for (int e = ns; e < n_exp; ++e) small[e] = -1;
     }
-    __syncthreads();
-    // scatter
-    for (int64_t p = lo; p < hi; ++p) {
-        const int32_t e = ids[p];
-        if (e >= 0 && e < n_exp) {
-            const int32_t pos = tab[e * nthr + t]++;
-            sorted[pos] = (int32_t)p;
+    // scatter (the table is not read by the dispatch above, so no barrier is needed here)
+    for (int64_t p0 = lo; p0 < hi; p0 += kGroupBatch) {
+        int32_t ev[kGroupBatch];
+#pragma unroll
+        for (int j = 0; j < kGroupBatch; ++j) ev[j] = p0 + j < hi ? ids[p0 + j] : -1;
+#pragma unroll
+        for (int j = 0; j < kGroupBatch; ++j) {
+            if (p0 + j >= hi) break;
+            const int32_t e = ev[j];
+            if (e >= 0 && e < n_exp) {
+                const int32_t pos = tab[e * nthr + t]++;
+                sorted[pos] = (int32_t)(p0 + j);
+            }
         }
     }
 }

@@ -113,6 +113,15 @@ qmm_status qmm_matmul_id(int type, const void *w, int64_t n_exp, int64_t rows, i
 /* Host pointer out receives the invalid-id count of the last qmm_matmul_id that used `ws`
  * (synchronizes `stream` first). */
 qmm_status qmm_matmul_id_invalid_count(const void *ws, int64_t *out, void *stream);
+/* Test hook (host logic only, no GPU call): where the expert grouping of a qmm_matmul_id call of
+ * this shape lives in its workspace, so a test can check it ([MMQ] "expert bounds").  out[6]:
+ * byte offsets of sorted (int32 [pairs]: pair indices t*top_k+slot grouped by expert, ascending
+ * inside an expert), bounds (int32 [n_exp+1]: segment starts, bounds[n_exp] = valid pairs),
+ * tile_start (int32 [n_exp+1]: prefix of tiled-kernel column tiles), small (int32 [n_exp]:
+ * experts with 1..small_max columns in ascending order, then -1), then the column-tile width
+ * and small_max the call uses.  Returns QMM_ERR_ARG for a bad shape. */
+qmm_status qmm_matmul_id_grouping_layout(int64_t n_exp, int64_t k, int64_t n_tok, int64_t top_k,
+                                         int64_t x_per_tok, int64_t *out);
 
 /* ---------------------------------------------------------------------------------------------
  * Test hook: the integer sub-block dots from the production kernels' own integer accumulators

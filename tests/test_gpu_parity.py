@@ -504,6 +504,54 @@ def test_moe_small_experts_both_kernels(qtype, kernel):
             assert_close(y[t, s][None], ref[t, s][None], wn_all[ids[t, s]], xn_all[a:a + 1], what=f"pair {t},{s}")
 
 
+def _grouping_ref(ids, n_exp, tile_j, small_max):
+    """Stable counting sort of the (token, slot) pairs by expert, as the expert-bounds passage
+    describes it: each expert's pairs contiguous and in ascending pair order."""
+    flat = ids.reshape(-1).astype(np.int64)
+    valid = (flat >= 0) & (flat < n_exp)
+    p = np.nonzero(valid)[0]
+    order = p[np.argsort(flat[p], kind="stable")]
+    counts = np.bincount(flat[p], minlength=n_exp)
+    bounds = np.concatenate([[0], np.cumsum(counts)])
+    tiles, tile_start, small = 0, [], []
+    for e in range(n_exp):
+        tile_start.append(tiles)
+        c = int(counts[e])
+        if c > small_max:
+            tiles += -(-c // tile_j)
+        elif c > 0:
+            small.append(e)
+    tile_start.append(tiles)
+    small += [-1] * (n_exp - len(small))
+    return order, bounds, np.array(tile_start), np.array(small), int((~valid).sum())
+
+
+@pytest.mark.parametrize("n_exp,n_tok,top_k,zipf", [(8, 512, 2, 1.1), (128, 2048, 8, 1.0), (6, 37, 3, 0.0),
+                                                     (1000, 333, 4, 0.8), (5000, 50, 2, 0.0)])
+def test_moe_grouping_is_a_stable_counting_sort(n_exp, n_tok, top_k, zipf):
+    """The device grouping pass (index work: bit-exact) against a host stable sort, including
+    invalid ids, ragged per-thread chunks and expert counts that shrink the per-thread table."""
+    rng = np.random.default_rng(1300 + n_exp)
+    qtype, rows, k = qmm.Q8_0, 16, 256
+    if zipf > 0:
+        pr = 1.0 / np.arange(1, n_exp + 1) ** zipf
+        pr /= pr.sum()
+        ids = np.stack([rng.choice(n_exp, top_k, replace=False, p=pr) for _ in range(n_tok)]).astype(np.int32)
+    else:
+        ids = rng.integers(0, n_exp, (n_tok, top_k)).astype(np.int32)
+    ids.reshape(-1)[rng.integers(0, n_tok * top_k, 5)] = np.array([-1, n_exp, n_exp + 7, -100, 1 << 30], np.int32)
+    w = synth.gen_weights(qtype, n_exp * rows, k, rng)
+    x = rng.standard_normal((n_tok, k)).astype(np.float32)
+    _, ws = qmm.matmul_id(to_dev(w), qtype, n_exp, rows, k, to_dev(x), to_dev(ids), x_per_tok=1)
+    g = qmm.matmul_id_grouping(ws, n_exp, k, n_tok, top_k, 1)
+    order, bounds, tile_start, small, bad = _grouping_ref(ids, n_exp, g["tile_j"], g["small_max"])
+    assert qmm.matmul_id_invalid_count(ws) == bad
+    assert np.array_equal(g["bounds"].numpy(), bounds)
+    assert np.array_equal(g["sorted"].numpy()[:bounds[-1]], order)
+    assert np.array_equal(g["tile_start"].numpy(), tile_start)
+    assert np.array_equal(g["small"].numpy(), small)
+
+
 def test_moe_rerun_is_bitwise():
     case = synth.MOE_CASES[3]
     w, x, ids = synth.make_moe(case)
