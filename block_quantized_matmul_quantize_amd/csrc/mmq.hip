@@ -623,12 +623,37 @@ __global__ __launch_bounds__(256) void streamk_fixup_kernel(float *__restrict__ 
             slot_off[threadIdx.x] = (2 * u + (first_tile == t ? 0 : 1)) * (int64_t)kTI * J;
         }
         __syncthreads();
-        for (int i = threadIdx.x; i < kTI * J; i += blockDim.x) {
-            const int c = i / kTI, r = i - c * kTI;
-            if (r0 + r >= rows || c0 + c >= n) continue;
-            float v = ub == u0 ? 0.f : y[(c0 + c) * rows + r0 + r];
-            for (int64_t j = 0; j < m; ++j) v += args.partials[slot_off[j] + (int64_t)c * kTI + r];
-            y[(c0 + c) * rows + r0 + r] = v;
+        // item it = threadIdx.x + 256*q: four consecutive rows of one column; the partials of all
+        // the thread's items are loaded together, one covering unit at a time
+        constexpr int PER = kTI * J / 4 / 256;
+        f32x4 v[PER];
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            v[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (ub != u0) {
+                const int it = threadIdx.x + 256 * q, c = (4 * it) / kTI, r = 4 * it - c * kTI;
+                if (c0 + c < n)
+                    for (int e = 0; e < 4 && r0 + r + e < rows; ++e) v[q][e] = y[(c0 + c) * rows + r0 + r + e];
+            }
+        }
+        for (int64_t j = 0; j < m; ++j) {
+            const float *src = args.partials + slot_off[j] + 4 * threadIdx.x;
+#pragma unroll
+            for (int q = 0; q < PER; ++q) v[q] += *(const f32x4 *)(src + 1024 * q);
+        }
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int it = threadIdx.x + 256 * q, c = (4 * it) / kTI, r = 4 * it - c * kTI;
+            if (c0 + c >= n) continue;
+            float *dst = y + (c0 + c) * rows + r0 + r;
+            if (r0 + r + 4 <= rows) {
+                dst[0] = v[q][0];
+                dst[1] = v[q][1];
+                dst[2] = v[q][2];
+                dst[3] = v[q][3];
+            } else {
+                for (int e = 0; r0 + r + e < rows; ++e) dst[e] = v[q][e];
+            }
         }
     }
 }
