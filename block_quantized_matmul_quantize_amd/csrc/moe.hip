@@ -5,15 +5,17 @@
 // One workgroup runs a stable counting sort of the (token, slot) pairs by expert id:
 //   1. thread t counts its contiguous chunk of pairs per expert into an LDS table cnt[e][t]
 //      (ids read in batches of independent loads, counted with LDS atomics on its own column);
-//   2. thread e sums row e into bounds[e]; a scan over the experts turns these into the segment
-//      starts; thread e then scans row e in thread order, so that (e, t) holds the first output
-//      position of thread t's pairs of expert e (rows are padded to nthr + 1 entries, so the
-//      threads of a wave walking their rows in step hit distinct LDS banks);
+//   2. thread t owns the experts [t*ce, t*ce + ce): it sums their rows, a block scan over the
+//      threads gives each expert its segment start bounds[e], and the thread scans each of its
+//      rows in thread order, so that (e, t') holds the first output position of thread t''s
+//      pairs of expert e (rows are padded to nthr + 1 entries, so the threads of a wave walking
+//      their rows in step hit distinct LDS banks);
 //   3. each thread walks its chunk again and writes pair indices to their positions, so the
 //      order inside an expert is ascending pair index (token-major, then slot).
 // It also emits the per-expert dispatch: experts with 1..small_max columns go to the
 // matrix-vector kernel (list `small`), larger ones get ceil(count / tile_j) column tiles whose
-// prefix is tile_start[].  Ids outside [0, n_exp) are skipped and counted in invalid[0].
+// prefix is tile_start[] (two more block scans).  Ids outside [0, n_exp) are skipped and counted
+// in invalid[0].  No step loops over all experts or all threads in one thread.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -25,6 +27,26 @@ constexpr int kGroupBatch = 32;          // ids in flight per thread
 
 __host__ __device__ constexpr int group_row_stride(int nthr) { return nthr == 1 ? 1 : nthr + 1; }
 
+// Exclusive scan of one value per thread over the workgroup (Hillis-Steele in LDS); returns the
+// thread's exclusive prefix and writes the total to *total.  buf: 2 * kGroupThreads ints.
+__device__ __forceinline__ int32_t block_excl_scan(int32_t v, int32_t *buf, int32_t *total) {
+    const int t = threadIdx.x;
+    int cur = 0;
+    buf[t] = v;
+    __syncthreads();
+#pragma unroll
+    for (int d = 1; d < kGroupThreads; d <<= 1) {
+        const int32_t x = buf[cur * kGroupThreads + t] + (t >= d ? buf[cur * kGroupThreads + t - d] : 0);
+        buf[(cur ^ 1) * kGroupThreads + t] = x;
+        cur ^= 1;
+        __syncthreads();
+    }
+    const int32_t incl = buf[cur * kGroupThreads + t];
+    *total = buf[cur * kGroupThreads + kGroupThreads - 1];
+    __syncthreads();   // buf is reused by the next scan
+    return incl - v;
+}
+
 __global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(const int32_t *__restrict__ ids, int64_t pairs,
                                                                   int32_t n_exp, int32_t nthr, int32_t tile_j,
                                                                   int32_t small_max, int32_t *__restrict__ sorted,
@@ -33,15 +55,18 @@ __global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(const int32_t 
                                                                   int32_t *__restrict__ small,
                                                                   int32_t *__restrict__ invalid) {
     __shared__ int32_t tab[kGroupTableInts];
-    __shared__ int32_t part[kGroupThreads];
-    __shared__ int32_t bad_sh[kGroupThreads];
+    __shared__ int32_t sbuf[2 * kGroupThreads];
+    __shared__ int32_t bad_sh;
     const int t = threadIdx.x;
     const int rs = group_row_stride(nthr);
     const bool active = t < nthr;
     const int64_t chunk = (pairs + nthr - 1) / nthr;
     const int64_t lo = active ? (int64_t)t * chunk : 0;
     const int64_t hi = active ? (lo + chunk < pairs ? lo + chunk : pairs) : 0;
+    const int ce = (n_exp + kGroupThreads - 1) / kGroupThreads;
+    const int e0 = t * ce < n_exp ? t * ce : n_exp, e1 = e0 + ce < n_exp ? e0 + ce : n_exp;
 
+    if (t == 0) bad_sh = 0;
     for (int i = t; i < n_exp * rs; i += kGroupThreads) tab[i] = 0;
     __syncthreads();
     int bad = 0;
@@ -56,68 +81,73 @@ __global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(const int32_t 
             else if (p0 + j < hi) bad++;
         }
     }
-    bad_sh[t] = bad;
+    if (bad) atomicAdd(&bad_sh, bad);
     __syncthreads();
 
-    // row totals into bounds[e] (thread e, e + 256, ...)
-    for (int e = t; e < n_exp; e += kGroupThreads) {
-        int32_t v = 0;
-        for (int i = 0; i < nthr; ++i) v += tab[e * rs + i];
+    // row totals of the thread's experts (kept in bounds[e] until the scan below)
+    int32_t mine = 0;
+    for (int e = e0; e < e1; ++e) {
+        const int32_t *row = tab + e * rs;
+        int32_t a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+        int i = 0;
+        for (; i + 4 <= nthr; i += 4) {
+            a0 += row[i];
+            a1 += row[i + 1];
+            a2 += row[i + 2];
+            a3 += row[i + 3];
+        }
+        for (; i < nthr; ++i) a0 += row[i];
+        const int32_t v = a0 + a1 + a2 + a3;
         bounds[e] = v;
+        mine += v;
     }
-    __syncthreads();
-    // exclusive scan of the totals over the experts: thread t takes experts [t*ce, t*ce + ce)
-    {
-        const int ce = (n_exp + kGroupThreads - 1) / kGroupThreads;
-        const int e0 = t * ce, e1 = e0 + ce < n_exp ? e0 + ce : n_exp;
-        int32_t sum = 0;
-        for (int e = e0; e < e1; ++e) sum += bounds[e];
-        part[t] = sum;
-        __syncthreads();
-        if (t == 0) {
-            int32_t run = 0, nbad = 0;
-            for (int i = 0; i < kGroupThreads; ++i) {
-                const int32_t v = part[i];
-                part[i] = run;
-                run += v;
-                nbad += bad_sh[i];
-            }
-            bounds[n_exp] = run;
-            invalid[0] = nbad;
+    int32_t total = 0;
+    int32_t run = block_excl_scan(mine, sbuf, &total);
+    // segment starts, row scans, and the thread's dispatch counts
+    int32_t my_tiles = 0, my_small = 0;
+    for (int e = e0; e < e1; ++e) {
+        const int32_t c = bounds[e];
+        bounds[e] = run;
+        int32_t *row = tab + e * rs;
+        int32_t r = run;
+        int i = 0;
+        for (; i + 4 <= nthr; i += 4) {
+            const int32_t v0 = row[i], v1 = row[i + 1], v2 = row[i + 2], v3 = row[i + 3];
+            row[i] = r;
+            row[i + 1] = r + v0;
+            row[i + 2] = r + v0 + v1;
+            row[i + 3] = r + v0 + v1 + v2;
+            r += v0 + v1 + v2 + v3;
         }
-        __syncthreads();
-        int32_t run = part[t];
-        for (int e = e0; e < e1; ++e) {
-            const int32_t v = bounds[e];
-            bounds[e] = run;
-            run += v;
+        for (; i < nthr; ++i) {
+            const int32_t v0 = row[i];
+            row[i] = r;
+            r += v0;
         }
+        run += c;
+        // count of tiles, or -1 for an expert the matrix-vector kernel takes (prefixes below)
+        const int32_t nt = c > small_max ? (c + tile_j - 1) / tile_j : (c > 0 ? -1 : 0);
+        tile_start[e] = nt;
+        my_tiles += nt > 0 ? nt : 0;
+        my_small += nt < 0 ? 1 : 0;
     }
-    __syncthreads();
-    // each row scanned in thread order from its segment start
-    for (int e = t; e < n_exp; e += kGroupThreads) {
-        int32_t run = bounds[e];
-        for (int i = 0; i < nthr; ++i) {
-            const int32_t v = tab[e * rs + i];
-            tab[e * rs + i] = run;
-            run += v;
-        }
+    int32_t tiles_total = 0, small_total = 0;
+    int32_t trun = block_excl_scan(my_tiles, sbuf, &tiles_total);
+    int32_t srun = block_excl_scan(my_small, sbuf, &small_total);
+    for (int e = e0; e < e1; ++e) {
+        const int32_t nt = tile_start[e];
+        if (nt < 0) small[srun++] = e;
+        tile_start[e] = trun;
+        trun += nt > 0 ? nt : 0;
     }
-    __syncthreads();
-    // the per-expert dispatch, from the segment starts
+    for (int i = small_total + t; i < n_exp; i += kGroupThreads) small[i] = -1;
     if (t == 0) {
-        int32_t tiles = 0, ns = 0;
-        for (int e = 0; e < n_exp; ++e) {
-            const int32_t c = bounds[e + 1] - bounds[e];
-            tile_start[e] = tiles;
-            if (c > small_max) tiles += (c + tile_j - 1) / tile_j;
-            else if (c > 0) small[ns++] = e;
-        }
-        tile_start[n_exp] = tiles;
-        for (int e = ns; e < n_exp; ++e) small[e] = -1;
+        bounds[n_exp] = total;
+        tile_start[n_exp] = tiles_total;
+        invalid[0] = bad_sh;
     }
-    // scatter (the table is not read by the dispatch above, so no barrier is needed here); each
-    // thread advances only its own column, in pair order
+    __syncthreads();
+    // scatter; each thread advances only its own column, in pair order
     for (int64_t p0 = lo; p0 < hi; p0 += kGroupBatch) {
         int32_t ev[kGroupBatch];
 #pragma unroll
