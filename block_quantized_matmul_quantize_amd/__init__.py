@@ -60,7 +60,7 @@ _sig("qmm_matmul_q8_1", _i32, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _sz, _
 _sig("qmm_matmul_id_workspace", _sz, _i32, _i64, _i64, _i64, _i64, _i64, _i64)
 _sig("qmm_matmul_id", _i32, _i32, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _sz, _vp)
 _sig("qmm_matmul_id_invalid_count", _i32, _vp, ctypes.POINTER(_i64), _vp)
-_sig("qmm_matmul_id_grouping_layout", _i32, _i64, _i64, _i64, _i64, _i64, ctypes.POINTER(_i64))
+_sig("qmm_matmul_id_grouping_layout", _i32, _i32, _i64, _i64, _i64, _i64, _i64, ctypes.POINTER(_i64))
 _sig("qmm_debug_subdots", _i32, _i32, _vp, _i64, _i64, _vp, _i64, _i32, _vp, _vp)
 _sig("qmm_set_override", _i32, _i32, _i32)
 _sig("qmm_plan_dense", _i32, _i32, _i64, _i64, _i64, ctypes.c_int32, ctypes.POINTER(Plan))
@@ -253,12 +253,19 @@ def matmul_id_invalid_count(ws):
     return int(v.value)
 
 
-def matmul_id_grouping(ws, n_exp, k, n_tok, top_k, x_per_tok=1):
+def matmul_id_layout(qtype, n_exp, k, n_tok, top_k, x_per_tok=1):
+    """Host logic only: workspace byte offsets of the expert grouping (sorted, bounds, tile_start,
+    small), the column-tile width and the small-expert limit a matmul_id of this shape uses."""
+    out = (_i64 * 6)()
+    _check(_L.qmm_matmul_id_grouping_layout(qtype, n_exp, k, n_tok, top_k, x_per_tok, out))
+    return tuple(int(v) for v in out)
+
+
+def matmul_id_grouping(ws, qtype, n_exp, k, n_tok, top_k, x_per_tok=1):
     """Expert grouping the last matmul_id with workspace `ws` built (synchronizes the stream):
     dict of int32 CPU tensors sorted, bounds, tile_start, small, plus tile_j and small_max."""
     torch = _torch()
-    out = (_i64 * 6)()
-    _check(_L.qmm_matmul_id_grouping_layout(n_exp, k, n_tok, top_k, x_per_tok, out))
+    out = matmul_id_layout(qtype, n_exp, k, n_tok, top_k, x_per_tok)
     torch.cuda.current_stream().synchronize()
     pairs = n_tok * top_k
     raw = ws.view(torch.uint8)

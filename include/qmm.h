@@ -120,8 +120,8 @@ qmm_status qmm_matmul_id_invalid_count(const void *ws, int64_t *out, void *strea
  * tile_start (int32 [n_exp+1]: prefix of tiled-kernel column tiles), small (int32 [n_exp]:
  * experts with 1..small_max columns in ascending order, then -1), then the column-tile width
  * and small_max the call uses.  Returns QMM_ERR_ARG for a bad shape. */
-qmm_status qmm_matmul_id_grouping_layout(int64_t n_exp, int64_t k, int64_t n_tok, int64_t top_k,
-                                         int64_t x_per_tok, int64_t *out);
+qmm_status qmm_matmul_id_grouping_layout(int type, int64_t n_exp, int64_t k, int64_t n_tok,
+                                         int64_t top_k, int64_t x_per_tok, int64_t *out);
 
 /* ---------------------------------------------------------------------------------------------
  * Test hook: the integer sub-block dots from the production kernels' own integer accumulators

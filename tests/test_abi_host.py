@@ -199,3 +199,25 @@ def test_matvec_kernel_choice_follows_alignment_and_overrides():
     finally:
         for key in (qmm.OVR_MV_KERNEL, qmm.OVR_FUSE_COLS, qmm.OVR_PATH):
             qmm.set_override(key, 0)
+
+
+@pytest.mark.parametrize("qtype,n_exp,n_tok,top_k,J", [
+    (qmm.Q6_K, 128, 2048, 8, 128),     # Q6_K keeps 128-column tiles
+    (qmm.Q4_K, 128, 2048, 8, 64),      # mean 128 columns per expert
+    (qmm.Q4_K, 8, 512, 2, 64),
+    (qmm.Q8_0, 64, 100, 4, 32),        # mean 6
+    (qmm.Q4_K, 4, 1024, 2, 128),       # mean 512
+])
+def test_expert_tile_width_follows_mean_columns_per_expert(qtype, n_exp, n_tok, top_k, J):
+    lay = qmm.matmul_id_layout(qtype, n_exp, 2048, n_tok, top_k, 1)
+    assert lay[4] == J
+    assert lay[5] == 8                                     # experts of <= 8 columns: matrix-vector
+    assert qmm.matmul_id_layout(qtype, n_exp, 256 * 1024, n_tok, top_k, 1)[5] == 0   # beyond its K limit
+    offs = lay[:4]
+    assert all(o % 256 == 0 for o in offs) and list(offs) == sorted(offs)
+    assert offs[-1] < qmm.matmul_id_workspace(qtype, n_exp, 64, 2048, n_tok, top_k, 1)
+    qmm.set_override(qmm.OVR_TILE_J, 32)
+    try:
+        assert qmm.matmul_id_layout(qtype, n_exp, 2048, n_tok, top_k, 1)[4] == 32
+    finally:
+        qmm.set_override(qmm.OVR_TILE_J, 0)

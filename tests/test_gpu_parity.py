@@ -543,7 +543,7 @@ def test_moe_grouping_is_a_stable_counting_sort(n_exp, n_tok, top_k, zipf):
     w = synth.gen_weights(qtype, n_exp * rows, k, rng)
     x = rng.standard_normal((n_tok, k)).astype(np.float32)
     _, ws = qmm.matmul_id(to_dev(w), qtype, n_exp, rows, k, to_dev(x), to_dev(ids), x_per_tok=1)
-    g = qmm.matmul_id_grouping(ws, n_exp, k, n_tok, top_k, 1)
+    g = qmm.matmul_id_grouping(ws, qtype, n_exp, k, n_tok, top_k, 1)
     order, bounds, tile_start, small, bad = _grouping_ref(ids, n_exp, g["tile_j"], g["small_max"])
     assert qmm.matmul_id_invalid_count(ws) == bad
     assert np.array_equal(g["bounds"].numpy(), bounds)
