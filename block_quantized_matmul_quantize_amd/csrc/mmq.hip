@@ -58,9 +58,7 @@ template <int T, int J> struct Smem {
     static constexpr int WM_OFF = WS_OFF + 8 * kTI * 4;                          // float [8][128] (Q4_K)
     static constexpr int A_OFF = WM_OFF + (T == kQ4_K ? 8 * kTI * 4 : 0);      // int8 [J][kLd]
     static constexpr int X_OFF = A_OFF + J * kLd;                                // float2 [8][J]
-    static constexpr int STG_OFF = X_OFF + 8 * J * 8;                            // Q6_K raw [128][224]
-    static constexpr int STG_BYTES = (T == kQ6_K && Cfg<J>::NT >= 512) ? kTI * 224 : 0;
-    static constexpr int BYTES = STG_OFF + STG_BYTES;
+    static constexpr int BYTES = X_OFF + 8 * J * 8;
 };
 
 // Two LDS step buffers where they fit beside the occupancy the tile runs at: Q4_K 8-wave tiles
@@ -231,7 +229,6 @@ __device__ __forceinline__ void q6_split4(uint32_t c6, s16x2 sc2, s16x2 off2, ui
 // (no register prefetch: the registers are taken by the accumulators).
 template <int NT> struct WFetchQ6Direct {
     __device__ __forceinline__ void fetch(const uint8_t *, int64_t, int64_t, int64_t, int64_t, int64_t) {}
-    template <int J> __device__ __forceinline__ void unpack(uint8_t *, int64_t, int64_t) const {}
     template <int J>
     __device__ __forceinline__ void store(uint8_t *sm, const uint8_t *wbase, int64_t row_bytes, int64_t r0,
                                           int64_t rows, int64_t kb, int64_t) const {
@@ -270,76 +267,61 @@ template <int NT> struct WFetchQ6Direct {
     }
 };
 
-// Q6_K with 8-wave tiles (J = 128): the step's 210-byte super-blocks of the 128 rows are
-// prefetched into registers as 14 pieces per row (13 of 16 bytes, the 14th ends at the fp16 d),
-// parked raw in a staging area, and unpacked from there into the two planes after a barrier
-// (the unpack needs ql, qh and the scale of a 16-value group, which different pieces hold).
-template <int NT> struct WFetchQ6Staged {
-    static constexpr int NP = kTI * 14, N = (NP + NT - 1) / NT;
-    u32x4 q[N];
+// Q6_K with 8-wave tiles (J = 128): thread u owns row u/4 and, of its 16 sixteen-value groups,
+// the four with G/8 = (u/2)%2 and G%2 = u%2 (gq = 0..3).  It prefetches exactly the pieces those
+// groups need -- the two 16-byte ql pieces (low nibbles: gq 0/1, high: gq 2/3), the 16-byte qh
+// piece (2-bit fields gq) and the 16 scale bytes (the thread takes its four), plus the fp16 d for
+// one thread per row -- and unpacks them from registers into the two planes at park time.
+template <int NT> struct WFetchQ6Reg {
+    static_assert(NT == 512, "one (row, half, group-parity) unit per thread");
+    u32x4 ql0, ql1, qh, sc;
+    uint16_t d;
     __device__ __forceinline__ void fetch(const uint8_t *wbase, int64_t row_bytes, int64_t r0, int64_t rows,
                                           int64_t kb, int64_t) {
-        const int tid = threadIdx.x;
-#pragma unroll
-        for (int it = 0; it < N; ++it) {
-            const int i = (tid + NT * it) < NP ? tid + NT * it : NP - 1;   // idle lanes re-read a valid piece
-            const int r = i / 14, j = i - 14 * r;
-            const int64_t row = r0 + r < rows ? r0 + r : rows - 1;       // ragged tile: re-read the last row
-            q[it] = ld16(wbase + row * row_bytes + kb * 210 + (j < 13 ? 16 * j : 194));
-        }
+        const int u = threadIdx.x;
+        const int r = u >> 2, hh = (u >> 1) & 1, l0 = 16 * (u & 1);
+        const int64_t row = r0 + r < rows ? r0 + r : rows - 1;   // ragged tile: re-read the last row
+        const uint8_t *blk = wbase + row * row_bytes + kb * 210;
+        ql0 = ld16(blk + 64 * hh + l0);
+        ql1 = ld16(blk + 64 * hh + 32 + l0);
+        qh = ld16(blk + 128 + 32 * hh + l0);
+        sc = ld16(blk + 192);
+        d = (u & 3) == 0 ? ld2(blk + 208) : (uint16_t)0;
     }
     template <int J>
-    __device__ __forceinline__ void store(uint8_t *sm, const uint8_t *, int64_t, int64_t, int64_t, int64_t,
+    __device__ __forceinline__ void store(uint8_t *sm, const uint8_t *, int64_t, int64_t r0, int64_t rows, int64_t,
                                           int64_t) const {
-        const int tid = threadIdx.x;
-        uint8_t *stg = sm + Smem<kQ6_K, J>::STG_OFF;
-        static_assert(Smem<kQ6_K, J>::STG_BYTES > 0, "staging area missing");
-#pragma unroll
-        for (int it = 0; it < N; ++it) {
-            const int i = tid + NT * it;
-            if (NT * it + NT <= NP || i < NP) {
-                const int r = i / 14, j = i - 14 * r;
-                if (j < 13) *(u32x4 *)(stg + r * 224 + 16 * j) = q[it];
-                else *(uint16_t *)(stg + r * 224 + 208) = (uint16_t)(q[it].w >> 16);   // bytes 208..209: d
-            }
-        }
-    }
-    // staging -> planes: item (row, 16-value group G); v = sc * (q - 32) = 128 * hi + lo
-    template <int J>
-    __device__ __forceinline__ void unpack(uint8_t *sm, int64_t r0, int64_t rows) const {
-        const int tid = threadIdx.x;
-        const uint8_t *stg = sm + Smem<kQ6_K, J>::STG_OFF;
+        const int u = threadIdx.x;
+        const int r = u >> 2, hh = (u >> 1) & 1, half = u & 1;
         int8_t *sLo = (int8_t *)(sm + Smem<kQ6_K, J>::W_OFF);
         int8_t *sHi = sLo + kTI * kLd;
-#pragma unroll 2
-        for (int it = 0; it < 2048 / NT; ++it) {
-            const int i = tid + NT * it;               // (row, 16-value group G): 128 x 16
-            const int r = i >> 4, G = i & 15;
-            const uint8_t *blk = stg + r * 224;
-            const int hh = G >> 3, gq = (G & 7) >> 1, l0 = 16 * (G & 1);
-            const u32x4 ql = *(const u32x4 *)(blk + 64 * hh + 32 * (gq & 1) + l0);
-            const u32x4 qh = *(const u32x4 *)(blk + 128 + 32 * hh + l0);
-            const int sc = (int)(int8_t)blk[192 + G];
-            const s16x2 sc2 = {(short)sc, (short)sc}, off2 = {(short)(-32 * sc), (short)(-32 * sc)};
+        const uint32_t scw[4] = {sc.x, sc.y, sc.z, sc.w};
+        const uint32_t qlw0[4] = {ql0.x, ql0.y, ql0.z, ql0.w}, qlw1[4] = {ql1.x, ql1.y, ql1.z, ql1.w};
+        const uint32_t qhw[4] = {qh.x, qh.y, qh.z, qh.w};
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            const int G = 8 * hh + 2 * gq + half;
+            const int scv = (int)(int8_t)((scw[G >> 2] >> (8 * (G & 3))) & 0xFF);
+            const s16x2 sc2 = {(short)scv, (short)scv}, off2 = {(short)(-32 * scv), (short)(-32 * scv)};
             const int nsh = gq < 2 ? 0 : 4, tsh = 2 * gq;
-            const uint32_t qlw[4] = {ql.x, ql.y, ql.z, ql.w}, qhw[4] = {qh.x, qh.y, qh.z, qh.w};
             uint32_t lo_w[4], hi_w[4];
 #pragma unroll
             for (int dd = 0; dd < 4; ++dd) {
-                const uint32_t code6 = ((qlw[dd] >> nsh) & 0x0F0F0F0Fu) | (((qhw[dd] >> tsh) & 0x03030303u) << 4);
+                const uint32_t q = (gq & 1) ? qlw1[dd] : qlw0[dd];
+                const uint32_t code6 = ((q >> nsh) & 0x0F0F0F0Fu) | (((qhw[dd] >> tsh) & 0x03030303u) << 4);
                 q6_split4(code6, sc2, off2, lo_w[dd], hi_w[dd]);
             }
             *(u32x4 *)(sLo + r * kLd + 16 * G) = u32x4{lo_w[0], lo_w[1], lo_w[2], lo_w[3]};
             *(u32x4 *)(sHi + r * kLd + 16 * G) = u32x4{hi_w[0], hi_w[1], hi_w[2], hi_w[3]};
         }
-        if (tid < kTI) {
+        if ((u & 3) == 0) {
             float *sWs = (float *)(sm + Smem<kQ6_K, J>::WS_OFF);
-            sWs[tid] = r0 + tid < rows ? h2f(*(const uint16_t *)(stg + tid * 224 + 208)) : 0.f;
+            sWs[r] = r0 + r < rows ? h2f(d) : 0.f;
         }
     }
 };
 
-template <int NT> struct WFetch<kQ6_K, NT> : std::conditional<(NT >= 512), WFetchQ6Staged<NT>, WFetchQ6Direct<NT>>::type {};
+template <int NT> struct WFetch<kQ6_K, NT> : std::conditional<(NT >= 512), WFetchQ6Reg<NT>, WFetchQ6Direct<NT>>::type {};
 
 // ---------------------------------------------------------------------------------------------
 // One 256-value step of MFMAs + fixups for this wave's 32 rows x JW columns.  Wave wid: row wave
@@ -508,10 +490,6 @@ __device__ __forceinline__ void run_tile(uint8_t *sm, f32x16 (&acc)[Cfg<J>::NCB]
         wf.template store<J>(sm, wbase, row_bytes, r0, rows, kb, nb32);
         af.template store<T>(sm);
         __syncthreads();
-        if constexpr (Smem<T, J>::STG_BYTES > 0) {   // Q6_K staged: raw bytes -> planes
-            wf.template unpack<J>(sm, r0, rows);
-            __syncthreads();
-        }
         if (kb + 1 < kb1) {
             wf.fetch(wbase, row_bytes, r0, rows, kb + 1, nb32);
             af.fetch(xq, nb32, kb + 1, acol, act_rows);
