@@ -41,6 +41,19 @@ struct MmqArgs {
     int32_t write_partials;     // stream-K active
 };
 
+// Tile order: bands of kBand row tiles, each walked column by column, so that consecutive tiles
+// (the ones an XCD runs at the same time, units being contiguous per XCD) share kBand weight row
+// tiles and a few activation column tiles in that XCD's L2, instead of every XCD sweeping all
+// column tiles for each pair of row tiles (which re-fetches the activations for every pair).
+constexpr int64_t kBand = 8;
+__device__ __forceinline__ void tile_coords(int64_t t, int64_t ntiles, int64_t n_ct, int64_t &rt, int64_t &ct) {
+    const int64_t n_rt = ntiles / n_ct;
+    const int64_t band = t / (kBand * n_ct), i = t - band * kBand * n_ct;
+    const int64_t rows_in_band = n_rt - band * kBand < kBand ? n_rt - band * kBand : kBand;
+    ct = i / rows_in_band;
+    rt = band * kBand + (i - ct * rows_in_band);
+}
+
 // Threads per tile: 4 row waves (32 rows each) times J/64 column waves (J = 128: two 64-column
 // halves, so every wave keeps at most 64 columns of accumulators and two waves fit per SIMD).
 template <int J> struct Cfg {
@@ -540,7 +553,8 @@ __global__ __launch_bounds__(Cfg<J>::NT, 2) void mmq_kernel(const uint8_t *__res
         const int64_t t = pos / args.k_iters;
         const int64_t kb0 = pos - t * args.k_iters;
         const int64_t kb1 = (kb0 + (end - pos) < args.k_iters) ? kb0 + (end - pos) : args.k_iters;
-        const int64_t rt = t / args.n_ct, ct = t - rt * args.n_ct;
+        int64_t rt, ct;
+        tile_coords(t, args.ntiles, args.n_ct, rt, ct);
         const int64_t r0 = rt * kTI, c0 = ct * J;
 
         int64_t acol[NA];
@@ -587,7 +601,8 @@ __global__ __launch_bounds__(256) void streamk_fixup_kernel(float *__restrict__ 
     const int64_t u0 = unit_of(t * args.k_iters, W, args.units);
     const int64_t u1 = unit_of((t + 1) * args.k_iters - 1, W, args.units);
     if (u0 == u1) return;                         // one unit covered the whole tile
-    const int64_t rt = t / args.n_ct, ct = t - rt * args.n_ct;
+    int64_t rt, ct;
+    tile_coords(t, args.ntiles, args.n_ct, rt, ct);
     const int64_t r0 = rt * kTI, c0 = ct * J;
     // partial-slot offsets of the covering units, computed once (kSlots at a time)
     constexpr int kSlots = 256;
