@@ -16,14 +16,16 @@ Also in the same JSON line:
   secondary     int8 TOPS and % of the 5.0 POP/s int8 MFMA peak for the prefill and MoE shapes.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-secondary]
+       python bench.py --secondary-only [--calib-copy]   only the prefill / MoE shapes (profiling)
 
 Profile summaries (no GPU; read the SQLite databases rocprofv3 writes under -d DIR):
   python bench.py --summarize-trace DIR          per-kernel durations of a --kernel-trace run
   python bench.py --summarize-pmc FDIR WDIR [--write-traffic]
                  per-kernel FETCH_SIZE / WRITE_SIZE of two --pmc runs of `bench.py --calib-copy`,
-                 scaled to bytes by the 256 MiB device copy; --write-traffic stores the
-                 matrix-vector kernels' average in profiles/mmvq_traffic.json (with a hash of
-                 the kernel sources, so the figure is dropped once they change).
+                 scaled to bytes by the 256 MiB device copy (tiled and grouping kernels get one
+                 line per launch shape); --write-traffic stores the matrix-vector kernels'
+                 average in profiles/mmvq_traffic.json (with a hash of the kernel sources, so
+                 the figure is dropped once they change).
 """
 import argparse
 import glob
@@ -41,10 +43,15 @@ HBM_PEAK_GBPS = 8000.0
 INT8_PEAK_TOPS = 5000.0
 
 
+# Sources the matrix-vector kernels are built and chosen from: a change to any of them drops the
+# stored counter traffic; changes elsewhere (tiled kernels, planner) do not affect those kernels.
+MV_SOURCES = ["common.hpp", "launch.hpp", "q8_1.hpp", "mmvq.hip", "mmvq_stream.hip", "mmvq_dot4.hip"]
+
+
 def source_hash():
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "block_quantized_matmul_quantize_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
+    for name in MV_SOURCES:
+        with open(os.path.join(ROOT, "block_quantized_matmul_quantize_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -71,6 +78,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--secondary-only", action="store_true",
+                    help="time only the prefill and MoE shapes (for profiling them); prints their JSON")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 256 MiB device copy (known bytes) to scale profiler counters")
     ap.add_argument("--summarize-trace", metavar="DIR")
@@ -105,6 +114,9 @@ def main():
     BB, BV = qmm.BLOCK_BYTES, qmm.BLOCK_VALUES
     cases = synth.MMVQ_CASES
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
+    if args.secondary_only:
+        print(json.dumps({"secondary": run_secondary(torch, np, qmm, synth, dev, log)}), flush=True)
+        return
 
     # ---------------------------------------------------------------- inputs (resident in HBM)
     R = max(1, args.rotations)
@@ -285,6 +297,12 @@ def summarize_pmc(fdir, wdir, write=False):
             by.setdefault(_short(name), []).append(value)
         return by
 
+    def by_grid(d):
+        out = {}
+        for name, value, grid in _rocpd(d).execute("select kernel_name, value, grid_size from counters_collection"):
+            out.setdefault((_short(name), grid), []).append(value)
+        return out
+
     F, Wr = load(fdir), load(wdir)
     copy = [k for k in F if "copyBuffer" in k or "copy" in k.lower()]
     if not copy:
@@ -303,8 +321,21 @@ def summarize_pmc(fdir, wdir, write=False):
         if "mmvq" in k:
             mv_tot += b * len(F[k])
             mv_cnt += len(F[k])
+    # tiled and grouping kernels: one line per launch shape (grid size), as the shapes differ
+    FG, WG = by_grid(fdir), by_grid(wdir)
+    tiled = sorted(k for k in FG if "mmq" in k[0] or "moe_group" in k[0] or "fixup" in k[0])
+    if tiled:
+        print()
+        print("| kernel | grid (threads) | dispatches | HBM bytes/dispatch fetched | written |")
+        print("|---|---|---|---|---|")
+        for k in tiled:
+            f = statistics.mean(FG[k]) * 1024 * fs
+            w = statistics.mean(WG.get(k, [0.0])) * 1024 * ws
+            print(f"| `{k[0]}` | {k[1]} | {len(FG[k])} | {f / 1e6:.1f} MB | {w / 1e6:.1f} MB |")
     if not mv_cnt:
-        raise SystemExit("no matrix-vector kernel dispatches in the counter runs")
+        if write:
+            raise SystemExit("no matrix-vector kernel dispatches in the counter runs")
+        return
     avg = mv_tot / mv_cnt
     print(f"matrix-vector kernels: {mv_cnt} dispatches, average HBM bytes per dispatch {avg / 1e6:.3f} MB")
     if write:

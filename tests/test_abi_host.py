@@ -66,6 +66,12 @@ def test_plan_regimes():
     # prefill down projection: 32 x 4 tiles underfill 256 units -> stream-K over 256 units
     p = qmm.plan_dense(qmm.Q6_K, 4096, 14336, 512)
     assert p["ntiles"] == 128 and p["stream_k"] == 1 and p["units"] == 256 and p["k_iters"] == 56
+    # up projection: 112 x 4 = 448 tiles in two rounds of 256 (87.5 %, below 90 %) -> stream-K
+    p = qmm.plan_dense(qmm.Q4_K, 14336, 4096, 512)
+    assert p["ntiles"] == 448 and p["efficiency_pct"] == 87 and p["stream_k"] == 1 and p["units"] == 256
+    # 2048 tokens: 1792 tiles, exactly seven rounds -> one workgroup per tile
+    p = qmm.plan_dense(qmm.Q4_K, 14336, 4096, 2048)
+    assert p["ntiles"] == 1792 and p["efficiency_pct"] == 100 and p["stream_k"] == 0 and p["units"] == 1792
 
 
 def test_overrides_and_restore():
