@@ -378,6 +378,28 @@ def test_streamk_on_off_agree_and_rerun_is_bitwise():
     assert_close(y_sk.cpu().numpy(), ref, wn, xn, what="stream-K vs oracle")
 
 
+@pytest.mark.parametrize("sk", [0, 1], ids=["streamk-auto", "streamk-off"])
+@pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
+def test_tile_bands_partial_band_ragged_tiles(qtype, sk):
+    """11 row tiles (one full band of 8 and a partial band of 3) x 3 column tiles, the last one
+    ragged, with stream-K splitting tiles (auto) or whole tiles (off); every output checked."""
+    rows, n = 1300, 300
+    k = 544 if qtype == qmm.Q8_0 else 512          # Q8_0: a ragged last 256-value step too
+    p = qmm.plan_dense(qtype, rows, k, n)
+    assert p["tile_j"] == 128 and p["ntiles"] == 33 and p["stream_k"] == 1
+    qmm.set_override(qmm.OVR_STREAMK, sk)
+    _full_check(qtype, rows, k, n, 1400 + qtype + sk, f"{TNAME[qtype]} {rows}x{k} n={n} sk={sk}")
+
+
+@pytest.mark.parametrize("qtype", [qmm.Q4_K, qmm.Q8_0], ids=TNAME.get)
+def test_few_columns_beyond_matvec_k_limit(qtype):
+    """At most 8 columns but K above the matrix-vector kernel's limit: the tiled kernel takes
+    the call (with the tiled activation layout)."""
+    rows, k, n = 40, 32768 + 256, 3
+    assert qmm.plan_dense(qtype, rows, k, n)["regime"] == 2
+    _full_check(qtype, rows, k, n, 1500 + qtype, f"{TNAME[qtype]} {rows}x{k} n={n}")
+
+
 @pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
 def test_forced_regimes_agree(qtype):
     rows, k, n = 520, 1024, 6
