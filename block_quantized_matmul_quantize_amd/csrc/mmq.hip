@@ -69,9 +69,11 @@ template <int T, int J> struct Smem {
     static constexpr int W_OFF = 0;
     static constexpr int WS_OFF = W_OFF + W_BYTES;                               // float [8][128]
     static constexpr int WM_OFF = WS_OFF + 8 * kTI * 4;                          // float [8][128] (Q4_K)
-    static constexpr int A_OFF = WM_OFF + (T == kQ4_K ? 8 * kTI * 4 : 0);      // int8 [J][kLd]
+    static constexpr int WM16_OFF = WM_OFF + (T == kQ4_K ? 8 * kTI * 4 : 0);   // fp16 (hi, lo) [128][8] (Q4_K)
+    static constexpr int A_OFF = WM16_OFF + (T == kQ4_K ? 8 * kTI * 4 : 0);    // int8 [J][kLd]
     static constexpr int X_OFF = A_OFF + J * kLd;                                // float2 [8][J]
-    static constexpr int BYTES = X_OFF + 8 * J * 8;
+    static constexpr int XS16_OFF = X_OFF + 8 * J * 8;                           // fp16 (s, s) [J][8] (Q4_K)
+    static constexpr int BYTES = XS16_OFF + (T == kQ4_K ? 8 * J * 4 : 0);
 };
 
 // Two LDS step buffers where they fit beside the occupancy the tile runs at: Q4_K 8-wave tiles
@@ -127,6 +129,8 @@ template <int J, bool TILED> struct ActFetch {
             *(u32x4 *)(sA + col * kLd + 32 * blk) = c0[it];
             *(u32x4 *)(sA + col * kLd + 32 * blk + 16) = c1[it];
             sX[blk * J + col] = make_float2(h2f((uint16_t)(ds[it] & 0xFFFF)), h2f((uint16_t)(ds[it] >> 16)));
+            if constexpr (T == kQ4_K)   // fp16 s twice: the B operand of the min-term MFMA
+                ((uint32_t *)(sm + Smem<T, J>::XS16_OFF))[col * 8 + blk] = (ds[it] >> 16) | (ds[it] & 0xFFFF0000u);
         }
     }
 };
@@ -169,12 +173,19 @@ template <int NT> struct WFetch<kQ4_K, NT> {
             const uint32_t sc_lo = h.y & 0x3F3F3F3Fu, m_lo = h.z & 0x3F3F3F3Fu;
             const uint32_t sc_hi = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
             const uint32_t m_hi = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
+            uint32_t *sWm16 = (uint32_t *)(sm + Smem<kQ4_K, J>::WM16_OFF) + tid * 8;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const uint32_t scw = j < 4 ? sc_lo : sc_hi, mw = j < 4 ? m_lo : m_hi;
                 const int sh = 8 * (j & 3);
                 sWs[j * kTI + tid] = d * (float)((scw >> sh) & 0xFF);
-                sWm[j * kTI + tid] = -(dmin * (float)((mw >> sh) & 0xFF));
+                const float c = -(dmin * (float)((mw >> sh) & 0xFF));   // exact: <= 17 significant bits
+                sWm[j * kTI + tid] = c;
+                // c = hi + lo exactly in fp16 (lo has <= 6 bits at or above 2^-24) unless |c|
+                // overflows fp16, which leaves hi infinite (the compute falls back to fp32 then)
+                const _Float16 hi = (_Float16)c;
+                const _Float16 lo = (_Float16)(c - (float)hi);
+                sWm16[j] = (uint32_t)__builtin_bit_cast(uint16_t, hi) | ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16);
             }
         }
     }
@@ -413,16 +424,32 @@ __device__ __forceinline__ void tile_step(const uint8_t *sm, f32x16 (&acc)[Cfg<J
             }
         }
         if (!DBG) {
-            // min term: acc += sum over the 8 sub-blocks of (-dmin*m)[row] * s_a[col], as four
-            // K=2 fp32 MFMAs (k = lane/32 selects sub-block 2i+k)
-            const float *sWm = (const float *)(sm + L::WM_OFF);
+            // min term: acc += sum over the 8 sub-blocks of (-dmin*m)[row] * s_a[col].  One
+            // K=16 fp16 MFMA per column block: lane (row, h) holds the (hi, lo) fp16 halves of
+            // the coefficients of sub-blocks 4h..4h+3, the B operand s_a of the same sub-blocks
+            // twice (products exact in fp32).  A wave with a coefficient beyond fp16 range
+            // (dmin > ~1040) takes four K=2 fp32 MFMAs instead.
+            const u32x4 am16 = *(const u32x4 *)(sm + L::WM16_OFF + arow * 32 + 16 * h);
+            const bool inf = ((am16.x & 0x7FFFu) == 0x7C00u) || ((am16.y & 0x7FFFu) == 0x7C00u) ||
+                             ((am16.z & 0x7FFFu) == 0x7C00u) || ((am16.w & 0x7FFFu) == 0x7C00u);
+            if (__builtin_amdgcn_ballot_w64(inf) == 0) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int sb = 2 * i + h;
-                const float am = sWm[sb * kTI + arow];
+                for (int cb = 0; cb < NCB; ++cb) {
+                    const u32x4 bs = *(const u32x4 *)(sm + L::XS16_OFF + (colw + 32 * cb) * 32 + 16 * h);
+                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, am16),
+                                                                    __builtin_bit_cast(f16x8, bs), acc[cb], 0, 0, 0);
+                }
+            } else {
+                const float *sWm = (const float *)(sm + L::WM_OFF);
 #pragma unroll
-                for (int cb = 0; cb < NCB; ++cb)
-                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(am, sX[sb * J + colw + 32 * cb].y, acc[cb], 0, 0, 0);
+                for (int i = 0; i < 4; ++i) {
+                    const int sb = 2 * i + h;
+                    const float am = sWm[sb * kTI + arow];
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb)
+                        acc[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(am, sX[sb * J + colw + 32 * cb].y, acc[cb], 0, 0,
+                                                                       0);
+                }
             }
         }
     } else if constexpr (T == kQ8_0) {

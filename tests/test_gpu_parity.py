@@ -400,6 +400,24 @@ def test_few_columns_beyond_matvec_k_limit(qtype):
     _full_check(qtype, rows, k, n, 1500 + qtype, f"{TNAME[qtype]} {rows}x{k} n={n}")
 
 
+@pytest.mark.parametrize("J", [32, 64, 128])
+def test_q4k_min_term_large_dmin(J):
+    """Q4_K min coefficients -dmin*m near and beyond the fp16 range: rows 64..127 with dmin = 1000
+    (|dmin*m| up to 63000, still fp16) and rows 128..159 with dmin = 60000 (beyond: that wave's
+    min term takes the fp32 path); every output against the oracle."""
+    rows, k, n = 256, 512, 70
+    w, x = _case(qmm.Q4_K, rows, k, n, 1600 + J)
+    blocks = w.reshape(rows, k // 256, 144)
+    blocks[64:128, :, 2:4] = np.frombuffer(np.float16(1000.0).tobytes(), np.uint8)
+    blocks[128:160, :, 2:4] = np.frombuffer(np.float16(60000.0).tobytes(), np.uint8)
+    qmm.set_override(qmm.OVR_TILE_J, J)
+    y = qmm.matmul(to_dev(w), qmm.Q4_K, rows, k, to_dev(x)).cpu().numpy()
+    xq = oracle.quantize_q8_1(x)
+    ref = oracle.matmul_q8_1(qmm.Q4_K, w, rows, k, xq, n)
+    assert np.all(np.isfinite(y))
+    assert_close(y, ref, row_norms(qmm.Q4_K, w, rows, k), col_norms(xq, n, k), what=f"J={J}")
+
+
 @pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
 def test_forced_regimes_agree(qtype):
     rows, k, n = 520, 1024, 6
