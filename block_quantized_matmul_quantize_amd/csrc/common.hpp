@@ -25,7 +25,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x32 __attribute__((ext_vector_type(32)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 // 16-byte vector with only 2-byte alignment guaranteed: Q6_K (210 B) and Q8_0 (34 B) blocks
 // and the q8_1 code arrays sit at 2- or 4-byte offsets.  gfx950 global loads accept these.
 typedef u32x4 __attribute__((aligned(2))) u32x4_a2;

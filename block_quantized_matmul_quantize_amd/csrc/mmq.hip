@@ -31,6 +31,8 @@
 
 namespace qmm {
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
 constexpr int kTI = 128;        // rows per tile
 constexpr int kLd = 272;        // LDS bytes per 256-value row of int8 codes (+16 to spread banks)
 constexpr int kLd4 = 144;       // LDS bytes per row of packed Q4_K qs (128 + 16)
