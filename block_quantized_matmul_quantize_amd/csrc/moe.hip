@@ -10,8 +10,10 @@
 //      rows in thread order, so that (e, t') holds the first output position of thread t''s
 //      pairs of expert e (rows are padded to nthr + 1 entries, so the threads of a wave walking
 //      their rows in step hit distinct LDS banks);
-//   3. each thread walks its chunk again and writes pair indices to their positions, so the
-//      order inside an expert is ascending pair index (token-major, then slot).
+//   3. each thread writes its pair indices to their positions (scanned start of (e, t) plus the
+//      pair's rank from the count pass, kept in registers for chunks up to 64 pairs; longer
+//      chunks walk again with atomics), so the order inside an expert is ascending pair index
+//      (token-major, then slot).
 // It also emits the per-expert dispatch: experts with 1..small_max columns go to the
 // matrix-vector kernel (list `small`), larger ones get ceil(count / tile_j) column tiles whose
 // prefix is tile_start[] (two more block scans).  Ids outside [0, n_exp) are skipped and counted
@@ -24,8 +26,29 @@ namespace qmm {
 constexpr int kGroupThreads = 256;
 constexpr int kGroupTableInts = 36864;   // LDS table: n_exp * row_stride(nthr) <= 36864 (144 KB)
 constexpr int kGroupBatch = 32;          // ids in flight per thread
+constexpr int kGroupKeep = 64;           // chunk length up to which ids and ranks stay in registers
 
 __host__ __device__ constexpr int group_row_stride(int nthr) { return nthr == 1 ? 1 : nthr + 1; }
+
+// ids [p0, p0 + kGroupBatch) of a chunk ending at hi into ev (-1 past hi): 16-byte loads where
+// the ids are 16-byte aligned (chunks start at multiples of 4 pairs), single ids otherwise.
+__device__ __forceinline__ void load_ids(const int32_t *ids, int64_t p0, int64_t hi, bool vec,
+                                         int32_t (&ev)[kGroupBatch]) {
+#pragma unroll
+    for (int v = 0; v < kGroupBatch / 4; ++v) {
+        const int64_t q = p0 + 4 * v;
+        if (vec && q + 4 <= hi) {
+            const u32x4 w = *(const u32x4 *)(ids + q);
+            ev[4 * v] = (int32_t)w.x;
+            ev[4 * v + 1] = (int32_t)w.y;
+            ev[4 * v + 2] = (int32_t)w.z;
+            ev[4 * v + 3] = (int32_t)w.w;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ev[4 * v + i] = q + i < hi ? ids[q + i] : -1;
+        }
+    }
+}
 
 // Exclusive scan of one value per thread over the workgroup (Hillis-Steele in LDS); returns the
 // thread's exclusive prefix and writes the total to *total.  buf: 2 * kGroupThreads ints.
@@ -54,31 +77,59 @@ __global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(const int32_t 
                                                                   int32_t *__restrict__ tile_start,
                                                                   int32_t *__restrict__ small,
                                                                   int32_t *__restrict__ invalid) {
-    __shared__ int32_t tab[kGroupTableInts];
+    __shared__ __align__(16) int32_t tab[kGroupTableInts];
     __shared__ int32_t sbuf[2 * kGroupThreads];
     __shared__ int32_t bad_sh;
     const int t = threadIdx.x;
     const int rs = group_row_stride(nthr);
     const bool active = t < nthr;
-    const int64_t chunk = (pairs + nthr - 1) / nthr;
-    const int64_t lo = active ? (int64_t)t * chunk : 0;
-    const int64_t hi = active ? (lo + chunk < pairs ? lo + chunk : pairs) : 0;
+    const int64_t chunk = ((pairs + nthr - 1) / nthr + 3) & ~(int64_t)3;   // a multiple of 4 pairs
+    const bool vec = (((uintptr_t)ids) & 15) == 0;
+    const int64_t lo0 = (int64_t)t * chunk;
+    const bool has = active && lo0 < pairs;                  // threads past the last chunk count nothing
+    const int64_t lo = has ? lo0 : 0, hi = has ? (lo0 + chunk < pairs ? lo0 + chunk : pairs) : 0;
     const int ce = (n_exp + kGroupThreads - 1) / kGroupThreads;
     const int e0 = t * ce < n_exp ? t * ce : n_exp, e1 = e0 + ce < n_exp ? e0 + ce : n_exp;
 
     if (t == 0) bad_sh = 0;
-    for (int i = t; i < n_exp * rs; i += kGroupThreads) tab[i] = 0;
+    {   // zero the table, 16 bytes per store (kGroupTableInts is a multiple of 4 * kGroupThreads)
+        u32x4 *tab4 = (u32x4 *)tab;
+        const int n4 = (n_exp * rs + 3) / 4;
+        for (int i = t; i < n4; i += kGroupThreads) tab4[i] = u32x4{0u, 0u, 0u, 0u};
+    }
     __syncthreads();
     int bad = 0;
-    for (int64_t p0 = lo; p0 < hi; p0 += kGroupBatch) {
-        int32_t ev[kGroupBatch];
+    // Chunks of at most kGroupKeep pairs (every chunk of the call: the chunk length is uniform)
+    // keep their ids and their ranks inside (expert, thread) in registers, so the scatter needs
+    // neither a second read of the ids nor a second atomic per pair.
+    const bool keep = chunk <= kGroupKeep;
+    int32_t kid[kGroupKeep], krank[kGroupKeep];
+    if (keep) {
 #pragma unroll
-        for (int j = 0; j < kGroupBatch; ++j) ev[j] = p0 + j < hi ? ids[p0 + j] : -1;
+        for (int b = 0; b < kGroupKeep / kGroupBatch; ++b) {
+            const int64_t p0 = lo + b * kGroupBatch;
+            int32_t ev[kGroupBatch];
+            load_ids(ids, p0, hi, vec, ev);
 #pragma unroll
-        for (int j = 0; j < kGroupBatch; ++j) {
-            const int32_t e = ev[j];
-            if (e >= 0 && e < n_exp) atomicAdd(&tab[e * rs + t], 1);
-            else if (p0 + j < hi) bad++;
+            for (int j = 0; j < kGroupBatch; ++j) {
+                const int32_t e = ev[j];
+                kid[b * kGroupBatch + j] = e;
+                // out-of-range ids (and the -1 past the chunk) skip the table; only real ones
+                // count as bad
+                krank[b * kGroupBatch + j] = (uint32_t)e < (uint32_t)n_exp ? atomicAdd(&tab[e * rs + t], 1) : 0;
+                if ((uint32_t)e >= (uint32_t)n_exp) bad += p0 + j < hi ? 1 : 0;
+            }
+        }
+    } else {
+        for (int64_t p0 = lo; p0 < hi; p0 += kGroupBatch) {
+            int32_t ev[kGroupBatch];
+            load_ids(ids, p0, hi, vec, ev);
+#pragma unroll
+            for (int j = 0; j < kGroupBatch; ++j) {
+                const int32_t e = ev[j];
+                if ((uint32_t)e < (uint32_t)n_exp) atomicAdd(&tab[e * rs + t], 1);
+                else bad += p0 + j < hi ? 1 : 0;
+            }
         }
     }
     if (bad) atomicAdd(&bad_sh, bad);
@@ -147,16 +198,29 @@ __global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(const int32_t 
         invalid[0] = bad_sh;
     }
     __syncthreads();
-    // scatter; each thread advances only its own column, in pair order
+    // scatter: position = the (expert, thread) start from the scan + the pair's rank there
+    if (keep) {
+#pragma unroll
+        for (int j = 0; j < kGroupKeep; ++j) {
+            const int32_t e = kid[j];
+            if ((uint32_t)e < (uint32_t)n_exp) sorted[tab[e * rs + t] + krank[j]] = (int32_t)(lo + j);
+        }
+        return;
+    }
+    // longer chunks: each thread advances its own column, in pair order
     for (int64_t p0 = lo; p0 < hi; p0 += kGroupBatch) {
         int32_t ev[kGroupBatch];
-#pragma unroll
-        for (int j = 0; j < kGroupBatch; ++j) ev[j] = p0 + j < hi ? ids[p0 + j] : -1;
+        load_ids(ids, p0, hi, vec, ev);
+        // positions first (LDS atomics in pair order on the thread's own column), then the stores
+        int32_t pos[kGroupBatch];
 #pragma unroll
         for (int j = 0; j < kGroupBatch; ++j) {
             const int32_t e = ev[j];
-            if (e >= 0 && e < n_exp) sorted[atomicAdd(&tab[e * rs + t], 1)] = (int32_t)(p0 + j);
+            pos[j] = (uint32_t)e < (uint32_t)n_exp ? atomicAdd(&tab[e * rs + t], 1) : -1;
         }
+#pragma unroll
+        for (int j = 0; j < kGroupBatch; ++j)
+            if (pos[j] >= 0) sorted[pos[j]] = (int32_t)(p0 + j);
     }
 }
 

@@ -567,7 +567,8 @@ def _grouping_ref(ids, n_exp, tile_j, small_max):
 
 
 @pytest.mark.parametrize("n_exp,n_tok,top_k,zipf", [(8, 512, 2, 1.1), (128, 2048, 8, 1.0), (6, 37, 3, 0.0),
-                                                     (1000, 333, 4, 0.8), (5000, 50, 2, 0.0)])
+                                                     (1000, 333, 4, 0.8), (5000, 50, 2, 0.0),
+                                                     (128, 5000, 8, 1.0)])   # chunks over 64 pairs
 def test_moe_grouping_is_a_stable_counting_sort(n_exp, n_tok, top_k, zipf):
     """The device grouping pass (index work: bit-exact) against a host stable sort, including
     invalid ids, ragged per-thread chunks and expert counts that shrink the per-thread table."""
