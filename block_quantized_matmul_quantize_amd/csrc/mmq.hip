@@ -3,16 +3,20 @@
 //
 // CDNA4 design.  A workgroup of 4 waves (8 for J = 128) owns a 128-row x J-column output tile
 // (J = 32/64/128) and walks K in 256-value steps.  Each step's weight and activation tiles are
-// fetched from HBM into registers while the previous step computes (software pipelining: the
-// loads of step kb+1 are issued right after step kb is parked in LDS), then parked in LDS: Q4_K as packed qs
-// bytes plus fp32 per-(row, sub-block) scales d*sc and mins -dmin*m, Q8_0 as int8 codes plus
-// fp32 d, Q6_K unpacked (below); activations as int8 codes plus fp32 (d, s) per 32-value block
-// (the MMQ page's "why not dequantize": stay quantized and reuse each unpacked tile for J
-// columns).  Each wave owns 32 rows; per 32-value block it runs one v_mfma_i32_32x32x32_i8 per
-// 32 columns -- K = 32 is exactly one q8_1 block, so every int32 result is one exact sub-block
-// dot D -- and folds it into its fp32 accumulators with one multiply-add:
+// fetched from HBM into registers while an earlier step computes (software pipelining: the loads
+// of the next step are issued right after a step is parked in LDS; Q4_K 8-wave tiles keep two
+// LDS step buffers and fetch two steps ahead), then parked in LDS: Q4_K as packed qs bytes plus
+// per-(row, sub-block) scales d*sc and mins -dmin*m (fp32, and the mins also as exact fp16
+// hi/lo pairs), Q8_0 as int8 codes plus fp32 d, Q6_K unpacked (below); activations, read from
+// the step-tiled q8_1 layout, as int8 codes plus fp32 (d, s) per 32-value block (the MMQ page's
+// "why not dequantize": stay quantized and reuse each unpacked tile for J columns).  Each wave
+// owns 32 rows; per 32-value block it runs one v_mfma_i32_32x32x32_i8 per 32 columns -- K = 32
+// is exactly one q8_1 block, so every int32 result is one exact sub-block dot D -- and folds it
+// into its fp32 accumulators with one multiply-add, the per-element scale coming from an
+// outer-product MFMA:
 //   Q4_K  acc += D * (d*sc * d_a);  the min term -(dmin*m) * s_a is a rank-8 product per step,
-//         done as four v_mfma_f32_32x32x2_f32 into the same accumulators
+//         one v_mfma_f32_32x32x16_f16 per column block (four K=2 fp32 MFMAs where the
+//         coefficients leave fp16 range)
 //   Q8_0  acc += D * (d_w * d_a)
 //   Q6_K  acc += (sc0*D0 + sc1*D1) * (d * d_a)
 // Q6_K changes scale every 16 values, so its int8 scale is folded into the codes at unpack time:
@@ -23,7 +27,8 @@
 // [u*W/units, (u+1)*W/units).  A unit that covers a whole tile writes it to y; a partial tile
 // goes to the unit's slot (0: its first tile, 1: its last) and the fixup kernel adds the slots
 // of a split tile in ascending unit order (deterministic, no atomics).  Without stream-K,
-// units == ntiles and every unit is exactly one tile.
+// units == ntiles and every unit is exactly one tile.  Tiles are numbered in bands of 8 row
+// tiles walked column by column (tile_coords), units are contiguous per XCD.
 #include <type_traits>
 
 #include "common.hpp"
@@ -354,8 +359,8 @@ template <int NT> struct WFetch<kQ6_K, NT> : std::conditional<(NT >= 512), WFetc
 // rw = wid % 4 (rows 32*rw..), column wave cw = wid / 4 (columns JW*cw..).  Accumulator block cb,
 // element e of lane l: row 32*rw + 8*(e/4) + 4*(l/32) + e%4, column JW*cw + 32*cb + l%32.
 // The per-element scale w_scale[row] * d_a[col] of a 32x32 block is their outer product, made
-// on the matrix pipe, so the vector ALU does two operations per result: int->float and a
-// multiply-add.
+// on the matrix pipe, so the vector ALU does two operations per result: int->float (Q4_K: an
+// exact subtraction, see BIAS below) and a multiply-add.
 // ---------------------------------------------------------------------------------------------
 template <int T, int J, bool DBG>
 __device__ __forceinline__ void tile_step(const uint8_t *sm, f32x16 (&acc)[Cfg<J>::NCB], int64_t kb, int64_t nb32,
