@@ -492,15 +492,12 @@ __device__ __forceinline__ void tile_step(const uint8_t *sm, f32x16 (&acc)[Cfg<J
                 fix(cb, j, mfma32x32x32(a, b, cinit), S[cb]);
             }
         }
-    } else {
+    } else if constexpr (DBG) {
         const int8_t *sW = (const int8_t *)(sm + L::W_OFF);
-        const float d6 = sWs[arow];
 #pragma unroll 1
         for (int j = 0; j < 8; ++j) {
             const u32x4 a = *(const u32x4 *)(sW + arow * kLd + 32 * j + koff);
             const u32x4 a_hi = *(const u32x4 *)(sW + kTI * kLd + arow * kLd + 32 * j + koff);
-            f32x16 S[NCB];
-            if (!DBG) scales(j, d6, S);
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
                 const u32x4 b = *(const u32x4 *)(sA + (colw + 32 * cb) * kLd + 32 * j + koff);
@@ -508,8 +505,40 @@ __device__ __forceinline__ void tile_step(const uint8_t *sm, f32x16 (&acc)[Cfg<J
                 const i32x16 Dh = mfma32x32x32(a_hi, b, zero);
 #pragma unroll
                 for (int e = 0; e < 16; ++e) D[e] = (Dh[e] << 7) + D[e];
-                fix(cb, j, D, S[cb]);
+                fix(cb, j, D, f32x16{});
             }
+        }
+    } else {
+        // Q6_K: the weight scale d is one per row for the whole step and every accumulator
+        // element of a lane is in the lane's column, so the per-element scale factors as
+        // d[row] * d_a[col]: T += D * d_a with d_a a per-lane scalar, then acc += d[row] * T once
+        // per step (no scale-product MFMAs).
+        const int8_t *sW = (const int8_t *)(sm + L::W_OFF);
+        f32x16 Tc[NCB];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) Tc[cb] = fzero;
+#pragma unroll 1
+        for (int j = 0; j < 8; ++j) {
+            const u32x4 a = *(const u32x4 *)(sW + arow * kLd + 32 * j + koff);
+            const u32x4 a_hi = *(const u32x4 *)(sW + kTI * kLd + arow * kLd + 32 * j + koff);
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                const u32x4 b = *(const u32x4 *)(sA + (colw + 32 * cb) * kLd + 32 * j + koff);
+                const float da = sX[j * J + colw + 32 * cb].x;
+                const i32x16 D = mfma32x32x32(a, b, zero);
+                const i32x16 Dh = mfma32x32x32(a_hi, b, zero);
+#pragma unroll
+                for (int e = 0; e < 16; ++e) Tc[cb][e] = fmaf((float)((Dh[e] << 7) + D[e]), da, Tc[cb][e]);
+            }
+        }
+        // row scales of the lane's elements: rows 32*rw + 8*q + 4*h + (0..3), q = e/4
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f32x4 dr = *(const f32x4 *)(sWs + 32 * rw + 8 * q + 4 * h);
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[cb][4 * q + i] = fmaf(dr[i], Tc[cb][4 * q + i], acc[cb][4 * q + i]);
         }
     }
 }
