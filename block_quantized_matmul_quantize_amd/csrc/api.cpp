@@ -426,13 +426,17 @@ IdWs id_layout(int64_t n_exp, int64_t k, int64_t n_tok, int64_t top_k, int64_t x
 int id_tile_j(int type, int64_t pairs, int64_t n_exp) {
     const int ov = g_ovr_tile_j.load();
     if (ov) return ov;
-    // The MMQ page's "MoE skew": per-expert column counts are skewed and mostly far below the
-    // call's total, so the tile width follows the mean columns per expert, not the total
-    // (measured on the MoE shapes: 32/64-column tiles beat 128 by 10-20 % for Q4_K).  Q6_K
-    // keeps 128: its 4-wave tiles hold the unpacked planes and run one workgroup per CU.
+    // The MMQ page's "MoE skew": per-expert column counts are skewed, so the tile width follows
+    // the columns of a typical expert, not the call's total: the mean for a few experts, half the
+    // mean for many (a handful of hot experts then hold most columns; on the Zipf MoE shapes the
+    // median expert has 0.7x the mean with 8 experts, 0.4x with 128), then the smallest tile that
+    // covers it.  Measured: 8 experts x 128 mean columns 128-column tiles best, 128 experts x 128
+    // mean 64-column tiles best.  Q6_K keeps 128: its 4-wave tiles hold the unpacked planes and
+    // run one workgroup per CU.
     if (type == QMM_Q6_K) return 128;
     const int64_t mean = pairs / (n_exp > 0 ? n_exp : 1);
-    return mean >= 256 ? 128 : (mean >= 48 ? 64 : 32);
+    const int64_t typical = n_exp > 16 ? mean / 2 : mean;
+    return typical > 64 ? 128 : (typical > 32 ? 64 : 32);
 }
 
 }  // namespace

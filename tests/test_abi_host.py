@@ -209,12 +209,14 @@ def test_matvec_kernel_choice_follows_alignment_and_overrides():
 
 @pytest.mark.parametrize("qtype,n_exp,n_tok,top_k,J", [
     (qmm.Q6_K, 128, 2048, 8, 128),     # Q6_K keeps 128-column tiles
-    (qmm.Q4_K, 128, 2048, 8, 64),      # mean 128 columns per expert
-    (qmm.Q4_K, 8, 512, 2, 64),
+    (qmm.Q4_K, 128, 2048, 8, 64),      # many experts: typical = mean/2 = 64
+    (qmm.Q4_K, 8, 512, 2, 128),        # few experts: typical = mean = 128
+    (qmm.Q4_K, 16, 384, 2, 64),        # mean 48
+    (qmm.Q4_K, 32, 1024, 2, 32),       # mean 64, typical 32
     (qmm.Q8_0, 64, 100, 4, 32),        # mean 6
     (qmm.Q4_K, 4, 1024, 2, 128),       # mean 512
 ])
-def test_expert_tile_width_follows_mean_columns_per_expert(qtype, n_exp, n_tok, top_k, J):
+def test_expert_tile_width_follows_typical_columns_per_expert(qtype, n_exp, n_tok, top_k, J):
     lay = qmm.matmul_id_layout(qtype, n_exp, 2048, n_tok, top_k, 1)
     assert lay[4] == J
     assert lay[5] == 8                                     # experts of <= 8 columns: matrix-vector
