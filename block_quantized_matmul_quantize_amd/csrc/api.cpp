@@ -88,8 +88,8 @@ qmm_status check_common(int type, int64_t rows, int64_t k, int64_t n) {
 // scales (and Q4_K mins), activation codes, fp32 (d, s).
 int mmq_smem(int type, int J) {
     const int wt = type == QMM_Q4_K ? kTI * 144 : (type == QMM_Q6_K ? 2 * kTI * 272 : kTI * 272);
-    const int wm = type == QMM_Q4_K ? 2 * 8 * kTI * 4 + 8 * J * 4 : 0;   // fp32 and fp16 mins, fp16 s
-    const int one = wt + 8 * kTI * 4 + wm + J * 272 + 8 * J * 8;
+    const int wm = type == QMM_Q4_K ? kTI * 48 + 8 * J * 4 : 0;   // bf16 pieces of the mins and of s
+    const int one = wt + 8 * kTI * 4 + wm + J * 272 + 8 * (J + 4) * 8;
     return type == QMM_Q4_K && J == 128 ? 2 * one : one;             // Q4_K 8-wave tiles: two step buffers
 }
 

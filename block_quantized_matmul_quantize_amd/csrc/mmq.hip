@@ -36,7 +36,10 @@
 
 namespace qmm {
 
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint32_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+__device__ __forceinline__ float bf16_val(uint32_t b) { return __builtin_bit_cast(float, b << 16); }
 
 constexpr int kTI = 128;        // rows per tile
 constexpr int kLd = 272;        // LDS bytes per 256-value row of int8 codes (+16 to spread banks)
@@ -75,12 +78,13 @@ template <int T, int J> struct Smem {
     static constexpr int W_BYTES = T == kQ4_K ? kTI * kLd4 : (T == kQ6_K ? 2 * kTI * kLd : kTI * kLd);
     static constexpr int W_OFF = 0;
     static constexpr int WS_OFF = W_OFF + W_BYTES;                               // float [8][128]
-    static constexpr int WM_OFF = WS_OFF + 8 * kTI * 4;                          // float [8][128] (Q4_K)
-    static constexpr int WM16_OFF = WM_OFF + (T == kQ4_K ? 8 * kTI * 4 : 0);   // fp16 (hi, lo) [128][8] (Q4_K)
-    static constexpr int A_OFF = WM16_OFF + (T == kQ4_K ? 8 * kTI * 4 : 0);    // int8 [J][kLd]
-    static constexpr int X_OFF = A_OFF + J * kLd;                                // float2 [8][J]
-    static constexpr int XS16_OFF = X_OFF + 8 * J * 8;                           // fp16 (s, s) [J][8] (Q4_K)
-    static constexpr int BYTES = XS16_OFF + (T == kQ4_K ? 8 * J * 4 : 0);
+    static constexpr int WM_OFF = WS_OFF + 8 * kTI * 4;                          // Q4_K: bf16 pieces of -dmin*m,
+    static constexpr int A_OFF = WM_OFF + (T == kQ4_K ? kTI * 48 : 0);          // [128][half][piece][4]; int8 [J][kLd]
+    static constexpr int XS = J + 4;                                             // (d, s) row stride: the
+    static constexpr int X_OFF = A_OFF + J * kLd;                                // float2 [8][XS] (8 blocks of a
+    static constexpr int XB_OFF = X_OFF + 8 * XS * 8;                            // column land in 2-way banks)
+                                                                                 // then bf16 pieces of s [J][8] (Q4_K)
+    static constexpr int BYTES = XB_OFF + (T == kQ4_K ? 8 * J * 4 : 0);
 };
 
 // Two LDS step buffers where they fit beside the occupancy the tile runs at: Q4_K 8-wave tiles
@@ -92,9 +96,11 @@ template <int T, int J> constexpr int kSmemBytes = (kDoubleBuffer<T, J> ? 2 : 1)
 // Activation tile: J columns of the step's 8 q8_1 blocks.  Thread tid owns (column, block) pairs
 // i = tid + NT*it: column i/8, block i%8.  TILED: the tiled layout (launch.hpp), where the 8
 // consecutive threads of a column read its 256 code bytes and 8 (d, s) pairs with aligned loads;
-// otherwise canonical 36-byte blocks (the debug export reads those).
+// otherwise canonical 36-byte blocks (the debug export reads those).  acol always names a valid
+// activation row (tile columns past the end repeat a valid one and are never written out), so the
+// loads need no predicate; RAGGED (Q8_0, K a multiple of 32 only): blocks past K read as zero.
 // ---------------------------------------------------------------------------------------------
-template <int J, bool TILED> struct ActFetch {
+template <int J, bool TILED, bool RAGGED> struct ActFetch {
     static constexpr int NT = Cfg<J>::NT, N = J * 8 / NT;
     uint32_t ds[N];   // fp16 d | fp16 s << 16
     u32x4 c0[N], c1[N];
@@ -105,10 +111,12 @@ template <int J, bool TILED> struct ActFetch {
         for (int it = 0; it < N; ++it) {
             const int blk = (tid + NT * it) & 7;
             const int64_t b = kb * 8 + blk;
-            ds[it] = 0u;
-            c0[it] = u32x4{0u, 0u, 0u, 0u};
-            c1[it] = c0[it];
-            if (acol[it] >= 0 && b < nb32) {
+            if (RAGGED) {
+                ds[it] = 0u;
+                c0[it] = u32x4{0u, 0u, 0u, 0u};
+                c1[it] = c0[it];
+            }
+            if (!RAGGED || b < nb32) {
                 if constexpr (TILED) {
                     const int64_t slot = kb * act_rows + acol[it];
                     const uint8_t *src = xq + slot * 256 + 32 * blk;
@@ -135,9 +143,12 @@ template <int J, bool TILED> struct ActFetch {
             const int col = i >> 3, blk = i & 7;
             *(u32x4 *)(sA + col * kLd + 32 * blk) = c0[it];
             *(u32x4 *)(sA + col * kLd + 32 * blk + 16) = c1[it];
-            sX[blk * J + col] = make_float2(h2f((uint16_t)(ds[it] & 0xFFFF)), h2f((uint16_t)(ds[it] >> 16)));
-            if constexpr (T == kQ4_K)   // fp16 s twice: the B operand of the min-term MFMA
-                ((uint32_t *)(sm + Smem<T, J>::XS16_OFF))[col * 8 + blk] = (ds[it] >> 16) | (ds[it] & 0xFFFF0000u);
+            sX[blk * Smem<T, J>::XS + col] = make_float2(h2f((uint16_t)(ds[it] & 0xFFFF)), h2f((uint16_t)(ds[it] >> 16)));
+            if constexpr (T == kQ4_K) {   // s = t1 + t2 exactly in bf16: the B operand of the min term
+                const float sf = h2f((uint16_t)(ds[it] >> 16));
+                const uint32_t t1 = bf16_bits(sf);
+                ((uint32_t *)(sm + Smem<T, J>::XB_OFF))[col * 8 + blk] = t1 | (bf16_bits(sf - bf16_val(t1)) << 16);
+            }
         }
     }
 };
@@ -147,7 +158,8 @@ template <int J, bool TILED> struct ActFetch {
 // ---------------------------------------------------------------------------------------------
 template <int T, int NT> struct WFetch;
 
-// Q4_K: qs pieces (row i/8, 16-byte piece i%8 of the 128 qs bytes) and the row headers.
+// Q4_K: qs pieces (row i/8, 16-byte piece i%8 of the 128 qs bytes) and the row headers (threads
+// below 128, whole waves).
 template <int NT> struct WFetch<kQ4_K, NT> {
     static constexpr int N = 1024 / NT;
     u32x4 q[N], h;
@@ -157,11 +169,10 @@ template <int NT> struct WFetch<kQ4_K, NT> {
 #pragma unroll
         for (int it = 0; it < N; ++it) {
             const int i = tid + NT * it;
-            const int64_t row = r0 + (i >> 3);
-            q[it] = row < rows ? ld16(wbase + row * row_bytes + kb * 144 + 16 + 16 * (i & 7)) : u32x4{0u, 0u, 0u, 0u};
+            const int64_t row = r0 + (i >> 3) < rows ? r0 + (i >> 3) : rows - 1;   // ragged tile: the last row
+            q[it] = ld16(wbase + row * row_bytes + kb * 144 + 16 + 16 * (i & 7));
         }
-        h = u32x4{0u, 0u, 0u, 0u};
-        if (tid < kTI && r0 + tid < rows) h = ld16(wbase + (r0 + tid) * row_bytes + kb * 144);
+        if (tid < kTI) h = ld16(wbase + (r0 + tid < rows ? r0 + tid : rows - 1) * row_bytes + kb * 144);
     }
     template <int J>
     __device__ __forceinline__ void store(uint8_t *sm, const uint8_t *, int64_t, int64_t, int64_t, int64_t,
@@ -175,25 +186,37 @@ template <int NT> struct WFetch<kQ4_K, NT> {
         }
         if (tid < kTI) {
             float *sWs = (float *)(sm + Smem<kQ4_K, J>::WS_OFF);
-            float *sWm = (float *)(sm + Smem<kQ4_K, J>::WM_OFF);
             const float d = h2f((uint16_t)(h.x & 0xFFFF)), dmin = h2f((uint16_t)(h.x >> 16));
             const uint32_t sc_lo = h.y & 0x3F3F3F3Fu, m_lo = h.z & 0x3F3F3F3Fu;
             const uint32_t sc_hi = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
             const uint32_t m_hi = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
-            uint32_t *sWm16 = (uint32_t *)(sm + Smem<kQ4_K, J>::WM16_OFF) + tid * 8;
+            // c = -dmin*m has at most 17 significant bits (exact in fp32) and splits exactly into
+            // three bf16 pieces p0 + p1 + p2 (8 + 8 + 1 bits), with fp32's exponent range
+            uint32_t pc[3][8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const uint32_t scw = j < 4 ? sc_lo : sc_hi, mw = j < 4 ? m_lo : m_hi;
                 const int sh = 8 * (j & 3);
                 sWs[j * kTI + tid] = d * (float)((scw >> sh) & 0xFF);
-                const float c = -(dmin * (float)((mw >> sh) & 0xFF));   // exact: <= 17 significant bits
-                sWm[j * kTI + tid] = c;
-                // c = hi + lo exactly in fp16 (lo has <= 6 bits at or above 2^-24) unless |c|
-                // overflows fp16, which leaves hi infinite (the compute falls back to fp32 then)
-                const _Float16 hi = (_Float16)c;
-                const _Float16 lo = (_Float16)(c - (float)hi);
-                sWm16[j] = (uint32_t)__builtin_bit_cast(uint16_t, hi) | ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16);
+                const float c = -(dmin * (float)((mw >> sh) & 0xFF));
+                pc[0][j] = bf16_bits(c);
+                const float r = c - bf16_val(pc[0][j]);
+                pc[1][j] = bf16_bits(r);
+                pc[2][j] = bf16_bits(r - bf16_val(pc[1][j]));
             }
+            // row layout [half][piece][4 sub-blocks]: the 24 bytes a lane of a half reads
+            uint32_t wv[12];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int m = 0; m < 3; ++m) {
+                    wv[6 * hf + 2 * m] = pc[m][4 * hf] | (pc[m][4 * hf + 1] << 16);
+                    wv[6 * hf + 2 * m + 1] = pc[m][4 * hf + 2] | (pc[m][4 * hf + 3] << 16);
+                }
+            u32x4 *dst = (u32x4 *)(sm + Smem<kQ4_K, J>::WM_OFF + tid * 48);
+            dst[0] = u32x4{wv[0], wv[1], wv[2], wv[3]};
+            dst[1] = u32x4{wv[4], wv[5], wv[6], wv[7]};
+            dst[2] = u32x4{wv[8], wv[9], wv[10], wv[11]};
         }
     }
 };
@@ -362,9 +385,20 @@ template <int NT> struct WFetch<kQ6_K, NT> : std::conditional<(NT >= 512), WFetc
 // on the matrix pipe, so the vector ALU does two operations per result: int->float (Q4_K: an
 // exact subtraction, see BIAS below) and a multiply-add.
 // ---------------------------------------------------------------------------------------------
+// Q4_K dots satisfy |D| <= 32 * 15 * 127 < 2^22, so an integer MFMA whose accumulator starts at
+// the bits of 1.5 * 2^23 (cinit) returns the float 1.5 * 2^23 + D exactly and one exact
+// subtraction recovers D (cheaper on the vector ALU than the int -> float conversion: ~9 % of the
+// Q4_K tile time).  The tile loop builds the seed once and makes it opaque, so that it stays in
+// registers instead of being rebuilt every step.  Q8_0 would qualify too but its tiles run out of
+// registers with the 16 seed registers; Q6_K's scale-folded dots can exceed the range.
+template <int T, bool DBG> constexpr bool kSeeded = !DBG && T == kQ4_K;
+constexpr int32_t kBiasBits = 0x4B400000;
+constexpr float kBias = 12582912.0f;   // 1.5 * 2^23
+
 template <int T, int J, bool DBG>
-__device__ __forceinline__ void tile_step(const uint8_t *sm, f32x16 (&acc)[Cfg<J>::NCB], int64_t kb, int64_t nb32,
-                                          int32_t *dbg, int64_t rows, int64_t n, int64_t r0, int64_t c0) {
+__device__ __forceinline__ void tile_step(const uint8_t *sm, f32x16 (&acc)[Cfg<J>::NCB], const i32x16 &cinit,
+                                          int64_t kb, int64_t nb32, int32_t *dbg, int64_t rows, int64_t n, int64_t r0,
+                                          int64_t c0) {
     using L = Smem<T, J>;
     constexpr int NCB = Cfg<J>::NCB, JW = Cfg<J>::JW;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -384,7 +418,7 @@ __device__ __forceinline__ void tile_step(const uint8_t *sm, f32x16 (&acc)[Cfg<J
     // columns); a single block from v_mfma_f32_32x32x2_f32 with the second K slot zero.
     auto scales = [&](int sb, float wsr, f32x16 (&S)[NCB]) {
         if constexpr (NCB == 2) {
-            const float da = sX[sb * J + JW * cw + 32 * h + (lane & 31)].x;
+            const float da = sX[sb * L::XS + JW * cw + 32 * h + (lane & 31)].x;
             const f32x32 S2 = __builtin_amdgcn_mfma_f32_32x32x1f32(wsr, da, f32x32{}, 0, 0, 0);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
@@ -392,26 +426,12 @@ __device__ __forceinline__ void tile_step(const uint8_t *sm, f32x16 (&acc)[Cfg<J
                 S[1][e] = S2[16 + e];
             }
         } else {
-            const float da = h ? 0.f : sX[sb * J + colw].x;
+            const float da = h ? 0.f : sX[sb * L::XS + colw].x;
             S[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(h ? 0.f : wsr, da, fzero, 0, 0, 0);
         }
     };
     // D of block (sb, cb) folded into the accumulators with its scales (or exported raw)
-    // Q4_K dots satisfy |D| <= 32 * 15 * 127 < 2^22, so an integer MFMA whose accumulator
-    // starts at the bits of 1.5 * 2^23 returns the float 1.5 * 2^23 + D exactly and one exact
-    // subtraction recovers D (cheaper on the vector ALU than the int -> float conversion: ~9 %
-    // of the Q4_K tile time).  The seed is made opaque so that it stays in registers instead of
-    // being rebuilt every block.  Q8_0 would qualify too but its tiles run out of registers with
-    // the 16 seed registers; Q6_K's scale-folded dots can exceed the range.
-    constexpr bool BIAS = !DBG && T == kQ4_K;
-    constexpr int32_t kBiasBits = 0x4B400000;
-    constexpr float kBias = 12582912.0f;   // 1.5 * 2^23
-    i32x16 cinit = zero;
-    if constexpr (BIAS) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) cinit[e] = kBiasBits;
-        asm volatile("" : "+v"(cinit));
-    }
+    constexpr bool BIAS = kSeeded<T, DBG>;
     auto fix = [&](int cb, int sb, const i32x16 &D, const f32x16 &S) {
         const int bcol = colw + 32 * cb;
         if (DBG) {
@@ -447,35 +467,6 @@ __device__ __forceinline__ void tile_step(const uint8_t *sm, f32x16 (&acc)[Cfg<J
             for (int cb = 0; cb < NCB; ++cb) {
                 const u32x4 b = *(const u32x4 *)(sA + (colw + 32 * cb) * kLd + 32 * sb + koff);
                 fix(cb, sb, mfma32x32x32(aop, b, cinit), S[cb]);
-            }
-        }
-        if (!DBG) {
-            // min term: acc += sum over the 8 sub-blocks of (-dmin*m)[row] * s_a[col].  One
-            // K=16 fp16 MFMA per column block: lane (row, h) holds the (hi, lo) fp16 halves of
-            // the coefficients of sub-blocks 4h..4h+3, the B operand s_a of the same sub-blocks
-            // twice (products exact in fp32).  A wave with a coefficient beyond fp16 range
-            // (dmin > ~1040) takes four K=2 fp32 MFMAs instead.
-            const u32x4 am16 = *(const u32x4 *)(sm + L::WM16_OFF + arow * 32 + 16 * h);
-            const bool inf = ((am16.x & 0x7FFFu) == 0x7C00u) || ((am16.y & 0x7FFFu) == 0x7C00u) ||
-                             ((am16.z & 0x7FFFu) == 0x7C00u) || ((am16.w & 0x7FFFu) == 0x7C00u);
-            if (__builtin_amdgcn_ballot_w64(inf) == 0) {
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) {
-                    const u32x4 bs = *(const u32x4 *)(sm + L::XS16_OFF + (colw + 32 * cb) * 32 + 16 * h);
-                    acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, am16),
-                                                                    __builtin_bit_cast(f16x8, bs), acc[cb], 0, 0, 0);
-                }
-            } else {
-                const float *sWm = (const float *)(sm + L::WM_OFF);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int sb = 2 * i + h;
-                    const float am = sWm[sb * kTI + arow];
-#pragma unroll
-                    for (int cb = 0; cb < NCB; ++cb)
-                        acc[cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(am, sX[sb * J + colw + 32 * cb].y, acc[cb], 0, 0,
-                                                                       0);
-                }
             }
         }
     } else if constexpr (T == kQ8_0) {
@@ -524,7 +515,7 @@ __device__ __forceinline__ void tile_step(const uint8_t *sm, f32x16 (&acc)[Cfg<J
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
                 const u32x4 b = *(const u32x4 *)(sA + (colw + 32 * cb) * kLd + 32 * j + koff);
-                const float da = sX[j * J + colw + 32 * cb].x;
+                const float da = sX[j * L::XS + colw + 32 * cb].x;
                 const i32x16 D = mfma32x32x32(a, b, zero);
                 const i32x16 Dh = mfma32x32x32(a_hi, b, zero);
 #pragma unroll
@@ -543,29 +534,58 @@ __device__ __forceinline__ void tile_step(const uint8_t *sm, f32x16 (&acc)[Cfg<J
     }
 }
 
-// One tile's steps [kb0, kb1): fetch step kb+1 into registers while step kb computes.
+// Q4_K min term of one step: acc += sum over the 8 sub-blocks of (-dmin*m)[row] * s_a[col], a
+// rank-8 product, on the matrix pipe in bf16 (fp32's exponent range, so no coefficient can
+// overflow): -dmin*m = p0 + p1 + p2 and s_a = t1 + t2 exactly, every product p*t is exact in fp32,
+// and three K = 16 MFMAs per column block sum them -- MFMA m, lane (row, h), slots 2q and 2q+1
+// hold p_m of sub-block 4h+q against t1 and t2 of the same sub-block.
+template <int J>
+__device__ __forceinline__ void q4k_min_term(const uint8_t *sm, f32x16 (&acc)[Cfg<J>::NCB]) {
+    using L = Smem<kQ4_K, J>;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int rw = wid & 3, cw = wid >> 2, h = lane >> 5;
+    const int arow = 32 * rw + (lane & 31), colw = Cfg<J>::JW * cw + (lane & 31);
+    const uint8_t *wp = sm + L::WM_OFF + arow * 48 + 24 * h;
+    u32x4 bs[Cfg<J>::NCB];
+#pragma unroll
+    for (int cb = 0; cb < Cfg<J>::NCB; ++cb) bs[cb] = *(const u32x4 *)(sm + L::XB_OFF + (colw + 32 * cb) * 32 + 16 * h);
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+        const u32x2 p = *(const u32x2 *)(wp + 8 * m);
+        const u32x4 a = {__builtin_amdgcn_perm(p.x, p.x, 0x01000100u), __builtin_amdgcn_perm(p.x, p.x, 0x03020302u),
+                         __builtin_amdgcn_perm(p.y, p.y, 0x01000100u), __builtin_amdgcn_perm(p.y, p.y, 0x03020302u)};
+#pragma unroll
+        for (int cb = 0; cb < Cfg<J>::NCB; ++cb)
+            acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                             __builtin_bit_cast(bf16x8, bs[cb]), acc[cb], 0, 0, 0);
+    }
+}
+
+// One tile's steps [kb0, kb1), software-pipelined: the loads of a later step are in flight while
+// a step computes.
 template <int T, int J, bool DBG>
 __device__ __forceinline__ void run_tile(uint8_t *sm, f32x16 (&acc)[Cfg<J>::NCB], const uint8_t *wbase,
                                          int64_t row_bytes, int64_t r0, int64_t rows, int64_t kb0, int64_t kb1,
                                          int64_t nb32, const uint8_t *xq, const int64_t (&acol)[J * 8 / Cfg<J>::NT],
                                          int32_t *dbg, int64_t n, int64_t c0, int64_t act_rows) {
+    constexpr bool DB = kDoubleBuffer<T, J>;
+    i32x16 cinit = {};
+    if constexpr (kSeeded<T, DBG>) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) cinit[e] = kBiasBits;
+        asm volatile("" : "+v"(cinit));
+    }
     WFetch<T, Cfg<J>::NT> wf;
-    ActFetch<J, !DBG> af;
+    ActFetch<J, !DBG, T == kQ8_0> af;
     wf.fetch(wbase, row_bytes, r0, rows, kb0, nb32);
     af.fetch(xq, nb32, kb0, acol, act_rows);
-    if constexpr (kDoubleBuffer<T, J>) {
-        // Two LDS buffers: step kb computes from one while step kb+1 is parked in the other, so a
-        // step needs one barrier (it publishes the parked step and retires the buffer computed
-        // before), and the fetch of step kb+2 flies during step kb.
-        uint8_t *buf0 = sm, *buf1 = sm + Smem<T, J>::BYTES;
-        __syncthreads();   // the previous tile's reads of both buffers are done
-        wf.template store<J>(buf0, wbase, row_bytes, r0, rows, kb0, nb32);
-        af.template store<T>(buf0);
-        if (kb0 + 1 < kb1) {
-            wf.fetch(wbase, row_bytes, r0, rows, kb0 + 1, nb32);
-            af.fetch(xq, nb32, kb0 + 1, acol, act_rows);
-        }
-        for (int64_t kb = kb0; kb < kb1; ++kb) {
+    uint8_t *const buf0 = sm, *const buf1 = sm + (DB ? Smem<T, J>::BYTES : 0);
+    // Publishes step kb in LDS and returns its buffer.  Two buffers: step kb computes from one
+    // while step kb+1 is parked in the other, so a step needs one barrier (it publishes the parked
+    // step and retires the buffer computed before) and the fetch of step kb+2 flies during step
+    // kb.  One buffer: step kb is parked between two barriers, then step kb+1 is fetched.
+    auto enter = [&](int64_t kb) -> const uint8_t * {
+        if constexpr (DB) {
             uint8_t *cur = ((kb - kb0) & 1) ? buf1 : buf0, *nxt = ((kb - kb0) & 1) ? buf0 : buf1;
             __syncthreads();
             if (kb + 1 < kb1) {
@@ -576,20 +596,32 @@ __device__ __forceinline__ void run_tile(uint8_t *sm, f32x16 (&acc)[Cfg<J>::NCB]
                     af.fetch(xq, nb32, kb + 2, acol, act_rows);
                 }
             }
-            tile_step<T, J, DBG>(cur, acc, kb, nb32, dbg, rows, n, r0, c0);
+            return cur;
+        } else {
+            __syncthreads();   // the previous step's LDS reads are done
+            wf.template store<J>(sm, wbase, row_bytes, r0, rows, kb, nb32);
+            af.template store<T>(sm);
+            __syncthreads();
+            if (kb + 1 < kb1) {
+                wf.fetch(wbase, row_bytes, r0, rows, kb + 1, nb32);
+                af.fetch(xq, nb32, kb + 1, acol, act_rows);
+            }
+            return sm;
         }
-        return;
+    };
+    if constexpr (DB) {
+        __syncthreads();   // the previous tile's reads of both buffers are done
+        wf.template store<J>(buf0, wbase, row_bytes, r0, rows, kb0, nb32);
+        af.template store<T>(buf0);
+        if (kb0 + 1 < kb1) {
+            wf.fetch(wbase, row_bytes, r0, rows, kb0 + 1, nb32);
+            af.fetch(xq, nb32, kb0 + 1, acol, act_rows);
+        }
     }
     for (int64_t kb = kb0; kb < kb1; ++kb) {
-        __syncthreads();   // the previous step's LDS reads are done
-        wf.template store<J>(sm, wbase, row_bytes, r0, rows, kb, nb32);
-        af.template store<T>(sm);
-        __syncthreads();
-        if (kb + 1 < kb1) {
-            wf.fetch(wbase, row_bytes, r0, rows, kb + 1, nb32);
-            af.fetch(xq, nb32, kb + 1, acol, act_rows);
-        }
-        tile_step<T, J, DBG>(sm, acc, kb, nb32, dbg, rows, n, r0, c0);
+        const uint8_t *cur = enter(kb);
+        if constexpr (T == kQ4_K && !DBG) q4k_min_term<J>(cur, acc);
+        tile_step<T, J, DBG>(cur, acc, cinit, kb, nb32, dbg, rows, n, r0, c0);
     }
 }
 
@@ -643,7 +675,7 @@ __global__ __launch_bounds__(Cfg<J>::NT, 2) void mmq_kernel(const uint8_t *__res
 #pragma unroll
         for (int it = 0; it < NA; ++it) {
             const int64_t c = c0 + ((tid + NT * it) >> 3);
-            acol[it] = c < n ? c : -1;
+            acol[it] = c < n ? c : n - 1;   // columns past the end repeat the last (not written)
         }
         f32x16 acc[Cfg<J>::NCB];
 #pragma unroll
@@ -770,7 +802,7 @@ __global__ __launch_bounds__(Cfg<J>::NT, 2) void mmq_id_kernel(const uint8_t *__
 #pragma unroll
     for (int it = 0; it < NA; ++it) {
         const int64_t c = c0 + ((tid + NT * it) >> 3);
-        acol[it] = c < cnt ? arow_of(c) : -1;
+        acol[it] = arow_of(c < cnt ? c : cnt - 1);   // past the end: the last column (not written)
     }
     f32x16 acc[Cfg<J>::NCB];
 #pragma unroll
