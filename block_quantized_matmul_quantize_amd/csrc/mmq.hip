@@ -6,17 +6,16 @@
 // fetched from HBM into registers while an earlier step computes (software pipelining: the loads
 // of the next step are issued right after a step is parked in LDS; Q4_K 8-wave tiles keep two
 // LDS step buffers and fetch two steps ahead), then parked in LDS: Q4_K as packed qs bytes plus
-// per-(row, sub-block) scales d*sc and mins -dmin*m (fp32, and the mins also as exact fp16
-// hi/lo pairs), Q8_0 as int8 codes plus fp32 d, Q6_K unpacked (below); activations, read from
-// the step-tiled q8_1 layout, as int8 codes plus fp32 (d, s) per 32-value block (the MMQ page's
+// per-(row, sub-block) scales d*sc (fp32) and mins -dmin*m (as exact bf16 pieces), Q8_0 as int8
+// codes plus fp32 d, Q6_K unpacked (below); activations, read from the step-tiled q8_1 layout, as
+// int8 codes plus fp32 (d, s) per 32-value block (the MMQ page's
 // "why not dequantize": stay quantized and reuse each unpacked tile for J columns).  Each wave
 // owns 32 rows; per 32-value block it runs one v_mfma_i32_32x32x32_i8 per 32 columns -- K = 32
 // is exactly one q8_1 block, so every int32 result is one exact sub-block dot D -- and folds it
 // into its fp32 accumulators with one multiply-add, the per-element scale coming from an
 // outer-product MFMA:
 //   Q4_K  acc += D * (d*sc * d_a);  the min term -(dmin*m) * s_a is a rank-8 product per step,
-//         one v_mfma_f32_32x32x16_f16 per column block (four K=2 fp32 MFMAs where the
-//         coefficients leave fp16 range)
+//         three v_mfma_f32_32x32x16_bf16 per column block over exact bf16 pieces
 //   Q8_0  acc += D * (d_w * d_a)
 //   Q6_K  acc += (sc0*D0 + sc1*D1) * (d * d_a)
 // Q6_K changes scale every 16 values, so its int8 scale is folded into the codes at unpack time:
