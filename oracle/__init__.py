@@ -59,6 +59,10 @@ def lib():
         L.oracle_matmul.restype = i32
         L.oracle_matmul_id.argtypes = [i32, vp, i64, i64, i64, vp, i64, vp, i64, i64, vp, vp]
         L.oracle_matmul_id.restype = i32
+        L.oracle_matmul_glu.argtypes = [i32, vp, vp, i64, i64, vp, i64, vp]
+        L.oracle_matmul_glu.restype = i32
+        L.oracle_matmul_id_glu.argtypes = [i32, vp, vp, i64, i64, i64, vp, vp, i64, i64, vp, vp]
+        L.oracle_matmul_id_glu.restype = i32
         _lib = L
     return _lib
 
@@ -182,4 +186,34 @@ def matmul_id(qtype, w, n_exp, rows, k, x, x_per_tok, ids, fill=np.nan):
                                 top_k, _ptr(y), ctypes.byref(bad))
     if rc:
         raise ValueError("oracle_matmul_id: bad arguments")
+    return y, int(bad.value)
+
+
+def matmul_glu(qtype, w_gate, w_up, rows, k, x):
+    """silu(W_gate x) * (W_up x) -> y [n, rows] (fp32)."""
+    w_gate = _c(w_gate, np.uint8)
+    w_up = _c(w_up, np.uint8)
+    x = _c(x, np.float32)
+    n = x.shape[0]
+    y = np.zeros((n, rows), dtype=np.float32)
+    rc = lib().oracle_matmul_glu(qtype, _ptr(w_gate), _ptr(w_up), rows, k, _ptr(x), n, _ptr(y))
+    if rc:
+        raise ValueError("oracle_matmul_glu: bad arguments")
+    return y
+
+
+def matmul_id_glu(qtype, w_gate, w_up, n_exp, rows, k, x, ids, fill=np.nan):
+    """Expert form of matmul_glu (one activation row per token); returns (y [n_tok, top_k, rows],
+    n_invalid).  Rows of y whose id is out of range keep `fill`."""
+    w_gate = _c(w_gate, np.uint8)
+    w_up = _c(w_up, np.uint8)
+    x = _c(x, np.float32)
+    ids = _c(ids, np.int32)
+    n_tok, top_k = ids.shape
+    y = np.full((n_tok, top_k, rows), fill, dtype=np.float32)
+    bad = ctypes.c_int64(0)
+    rc = lib().oracle_matmul_id_glu(qtype, _ptr(w_gate), _ptr(w_up), n_exp, rows, k, _ptr(x), _ptr(ids), n_tok,
+                                    top_k, _ptr(y), ctypes.byref(bad))
+    if rc:
+        raise ValueError("oracle_matmul_id_glu: bad arguments")
     return y, int(bad.value)

@@ -481,3 +481,54 @@ int oracle_matmul_id(int type, const uint8_t *w, int64_t n_exp, int64_t rows, in
     free(xq);
     return ORC_OK;
 }
+
+/* ---------------------------------------------------------------------------------------------
+ * Gate/up products fused with SwiGLU (the "llama.cpp MMQ" page, the fusion passage after the MoE
+ * dispatch: the gate and up products of one input are taken together and the GLU is applied as
+ * they are written back).  The pages name SwiGLU without writing it out; read here as the usual
+ *     out = silu(g) * u,   silu(g) = g / (1 + exp(-g)),
+ * with g the gate product and u the up product of the same row and column.  Each product is the
+ * oracle's own (above); the GLU is evaluated in fp64 from the two fp32 products and rounded once.
+ * ------------------------------------------------------------------------------------------- */
+static float swiglu_ref(float g, float u) {
+    const double gd = (double)g;
+    return (float)(gd / (1.0 + exp(-gd)) * (double)u);
+}
+
+/* y[n][rows] = silu(W_gate x) * (W_up x); both weights (rows x k) of one type. */
+int oracle_matmul_glu(int type, const uint8_t *wg, const uint8_t *wu, int64_t rows, int64_t k, const float *x,
+                      int64_t n, float *y) {
+    if (check_args(type, rows, k, n)) return ORC_ERR;
+    float *g = (float *)malloc((size_t)(n * rows) * sizeof(float) + 4);
+    int rc = oracle_matmul(type, wg, rows, k, x, n, g);
+    if (!rc) rc = oracle_matmul(type, wu, rows, k, x, n, y);
+    if (!rc)
+        for (int64_t i = 0; i < n * rows; ++i) y[i] = swiglu_ref(g[i], y[i]);
+    free(g);
+    return rc;
+}
+
+/* Expert form: wg, wu hold n_exp (rows x k) matrices each; x fp32 [n_tok][k] (one activation row
+ * per token, shared by its top_k slots); y fp32 [n_tok][top_k][rows].  An id outside [0, n_exp)
+ * leaves its output row untouched and is counted in *n_invalid. */
+int oracle_matmul_id_glu(int type, const uint8_t *wg, const uint8_t *wu, int64_t n_exp, int64_t rows, int64_t k,
+                         const float *x, const int32_t *ids, int64_t n_tok, int64_t top_k, float *y,
+                         int64_t *n_invalid) {
+    if (check_args(type, rows, k, n_tok)) return ORC_ERR;
+    if (n_exp <= 0 || top_k <= 0) return ORC_ERR;
+    const int64_t m = n_tok * top_k * rows;
+    float *g = (float *)malloc((size_t)m * sizeof(float) + 4);
+    float *u = (float *)malloc((size_t)m * sizeof(float) + 4);
+    int64_t bad = 0;
+    int rc = oracle_matmul_id(type, wg, n_exp, rows, k, x, 1, ids, n_tok, top_k, g, &bad);
+    if (!rc) rc = oracle_matmul_id(type, wu, n_exp, rows, k, x, 1, ids, n_tok, top_k, u, NULL);
+    if (!rc)
+        for (int64_t p = 0; p < n_tok * top_k; ++p) {
+            if (ids[p] < 0 || ids[p] >= n_exp) continue;
+            for (int64_t r = 0; r < rows; ++r) y[p * rows + r] = swiglu_ref(g[p * rows + r], u[p * rows + r]);
+        }
+    if (n_invalid) *n_invalid = bad;
+    free(g);
+    free(u);
+    return rc;
+}
