@@ -60,6 +60,10 @@ _sig("qmm_matmul_q8_1", _i32, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _sz, _
 _sig("qmm_matmul_id_workspace", _sz, _i32, _i64, _i64, _i64, _i64, _i64, _i64)
 _sig("qmm_matmul_id", _i32, _i32, _vp, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _vp, _sz, _vp)
 _sig("qmm_matmul_id_invalid_count", _i32, _vp, ctypes.POINTER(_i64), _vp)
+_sig("qmm_matmul_glu_workspace", _sz, _i32, _i64, _i64, _i64)
+_sig("qmm_matmul_glu", _i32, _i32, _vp, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _sz, _vp)
+_sig("qmm_matmul_id_glu_workspace", _sz, _i32, _i64, _i64, _i64, _i64, _i64)
+_sig("qmm_matmul_id_glu", _i32, _i32, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _vp, _sz, _vp)
 _sig("qmm_matmul_id_grouping_layout", _i32, _i32, _i64, _i64, _i64, _i64, _i64, ctypes.POINTER(_i64))
 _sig("qmm_debug_subdots", _i32, _i32, _vp, _i64, _i64, _vp, _i64, _i32, _vp, _vp)
 _sig("qmm_set_override", _i32, _i32, _i32)
@@ -145,6 +149,14 @@ def matmul_q8_1_workspace(qtype, rows, k, n):
 
 def matmul_id_workspace(qtype, n_exp, rows, k, n_tok, top_k, x_per_tok):
     return int(_L.qmm_matmul_id_workspace(qtype, n_exp, rows, k, n_tok, top_k, x_per_tok))
+
+
+def matmul_glu_workspace(qtype, rows, k, n):
+    return int(_L.qmm_matmul_glu_workspace(qtype, rows, k, n))
+
+
+def matmul_id_glu_workspace(qtype, n_exp, rows, k, n_tok, top_k):
+    return int(_L.qmm_matmul_id_glu_workspace(qtype, n_exp, rows, k, n_tok, top_k))
 
 
 # --------------------------------------------------------------------------------------------
@@ -244,6 +256,50 @@ def matmul_id(w, qtype, n_exp, rows, k, x, ids, x_per_tok=1, out=None, ws=None):
         ws = _workspace(nbytes, x.device)
     _check(_L.qmm_matmul_id(qtype, pw, n_exp, rows, k, px, x_per_tok, pi, n_tok, top_k, py,
                             ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream()))
+    return out, ws
+
+
+def matmul_glu(w_gate, w_up, qtype, rows, k, x, out=None, ws=None):
+    """Y[n, rows] = silu(W_gate . X^T) * (W_up . X^T), both products of X quantized to q8_1 once."""
+    torch = _torch()
+    pg = _need(w_gate, torch.uint8, "w_gate")
+    pu = _need(w_up, torch.uint8, "w_up")
+    if w_gate.numel() != w_up.numel():
+        raise ValueError("w_gate and w_up must have the same size")
+    px = _need(x, torch.float32, "x")
+    if x.dim() != 2 or x.shape[1] != k:
+        raise ValueError(f"x must be [n, {k}]")
+    n = x.shape[0]
+    if out is None:
+        out = torch.empty((n, rows), dtype=torch.float32, device=x.device)
+    py = _need(out, torch.float32, "out")
+    if ws is None:
+        ws = _workspace(matmul_glu_workspace(qtype, rows, k, n), x.device)
+    _check(_L.qmm_matmul_glu(qtype, pg, pu, rows, k, px, n, py, ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                             _stream()))
+    return out
+
+
+def matmul_id_glu(w_gate, w_up, qtype, n_exp, rows, k, x, ids, out=None, ws=None):
+    """Expert form of matmul_glu.  x: fp32 [n_tok, k]; ids: int32 [n_tok, top_k]; returns
+    (y fp32 [n_tok, top_k, rows], ws) -- rows with an invalid id keep their value in `out`."""
+    torch = _torch()
+    pg = _need(w_gate, torch.uint8, "w_gate")
+    pu = _need(w_up, torch.uint8, "w_up")
+    if w_gate.numel() != w_up.numel():
+        raise ValueError("w_gate and w_up must have the same size")
+    px = _need(x, torch.float32, "x")
+    pi = _need(ids, torch.int32, "ids")
+    n_tok, top_k = ids.shape
+    if x.shape != (n_tok, k):
+        raise ValueError(f"x must be [{n_tok}, {k}]")
+    if out is None:
+        out = torch.zeros((n_tok, top_k, rows), dtype=torch.float32, device=x.device)
+    py = _need(out, torch.float32, "out")
+    if ws is None:
+        ws = _workspace(matmul_id_glu_workspace(qtype, n_exp, rows, k, n_tok, top_k), x.device)
+    _check(_L.qmm_matmul_id_glu(qtype, pg, pu, n_exp, rows, k, px, pi, n_tok, top_k, py,
+                                ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream()))
     return out, ws
 
 

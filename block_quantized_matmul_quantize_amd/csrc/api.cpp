@@ -385,6 +385,56 @@ qmm_status qmm_matmul_q8_1(int type, const void *w, int64_t rows, int64_t k, con
     return run_dense(type, w, rows, k, (const uint8_t *)xq, n, y, (uint8_t *)ws, L, nullptr, 0, (hipStream_t)stream);
 }
 
+// ----------------------------------------------------------------------------------------------
+// Dense gate/up fusion
+// ----------------------------------------------------------------------------------------------
+namespace {
+
+bool glu_matvec(int64_t n, int64_t k) { return n <= 8 && k <= kMvMaxK && g_ovr_path.load() != 2; }
+
+size_t glu_ws(int64_t k, int64_t n) {
+    return glu_matvec(n, k) ? align_up((size_t)(n * (k / 32) * 36), 256) : align_up(qmm::q8_1_tiled_bytes(n, k), 256);
+}
+
+}  // namespace
+
+size_t qmm_matmul_glu_workspace(int type, int64_t rows, int64_t k, int64_t n) {
+    if (check_common(type, rows, k, n)) return 0;
+    return glu_ws(k, n);
+}
+
+qmm_status qmm_matmul_glu(int type, const void *w_gate, const void *w_up, int64_t rows, int64_t k, const float *x,
+                          int64_t n, float *y, void *ws, size_t ws_bytes, void *stream) {
+    qmm_status st = check_common(type, rows, k, n);
+    if (st) return st;
+    if ((st = check_ptrs_dense(w_gate, x, y, n))) return st;
+    if (n == 0) return QMM_OK;
+    if (!w_up) return fail(QMM_ERR_ARG, "null w_up");
+    if (((uintptr_t)w_up) & 1) return fail(QMM_ERR_ARG, "w must be 2-byte aligned");
+    if (((uintptr_t)x) & 15) return fail(QMM_ERR_ARG, "x must be 16-byte aligned");
+    const size_t need = glu_ws(k, n);
+    if (!ws || ws_bytes < need)
+        return fail(QMM_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", ws_bytes, need);
+    if (((uintptr_t)ws) & 255) return fail(QMM_ERR_ARG, "workspace must be 256-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    uint8_t *wsb = (uint8_t *)ws;
+    const uint8_t *wg = (const uint8_t *)w_gate, *wu = (const uint8_t *)w_up;
+    hipError_t e;
+    if (glu_matvec(n, k)) {
+        e = qmm::launch_quantize_q8_1(x, n, k, wsb, s);
+        if (e != hipSuccess) return hip_fail(e, "quantize launch");
+        e = qmm::launch_mmvq_glu(type, wg, wu, rows, k, wsb, n, y, nullptr, 0, s);
+        if (e != hipSuccess) return hip_fail(e, "fused matrix-vector kernel launch");
+        return QMM_OK;
+    }
+    e = qmm::launch_quantize_q8_1_tiled(x, n, k, wsb, nullptr, s);
+    if (e != hipSuccess) return hip_fail(e, "quantize launch");
+    const int tile_j = g_ovr_tile_j.load() ? g_ovr_tile_j.load() : qmm_select_tile_j(n);
+    e = qmm::launch_mmq_glu(type, wg, wu, rows, k, wsb, n, y, tile_j, s);
+    if (e != hipSuccess) return hip_fail(e, "fused tiled kernel launch");
+    return QMM_OK;
+}
+
 qmm_status qmm_debug_subdots(int type, const void *w, int64_t rows, int64_t k, const void *xq, int64_t n, int path,
                              int32_t *d_out, void *stream) {
     qmm_status st = check_common(type, rows, k, n);
@@ -448,9 +498,12 @@ size_t qmm_matmul_id_workspace(int type, int64_t n_exp, int64_t rows, int64_t k,
     return id_layout(n_exp, k, n_tok, top_k, x_per_tok).total;
 }
 
-qmm_status qmm_matmul_id(int type, const void *w, int64_t n_exp, int64_t rows, int64_t k, const float *x,
-                         int64_t x_per_tok, const int32_t *ids, int64_t n_tok, int64_t top_k, float *y, void *ws,
-                         size_t ws_bytes, void *stream) {
+namespace {
+
+// Expert-indexed product; w_up not null: gate/up fusion (w the gate matrices, x_per_tok == 1).
+qmm_status run_id(int type, const void *w, const void *w_up, int64_t n_exp, int64_t rows, int64_t k, const float *x,
+                  int64_t x_per_tok, const int32_t *ids, int64_t n_tok, int64_t top_k, float *y, void *ws,
+                  size_t ws_bytes, void *stream) {
     qmm_status st = check_common(type, rows, k, n_tok);
     if (st) return st;
     if (n_exp <= 0 || n_exp > 32768) return fail(QMM_ERR_ARG, "n_exp must be in [1, 32768]");
@@ -469,7 +522,7 @@ qmm_status qmm_matmul_id(int type, const void *w, int64_t n_exp, int64_t rows, i
         return e == hipSuccess ? QMM_OK : hip_fail(e, "fill launch");
     }
     if (!w || !x || !ids || !y) return fail(QMM_ERR_ARG, "null w, x, ids or y");
-    if (((uintptr_t)w) & 1) return fail(QMM_ERR_ARG, "w must be 2-byte aligned");
+    if (((uintptr_t)w) & 1 || ((uintptr_t)w_up) & 1) return fail(QMM_ERR_ARG, "w must be 2-byte aligned");
     if (((uintptr_t)x) & 15) return fail(QMM_ERR_ARG, "x must be 16-byte aligned");
     if (((uintptr_t)y) & 3 || ((uintptr_t)ids) & 3) return fail(QMM_ERR_ARG, "y and ids must be 4-byte aligned");
 
@@ -495,15 +548,35 @@ qmm_status qmm_matmul_id(int type, const void *w, int64_t n_exp, int64_t rows, i
     if (e != hipSuccess) return hip_fail(e, "grouping launch");
     // experts with <= 8 columns: matrix-vector kernel, one workgroup row per listed expert
     if (k <= kMvMaxK) {
-        e = qmm::launch_mmvq(type, (const uint8_t *)w, rows, k, xq, 0, y, nullptr, &cm, n_exp, s);
+        e = w_up ? qmm::launch_mmvq_glu(type, (const uint8_t *)w, (const uint8_t *)w_up, rows, k, xq, 0, y, &cm, n_exp, s)
+                 : qmm::launch_mmvq(type, (const uint8_t *)w, rows, k, xq, 0, y, nullptr, &cm, n_exp, s);
         if (e != hipSuccess) return hip_fail(e, "expert matrix-vector launch");
     }
     // the rest: tiled kernel over the device-built column-tile list
     const int64_t mmq_experts = std::min<int64_t>(n_exp, pairs / (small_max + 1));
     const int64_t max_ct = (pairs + tile_j - 1) / tile_j + mmq_experts;
-    e = qmm::launch_mmq_id(type, (const uint8_t *)w, rows, k, xt, y, cm, tile_j, max_ct, s);
+    e = qmm::launch_mmq_id(type, (const uint8_t *)w, (const uint8_t *)w_up, rows, k, xt, y, cm, tile_j, max_ct, s);
     if (e != hipSuccess) return hip_fail(e, "expert tiled launch");
     return QMM_OK;
+}
+
+}  // namespace
+
+qmm_status qmm_matmul_id(int type, const void *w, int64_t n_exp, int64_t rows, int64_t k, const float *x,
+                         int64_t x_per_tok, const int32_t *ids, int64_t n_tok, int64_t top_k, float *y, void *ws,
+                         size_t ws_bytes, void *stream) {
+    return run_id(type, w, nullptr, n_exp, rows, k, x, x_per_tok, ids, n_tok, top_k, y, ws, ws_bytes, stream);
+}
+
+size_t qmm_matmul_id_glu_workspace(int type, int64_t n_exp, int64_t rows, int64_t k, int64_t n_tok, int64_t top_k) {
+    return qmm_matmul_id_workspace(type, n_exp, rows, k, n_tok, top_k, 1);
+}
+
+qmm_status qmm_matmul_id_glu(int type, const void *w_gate, const void *w_up, int64_t n_exp, int64_t rows, int64_t k,
+                             const float *x, const int32_t *ids, int64_t n_tok, int64_t top_k, float *y, void *ws,
+                             size_t ws_bytes, void *stream) {
+    if (n_tok > 0 && !w_up) return fail(QMM_ERR_ARG, "null w_up");
+    return run_id(type, w_gate, w_up, n_exp, rows, k, x, 1, ids, n_tok, top_k, y, ws, ws_bytes, stream);
 }
 
 qmm_status qmm_matmul_id_grouping_layout(int type, int64_t n_exp, int64_t k, int64_t n_tok, int64_t top_k,

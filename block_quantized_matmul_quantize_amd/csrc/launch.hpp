@@ -38,6 +38,11 @@ struct ColMap {
 hipError_t launch_mmvq(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n,
                        float *y, int32_t *dbg, const ColMap *cm, int64_t n_exp, hipStream_t s);
 
+// Gate/up fusion on the register-streamed matrix-vector kernel: y = silu(W_gate x) * (W_up x)
+// for n <= 8 dense columns (cm null) or the small experts (cm set, grid.y = n_exp).
+hipError_t launch_mmvq_glu(int type, const uint8_t *wg, const uint8_t *wu, int64_t rows, int64_t k, const uint8_t *xq,
+                           int64_t n, float *y, const ColMap *cm, int64_t n_exp, hipStream_t s);
+
 // fp32-input matrix-vector product with the q8_1 quantization done inside the dot4 or the
 // LDS-staged kernel (no separate quantize launch): dense calls either kernel would take.
 bool mmvq_fused_applies(int type, const void *w, int64_t k, const float *x, int64_t n);
@@ -85,9 +90,14 @@ struct MmqLaunch {
 };
 hipError_t launch_mmq(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n,
                       float *y, int32_t *dbg, const MmqLaunch &plan, hipStream_t s);
-// Expert mode: grid over (row tiles, max column tiles); experts with > 8 columns.
-hipError_t launch_mmq_id(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, float *y,
-                         const ColMap &cm, int tile_j, int64_t max_col_tiles, hipStream_t s);
+// Gate/up fusion: y[n][rows] = silu(W_gate x) * (W_up x), tiles of 64 outputs, no stream-K.
+hipError_t launch_mmq_glu(int type, const uint8_t *wg, const uint8_t *wu, int64_t rows, int64_t k, const uint8_t *xq,
+                          int64_t n, float *y, int tile_j, hipStream_t s);
+// Expert mode: grid over (row tiles, max column tiles); experts with > 8 columns.  w_up not null:
+// gate/up fusion, w the gate matrices.
+hipError_t launch_mmq_id(int type, const uint8_t *w, const uint8_t *w_up, int64_t rows, int64_t k,
+                         const uint8_t *xq, float *y, const ColMap &cm, int tile_j, int64_t max_col_tiles,
+                         hipStream_t s);
 
 // Expert grouping: counts, bounds, stable sorted pair list, column-tile prefix, small-expert list.
 hipError_t launch_moe_group(const int32_t *ids, int64_t pairs, int32_t n_exp, int32_t tile_j,

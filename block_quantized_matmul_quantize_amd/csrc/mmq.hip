@@ -153,7 +153,28 @@ template <int J, bool TILED, bool RAGGED> struct ActFetch {
 };
 
 // ---------------------------------------------------------------------------------------------
-// Weight tile fetch / park, rows [r0, r0+128) of step kb.
+// Weight rows of a tile.  Plain: tile row t is matrix row r0 + t.  GLU (gate/up fusion, the MMQ
+// page's fusion passage): the tile's 128 rows hold 64 outputs, alternating in groups of 8 between
+// the gate (w0) and up (w1) matrices -- tile row t is row r0 + 8*(t/16) + t%8 of w1 if t & 8, else
+// of w0 -- which in the accumulator layout puts the gate and up values of one output in elements
+// e and e + 4 of the same lane.  Rows past the end repeat the last row (never written out).
+// ---------------------------------------------------------------------------------------------
+template <bool GLU> struct WRows {
+    const uint8_t *w0;
+    int64_t d01;   // GLU: byte distance from w0 to w1 (an offset, not a select: a select between two
+                   // fields makes the compiler keep the struct in scratch memory)
+    int64_t row_bytes, r0, rows;
+    __device__ __forceinline__ WRows(const uint8_t *w0_, const uint8_t *w1_, int64_t rb, int64_t r0_, int64_t rows_)
+        : w0(w0_), d01(GLU ? (int64_t)((uintptr_t)w1_ - (uintptr_t)w0_) : 0), row_bytes(rb), r0(r0_), rows(rows_) {}
+    __device__ __forceinline__ const uint8_t *row(int t) const {
+        int64_t r = GLU ? r0 + 8 * (t >> 4) + (t & 7) : r0 + t;
+        r = r < rows ? r : rows - 1;
+        return w0 + (GLU ? (int64_t)((t >> 3) & 1) * d01 : 0) + r * row_bytes;
+    }
+};
+
+// ---------------------------------------------------------------------------------------------
+// Weight tile fetch / park: the tile's 128 rows (WRows) of step kb.
 // ---------------------------------------------------------------------------------------------
 template <int T, int NT> struct WFetch;
 
@@ -162,20 +183,18 @@ template <int T, int NT> struct WFetch;
 template <int NT> struct WFetch<kQ4_K, NT> {
     static constexpr int N = 1024 / NT;
     u32x4 q[N], h;
-    __device__ __forceinline__ void fetch(const uint8_t *wbase, int64_t row_bytes, int64_t r0, int64_t rows,
-                                          int64_t kb, int64_t) {
+    template <class WR>
+    __device__ __forceinline__ void fetch(const WR &wr, int64_t kb, int64_t) {
         const int tid = threadIdx.x;
 #pragma unroll
         for (int it = 0; it < N; ++it) {
             const int i = tid + NT * it;
-            const int64_t row = r0 + (i >> 3) < rows ? r0 + (i >> 3) : rows - 1;   // ragged tile: the last row
-            q[it] = ld16(wbase + row * row_bytes + kb * 144 + 16 + 16 * (i & 7));
+            q[it] = ld16(wr.row(i >> 3) + kb * 144 + 16 + 16 * (i & 7));
         }
-        if (tid < kTI) h = ld16(wbase + (r0 + tid < rows ? r0 + tid : rows - 1) * row_bytes + kb * 144);
+        if (tid < kTI) h = ld16(wr.row(tid) + kb * 144);
     }
-    template <int J>
-    __device__ __forceinline__ void store(uint8_t *sm, const uint8_t *, int64_t, int64_t, int64_t, int64_t,
-                                          int64_t) const {
+    template <int J, class WR>
+    __device__ __forceinline__ void store(uint8_t *sm, const WR &, int64_t, int64_t) const {
         const int tid = threadIdx.x;
         uint8_t *sW = sm + Smem<kQ4_K, J>::W_OFF;
 #pragma unroll
@@ -226,26 +245,24 @@ template <int NT> struct WFetch<kQ8_0, NT> {
     static constexpr int NQ = 2048 / NT, ND = 1024 / NT;
     u32x4 q[NQ];
     uint16_t d[ND];
-    __device__ __forceinline__ void fetch(const uint8_t *wbase, int64_t row_bytes, int64_t r0, int64_t rows,
-                                          int64_t kb, int64_t nb32) {
+    template <class WR>
+    __device__ __forceinline__ void fetch(const WR &wr, int64_t kb, int64_t nb32) {
         const int tid = threadIdx.x;
 #pragma unroll
         for (int it = 0; it < NQ; ++it) {
             const int i = tid + NT * it;
-            const int64_t row = r0 + (i >> 4), b = kb * 8 + ((i >> 1) & 7);
-            q[it] = (row < rows && b < nb32) ? ld16(wbase + row * row_bytes + b * 34 + 2 + 16 * (i & 1))
-                                             : u32x4{0u, 0u, 0u, 0u};
+            const int64_t b = kb * 8 + ((i >> 1) & 7);
+            q[it] = b < nb32 ? ld16(wr.row(i >> 4) + b * 34 + 2 + 16 * (i & 1)) : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int it = 0; it < ND; ++it) {
             const int i = tid + NT * it;
-            const int64_t row = r0 + (i >> 3), b = kb * 8 + (i & 7);
-            d[it] = (row < rows && b < nb32) ? ld2(wbase + row * row_bytes + b * 34) : (uint16_t)0;
+            const int64_t b = kb * 8 + (i & 7);
+            d[it] = b < nb32 ? ld2(wr.row(i >> 3) + b * 34) : (uint16_t)0;
         }
     }
-    template <int J>
-    __device__ __forceinline__ void store(uint8_t *sm, const uint8_t *, int64_t, int64_t, int64_t, int64_t,
-                                          int64_t) const {
+    template <int J, class WR>
+    __device__ __forceinline__ void store(uint8_t *sm, const WR &, int64_t, int64_t) const {
         const int tid = threadIdx.x;
         uint8_t *sW = sm + Smem<kQ8_0, J>::W_OFF;
         float *sWs = (float *)(sm + Smem<kQ8_0, J>::WS_OFF);
@@ -281,10 +298,10 @@ __device__ __forceinline__ void q6_split4(uint32_t c6, s16x2 sc2, s16x2 off2, ui
 // Q6_K with 4-wave tiles (J <= 64): unpacked straight from HBM into the two planes at park time
 // (no register prefetch: the registers are taken by the accumulators).
 template <int NT> struct WFetchQ6Direct {
-    __device__ __forceinline__ void fetch(const uint8_t *, int64_t, int64_t, int64_t, int64_t, int64_t) {}
-    template <int J>
-    __device__ __forceinline__ void store(uint8_t *sm, const uint8_t *wbase, int64_t row_bytes, int64_t r0,
-                                          int64_t rows, int64_t kb, int64_t) const {
+    template <class WR>
+    __device__ __forceinline__ void fetch(const WR &, int64_t, int64_t) {}
+    template <int J, class WR>
+    __device__ __forceinline__ void store(uint8_t *sm, const WR &wr, int64_t kb, int64_t) const {
         const int tid = threadIdx.x;
         int8_t *sLo = (int8_t *)(sm + Smem<kQ6_K, J>::W_OFF);
         int8_t *sHi = sLo + kTI * kLd;
@@ -292,10 +309,9 @@ template <int NT> struct WFetchQ6Direct {
         for (int it = 0; it < 2048 / NT; ++it) {
             const int i = tid + NT * it;               // (row, 16-value group G): 128 x 16
             const int r = i >> 4, G = i & 15;
-            const int64_t row = r0 + r;
-            uint32_t lo_w[4] = {0u, 0u, 0u, 0u}, hi_w[4] = {0u, 0u, 0u, 0u};
-            if (row < rows) {
-                const uint8_t *blk = wbase + row * row_bytes + kb * 210;
+            uint32_t lo_w[4], hi_w[4];
+            {
+                const uint8_t *blk = wr.row(r) + kb * 210;
                 const int hh = G >> 3, gq = (G & 7) >> 1, l0 = 16 * (G & 1);
                 const u32x4 ql = ld16(blk + 64 * hh + 32 * (gq & 1) + l0);
                 const u32x4 qh = ld16(blk + 128 + 32 * hh + l0);
@@ -314,8 +330,7 @@ template <int NT> struct WFetchQ6Direct {
         }
         if (tid < kTI) {
             float *sWs = (float *)(sm + Smem<kQ6_K, J>::WS_OFF);
-            const int64_t row = r0 + tid;
-            sWs[tid] = row < rows ? h2f(ld2(wbase + row * row_bytes + kb * 210 + 208)) : 0.f;
+            sWs[tid] = h2f(ld2(wr.row(tid) + kb * 210 + 208));
         }
     }
 };
@@ -329,21 +344,19 @@ template <int NT> struct WFetchQ6Reg {
     static_assert(NT == 512, "one (row, half, group-parity) unit per thread");
     u32x4 ql0, ql1, qh, sc;
     uint16_t d;
-    __device__ __forceinline__ void fetch(const uint8_t *wbase, int64_t row_bytes, int64_t r0, int64_t rows,
-                                          int64_t kb, int64_t) {
+    template <class WR>
+    __device__ __forceinline__ void fetch(const WR &wr, int64_t kb, int64_t) {
         const int u = threadIdx.x;
         const int r = u >> 2, hh = (u >> 1) & 1, l0 = 16 * (u & 1);
-        const int64_t row = r0 + r < rows ? r0 + r : rows - 1;   // ragged tile: re-read the last row
-        const uint8_t *blk = wbase + row * row_bytes + kb * 210;
+        const uint8_t *blk = wr.row(r) + kb * 210;
         ql0 = ld16(blk + 64 * hh + l0);
         ql1 = ld16(blk + 64 * hh + 32 + l0);
         qh = ld16(blk + 128 + 32 * hh + l0);
         sc = ld16(blk + 192);
         d = (u & 3) == 0 ? ld2(blk + 208) : (uint16_t)0;
     }
-    template <int J>
-    __device__ __forceinline__ void store(uint8_t *sm, const uint8_t *, int64_t, int64_t r0, int64_t rows, int64_t,
-                                          int64_t) const {
+    template <int J, class WR>
+    __device__ __forceinline__ void store(uint8_t *sm, const WR &, int64_t, int64_t) const {
         const int u = threadIdx.x;
         const int r = u >> 2, hh = (u >> 1) & 1, half = u & 1;
         int8_t *sLo = (int8_t *)(sm + Smem<kQ6_K, J>::W_OFF);
@@ -369,7 +382,7 @@ template <int NT> struct WFetchQ6Reg {
         }
         if ((u & 3) == 0) {
             float *sWs = (float *)(sm + Smem<kQ6_K, J>::WS_OFF);
-            sWs[r] = r0 + r < rows ? h2f(d) : 0.f;
+            sWs[r] = h2f(d);
         }
     }
 };
@@ -562,11 +575,11 @@ __device__ __forceinline__ void q4k_min_term(const uint8_t *sm, f32x16 (&acc)[Cf
 
 // One tile's steps [kb0, kb1), software-pipelined: the loads of a later step are in flight while
 // a step computes.
-template <int T, int J, bool DBG>
-__device__ __forceinline__ void run_tile(uint8_t *sm, f32x16 (&acc)[Cfg<J>::NCB], const uint8_t *wbase,
-                                         int64_t row_bytes, int64_t r0, int64_t rows, int64_t kb0, int64_t kb1,
-                                         int64_t nb32, const uint8_t *xq, const int64_t (&acol)[J * 8 / Cfg<J>::NT],
-                                         int32_t *dbg, int64_t n, int64_t c0, int64_t act_rows) {
+template <int T, int J, bool DBG, class WR>
+__device__ __forceinline__ void run_tile(uint8_t *sm, f32x16 (&acc)[Cfg<J>::NCB], const WR &wr, int64_t kb0,
+                                         int64_t kb1, int64_t nb32, const uint8_t *xq,
+                                         const int64_t (&acol)[J * 8 / Cfg<J>::NT], int32_t *dbg, int64_t n,
+                                         int64_t c0, int64_t act_rows) {
     constexpr bool DB = kDoubleBuffer<T, J>;
     i32x16 cinit = {};
     if constexpr (kSeeded<T, DBG>) {
@@ -576,7 +589,7 @@ __device__ __forceinline__ void run_tile(uint8_t *sm, f32x16 (&acc)[Cfg<J>::NCB]
     }
     WFetch<T, Cfg<J>::NT> wf;
     ActFetch<J, !DBG, T == kQ8_0> af;
-    wf.fetch(wbase, row_bytes, r0, rows, kb0, nb32);
+    wf.fetch(wr, kb0, nb32);
     af.fetch(xq, nb32, kb0, acol, act_rows);
     uint8_t *const buf0 = sm, *const buf1 = sm + (DB ? Smem<T, J>::BYTES : 0);
     // Publishes step kb in LDS and returns its buffer.  Two buffers: step kb computes from one
@@ -588,21 +601,21 @@ __device__ __forceinline__ void run_tile(uint8_t *sm, f32x16 (&acc)[Cfg<J>::NCB]
             uint8_t *cur = ((kb - kb0) & 1) ? buf1 : buf0, *nxt = ((kb - kb0) & 1) ? buf0 : buf1;
             __syncthreads();
             if (kb + 1 < kb1) {
-                wf.template store<J>(nxt, wbase, row_bytes, r0, rows, kb + 1, nb32);
+                wf.template store<J>(nxt, wr, kb + 1, nb32);
                 af.template store<T>(nxt);
                 if (kb + 2 < kb1) {
-                    wf.fetch(wbase, row_bytes, r0, rows, kb + 2, nb32);
+                    wf.fetch(wr, kb + 2, nb32);
                     af.fetch(xq, nb32, kb + 2, acol, act_rows);
                 }
             }
             return cur;
         } else {
             __syncthreads();   // the previous step's LDS reads are done
-            wf.template store<J>(sm, wbase, row_bytes, r0, rows, kb, nb32);
+            wf.template store<J>(sm, wr, kb, nb32);
             af.template store<T>(sm);
             __syncthreads();
             if (kb + 1 < kb1) {
-                wf.fetch(wbase, row_bytes, r0, rows, kb + 1, nb32);
+                wf.fetch(wr, kb + 1, nb32);
                 af.fetch(xq, nb32, kb + 1, acol, act_rows);
             }
             return sm;
@@ -610,17 +623,17 @@ __device__ __forceinline__ void run_tile(uint8_t *sm, f32x16 (&acc)[Cfg<J>::NCB]
     };
     if constexpr (DB) {
         __syncthreads();   // the previous tile's reads of both buffers are done
-        wf.template store<J>(buf0, wbase, row_bytes, r0, rows, kb0, nb32);
+        wf.template store<J>(buf0, wr, kb0, nb32);
         af.template store<T>(buf0);
         if (kb0 + 1 < kb1) {
-            wf.fetch(wbase, row_bytes, r0, rows, kb0 + 1, nb32);
+            wf.fetch(wr, kb0 + 1, nb32);
             af.fetch(xq, nb32, kb0 + 1, acol, act_rows);
         }
     }
     for (int64_t kb = kb0; kb < kb1; ++kb) {
         const uint8_t *cur = enter(kb);
         if constexpr (T == kQ4_K && !DBG) q4k_min_term<J>(cur, acc);
-        tile_step<T, J, DBG>(cur, acc, cinit, kb, nb32, dbg, rows, n, r0, c0);
+        tile_step<T, J, DBG>(cur, acc, cinit, kb, nb32, dbg, wr.rows, n, wr.r0, c0);
     }
 }
 
@@ -639,6 +652,30 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[Cfg<J>::NCB], flo
         for (int e = 0; e < 16; ++e) {
             const int r = 32 * rw + 4 * (lane >> 5) + 8 * (e >> 2) + (e & 3);
             if (r < rlim) dst[(int64_t)col * ld + r] = acc[cb][e];
+        }
+    }
+}
+
+// SwiGLU of a gate value g and an up value u: silu(g) * u, silu(g) = g / (1 + e^-g).
+__device__ __forceinline__ float swiglu(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+// GLU tile (WRows<true>): 64 outputs; element e (e % 8 < 4) of a lane is the gate value and e + 4
+// the up value of output row 16*rw + 8*(e/8) + 4*(lane/32) + e%4.  dst[col * ld + row], rows <
+// rlim, columns < clim.
+template <int J>
+__device__ __forceinline__ void store_tile_glu(const f32x16 (&acc)[Cfg<J>::NCB], float *dst, int64_t ld,
+                                               int64_t rlim, int64_t clim) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int rw = wid & 3, cw = wid >> 2;
+#pragma unroll
+    for (int cb = 0; cb < Cfg<J>::NCB; ++cb) {
+        const int col = Cfg<J>::JW * cw + 32 * cb + (lane & 31);
+        if (col >= clim) continue;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int e = (q & 3) + 8 * (q >> 2);
+            const int r = 16 * rw + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+            if (r < rlim) dst[(int64_t)col * ld + r] = swiglu(acc[cb][e], acc[cb][e + 4]);
         }
     }
 }
@@ -680,7 +717,8 @@ __global__ __launch_bounds__(Cfg<J>::NT, 2) void mmq_kernel(const uint8_t *__res
 #pragma unroll
         for (int cb = 0; cb < Cfg<J>::NCB; ++cb) acc[cb] = f32x16{};
 
-        run_tile<T, J, DBG>(sm, acc, w, row_bytes, r0, rows, kb0, kb1, nb32, xq, acol, dbg, n, c0, n);
+        const WRows<false> wr{w, w, row_bytes, r0, rows};
+        run_tile<T, J, DBG>(sm, acc, wr, kb0, kb1, nb32, xq, acol, dbg, n, c0, n);
 
         if (!DBG) {
             const bool whole = kb0 == 0 && kb1 == args.k_iters;
@@ -693,6 +731,35 @@ __global__ __launch_bounds__(Cfg<J>::NT, 2) void mmq_kernel(const uint8_t *__res
         }
         pos += kb1 - kb0;
     }
+}
+
+// Dense gate/up kernel (GLU tiles of 64 outputs): one tile per workgroup over the whole K range
+// (the two products of an output must meet in one workgroup, so no stream-K split).
+template <int T, int J>
+__global__ __launch_bounds__(Cfg<J>::NT, 2) void mmq_glu_kernel(const uint8_t *__restrict__ wg,
+                                                             const uint8_t *__restrict__ wu, int64_t rows, int64_t k,
+                                                             const uint8_t *__restrict__ xq, int64_t n,
+                                                             float *__restrict__ y, int64_t ntiles, int64_t n_ct) {
+    extern __shared__ __align__(16) uint8_t sm[];
+    constexpr int NA = J * 8 / Cfg<J>::NT, NT = Cfg<J>::NT;
+    const int64_t nb32 = k / 32;
+    const int64_t row_bytes = (k / Fmt<T>::QK) * Fmt<T>::BYTES;
+    const int64_t t = xcd_remap(blockIdx.x, ntiles);
+    int64_t rt, ct;
+    tile_coords(t, ntiles, n_ct, rt, ct);
+    const int64_t r0 = rt * (kTI / 2), c0 = ct * J;
+    int64_t acol[NA];
+#pragma unroll
+    for (int it = 0; it < NA; ++it) {
+        const int64_t c = c0 + ((threadIdx.x + NT * it) >> 3);
+        acol[it] = c < n ? c : n - 1;
+    }
+    f32x16 acc[Cfg<J>::NCB];
+#pragma unroll
+    for (int cb = 0; cb < Cfg<J>::NCB; ++cb) acc[cb] = f32x16{};
+    const WRows<true> wr{wg, wu, row_bytes, r0, rows};
+    run_tile<T, J, false>(sm, acc, wr, 0, (k + kSuper - 1) / kSuper, nb32, xq, acol, nullptr, n, c0, n);
+    store_tile_glu<J>(acc, y + c0 * rows + r0, rows, rows - r0, n - c0);
 }
 
 // Sum of the partial slots of every split tile, in ascending unit order.
@@ -767,8 +834,9 @@ __global__ __launch_bounds__(256) void streamk_fixup_kernel(float *__restrict__ 
 // ---------------------------------------------------------------------------------------------
 // Expert kernel: one tile per workgroup, full K; grid (row tiles, column-tile slots).
 // ---------------------------------------------------------------------------------------------
-template <int T, int J>
-__global__ __launch_bounds__(Cfg<J>::NT, 2) void mmq_id_kernel(const uint8_t *__restrict__ w, int64_t rows, int64_t k,
+template <int T, int J, bool GLU>
+__global__ __launch_bounds__(Cfg<J>::NT, 2) void mmq_id_kernel(const uint8_t *__restrict__ w,
+                                                            const uint8_t *__restrict__ w2, int64_t rows, int64_t k,
                                                             const uint8_t *__restrict__ xq, float *__restrict__ y,
                                                             ColMap cm, int32_t n_exp) {
     extern __shared__ __align__(16) uint8_t sm[];
@@ -787,8 +855,7 @@ __global__ __launch_bounds__(Cfg<J>::NT, 2) void mmq_id_kernel(const uint8_t *__
     const int64_t cnt = cm.bounds[e + 1] - seg;
     const int64_t nb32 = k / 32;
     const int64_t row_bytes = (k / Fmt<T>::QK) * Fmt<T>::BYTES;
-    const uint8_t *wbase = w + (int64_t)e * cm.w_expert_stride;
-    const int64_t r0 = (int64_t)blockIdx.x * kTI;
+    const int64_t r0 = (int64_t)blockIdx.x * (GLU ? kTI / 2 : kTI);
     const int64_t c0 = jt * J;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
 
@@ -808,18 +875,28 @@ __global__ __launch_bounds__(Cfg<J>::NT, 2) void mmq_id_kernel(const uint8_t *__
     for (int cb = 0; cb < Cfg<J>::NCB; ++cb) acc[cb] = f32x16{};
 
     const int64_t k_iters = (k + kSuper - 1) / kSuper;
-    run_tile<T, J, false>(sm, acc, wbase, row_bytes, r0, rows, 0, k_iters, nb32, xq, acol, nullptr, cnt, c0,
-                          cm.act_rows);
+    const WRows<GLU> wr{w + (int64_t)e * cm.w_expert_stride, GLU ? w2 + (int64_t)e * cm.w_expert_stride : nullptr,
+                        row_bytes, r0, rows};
+    run_tile<T, J, false>(sm, acc, wr, 0, k_iters, nb32, xq, acol, nullptr, cnt, c0, cm.act_rows);
     const int rw = wid & 3, cw = wid >> 2;
 #pragma unroll
     for (int cb = 0; cb < Cfg<J>::NCB; ++cb) {
         const int64_t c = c0 + Cfg<J>::JW * cw + 32 * cb + (lane & 31);
         if (c >= cnt) continue;
         const int64_t orow = cm.sorted[seg + c];
+        if constexpr (GLU) {
 #pragma unroll
-        for (int e2 = 0; e2 < 16; ++e2) {
-            const int64_t r = r0 + 32 * rw + 4 * (lane >> 5) + 8 * (e2 >> 2) + (e2 & 3);
-            if (r < rows) y[orow * rows + r] = acc[cb][e2];
+            for (int q = 0; q < 8; ++q) {
+                const int e2 = (q & 3) + 8 * (q >> 2);
+                const int64_t r = r0 + 16 * rw + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
+                if (r < rows) y[orow * rows + r] = swiglu(acc[cb][e2], acc[cb][e2 + 4]);
+            }
+        } else {
+#pragma unroll
+            for (int e2 = 0; e2 < 16; ++e2) {
+                const int64_t r = r0 + 32 * rw + 4 * (lane >> 5) + 8 * (e2 >> 2) + (e2 & 3);
+                if (r < rows) y[orow * rows + r] = acc[cb][e2];
+            }
         }
     }
 }
@@ -869,10 +946,42 @@ hipError_t launch_mmq(int type, const uint8_t *w, int64_t rows, int64_t k, const
 }
 
 template <int T, int J>
-static hipError_t launch_mmq_id_t(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, float *y,
-                                  const ColMap &cm, int32_t n_exp, int64_t max_ct, hipStream_t s) {
+static hipError_t launch_mmq_glu_t(const uint8_t *wg, const uint8_t *wu, int64_t rows, int64_t k, const uint8_t *xq,
+                                   int64_t n, float *y, hipStream_t s) {
     constexpr int smem = kSmemBytes<T, J>;
-    auto kern = mmq_id_kernel<T, J>;
+    auto kern = mmq_glu_kernel<T, J>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    const int64_t n_ct = (n + J - 1) / J;
+    const int64_t ntiles = ((rows + kTI / 2 - 1) / (kTI / 2)) * n_ct;
+    hipLaunchKernelGGL(kern, dim3((unsigned)ntiles), dim3(Cfg<J>::NT), smem, s, wg, wu, rows, k, xq, n, y, ntiles, n_ct);
+    return hipGetLastError();
+}
+
+hipError_t launch_mmq_glu(int type, const uint8_t *wg, const uint8_t *wu, int64_t rows, int64_t k, const uint8_t *xq,
+                          int64_t n, float *y, int tile_j, hipStream_t s) {
+#define QMM_MG(TT)                                                                                    \
+    if (type == TT) {                                                                                 \
+        if (tile_j == 32) return launch_mmq_glu_t<TT, 32>(wg, wu, rows, k, xq, n, y, s);             \
+        if (tile_j == 64) return launch_mmq_glu_t<TT, 64>(wg, wu, rows, k, xq, n, y, s);             \
+        if (tile_j == 128) return launch_mmq_glu_t<TT, 128>(wg, wu, rows, k, xq, n, y, s);           \
+    }
+    QMM_MG(kQ4_K)
+    QMM_MG(kQ6_K)
+    QMM_MG(kQ8_0)
+#undef QMM_MG
+    return hipErrorInvalidValue;
+}
+
+template <int T, int J, bool GLU>
+static hipError_t launch_mmq_id_t(const uint8_t *w, const uint8_t *w2, int64_t rows, int64_t k, const uint8_t *xq,
+                                  float *y, const ColMap &cm, int32_t n_exp, int64_t max_ct, hipStream_t s) {
+    constexpr int smem = kSmemBytes<T, J>;
+    auto kern = mmq_id_kernel<T, J, GLU>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
@@ -880,18 +989,28 @@ static hipError_t launch_mmq_id_t(const uint8_t *w, int64_t rows, int64_t k, con
         attr_set = true;
     }
     if (max_ct <= 0) return hipSuccess;
-    dim3 grid((unsigned)((rows + kTI - 1) / kTI), (unsigned)max_ct);
-    hipLaunchKernelGGL(kern, grid, dim3(Cfg<J>::NT), smem, s, w, rows, k, xq, y, cm, n_exp);
+    constexpr int64_t TR = GLU ? kTI / 2 : kTI;   // outputs per row tile
+    dim3 grid((unsigned)((rows + TR - 1) / TR), (unsigned)max_ct);
+    hipLaunchKernelGGL(kern, grid, dim3(Cfg<J>::NT), smem, s, w, w2, rows, k, xq, y, cm, n_exp);
     return hipGetLastError();
 }
 
-hipError_t launch_mmq_id(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, float *y,
-                         const ColMap &cm, int tile_j, int64_t max_col_tiles, hipStream_t s) {
+template <int T, bool GLU>
+static hipError_t launch_mmq_id_j(const uint8_t *w, const uint8_t *w2, int64_t rows, int64_t k, const uint8_t *xq,
+                                  float *y, const ColMap &cm, int tile_j, int64_t max_ct, hipStream_t s) {
+    if (tile_j == 32) return launch_mmq_id_t<T, 32, GLU>(w, w2, rows, k, xq, y, cm, cm.n_exp, max_ct, s);
+    if (tile_j == 64) return launch_mmq_id_t<T, 64, GLU>(w, w2, rows, k, xq, y, cm, cm.n_exp, max_ct, s);
+    if (tile_j == 128) return launch_mmq_id_t<T, 128, GLU>(w, w2, rows, k, xq, y, cm, cm.n_exp, max_ct, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_mmq_id(int type, const uint8_t *w, const uint8_t *w_up, int64_t rows, int64_t k,
+                         const uint8_t *xq, float *y, const ColMap &cm, int tile_j, int64_t max_col_tiles,
+                         hipStream_t s) {
 #define QMM_MQI(TT)                                                                                   \
     if (type == TT) {                                                                                 \
-        if (tile_j == 32) return launch_mmq_id_t<TT, 32>(w, rows, k, xq, y, cm, cm.n_exp, max_col_tiles, s); \
-        if (tile_j == 64) return launch_mmq_id_t<TT, 64>(w, rows, k, xq, y, cm, cm.n_exp, max_col_tiles, s); \
-        if (tile_j == 128) return launch_mmq_id_t<TT, 128>(w, rows, k, xq, y, cm, cm.n_exp, max_col_tiles, s); \
+        return w_up ? launch_mmq_id_j<TT, true>(w, w_up, rows, k, xq, y, cm, tile_j, max_col_tiles, s)    \
+                    : launch_mmq_id_j<TT, false>(w, nullptr, rows, k, xq, y, cm, tile_j, max_col_tiles, s); \
     }
     QMM_MQI(kQ4_K)
     QMM_MQI(kQ6_K)

@@ -22,6 +22,9 @@
 //                                       constant -32 operand, chained through the accumulator)
 //   Q8_0  acc += D * d_w * d_a
 // Partial sums are combined with lane shuffles, then across waves in LDS in a fixed order.
+// GLU (gate/up fusion, the MMQ page's fusion passage): the workgroup's 16 rows are 8 gate rows
+// (lanes r16 < 8) and the same 8 rows of the up matrix (r16 >= 8); the write-back applies
+// silu(gate) * up.
 #include "common.hpp"
 #include "launch.hpp"
 #include "mv_cols.hpp"
@@ -297,16 +300,18 @@ template <> struct MvStep<kQ8_0> {
 
 constexpr int mv_max_waves(int spw) { return spw == 1 ? 16 : spw == 2 ? 8 : 4; }
 
-template <int T, int SPW, bool DBG, bool EXPERT>
-__global__ __launch_bounds__(64 * mv_max_waves(SPW)) void mmvq_kernel(const uint8_t *__restrict__ w, int64_t rows, int64_t k,
+template <int T, int SPW, bool DBG, bool EXPERT, bool GLU>
+__global__ __launch_bounds__(64 * mv_max_waves(SPW)) void mmvq_kernel(const uint8_t *__restrict__ w,
+                                                    const uint8_t *__restrict__ w2, int64_t rows, int64_t k,
                                                     const uint8_t *__restrict__ xq, int64_t n, float *__restrict__ y,
                                                     int32_t *__restrict__ dbg, ColMap cm) {
+    static_assert(!(GLU && DBG), "no debug export of the fused form");
     extern __shared__ __align__(16) uint8_t mv_smem[];
     using S = MvStep<T>;
     constexpr int NCG = S::NCG;
 
     MvCols mc;
-    if (!mv_resolve(mc, w, n, cm, EXPERT)) return;   // workgroup-uniform
+    if (!mv_resolve(mc, w, n, cm, EXPERT, GLU ? w2 : nullptr)) return;   // workgroup-uniform
     const int ncols = mc.ncols;
 
     const int lane = threadIdx.x & 63;
@@ -315,7 +320,7 @@ __global__ __launch_bounds__(64 * mv_max_waves(SPW)) void mmvq_kernel(const uint
     const int64_t nb = k / 32;                         // q8_1 blocks per activation row
     const int64_t row_bytes = (k / Fmt<T>::QK) * Fmt<T>::BYTES;
     const int64_t nsteps = (k + kSuper - 1) / kSuper;
-    const int64_t row0 = (int64_t)blockIdx.x * kMvRows;
+    const int64_t row0 = (int64_t)blockIdx.x * (GLU ? kMvRows / 2 : kMvRows);
     const uint8_t *wg = mc.wbase + row0 * row_bytes;   // uniform base of the 16-row group
     float2 *sTab = (float2 *)mv_smem;                          // [nb][8] (d, s)
     float *sRed = (float *)(mv_smem + nb * 8 * sizeof(float2)); // [nwaves][128]
@@ -323,9 +328,15 @@ __global__ __launch_bounds__(64 * mv_max_waves(SPW)) void mmvq_kernel(const uint
     MvLane L;
     L.g = lane >> 4;
     L.r16 = lane & 15;
-    const int64_t row = row0 + L.r16;
+    const int64_t row = row0 + (GLU ? (L.r16 & 7) : L.r16);   // GLU: output row of the lane's gate/up row
     const int64_t rclamp = row < rows ? row : rows - 1;
-    L.wrow_off = (uint32_t)((rclamp - row0) * row_bytes);
+    if constexpr (GLU) {
+        // per-lane base: gate rows for r16 < 8, up rows for r16 >= 8 (two separate matrices)
+        wg = (L.r16 < 8 ? mc.wbase : mc.wbase2) + rclamp * row_bytes;
+        L.wrow_off = 0;
+    } else {
+        L.wrow_off = (uint32_t)((rclamp - row0) * row_bytes);
+    }
     const int m = L.r16;
     S::lane_setup(L, m);
 #pragma unroll
@@ -412,38 +423,43 @@ __global__ __launch_bounds__(64 * mv_max_waves(SPW)) void mmvq_kernel(const uint
             for (int e = 0; e < 4; ++e) sRed[wave * 128 + lane * (4 * NCG) + cg * 4 + e] = acc[cg][e];
     }
     __syncthreads();
-    if (wave != 0 || !holder || row >= rows) return;
+    if (wave != 0 || !holder || row >= rows || (GLU && L.r16 >= 8)) return;
 #pragma unroll
     for (int cg = 0; cg < NCG; ++cg)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            float v = 0.f;
-            for (int wv = 0; wv < nwaves; ++wv) v += sRed[wv * 128 + lane * (4 * NCG) + cg * 4 + e];
+            float v = 0.f, u = 0.f;
+            for (int wv = 0; wv < nwaves; ++wv) {
+                v += sRed[wv * 128 + lane * (4 * NCG) + cg * 4 + e];
+                if (GLU) u += sRed[wv * 128 + (lane + 8) * (4 * NCG) + cg * 4 + e];   // the up row
+            }
             const int c = (T == kQ6_K) ? 4 * cg + e : 4 * L.g + e;
-            if (c < ncols) y[mc.pair(c) * rows + row] = v;
+            if (c < ncols) y[mc.pair(c) * rows + row] = GLU ? v / (1.0f + expf(-v)) * u : v;
         }
 }
 
 static int g_mv_spw = 0;   // 0: automatic
 
-template <int T, int SPW, bool DBG, bool EXPERT>
+template <int T, int SPW, bool DBG, bool EXPERT, bool GLU = false>
 static hipError_t launch_mmvq_spw(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y,
-                                  int32_t *dbg, const ColMap &c, int64_t n_exp, hipStream_t s) {
+                                  int32_t *dbg, const ColMap &c, int64_t n_exp, hipStream_t s,
+                                  const uint8_t *w2 = nullptr) {
     const int64_t nsteps = (k + kSuper - 1) / kSuper;
     int64_t nw = (nsteps + SPW - 1) / SPW;
     if (nw > mv_max_waves(SPW)) nw = mv_max_waves(SPW);
     if (nw < 1) nw = 1;
-    dim3 grid((unsigned)((rows + kMvRows - 1) / kMvRows), EXPERT ? (unsigned)n_exp : 1u);
+    constexpr int RW = GLU ? kMvRows / 2 : kMvRows;   // outputs per workgroup
+    dim3 grid((unsigned)((rows + RW - 1) / RW), EXPERT ? (unsigned)n_exp : 1u);
     const size_t smem = (size_t)(k / 32) * 8 * sizeof(float2) + (size_t)nw * 128 * sizeof(float);
     static bool attr = false;
     if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void *)mmvq_kernel<T, SPW, DBG, EXPERT>,
+        hipError_t e = hipFuncSetAttribute((const void *)mmvq_kernel<T, SPW, DBG, EXPERT, GLU>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
         attr = true;
     }
-    hipLaunchKernelGGL((mmvq_kernel<T, SPW, DBG, EXPERT>), grid, dim3(64 * (unsigned)nw), smem, s, w, rows, k, xq, n,
-                       y, dbg, c);
+    hipLaunchKernelGGL((mmvq_kernel<T, SPW, DBG, EXPERT, GLU>), grid, dim3(64 * (unsigned)nw), smem, s, w, w2, rows, k,
+                       xq, n, y, dbg, c);
     return hipGetLastError();
 }
 
@@ -541,6 +557,25 @@ hipError_t launch_mmvq(int type, const uint8_t *w, int64_t rows, int64_t k, cons
     QMM_MV(kQ6_K)
     QMM_MV(kQ8_0)
 #undef QMM_MV
+    return hipErrorInvalidValue;
+}
+
+}  // namespace qmm
+
+namespace qmm {
+
+hipError_t launch_mmvq_glu(int type, const uint8_t *wg, const uint8_t *wu, int64_t rows, int64_t k, const uint8_t *xq,
+                           int64_t n, float *y, const ColMap *cm, int64_t n_exp, hipStream_t s) {
+    const ColMap c = cm ? *cm : ColMap{};
+#define QMM_MVG(TT)                                                                                      \
+    if (type == TT) {                                                                                  \
+        if (cm) return launch_mmvq_spw<TT, 2, false, true, true>(wg, rows, k, xq, n, y, nullptr, c, n_exp, s, wu); \
+        return launch_mmvq_spw<TT, 2, false, false, true>(wg, rows, k, xq, n, y, nullptr, c, n_exp, s, wu);     \
+    }
+    QMM_MVG(kQ4_K)
+    QMM_MVG(kQ6_K)
+    QMM_MVG(kQ8_0)
+#undef QMM_MVG
     return hipErrorInvalidValue;
 }
 

@@ -11,6 +11,7 @@ struct MvCols {
     int ncols;
     int lo;
     const uint8_t *wbase;
+    const uint8_t *wbase2;   // gate/up fusion: the up matrix (wbase the gate)
     bool expert;
     ColMap cm;
     __device__ __forceinline__ int64_t pair(int c) const { return expert ? cm.sorted[lo + c] : c; }
@@ -23,8 +24,9 @@ struct MvCols {
 };
 
 __device__ __forceinline__ bool mv_resolve(MvCols &mc, const uint8_t *w, int64_t n, const ColMap &cm,
-                                           bool expert) {
+                                           bool expert, const uint8_t *w2 = nullptr) {
     mc.wbase = w;
+    mc.wbase2 = w2;
     mc.expert = expert;
     mc.cm = cm;
     mc.lo = 0;
@@ -37,6 +39,7 @@ __device__ __forceinline__ bool mv_resolve(MvCols &mc, const uint8_t *w, int64_t
     mc.lo = cm.bounds[e];
     mc.ncols = cm.bounds[e + 1] - mc.lo;
     mc.wbase = w + (int64_t)e * cm.w_expert_stride;
+    if (w2) mc.wbase2 = w2 + (int64_t)e * cm.w_expert_stride;
     return true;
 }
 

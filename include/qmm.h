@@ -124,6 +124,31 @@ qmm_status qmm_matmul_id_grouping_layout(int type, int64_t n_exp, int64_t k, int
                                          int64_t top_k, int64_t x_per_tok, int64_t *out);
 
 /* ---------------------------------------------------------------------------------------------
+ * Gate/up products fused with SwiGLU ([MMQ] the fusion passage after "MoE dispatch": the gate and
+ * up products of one input are computed together and the GLU is applied at write-back; SwiGLU
+ * read as silu(g) * u, silu(g) = g / (1 + exp(-g))).
+ * qmm_matmul_glu: y[n][rows] = silu(W_gate . x) * (W_up . x) elementwise; w_gate and w_up are two
+ *   [rows][k] matrices of the same type (2-byte aligned), x fp32 [n][k] (16-byte aligned).  n <= 8:
+ *   the matrix-vector kernel with 8 gate and 8 up rows per workgroup; otherwise the tiled kernel
+ *   with tiles of 64 outputs whose 128 weight rows alternate in groups of 8 between gate and up
+ *   (no stream-K: the two products of an output must meet in one workgroup).  Workspace:
+ *   qmm_matmul_glu_workspace bytes, 256-byte aligned.
+ * qmm_matmul_id_glu: the expert form; w_gate and w_up hold n_exp matrices each (as qmm_matmul_id),
+ *   x fp32 [n_tok][k] (one row per token, shared by its slots), y fp32 [n_tok][top_k][rows].
+ *   Grouping, small-expert dispatch, invalid-id handling and the workspace counter as
+ *   qmm_matmul_id; workspace qmm_matmul_id_glu_workspace bytes.
+ * The same shape rules and errors as the unfused calls; a null w_up is QMM_ERR_ARG.
+ * ------------------------------------------------------------------------------------------- */
+size_t qmm_matmul_glu_workspace(int type, int64_t rows, int64_t k, int64_t n);
+qmm_status qmm_matmul_glu(int type, const void *w_gate, const void *w_up, int64_t rows, int64_t k,
+                          const float *x, int64_t n, float *y, void *ws, size_t ws_bytes, void *stream);
+size_t qmm_matmul_id_glu_workspace(int type, int64_t n_exp, int64_t rows, int64_t k, int64_t n_tok,
+                                   int64_t top_k);
+qmm_status qmm_matmul_id_glu(int type, const void *w_gate, const void *w_up, int64_t n_exp, int64_t rows,
+                             int64_t k, const float *x, const int32_t *ids, int64_t n_tok, int64_t top_k,
+                             float *y, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Test hook: the integer sub-block dots from the production kernels' own integer accumulators
  * ([MMQ] "write-back": the integer part is exact).  path: 1 = matrix-vector kernel,
  * 2 = tiled MFMA kernel.  d_out: int32 [n][rows][per] with

@@ -143,6 +143,31 @@ def test_argument_validation_without_gpu():
     assert L.qmm_debug_subdots(qmm.Q4_K, null, 16, 256, null, 9, 1, null, null) == -1
 
 
+def test_glu_argument_validation_without_gpu():
+    L = qmm.lib()
+    null = ctypes.c_void_p(0)
+    one = ctypes.c_void_p(4096)   # a non-null address, never dereferenced: the calls fail first
+    assert L.qmm_matmul_glu(13, null, null, 16, 256, null, 1, null, null, 0, null) == -2
+    assert L.qmm_matmul_glu(qmm.Q4_K, null, null, 16, 100, null, 1, null, null, 0, null) == -3
+    assert L.qmm_matmul_glu(qmm.Q4_K, null, null, 16, 256, null, 0, null, null, 0, null) == 0
+    # null up matrix with columns to compute
+    assert L.qmm_matmul_glu(qmm.Q4_K, one, null, 16, 256, one, 1, one, null, 0, null) == -1
+    assert b"w_up" in L.qmm_last_error()
+    # workspace too small (host check, before any launch)
+    assert L.qmm_matmul_glu(qmm.Q4_K, one, one, 16, 256, one, 1, one, null, 0, null) == -4
+    assert L.qmm_matmul_id_glu(qmm.Q4_K, one, null, 4, 16, 256, one, one, 8, 2, one, null, 0, null) == -1
+    assert L.qmm_matmul_id_glu(qmm.Q4_K, null, null, 4, 16, 256, null, null, 8, 0, null, null, 0, null) == -1
+
+
+def test_glu_workspace_sizes():
+    # matrix-vector form: the q8_1 copy of x; tiled form: the tiled activation layout, no partials
+    assert qmm.matmul_glu_workspace(qmm.Q4_K, 4096, 4096, 3) >= 3 * 4096 // 32 * 36
+    assert qmm.matmul_glu_workspace(qmm.Q4_K, 14336, 4096, 512) >= 512 * 4096 // 32 * 36
+    assert qmm.matmul_glu_workspace(qmm.Q4_K, 14336, 4096, 512) < qmm.matmul_workspace(qmm.Q4_K, 14336, 4096, 512)
+    assert qmm.matmul_id_glu_workspace(qmm.Q4_K, 8, 768, 2048, 64, 8) == \
+        qmm.matmul_id_workspace(qmm.Q4_K, 8, 768, 2048, 64, 8, 1)
+
+
 def test_workspace_sizes_monotone():
     # matrix-vector from q8_1 input needs no workspace; from fp32 it holds the q8_1 codes
     assert qmm.matmul_q8_1_workspace(qmm.Q4_K, 4096, 4096, 1) == 0
