@@ -420,6 +420,13 @@ qmm_status qmm_matmul_glu(int type, const void *w_gate, const void *w_up, int64_
     uint8_t *wsb = (uint8_t *)ws;
     const uint8_t *wg = (const uint8_t *)w_gate, *wu = (const uint8_t *)w_up;
     hipError_t e;
+    if (glu_matvec(n, k) && n <= 3 && g_ovr_path.load() == 0 && qmm::mmvq_dot4_supported(type, wg, k, x, nullptr) &&
+        qmm::mmvq_dot4_supported(type, wu, k, x, nullptr)) {
+        // 1..3 columns: the dot4 kernel, quantizing x itself (one launch)
+        e = qmm::launch_mmvq_dot4_glu_f32(type, wg, wu, rows, k, x, n, y, s);
+        if (e != hipSuccess) return hip_fail(e, "fused matrix-vector kernel launch");
+        return QMM_OK;
+    }
     if (glu_matvec(n, k)) {
         e = qmm::launch_quantize_q8_1(x, n, k, wsb, s);
         if (e != hipSuccess) return hip_fail(e, "quantize launch");

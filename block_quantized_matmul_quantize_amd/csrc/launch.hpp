@@ -43,6 +43,11 @@ hipError_t launch_mmvq(int type, const uint8_t *w, int64_t rows, int64_t k, cons
 hipError_t launch_mmvq_glu(int type, const uint8_t *wg, const uint8_t *wu, int64_t rows, int64_t k, const uint8_t *xq,
                            int64_t n, float *y, const ColMap *cm, int64_t n_exp, hipStream_t s);
 
+// The same on the dot4 kernel for 1..3 dense fp32 columns (quantized inside); Q4_K and Q8_0 under
+// mmvq_dot4_supported's alignment rules for both matrices.
+hipError_t launch_mmvq_dot4_glu_f32(int type, const uint8_t *wg, const uint8_t *wu, int64_t rows, int64_t k,
+                                    const float *x, int64_t n, float *y, hipStream_t s);
+
 // fp32-input matrix-vector product with the q8_1 quantization done inside the dot4 or the
 // LDS-staged kernel (no separate quantize launch): dense calls either kernel would take.
 bool mmvq_fused_applies(int type, const void *w, int64_t k, const float *x, int64_t n);

@@ -16,6 +16,8 @@
 //   Q4_K  acc += D(2g)*(d*sc)*d_a - (dmin*m)*s_a   (+ the same for sub-block 2g+1)
 //   Q8_0  acc += D*d_w*d_a                         (both blocks)
 // The four quarters of a row are summed with lane shuffles, the waves in LDS in a fixed order.
+// GLU (gate/up fusion, the MMQ page's fusion passage): rows 0-7 of the workgroup are 8 gate rows,
+// rows 8-15 the same 8 rows of the up matrix, and the write-back applies silu(gate) * up.
 // Requirements (checked by the host): K a multiple of 256; Q4_K weights and rows 16-byte
 // aligned, Q8_0 4-byte aligned; activations 4-byte aligned.
 #include "common.hpp"
@@ -69,8 +71,9 @@ template <int T> struct StepBytes;
 template <> struct StepBytes<kQ4_K> { static constexpr int V = 144; };
 template <> struct StepBytes<kQ8_0> { static constexpr int V = 272; };
 
-template <int T, int NC, bool DBG, bool EXPERT, bool F32>
-__global__ __launch_bounds__(1024) void mmvq_dot4_kernel(const uint8_t *__restrict__ w, const void *__restrict__ xin,
+template <int T, int NC, bool DBG, bool EXPERT, bool F32, bool GLU>
+__global__ __launch_bounds__(1024) void mmvq_dot4_kernel(const uint8_t *__restrict__ w, const uint8_t *__restrict__ w2,
+                                                        const void *__restrict__ xin,
                                                         float *__restrict__ y, int32_t *__restrict__ dbg, D4Args P,
                                                         ColMap cm) {
     extern __shared__ __align__(16) uint8_t smem[];
@@ -83,10 +86,17 @@ __global__ __launch_bounds__(1024) void mmvq_dot4_kernel(const uint8_t *__restri
     const int r = lane >> 2, g = lane & 3;
     const int64_t rows = P.rows;
     const uint32_t nb = P.nb;
-    const int64_t row0 = (int64_t)blockIdx.x * kRows;
+    static_assert(!GLU || (!DBG && !EXPERT), "the fused form is dense only");
+    const int64_t row0 = (int64_t)blockIdx.x * (GLU ? kRows / 2 : kRows);
     const int rmax = (int)((rows - row0) < kRows ? (rows - row0) : kRows) - 1;
     const uint8_t *wg = mc.wbase + row0 * (int64_t)P.row_bytes;
-    const uint32_t woff = (uint32_t)(r < rmax ? r : rmax) * P.row_bytes;   // rows past the end re-read the last
+    uint32_t woff = (uint32_t)(r < rmax ? r : rmax) * P.row_bytes;   // rows past the end re-read the last
+    if constexpr (GLU) {
+        // per-lane base: gate row r or up row r - 8 of output row0 + r % 8 (clamped)
+        const int64_t orow = row0 + (r & 7) < rows ? row0 + (r & 7) : rows - 1;
+        wg = (r < 8 ? w : w2) + orow * (int64_t)P.row_bytes;
+        woff = 0;
+    }
     const int my_steps = P.q + (wave < P.r ? 1 : 0);
 
     W4<T> cur;
@@ -240,16 +250,19 @@ __global__ __launch_bounds__(1024) void mmvq_dot4_kernel(const uint8_t *__restri
     }
     __syncthreads();
     const int t = threadIdx.x;
-    if (t >= 16 * NC) return;
-    float v = 0.f;
-    for (int wv = 0; wv < nwaves; ++wv) v += red[wv * (16 * NC) + t];
+    if (t >= (GLU ? 8 : 16) * NC) return;
+    float v = 0.f, u = 0.f;
+    for (int wv = 0; wv < nwaves; ++wv) {
+        v += red[wv * (16 * NC) + t];
+        if (GLU) u += red[wv * (16 * NC) + 8 * NC + t];   // the up row of the same output
+    }
     const int rr = t / NC, c = t - rr * NC;
-    if (c < ncols && row0 + rr < rows) y[mc.pair(c) * rows + row0 + rr] = v;
+    if (c < ncols && row0 + rr < rows) y[mc.pair(c) * rows + row0 + rr] = GLU ? v / (1.0f + expf(-v)) * u : v;
 }
 
-template <int T, int NC, bool DBG, bool EXPERT, bool F32 = false>
+template <int T, int NC, bool DBG, bool EXPERT, bool F32 = false, bool GLU = false>
 hipError_t launch_nc(const uint8_t *w, int64_t rows, int64_t k, const void *xq, int64_t n, float *y, int32_t *dbg,
-                     const ColMap &cm, int64_t n_exp, hipStream_t s) {
+                     const ColMap &cm, int64_t n_exp, hipStream_t s, const uint8_t *w2 = nullptr) {
     const int64_t nsteps = k / kSuper;
     const int nw = (int)(nsteps < 16 ? nsteps : 16);
     D4Args a;
@@ -263,14 +276,15 @@ hipError_t launch_nc(const uint8_t *w, int64_t rows, int64_t k, const void *xq, 
     const size_t smem = (size_t)NC * a.nb * 40 + (size_t)nw * 16 * NC * sizeof(float);
     static bool attr = false;
     if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void *)mmvq_dot4_kernel<T, NC, DBG, EXPERT, F32>,
+        hipError_t e = hipFuncSetAttribute((const void *)mmvq_dot4_kernel<T, NC, DBG, EXPERT, F32, GLU>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
         attr = true;
     }
-    dim3 grid((unsigned)((rows + kRows - 1) / kRows), EXPERT ? (unsigned)n_exp : 1u);
-    hipLaunchKernelGGL((mmvq_dot4_kernel<T, NC, DBG, EXPERT, F32>), grid, dim3(64 * (unsigned)nw), smem, s, w, xq, y, dbg, a,
-                       cm);
+    constexpr int RW = GLU ? kRows / 2 : kRows;   // outputs per workgroup
+    dim3 grid((unsigned)((rows + RW - 1) / RW), EXPERT ? (unsigned)n_exp : 1u);
+    hipLaunchKernelGGL((mmvq_dot4_kernel<T, NC, DBG, EXPERT, F32, GLU>), grid, dim3(64 * (unsigned)nw), smem, s, w, w2,
+                       xq, y, dbg, a, cm);
     return hipGetLastError();
 }
 
@@ -325,6 +339,21 @@ hipError_t launch_mmvq_dot4_f32(int type, const uint8_t *w, int64_t rows, int64_
     QMM_D4F(kQ4_K)
     QMM_D4F(kQ8_0)
 #undef QMM_D4F
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_mmvq_dot4_glu_f32(int type, const uint8_t *wg, const uint8_t *wu, int64_t rows, int64_t k,
+                                    const float *x, int64_t n, float *y, hipStream_t s) {
+    const ColMap c{};
+#define QMM_D4G(TT)                                                                                            \
+    if (type == TT) {                                                                                         \
+        if (n <= 1) return launch_nc<TT, 1, false, false, true, true>(wg, rows, k, x, n, y, nullptr, c, 0, s, wu); \
+        if (n == 2) return launch_nc<TT, 2, false, false, true, true>(wg, rows, k, x, n, y, nullptr, c, 0, s, wu); \
+        return launch_nc<TT, 3, false, false, true, true>(wg, rows, k, x, n, y, nullptr, c, 0, s, wu);              \
+    }
+    QMM_D4G(kQ4_K)
+    QMM_D4G(kQ8_0)
+#undef QMM_D4G
     return hipErrorInvalidValue;
 }
 
