@@ -420,14 +420,15 @@ qmm_status qmm_matmul_glu(int type, const void *w_gate, const void *w_up, int64_
     uint8_t *wsb = (uint8_t *)ws;
     const uint8_t *wg = (const uint8_t *)w_gate, *wu = (const uint8_t *)w_up;
     hipError_t e;
-    if (glu_matvec(n, k) && n <= 3 && g_ovr_path.load() == 0 && qmm::mmvq_dot4_supported(type, wg, k, x, nullptr) &&
-        qmm::mmvq_dot4_supported(type, wu, k, x, nullptr)) {
-        // 1..3 columns: the dot4 kernel, quantizing x itself (one launch)
-        e = qmm::launch_mmvq_dot4_glu_f32(type, wg, wu, rows, k, x, n, y, s);
-        if (e != hipSuccess) return hip_fail(e, "fused matrix-vector kernel launch");
-        return QMM_OK;
-    }
     if (glu_matvec(n, k)) {
+        // the dot4 or LDS-staged kernel quantizing x itself (one launch), as for one matrix
+        const int kc = qmm::mmvq_glu_f32_choice(type, wg, wu, k, x, n);
+        if (kc == 3 || kc == 2) {
+            e = kc == 3 ? qmm::launch_mmvq_dot4_glu_f32(type, wg, wu, rows, k, x, n, y, s)
+                        : qmm::launch_mmvq_stream_glu(type, wg, wu, rows, k, x, true, n, y, nullptr, 0, s);
+            if (e != hipSuccess) return hip_fail(e, "fused matrix-vector kernel launch");
+            return QMM_OK;
+        }
         e = qmm::launch_quantize_q8_1(x, n, k, wsb, s);
         if (e != hipSuccess) return hip_fail(e, "quantize launch");
         e = qmm::launch_mmvq_glu(type, wg, wu, rows, k, wsb, n, y, nullptr, 0, s);

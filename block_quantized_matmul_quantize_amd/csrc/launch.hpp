@@ -38,8 +38,10 @@ struct ColMap {
 hipError_t launch_mmvq(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n,
                        float *y, int32_t *dbg, const ColMap *cm, int64_t n_exp, hipStream_t s);
 
-// Gate/up fusion on the register-streamed matrix-vector kernel: y = silu(W_gate x) * (W_up x)
-// for n <= 8 dense columns (cm null) or the small experts (cm set, grid.y = n_exp).
+// Gate/up fusion, matrix-vector: y = silu(W_gate x) * (W_up x) for n <= 8 dense q8_1 columns (cm
+// null) or the small experts (cm set, grid.y = n_exp); the LDS-staged kernel where both matrices
+// meet its rules, else the register-streamed one.
+int mmvq_glu_f32_choice(int type, const void *wg, const void *wu, int64_t k, const float *x, int64_t n);
 hipError_t launch_mmvq_glu(int type, const uint8_t *wg, const uint8_t *wu, int64_t rows, int64_t k, const uint8_t *xq,
                            int64_t n, float *y, const ColMap *cm, int64_t n_exp, hipStream_t s);
 
@@ -47,6 +49,12 @@ hipError_t launch_mmvq_glu(int type, const uint8_t *wg, const uint8_t *wu, int64
 // mmvq_dot4_supported's alignment rules for both matrices.
 hipError_t launch_mmvq_dot4_glu_f32(int type, const uint8_t *wg, const uint8_t *wu, int64_t rows, int64_t k,
                                     const float *x, int64_t n, float *y, hipStream_t s);
+
+// And on the LDS-staged kernel (mmvq_stream_supported's rules for both matrices): dense fp32
+// (x_fp32, quantized inside) or q8_1 columns, or the small experts (cm set, q8_1).
+hipError_t launch_mmvq_stream_glu(int type, const uint8_t *wg, const uint8_t *wu, int64_t rows, int64_t k,
+                                  const void *x, bool x_fp32, int64_t n, float *y, const ColMap *cm, int64_t n_exp,
+                                  hipStream_t s);
 
 // fp32-input matrix-vector product with the q8_1 quantization done inside the dot4 or the
 // LDS-staged kernel (no separate quantize launch): dense calls either kernel would take.

@@ -564,8 +564,14 @@ hipError_t launch_mmvq(int type, const uint8_t *w, int64_t rows, int64_t k, cons
 
 namespace qmm {
 
+// Gate/up fusion from q8_1 columns (dense or the small experts): the LDS-staged kernel where both
+// matrices meet its alignment rules (and no override forces the register-streamed one), else the
+// register-streamed kernel.
 hipError_t launch_mmvq_glu(int type, const uint8_t *wg, const uint8_t *wu, int64_t rows, int64_t k, const uint8_t *xq,
                            int64_t n, float *y, const ColMap *cm, int64_t n_exp, hipStream_t s) {
+    if (g_mv_kernel != 1 && g_mv_kernel != 3 && mmvq_stream_supported(type, wg, k, xq, cm) &&
+        mmvq_stream_supported(type, wu, k, xq, cm))
+        return launch_mmvq_stream_glu(type, wg, wu, rows, k, xq, false, n, y, cm, n_exp, s);
     const ColMap c = cm ? *cm : ColMap{};
 #define QMM_MVG(TT)                                                                                      \
     if (type == TT) {                                                                                  \
@@ -577,6 +583,14 @@ hipError_t launch_mmvq_glu(int type, const uint8_t *wg, const uint8_t *wu, int64
     QMM_MVG(kQ8_0)
 #undef QMM_MVG
     return hipErrorInvalidValue;
+}
+
+// Kernel for a dense fp32-input gate/up call of n <= 8 columns, as fused_kernel decides for one
+// matrix, with both matrices checked: 3 dot4, 2 LDS-staged (both quantize x themselves), 0 none
+// (quantize first, then launch_mmvq_glu).
+int mmvq_glu_f32_choice(int type, const void *wg, const void *wu, int64_t k, const float *x, int64_t n) {
+    const int a = fused_kernel(type, wg, k, x, n), b = fused_kernel(type, wu, k, x, n);
+    return a == b ? a : 0;
 }
 
 }  // namespace qmm

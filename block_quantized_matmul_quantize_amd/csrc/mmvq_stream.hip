@@ -24,6 +24,9 @@
 // (q8_1.hpp) -- one launch instead of two.
 // Requirements (checked by the host): K a multiple of 256; Q4_K and Q6_K weights and rows 16-byte
 // aligned, Q8_0 weights 4-byte aligned; q8_1 activations 4-byte aligned (fp32: 16-byte).
+// GLU (gate/up fusion, the MMQ page's fusion passage): the 16 rows are 8 gate rows (load
+// instructions 0-1) and the same 8 rows of the up matrix (instructions 2-3); the write-back applies
+// silu(gate) * up.
 #include "common.hpp"
 #include "launch.hpp"
 #include "mv_cols.hpp"
@@ -101,8 +104,9 @@ struct MvArgs {
     int32_t n;            // dense column count
 };
 
-template <int T, bool DBG, bool EXPERT, bool F32>
-__global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__restrict__ w, const void *__restrict__ xin,
+template <int T, bool DBG, bool EXPERT, bool F32, bool GLU>
+__global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__restrict__ w, const uint8_t *__restrict__ w2,
+                                                          const void *__restrict__ xin,
                                                           float *__restrict__ y, int32_t *__restrict__ dbg,
                                                           MvArgs P, ColMap cm) {
     using S = Stage<T>;
@@ -112,16 +116,19 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
     extern __shared__ __align__(16) uint8_t smem[];
 
     MvCols mc;
-    if (!mv_resolve(mc, w, P.n, cm, EXPERT)) return;   // workgroup-uniform
+    static_assert(!(GLU && DBG), "no debug export of the fused form");
+    if (!mv_resolve(mc, w, P.n, cm, EXPERT, GLU ? w2 : nullptr)) return;   // workgroup-uniform
     const int ncols = mc.ncols;                           // >= 1
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int nwaves = blockDim.x >> 6;
     const int64_t rows = P.rows;
     const uint32_t row_bytes = P.row_bytes, col_bytes = P.col_bytes;
-    const int64_t row0 = (int64_t)blockIdx.x * kRows;
-    const int rmax = (int)((rows - row0) < kRows ? (rows - row0) : kRows) - 1;   // last live row of the group
+    constexpr int RW = GLU ? kRows / 2 : kRows;   // outputs per workgroup
+    const int64_t row0 = (int64_t)blockIdx.x * RW;
+    const int rmax = (int)((rows - row0) < RW ? (rows - row0) : RW) - 1;   // last live output row of the group
     const uint8_t *wg = mc.wbase + row0 * (int64_t)row_bytes;
+    const uint8_t *wg2 = GLU ? mc.wbase2 + row0 * (int64_t)row_bytes : wg;   // up rows (GLU)
     uint8_t *zero = smem + (size_t)wave * (kHead + SB);   // zero block (off-diagonal A lanes)
     uint8_t *st = zero + kHead;                            // this wave's stage
     constexpr int kSink = kZeroBytes - kHead;              // sink offset relative to st
@@ -139,24 +146,26 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
     int32_t pofs[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int r = 4 * i + rq;
-        wofs[i] = (uint32_t)(r < rmax ? r : rmax) * row_bytes + 16u * (jq < PM ? jq : 0);
+        const int r = 4 * i + rq, ro = GLU ? (r & 7) : r;
+        wofs[i] = (uint32_t)(ro < rmax ? ro : rmax) * row_bytes + 16u * (jq < PM ? jq : 0);
         pofs[i] = jq < PM ? r * RSTR + 16 * jq : kSink;
     }
-    const uint32_t wofs8 = (uint32_t)(r8 < rmax ? r8 : rmax) * row_bytes + 68u * p8;
+    const int ro8 = GLU ? (r8 & 7) : r8;
+    const uint32_t wofs8 = (uint32_t)(ro8 < rmax ? ro8 : rmax) * row_bytes + 68u * p8;
+    const uint8_t *wg8 = (GLU && r8 >= 8) ? wg2 : wg;
 
     u32x4 wv[4];
     uint32_t wv4 = 0;
     auto load_w = [&](int s) __attribute__((always_inline)) {
         if constexpr (T == kQ8_0) {
-            const uint8_t *src = wg + (uint32_t)(s * 272) + wofs8;
+            const uint8_t *src = wg8 + (uint32_t)(s * 272) + wofs8;
 #pragma unroll
             for (int i = 0; i < 4; ++i) wv[i] = *(const u32x4_a4 *)(src + 16 * i);
             wv4 = *(const uint32_t *)(src + 64);
         } else {
-            const uint8_t *wstep = wg + ((uint32_t)(s * Geo<T>::STEP) & ~15u);
+            const uint32_t so = (uint32_t)(s * Geo<T>::STEP) & ~15u;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) wv[i] = *(const u32x4 *)(wstep + wofs[i]);
+            for (int i = 0; i < 4; ++i) wv[i] = *(const u32x4 *)(((GLU && i >= 2) ? wg2 : wg) + so + wofs[i]);
         }
     };
 
@@ -490,17 +499,24 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
     // 128 threads each sum one (row, column) over the waves, all loads in flight at once.
     const int t = threadIdx.x;
     if (t >= 128) return;
-    float v = 0.f;
-    for (int wv = 0; wv < nwaves; ++wv) v += ((const float *)(smem + (size_t)wv * (kHead + SB) + kHead))[t];
     int rr, c;
     if (T == kQ6_K) { rr = t >> 3; c = t & 7; }
     else { rr = (t >> 2) & 15; c = 4 * (t >> 6) + (t & 3); }
-    if (c < ncols && row0 + rr < rows) y[mc.pair(c) * rows + row0 + rr] = v;
+    if (GLU && rr >= 8) return;
+    // GLU: the up value of (rr, c) sits at row rr + 8: index t + 64 (Q6_K) or t + 32
+    constexpr int kUp = T == kQ6_K ? 64 : 32;
+    float v = 0.f, u = 0.f;
+    for (int wv = 0; wv < nwaves; ++wv) {
+        const float *rb = (const float *)(smem + (size_t)wv * (kHead + SB) + kHead);
+        v += rb[t];
+        if (GLU) u += rb[t + kUp];
+    }
+    if (c < ncols && row0 + rr < rows) y[mc.pair(c) * rows + row0 + rr] = GLU ? v / (1.0f + expf(-v)) * u : v;
 }
 
-template <int T, bool DBG, bool EXPERT, bool F32 = false>
+template <int T, bool DBG, bool EXPERT, bool F32 = false, bool GLU = false>
 hipError_t launch_t(const uint8_t *w, int64_t rows, int64_t k, const void *xq, int64_t n, float *y,
-                    int32_t *dbg, const ColMap &c, int64_t n_exp, hipStream_t s) {
+                    int32_t *dbg, const ColMap &c, int64_t n_exp, hipStream_t s, const uint8_t *w2 = nullptr) {
     const int64_t nsteps = k / kSuper;
     const int nw = (int)(nsteps < 16 ? nsteps : 16);
     const size_t smem = (size_t)nw * (kHead + Stage<T>::BYTES);
@@ -514,14 +530,15 @@ hipError_t launch_t(const uint8_t *w, int64_t rows, int64_t k, const void *xq, i
     a.n = (int32_t)n;
     static bool attr = false;
     if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void *)mmvq_stream_kernel<T, DBG, EXPERT, F32>,
+        hipError_t e = hipFuncSetAttribute((const void *)mmvq_stream_kernel<T, DBG, EXPERT, F32, GLU>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
         if (e != hipSuccess) return e;
         attr = true;
     }
-    dim3 grid((unsigned)((rows + kRows - 1) / kRows), EXPERT ? (unsigned)n_exp : 1u);
-    hipLaunchKernelGGL((mmvq_stream_kernel<T, DBG, EXPERT, F32>), grid, dim3(64 * (unsigned)nw), smem, s, w, xq, y, dbg,
-                       a, c);
+    constexpr int RW = GLU ? kRows / 2 : kRows;
+    dim3 grid((unsigned)((rows + RW - 1) / RW), EXPERT ? (unsigned)n_exp : 1u);
+    hipLaunchKernelGGL((mmvq_stream_kernel<T, DBG, EXPERT, F32, GLU>), grid, dim3(64 * (unsigned)nw), smem, s, w, w2, xq,
+                       y, dbg, a, c);
     return hipGetLastError();
 }
 
@@ -561,6 +578,23 @@ hipError_t launch_mmvq_stream(int type, const uint8_t *w, int64_t rows, int64_t 
     if (type == kQ4_K) return dispatch<kQ4_K>(w, rows, k, xq, n, y, dbg, cm, n_exp, s);
     if (type == kQ6_K) return dispatch<kQ6_K>(w, rows, k, xq, n, y, dbg, cm, n_exp, s);
     if (type == kQ8_0) return dispatch<kQ8_0>(w, rows, k, xq, n, y, dbg, cm, n_exp, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_mmvq_stream_glu(int type, const uint8_t *wg, const uint8_t *wu, int64_t rows, int64_t k,
+                                  const void *x, bool x_fp32, int64_t n, float *y, const ColMap *cm, int64_t n_exp,
+                                  hipStream_t s) {
+    const ColMap c = cm ? *cm : ColMap{};
+#define QMM_SG(TT)                                                                                                   \
+    if (type == TT) {                                                                                                \
+        if (cm) return launch_t<TT, false, true, false, true>(wg, rows, k, x, n, y, nullptr, c, n_exp, s, wu);     \
+        if (x_fp32) return launch_t<TT, false, false, true, true>(wg, rows, k, x, n, y, nullptr, c, 0, s, wu);     \
+        return launch_t<TT, false, false, false, true>(wg, rows, k, x, n, y, nullptr, c, 0, s, wu);                \
+    }
+    QMM_SG(kQ4_K)
+    QMM_SG(kQ6_K)
+    QMM_SG(kQ8_0)
+#undef QMM_SG
     return hipErrorInvalidValue;
 }
 

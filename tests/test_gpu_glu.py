@@ -24,10 +24,11 @@ TNAME = {qmm.Q4_K: "q4_K", qmm.Q6_K: "q6_K", qmm.Q8_0: "q8_0"}
 
 @pytest.fixture(autouse=True)
 def _clean_overrides():
-    for key in (qmm.OVR_PATH, qmm.OVR_TILE_J):
+    keys = (qmm.OVR_PATH, qmm.OVR_TILE_J, qmm.OVR_MV_KERNEL)
+    for key in keys:
         qmm.set_override(key, 0)
     yield
-    for key in (qmm.OVR_PATH, qmm.OVR_TILE_J):
+    for key in keys:
         qmm.set_override(key, 0)
 
 
@@ -90,13 +91,25 @@ def test_glu_dense_tile_widths(qtype, J):
     _check_dense(qtype, 300, 1024, 150, 950 + J, f"{TNAME[qtype]} J={J}")
 
 
+@pytest.mark.parametrize("kernel", [0, 1, 2, 3], ids=["auto", "regs", "lds", "dot4"])
+@pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
+@pytest.mark.parametrize("n", [1, 2, 5, 8])
+def test_glu_matvec_kernels(qtype, n, kernel):
+    """Each matrix-vector kernel's fused form (a forced kernel that cannot serve the call falls
+    back to the register-streamed one): 232 rows = 29 workgroups of 8 outputs, the last ragged."""
+    qmm.set_override(qmm.OVR_MV_KERNEL, kernel)
+    _check_dense(qtype, 229, 1024, n, 1200 + 10 * n + kernel, f"{TNAME[qtype]} n={n} kernel={kernel}")
+
+
 def test_glu_dense_tiled_path_for_few_columns():
     qmm.set_override(qmm.OVR_PATH, 2)
     _check_dense(qmm.Q4_K, 136, 768, 5, 990, "q4_K n=5 tiled")
 
 
+@pytest.mark.parametrize("kernel", [0, 1], ids=["auto", "regs"])
 @pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
-def test_glu_expert(qtype):
+def test_glu_expert(qtype, kernel):
+    qmm.set_override(qmm.OVR_MV_KERNEL, kernel)   # the small experts' matrix-vector kernel
     n_exp, rows, k, n_tok, top_k = 10, 136, 512, 150, 2
     g = synth.rngs(1000 + qtype, 4)
     wg = synth.gen_weights(qtype, n_exp * rows, k, g[0])
