@@ -13,7 +13,8 @@ Also in the same JSON line:
                 events on the launch stream; peak = 8 TB/s HBM.  traffic comes from the committed
                 rocprofv3 FETCH_SIZE/WRITE_SIZE summary when it matches the current sources.
   cpu_baseline  the oracle (plain C, all host threads) on whole steps of the same workload.
-  secondary     int8 TOPS and % of the 5.0 POP/s int8 MFMA peak for the prefill and MoE shapes.
+  secondary     int8 TOPS and % of the 5.0 POP/s int8 MFMA peak for the prefill and MoE shapes, and
+                for the gate/up products fused with SwiGLU (decode: also GB/s of the two matrices).
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-secondary]
        python bench.py --secondary-only [--calib-copy]   only the prefill / MoE shapes (profiling)
@@ -397,6 +398,39 @@ def run_secondary(torch, np, qmm, synth, dev, log):
                     "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4), "cache": "weights resident (warm)"})
         log(f"[bench] {c['name']:36s} {us:9.1f} us {tops:8.1f} TOPS")
         del wd
+    # gate/up products fused with SwiGLU (one call for both matrices)
+    for c in synth.GLU_CASES:
+        wg, wu, x, ids = synth.make_glu(c)
+        xd = torch.from_numpy(x).to(dev)
+        if c["kind"] == "dense":
+            nrot = max(1, min(8, int(np.ceil(512e6 / (2 * wg.nbytes)))))
+            gs = [torch.roll(torch.from_numpy(wg).to(dev), r, 0) for r in range(nrot)]
+            us_ = [torch.roll(torch.from_numpy(wu).to(dev), r, 0) for r in range(nrot)]
+            y = torch.empty((c["n"], c["rows"]), dtype=torch.float32, device=dev)
+            wsb = qmm._workspace(qmm.matmul_glu_workspace(c["qtype"], c["rows"], c["k"], c["n"]), dev)
+            us = timed(lambda r: qmm.matmul_glu(gs[r % nrot], us_[r % nrot], c["qtype"], c["rows"], c["k"], xd,
+                                                out=y, ws=wsb), warm=2 * nrot)
+            cols = c["n"]
+            del gs, us_
+        else:
+            wgd, wud = torch.from_numpy(wg).to(dev), torch.from_numpy(wu).to(dev)
+            idd = torch.from_numpy(ids).to(dev)
+            out = torch.empty((c["n_tok"], c["top_k"], c["rows"]), dtype=torch.float32, device=dev)
+            wsb = qmm._workspace(qmm.matmul_id_glu_workspace(c["qtype"], c["n_exp"], c["rows"], c["k"], c["n_tok"],
+                                                             c["top_k"]), dev)
+            us = timed(lambda r: qmm.matmul_id_glu(wgd, wud, c["qtype"], c["n_exp"], c["rows"], c["k"], xd, idd,
+                                                   out=out, ws=wsb), warm=8)
+            cols = c["n_tok"] * c["top_k"]
+            del wgd, wud
+        ops = 2.0 * 2 * c["rows"] * c["k"] * cols
+        entry = {"case": c["name"], "us": round(us, 1), "TOPS": round(ops / us / 1e6, 1),
+                 "frac_int8_peak": round(ops / us / 1e6 / INT8_PEAK_TOPS, 4)}
+        if c["kind"] == "dense" and c["n"] <= 8:
+            gbs = 2.0 * wg.nbytes / us / 1e3
+            entry["GBps_weights"] = round(gbs, 1)
+            entry["frac_hbm"] = round(gbs / HBM_PEAK_GBPS, 4)
+        res.append(entry)
+        log(f"[bench] {c['name']:36s} {us:9.1f} us {ops / us / 1e6:8.1f} TOPS")
     return res
 
 

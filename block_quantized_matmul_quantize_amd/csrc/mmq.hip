@@ -841,8 +841,18 @@ __global__ __launch_bounds__(Cfg<J>::NT, 2) void mmq_id_kernel(const uint8_t *__
                                                             ColMap cm, int32_t n_exp) {
     extern __shared__ __align__(16) uint8_t sm[];
     constexpr int NA = J * 8 / Cfg<J>::NT, NT = Cfg<J>::NT;
-    const int64_t ct = blockIdx.y;
-    if (ct >= cm.tile_start[n_exp]) return;
+    // The grid is sized for the most column tiles the call can have; the valid ones are
+    // tile_start[n_exp] (device).  Valid (row tile, column tile) pairs are numbered in the dense
+    // kernel's banded order and dealt out in contiguous ranges per XCD (hardware workgroup b runs
+    // on XCD b % 8), so an XCD walks an expert's column tiles back to back with that expert's
+    // weight rows in its L2; workgroups past the valid count exit.
+    const int64_t V = cm.tile_start[n_exp];
+    const int64_t total = (int64_t)gridDim.x * V;
+    const int64_t b = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+    const int64_t xcd = b % 8, slot = b / 8, q8 = total / 8, r8 = total % 8;
+    if (slot >= q8 + (xcd < r8 ? 1 : 0)) return;
+    int64_t rt, ct;
+    tile_coords(xcd * q8 + (xcd < r8 ? xcd : r8) + slot, total, V, rt, ct);
     // expert owning column tile ct: largest e with tile_start[e] <= ct
     int lo = 0, hi = n_exp - 1;
     while (lo < hi) {
@@ -855,7 +865,7 @@ __global__ __launch_bounds__(Cfg<J>::NT, 2) void mmq_id_kernel(const uint8_t *__
     const int64_t cnt = cm.bounds[e + 1] - seg;
     const int64_t nb32 = k / 32;
     const int64_t row_bytes = (k / Fmt<T>::QK) * Fmt<T>::BYTES;
-    const int64_t r0 = (int64_t)blockIdx.x * (GLU ? kTI / 2 : kTI);
+    const int64_t r0 = rt * (GLU ? kTI / 2 : kTI);
     const int64_t c0 = jt * J;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
 

@@ -101,6 +101,29 @@ MOE_CASES = [
 ]
 
 
+# Gate/up products fused with SwiGLU: two matrices of `rows` rows each.
+GLU_CASES = [
+    dict(name="ffn gate/up+swiglu q4_K 2x14336x4096 N=1", kind="dense", qtype=Q4_K, rows=14336, k=4096, n=1),
+    dict(name="ffn gate/up+swiglu q4_K 2x14336x4096 T=512", kind="dense", qtype=Q4_K, rows=14336, k=4096, n=512),
+    dict(name="moe 128x gate/up+swiglu q4_K 2x768x2048, 2048 tok top-8 zipf1.0", kind="moe", qtype=Q4_K,
+         n_exp=128, rows=768, k=2048, n_tok=2048, top_k=8, zipf=1.0, x_per_tok=1),
+]
+
+
+def make_glu(case, seed=0):
+    """(w_gate, w_up, x, ids or None) of a GLU case."""
+    if case["kind"] == "dense":
+        g_g, g_u, g_x = rngs(seed, 3)
+        return (gen_weights(case["qtype"], case["rows"], case["k"], g_g),
+                gen_weights(case["qtype"], case["rows"], case["k"], g_u),
+                gen_activations(case["n"], case["k"], g_x), None)
+    g_g, g_u, g_x, g_r = rngs(seed, 4)
+    nr = case["n_exp"] * case["rows"]
+    return (gen_weights(case["qtype"], nr, case["k"], g_g), gen_weights(case["qtype"], nr, case["k"], g_u),
+            gen_activations(case["n_tok"], case["k"], g_x),
+            gen_routing(case["n_tok"], case["top_k"], case["n_exp"], case["zipf"], g_r))
+
+
 def make_dense(case, seed=0):
     g_w, g_x = rngs(seed, 2)
     w = gen_weights(case["qtype"], case["rows"], case["k"], g_w)
