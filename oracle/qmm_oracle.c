@@ -12,6 +12,9 @@
  *    activation half2 (d, s) and s = d*sum(q) are described).
  *  - Q4_K weights: value = d*sc*q - dmin*m over 32-value sub-blocks of a 144-byte super-block
  *    ("llama.cpp MMQ" page, "why not dequantize" and "Q4_K load" sections).
+ *  - Q5_K weights: as Q4_K with a fifth code bit, value = d*sc*q - dmin*m with q in [0, 31]; the
+ *    pages name Q5_K beside Q4_K and give the two the same 6-bit scale/min packing ("llama.cpp MMQ"
+ *    page, "Q4_K load" section); the byte layout is GGUF's block_q5_K.
  *  - Q6_K weights: value = d*sc*(q - 32), 6-bit q built from 4 low bits (ql) and 2 high bits (qh),
  *    signed 8-bit scale per 16 values ("llama.cpp MMQ" page, "Q6_K load" and "Q6_K dot" sections).
  *  - Q8_0 weights: value = d*q, int8 q, fp16 d per 32 values (named on the GP100 patch page and the
@@ -26,7 +29,9 @@
  *    amax == 0 gives d = s = 0 and q = 0.
  *  - Block byte layouts follow GGUF: q4_K {d, dmin, scales[12], qs[128]} (144 B),
  *    q6_K {ql[128], qh[64], scales[16], d} (210 B), q8_0 {d, qs[32]} (34 B),
- *    q8_1 {d, s, qs[32]} (36 B); fp16 is little-endian IEEE binary16.
+ *    q8_1 {d, s, qs[32]} (36 B); fp16 is little-endian IEEE binary16.  q5_K {d, dmin, scales[12],
+ *    qh[32], qs[128]} (176 B): the low 4 bits of value v as in Q4_K, the fifth bit is bit v/32 of
+ *    qh[v % 32].
  *  - Q4_K 6-bit scale/min unpacking (the page's description is garbled) follows GGUF:
  *    j < 4: sc = s[j] & 63, m = s[j+4] & 63;
  *    j >= 4: sc = (s[j+4] & 15) | ((s[j-4] >> 6) << 4), m = (s[j+4] >> 4) | ((s[j] >> 6) << 4).
@@ -44,6 +49,7 @@
 
 #define ORC_Q8_0 8
 #define ORC_Q4_K 12
+#define ORC_Q5_K 13
 #define ORC_Q6_K 14
 
 #define ORC_OK 0
@@ -180,6 +186,17 @@ static void decode_q4_K(const uint8_t *blk, double *d, double *dmin, int sc[8], 
     }
 }
 
+/* Q5_K, 176 bytes per 256 values: the Q4_K header (d, dmin, 12 scale bytes), then qh[32], then
+ * qs[128] laid out as Q4_K's.  code[v] in [0,31]: Q4_K's nibble plus 16 * bit (v/32) of qh[v%32]. */
+static void decode_q5_K(const uint8_t *blk, double *d, double *dmin, int sc[8], int m[8], int code[256]) {
+    uint8_t q4[144];
+    memcpy(q4, blk, 16);                 /* same header and scale packing as Q4_K */
+    memcpy(q4 + 16, blk + 48, 128);      /* the low nibbles, in Q4_K's order */
+    decode_q4_K(q4, d, dmin, sc, m, code);
+    const uint8_t *qh = blk + 16;
+    for (int v = 0; v < 256; ++v) code[v] += 16 * ((qh[v % 32] >> (v / 32)) & 1);
+}
+
 /* Q6_K, 210 bytes per 256 values. code[v] in [-32,31] (the 6-bit value minus 32),
  * sc[v/16] signed 8-bit. */
 static void decode_q6_K(const uint8_t *blk, double *d, int sc[16], int code[256]) {
@@ -213,12 +230,13 @@ static void decode_q8_1(const uint8_t *blk, double *d, double *s, int code[32]) 
 }
 
 static int type_block_values(int type) {
-    if (type == ORC_Q4_K || type == ORC_Q6_K) return 256;
+    if (type == ORC_Q4_K || type == ORC_Q5_K || type == ORC_Q6_K) return 256;
     if (type == ORC_Q8_0) return 32;
     return 0;
 }
 static int type_block_bytes(int type) {
     if (type == ORC_Q4_K) return 144;
+    if (type == ORC_Q5_K) return 176;
     if (type == ORC_Q6_K) return 210;
     if (type == ORC_Q8_0) return 34;
     return 0;
@@ -247,9 +265,10 @@ int oracle_dequantize(int type, const uint8_t *w, int64_t rows, int64_t k, doubl
         for (int64_t blk = 0; blk < k / bv; ++blk) {
             const uint8_t *p = w + r * rb + blk * bb;
             double *o = out + r * k + blk * bv;
-            if (type == ORC_Q4_K) {
+            if (type == ORC_Q4_K || type == ORC_Q5_K) {
                 double d, dmin; int sc[8], m[8], code[256];
-                decode_q4_K(p, &d, &dmin, sc, m, code);
+                if (type == ORC_Q4_K) decode_q4_K(p, &d, &dmin, sc, m, code);
+                else decode_q5_K(p, &d, &dmin, sc, m, code);
                 for (int v = 0; v < 256; ++v) o[v] = d * sc[v / 32] * code[v] - dmin * m[v / 32];
             } else if (type == ORC_Q6_K) {
                 double d; int sc[16], code[256];
@@ -318,10 +337,11 @@ static float dot_row_col(int type, const uint8_t *wrow, int64_t k, const act_t *
     const double *da = a->da + col * nb32;
     const double *sa = a->sa + col * nb32;
 
-    if (type == ORC_Q4_K) {
+    if (type == ORC_Q4_K || type == ORC_Q5_K) {
         for (int64_t sb = 0; sb < k / 256; ++sb) {
             double d, dmin; int sc[8], m[8], code[256];
-            decode_q4_K(wrow + sb * 144, &d, &dmin, sc, m, code);
+            if (type == ORC_Q4_K) decode_q4_K(wrow + sb * 144, &d, &dmin, sc, m, code);
+            else decode_q5_K(wrow + sb * 176, &d, &dmin, sc, m, code);
             for (int j = 0; j < 8; ++j) {
                 int64_t b = sb * 8 + j;
                 int32_t Db = 0;

@@ -7,6 +7,7 @@ numbers and places them in the block byte layouts; it holds none of the method's
 Value distributions (the workload descriptions give Q4_K's; the rest are the plainest readings):
   * Q4_K super-block (144 B): fp16 d and dmin ~ U(0.001, 0.02); 12 bytes of uniform random
     6-bit-packed scales/mins; 128 bytes of uniform random nibbles.
+  * Q5_K super-block (176 B): as Q4_K, with 32 bytes of uniform random fifth bits (qh).
   * Q6_K super-block (210 B): uniform random ql (128 B) and qh (64 B); int8 scales ~ U{-32..31};
     fp16 d ~ U(0.001, 0.02).
   * Q8_0 block (34 B): fp16 d ~ U(0.001, 0.02); int8 codes ~ U{-127..127}.
@@ -19,10 +20,11 @@ import numpy as np
 
 Q8_0 = 8
 Q4_K = 12
+Q5_K = 13
 Q6_K = 14
-TYPE_NAMES = {Q8_0: "q8_0", Q4_K: "q4_K", Q6_K: "q6_K"}
-BLOCK_VALUES = {Q8_0: 32, Q4_K: 256, Q6_K: 256}
-BLOCK_BYTES = {Q8_0: 34, Q4_K: 144, Q6_K: 210}
+TYPE_NAMES = {Q8_0: "q8_0", Q4_K: "q4_K", Q5_K: "q5_K", Q6_K: "q6_K"}
+BLOCK_VALUES = {Q8_0: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256}
+BLOCK_BYTES = {Q8_0: 34, Q4_K: 144, Q5_K: 176, Q6_K: 210}
 
 
 def rngs(seed, n):
@@ -42,7 +44,7 @@ def gen_weights(qtype, rows, k, rng):
     assert k % qk == 0
     nb = rows * (k // qk)
     blk = rng.integers(0, 256, size=(nb, bb), dtype=np.uint8)
-    if qtype == Q4_K:
+    if qtype in (Q4_K, Q5_K):
         blk[:, 0:2] = _fp16_bytes(rng.uniform(0.001, 0.02, size=nb))
         blk[:, 2:4] = _fp16_bytes(rng.uniform(0.001, 0.02, size=nb))
     elif qtype == Q6_K:

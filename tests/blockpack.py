@@ -6,6 +6,8 @@ Q4_K size (144 B per 256 values), the half2 (d, dmin), the low/high nibble split
 sub-blocks, and the Q6_K ql/qh bit composition):
 
   q4_K: d f16 @0, dmin f16 @2, 12 bytes of packed 6-bit (sc, m) @4, qs[128] @16
+  q5_K: the q4_K header @0..15, qh[32] @16 (bit j of qh[l] = fifth bit of value 32j + l),
+        qs[128] @48 laid out as q4_K's (the pages give Q5_K the Q4_K scale packing)
   q6_K: ql[128] @0, qh[64] @128, int8 scales[16] @192, d f16 @208
   q8_0: d f16 @0, int8 qs[32] @2
 """
@@ -48,6 +50,20 @@ def pack_q4_K(d, dmin, sc, m, q):
             lo = q[64 * chunk + l]              # first sub-block of the pair -> low nibble
             hi = q[64 * chunk + 32 + l]         # second sub-block -> high nibble
             b[16 + 32 * chunk + l] = lo | (hi << 4)
+    return b
+
+
+def pack_q5_K(d, dmin, sc, m, q):
+    """sc, m: 8 ints in [0,63]; q: 256 ints in [0,31] (value index order).  Returns 176 bytes."""
+    q = [int(v) for v in q]
+    assert len(q) == 256 and all(0 <= v < 32 for v in q)
+    low = pack_q4_K(d, dmin, sc, m, [v & 15 for v in q])
+    b = np.zeros(176, dtype=np.uint8)
+    b[0:16] = low[0:16]
+    b[48:176] = low[16:144]
+    for v in range(256):
+        if q[v] >> 4:
+            b[16 + v % 32] |= 1 << (v // 32)
     return b
 
 
@@ -95,6 +111,19 @@ def random_q4_K_row(rng, k):
     return np.concatenate(blocks), fields
 
 
+def random_q5_K_row(rng, k):
+    blocks, fields = [], []
+    for _ in range(k // 256):
+        d = f16_value(rng.uniform(0.001, 0.02))
+        dmin = f16_value(rng.uniform(0.001, 0.02))
+        sc = rng.integers(0, 64, 8)
+        m = rng.integers(0, 64, 8)
+        q = rng.integers(0, 32, 256)
+        blocks.append(pack_q5_K(d, dmin, sc, m, q))
+        fields.append((d, dmin, sc, m, q))
+    return np.concatenate(blocks), fields
+
+
 def random_q6_K_row(rng, k):
     blocks, fields = [], []
     for _ in range(k // 256):
@@ -117,8 +146,8 @@ def random_q8_0_row(rng, k):
 
 
 def weight_codes(qtype, fields):
-    """Integer weight codes per value (Q4_K: [0,15]; Q6_K: q-32; Q8_0: int8) for one row."""
-    if qtype == 12:
+    """Integer weight codes per value (Q4_K: [0,15]; Q5_K: [0,31]; Q6_K: q-32; Q8_0: int8) for one row."""
+    if qtype in (12, 13):
         return np.concatenate([f[4] for f in fields]).astype(np.int64)
     if qtype == 14:
         return np.concatenate([f[2] for f in fields]).astype(np.int64) - 32

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
-from blockpack import pack_q4_K, pack_q6_K, pack_q8_0, f16_value
+from blockpack import pack_q4_K, pack_q5_K, pack_q6_K, pack_q8_0, f16_value
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -94,6 +94,45 @@ def test_q4_K_single_scale(j):
     w = oracle.dequantize(oracle.Q4_K, pack_q4_K(0.5, 0.25, sc, m, q), 1, 256)[0]
     expect = np.zeros(256); expect[32 * j:32 * j + 32] = 0.5 * 63 * 15 - 0.25 * 33
     assert np.array_equal(w, expect)
+
+
+def test_q5_K_encoder_roundtrip_random():
+    rng = np.random.default_rng(12)
+    for _ in range(50):
+        d, dmin = f16_value(rng.uniform(-2, 2)), f16_value(rng.uniform(-2, 2))
+        sc, m, q = rng.integers(0, 64, 8), rng.integers(0, 64, 8), rng.integers(0, 32, 256)
+        w = oracle.dequantize(oracle.Q5_K, pack_q5_K(d, dmin, sc, m, q), 1, 256)[0]
+        expect = d * np.repeat(sc, 32) * q - dmin * np.repeat(m, 32)
+        assert np.array_equal(w, expect)
+
+
+@pytest.mark.parametrize("v", list(range(0, 256, 7)) + [31, 32, 63, 64, 95, 255])
+@pytest.mark.parametrize("code", [9, 16, 25])
+def test_q5_K_one_hot_position(v, code):
+    """A single nonzero code (low nibble only, fifth bit only, both) lands at its own value."""
+    q = np.zeros(256, dtype=int); q[v] = code
+    w = oracle.dequantize(oracle.Q5_K, pack_q5_K(1.0, 0.0, np.ones(8, int), np.zeros(8, int), q), 1, 256)[0]
+    assert np.nonzero(w)[0].tolist() == [v] and w[v] == float(code)
+
+
+def test_q5_K_fifth_bits_are_bit_j_of_qh_l():
+    """Stated from the layout directly: setting bit j of qh byte l (and nothing else, scale 1)
+    gives the value 16 at position 32*j + l."""
+    for j in range(8):
+        for l in (0, 5, 31):
+            blk = pack_q5_K(1.0, 0.0, np.ones(8, int), np.zeros(8, int), np.zeros(256, int))
+            blk[16 + l] |= 1 << j
+            w = oracle.dequantize(oracle.Q5_K, blk, 1, 256)[0]
+            assert np.nonzero(w)[0].tolist() == [32 * j + l] and w[32 * j + l] == 16.0
+
+
+def test_q5_K_without_fifth_bits_is_q4_K():
+    rng = np.random.default_rng(13)
+    d, dmin = f16_value(0.37), f16_value(0.11)
+    sc, m, q = rng.integers(0, 64, 8), rng.integers(0, 64, 8), rng.integers(0, 16, 256)
+    w5 = oracle.dequantize(oracle.Q5_K, pack_q5_K(d, dmin, sc, m, q), 1, 256)[0]
+    w4 = oracle.dequantize(oracle.Q4_K, pack_q4_K(d, dmin, sc, m, q), 1, 256)[0]
+    assert np.array_equal(w5, w4)
 
 
 def test_q6_K_encoder_roundtrip_random():
