@@ -15,6 +15,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "qmm.h")
 
 Q8_0 = 8
 Q4_K = 12
+Q5_K = 13
 Q6_K = 14
 BLOCK_VALUES = {Q8_0: 32, Q4_K: 256, Q6_K: 256}
 BLOCK_BYTES = {Q8_0: 34, Q4_K: 144, Q6_K: 210}

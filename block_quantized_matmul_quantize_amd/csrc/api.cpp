@@ -42,7 +42,7 @@ constexpr int kSmallMax = 8;           // experts with <= 8 columns use the matr
 
 int block_values(int type) {
     switch (type) {
-        case QMM_Q4_K: case QMM_Q6_K: return 256;
+        case QMM_Q4_K: case QMM_Q5_K: case QMM_Q6_K: return 256;
         case QMM_Q8_0: return 32;
         default: return 0;
     }
@@ -50,6 +50,7 @@ int block_values(int type) {
 int block_bytes(int type) {
     switch (type) {
         case QMM_Q4_K: return 144;
+        case QMM_Q5_K: return 176;
         case QMM_Q6_K: return 210;
         case QMM_Q8_0: return 34;
         default: return 0;
@@ -74,7 +75,7 @@ int device_cus() {
 
 qmm_status check_common(int type, int64_t rows, int64_t k, int64_t n) {
     const int qk = block_values(type);
-    if (qk == 0) return fail(QMM_ERR_TYPE, "unsupported weight type %d (supported: Q8_0=8, Q4_K=12, Q6_K=14)", type);
+    if (qk == 0) return fail(QMM_ERR_TYPE, "unsupported weight type %d (supported: Q8_0=8, Q4_K=12, Q5_K=13, Q6_K=14)", type);
     if (rows <= 0) return fail(QMM_ERR_ARG, "rows must be >= 1 (got %lld)", (long long)rows);
     if (n < 0) return fail(QMM_ERR_ARG, "n must be >= 0 (got %lld)", (long long)n);
     if (k <= 0 || k % qk != 0) return fail(QMM_ERR_SHAPE, "k=%lld is not a positive multiple of the block size %d", (long long)k, qk);
@@ -87,10 +88,12 @@ qmm_status check_common(int type, int64_t rows, int64_t k, int64_t n) {
 // LDS bytes of one tiled-kernel workgroup (the Smem layout in mmq.hip): weight tile, fp32 row
 // scales (and Q4_K mins), activation codes, fp32 (d, s).
 int mmq_smem(int type, int J) {
-    const int wt = type == QMM_Q4_K ? kTI * 144 : (type == QMM_Q6_K ? 2 * kTI * 272 : kTI * 272);
-    const int wm = type == QMM_Q4_K ? kTI * 48 + 8 * J * 4 : 0;   // bf16 pieces of the mins and of s
+    const bool k45 = type == QMM_Q4_K || type == QMM_Q5_K;
+    const int wt = k45 ? kTI * 144 + (type == QMM_Q5_K ? kTI * 32 : 0)   // packed qs (+ Q5_K qh)
+                       : (type == QMM_Q6_K ? 2 * kTI * 272 : kTI * 272);
+    const int wm = k45 ? kTI * 48 + 8 * J * 4 : 0;   // bf16 pieces of the mins and of s
     const int one = wt + 8 * kTI * 4 + wm + J * 272 + 8 * (J + 4) * 8;
-    return type == QMM_Q4_K && J == 128 ? 2 * one : one;             // Q4_K 8-wave tiles: two step buffers
+    return k45 && J == 128 ? 2 * one : one;   // Q4_K / Q5_K 8-wave tiles: two step buffers
 }
 
 // Tiled-kernel workgroups resident per compute unit: the kernels keep about 200 registers per

@@ -8,11 +8,13 @@ namespace qmm {
 
 constexpr int kQ8_0 = 8;
 constexpr int kQ4_K = 12;
+constexpr int kQ5_K = 13;
 constexpr int kQ6_K = 14;
 
 // GGUF block geometry.
 template <int T> struct Fmt;
 template <> struct Fmt<kQ4_K> { static constexpr int QK = 256, BYTES = 144; };
+template <> struct Fmt<kQ5_K> { static constexpr int QK = 256, BYTES = 176; };
 template <> struct Fmt<kQ6_K> { static constexpr int QK = 256, BYTES = 210; };
 template <> struct Fmt<kQ8_0> { static constexpr int QK = 32, BYTES = 34; };
 

@@ -72,23 +72,29 @@ template <int J> struct Cfg {
     static constexpr int NCB = JW / 32;             // 32-column MFMA blocks per wave
 };
 
+// Q4_K and Q5_K share the super-block header, the scale/min packing and the fixup (the MMQ page
+// pairs them in its "Q4_K load" section); Q5_K adds a fifth code bit per value.
+template <int T> constexpr bool kK45 = T == kQ4_K || T == kQ5_K;
+
 // LDS layout of one step.
 template <int T, int J> struct Smem {
-    static constexpr int W_BYTES = T == kQ4_K ? kTI * kLd4 : (T == kQ6_K ? 2 * kTI * kLd : kTI * kLd);
+    static constexpr int W_BYTES = kK45<T> ? kTI * kLd4 + (T == kQ5_K ? kTI * 32 : 0)   // qs (+ Q5_K qh)
+                                          : (T == kQ6_K ? 2 * kTI * kLd : kTI * kLd);
     static constexpr int W_OFF = 0;
+    static constexpr int QH_OFF = kTI * kLd4;                                     // Q5_K qh [128][32]
     static constexpr int WS_OFF = W_OFF + W_BYTES;                               // float [8][128]
     static constexpr int WM_OFF = WS_OFF + 8 * kTI * 4;                          // Q4_K: bf16 pieces of -dmin*m,
-    static constexpr int A_OFF = WM_OFF + (T == kQ4_K ? kTI * 48 : 0);          // [128][half][piece][4]; int8 [J][kLd]
+    static constexpr int A_OFF = WM_OFF + (kK45<T> ? kTI * 48 : 0);             // [128][half][piece][4]; int8 [J][kLd]
     static constexpr int XS = J + 4;                                             // (d, s) row stride: the
     static constexpr int X_OFF = A_OFF + J * kLd;                                // float2 [8][XS] (8 blocks of a
     static constexpr int XB_OFF = X_OFF + 8 * XS * 8;                            // column land in 2-way banks)
                                                                                  // then bf16 pieces of s [J][8] (Q4_K)
-    static constexpr int BYTES = XB_OFF + (T == kQ4_K ? 8 * J * 4 : 0);
+    static constexpr int BYTES = XB_OFF + (kK45<T> ? 8 * J * 4 : 0);
 };
 
 // Two LDS step buffers where they fit beside the occupancy the tile runs at: Q4_K 8-wave tiles
 // (one workgroup per CU either way, 2 x 68 KB).
-template <int T, int J> constexpr bool kDoubleBuffer = T == kQ4_K && J == 128;
+template <int T, int J> constexpr bool kDoubleBuffer = kK45<T> && J == 128;
 template <int T, int J> constexpr int kSmemBytes = (kDoubleBuffer<T, J> ? 2 : 1) * Smem<T, J>::BYTES;
 
 // ---------------------------------------------------------------------------------------------
@@ -143,7 +149,7 @@ template <int J, bool TILED, bool RAGGED> struct ActFetch {
             *(u32x4 *)(sA + col * kLd + 32 * blk) = c0[it];
             *(u32x4 *)(sA + col * kLd + 32 * blk + 16) = c1[it];
             sX[blk * Smem<T, J>::XS + col] = make_float2(h2f((uint16_t)(ds[it] & 0xFFFF)), h2f((uint16_t)(ds[it] >> 16)));
-            if constexpr (T == kQ4_K) {   // s = t1 + t2 exactly in bf16: the B operand of the min term
+            if constexpr (kK45<T>) {   // s = t1 + t2 exactly in bf16: the B operand of the min term
                 const float sf = h2f((uint16_t)(ds[it] >> 16));
                 const uint32_t t1 = bf16_bits(sf);
                 ((uint32_t *)(sm + Smem<T, J>::XB_OFF))[col * 8 + blk] = t1 | (bf16_bits(sf - bf16_val(t1)) << 16);
@@ -180,30 +186,43 @@ template <int T, int NT> struct WFetch;
 
 // Q4_K: qs pieces (row i/8, 16-byte piece i%8 of the 128 qs bytes) and the row headers (threads
 // below 128, whole waves).
-template <int NT> struct WFetch<kQ4_K, NT> {
-    static constexpr int N = 1024 / NT;
-    u32x4 q[N], h;
+// Q5_K: the same, with the qs bytes 32 bytes further (after qh[32]) and the two 16-byte qh pieces
+// of each row (threads below 256, whole waves) parked beside the qs.
+template <int T, int NT> struct WFetchK45 {
+    static constexpr int N = 1024 / NT, NH = T == kQ5_K ? (256 + NT - 1) / NT : 0;
+    static constexpr int BB = Fmt<T>::BYTES, QS = T == kQ5_K ? 48 : 16;   // block bytes, qs offset
+    u32x4 q[N], h, qh[NH > 0 ? NH : 1];
     template <class WR>
     __device__ __forceinline__ void fetch(const WR &wr, int64_t kb, int64_t) {
         const int tid = threadIdx.x;
 #pragma unroll
         for (int it = 0; it < N; ++it) {
             const int i = tid + NT * it;
-            q[it] = ld16(wr.row(i >> 3) + kb * 144 + 16 + 16 * (i & 7));
+            q[it] = ld16(wr.row(i >> 3) + kb * BB + QS + 16 * (i & 7));
         }
-        if (tid < kTI) h = ld16(wr.row(tid) + kb * 144);
+        if (tid < kTI) h = ld16(wr.row(tid) + kb * BB);
+#pragma unroll
+        for (int it = 0; it < NH; ++it) {
+            const int i = tid + NT * it;
+            if (i < 256) qh[it] = ld16(wr.row(i >> 1) + kb * BB + 16 + 16 * (i & 1));
+        }
     }
     template <int J, class WR>
     __device__ __forceinline__ void store(uint8_t *sm, const WR &, int64_t, int64_t) const {
         const int tid = threadIdx.x;
-        uint8_t *sW = sm + Smem<kQ4_K, J>::W_OFF;
+        uint8_t *sW = sm + Smem<T, J>::W_OFF;
 #pragma unroll
         for (int it = 0; it < N; ++it) {
             const int i = tid + NT * it;
             *(u32x4 *)(sW + (i >> 3) * kLd4 + 16 * (i & 7)) = q[it];
         }
+#pragma unroll
+        for (int it = 0; it < NH; ++it) {
+            const int i = tid + NT * it;
+            if (i < 256) *(u32x4 *)(sm + Smem<T, J>::QH_OFF + (i >> 1) * 32 + 16 * (i & 1)) = qh[it];
+        }
         if (tid < kTI) {
-            float *sWs = (float *)(sm + Smem<kQ4_K, J>::WS_OFF);
+            float *sWs = (float *)(sm + Smem<T, J>::WS_OFF);
             const float d = h2f((uint16_t)(h.x & 0xFFFF)), dmin = h2f((uint16_t)(h.x >> 16));
             const uint32_t sc_lo = h.y & 0x3F3F3F3Fu, m_lo = h.z & 0x3F3F3F3Fu;
             const uint32_t sc_hi = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
@@ -231,13 +250,16 @@ template <int NT> struct WFetch<kQ4_K, NT> {
                     wv[6 * hf + 2 * m] = pc[m][4 * hf] | (pc[m][4 * hf + 1] << 16);
                     wv[6 * hf + 2 * m + 1] = pc[m][4 * hf + 2] | (pc[m][4 * hf + 3] << 16);
                 }
-            u32x4 *dst = (u32x4 *)(sm + Smem<kQ4_K, J>::WM_OFF + tid * 48);
+            u32x4 *dst = (u32x4 *)(sm + Smem<T, J>::WM_OFF + tid * 48);
             dst[0] = u32x4{wv[0], wv[1], wv[2], wv[3]};
             dst[1] = u32x4{wv[4], wv[5], wv[6], wv[7]};
             dst[2] = u32x4{wv[8], wv[9], wv[10], wv[11]};
         }
     }
 };
+
+template <int NT> struct WFetch<kQ4_K, NT> : WFetchK45<kQ4_K, NT> {};
+template <int NT> struct WFetch<kQ5_K, NT> : WFetchK45<kQ5_K, NT> {};
 
 // Q8_0: 16 code bytes per (row, block, half) and the fp16 d per (row, block); blocks past the end
 // of a ragged last step read as zero.
@@ -403,7 +425,7 @@ template <int NT> struct WFetch<kQ6_K, NT> : std::conditional<(NT >= 512), WFetc
 // Q4_K tile time).  The tile loop builds the seed once and makes it opaque, so that it stays in
 // registers instead of being rebuilt every step.  Q8_0 would qualify too but its tiles run out of
 // registers with the 16 seed registers; Q6_K's scale-folded dots can exceed the range.
-template <int T, bool DBG> constexpr bool kSeeded = !DBG && T == kQ4_K;
+template <int T, bool DBG> constexpr bool kSeeded = !DBG && kK45<T>;   // Q5_K: |D| <= 32*31*127 too
 constexpr int32_t kBiasBits = 0x4B400000;
 constexpr float kBias = 12582912.0f;   // 1.5 * 2^23
 
@@ -463,16 +485,26 @@ __device__ __forceinline__ void tile_step(const uint8_t *sm, f32x16 (&acc)[Cfg<J
         }
     };
 
-    if constexpr (T == kQ4_K) {
+    if constexpr (kK45<T>) {
         const uint8_t *sW = sm + L::W_OFF;
+        // Q5_K: qh bytes 16h..16h+15 of the lane's row; bit sb of byte l is the fifth bit of value
+        // l of sub-block sb
+        u32x4 qh = {0u, 0u, 0u, 0u};
+        if constexpr (T == kQ5_K) qh = *(const u32x4 *)(sm + L::QH_OFF + arow * 32 + koff);
 #pragma unroll 1
         for (int sb = 0; sb < 8; ++sb) {
             // qs bytes 32*(sb/2)+16h .. +15: low nibbles = values 16h.. of the even sub-block of
             // the pair, high nibbles = of the odd one
             const u32x4 q = *(const u32x4 *)(sW + arow * kLd4 + 32 * (sb >> 1) + koff);
             const int sh = 4 * (sb & 1);
-            const u32x4 aop = {(q.x >> sh) & 0x0F0F0F0Fu, (q.y >> sh) & 0x0F0F0F0Fu, (q.z >> sh) & 0x0F0F0F0Fu,
-                               (q.w >> sh) & 0x0F0F0F0Fu};
+            u32x4 aop = {(q.x >> sh) & 0x0F0F0F0Fu, (q.y >> sh) & 0x0F0F0F0Fu, (q.z >> sh) & 0x0F0F0F0Fu,
+                         (q.w >> sh) & 0x0F0F0F0Fu};
+            if constexpr (T == kQ5_K) {
+                aop.x |= ((qh.x >> sb) & 0x01010101u) << 4;
+                aop.y |= ((qh.y >> sb) & 0x01010101u) << 4;
+                aop.z |= ((qh.z >> sb) & 0x01010101u) << 4;
+                aop.w |= ((qh.w >> sb) & 0x01010101u) << 4;
+            }
             f32x16 S[NCB];
             if (!DBG) scales(sb, sWs[sb * kTI + arow], S);
 #pragma unroll
@@ -551,9 +583,9 @@ __device__ __forceinline__ void tile_step(const uint8_t *sm, f32x16 (&acc)[Cfg<J
 // overflow): -dmin*m = p0 + p1 + p2 and s_a = t1 + t2 exactly, every product p*t is exact in fp32,
 // and three K = 16 MFMAs per column block sum them -- MFMA m, lane (row, h), slots 2q and 2q+1
 // hold p_m of sub-block 4h+q against t1 and t2 of the same sub-block.
-template <int J>
+template <int T, int J>
 __device__ __forceinline__ void q4k_min_term(const uint8_t *sm, f32x16 (&acc)[Cfg<J>::NCB]) {
-    using L = Smem<kQ4_K, J>;
+    using L = Smem<T, J>;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int rw = wid & 3, cw = wid >> 2, h = lane >> 5;
     const int arow = 32 * rw + (lane & 31), colw = Cfg<J>::JW * cw + (lane & 31);
@@ -632,7 +664,7 @@ __device__ __forceinline__ void run_tile(uint8_t *sm, f32x16 (&acc)[Cfg<J>::NCB]
     }
     for (int64_t kb = kb0; kb < kb1; ++kb) {
         const uint8_t *cur = enter(kb);
-        if constexpr (T == kQ4_K && !DBG) q4k_min_term<J>(cur, acc);
+        if constexpr (kK45<T> && !DBG) q4k_min_term<T, J>(cur, acc);
         tile_step<T, J, DBG>(cur, acc, cinit, kb, nb32, dbg, wr.rows, n, wr.r0, c0);
     }
 }
@@ -949,6 +981,7 @@ hipError_t launch_mmq(int type, const uint8_t *w, int64_t rows, int64_t k, const
     if (type == TT) return d ? launch_mmq_j<TT, true>(w, rows, k, xq, n, y, dbg, p, s)    \
                              : launch_mmq_j<TT, false>(w, rows, k, xq, n, y, dbg, p, s);
     QMM_MQ(kQ4_K)
+    QMM_MQ(kQ5_K)
     QMM_MQ(kQ6_K)
     QMM_MQ(kQ8_0)
 #undef QMM_MQ
@@ -981,6 +1014,7 @@ hipError_t launch_mmq_glu(int type, const uint8_t *wg, const uint8_t *wu, int64_
         if (tile_j == 128) return launch_mmq_glu_t<TT, 128>(wg, wu, rows, k, xq, n, y, s);           \
     }
     QMM_MG(kQ4_K)
+    QMM_MG(kQ5_K)
     QMM_MG(kQ6_K)
     QMM_MG(kQ8_0)
 #undef QMM_MG
@@ -1023,6 +1057,7 @@ hipError_t launch_mmq_id(int type, const uint8_t *w, const uint8_t *w_up, int64_
                     : launch_mmq_id_j<TT, false>(w, nullptr, rows, k, xq, y, cm, tile_j, max_col_tiles, s); \
     }
     QMM_MQI(kQ4_K)
+    QMM_MQI(kQ5_K)
     QMM_MQI(kQ6_K)
     QMM_MQI(kQ8_0)
 #undef QMM_MQI

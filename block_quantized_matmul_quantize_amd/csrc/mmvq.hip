@@ -63,10 +63,15 @@ template <int T> struct MvStep;
 // src1 = g==0 ? piece 4 : piece g, src2 = g==0 ? piece 8 : piece 4+g; lanes g = 1, 2 carry the
 // first sub-block of the pair (values 0-15 / 16-31) and g = 3, 0 the second.
 // ------------------------------------------------------------------------------------------
-template <> struct MvStep<kQ4_K> {
+// Q5_K (176 bytes: the Q4_K header, qh[32], then qs[128] as Q4_K's) takes the same pieces 32
+// bytes further on and ORs the fifth bits in: lane g's bytes hold values 16*half(g).. of its
+// sub-blocks 2*group(g) + (j&1) + 4*(j>>1) (MFMA j), whose fifth bits are bit (sub-block) of qh
+// bytes 16*half(g)..16*half(g)+15.
+template <int T> struct MvStepK45 {
     static constexpr int NCG = 1;
-    static constexpr int BYTES = 144;
-    u32x4 pa, pb, pc, hdr;
+    static constexpr int BYTES = Fmt<T>::BYTES;
+    static constexpr int QS = T == kQ5_K ? 48 : 16;   // qs offset in the super-block
+    u32x4 pa, pb, pc, hdr, qh;
     u32x4 a[4];
 
     // K-slot group of lane g for the block diagonal: 0 for g in {1,2}, 1 for g in {3,0}; the half
@@ -88,10 +93,11 @@ template <> struct MvStep<kQ4_K> {
 
     __device__ __forceinline__ void load(const uint8_t *wg, const MvLane &L, int64_t step) {
         const uint8_t *blk = wg + L.wrow_off + step * BYTES;
-        pa = ld16(blk + 16 * L.g);
-        pb = ld16(blk + 64 + 16 * L.g);
-        pc = ld16(blk + 128);
+        pa = ld16(blk + (QS - 16) + 16 * L.g);
+        pb = ld16(blk + (QS + 48) + 16 * L.g);
+        pc = ld16(blk + (QS + 112));
         hdr = ld16(blk);
+        if constexpr (T == kQ5_K) qh = ld16(blk + 16 + 16 * half(L.g));
 #pragma unroll
         for (int j = 0; j < 4; ++j) a[j] = ld16(L.abase[0] + step * L.astride[0] + L.aoff[0][j]);
     }
@@ -109,7 +115,17 @@ template <> struct MvStep<kQ4_K> {
         const uint32_t sc_hi = ((hdr.w & 0x0F0F0F0Fu) | ((hdr.y >> 2) & 0x30303030u)) >> (16 * sel);
         const uint32_t m_hi = (((hdr.w >> 4) & 0x0F0F0F0Fu) | ((hdr.z >> 2) & 0x30303030u)) >> (16 * sel);
         const u32x4 src1 = sel4(g == 0, pb, pa), src2 = sel4(g == 0, pc, pb);
-        const u32x4 bop[4] = {nib_lo4(src1), nib_hi4(src1), nib_lo4(src2), nib_hi4(src2)};
+        u32x4 bop[4] = {nib_lo4(src1), nib_hi4(src1), nib_lo4(src2), nib_hi4(src2)};
+        if constexpr (T == kQ5_K) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int sbb = 2 * group(g) + (j & 1) + 4 * (j >> 1);
+                bop[j].x |= ((qh.x >> sbb) & 0x01010101u) << 4;
+                bop[j].y |= ((qh.y >> sbb) & 0x01010101u) << 4;
+                bop[j].z |= ((qh.z >> sbb) & 0x01010101u) << 4;
+                bop[j].w |= ((qh.w >> sbb) & 0x01010101u) << 4;
+            }
+        }
         const i32x4 zero = {0, 0, 0, 0};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -136,6 +152,9 @@ template <> struct MvStep<kQ4_K> {
         }
     }
 };
+
+template <> struct MvStep<kQ4_K> : MvStepK45<kQ4_K> {};
+template <> struct MvStep<kQ5_K> : MvStepK45<kQ5_K> {};
 
 // ------------------------------------------------------------------------------------------
 // Q6_K: 210-byte super-block = {ql[128], qh[64], int8 scales[16], d}.  Value v: half h = v/128,
@@ -484,7 +503,7 @@ void set_mmvq_kernel(int which) { g_mv_kernel = which; }
 // Largest column count the automatic choice sends to the dot4 kernel, per type: measured at
 // 4096 x 4096 (fp32 input, graph-replayed calls), dot4 is ~0.1 us faster than the LDS-staged
 // kernel at one column and 0.8-1.4 us slower at two or three.
-static int dot4_auto_cols(int type) { return type == kQ4_K || type == kQ8_0 ? 1 : 0; }
+static int dot4_auto_cols(int type) { return type == kQ4_K || type == kQ5_K || type == kQ8_0 ? 1 : 0; }
 
 static int g_fuse_cols = 0;   // 0: automatic (5)
 
@@ -554,6 +573,7 @@ hipError_t launch_mmvq(int type, const uint8_t *w, int64_t rows, int64_t k, cons
         return launch_mmvq_t<TT, false, false>(w, rows, k, xq, n, y, dbg, cm, n_exp, s);   \
     }
     QMM_MV(kQ4_K)
+    QMM_MV(kQ5_K)
     QMM_MV(kQ6_K)
     QMM_MV(kQ8_0)
 #undef QMM_MV
@@ -579,6 +599,7 @@ hipError_t launch_mmvq_glu(int type, const uint8_t *wg, const uint8_t *wu, int64
         return launch_mmvq_spw<TT, 2, false, false, true>(wg, rows, k, xq, n, y, nullptr, c, n_exp, s, wu);     \
     }
     QMM_MVG(kQ4_K)
+    QMM_MVG(kQ5_K)
     QMM_MVG(kQ6_K)
     QMM_MVG(kQ8_0)
 #undef QMM_MVG

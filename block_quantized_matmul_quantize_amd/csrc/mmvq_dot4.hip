@@ -55,6 +55,16 @@ template <> struct W4<kQ4_K> {
         q1 = *(const u32x4 *)(base + off + 32 + 32 * g);
     }
 };
+template <> struct W4<kQ5_K> {
+    u32x4 h, q0, q1, qh0, qh1;   // header, qs bytes 32g..32g+31 (after qh[32]), all 32 qh bytes
+    __device__ __forceinline__ void load(const uint8_t *base, uint32_t off, int g) {
+        h = *(const u32x4 *)(base + off);
+        q0 = *(const u32x4 *)(base + off + 48 + 32 * g);
+        q1 = *(const u32x4 *)(base + off + 64 + 32 * g);
+        qh0 = *(const u32x4 *)(base + off + 16);
+        qh1 = *(const u32x4 *)(base + off + 32);
+    }
+};
 template <> struct W4<kQ8_0> {
     u32x4 v0, v1, v2, v3;   // bytes 68g..68g+63 of the step: {d0, q0[32], d1, q1[0..29]}
     uint32_t v4;            // bytes 68g+64..68g+67: q1[30..31] ... (the last 4 bytes)
@@ -69,6 +79,7 @@ template <> struct W4<kQ8_0> {
 };
 template <int T> struct StepBytes;
 template <> struct StepBytes<kQ4_K> { static constexpr int V = 144; };
+template <> struct StepBytes<kQ5_K> { static constexpr int V = 176; };
 template <> struct StepBytes<kQ8_0> { static constexpr int V = 272; };
 
 template <int T, int NC, bool DBG, bool EXPERT, bool F32, bool GLU>
@@ -154,7 +165,7 @@ __global__ __launch_bounds__(1024) void mmvq_dot4_kernel(const uint8_t *__restri
         if (it + 1 < my_steps) cur.load(wg + (s + nwaves) * StepBytes<T>::V, woff, g);   // next step in flight
         const uint32_t b0 = 8 * s + 2 * g;   // q8_1 block of sub-block 2g
 
-        if constexpr (T == kQ4_K) {
+        if constexpr (T == kQ4_K || T == kQ5_K) {
             const float d = h2f((uint16_t)(x.h.x & 0xFFFF));
             const float dmin = h2f((uint16_t)(x.h.x >> 16));
             // 6-bit scale / min of sub-blocks 2g, 2g+1 in bytes 0, 1: sub-blocks 0-3 sit in the low
@@ -173,6 +184,15 @@ __global__ __launch_bounds__(1024) void mmvq_dot4_kernel(const uint8_t *__restri
             for (int i = 0; i < 8; ++i) {
                 lo[i] = qv[i] & 0x0F0F0F0Fu;
                 hi[i] = (qv[i] >> 4) & 0x0F0F0F0Fu;
+            }
+            if constexpr (T == kQ5_K) {
+                // fifth bits: bit 2g (sub-block 2g) and 2g+1 of qh byte l, l = the value's position
+                const uint32_t hv[8] = {x.qh0.x, x.qh0.y, x.qh0.z, x.qh0.w, x.qh1.x, x.qh1.y, x.qh1.z, x.qh1.w};
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    lo[i] |= ((hv[i] >> (2 * g)) & 0x01010101u) << 4;
+                    hi[i] |= ((hv[i] >> (2 * g + 1)) & 0x01010101u) << 4;
+                }
             }
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
@@ -310,10 +330,10 @@ hipError_t dispatch(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq
 int mmvq_dot4_max_cols() { return 3; }
 
 bool mmvq_dot4_supported(int type, const void *w, int64_t k, const void *xq, const ColMap *cm) {
-    if (type != kQ4_K && type != kQ8_0) return false;
+    if (type != kQ4_K && type != kQ5_K && type != kQ8_0) return false;
     if (k % kSuper != 0 || k < kSuper || k > 32768) return false;
-    const int64_t row_bytes = type == kQ8_0 ? k / 32 * 34 : k / 256 * 144;
-    const int align = type == kQ4_K ? 16 : 4;
+    const int64_t row_bytes = type == kQ8_0 ? k / 32 * 34 : k / 256 * (type == kQ5_K ? 176 : 144);
+    const int align = type == kQ8_0 ? 4 : 16;
     if (row_bytes % align != 0 || (uintptr_t)w % align != 0) return false;
     if ((uintptr_t)xq % 4 != 0) return false;
     if (cm && cm->w_expert_stride % align != 0) return false;
@@ -323,6 +343,7 @@ bool mmvq_dot4_supported(int type, const void *w, int64_t k, const void *xq, con
 hipError_t launch_mmvq_dot4(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n,
                             float *y, int32_t *dbg, const ColMap *cm, int64_t n_exp, int max_cols, hipStream_t s) {
     if (type == kQ4_K) return dispatch<kQ4_K>(w, rows, k, xq, n, y, dbg, cm, n_exp, max_cols, s);
+    if (type == kQ5_K) return dispatch<kQ5_K>(w, rows, k, xq, n, y, dbg, cm, n_exp, max_cols, s);
     if (type == kQ8_0) return dispatch<kQ8_0>(w, rows, k, xq, n, y, dbg, cm, n_exp, max_cols, s);
     return hipErrorInvalidValue;
 }
@@ -337,6 +358,7 @@ hipError_t launch_mmvq_dot4_f32(int type, const uint8_t *w, int64_t rows, int64_
         return launch_nc<TT, 3, false, false, true>(w, rows, k, x, n, y, nullptr, c, 0, s);                  \
     }
     QMM_D4F(kQ4_K)
+    QMM_D4F(kQ5_K)
     QMM_D4F(kQ8_0)
 #undef QMM_D4F
     return hipErrorInvalidValue;
@@ -352,6 +374,7 @@ hipError_t launch_mmvq_dot4_glu_f32(int type, const uint8_t *wg, const uint8_t *
         return launch_nc<TT, 3, false, false, true, true>(wg, rows, k, x, n, y, nullptr, c, 0, s, wu);              \
     }
     QMM_D4G(kQ4_K)
+    QMM_D4G(kQ5_K)
     QMM_D4G(kQ8_0)
 #undef QMM_D4G
     return hipErrorInvalidValue;

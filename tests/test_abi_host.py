@@ -122,7 +122,7 @@ def test_argument_validation_without_gpu():
     L = qmm.lib()
     null = ctypes.c_void_p(0)
     # unsupported type
-    assert L.qmm_matmul(13, null, 16, 256, null, 1, null, null, 0, null) == -2
+    assert L.qmm_matmul(11, null, 16, 256, null, 1, null, null, 0, null) == -2
     assert b"unsupported" in L.qmm_last_error()
     # k not a multiple of the block size
     assert L.qmm_matmul(qmm.Q4_K, null, 16, 100, null, 1, null, null, 0, null) == -3
@@ -147,7 +147,7 @@ def test_glu_argument_validation_without_gpu():
     L = qmm.lib()
     null = ctypes.c_void_p(0)
     one = ctypes.c_void_p(4096)   # a non-null address, never dereferenced: the calls fail first
-    assert L.qmm_matmul_glu(13, null, null, 16, 256, null, 1, null, null, 0, null) == -2
+    assert L.qmm_matmul_glu(11, null, null, 16, 256, null, 1, null, null, 0, null) == -2
     assert L.qmm_matmul_glu(qmm.Q4_K, null, null, 16, 100, null, 1, null, null, 0, null) == -3
     assert L.qmm_matmul_glu(qmm.Q4_K, null, null, 16, 256, null, 0, null, null, 0, null) == 0
     # null up matrix with columns to compute
@@ -174,7 +174,7 @@ def test_workspace_sizes_monotone():
     assert qmm.matmul_workspace(qmm.Q4_K, 4096, 4096, 1) >= 4096 // 32 * 36
     # the tiled path reserves stream-K partial slots
     assert qmm.matmul_q8_1_workspace(qmm.Q6_K, 4096, 14336, 512) >= 256 * 2 * 128 * 128 * 4
-    assert qmm.matmul_workspace(13, 16, 256, 1) == 0
+    assert qmm.matmul_workspace(11, 16, 256, 1) == 0
     assert qmm.matmul_id_workspace(qmm.Q4_K, 8, 14336, 4096, 512, 2, 1) > 512 * 128 * 36
     assert qmm.matmul_id_workspace(qmm.Q4_K, 8, 14336, 4096, 512, 2, 3) == 0
 
@@ -187,6 +187,9 @@ MV_AUTO = [
     *[(qmm.Q4_K, n, (2, True)) for n in range(2, 9)],
     *[(qmm.Q6_K, n, (2, True)) for n in range(1, 9)],
     (qmm.Q8_0, 1, (3, True)),
+    # Q5_K: dot4 at n = 1; no LDS-staged form, so quantize + register-streamed above
+    (qmm.Q5_K, 1, (3, True)),
+    *[(qmm.Q5_K, n, (1, False)) for n in range(2, 9)],
     *[(qmm.Q8_0, n, (2, True)) for n in range(2, 9)],
     *[(t, 9, (0, False)) for t in (qmm.Q4_K, qmm.Q6_K, qmm.Q8_0)],
 ]

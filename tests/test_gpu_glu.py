@@ -18,8 +18,8 @@ from gpu_util import DEV, col_norms, row_norms, to_dev
 
 pytestmark = pytest.mark.gpu
 
-TYPES = [qmm.Q4_K, qmm.Q6_K, qmm.Q8_0]
-TNAME = {qmm.Q4_K: "q4_K", qmm.Q6_K: "q6_K", qmm.Q8_0: "q8_0"}
+TYPES = [qmm.Q4_K, qmm.Q5_K, qmm.Q6_K, qmm.Q8_0]
+TNAME = {qmm.Q4_K: "q4_K", qmm.Q5_K: "q5_K", qmm.Q6_K: "q6_K", qmm.Q8_0: "q8_0"}
 
 
 @pytest.fixture(autouse=True)
