@@ -7,18 +7,19 @@
 // A workgroup owns 16 weight rows; wave w takes the 256-value steps w, w+W, ... (up to 16 waves).
 // Lane 4r+g holds row r and the quarter g of the step: values 64g..64g+63, i.e. the two 32-value
 // sub-blocks 2g and 2g+1 -- for Q4_K the 32 qs bytes 32g..32g+31 (low nibbles sub-block 2g, high
-// nibbles 2g+1), for Q8_0 the two 34-byte blocks.  Consecutive lanes of a row read consecutive
+// nibbles 2g+1; Q5_K: the same qs bytes 32 further on, plus all 32 qh bytes, whose bits 2g and
+// 2g+1 are the fifth bits of the two sub-blocks), for Q8_0 the two 34-byte blocks.  Consecutive lanes of a row read consecutive
 // bytes, so each quarter-wave load touches one or two cache lines.  The columns' q8_1 codes and
 // fp32 (d, s) are staged once per workgroup in LDS -- read from q8_1 blocks, or, for fp32 input,
 // quantized on the spot with the same arithmetic as the standalone quantize kernel (q8_1.hpp),
 // which saves that kernel's launch; every lane with the same quarter reads the same LDS words (a
 // broadcast).  Next step's weights load while this step computes.
-//   Q4_K  acc += D(2g)*(d*sc)*d_a - (dmin*m)*s_a   (+ the same for sub-block 2g+1)
+//   Q4_K, Q5_K  acc += D(2g)*(d*sc)*d_a - (dmin*m)*s_a   (+ the same for sub-block 2g+1)
 //   Q8_0  acc += D*d_w*d_a                         (both blocks)
 // The four quarters of a row are summed with lane shuffles, the waves in LDS in a fixed order.
 // GLU (gate/up fusion, the MMQ page's fusion passage): rows 0-7 of the workgroup are 8 gate rows,
 // rows 8-15 the same 8 rows of the up matrix, and the write-back applies silu(gate) * up.
-// Requirements (checked by the host): K a multiple of 256; Q4_K weights and rows 16-byte
+// Requirements (checked by the host): K a multiple of 256; Q4_K / Q5_K weights and rows 16-byte
 // aligned, Q8_0 4-byte aligned; activations 4-byte aligned.
 #include "common.hpp"
 #include "launch.hpp"

@@ -11,7 +11,7 @@
 // activations placed block-diagonally over (column, sub-block) so every int32 result is one exact
 // sub-block dot D (the same contraction as the register-streamed kernel in mmvq.hip, which serves
 // the shapes this one does not).  Fixups per D in fp32 ("dp4a path Q4_K" section of the MMQ page):
-//   Q4_K  acc += D * (d*sc) * d_a - (dmin*m) * s_a
+//   Q4_K, Q5_K  acc += D * (d*sc) * d_a - (dmin*m) * s_a   (Q5_K: fifth bits from qh ORed in)
 //   Q6_K  acc += D * (d*sc) * d_a      (D includes -32 * sum q_a via a second MFMA)
 //   Q8_0  acc += D * d_w * d_a
 // Every 16-byte LDS operand sits at a 16-byte aligned address (a misaligned ds_read_b128 runs at
@@ -22,7 +22,7 @@
 // split into aligned codes and fp32 scales.  For fp32 activations (dense) the wave quantizes its
 // step's blocks itself, 4 lanes per block with the arithmetic of the standalone quantize kernel
 // (q8_1.hpp) -- one launch instead of two.
-// Requirements (checked by the host): K a multiple of 256; Q4_K and Q6_K weights and rows 16-byte
+// Requirements (checked by the host): K a multiple of 256; Q4_K, Q5_K and Q6_K weights and rows 16-byte
 // aligned, Q8_0 weights 4-byte aligned; q8_1 activations 4-byte aligned (fp32: 16-byte).
 // GLU (gate/up fusion, the MMQ page's fusion passage): the 16 rows are 8 gate rows (load
 // instructions 0-1) and the same 8 rows of the up matrix (instructions 2-3); the write-back applies
@@ -54,6 +54,9 @@ typedef u32x4 __attribute__((aligned(4))) u32x4_a4;
 // fp32 block scales [16 rows][8 blocks].
 template <int T> struct Geo;
 template <> struct Geo<kQ4_K> { static constexpr int PPR = 9, STEP = 144, RSTR = 144, WD = 0; };
+template <> struct Geo<kQ5_K> { static constexpr int PPR = 11, STEP = 176, RSTR = 176, WD = 0; };
+// Q4_K and Q5_K (the Q4_K header and nibbles, qs 32 bytes further on after qh[32]) share a path.
+template <int T> constexpr bool kK45 = T == kQ4_K || T == kQ5_K;
 template <> struct Geo<kQ6_K> { static constexpr int PPR = 14, STEP = 210, RSTR = 240, WD = 0; };
 template <> struct Geo<kQ8_0> { static constexpr int PPR = 0, STEP = 272, RSTR = 272, WD = 16 * 8 * 4; };
 
@@ -261,7 +264,7 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
                 if (i < nic) *(u32x4 *)(st + acdst[i]) = av[i];
             *(float2 *)(st + asdst) = make_float2(h2f((uint16_t)(ads & 0xFFFF)), h2f((uint16_t)(ads >> 16)));
         }
-        if constexpr (T == kQ4_K) {
+        if constexpr (kK45<T>) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) *(u32x4 *)(st + pofs[i]) = wv[i];
         } else if constexpr (T == kQ6_K) {
@@ -312,7 +315,7 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
     for (int cg = 0; cg < NCG; ++cg) {
         int c, blk0, half;
         bool on;
-        if (T == kQ4_K) {
+        if (kK45<T>) {
             const int sel = m >> 3;
             c = m & 7;
             on = q4_group(g) == sel;
@@ -334,8 +337,8 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
         abase[cg] = on && c < ncols ? st + A0 + c * 256 + blk0 * 32 + 16 * half : zero;
     }
     // Q4_K: slice j covers sub-blocks (j>>1)*4 + (j&1) + 2*sel; Q6_K / Q8_0: blocks 2j + ...
-    auto aoffj = [](int j) { return T == kQ4_K ? 32 * ((j >> 1) * 4 + (j & 1)) : 64 * j; };
-    static_assert(T != kQ4_K || 32 * 5 + 16 <= kZeroBytes, "zero block too small");
+    auto aoffj = [](int j) { return kK45<T> ? 32 * ((j >> 1) * 4 + (j & 1)) : 64 * j; };
+    static_assert(!kK45<T> || 32 * 5 + 16 <= kZeroBytes, "zero block too small");
     static_assert(64 * 3 + 16 <= kZeroBytes, "zero block too small");
 
     float acc[NCG][4];
@@ -364,11 +367,12 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
         }
 
         auto aop = [&](int cg, int j) -> u32x4 { return lds16(abase[cg] + aoffj(j)); };
-        if constexpr (T == kQ4_K) {
+        if constexpr (kK45<T>) {
+            constexpr int QS = T == kQ5_K ? 32 : 0;   // Q5_K: qs after qh[32]
             const uint8_t *wr = st + wrow;
             const u32x4 hdr = lds16(wr);
-            const u32x4 src1 = lds16(wr + 16 * (g ? g : 4));
-            const u32x4 src2 = lds16(wr + 16 * (g ? 4 + g : 8));
+            const u32x4 src1 = lds16(wr + QS + 16 * (g ? g : 4));
+            const u32x4 src2 = lds16(wr + QS + 16 * (g ? 4 + g : 8));
             const int sel = g >> 1;
             const float d = h2f((uint16_t)(hdr.x & 0xFFFF));
             const float dmin = h2f((uint16_t)(hdr.x >> 16));
@@ -376,7 +380,20 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
             const uint32_t m_lo = (hdr.z & 0x3F3F3F3Fu) >> (16 * sel);
             const uint32_t sc_hi = ((hdr.w & 0x0F0F0F0Fu) | ((hdr.y >> 2) & 0x30303030u)) >> (16 * sel);
             const uint32_t m_hi = (((hdr.w >> 4) & 0x0F0F0F0Fu) | ((hdr.z >> 2) & 0x30303030u)) >> (16 * sel);
-            const u32x4 bop[4] = {nib_lo4(src1), nib_hi4(src1), nib_lo4(src2), nib_hi4(src2)};
+            u32x4 bop[4] = {nib_lo4(src1), nib_hi4(src1), nib_lo4(src2), nib_hi4(src2)};
+            if constexpr (T == kQ5_K) {
+                // fifth bits: this lane's bytes are values 16*half.. of sub-blocks
+                // 2*group + (j&1) + 4*(j>>1); bit (sub-block) of qh bytes 16*half..
+                const u32x4 qh = lds16(wr + 16 + 16 * q4_half(g));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int sbb = 2 * q4_group(g) + (j & 1) + 4 * (j >> 1);
+                    bop[j].x |= ((qh.x >> sbb) & 0x01010101u) << 4;
+                    bop[j].y |= ((qh.y >> sbb) & 0x01010101u) << 4;
+                    bop[j].z |= ((qh.z >> sbb) & 0x01010101u) << 4;
+                    bop[j].w |= ((qh.w >> sbb) & 0x01010101u) << 4;
+                }
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const i32x4 D = mfma16x16x64(aop(0, j), bop[j], zero4);
@@ -554,9 +571,9 @@ hipError_t dispatch(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq
 }  // namespace
 
 bool mmvq_stream_supported(int type, const void *w, int64_t k, const void *xq, const ColMap *cm) {
-    if (type != kQ4_K && type != kQ6_K && type != kQ8_0) return false;
+    if (type != kQ4_K && type != kQ5_K && type != kQ6_K && type != kQ8_0) return false;
     if (k % kSuper != 0 || k < kSuper) return false;
-    const int64_t row_bytes = type == kQ8_0 ? k / 32 * 34 : k / 256 * (type == kQ4_K ? 144 : 210);
+    const int64_t row_bytes = type == kQ8_0 ? k / 32 * 34 : k / 256 * (type == kQ4_K ? 144 : type == kQ5_K ? 176 : 210);
     const int64_t walign = type == kQ8_0 ? 4 : 16;   // Q8_0: 68-byte block pairs; else aligned windows
     if (row_bytes % walign != 0 || (uintptr_t)w % walign != 0) return false;
     if ((uintptr_t)xq % 4 != 0) return false;
@@ -568,6 +585,7 @@ hipError_t launch_mmvq_stream_f32(int type, const uint8_t *w, int64_t rows, int6
                                   float *y, hipStream_t s) {
     const ColMap c{};
     if (type == kQ4_K) return launch_t<kQ4_K, false, false, true>(w, rows, k, x, n, y, nullptr, c, 0, s);
+    if (type == kQ5_K) return launch_t<kQ5_K, false, false, true>(w, rows, k, x, n, y, nullptr, c, 0, s);
     if (type == kQ6_K) return launch_t<kQ6_K, false, false, true>(w, rows, k, x, n, y, nullptr, c, 0, s);
     if (type == kQ8_0) return launch_t<kQ8_0, false, false, true>(w, rows, k, x, n, y, nullptr, c, 0, s);
     return hipErrorInvalidValue;
@@ -576,6 +594,7 @@ hipError_t launch_mmvq_stream_f32(int type, const uint8_t *w, int64_t rows, int6
 hipError_t launch_mmvq_stream(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n,
                               float *y, int32_t *dbg, const ColMap *cm, int64_t n_exp, hipStream_t s) {
     if (type == kQ4_K) return dispatch<kQ4_K>(w, rows, k, xq, n, y, dbg, cm, n_exp, s);
+    if (type == kQ5_K) return dispatch<kQ5_K>(w, rows, k, xq, n, y, dbg, cm, n_exp, s);
     if (type == kQ6_K) return dispatch<kQ6_K>(w, rows, k, xq, n, y, dbg, cm, n_exp, s);
     if (type == kQ8_0) return dispatch<kQ8_0>(w, rows, k, xq, n, y, dbg, cm, n_exp, s);
     return hipErrorInvalidValue;
@@ -592,6 +611,7 @@ hipError_t launch_mmvq_stream_glu(int type, const uint8_t *wg, const uint8_t *wu
         return launch_t<TT, false, false, false, true>(wg, rows, k, x, n, y, nullptr, c, 0, s, wu);                \
     }
     QMM_SG(kQ4_K)
+    QMM_SG(kQ5_K)
     QMM_SG(kQ6_K)
     QMM_SG(kQ8_0)
 #undef QMM_SG

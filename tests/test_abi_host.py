@@ -187,11 +187,10 @@ MV_AUTO = [
     *[(qmm.Q4_K, n, (2, True)) for n in range(2, 9)],
     *[(qmm.Q6_K, n, (2, True)) for n in range(1, 9)],
     (qmm.Q8_0, 1, (3, True)),
-    # Q5_K: dot4 at n = 1; no LDS-staged form, so quantize + register-streamed above
     (qmm.Q5_K, 1, (3, True)),
-    *[(qmm.Q5_K, n, (1, False)) for n in range(2, 9)],
+    *[(qmm.Q5_K, n, (2, True)) for n in range(2, 9)],
     *[(qmm.Q8_0, n, (2, True)) for n in range(2, 9)],
-    *[(t, 9, (0, False)) for t in (qmm.Q4_K, qmm.Q6_K, qmm.Q8_0)],
+    *[(t, 9, (0, False)) for t in (qmm.Q4_K, qmm.Q5_K, qmm.Q6_K, qmm.Q8_0)],
 ]
 
 

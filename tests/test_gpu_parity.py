@@ -196,8 +196,6 @@ def test_matvec_kernel_variants(qtype, kernel):
     kernel handles; fp32 outputs and the integer sub-block dots."""
     if kernel == 3 and qtype == qmm.Q6_K:
         pytest.skip("the dot4 kernel serves Q4_K, Q5_K and Q8_0")
-    if kernel == 2 and qtype == qmm.Q5_K:
-        pytest.skip("the LDS-staged kernel serves Q4_K, Q6_K and Q8_0")
     qmm.set_override(qmm.OVR_MV_KERNEL, kernel)
     k = 6144 if qtype == qmm.Q6_K else 4352
     ns = (1, 2, 3) if kernel == 3 else (1, 3, 4, 5, 8)
@@ -220,8 +218,8 @@ def _at_offset(a, off):
     return view
 
 
-@pytest.mark.parametrize("qtype,woff", [(qmm.Q4_K, 16), (qmm.Q6_K, 16), (qmm.Q8_0, 4), (qmm.Q8_0, 36)],
-                         ids=["q4_K", "q6_K", "q8_0_w4", "q8_0_w36"])
+@pytest.mark.parametrize("qtype,woff", [(qmm.Q4_K, 16), (qmm.Q5_K, 16), (qmm.Q6_K, 16), (qmm.Q8_0, 4),
+                                        (qmm.Q8_0, 36)], ids=["q4_K", "q5_K", "q6_K", "q8_0_w4", "q8_0_w36"])
 def test_matvec_lds_kernel_at_minimum_alignment(qtype, woff):
     """The LDS-staged kernel at the least alignment it accepts: q8_1 activations 4 bytes past a
     16-byte boundary (the 36-byte blocks are re-laid at park time), Q8_0 weights 4 bytes off."""
@@ -241,8 +239,7 @@ def test_matvec_lds_kernel_at_minimum_alignment(qtype, woff):
 
 @pytest.mark.parametrize("kernel,qtype,k,n", [(2, qmm.Q6_K, 768, 1),    # 630-byte rows: not 16-byte aligned
                                               (3, qmm.Q6_K, 4096, 1),   # dot4 serves Q4_K / Q8_0 only
-                                              (3, qmm.Q4_K, 4096, 4),   # dot4 takes at most 3 columns
-                                              (2, qmm.Q5_K, 4096, 2)])  # no LDS-staged Q5_K form
+                                              (3, qmm.Q4_K, 4096, 4)])  # dot4 takes at most 3 columns
 def test_forced_matvec_kernel_refuses_unsupported_call(kernel, qtype, k, n):
     qmm.set_override(qmm.OVR_MV_KERNEL, kernel)
     w, x = _case(qtype, 32, k, n, 540)
@@ -254,7 +251,8 @@ def test_forced_matvec_kernel_refuses_unsupported_call(kernel, qtype, k, n):
 @pytest.mark.parametrize("kernel", [0, 2], ids=["auto", "lds"])
 @pytest.mark.parametrize("qtype,n", [(qmm.Q4_K, 1), (qmm.Q4_K, 2), (qmm.Q8_0, 1), (qmm.Q8_0, 2), (qmm.Q8_0, 3),
                                      (qmm.Q4_K, 3), (qmm.Q4_K, 5), (qmm.Q4_K, 8), (qmm.Q8_0, 4), (qmm.Q8_0, 8),
-                                     (qmm.Q6_K, 1), (qmm.Q6_K, 2), (qmm.Q6_K, 3), (qmm.Q6_K, 8)])
+                                     (qmm.Q6_K, 1), (qmm.Q6_K, 2), (qmm.Q6_K, 3), (qmm.Q6_K, 8),
+                                     (qmm.Q5_K, 1), (qmm.Q5_K, 2), (qmm.Q5_K, 8)])
 def test_fused_quantize_matches_separate_quantize_bitwise(qtype, n, kernel):
     """fp32 input to the matrix-vector path with fusion forced for every column count: the dot4 or
     LDS-staged kernel quantizes the activations itself; the output equals
@@ -527,8 +525,6 @@ def test_moe_invalid_ids_and_per_slot_activations():
 def test_moe_small_experts_both_kernels(qtype, kernel):
     """Experts with at most 8 columns go to the matrix-vector kernel in expert mode; both kernels,
     ragged rows, per-slot activations, every output against the oracle."""
-    if kernel == 2 and qtype == qmm.Q5_K:
-        pytest.skip("the LDS-staged kernel serves Q4_K, Q6_K and Q8_0")
     qmm.set_override(qmm.OVR_MV_KERNEL, kernel)
     rng = np.random.default_rng(1100 + qtype)
     n_exp, rows, k, n_tok, top_k = 6, 77, 2048, 20, 2
