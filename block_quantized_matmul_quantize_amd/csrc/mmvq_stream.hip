@@ -199,9 +199,10 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
 
     // fp32 input: a column's 256 step values are 8 blocks of 4 lanes, 8 values per lane, so a
     // pass covers columns 2i + lane/32; the first NPF passes are fetched ahead into registers
-    // (one for Q6_K, whose unpacking needs registers), the rest at park time.  Lanes of a
+    // (one for Q6_K, whose unpacking needs registers, three for Q5_K, whose fifth bits do: four
+    // would spill at the 128 registers 16 waves allow), the rest at park time.  Lanes of a
     // missing odd column quantize a copy of the last column and park it in the sink.
-    constexpr int NPF = T == kQ6_K ? 1 : 4;
+    constexpr int NPF = T == kQ6_K ? 1 : T == kQ5_K ? 3 : 4;
     const int cq = lane >> 5, ja = lane & 31;
     const size_t xstride = (size_t)P.nsteps * kSuper;
     const float *xf = (const float *)xin + 8 * ja;

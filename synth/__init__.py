@@ -103,6 +103,10 @@ MOE_CASES = [
 ]
 
 
+# Q5_K (beyond the headline types): the matrix-vector shapes and one prefill shape.
+Q5_MMVQ_CASES = [dict(name=f"q5_K 4096x4096 N={n}", qtype=Q5_K, rows=4096, k=4096, n=n) for n in (1, 2, 5, 8)]
+Q5_PREFILL_CASES = [dict(name="ffn up q5_K 14336x4096 T=512", qtype=Q5_K, rows=14336, k=4096, n=512)]
+
 # Gate/up products fused with SwiGLU: two matrices of `rows` rows each.
 GLU_CASES = [
     dict(name="ffn gate/up+swiglu q4_K 2x14336x4096 N=1", kind="dense", qtype=Q4_K, rows=14336, k=4096, n=1),
