@@ -13,13 +13,14 @@ import numpy as np
 
 from . import build as _build
 
+Q4_0 = 2
 Q8_0 = 8
 Q4_K = 12
 Q5_K = 13
 Q6_K = 14
 
-BLOCK_VALUES = {Q8_0: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256}
-BLOCK_BYTES = {Q8_0: 34, Q4_K: 144, Q5_K: 176, Q6_K: 210}
+BLOCK_VALUES = {Q4_0: 32, Q8_0: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256}
+BLOCK_BYTES = {Q4_0: 18, Q8_0: 34, Q4_K: 144, Q5_K: 176, Q6_K: 210}
 Q8_1_BYTES = 36
 
 _lib = None

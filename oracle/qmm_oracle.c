@@ -19,6 +19,9 @@
  *    signed 8-bit scale per 16 values ("llama.cpp MMQ" page, "Q6_K load" and "Q6_K dot" sections).
  *  - Q8_0 weights: value = d*q, int8 q, fp16 d per 32 values (named on the GP100 patch page and the
  *    candle page; the byte layout follows the GGUF block_q8_0 definition).
+ *  - Q4_0 weights: value = d*(q - 8), 4-bit q, fp16 d per 32 values (named with the other types on
+ *    the MMQ page, whose tile-size table gives it only qs and one scale; the byte layout is GGUF's
+ *    block_q4_0: low nibbles of qs[0..15] are values 0..15, high nibbles values 16..31).
  *  - The product: per 32-value activation block b, an exact integer dot D_b of weight codes and
  *    activation codes, then the scale fixups of the "dp4a path Q4_K" / "Q6_K dot" sections.
  *    This oracle combines every exact term in fp64 and rounds to fp32 once.
@@ -47,6 +50,7 @@
 #include <math.h>
 #include <stdlib.h>
 
+#define ORC_Q4_0 2
 #define ORC_Q8_0 8
 #define ORC_Q4_K 12
 #define ORC_Q5_K 13
@@ -223,6 +227,15 @@ static void decode_q8_0(const uint8_t *blk, double *d, int code[32]) {
     for (int i = 0; i < 32; ++i) code[i] = (int8_t)blk[2 + i];
 }
 
+/* Q4_0, 18 bytes per 32 values: {d, qs[16]}; code[i] = nibble - 8 in [-8, 7]. */
+static void decode_q4_0(const uint8_t *blk, double *d, int code[32]) {
+    *d = oracle_half_to_double(rd16(blk + 0));
+    for (int i = 0; i < 16; ++i) {
+        code[i] = (blk[2 + i] & 15) - 8;
+        code[i + 16] = (blk[2 + i] >> 4) - 8;
+    }
+}
+
 static void decode_q8_1(const uint8_t *blk, double *d, double *s, int code[32]) {
     *d = oracle_half_to_double(rd16(blk + 0));
     *s = oracle_half_to_double(rd16(blk + 2));
@@ -231,7 +244,7 @@ static void decode_q8_1(const uint8_t *blk, double *d, double *s, int code[32]) 
 
 static int type_block_values(int type) {
     if (type == ORC_Q4_K || type == ORC_Q5_K || type == ORC_Q6_K) return 256;
-    if (type == ORC_Q8_0) return 32;
+    if (type == ORC_Q8_0 || type == ORC_Q4_0) return 32;
     return 0;
 }
 static int type_block_bytes(int type) {
@@ -239,6 +252,7 @@ static int type_block_bytes(int type) {
     if (type == ORC_Q5_K) return 176;
     if (type == ORC_Q6_K) return 210;
     if (type == ORC_Q8_0) return 34;
+    if (type == ORC_Q4_0) return 18;
     return 0;
 }
 
@@ -276,7 +290,8 @@ int oracle_dequantize(int type, const uint8_t *w, int64_t rows, int64_t k, doubl
                 for (int v = 0; v < 256; ++v) o[v] = d * sc[v / 16] * code[v];
             } else {
                 double d; int code[32];
-                decode_q8_0(p, &d, code);
+                if (type == ORC_Q8_0) decode_q8_0(p, &d, code);
+                else decode_q4_0(p, &d, code);
                 for (int v = 0; v < 32; ++v) o[v] = d * code[v];
             }
         }
@@ -363,10 +378,11 @@ static float dot_row_col(int type, const uint8_t *wrow, int64_t k, const act_t *
                 acc += d * da[b] * ((double)sc[2 * j] * D0 + (double)sc[2 * j + 1] * D1);
             }
         }
-    } else { /* Q8_0 */
+    } else { /* Q8_0, Q4_0: one scale per 32-value block */
         for (int64_t b = 0; b < nb32; ++b) {
             double d; int code[32];
-            decode_q8_0(wrow + b * 34, &d, code);
+            if (type == ORC_Q8_0) decode_q8_0(wrow + b * 34, &d, code);
+            else decode_q4_0(wrow + b * 18, &d, code);
             int32_t Db = 0;
             for (int i = 0; i < 32; ++i) Db += code[i] * qa[b * 32 + i];
             if (D) D[b] = Db;

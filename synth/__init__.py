@@ -8,6 +8,7 @@ Value distributions (the workload descriptions give Q4_K's; the rest are the pla
   * Q4_K super-block (144 B): fp16 d and dmin ~ U(0.001, 0.02); 12 bytes of uniform random
     6-bit-packed scales/mins; 128 bytes of uniform random nibbles.
   * Q5_K super-block (176 B): as Q4_K, with 32 bytes of uniform random fifth bits (qh).
+  * Q4_0 block (18 B): fp16 d ~ U(0.001, 0.02), 16 bytes of uniform random nibbles.
   * Q6_K super-block (210 B): uniform random ql (128 B) and qh (64 B); int8 scales ~ U{-32..31};
     fp16 d ~ U(0.001, 0.02).
   * Q8_0 block (34 B): fp16 d ~ U(0.001, 0.02); int8 codes ~ U{-127..127}.
@@ -19,12 +20,13 @@ fp16 values are produced by numpy's float32 -> float16 cast.
 import numpy as np
 
 Q8_0 = 8
+Q4_0 = 2
 Q4_K = 12
 Q5_K = 13
 Q6_K = 14
-TYPE_NAMES = {Q8_0: "q8_0", Q4_K: "q4_K", Q5_K: "q5_K", Q6_K: "q6_K"}
-BLOCK_VALUES = {Q8_0: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256}
-BLOCK_BYTES = {Q8_0: 34, Q4_K: 144, Q5_K: 176, Q6_K: 210}
+TYPE_NAMES = {Q4_0: "q4_0", Q8_0: "q8_0", Q4_K: "q4_K", Q5_K: "q5_K", Q6_K: "q6_K"}
+BLOCK_VALUES = {Q4_0: 32, Q8_0: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256}
+BLOCK_BYTES = {Q4_0: 18, Q8_0: 34, Q4_K: 144, Q5_K: 176, Q6_K: 210}
 
 
 def rngs(seed, n):
@@ -50,6 +52,8 @@ def gen_weights(qtype, rows, k, rng):
     elif qtype == Q6_K:
         blk[:, 192:208] = rng.integers(-32, 32, size=(nb, 16)).astype(np.int8).view(np.uint8)
         blk[:, 208:210] = _fp16_bytes(rng.uniform(0.001, 0.02, size=nb))
+    elif qtype == Q4_0:
+        blk[:, 0:2] = _fp16_bytes(rng.uniform(0.001, 0.02, size=nb))
     elif qtype == Q8_0:
         blk[:, 0:2] = _fp16_bytes(rng.uniform(0.001, 0.02, size=nb))
         blk[:, 2:34] = rng.integers(-127, 128, size=(nb, 32)).astype(np.int8).view(np.uint8)

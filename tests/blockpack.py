@@ -10,6 +10,7 @@ sub-blocks, and the Q6_K ql/qh bit composition):
         qs[128] @48 laid out as q4_K's (the pages give Q5_K the Q4_K scale packing)
   q6_K: ql[128] @0, qh[64] @128, int8 scales[16] @192, d f16 @208
   q8_0: d f16 @0, int8 qs[32] @2
+  q4_0: d f16 @0, qs[16] @2 (low nibble of qs[i] = value i, high nibble = value i + 16; code q - 8)
 """
 import numpy as np
 
@@ -93,6 +94,27 @@ def pack_q8_0(d, q):
     return b
 
 
+def pack_q4_0(d, q):
+    """q: 32 ints in [0,15] (stored nibbles, value order).  Returns 18 bytes."""
+    q = [int(v) for v in q]
+    assert len(q) == 32 and all(0 <= v < 16 for v in q)
+    b = np.zeros(18, dtype=np.uint8)
+    _put16(b, 0, f16_bits(d))
+    for i in range(16):
+        b[2 + i] = q[i] | (q[i + 16] << 4)
+    return b
+
+
+def random_q4_0_row(rng, k):
+    blocks, fields = [], []
+    for _ in range(k // 32):
+        d = f16_value(rng.uniform(0.001, 0.02))
+        q = rng.integers(0, 16, 32)
+        blocks.append(pack_q4_0(d, q))
+        fields.append((d, q))
+    return np.concatenate(blocks), fields
+
+
 def f16_value(x):
     return float(np.float32(x).astype(np.float16))
 
@@ -149,6 +171,8 @@ def weight_codes(qtype, fields):
     """Integer weight codes per value (Q4_K: [0,15]; Q5_K: [0,31]; Q6_K: q-32; Q8_0: int8) for one row."""
     if qtype in (12, 13):
         return np.concatenate([f[4] for f in fields]).astype(np.int64)
+    if qtype == 2:
+        return np.concatenate([f[1] for f in fields]).astype(np.int64) - 8
     if qtype == 14:
         return np.concatenate([f[2] for f in fields]).astype(np.int64) - 32
     return np.concatenate([f[1] for f in fields]).astype(np.int64)

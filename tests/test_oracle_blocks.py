@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
-from blockpack import pack_q4_K, pack_q5_K, pack_q6_K, pack_q8_0, f16_value
+from blockpack import pack_q4_0, pack_q4_K, pack_q5_K, pack_q6_K, pack_q8_0, f16_value
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -133,6 +133,21 @@ def test_q5_K_without_fifth_bits_is_q4_K():
     w5 = oracle.dequantize(oracle.Q5_K, pack_q5_K(d, dmin, sc, m, q), 1, 256)[0]
     w4 = oracle.dequantize(oracle.Q4_K, pack_q4_K(d, dmin, sc, m, q), 1, 256)[0]
     assert np.array_equal(w5, w4)
+
+
+def test_q4_0_encoder_roundtrip_and_one_hot():
+    rng = np.random.default_rng(14)
+    for _ in range(50):
+        d = f16_value(rng.uniform(-2, 2))
+        q = rng.integers(0, 16, 32)
+        w = oracle.dequantize(oracle.Q4_0, pack_q4_0(d, q), 1, 32)[0]
+        assert np.array_equal(w, d * (q - 8.0))
+    for v in range(32):
+        q = np.full(32, 8); q[v] = 13          # code 8 is the zero point
+        w = oracle.dequantize(oracle.Q4_0, pack_q4_0(1.0, q), 1, 32)[0]
+        assert np.nonzero(w)[0].tolist() == [v] and w[v] == 5.0
+    w = oracle.dequantize(oracle.Q4_0, pack_q4_0(0.5, np.zeros(32, int)), 1, 32)[0]
+    assert np.all(w == -4.0)                 # nibble 0 is -8 * d
 
 
 def test_q6_K_encoder_roundtrip_random():

@@ -10,11 +10,12 @@ import pytest
 
 import oracle
 import synth
-from blockpack import (pack_q4_K, random_q4_K_row, random_q5_K_row, random_q6_K_row, random_q8_0_row, weight_codes,
+from blockpack import (pack_q4_K, random_q4_0_row, random_q4_K_row, random_q5_K_row, random_q6_K_row, random_q8_0_row,
+                       weight_codes,
                        q8_1_codes, q8_1_scales)
 
 ROWGEN = {oracle.Q4_K: random_q4_K_row, oracle.Q5_K: random_q5_K_row, oracle.Q6_K: random_q6_K_row,
-          oracle.Q8_0: random_q8_0_row}
+          oracle.Q8_0: random_q8_0_row, oracle.Q4_0: random_q4_0_row}
 
 
 def _rows(qtype, rows, k, rng):
@@ -22,7 +23,7 @@ def _rows(qtype, rows, k, rng):
     return np.stack(data), list(fields)
 
 
-@pytest.mark.parametrize("qtype", [oracle.Q4_K, oracle.Q5_K, oracle.Q6_K, oracle.Q8_0])
+@pytest.mark.parametrize("qtype", [oracle.Q4_K, oracle.Q5_K, oracle.Q6_K, oracle.Q8_0, oracle.Q4_0])
 def test_subdots_brute_force(qtype):
     """Integer dots from the encoder's own codes and the q8_1 bytes, summed in Python ints."""
     rng = np.random.default_rng(20)
@@ -57,7 +58,7 @@ def _min_correction(qtype, fields, xq_row):
     return corr
 
 
-@pytest.mark.parametrize("qtype", [oracle.Q4_K, oracle.Q5_K, oracle.Q6_K, oracle.Q8_0])
+@pytest.mark.parametrize("qtype", [oracle.Q4_K, oracle.Q5_K, oracle.Q6_K, oracle.Q8_0, oracle.Q4_0])
 @pytest.mark.parametrize("shape", [(7, 256, 3), (16, 1024, 5), (3, 512, 17)])
 def test_matches_fp64_dequantize_then_multiply(qtype, shape):
     """Y equals the fp64 product of the dequantized weights and dequantized q8_1 activations
