@@ -13,12 +13,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqmm.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "qmm.h")
 
+Q4_0 = 2
 Q8_0 = 8
 Q4_K = 12
 Q5_K = 13
 Q6_K = 14
-BLOCK_VALUES = {Q8_0: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256}
-BLOCK_BYTES = {Q8_0: 34, Q4_K: 144, Q5_K: 176, Q6_K: 210}
+BLOCK_VALUES = {Q4_0: 32, Q8_0: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256}
+BLOCK_BYTES = {Q4_0: 18, Q8_0: 34, Q4_K: 144, Q5_K: 176, Q6_K: 210}
 Q8_1_BYTES = 36
 
 OVR_PATH, OVR_STREAMK, OVR_TILE_J, OVR_MV_STEPS, OVR_MV_KERNEL, OVR_FUSE_COLS = 1, 2, 3, 4, 5, 6

@@ -43,7 +43,7 @@ constexpr int kSmallMax = 8;           // experts with <= 8 columns use the matr
 int block_values(int type) {
     switch (type) {
         case QMM_Q4_K: case QMM_Q5_K: case QMM_Q6_K: return 256;
-        case QMM_Q8_0: return 32;
+        case QMM_Q8_0: case QMM_Q4_0: return 32;
         default: return 0;
     }
 }
@@ -53,6 +53,7 @@ int block_bytes(int type) {
         case QMM_Q5_K: return 176;
         case QMM_Q6_K: return 210;
         case QMM_Q8_0: return 34;
+        case QMM_Q4_0: return 18;
         default: return 0;
     }
 }
@@ -75,7 +76,7 @@ int device_cus() {
 
 qmm_status check_common(int type, int64_t rows, int64_t k, int64_t n) {
     const int qk = block_values(type);
-    if (qk == 0) return fail(QMM_ERR_TYPE, "unsupported weight type %d (supported: Q8_0=8, Q4_K=12, Q5_K=13, Q6_K=14)", type);
+    if (qk == 0) return fail(QMM_ERR_TYPE, "unsupported weight type %d (supported: Q4_0=2, Q8_0=8, Q4_K=12, Q5_K=13, Q6_K=14)", type);
     if (rows <= 0) return fail(QMM_ERR_ARG, "rows must be >= 1 (got %lld)", (long long)rows);
     if (n < 0) return fail(QMM_ERR_ARG, "n must be >= 0 (got %lld)", (long long)n);
     if (k <= 0 || k % qk != 0) return fail(QMM_ERR_SHAPE, "k=%lld is not a positive multiple of the block size %d", (long long)k, qk);

@@ -6,6 +6,7 @@
 
 namespace qmm {
 
+constexpr int kQ4_0 = 2;
 constexpr int kQ8_0 = 8;
 constexpr int kQ4_K = 12;
 constexpr int kQ5_K = 13;
@@ -17,6 +18,7 @@ template <> struct Fmt<kQ4_K> { static constexpr int QK = 256, BYTES = 144; };
 template <> struct Fmt<kQ5_K> { static constexpr int QK = 256, BYTES = 176; };
 template <> struct Fmt<kQ6_K> { static constexpr int QK = 256, BYTES = 210; };
 template <> struct Fmt<kQ8_0> { static constexpr int QK = 32, BYTES = 34; };
+template <> struct Fmt<kQ4_0> { static constexpr int QK = 32, BYTES = 18; };
 
 constexpr int kQ8_1Bytes = 36;       // {fp16 d, fp16 s, int8 q[32]}
 constexpr int kSuper = 256;          // K values per planning step (one K-quant super-block)

@@ -75,6 +75,8 @@ template <int J> struct Cfg {
 // Q4_K and Q5_K share the super-block header, the scale/min packing and the fixup (the MMQ page
 // pairs them in its "Q4_K load" section); Q5_K adds a fifth code bit per value.
 template <int T> constexpr bool kK45 = T == kQ4_K || T == kQ5_K;
+// Q8_0 and Q4_0: one fp16 scale per 32-value block; parked alike (int8 codes + fp32 d).
+template <int T> constexpr bool kB32 = T == kQ8_0 || T == kQ4_0;
 
 // LDS layout of one step.
 template <int T, int J> struct Smem {
@@ -301,6 +303,47 @@ template <int NT> struct WFetch<kQ8_0, NT> {
     }
 };
 
+// Q4_0: the 16 nibble bytes and the fp16 d per (row, block), parked as Q8_0's int8 codes
+// (nibble - 8; low nibbles are values 0-15, high 16-31) and fp32 d; blocks past the end of a
+// ragged last step get d = 0.
+template <int NT> struct WFetch<kQ4_0, NT> {
+    static constexpr int N = 1024 / NT;
+    u32x4 q[N];
+    uint16_t d[N];
+    template <class WR>
+    __device__ __forceinline__ void fetch(const WR &wr, int64_t kb, int64_t nb32) {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int it = 0; it < N; ++it) {
+            const int i = tid + NT * it;   // (row i/8, block i%8)
+            const int64_t b = kb * 8 + (i & 7);
+            const uint8_t *blk = wr.row(i >> 3) + b * 18;
+            q[it] = b < nb32 ? ld16(blk + 2) : u32x4{0u, 0u, 0u, 0u};
+            d[it] = b < nb32 ? ld2(blk) : (uint16_t)0;
+        }
+    }
+    // nibble - 8 as int8, four bytes at a time: (n + 120) has bit 7 set iff n >= 8, so flipping
+    // bit 7 gives n - 8 in two's complement; no byte carries (n + 120 <= 135)
+    static __device__ __forceinline__ uint32_t code4(uint32_t nib) { return (nib + 0x78787878u) ^ 0x80808080u; }
+    template <int J, class WR>
+    __device__ __forceinline__ void store(uint8_t *sm, const WR &, int64_t, int64_t) const {
+        const int tid = threadIdx.x;
+        uint8_t *sW = sm + Smem<kQ4_0, J>::W_OFF;
+        float *sWs = (float *)(sm + Smem<kQ4_0, J>::WS_OFF);
+#pragma unroll
+        for (int it = 0; it < N; ++it) {
+            const int i = tid + NT * it;
+            uint8_t *dst = sW + (i >> 3) * kLd + 32 * (i & 7);
+            const u32x4 v = q[it];
+            *(u32x4 *)dst = u32x4{code4(v.x & 0x0F0F0F0Fu), code4(v.y & 0x0F0F0F0Fu), code4(v.z & 0x0F0F0F0Fu),
+                                  code4(v.w & 0x0F0F0F0Fu)};
+            *(u32x4 *)(dst + 16) = u32x4{code4((v.x >> 4) & 0x0F0F0F0Fu), code4((v.y >> 4) & 0x0F0F0F0Fu),
+                                         code4((v.z >> 4) & 0x0F0F0F0Fu), code4((v.w >> 4) & 0x0F0F0F0Fu)};
+            sWs[(i & 7) * kTI + (i >> 3)] = h2f(d[it]);
+        }
+    }
+};
+
 // Q6_K scale folding for four codes c (the bytes of c6, each in [0, 63]) of one 16-value group:
 // v = sc * (c - 32) in [-4064, 4096], split as v = 128 * hi + lo with lo in [0, 127] and hi in
 // [-32, 32], returned as the byte vectors lo and hi.  Two codes per 32-bit lane pair: packed
@@ -513,7 +556,7 @@ __device__ __forceinline__ void tile_step(const uint8_t *sm, f32x16 (&acc)[Cfg<J
                 fix(cb, sb, mfma32x32x32(aop, b, cinit), S[cb]);
             }
         }
-    } else if constexpr (T == kQ8_0) {
+    } else if constexpr (kB32<T>) {
         const int8_t *sW = (const int8_t *)(sm + L::W_OFF);
 #pragma unroll 1
         for (int j = 0; j < 8; ++j) {
@@ -620,7 +663,7 @@ __device__ __forceinline__ void run_tile(uint8_t *sm, f32x16 (&acc)[Cfg<J>::NCB]
         asm volatile("" : "+v"(cinit));
     }
     WFetch<T, Cfg<J>::NT> wf;
-    ActFetch<J, !DBG, T == kQ8_0> af;
+    ActFetch<J, !DBG, kB32<T>> af;
     wf.fetch(wr, kb0, nb32);
     af.fetch(xq, nb32, kb0, acol, act_rows);
     uint8_t *const buf0 = sm, *const buf1 = sm + (DB ? Smem<T, J>::BYTES : 0);
@@ -984,6 +1027,7 @@ hipError_t launch_mmq(int type, const uint8_t *w, int64_t rows, int64_t k, const
     QMM_MQ(kQ5_K)
     QMM_MQ(kQ6_K)
     QMM_MQ(kQ8_0)
+    QMM_MQ(kQ4_0)
 #undef QMM_MQ
     return hipErrorInvalidValue;
 }
@@ -1017,6 +1061,7 @@ hipError_t launch_mmq_glu(int type, const uint8_t *wg, const uint8_t *wu, int64_
     QMM_MG(kQ5_K)
     QMM_MG(kQ6_K)
     QMM_MG(kQ8_0)
+    QMM_MG(kQ4_0)
 #undef QMM_MG
     return hipErrorInvalidValue;
 }
@@ -1060,6 +1105,7 @@ hipError_t launch_mmq_id(int type, const uint8_t *w, const uint8_t *w_up, int64_
     QMM_MQI(kQ5_K)
     QMM_MQI(kQ6_K)
     QMM_MQI(kQ8_0)
+    QMM_MQI(kQ4_0)
 #undef QMM_MQI
     return hipErrorInvalidValue;
 }

@@ -255,10 +255,12 @@ template <> struct MvStep<kQ6_K> {
 // 2p (lanes g = 0, 1) and 2p+1 (lanes g = 2, 3); lane g loads 16 codes of its block, so the
 // 4 lanes of a row read the 64 code bytes of two adjacent blocks.  The last step of a row may be
 // partial (k/32 blocks): blocks beyond it are clamped to the last block and their results dropped.
+// Q4_0 (18-byte blocks {d, 16 nibble bytes}) takes the same roles: lane g reads the block's 16
+// nibble bytes and keeps the low (g even: values 0-15) or high nibbles (values 16-31), minus 8.
 // ------------------------------------------------------------------------------------------
-template <> struct MvStep<kQ8_0> {
+template <int T> struct MvStepB32 {
     static constexpr int NCG = 1;
-    static constexpr int BYTES = 272;
+    static constexpr int BB = Fmt<T>::BYTES;   // bytes per 32-value block
     uint32_t dbits[4];
     u32x4 q[4];
     u32x4 a[4];
@@ -278,9 +280,19 @@ template <> struct MvStep<kQ8_0> {
         for (int p = 0; p < 4; ++p) {
             int64_t bw = step * 8 + 2 * p + (L.g >> 1);
             bw = bw < nb ? bw : nb - 1;
-            const uint8_t *blk = wg + L.wrow_off + bw * 34;
+            const uint8_t *blk = wg + L.wrow_off + bw * BB;
             dbits[p] = ld2(blk);
-            q[p] = ld16(blk + 2 + 16 * (L.g & 1));
+            if constexpr (T == kQ4_0) {
+                // nibble - 8 as int8: (n + 120) ^ 0x80 per byte (no carries)
+                const u32x4 v = ld16(blk + 2);
+                const int sh = 4 * (L.g & 1);
+                q[p] = u32x4{(((v.x >> sh) & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u,
+                             (((v.y >> sh) & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u,
+                             (((v.z >> sh) & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u,
+                             (((v.w >> sh) & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u};
+            } else {
+                q[p] = ld16(blk + 2 + 16 * (L.g & 1));
+            }
             int64_t ba = step * 8 + L.aoff[0][p];
             ba = ba < nb ? ba : nb - 1;
             a[p] = ld16(L.abase[0] + live * (ba * kQ8_1Bytes + 4 + 16 * (L.g & 1)));
@@ -316,6 +328,9 @@ template <> struct MvStep<kQ8_0> {
         }
     }
 };
+
+template <> struct MvStep<kQ8_0> : MvStepB32<kQ8_0> {};
+template <> struct MvStep<kQ4_0> : MvStepB32<kQ4_0> {};
 
 constexpr int mv_max_waves(int spw) { return spw == 1 ? 16 : spw == 2 ? 8 : 4; }
 
@@ -405,7 +420,7 @@ __global__ __launch_bounds__(64 * mv_max_waves(SPW)) void mmvq_kernel(const uint
         for (int i = 0; i < SPW; ++i) {
             const int64_t s = base + wave + (int64_t)i * nwaves;
             if (s < nsteps) {
-                if constexpr (T == kQ8_0) st[i].load(wg, L, s, nb);
+                if constexpr (T == kQ8_0 || T == kQ4_0) st[i].load(wg, L, s, nb);
                 else st[i].load(wg, L, s);
             }
         }
@@ -414,7 +429,7 @@ __global__ __launch_bounds__(64 * mv_max_waves(SPW)) void mmvq_kernel(const uint
         for (int i = 0; i < SPW; ++i) {
             const int64_t s = base + wave + (int64_t)i * nwaves;
             if (s < nsteps) {
-                if constexpr (T == kQ8_0) st[i].template compute<DBG>(s, L, sTab, acc, dbg_row, dbg_ld, ncols, nb);
+                if constexpr (T == kQ8_0 || T == kQ4_0) st[i].template compute<DBG>(s, L, sTab, acc, dbg_row, dbg_ld, ncols, nb);
                 else st[i].template compute<DBG>(s, L, sTab, acc, dbg_row, dbg_ld, ncols);
             }
         }
@@ -576,6 +591,7 @@ hipError_t launch_mmvq(int type, const uint8_t *w, int64_t rows, int64_t k, cons
     QMM_MV(kQ5_K)
     QMM_MV(kQ6_K)
     QMM_MV(kQ8_0)
+    QMM_MV(kQ4_0)
 #undef QMM_MV
     return hipErrorInvalidValue;
 }
@@ -602,6 +618,7 @@ hipError_t launch_mmvq_glu(int type, const uint8_t *wg, const uint8_t *wu, int64
     QMM_MVG(kQ5_K)
     QMM_MVG(kQ6_K)
     QMM_MVG(kQ8_0)
+    QMM_MVG(kQ4_0)
 #undef QMM_MVG
     return hipErrorInvalidValue;
 }

@@ -54,7 +54,7 @@ typedef enum {
     QMM_ERR_HIP = -5         /* a HIP call failed (message in qmm_last_error) */
 } qmm_status;
 
-typedef enum { QMM_Q8_0 = 8, QMM_Q4_K = 12, QMM_Q5_K = 13, QMM_Q6_K = 14 } qmm_type; /* GGUF type ids */
+typedef enum { QMM_Q4_0 = 2, QMM_Q8_0 = 8, QMM_Q4_K = 12, QMM_Q5_K = 13, QMM_Q6_K = 14 } qmm_type; /* GGUF type ids */
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char *qmm_last_error(void);

@@ -190,7 +190,9 @@ MV_AUTO = [
     (qmm.Q5_K, 1, (3, True)),
     *[(qmm.Q5_K, n, (2, True)) for n in range(2, 9)],
     *[(qmm.Q8_0, n, (2, True)) for n in range(2, 9)],
-    *[(t, 9, (0, False)) for t in (qmm.Q4_K, qmm.Q5_K, qmm.Q6_K, qmm.Q8_0)],
+    # Q4_0: only the register-streamed kernel (quantize first)
+    *[(qmm.Q4_0, n, (1, False)) for n in range(1, 9)],
+    *[(t, 9, (0, False)) for t in (qmm.Q4_K, qmm.Q5_K, qmm.Q6_K, qmm.Q8_0, qmm.Q4_0)],
 ]
 
 

@@ -18,8 +18,8 @@ from gpu_util import DEV, col_norms, row_norms, to_dev
 
 pytestmark = pytest.mark.gpu
 
-TYPES = [qmm.Q4_K, qmm.Q5_K, qmm.Q6_K, qmm.Q8_0]
-TNAME = {qmm.Q4_K: "q4_K", qmm.Q5_K: "q5_K", qmm.Q6_K: "q6_K", qmm.Q8_0: "q8_0"}
+TYPES = [qmm.Q4_K, qmm.Q5_K, qmm.Q6_K, qmm.Q8_0, qmm.Q4_0]
+TNAME = {qmm.Q4_K: "q4_K", qmm.Q5_K: "q5_K", qmm.Q6_K: "q6_K", qmm.Q8_0: "q8_0", qmm.Q4_0: "q4_0"}
 
 
 @pytest.fixture(autouse=True)
@@ -79,7 +79,7 @@ def _check_dense(qtype, rows, k, n, seed, what):
 def test_glu_dense(qtype, n):
     # 200 rows: three 64-output tiles and a ragged one, 25 matrix-vector workgroups of 8;
     # Q8_0 at k = 544 ends in a partial 256-value step
-    k = 544 if qtype == qmm.Q8_0 else 512
+    k = 544 if qtype in (qmm.Q8_0, qmm.Q4_0) else 512
     G = _check_dense(qtype, 200, k, n, 900 + n, f"{TNAME[qtype]} n={n}")
     assert np.mean(np.abs(G) < 4) > 0.2    # the gates exercise silu's curve, not only its limits
 
