@@ -13,7 +13,8 @@ Also in the same JSON line:
                 events on the launch stream; peak = 8 TB/s HBM.  traffic comes from the committed
                 rocprofv3 FETCH_SIZE/WRITE_SIZE summary when it matches the current sources.
   cpu_baseline  the oracle (plain C, all host threads) on whole steps of the same workload.
-  q5_K_matvec   per-launch timing of the same matrix-vector shapes in Q5_K (not part of the step).
+  extra_types_matvec  per-launch timing of the same matrix-vector shapes in Q5_K and Q4_0 (not
+                part of the step).
   secondary     int8 TOPS and % of the 5.0 POP/s int8 MFMA peak for the prefill and MoE shapes, and
                 for the gate/up products fused with SwiGLU (decode: also GB/s of the two matrices).
 
@@ -217,9 +218,9 @@ def main():
     for pc in per_case:
         log(f"[bench]   {pc['case']:24s} {pc['kernel']:30s} {pc['us']:8.3f} us  {pc['GBps']:8.1f} GB/s")
 
-    # Q5_K, a type beyond the headline workload: the same per-launch timing (not in the step)
+    # Q5_K and Q4_0, types beyond the headline workload: the same per-launch timing (not in the step)
     q5_cases = []
-    for i, c in enumerate(synth.Q5_MMVQ_CASES):
+    for i, c in enumerate(synth.EXTRA_MMVQ_CASES):
         w5 = [torch.from_numpy(synth.gen_weights(c["qtype"], c["rows"], c["k"], synth.rngs(3000 * r + i, 1)[0])).to(dev)
               for r in range(R)]
         x5 = torch.from_numpy(synth.gen_activations(c["n"], c["k"], synth.rngs(70 + i, 1)[0])).to(dev)
@@ -231,7 +232,9 @@ def main():
         g.replay()
         us = run(nrep, lambda s: g.replay()) * 1e3 / (4 * R)
         b = launch_bytes(c["qtype"], c["rows"], c["k"], c["n"], BB, BV, fused)
-        q5_cases.append({"case": c["name"], "kernel": qmm.MV_KERNEL_NAMES.get(kid, "?") + (" (fp32 in)" if fused else ""),
+        # one call = one launch where the kernel quantizes x itself, else quantize + kernel
+        q5_cases.append({"case": c["name"], "launches_per_call": 1 if fused else 2,
+                         "kernel": qmm.MV_KERNEL_NAMES.get(kid, "?") + (" (fp32 in)" if fused else ""),
                          "us": round(us, 3), "GBps": round(b / us / 1e3, 1), "frac": round(b / us / 1e3 / HBM_PEAK_GBPS, 4)})
         log(f"[bench]   {c['name']:24s} {q5_cases[-1]['kernel']:30s} {us:8.3f} us  {b / us / 1e3:8.1f} GB/s")
         del w5
@@ -275,7 +278,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "secondary": secondary,
-        "q5_K_matvec": q5_cases,
+        "extra_types_matvec": q5_cases,
     }
     print(json.dumps(out), flush=True)
 
@@ -341,7 +344,7 @@ def summarize_pmc(fdir, wdir, write=False):
         w = statistics.mean(Wr.get(k, [0.0]))
         b = f * 1024 * fs + w * 1024 * ws
         print(f"| `{k}` | {len(F[k])} | {f:.1f} | {w:.1f} | {b / 1e6:.3f} MB |")
-        # the step's launches: the headline types (8, 12, 14), not the Q5_K per-launch timing
+        # the step's launches: the headline types (8, 12, 14), not the extra types' timing
         if "mmvq" in k and re.search(r"<(8|12|14),", k):
             mv_tot += b * len(F[k])
             mv_cnt += len(F[k])
@@ -391,7 +394,7 @@ def run_secondary(torch, np, qmm, synth, dev, log):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps * 1e3   # us
 
-    for c in synth.PREFILL_CASES + synth.Q5_PREFILL_CASES:
+    for c in synth.PREFILL_CASES + synth.EXTRA_PREFILL_CASES:
         w, x = synth.make_dense(c)
         nrot = max(1, int(np.ceil(512e6 / w.nbytes)))
         ws_ = [torch.from_numpy(w).to(dev)] + [torch.roll(torch.from_numpy(w).to(dev), 1, 0) for _ in range(min(nrot, 8) - 1)]

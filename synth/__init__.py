@@ -107,9 +107,11 @@ MOE_CASES = [
 ]
 
 
-# Q5_K (beyond the headline types): the matrix-vector shapes and one prefill shape.
-Q5_MMVQ_CASES = [dict(name=f"q5_K 4096x4096 N={n}", qtype=Q5_K, rows=4096, k=4096, n=n) for n in (1, 2, 5, 8)]
-Q5_PREFILL_CASES = [dict(name="ffn up q5_K 14336x4096 T=512", qtype=Q5_K, rows=14336, k=4096, n=512)]
+# Q5_K and Q4_0 (beyond the headline types): the matrix-vector shapes and one prefill shape each.
+EXTRA_MMVQ_CASES = [dict(name=f"{TYPE_NAMES[t]} 4096x4096 N={n}", qtype=t, rows=4096, k=4096, n=n)
+                    for t in (Q5_K, Q4_0) for n in (1, 2, 5, 8)]
+EXTRA_PREFILL_CASES = [dict(name="ffn up q5_K 14336x4096 T=512", qtype=Q5_K, rows=14336, k=4096, n=512),
+                       dict(name="ffn up q4_0 14336x4096 T=512", qtype=Q4_0, rows=14336, k=4096, n=512)]
 
 # Gate/up products fused with SwiGLU: two matrices of `rows` rows each.
 GLU_CASES = [
