@@ -59,6 +59,8 @@ template <> struct Geo<kQ5_K> { static constexpr int PPR = 11, STEP = 176, RSTR 
 template <int T> constexpr bool kK45 = T == kQ4_K || T == kQ5_K;
 template <> struct Geo<kQ6_K> { static constexpr int PPR = 14, STEP = 210, RSTR = 240, WD = 0; };
 template <> struct Geo<kQ8_0> { static constexpr int PPR = 0, STEP = 272, RSTR = 272, WD = 16 * 8 * 4; };
+// Q4_0 (18-byte blocks {d, 16 nibble bytes}): loaded as 36-byte block pairs, parked as Q8_0's codes.
+template <> struct Geo<kQ4_0> { static constexpr int PPR = 0, STEP = 144, RSTR = 272, WD = 16 * 8 * 4; };
 
 template <int T> struct Stage {
     static constexpr int WB = kRows * Geo<T>::RSTR + Geo<T>::WD;   // weights (+ Q8_0 scales)
@@ -154,7 +156,7 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
         pofs[i] = jq < PM ? r * RSTR + 16 * jq : kSink;
     }
     const int ro8 = GLU ? (r8 & 7) : r8;
-    const uint32_t wofs8 = (uint32_t)(ro8 < rmax ? ro8 : rmax) * row_bytes + 68u * p8;
+    const uint32_t wofs8 = (uint32_t)(ro8 < rmax ? ro8 : rmax) * row_bytes + (T == kQ4_0 ? 36u : 68u) * p8;
     const uint8_t *wg8 = (GLU && r8 >= 8) ? wg2 : wg;
 
     u32x4 wv[4];
@@ -165,6 +167,11 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
 #pragma unroll
             for (int i = 0; i < 4; ++i) wv[i] = *(const u32x4_a4 *)(src + 16 * i);
             wv4 = *(const uint32_t *)(src + 64);
+        } else if constexpr (T == kQ4_0) {
+            const uint8_t *src = wg8 + (uint32_t)(s * 144) + wofs8;
+            wv[0] = *(const u32x4_a4 *)src;
+            wv[1] = *(const u32x4_a4 *)(src + 16);
+            wv4 = *(const uint32_t *)(src + 32);
         } else {
             const uint32_t so = (uint32_t)(s * Geo<T>::STEP) & ~15u;
 #pragma unroll
@@ -288,6 +295,22 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
                 case 2: put(IC<2>{}); break;
                 default: put(IC<3>{}); break;
             }
+        } else if constexpr (T == kQ4_0) {
+            // bytes 0..35 of blocks 2p, 2p+1 = {d0, qs0[16], d1, qs1[16]}: qs0 sits 2 bytes off a
+            // dword boundary, qs1 on one; nibble - 8 as int8 is (n + 120) ^ 0x80 per byte
+            const uint32_t D[9] = {wv[0].x, wv[0].y, wv[0].z, wv[0].w, wv[1].x, wv[1].y, wv[1].z, wv[1].w, wv4};
+            const uint32_t q0[4] = {abyte(D[1], D[0], 2), abyte(D[2], D[1], 2), abyte(D[3], D[2], 2), abyte(D[4], D[3], 2)};
+            const uint32_t q1[4] = {D[5], D[6], D[7], D[8]};
+            auto c4 = [](uint32_t nib) { return (nib + 0x78787878u) ^ 0x80808080u; };
+            uint8_t *dst = st + r8 * RSTR + 64 * p8;
+            *(u32x4 *)dst = u32x4{c4(q0[0] & 0x0F0F0F0Fu), c4(q0[1] & 0x0F0F0F0Fu), c4(q0[2] & 0x0F0F0F0Fu), c4(q0[3] & 0x0F0F0F0Fu)};
+            *(u32x4 *)(dst + 16) = u32x4{c4((q0[0] >> 4) & 0x0F0F0F0Fu), c4((q0[1] >> 4) & 0x0F0F0F0Fu),
+                                         c4((q0[2] >> 4) & 0x0F0F0F0Fu), c4((q0[3] >> 4) & 0x0F0F0F0Fu)};
+            *(u32x4 *)(dst + 32) = u32x4{c4(q1[0] & 0x0F0F0F0Fu), c4(q1[1] & 0x0F0F0F0Fu), c4(q1[2] & 0x0F0F0F0Fu), c4(q1[3] & 0x0F0F0F0Fu)};
+            *(u32x4 *)(dst + 48) = u32x4{c4((q1[0] >> 4) & 0x0F0F0F0Fu), c4((q1[1] >> 4) & 0x0F0F0F0Fu),
+                                         c4((q1[2] >> 4) & 0x0F0F0F0Fu), c4((q1[3] >> 4) & 0x0F0F0F0Fu)};
+            *(float2 *)(st + kRows * RSTR + 4 * (8 * r8 + 2 * p8)) =
+                make_float2(h2f((uint16_t)(D[0] & 0xFFFF)), h2f((uint16_t)(D[4] >> 16)));
         } else {
             // Q8_0: bytes 0..67 of blocks 2p, 2p+1 = {d0, q0[32], d1, q1[32]}; q0 sits 2 bytes off
             // a dword boundary, q1 on one
@@ -572,10 +595,13 @@ hipError_t dispatch(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq
 }  // namespace
 
 bool mmvq_stream_supported(int type, const void *w, int64_t k, const void *xq, const ColMap *cm) {
-    if (type != kQ4_K && type != kQ5_K && type != kQ6_K && type != kQ8_0) return false;
+    if (type != kQ4_K && type != kQ5_K && type != kQ6_K && type != kQ8_0 && type != kQ4_0) return false;
     if (k % kSuper != 0 || k < kSuper) return false;
-    const int64_t row_bytes = type == kQ8_0 ? k / 32 * 34 : k / 256 * (type == kQ4_K ? 144 : type == kQ5_K ? 176 : 210);
-    const int64_t walign = type == kQ8_0 ? 4 : 16;   // Q8_0: 68-byte block pairs; else aligned windows
+    const int64_t row_bytes = type == kQ8_0   ? k / 32 * 34
+                              : type == kQ4_0 ? k / 32 * 18
+                                              : k / 256 * (type == kQ4_K ? 144 : type == kQ5_K ? 176 : 210);
+    // Q8_0 / Q4_0: 68- / 36-byte block pairs; else aligned windows
+    const int64_t walign = type == kQ8_0 || type == kQ4_0 ? 4 : 16;
     if (row_bytes % walign != 0 || (uintptr_t)w % walign != 0) return false;
     if ((uintptr_t)xq % 4 != 0) return false;
     if (cm && cm->w_expert_stride % walign != 0) return false;
@@ -589,6 +615,7 @@ hipError_t launch_mmvq_stream_f32(int type, const uint8_t *w, int64_t rows, int6
     if (type == kQ5_K) return launch_t<kQ5_K, false, false, true>(w, rows, k, x, n, y, nullptr, c, 0, s);
     if (type == kQ6_K) return launch_t<kQ6_K, false, false, true>(w, rows, k, x, n, y, nullptr, c, 0, s);
     if (type == kQ8_0) return launch_t<kQ8_0, false, false, true>(w, rows, k, x, n, y, nullptr, c, 0, s);
+    if (type == kQ4_0) return launch_t<kQ4_0, false, false, true>(w, rows, k, x, n, y, nullptr, c, 0, s);
     return hipErrorInvalidValue;
 }
 
@@ -598,6 +625,7 @@ hipError_t launch_mmvq_stream(int type, const uint8_t *w, int64_t rows, int64_t 
     if (type == kQ5_K) return dispatch<kQ5_K>(w, rows, k, xq, n, y, dbg, cm, n_exp, s);
     if (type == kQ6_K) return dispatch<kQ6_K>(w, rows, k, xq, n, y, dbg, cm, n_exp, s);
     if (type == kQ8_0) return dispatch<kQ8_0>(w, rows, k, xq, n, y, dbg, cm, n_exp, s);
+    if (type == kQ4_0) return dispatch<kQ4_0>(w, rows, k, xq, n, y, dbg, cm, n_exp, s);
     return hipErrorInvalidValue;
 }
 
@@ -615,6 +643,7 @@ hipError_t launch_mmvq_stream_glu(int type, const uint8_t *wg, const uint8_t *wu
     QMM_SG(kQ5_K)
     QMM_SG(kQ6_K)
     QMM_SG(kQ8_0)
+    QMM_SG(kQ4_0)
 #undef QMM_SG
     return hipErrorInvalidValue;
 }

@@ -196,8 +196,6 @@ def test_matvec_kernel_variants(qtype, kernel):
     kernel handles; fp32 outputs and the integer sub-block dots."""
     if kernel == 3 and qtype in (qmm.Q6_K, qmm.Q4_0):
         pytest.skip("the dot4 kernel serves Q4_K, Q5_K and Q8_0")
-    if kernel == 2 and qtype == qmm.Q4_0:
-        pytest.skip("the LDS-staged kernel serves Q4_K, Q5_K, Q6_K and Q8_0")
     qmm.set_override(qmm.OVR_MV_KERNEL, kernel)
     k = 6144 if qtype == qmm.Q6_K else 4352
     ns = (1, 2, 3) if kernel == 3 else (1, 3, 4, 5, 8)
@@ -242,7 +240,7 @@ def test_matvec_lds_kernel_at_minimum_alignment(qtype, woff):
 @pytest.mark.parametrize("kernel,qtype,k,n", [(2, qmm.Q6_K, 768, 1),    # 630-byte rows: not 16-byte aligned
                                               (3, qmm.Q6_K, 4096, 1),   # dot4 serves Q4_K / Q8_0 only
                                               (3, qmm.Q4_K, 4096, 4),   # dot4 takes at most 3 columns
-                                              (2, qmm.Q4_0, 4096, 2)])  # no LDS-staged Q4_0 form
+                                              (3, qmm.Q4_0, 4096, 1)])  # no dot4 Q4_0 form
 def test_forced_matvec_kernel_refuses_unsupported_call(kernel, qtype, k, n):
     qmm.set_override(qmm.OVR_MV_KERNEL, kernel)
     w, x = _case(qtype, 32, k, n, 540)
@@ -528,8 +526,6 @@ def test_moe_invalid_ids_and_per_slot_activations():
 def test_moe_small_experts_both_kernels(qtype, kernel):
     """Experts with at most 8 columns go to the matrix-vector kernel in expert mode; both kernels,
     ragged rows, per-slot activations, every output against the oracle."""
-    if kernel == 2 and qtype == qmm.Q4_0:
-        pytest.skip("the LDS-staged kernel serves Q4_K, Q5_K, Q6_K and Q8_0")
     qmm.set_override(qmm.OVR_MV_KERNEL, kernel)
     rng = np.random.default_rng(1100 + qtype)
     n_exp, rows, k, n_tok, top_k = 6, 77, 2048, 20, 2
