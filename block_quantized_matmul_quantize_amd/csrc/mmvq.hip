@@ -518,7 +518,9 @@ void set_mmvq_kernel(int which) { g_mv_kernel = which; }
 // Largest column count the automatic choice sends to the dot4 kernel, per type: measured at
 // 4096 x 4096 (fp32 input, graph-replayed calls), dot4 is ~0.1 us faster than the LDS-staged
 // kernel at one column and 0.8-1.4 us slower at two or three.
-static int dot4_auto_cols(int type) { return type == kQ4_K || type == kQ5_K || type == kQ8_0 ? 1 : 0; }
+static int dot4_auto_cols(int type) {
+    return type == kQ4_K || type == kQ5_K || type == kQ8_0 || type == kQ4_0 ? 1 : 0;
+}
 
 static int g_fuse_cols = 0;   // 0: automatic (5)
 

@@ -8,19 +8,20 @@
 // Lane 4r+g holds row r and the quarter g of the step: values 64g..64g+63, i.e. the two 32-value
 // sub-blocks 2g and 2g+1 -- for Q4_K the 32 qs bytes 32g..32g+31 (low nibbles sub-block 2g, high
 // nibbles 2g+1; Q5_K: the same qs bytes 32 further on, plus all 32 qh bytes, whose bits 2g and
-// 2g+1 are the fifth bits of the two sub-blocks), for Q8_0 the two 34-byte blocks.  Consecutive lanes of a row read consecutive
-// bytes, so each quarter-wave load touches one or two cache lines.  The columns' q8_1 codes and
+// // 2g+1 are the fifth bits of the two sub-blocks), for Q8_0 the two 34-byte blocks, for Q4_0 the two
+// 18-byte blocks (nibbles turned into int8 codes minus 8 in registers).  Consecutive lanes of a row
+// read consecutive bytes, so each quarter-wave load touches one or two cache lines.  The columns' q8_1 codes and
 // fp32 (d, s) are staged once per workgroup in LDS -- read from q8_1 blocks, or, for fp32 input,
 // quantized on the spot with the same arithmetic as the standalone quantize kernel (q8_1.hpp),
 // which saves that kernel's launch; every lane with the same quarter reads the same LDS words (a
 // broadcast).  Next step's weights load while this step computes.
 //   Q4_K, Q5_K  acc += D(2g)*(d*sc)*d_a - (dmin*m)*s_a   (+ the same for sub-block 2g+1)
-//   Q8_0  acc += D*d_w*d_a                         (both blocks)
+//   Q8_0, Q4_0  acc += D*d_w*d_a                   (both blocks)
 // The four quarters of a row are summed with lane shuffles, the waves in LDS in a fixed order.
 // GLU (gate/up fusion, the MMQ page's fusion passage): rows 0-7 of the workgroup are 8 gate rows,
 // rows 8-15 the same 8 rows of the up matrix, and the write-back applies silu(gate) * up.
 // Requirements (checked by the host): K a multiple of 256; Q4_K / Q5_K weights and rows 16-byte
-// aligned, Q8_0 4-byte aligned; activations 4-byte aligned.
+// aligned, Q8_0 / Q4_0 4-byte aligned; activations 4-byte aligned.
 #include "common.hpp"
 #include "launch.hpp"
 #include "mv_cols.hpp"
@@ -78,10 +79,21 @@ template <> struct W4<kQ8_0> {
         v4 = *(const uint32_t *)(p + 64);
     }
 };
+template <> struct W4<kQ4_0> {
+    u32x4 v0, v1;   // bytes 36g..36g+31 of the step: {d0, qs0[16], d1, qs1[0..13]}
+    uint32_t v4;    // bytes 36g+32..36g+35: qs1[12..15]
+    __device__ __forceinline__ void load(const uint8_t *base, uint32_t off, int g) {
+        const uint8_t *p = base + off + 36 * g;
+        v0 = *(const u32x4_a4 *)(p);
+        v1 = *(const u32x4_a4 *)(p + 16);
+        v4 = *(const uint32_t *)(p + 32);
+    }
+};
 template <int T> struct StepBytes;
 template <> struct StepBytes<kQ4_K> { static constexpr int V = 144; };
 template <> struct StepBytes<kQ5_K> { static constexpr int V = 176; };
 template <> struct StepBytes<kQ8_0> { static constexpr int V = 272; };
+template <> struct StepBytes<kQ4_0> { static constexpr int V = 144; };
 
 template <int T, int NC, bool DBG, bool EXPERT, bool F32, bool GLU>
 __global__ __launch_bounds__(1024) void mmvq_dot4_kernel(const uint8_t *__restrict__ w, const uint8_t *__restrict__ w2,
@@ -222,13 +234,37 @@ __global__ __launch_bounds__(1024) void mmvq_dot4_kernel(const uint8_t *__restri
                 }
             }
         } else {
-            // bytes 0-1: d0; 2-33: q0; 34-35: d1; 36-67: q1 -> q0 realigned by two bytes
-            const uint32_t v[17] = {x.v0.x, x.v0.y, x.v0.z, x.v0.w, x.v1.x, x.v1.y, x.v1.z, x.v1.w,
-                                    x.v2.x, x.v2.y, x.v2.z, x.v2.w, x.v3.x, x.v3.y, x.v3.z, x.v3.w, x.v4};
-            uint32_t q0[8];
+            // the lane's two blocks as int8 codes q0[32 B], q1[32 B] and their scales
+            uint32_t q0[8], q1[8];
+            float dw0, dw1;
+            if constexpr (T == kQ8_0) {
+                // bytes 0-1: d0; 2-33: q0; 34-35: d1; 36-67: q1 -> q0 realigned by two bytes
+                const uint32_t v[17] = {x.v0.x, x.v0.y, x.v0.z, x.v0.w, x.v1.x, x.v1.y, x.v1.z, x.v1.w,
+                                        x.v2.x, x.v2.y, x.v2.z, x.v2.w, x.v3.x, x.v3.y, x.v3.z, x.v3.w, x.v4};
 #pragma unroll
-            for (int i = 0; i < 8; ++i) q0[i] = __builtin_amdgcn_alignbyte(v[i + 1], v[i], 2);
-            const float dw0 = h2f((uint16_t)(v[0] & 0xFFFF)), dw1 = h2f((uint16_t)(v[8] >> 16));
+                for (int i = 0; i < 8; ++i) {
+                    q0[i] = __builtin_amdgcn_alignbyte(v[i + 1], v[i], 2);
+                    q1[i] = v[9 + i];
+                }
+                dw0 = h2f((uint16_t)(v[0] & 0xFFFF));
+                dw1 = h2f((uint16_t)(v[8] >> 16));
+            } else {
+                // Q4_0 bytes 0-1: d0; 2-17: qs0; 18-19: d1; 20-35: qs1.  Value i of a block is the
+                // low nibble of byte i, value i + 16 the high nibble; code = nibble - 8, which per
+                // byte is (nibble + 120) ^ 0x80
+                const uint32_t v[9] = {x.v0.x, x.v0.y, x.v0.z, x.v0.w, x.v1.x, x.v1.y, x.v1.z, x.v1.w, x.v4};
+                auto c4 = [](uint32_t nib) { return (nib + 0x78787878u) ^ 0x80808080u; };
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t n0 = __builtin_amdgcn_alignbyte(v[i + 1], v[i], 2), n1 = v[5 + i];
+                    q0[i] = c4(n0 & 0x0F0F0F0Fu);
+                    q0[4 + i] = c4((n0 >> 4) & 0x0F0F0F0Fu);
+                    q1[i] = c4(n1 & 0x0F0F0F0Fu);
+                    q1[4 + i] = c4((n1 >> 4) & 0x0F0F0F0Fu);
+                }
+                dw0 = h2f((uint16_t)(v[0] & 0xFFFF));
+                dw1 = h2f((uint16_t)(v[4] >> 16));
+            }
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
                 if (c >= ncols) break;
@@ -238,8 +274,8 @@ __global__ __launch_bounds__(1024) void mmvq_dot4_kernel(const uint8_t *__restri
                 int D0 = 0, D1 = 0;
                 D0 = dot4(q0[0], a0.x, D0); D0 = dot4(q0[1], a0.y, D0); D0 = dot4(q0[2], a0.z, D0); D0 = dot4(q0[3], a0.w, D0);
                 D0 = dot4(q0[4], a1.x, D0); D0 = dot4(q0[5], a1.y, D0); D0 = dot4(q0[6], a1.z, D0); D0 = dot4(q0[7], a1.w, D0);
-                D1 = dot4(v[9], a2.x, D1); D1 = dot4(v[10], a2.y, D1); D1 = dot4(v[11], a2.z, D1); D1 = dot4(v[12], a2.w, D1);
-                D1 = dot4(v[13], a3.x, D1); D1 = dot4(v[14], a3.y, D1); D1 = dot4(v[15], a3.z, D1); D1 = dot4(v[16], a3.w, D1);
+                D1 = dot4(q1[0], a2.x, D1); D1 = dot4(q1[1], a2.y, D1); D1 = dot4(q1[2], a2.z, D1); D1 = dot4(q1[3], a2.w, D1);
+                D1 = dot4(q1[4], a3.x, D1); D1 = dot4(q1[5], a3.y, D1); D1 = dot4(q1[6], a3.z, D1); D1 = dot4(q1[7], a3.w, D1);
                 if (DBG) {
                     if (dbg_row) {
                         dbg_row[(int64_t)c * dbg_ld + b0] = D0;
@@ -331,10 +367,10 @@ hipError_t dispatch(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq
 int mmvq_dot4_max_cols() { return 3; }
 
 bool mmvq_dot4_supported(int type, const void *w, int64_t k, const void *xq, const ColMap *cm) {
-    if (type != kQ4_K && type != kQ5_K && type != kQ8_0) return false;
+    if (type != kQ4_K && type != kQ5_K && type != kQ8_0 && type != kQ4_0) return false;
     if (k % kSuper != 0 || k < kSuper || k > 32768) return false;
-    const int64_t row_bytes = type == kQ8_0 ? k / 32 * 34 : k / 256 * (type == kQ5_K ? 176 : 144);
-    const int align = type == kQ8_0 ? 4 : 16;
+    const int64_t row_bytes = type == kQ8_0 ? k / 32 * 34 : type == kQ4_0 ? k / 32 * 18 : k / 256 * (type == kQ5_K ? 176 : 144);
+    const int align = type == kQ8_0 || type == kQ4_0 ? 4 : 16;
     if (row_bytes % align != 0 || (uintptr_t)w % align != 0) return false;
     if ((uintptr_t)xq % 4 != 0) return false;
     if (cm && cm->w_expert_stride % align != 0) return false;
@@ -346,6 +382,7 @@ hipError_t launch_mmvq_dot4(int type, const uint8_t *w, int64_t rows, int64_t k,
     if (type == kQ4_K) return dispatch<kQ4_K>(w, rows, k, xq, n, y, dbg, cm, n_exp, max_cols, s);
     if (type == kQ5_K) return dispatch<kQ5_K>(w, rows, k, xq, n, y, dbg, cm, n_exp, max_cols, s);
     if (type == kQ8_0) return dispatch<kQ8_0>(w, rows, k, xq, n, y, dbg, cm, n_exp, max_cols, s);
+    if (type == kQ4_0) return dispatch<kQ4_0>(w, rows, k, xq, n, y, dbg, cm, n_exp, max_cols, s);
     return hipErrorInvalidValue;
 }
 
@@ -361,6 +398,7 @@ hipError_t launch_mmvq_dot4_f32(int type, const uint8_t *w, int64_t rows, int64_
     QMM_D4F(kQ4_K)
     QMM_D4F(kQ5_K)
     QMM_D4F(kQ8_0)
+    QMM_D4F(kQ4_0)
 #undef QMM_D4F
     return hipErrorInvalidValue;
 }
@@ -377,6 +415,7 @@ hipError_t launch_mmvq_dot4_glu_f32(int type, const uint8_t *wg, const uint8_t *
     QMM_D4G(kQ4_K)
     QMM_D4G(kQ5_K)
     QMM_D4G(kQ8_0)
+    QMM_D4G(kQ4_0)
 #undef QMM_D4G
     return hipErrorInvalidValue;
 }

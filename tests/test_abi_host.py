@@ -181,7 +181,7 @@ def test_workspace_sizes_monotone():
 
 MV_AUTO = [
     # (type, n, expected (kernel, fused)) for aligned weights and fp32 activations, K = 4096:
-    # dot4 for Q4_K, Q5_K and Q8_0 at n = 1, else the LDS-staged kernel; both quantize the fp32 input
+    # dot4 for Q4_K, Q5_K, Q8_0 and Q4_0 at n = 1, else the LDS-staged kernel; both quantize the fp32 input
     # themselves at every n <= 8.
     (qmm.Q4_K, 1, (3, True)),
     *[(qmm.Q4_K, n, (2, True)) for n in range(2, 9)],
@@ -190,8 +190,8 @@ MV_AUTO = [
     (qmm.Q5_K, 1, (3, True)),
     *[(qmm.Q5_K, n, (2, True)) for n in range(2, 9)],
     *[(qmm.Q8_0, n, (2, True)) for n in range(2, 9)],
-    # Q4_0: the LDS-staged kernel at every n (no dot4 form)
-    *[(qmm.Q4_0, n, (2, True)) for n in range(1, 9)],
+    (qmm.Q4_0, 1, (3, True)),
+    *[(qmm.Q4_0, n, (2, True)) for n in range(2, 9)],
     *[(t, 9, (0, False)) for t in (qmm.Q4_K, qmm.Q5_K, qmm.Q6_K, qmm.Q8_0, qmm.Q4_0)],
 ]
 

@@ -194,8 +194,8 @@ def test_matvec_kernel_variants(qtype, kernel):
     """Every matrix-vector kernel on shapes it serves (aligned rows, K a multiple of 256): ragged
     rows, more 256-value steps than waves so some waves take two, every column-count class the
     kernel handles; fp32 outputs and the integer sub-block dots."""
-    if kernel == 3 and qtype in (qmm.Q6_K, qmm.Q4_0):
-        pytest.skip("the dot4 kernel serves Q4_K, Q5_K and Q8_0")
+    if kernel == 3 and qtype == qmm.Q6_K:
+        pytest.skip("the dot4 kernel serves Q4_K, Q5_K, Q8_0 and Q4_0")
     qmm.set_override(qmm.OVR_MV_KERNEL, kernel)
     k = 6144 if qtype == qmm.Q6_K else 4352
     ns = (1, 2, 3) if kernel == 3 else (1, 3, 4, 5, 8)
@@ -240,7 +240,7 @@ def test_matvec_lds_kernel_at_minimum_alignment(qtype, woff):
 @pytest.mark.parametrize("kernel,qtype,k,n", [(2, qmm.Q6_K, 768, 1),    # 630-byte rows: not 16-byte aligned
                                               (3, qmm.Q6_K, 4096, 1),   # dot4 serves Q4_K / Q8_0 only
                                               (3, qmm.Q4_K, 4096, 4),   # dot4 takes at most 3 columns
-                                              (3, qmm.Q4_0, 4096, 1)])  # no dot4 Q4_0 form
+                                              (3, qmm.Q4_0, 2080, 1)])  # Q4_0, K not a multiple of 256
 def test_forced_matvec_kernel_refuses_unsupported_call(kernel, qtype, k, n):
     qmm.set_override(qmm.OVR_MV_KERNEL, kernel)
     w, x = _case(qtype, 32, k, n, 540)
