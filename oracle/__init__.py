@@ -65,6 +65,10 @@ def lib():
         L.oracle_matmul_glu.restype = i32
         L.oracle_matmul_id_glu.argtypes = [i32, vp, vp, i64, i64, i64, vp, vp, i64, i64, vp, vp]
         L.oracle_matmul_id_glu.restype = i32
+        L.oracle_f16act_encode.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.oracle_f16act_encode.restype = i32
+        L.oracle_matmul_f16act.argtypes = [i32, vp, i64, i64, vp, i64, vp]
+        L.oracle_matmul_f16act.restype = i32
         _lib = L
     return _lib
 
@@ -219,3 +223,27 @@ def matmul_id_glu(qtype, w_gate, w_up, n_exp, rows, k, x, ids, fill=np.nan):
     if rc:
         raise ValueError("oracle_matmul_id_glu: bad arguments")
     return y, int(bad.value)
+
+
+def f16act_encode(x):
+    """fp16-activation mode encoder: x fp32 [n, k] -> (fp16 bit patterns uint16 [n, k], prescale
+    exponents e int32 [n, k/32], exact block sums of the fp16 values fp64 [n, k/32])."""
+    x = _c(x, np.float32)
+    n, k = x.shape
+    y = np.zeros((n, k), dtype=np.uint16)
+    e = np.zeros((n, k // 32), dtype=np.int32)
+    s = np.zeros((n, k // 32), dtype=np.float64)
+    if lib().oracle_f16act_encode(_ptr(x), n, k, _ptr(y), _ptr(e), _ptr(s)):
+        raise ValueError("oracle_f16act_encode: bad arguments")
+    return y, e, s
+
+
+def matmul_f16act(qtype, w, rows, k, x):
+    """fp16-activation mode product W . x -> y [n, rows] (fp32)."""
+    w = _c(w, np.uint8)
+    x = _c(x, np.float32)
+    n = x.shape[0]
+    y = np.zeros((n, rows), dtype=np.float32)
+    if lib().oracle_matmul_f16act(qtype, _ptr(w), rows, k, _ptr(x), n, _ptr(y)):
+        raise ValueError("oracle_matmul_f16act: bad arguments")
+    return y

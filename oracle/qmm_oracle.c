@@ -22,6 +22,12 @@
  *  - Q4_0 weights: value = d*(q - 8), 4-bit q, fp16 d per 32 values (named with the other types on
  *    the MMQ page, whose tile-size table gives it only qs and one scale; the byte layout is GGUF's
  *    block_q4_0: low nibbles of qs[0..15] are values 0..15, high nibbles values 16..31).
+ *  - fp16-activation mode ("GP100 MMVQ" page, "How" step 1 and the accuracy paragraph under the
+ *    results table): per 32 values of a column a power-of-two prescale 2^e, e the largest integer
+ *    with max|x| * 2^e < 2^15 (e = 0 for an all-zero block), the values rounded once to fp16, and
+ *    the product taken with those fp16 values unscaled by 2^-e per block.  The page's fp16
+ *    partial sums are an implementation of that product on its card; the oracle takes the plain
+ *    definition (exact fp64 sums, one rounding to fp32).
  *  - The product: per 32-value activation block b, an exact integer dot D_b of weight codes and
  *    activation codes, then the scale fixups of the "dp4a path Q4_K" / "Q6_K dot" sections.
  *    This oracle combines every exact term in fp64 and rounds to fp32 once.
@@ -566,5 +572,67 @@ int oracle_matmul_id_glu(int type, const uint8_t *wg, const uint8_t *wu, int64_t
     if (n_invalid) *n_invalid = bad;
     free(g);
     free(u);
+    return rc;
+}
+
+/* ---------------------------------------------------------------------------------------------
+ * fp16-activation mode: encoder and product (see the header).
+ * ------------------------------------------------------------------------------------------- */
+
+/* Block prescale exponent: amax in [2^(p-1), 2^p) (frexp) -> e = 15 - p puts amax * 2^e in
+ * [2^14, 2^15). */
+static int f16act_exponent(double amax) {
+    if (amax == 0.0) return 0;
+    int p;
+    frexp(amax, &p);
+    return 15 - p;
+}
+
+/* x fp32 [n][k] (k % 32 == 0) -> y fp16 bit patterns [n][k], e int32 [n][k/32], block sums
+ * bsum fp64 [n][k/32] (exact: 32 multiples of 2^-24 below 2^16). */
+int oracle_f16act_encode(const float *x, int64_t n, int64_t k, uint16_t *y, int32_t *e, double *bsum) {
+    if (n < 0 || k <= 0 || k % 32) return ORC_ERR;
+    for (int64_t c = 0; c < n; ++c)
+        for (int64_t b = 0; b < k / 32; ++b) {
+            const float *xb = x + c * k + 32 * b;
+            double amax = 0.0;
+            for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs((double)xb[i]));
+            const int eb = f16act_exponent(amax);
+            double sum = 0.0;
+            for (int i = 0; i < 32; ++i) {
+                const double v = ldexp((double)xb[i], eb);    /* exact */
+                const uint16_t h = oracle_float_to_half((float)v);  /* v is exact as fp32 or below fp16's range */
+                y[c * k + 32 * b + i] = h;
+                sum += oracle_half_to_double(h);
+            }
+            e[c * (k / 32) + b] = eb;
+            if (bsum) bsum[c * (k / 32) + b] = sum;
+        }
+    return ORC_OK;
+}
+
+/* Y[n][rows] = W . (fp16 activations unscaled per block), exact fp64 sums, one rounding. */
+int oracle_matmul_f16act(int type, const uint8_t *w, int64_t rows, int64_t k, const float *x, int64_t n, float *y) {
+    if (check_args(type, rows, k, n) || k % 32) return ORC_ERR;
+    const int64_t nb = k / 32, rb = oracle_row_bytes(type, k);
+    uint16_t *yh = (uint16_t *)malloc((size_t)(n * k) * 2 + 4);
+    int32_t *e = (int32_t *)malloc((size_t)(n * nb) * 4 + 4);
+    double *xa = (double *)malloc((size_t)(n * k) * 8 + 8);
+    double *wr = (double *)malloc((size_t)k * 8);
+    int rc = oracle_f16act_encode(x, n, k, yh, e, NULL);
+    for (int64_t c = 0; c < n && !rc; ++c)
+        for (int64_t i = 0; i < k; ++i) xa[c * k + i] = ldexp(oracle_half_to_double(yh[c * k + i]), -e[c * nb + i / 32]);
+    for (int64_t r = 0; r < rows && !rc; ++r) {
+        rc = oracle_dequantize(type, w + r * rb, 1, k, wr);
+        for (int64_t c = 0; c < n && !rc; ++c) {
+            double acc = 0.0;
+            for (int64_t i = 0; i < k; ++i) acc += wr[i] * xa[c * k + i];
+            y[c * rows + r] = (float)acc;
+        }
+    }
+    free(yh);
+    free(e);
+    free(xa);
+    free(wr);
     return rc;
 }
