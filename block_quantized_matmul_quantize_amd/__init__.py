@@ -56,6 +56,9 @@ _sig("qmm_last_error", ctypes.c_char_p)
 _sig("qmm_version", ctypes.c_char_p)
 _sig("qmm_quantize_q8_1", _i32, _vp, _i64, _i64, _vp, _vp)
 _sig("qmm_matmul_workspace", _sz, _i32, _i64, _i64, _i64)
+_sig("qmm_encode_f16act", _i32, _vp, _i64, _i64, _vp, _vp, _vp, _vp)
+_sig("qmm_matmul_f16act_workspace", _sz, _i64, _i64)
+_sig("qmm_matmul_f16act", _i32, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _sz, _vp)
 _sig("qmm_matmul", _i32, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _sz, _vp)
 _sig("qmm_matmul_q8_1_workspace", _sz, _i32, _i64, _i64, _i64)
 _sig("qmm_matmul_q8_1", _i32, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _sz, _vp)
@@ -220,6 +223,43 @@ def matmul(w, qtype, rows, k, x, out=None, ws=None):
     if ws is None:
         ws = _workspace(nbytes, x.device)
     _check(_L.qmm_matmul(qtype, pw, rows, k, px, n, py, ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream()))
+    return out
+
+
+def encode_f16act(x):
+    """fp16-activation mode encoder: fp32 [n, k] -> (fp16 bit patterns int16 [n, k], prescale
+    exponents int32 [n, k/32], fp32 block sums [n, k/32])."""
+    torch = _torch()
+    px = _need(x, torch.float32, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [n, k]")
+    n, k = x.shape
+    y16 = torch.empty((n, k), dtype=torch.int16, device=x.device)
+    e = torch.empty((n, k // 32), dtype=torch.int32, device=x.device)
+    s = torch.empty((n, k // 32), dtype=torch.float32, device=x.device)
+    _check(_L.qmm_encode_f16act(px, n, k, ctypes.c_void_p(y16.data_ptr()), ctypes.c_void_p(e.data_ptr()),
+                                ctypes.c_void_p(s.data_ptr()), _stream()))
+    return y16, e, s
+
+
+def matmul_f16act_workspace(k, n):
+    return _L.qmm_matmul_f16act_workspace(k, n)
+
+
+def matmul_f16act(w, qtype, rows, k, x, out=None, ws=None):
+    """Y[n, rows] = W[rows, k] . X[n, k]^T in the fp16-activation mode (n <= 8)."""
+    torch = _torch()
+    pw = _need(w, torch.uint8, "w")
+    px = _need(x, torch.float32, "x")
+    if x.dim() != 2 or x.shape[1] != k:
+        raise ValueError(f"x must be [n, {k}]")
+    n = x.shape[0]
+    if out is None:
+        out = torch.empty((n, rows), dtype=torch.float32, device=x.device)
+    py = _need(out, torch.float32, "out")
+    if ws is None:
+        ws = _workspace(matmul_f16act_workspace(k, n), x.device)
+    _check(_L.qmm_matmul_f16act(qtype, pw, rows, k, px, n, py, ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream()))
     return out
 
 

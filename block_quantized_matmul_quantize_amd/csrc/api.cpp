@@ -309,6 +309,60 @@ qmm_status qmm_quantize_q8_1(const float *x, int64_t n_rows, int64_t k, void *y,
     return QMM_OK;
 }
 
+static size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+qmm_status qmm_encode_f16act(const float *x, int64_t n, int64_t k, void *y16, int32_t *e, float *bsum,
+                             void *stream) {
+    if (n < 0) return fail(QMM_ERR_ARG, "n must be >= 0");
+    if (k <= 0 || k % 32 != 0) return fail(QMM_ERR_SHAPE, "k=%lld is not a positive multiple of 32", (long long)k);
+    if (k > kMaxK) return fail(QMM_ERR_SHAPE, "k too large");
+    if ((n * k + 255) / 256 >= ((int64_t)1 << 31)) return fail(QMM_ERR_SHAPE, "n * k too large");
+    if (n == 0) return QMM_OK;
+    if (!x || !y16 || !e || !bsum) return fail(QMM_ERR_ARG, "null pointer");
+    if ((((uintptr_t)x) & 3) || (((uintptr_t)y16) & 1) || (((uintptr_t)e) & 3) || (((uintptr_t)bsum) & 3))
+        return fail(QMM_ERR_ARG, "x, e, bsum must be 4-byte and y16 2-byte aligned");
+    hipError_t h = qmm::launch_f16act_encode(x, n, k, (uint16_t *)y16, e, bsum, (hipStream_t)stream);
+    if (h != hipSuccess) return hip_fail(h, "f16act encode launch");
+    return QMM_OK;
+}
+
+size_t qmm_matmul_f16act_workspace(int64_t k, int64_t n) {
+    if (k <= 0 || k % 32 != 0 || k > kMaxK || n < 0 || n > 8) return 0;
+    return up256((size_t)(n * k) * 2) + 2 * up256((size_t)(n * (k / 32)) * 4);
+}
+
+qmm_status qmm_matmul_f16act(int type, const void *w, int64_t rows, int64_t k, const float *x, int64_t n, float *y,
+                             void *ws, size_t ws_bytes, void *stream) {
+    if (type != QMM_Q4_0 && type != QMM_Q8_0 && type != QMM_Q4_K && type != QMM_Q5_K && type != QMM_Q6_K)
+        return fail(QMM_ERR_TYPE, "type %d: the fp16-activation mode serves Q4_0=2, Q8_0=8, Q4_K=12, Q5_K=13, Q6_K=14",
+                    type);
+    if (rows < 1) return fail(QMM_ERR_ARG, "rows must be >= 1");
+    if (n < 0 || n > 8) return fail(QMM_ERR_ARG, "the fp16-activation mode takes 0..8 columns (n=%lld)", (long long)n);
+    const int64_t qk = (type == QMM_Q4_0 || type == QMM_Q8_0) ? 32 : 256;
+    if (k <= 0 || k % qk != 0) return fail(QMM_ERR_SHAPE, "k=%lld is not a positive multiple of %lld", (long long)k,
+                                           (long long)qk);
+    if (k > kMaxK) return fail(QMM_ERR_SHAPE, "k too large");
+    if (rows >= ((int64_t)1 << 33)) return fail(QMM_ERR_SHAPE, "rows too large");
+    if (n == 0) return QMM_OK;
+    if (!w || !x || !y) return fail(QMM_ERR_ARG, "null w, x or y");
+    const bool k45 = type == QMM_Q4_K || type == QMM_Q5_K;
+    if (((uintptr_t)w) & (k45 ? 15 : 1)) return fail(QMM_ERR_ARG, k45 ? "w must be 16-byte aligned" : "w must be 2-byte aligned");
+    if ((((uintptr_t)x) & 3) || (((uintptr_t)y) & 3)) return fail(QMM_ERR_ARG, "x and y must be 4-byte aligned");
+    const size_t need = qmm_matmul_f16act_workspace(k, n);
+    if (!ws || ws_bytes < need) return fail(QMM_ERR_WORKSPACE, "workspace needs %zu bytes", need);
+    if (((uintptr_t)ws) & 255) return fail(QMM_ERR_ARG, "workspace must be 256-byte aligned");
+    uint8_t *base = (uint8_t *)ws;
+    uint16_t *y16 = (uint16_t *)base;
+    int32_t *e = (int32_t *)(base + up256((size_t)(n * k) * 2));
+    float *bsum = (float *)(base + up256((size_t)(n * k) * 2) + up256((size_t)(n * (k / 32)) * 4));
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t h = qmm::launch_f16act_encode(x, n, k, y16, e, bsum, s);
+    if (h != hipSuccess) return hip_fail(h, "f16act encode launch");
+    h = qmm::launch_mmvq_f16act(type, (const uint8_t *)w, rows, k, y16, e, bsum, n, y, s);
+    if (h != hipSuccess) return hip_fail(h, "f16act matrix-vector launch");
+    return QMM_OK;
+}
+
 size_t qmm_matmul_workspace(int type, int64_t rows, int64_t k, int64_t n) {
     if (check_common(type, rows, k, n)) return 0;
     return dense_layout(type, rows, k, n, true).total;

@@ -117,4 +117,10 @@ hipError_t launch_moe_group(const int32_t *ids, int64_t pairs, int32_t n_exp, in
                             int32_t small_max, int32_t *sorted, int32_t *bounds, int32_t *tile_start,
                             int32_t *small, int32_t *invalid, hipStream_t s);
 
+// fp16-activation mode (f16act.hip)
+hipError_t launch_f16act_encode(const float *x, int64_t n, int64_t k, uint16_t *y16, int32_t *e, float *bsum,
+                                hipStream_t s);
+hipError_t launch_mmvq_f16act(int type, const uint8_t *w, int64_t rows, int64_t k, const uint16_t *y16,
+                              const int32_t *e, const float *bsum, int64_t n, float *out, hipStream_t s);
+
 }  // namespace qmm

@@ -124,6 +124,29 @@ qmm_status qmm_matmul_id_grouping_layout(int type, int64_t n_exp, int64_t k, int
                                          int64_t top_k, int64_t x_per_tok, int64_t *out);
 
 /* ---------------------------------------------------------------------------------------------
+ * fp16-activation matrix-vector mode ([GP100] "How", step 1, and the accuracy paragraph under its
+ * results table): an alternative numeric definition for 1..8 columns in which the activations
+ * are not quantized to 8 bits but rounded once to fp16 after a power-of-two prescale per 32
+ * values: e = the largest integer with max|x| * 2^e < 2^15 over the block (0 for an all-zero
+ * block), y = fp16(x * 2^e) (round to nearest even), and the block sum of the y kept in fp32.
+ * The product is W . (y * 2^-e) with fp32 accumulation.
+ *
+ * qmm_encode_f16act: x fp32 [n][k] (k % 32 == 0, 4-byte aligned) -> y16 fp16 bit patterns [n][k]
+ *   (2-byte aligned), e int32 [n][k/32], bsum fp32 [n][k/32] (4-byte aligned), all device memory
+ *   owned by the caller.  n == 0 is a no-op.
+ * qmm_matmul_f16act_workspace: bytes of device workspace (256-byte aligned) for n columns of k.
+ * qmm_matmul_f16act: Y[n][rows] = W[rows][k] . X[n][k]^T in this mode; types Q4_0, Q8_0, Q4_K,
+ *   Q5_K, Q6_K; 0 <= n <= 8 (more columns: QMM_ERR_ARG; n == 0 is a no-op); k a multiple of the
+ *   type's block (256 for the K types), k <= 1<<20; Q4_K / Q5_K weights 16-byte aligned, the
+ *   others 2-byte aligned; x and y 4-byte aligned.  Asynchronous on stream.
+ * ------------------------------------------------------------------------------------------- */
+qmm_status qmm_encode_f16act(const float *x, int64_t n, int64_t k, void *y16, int32_t *e, float *bsum,
+                             void *stream);
+size_t qmm_matmul_f16act_workspace(int64_t k, int64_t n);
+qmm_status qmm_matmul_f16act(int type, const void *w, int64_t rows, int64_t k, const float *x, int64_t n,
+                             float *y, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Gate/up products fused with SwiGLU ([MMQ] the fusion passage after "MoE dispatch": the gate and
  * up products of one input are computed together and the GLU is applied at write-back; SwiGLU
  * read as silu(g) * u, silu(g) = g / (1 + exp(-g))).
