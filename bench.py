@@ -13,6 +13,7 @@ Also in the same JSON line:
                 events on the launch stream; peak = 8 TB/s HBM.  traffic comes from the committed
                 rocprofv3 FETCH_SIZE/WRITE_SIZE summary when it matches the current sources.
   cpu_baseline  the oracle (plain C, all host threads) on whole steps of the same workload.
+  f16act_matvec  per-call timing (encoder + kernel) of the fp16-activation mode on the step's shapes
   extra_types_matvec  per-launch timing of the same matrix-vector shapes in Q5_K and Q4_0 (not
                 part of the step).
   secondary     int8 TOPS and % of the 5.0 POP/s int8 MFMA peak for the prefill and MoE shapes, and
@@ -239,6 +240,24 @@ def main():
         log(f"[bench]   {c['name']:24s} {q5_cases[-1]['kernel']:30s} {us:8.3f} us  {b / us / 1e3:8.1f} GB/s")
         del w5
 
+    # fp16-activation mode (encoder + wave-per-row kernel: two launches per call) on the step's shapes
+    f16_cases = []
+    for i, c in enumerate(synth.MMVQ_CASES):
+        wf = [torch.from_numpy(synth.gen_weights(c["qtype"], c["rows"], c["k"], synth.rngs(5000 * r + i, 1)[0])).to(dev)
+              for r in range(R)]
+        xf = torch.from_numpy(synth.gen_activations(c["n"], c["k"], synth.rngs(90 + i, 1)[0])).to(dev)
+        yf = torch.empty((c["n"], c["rows"]), dtype=torch.float32, device=dev)
+        wsf = qmm._workspace(qmm.matmul_f16act_workspace(c["k"], c["n"]), dev)
+        g = capture(lambda: [qmm.matmul_f16act(wf[r], c["qtype"], c["rows"], c["k"], xf, out=yf, ws=wsf)
+                             for _ in range(4) for r in range(R)])
+        g.replay()
+        us = run(nrep, lambda s: g.replay()) * 1e3 / (4 * R)
+        b = launch_bytes(c["qtype"], c["rows"], c["k"], c["n"], BB, BV, True)
+        f16_cases.append({"case": c["name"], "launches_per_call": 2, "us": round(us, 3),
+                          "GBps": round(b / us / 1e3, 1), "frac": round(b / us / 1e3 / HBM_PEAK_GBPS, 4)})
+        log(f"[bench]   f16act {c['name']:24s} {us:8.3f} us  {b / us / 1e3:8.1f} GB/s")
+        del wf
+
     traffic = None
     tpath = os.path.join(ROOT, "profiles", "mmvq_traffic.json")
     if os.path.exists(tpath):
@@ -279,6 +298,7 @@ def main():
         "cpu_baseline": cpu,
         "secondary": secondary,
         "extra_types_matvec": q5_cases,
+        "f16act_matvec": f16_cases,
     }
     print(json.dumps(out), flush=True)
 
