@@ -39,7 +39,8 @@ _i64, _i32, _vp, _sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_s
 class Plan(ctypes.Structure):
     _fields_ = [("regime", ctypes.c_int32), ("tile_i", ctypes.c_int32), ("tile_j", ctypes.c_int32),
                 ("ntiles", ctypes.c_int64), ("efficiency_pct", ctypes.c_int32), ("stream_k", ctypes.c_int32),
-                ("k_iters", ctypes.c_int64), ("units", ctypes.c_int64), ("fixup", ctypes.c_int32)]
+                ("k_iters", ctypes.c_int64), ("units", ctypes.c_int64), ("fixup", ctypes.c_int32),
+                ("ws_bytes", ctypes.c_uint64)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -70,7 +71,8 @@ _sig("qmm_matmul_glu", _i32, _i32, _vp, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _s
 _sig("qmm_matmul_id_glu_workspace", _sz, _i32, _i64, _i64, _i64, _i64, _i64)
 _sig("qmm_matmul_id_glu", _i32, _i32, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _vp, _sz, _vp)
 _sig("qmm_matmul_id_grouping_layout", _i32, _i32, _i64, _i64, _i64, _i64, _i64, ctypes.POINTER(_i64))
-_sig("qmm_debug_subdots", _i32, _i32, _vp, _i64, _i64, _vp, _i64, _i32, _vp, _vp)
+_sig("qmm_debug_subdots_workspace", _sz, _i32, _i64, _i64, _i64, _i32)
+_sig("qmm_debug_subdots", _i32, _i32, _vp, _i64, _i64, _vp, _i64, _i32, _vp, _vp, _sz, _vp)
 _sig("qmm_set_override", _i32, _i32, _i32)
 _sig("qmm_plan_dense", _i32, _i32, _i64, _i64, _i64, ctypes.c_int32, ctypes.POINTER(Plan))
 _sig("qmm_tile_efficiency", ctypes.c_int32, _i64, ctypes.c_int32)
@@ -182,11 +184,34 @@ def _need(t, dtype, name):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return ctypes.c_void_p(t.data_ptr())
+
+
+def _on_device(**tensors):
+    """Last check before a pointer crosses the C ABI: every tensor lives in device memory."""
+    for name, t in tensors.items():
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+
+
+def weight_bytes(qtype, rows, k):
+    """Bytes of a [rows][k] weight matrix of GGUF blocks (ValueError for an unknown type or a k
+    that is not a multiple of the block size)."""
+    if qtype not in BLOCK_VALUES:
+        raise ValueError(f"unsupported weight type {qtype}")
+    if k <= 0 or k % BLOCK_VALUES[qtype]:
+        raise ValueError(f"k={k} is not a positive multiple of the block size {BLOCK_VALUES[qtype]}")
+    return rows * (k // BLOCK_VALUES[qtype]) * BLOCK_BYTES[qtype]
+
+
+def _need_size(t, nbytes, name):
+    """The C ABI receives bare pointers, so a tensor smaller than the shape it stands for would be
+    read or written past its end on the device: refuse it here."""
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{name} holds {have} bytes, the call needs {nbytes}")
 
 
 def _workspace(nbytes, device):
@@ -204,6 +229,8 @@ def quantize_q8_1(x, out=None):
     if out is None:
         out = torch.empty((n, (k // 32) * Q8_1_BYTES), dtype=torch.uint8, device=x.device)
     py = _need(out, torch.uint8, "out")
+    _need_size(out, n * (k // 32) * Q8_1_BYTES, "out")
+    _on_device(x=x, out=out)
     _check(_L.qmm_quantize_q8_1(px, n, k, py, _stream()))
     return out
 
@@ -216,12 +243,15 @@ def matmul(w, qtype, rows, k, x, out=None, ws=None):
     if x.dim() != 2 or x.shape[1] != k:
         raise ValueError(f"x must be [n, {k}]")
     n = x.shape[0]
+    _need_size(w, weight_bytes(qtype, rows, k), "w")
     if out is None:
         out = torch.empty((n, rows), dtype=torch.float32, device=x.device)
     py = _need(out, torch.float32, "out")
+    _need_size(out, n * rows * 4, "out")
     nbytes = matmul_workspace(qtype, rows, k, n)
     if ws is None:
         ws = _workspace(nbytes, x.device)
+    _on_device(w=w, x=x, out=out, ws=ws)
     _check(_L.qmm_matmul(qtype, pw, rows, k, px, n, py, ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream()))
     return out
 
@@ -237,6 +267,7 @@ def encode_f16act(x):
     y16 = torch.empty((n, k), dtype=torch.int16, device=x.device)
     e = torch.empty((n, k // 32), dtype=torch.int32, device=x.device)
     s = torch.empty((n, k // 32), dtype=torch.float32, device=x.device)
+    _on_device(x=x)
     _check(_L.qmm_encode_f16act(px, n, k, ctypes.c_void_p(y16.data_ptr()), ctypes.c_void_p(e.data_ptr()),
                                 ctypes.c_void_p(s.data_ptr()), _stream()))
     return y16, e, s
@@ -254,11 +285,14 @@ def matmul_f16act(w, qtype, rows, k, x, out=None, ws=None):
     if x.dim() != 2 or x.shape[1] != k:
         raise ValueError(f"x must be [n, {k}]")
     n = x.shape[0]
+    _need_size(w, weight_bytes(qtype, rows, k), "w")
     if out is None:
         out = torch.empty((n, rows), dtype=torch.float32, device=x.device)
     py = _need(out, torch.float32, "out")
+    _need_size(out, n * rows * 4, "out")
     if ws is None:
         ws = _workspace(matmul_f16act_workspace(k, n), x.device)
+    _on_device(w=w, x=x, out=out, ws=ws)
     _check(_L.qmm_matmul_f16act(qtype, pw, rows, k, px, n, py, ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream()))
     return out
 
@@ -270,12 +304,15 @@ def matmul_q8_1(w, qtype, rows, k, xq, n, out=None, ws=None):
     px = _need(xq, torch.uint8, "xq")
     if xq.numel() != n * (k // 32) * Q8_1_BYTES:
         raise ValueError("xq has the wrong number of bytes")
+    _need_size(w, weight_bytes(qtype, rows, k), "w")
     if out is None:
         out = torch.empty((n, rows), dtype=torch.float32, device=xq.device)
     py = _need(out, torch.float32, "out")
+    _need_size(out, n * rows * 4, "out")
     nbytes = matmul_q8_1_workspace(qtype, rows, k, n)
     if ws is None:
         ws = _workspace(nbytes, xq.device)
+    _on_device(w=w, xq=xq, out=out, ws=ws)
     _check(_L.qmm_matmul_q8_1(qtype, pw, rows, k, px, n, py, ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream()))
     return out
 
@@ -287,15 +324,20 @@ def matmul_id(w, qtype, n_exp, rows, k, x, ids, x_per_tok=1, out=None, ws=None):
     pw = _need(w, torch.uint8, "w")
     px = _need(x, torch.float32, "x")
     pi = _need(ids, torch.int32, "ids")
+    if ids.dim() != 2:
+        raise ValueError("ids must be 2-D [n_tok, top_k]")
     n_tok, top_k = ids.shape
     if x.shape != (n_tok * x_per_tok, k):
         raise ValueError(f"x must be [{n_tok * x_per_tok}, {k}]")
+    _need_size(w, n_exp * weight_bytes(qtype, rows, k), "w")
     if out is None:
         out = torch.zeros((n_tok, top_k, rows), dtype=torch.float32, device=x.device)
     py = _need(out, torch.float32, "out")
+    _need_size(out, n_tok * top_k * rows * 4, "out")
     nbytes = matmul_id_workspace(qtype, n_exp, rows, k, n_tok, top_k, x_per_tok)
     if ws is None:
         ws = _workspace(nbytes, x.device)
+    _on_device(w=w, x=x, ids=ids, out=out, ws=ws)
     _check(_L.qmm_matmul_id(qtype, pw, n_exp, rows, k, px, x_per_tok, pi, n_tok, top_k, py,
                             ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream()))
     return out, ws
@@ -308,6 +350,7 @@ def matmul_glu(w_gate, w_up, qtype, rows, k, x, out=None, ws=None):
     pu = _need(w_up, torch.uint8, "w_up")
     if w_gate.numel() != w_up.numel():
         raise ValueError("w_gate and w_up must have the same size")
+    _need_size(w_gate, weight_bytes(qtype, rows, k), "w_gate")
     px = _need(x, torch.float32, "x")
     if x.dim() != 2 or x.shape[1] != k:
         raise ValueError(f"x must be [n, {k}]")
@@ -315,8 +358,10 @@ def matmul_glu(w_gate, w_up, qtype, rows, k, x, out=None, ws=None):
     if out is None:
         out = torch.empty((n, rows), dtype=torch.float32, device=x.device)
     py = _need(out, torch.float32, "out")
+    _need_size(out, n * rows * 4, "out")
     if ws is None:
         ws = _workspace(matmul_glu_workspace(qtype, rows, k, n), x.device)
+    _on_device(w_gate=w_gate, w_up=w_up, x=x, out=out, ws=ws)
     _check(_L.qmm_matmul_glu(qtype, pg, pu, rows, k, px, n, py, ctypes.c_void_p(ws.data_ptr()), ws.numel(),
                              _stream()))
     return out
@@ -330,16 +375,21 @@ def matmul_id_glu(w_gate, w_up, qtype, n_exp, rows, k, x, ids, out=None, ws=None
     pu = _need(w_up, torch.uint8, "w_up")
     if w_gate.numel() != w_up.numel():
         raise ValueError("w_gate and w_up must have the same size")
+    _need_size(w_gate, n_exp * weight_bytes(qtype, rows, k), "w_gate")
     px = _need(x, torch.float32, "x")
     pi = _need(ids, torch.int32, "ids")
+    if ids.dim() != 2:
+        raise ValueError("ids must be 2-D [n_tok, top_k]")
     n_tok, top_k = ids.shape
     if x.shape != (n_tok, k):
         raise ValueError(f"x must be [{n_tok}, {k}]")
     if out is None:
         out = torch.zeros((n_tok, top_k, rows), dtype=torch.float32, device=x.device)
     py = _need(out, torch.float32, "out")
+    _need_size(out, n_tok * top_k * rows * 4, "out")
     if ws is None:
         ws = _workspace(matmul_id_glu_workspace(qtype, n_exp, rows, k, n_tok, top_k), x.device)
+    _on_device(w_gate=w_gate, w_up=w_up, x=x, ids=ids, out=out, ws=ws)
     _check(_L.qmm_matmul_id_glu(qtype, pg, pu, n_exp, rows, k, px, pi, n_tok, top_k, py,
                                 ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream()))
     return out, ws
@@ -375,12 +425,22 @@ def matmul_id_grouping(ws, qtype, n_exp, k, n_tok, top_k, x_per_tok=1):
             "small": take(out[3], n_exp), "tile_j": int(out[4]), "small_max": int(out[5])}
 
 
+def debug_subdots_workspace(qtype, rows, k, n, path):
+    return int(_L.qmm_debug_subdots_workspace(qtype, rows, k, n, path))
+
+
 def debug_subdots(w, qtype, rows, k, xq, n, path):
-    """Integer sub-block dots from the chosen production kernel: int32 [n, rows, per]."""
+    """Integer sub-block dots from the chosen production kernel in its production plan: int32
+    [n, rows, per]."""
     torch = _torch()
     pw = _need(w, torch.uint8, "w")
     px = _need(xq, torch.uint8, "xq")
+    _need_size(w, weight_bytes(qtype, rows, k), "w")
+    _need_size(xq, n * (k // 32) * Q8_1_BYTES, "xq")
     per = k // 16 if (qtype == Q6_K and path == PATH_MATVEC) else k // 32
     out = torch.zeros((n, rows, per), dtype=torch.int32, device=xq.device)
-    _check(_L.qmm_debug_subdots(qtype, pw, rows, k, px, n, path, ctypes.c_void_p(out.data_ptr()), _stream()))
+    ws = _workspace(debug_subdots_workspace(qtype, rows, k, n, path), xq.device)
+    _on_device(w=w, xq=xq, out=out, ws=ws)
+    _check(_L.qmm_debug_subdots(qtype, pw, rows, k, px, n, path, ctypes.c_void_p(out.data_ptr()),
+                                ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream()))
     return out

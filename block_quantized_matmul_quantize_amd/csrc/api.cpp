@@ -33,7 +33,21 @@ qmm_status hip_fail(hipError_t e, const char *what) {
     return fail(QMM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-std::atomic<int> g_ovr_path{0}, g_ovr_streamk{0}, g_ovr_tile_j{0};
+// qmm_set_override's values (the only process-wide state an entry point depends on besides the
+// device-property cache); each call reads them once, into a qmm::Ovr.
+std::atomic<int> g_ovr_path{0}, g_ovr_streamk{0}, g_ovr_tile_j{0}, g_ovr_mv_steps{0}, g_ovr_mv_kernel{0},
+    g_ovr_fuse_cols{0};
+
+qmm::Ovr load_ovr() {
+    qmm::Ovr o;
+    o.path = g_ovr_path.load();
+    o.streamk = g_ovr_streamk.load();
+    o.tile_j = g_ovr_tile_j.load();
+    o.mv_steps = g_ovr_mv_steps.load();
+    o.mv_kernel = g_ovr_mv_kernel.load();
+    o.fuse_cols = g_ovr_fuse_cols.load();
+    return o;
+}
 
 constexpr int64_t kMaxK = 1 << 20;
 constexpr int64_t kMvMaxK = 32768;     // matrix-vector kernel stages k/32 scales in LDS
@@ -153,26 +167,26 @@ qmm_status qmm_set_override(int key, int value) {
         case QMM_OVR_MV_STEPS:
             if (value != 0 && value != 1 && value != 2 && value != 4)
                 return fail(QMM_ERR_ARG, "steps-per-wave override must be 0, 1, 2 or 4");
-            qmm::set_mmvq_steps_per_wave(value); return QMM_OK;
+            g_ovr_mv_steps = value; return QMM_OK;
         case QMM_OVR_MV_KERNEL:
             if (value < 0 || value > 3) return fail(QMM_ERR_ARG, "matrix-vector kernel override must be 0..3");
-            qmm::set_mmvq_kernel(value); return QMM_OK;
+            g_ovr_mv_kernel = value; return QMM_OK;
         case QMM_OVR_FUSE_COLS:
             if (value < 0 || value > 8) return fail(QMM_ERR_ARG, "fused-quantize column override must be 0..8");
-            qmm::set_mmvq_fuse_cols(value); return QMM_OK;
+            g_ovr_fuse_cols = value; return QMM_OK;
         default:
             return fail(QMM_ERR_ARG, "unknown override key %d", key);
     }
 }
 
-qmm_status qmm_plan_dense(int type, int64_t rows, int64_t k, int64_t n, int32_t nsm, qmm_plan *out) {
-    qmm_status st = check_common(type, rows, k, n);
-    if (st) return st;
-    if (!out || nsm <= 0) return fail(QMM_ERR_ARG, "null plan pointer or nsm <= 0");
+}  // extern "C"
+
+namespace {
+
+// The planner under a given override snapshot (arguments already checked).
+qmm_plan plan_dense_impl(int type, int64_t rows, int64_t k, int64_t n, int32_t nsm, const qmm::Ovr &o) {
     qmm_plan p{};
-    const int path = g_ovr_path.load();
-    const bool mv = (path == 1) ? (n <= 8 && k <= kMvMaxK) : (path == 2 ? false : (n <= 8 && k <= kMvMaxK));
-    if (path == 1 && !mv) return fail(QMM_ERR_ARG, "matrix-vector path forced but n=%lld > 8 or k > %lld", (long long)n, (long long)kMvMaxK);
+    const bool mv = o.path == 2 ? false : (n <= 8 && k <= kMvMaxK);
     p.k_iters = (k + 255) / 256;
     if (mv) {
         p.regime = 1;
@@ -181,29 +195,54 @@ qmm_status qmm_plan_dense(int type, int64_t rows, int64_t k, int64_t n, int32_t 
         p.ntiles = (rows + 15) / 16;
         p.efficiency_pct = qmm_tile_efficiency(p.ntiles, nsm);
         p.units = p.ntiles;
-        out[0] = p;
-        return QMM_OK;
+        return p;
     }
     p.regime = 2;
     p.tile_i = kTI;
-    p.tile_j = g_ovr_tile_j.load() ? g_ovr_tile_j.load() : qmm_select_tile_j(n);
+    p.tile_j = o.tile_j ? o.tile_j : qmm_select_tile_j(n);
     const int64_t n_ct = (n + p.tile_j - 1) / p.tile_j;
     p.ntiles = ((rows + kTI - 1) / kTI) * n_ct;
     const int occ = mmq_resident(type, p.tile_j);
     const int32_t slots = nsm * occ;
     p.efficiency_pct = qmm_tile_efficiency(p.ntiles, slots);
-    const int sk = g_ovr_streamk.load();
     // stream-K pays a partial-tile round trip and a fixup pass: the MMQ page's "when not to use
     // stream-K" threshold, tile efficiency below 90 % (measured here: at 87.5 % stream-K is ~5 %
     // faster, at 100 % within noise)
     bool use_sk = p.efficiency_pct < 90 && p.k_iters > 1;
-    if (sk == 1) use_sk = false;
-    if (sk == 2) use_sk = p.k_iters > 1 || p.ntiles > 1;
+    if (o.streamk == 1) use_sk = false;
+    if (o.streamk == 2) use_sk = p.k_iters > 1 || p.ntiles > 1;
+    if (p.ntiles == 0) use_sk = false;   // n == 0: nothing to split (and no unit to divide by)
     p.stream_k = use_sk ? 1 : 0;
     const int64_t nwork = p.ntiles * p.k_iters;
     p.units = use_sk ? std::min<int64_t>(slots, nwork) : p.ntiles;
     p.fixup = use_sk && (p.ntiles % p.units != 0) ? 1 : 0;
-    out[0] = p;
+    return p;
+}
+
+qmm_status check_plan_args(int type, int64_t rows, int64_t k, int64_t n, const qmm::Ovr &o) {
+    qmm_status st = check_common(type, rows, k, n);
+    if (st) return st;
+    if (o.path == 1 && !(n <= 8 && k <= kMvMaxK))
+        return fail(QMM_ERR_ARG, "matrix-vector path forced but n=%lld > 8 or k > %lld", (long long)n, (long long)kMvMaxK);
+    return QMM_OK;
+}
+
+struct DenseWs {
+    size_t xq_off, tiled_off, part_off, total;
+};
+DenseWs dense_layout(int type, int64_t rows, int64_t k, int64_t n, bool with_xq, const qmm::Ovr &o);
+
+}  // namespace
+
+extern "C" {
+
+qmm_status qmm_plan_dense(int type, int64_t rows, int64_t k, int64_t n, int32_t nsm, qmm_plan *out) {
+    const qmm::Ovr o = load_ovr();
+    qmm_status st = check_plan_args(type, rows, k, n, o);
+    if (st) return st;
+    if (!out || nsm <= 0) return fail(QMM_ERR_ARG, "null plan pointer or nsm <= 0");
+    out[0] = plan_dense_impl(type, rows, k, n, nsm, o);
+    out[0].ws_bytes = dense_layout(type, rows, k, n, true, o).total;
     return QMM_OK;
 }
 
@@ -212,17 +251,13 @@ qmm_status qmm_plan_dense(int type, int64_t rows, int64_t k, int64_t n, int32_t 
 // ----------------------------------------------------------------------------------------------
 namespace {
 
-struct DenseWs {
-    size_t xq_off, tiled_off, part_off, total;
-};
-
 // Workspace of a dense call: canonical q8_1 blocks for fp32 input on the matrix-vector path (used
 // only where the kernel does not quantize itself), the tiled-kernel activation layout and the
 // stream-K partial slots on the tiled path.
-DenseWs dense_layout(int type, int64_t rows, int64_t k, int64_t n, bool with_xq) {
+DenseWs dense_layout(int type, int64_t rows, int64_t k, int64_t n, bool with_xq, const qmm::Ovr &o) {
     DenseWs L{};
     const int64_t nb = k / 32;
-    const bool tiled = n > 8 || k > kMvMaxK || g_ovr_path.load() == 2;   // as qmm_plan_dense decides
+    const bool tiled = n > 8 || k > kMvMaxK || o.path == 2;   // as plan_dense_impl decides
     size_t off = 0;
     L.xq_off = off;
     if (with_xq && !tiled) off = align_up(off + (size_t)(n * nb * 36), 256);
@@ -240,30 +275,23 @@ DenseWs dense_layout(int type, int64_t rows, int64_t k, int64_t n, bool with_xq)
     return L;
 }
 
-// xq: canonical q8_1 blocks, or (x_tiled) activations already in the tiled layout.
+// xq: canonical q8_1 blocks, or (x_tiled) activations already in the tiled layout.  The plan,
+// the workspace layout L and the kernel choices all come from the one override snapshot o.  dbg
+// set: the integer-dot export of the planned kernel (the tiled kernel in its production plan,
+// stream-K included, with only its epilogue changed; y is not written).
 qmm_status run_dense(int type, const void *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y,
-                     uint8_t *ws, const DenseWs &L, int32_t *dbg, int dbg_path, hipStream_t s, bool x_tiled = false) {
+                     uint8_t *ws, const DenseWs &L, int32_t *dbg, const qmm::Ovr &o, hipStream_t s,
+                     bool x_tiled = false) {
     hipError_t e;
-    qmm_plan p{};
-    qmm_status st;
-    if (dbg) {
-        // debug export: the chosen kernel, no stream-K
-        const int save_path = g_ovr_path.load(), save_sk = g_ovr_streamk.load();
-        g_ovr_path = dbg_path;
-        g_ovr_streamk = 1;
-        st = qmm_plan_dense(type, rows, k, n, device_cus(), &p);
-        g_ovr_path = save_path;
-        g_ovr_streamk = save_sk;
-    } else {
-        st = qmm_plan_dense(type, rows, k, n, device_cus(), &p);
-    }
-    if (st) return st;
+    const qmm_plan p = plan_dense_impl(type, rows, k, n, device_cus(), o);
+    const bool tiled_ws = L.tiled_off != L.part_off;   // the layout reserved the tiled copy
     if (p.regime == 1) {
         if (x_tiled) return fail(QMM_ERR_ARG, "internal: tiled activations on the matrix-vector path");
-        e = qmm::launch_mmvq(type, (const uint8_t *)w, rows, k, xq, n, y, dbg, nullptr, 0, s);
+        e = qmm::launch_mmvq(type, (const uint8_t *)w, rows, k, xq, n, y, dbg, nullptr, 0, o, s);
         if (e != hipSuccess) return hip_fail(e, "matrix-vector kernel launch");
         return QMM_OK;
     }
+    if (!tiled_ws) return fail(QMM_ERR_ARG, "internal: workspace layout without the tiled activations");
     qmm::MmqLaunch ml{};
     ml.tile_j = p.tile_j;
     ml.ntiles = p.ntiles;
@@ -274,9 +302,8 @@ qmm_status run_dense(int type, const void *w, int64_t rows, int64_t k, const uin
     ml.partials = (float *)(ws + L.part_off);
     if (ml.stream_k && (size_t)(L.part_off + (size_t)ml.units * 2 * kTI * p.tile_j * 4) > L.total)
         return fail(QMM_ERR_WORKSPACE, "internal: stream-K partials exceed the workspace");
-    // the production tiled kernel reads the tiled layout, the debug export canonical blocks
     const uint8_t *xa = xq;
-    if (!dbg && !x_tiled) {
+    if (!x_tiled) {
         e = qmm::launch_relayout_q8_1_tiled(xq, n, k, ws + L.tiled_off, s);
         if (e != hipSuccess) return hip_fail(e, "relayout launch");
         xa = ws + L.tiled_off;
@@ -292,6 +319,29 @@ qmm_status check_ptrs_dense(const void *w, const void *x, const float *y, int64_
     if (((uintptr_t)w) & 1) return fail(QMM_ERR_ARG, "w must be 2-byte aligned");
     if (((uintptr_t)y) & 3) return fail(QMM_ERR_ARG, "y must be 4-byte aligned");
     return QMM_OK;
+}
+
+// fp32-input dense product once the arguments are checked; wsb holds at least L.total bytes.
+qmm_status dense_f32(int type, const void *w, int64_t rows, int64_t k, const float *x, int64_t n, float *y,
+                     uint8_t *wsb, const DenseWs &L, const qmm::Ovr &o, hipStream_t s) {
+    const qmm_plan p = plan_dense_impl(type, rows, k, n, device_cus(), o);
+    if (p.regime == 1) {
+        const int fc = qmm::mmvq_fused_choice(type, w, k, x, n, o);
+        if (fc) {
+            // few columns: the dot4 or LDS-staged kernel quantizes the activations itself (the same
+            // q8_1 bytes as the quantize kernel below), one launch instead of two
+            hipError_t e = qmm::launch_mmvq_fused(fc, type, (const uint8_t *)w, rows, k, x, n, y, s);
+            if (e != hipSuccess) return hip_fail(e, "fused matrix-vector kernel launch");
+            return QMM_OK;
+        }
+        hipError_t e = qmm::launch_quantize_q8_1(x, n, k, wsb + L.xq_off, s);
+        if (e != hipSuccess) return hip_fail(e, "quantize launch");
+        return run_dense(type, w, rows, k, wsb + L.xq_off, n, y, wsb, L, nullptr, o, s);
+    }
+    // tiled path: quantize straight into the tiled kernel's layout
+    hipError_t e = qmm::launch_quantize_q8_1_tiled(x, n, k, wsb + L.tiled_off, nullptr, s);
+    if (e != hipSuccess) return hip_fail(e, "quantize launch");
+    return run_dense(type, w, rows, k, wsb + L.tiled_off, n, y, wsb, L, nullptr, o, s, true);
 }
 
 }  // namespace
@@ -365,82 +415,65 @@ qmm_status qmm_matmul_f16act(int type, const void *w, int64_t rows, int64_t k, c
 
 size_t qmm_matmul_workspace(int type, int64_t rows, int64_t k, int64_t n) {
     if (check_common(type, rows, k, n)) return 0;
-    return dense_layout(type, rows, k, n, true).total;
+    return dense_layout(type, rows, k, n, true, load_ovr()).total;
 }
 
 size_t qmm_matmul_q8_1_workspace(int type, int64_t rows, int64_t k, int64_t n) {
     if (check_common(type, rows, k, n)) return 0;
-    return dense_layout(type, rows, k, n, false).total;
+    return dense_layout(type, rows, k, n, false, load_ovr()).total;
 }
 
 qmm_status qmm_matmul(int type, const void *w, int64_t rows, int64_t k, const float *x, int64_t n, float *y,
                       void *ws, size_t ws_bytes, void *stream) {
-    qmm_status st = check_common(type, rows, k, n);
+    const qmm::Ovr o = load_ovr();
+    qmm_status st = check_plan_args(type, rows, k, n, o);
     if (st) return st;
     if ((st = check_ptrs_dense(w, x, y, n))) return st;
     if (n == 0) return QMM_OK;
     if (((uintptr_t)x) & 15) return fail(QMM_ERR_ARG, "x must be 16-byte aligned");
-    const DenseWs L = dense_layout(type, rows, k, n, true);
+    const DenseWs L = dense_layout(type, rows, k, n, true, o);
     if (L.total > 0 && (!ws || ws_bytes < L.total))
         return fail(QMM_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", ws_bytes, L.total);
     if (((uintptr_t)ws) & 255) return fail(QMM_ERR_ARG, "workspace must be 256-byte aligned");
-    hipStream_t s = (hipStream_t)stream;
-    uint8_t *wsb = (uint8_t *)ws;
-    qmm_plan p{};
-    if ((st = qmm_plan_dense(type, rows, k, n, device_cus(), &p))) return st;
-    if (p.regime == 1 && qmm::mmvq_fused_applies(type, w, k, x, n)) {
-        // few columns: the dot4 or LDS-staged kernel quantizes the activations itself (the same
-        // q8_1 bytes as the quantize kernel below), one launch instead of two
-        hipError_t e = qmm::launch_mmvq_fused(type, (const uint8_t *)w, rows, k, x, n, y, s);
-        if (e != hipSuccess) return hip_fail(e, "fused matrix-vector kernel launch");
-        return QMM_OK;
-    }
-    if (p.regime == 2) {
-        // tiled path: quantize straight into the tiled kernel's layout
-        hipError_t e = qmm::launch_quantize_q8_1_tiled(x, n, k, wsb + L.tiled_off, nullptr, s);
-        if (e != hipSuccess) return hip_fail(e, "quantize launch");
-        return run_dense(type, w, rows, k, wsb + L.tiled_off, n, y, wsb, L, nullptr, 0, s, true);
-    }
-    hipError_t e = qmm::launch_quantize_q8_1(x, n, k, wsb + L.xq_off, s);
-    if (e != hipSuccess) return hip_fail(e, "quantize launch");
-    return run_dense(type, w, rows, k, wsb + L.xq_off, n, y, wsb, L, nullptr, 0, s);
+    return dense_f32(type, w, rows, k, x, n, y, (uint8_t *)ws, L, o, (hipStream_t)stream);
 }
 
 qmm_status qmm_matvec_kernel(int type, const void *w, int64_t k, const void *x, int64_t n, int32_t x_fp32,
                              int32_t *out) {
+    const qmm::Ovr o = load_ovr();
     qmm_status st = check_common(type, 1, k, n);
     if (st) return st;
     if (!out) return fail(QMM_ERR_ARG, "null out");
-    const int path = g_ovr_path.load();
-    if (n < 1 || n > 8 || k > kMvMaxK || path == 2) {
+    if (n < 1 || n > 8 || k > kMvMaxK || o.path == 2) {
         *out = 0;
         return QMM_OK;
     }
     if (x_fp32) {
         if (((uintptr_t)x) & 15) return fail(QMM_ERR_ARG, "x must be 16-byte aligned");
-        const int f = qmm::mmvq_fused_choice(type, w, k, (const float *)x, n);
+        const int f = qmm::mmvq_fused_choice(type, w, k, (const float *)x, n, o);
         if (f) {
             *out = f + 16;
             return QMM_OK;
         }
         x = (const void *)(uintptr_t)256;   // the q8_1 copy sits at the 256-byte aligned workspace start
     }
-    *out = qmm::mmvq_kernel_choice(type, w, k, x, n, nullptr);
+    *out = qmm::mmvq_kernel_choice(type, w, k, x, n, nullptr, o);
     return QMM_OK;
 }
 
 qmm_status qmm_matmul_q8_1(int type, const void *w, int64_t rows, int64_t k, const void *xq, int64_t n, float *y,
                            void *ws, size_t ws_bytes, void *stream) {
-    qmm_status st = check_common(type, rows, k, n);
+    const qmm::Ovr o = load_ovr();
+    qmm_status st = check_plan_args(type, rows, k, n, o);
     if (st) return st;
     if ((st = check_ptrs_dense(w, xq, y, n))) return st;
     if (n == 0) return QMM_OK;
     if (((uintptr_t)xq) & 3) return fail(QMM_ERR_ARG, "xq must be 4-byte aligned");
-    const DenseWs L = dense_layout(type, rows, k, n, false);
+    const DenseWs L = dense_layout(type, rows, k, n, false, o);
     if (L.total > 0 && (!ws || ws_bytes < L.total))
         return fail(QMM_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", ws_bytes, L.total);
     if (((uintptr_t)ws) & 255) return fail(QMM_ERR_ARG, "workspace must be 256-byte aligned");
-    return run_dense(type, w, rows, k, (const uint8_t *)xq, n, y, (uint8_t *)ws, L, nullptr, 0, (hipStream_t)stream);
+    return run_dense(type, w, rows, k, (const uint8_t *)xq, n, y, (uint8_t *)ws, L, nullptr, o, (hipStream_t)stream);
 }
 
 // ----------------------------------------------------------------------------------------------
@@ -448,21 +481,23 @@ qmm_status qmm_matmul_q8_1(int type, const void *w, int64_t rows, int64_t k, con
 // ----------------------------------------------------------------------------------------------
 namespace {
 
-bool glu_matvec(int64_t n, int64_t k) { return n <= 8 && k <= kMvMaxK && g_ovr_path.load() != 2; }
+bool glu_matvec(int64_t n, int64_t k, const qmm::Ovr &o) { return n <= 8 && k <= kMvMaxK && o.path != 2; }
 
-size_t glu_ws(int64_t k, int64_t n) {
-    return glu_matvec(n, k) ? align_up((size_t)(n * (k / 32) * 36), 256) : align_up(qmm::q8_1_tiled_bytes(n, k), 256);
+size_t glu_ws(int64_t k, int64_t n, const qmm::Ovr &o) {
+    return glu_matvec(n, k, o) ? align_up((size_t)(n * (k / 32) * 36), 256)
+                               : align_up(qmm::q8_1_tiled_bytes(n, k), 256);
 }
 
 }  // namespace
 
 size_t qmm_matmul_glu_workspace(int type, int64_t rows, int64_t k, int64_t n) {
     if (check_common(type, rows, k, n)) return 0;
-    return glu_ws(k, n);
+    return glu_ws(k, n, load_ovr());
 }
 
 qmm_status qmm_matmul_glu(int type, const void *w_gate, const void *w_up, int64_t rows, int64_t k, const float *x,
                           int64_t n, float *y, void *ws, size_t ws_bytes, void *stream) {
+    const qmm::Ovr o = load_ovr();
     qmm_status st = check_common(type, rows, k, n);
     if (st) return st;
     if ((st = check_ptrs_dense(w_gate, x, y, n))) return st;
@@ -470,7 +505,7 @@ qmm_status qmm_matmul_glu(int type, const void *w_gate, const void *w_up, int64_
     if (!w_up) return fail(QMM_ERR_ARG, "null w_up");
     if (((uintptr_t)w_up) & 1) return fail(QMM_ERR_ARG, "w must be 2-byte aligned");
     if (((uintptr_t)x) & 15) return fail(QMM_ERR_ARG, "x must be 16-byte aligned");
-    const size_t need = glu_ws(k, n);
+    const size_t need = glu_ws(k, n, o);
     if (!ws || ws_bytes < need)
         return fail(QMM_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", ws_bytes, need);
     if (((uintptr_t)ws) & 255) return fail(QMM_ERR_ARG, "workspace must be 256-byte aligned");
@@ -478,9 +513,9 @@ qmm_status qmm_matmul_glu(int type, const void *w_gate, const void *w_up, int64_
     uint8_t *wsb = (uint8_t *)ws;
     const uint8_t *wg = (const uint8_t *)w_gate, *wu = (const uint8_t *)w_up;
     hipError_t e;
-    if (glu_matvec(n, k)) {
+    if (glu_matvec(n, k, o)) {
         // the dot4 or LDS-staged kernel quantizing x itself (one launch), as for one matrix
-        const int kc = qmm::mmvq_glu_f32_choice(type, wg, wu, k, x, n);
+        const int kc = qmm::mmvq_glu_f32_choice(type, wg, wu, k, x, n, o);
         if (kc == 3 || kc == 2) {
             e = kc == 3 ? qmm::launch_mmvq_dot4_glu_f32(type, wg, wu, rows, k, x, n, y, s)
                         : qmm::launch_mmvq_stream_glu(type, wg, wu, rows, k, x, true, n, y, nullptr, 0, s);
@@ -489,28 +524,45 @@ qmm_status qmm_matmul_glu(int type, const void *w_gate, const void *w_up, int64_
         }
         e = qmm::launch_quantize_q8_1(x, n, k, wsb, s);
         if (e != hipSuccess) return hip_fail(e, "quantize launch");
-        e = qmm::launch_mmvq_glu(type, wg, wu, rows, k, wsb, n, y, nullptr, 0, s);
+        e = qmm::launch_mmvq_glu(type, wg, wu, rows, k, wsb, n, y, nullptr, 0, o, s);
         if (e != hipSuccess) return hip_fail(e, "fused matrix-vector kernel launch");
         return QMM_OK;
     }
     e = qmm::launch_quantize_q8_1_tiled(x, n, k, wsb, nullptr, s);
     if (e != hipSuccess) return hip_fail(e, "quantize launch");
-    const int tile_j = g_ovr_tile_j.load() ? g_ovr_tile_j.load() : qmm_select_tile_j(n);
+    const int tile_j = o.tile_j ? o.tile_j : qmm_select_tile_j(n);
     e = qmm::launch_mmq_glu(type, wg, wu, rows, k, wsb, n, y, tile_j, s);
     if (e != hipSuccess) return hip_fail(e, "fused tiled kernel launch");
     return QMM_OK;
 }
 
+size_t qmm_debug_subdots_workspace(int type, int64_t rows, int64_t k, int64_t n, int path) {
+    if (check_common(type, rows, k, n) || (path != 1 && path != 2)) return 0;
+    qmm::Ovr o = load_ovr();
+    o.path = path;
+    return dense_layout(type, rows, k, n, false, o).total;
+}
+
 qmm_status qmm_debug_subdots(int type, const void *w, int64_t rows, int64_t k, const void *xq, int64_t n, int path,
-                             int32_t *d_out, void *stream) {
+                             int32_t *d_out, void *ws, size_t ws_bytes, void *stream) {
     qmm_status st = check_common(type, rows, k, n);
     if (st) return st;
     if (path != 1 && path != 2) return fail(QMM_ERR_ARG, "path must be 1 (matrix-vector) or 2 (tiled)");
     if (path == 1 && (n > 8 || k > kMvMaxK)) return fail(QMM_ERR_ARG, "matrix-vector debug export needs n <= 8");
     if (n == 0) return QMM_OK;
     if (!w || !xq || !d_out) return fail(QMM_ERR_ARG, "null pointer");
-    DenseWs L{};
-    return run_dense(type, w, rows, k, (const uint8_t *)xq, n, nullptr, nullptr, L, d_out, path, (hipStream_t)stream);
+    if ((((uintptr_t)w) & 1) || (((uintptr_t)xq) & 3) || (((uintptr_t)d_out) & 3))
+        return fail(QMM_ERR_ARG, "w must be 2-byte, xq and d_out 4-byte aligned");
+    // the plan a production call of this shape would take under the current overrides, with
+    // the path forced
+    qmm::Ovr o = load_ovr();
+    o.path = path;
+    const DenseWs L = dense_layout(type, rows, k, n, false, o);
+    if (L.total > 0 && (!ws || ws_bytes < L.total))
+        return fail(QMM_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", ws_bytes, L.total);
+    if (((uintptr_t)ws) & 255) return fail(QMM_ERR_ARG, "workspace must be 256-byte aligned");
+    return run_dense(type, w, rows, k, (const uint8_t *)xq, n, nullptr, (uint8_t *)ws, L, d_out, o,
+                     (hipStream_t)stream);
 }
 
 // ----------------------------------------------------------------------------------------------
@@ -539,9 +591,8 @@ IdWs id_layout(int64_t n_exp, int64_t k, int64_t n_tok, int64_t top_k, int64_t x
     return L;
 }
 
-int id_tile_j(int type, int64_t pairs, int64_t n_exp) {
-    const int ov = g_ovr_tile_j.load();
-    if (ov) return ov;
+int id_tile_j(int type, int64_t pairs, int64_t n_exp, const qmm::Ovr &o) {
+    if (o.tile_j) return o.tile_j;
     // The MMQ page's "MoE skew": per-expert column counts are skewed, so the tile width follows
     // the columns of a typical expert, not the call's total: the mean for a few experts, half the
     // mean for many (a handful of hot experts then hold most columns; on the Zipf MoE shapes the
@@ -570,6 +621,7 @@ namespace {
 qmm_status run_id(int type, const void *w, const void *w_up, int64_t n_exp, int64_t rows, int64_t k, const float *x,
                   int64_t x_per_tok, const int32_t *ids, int64_t n_tok, int64_t top_k, float *y, void *ws,
                   size_t ws_bytes, void *stream) {
+    const qmm::Ovr o = load_ovr();
     qmm_status st = check_common(type, rows, k, n_tok);
     if (st) return st;
     if (n_exp <= 0 || n_exp > 32768) return fail(QMM_ERR_ARG, "n_exp must be in [1, 32768]");
@@ -597,7 +649,7 @@ qmm_status run_id(int type, const void *w, const void *w_up, int64_t n_exp, int6
     uint8_t *xq = wsb + L.xq_off, *xt = wsb + L.tiled_off;
     hipError_t e = qmm::launch_quantize_q8_1_tiled(x, nx, k, xt, xq, s);   // both layouts, one launch
     if (e != hipSuccess) return hip_fail(e, "quantize launch");
-    const int tile_j = id_tile_j(type, pairs, n_exp);
+    const int tile_j = id_tile_j(type, pairs, n_exp, o);
     qmm::ColMap cm{};
     cm.sorted = (const int32_t *)(wsb + L.sorted_off);
     cm.bounds = (const int32_t *)(wsb + L.bounds_off);
@@ -614,8 +666,8 @@ qmm_status run_id(int type, const void *w, const void *w_up, int64_t n_exp, int6
     if (e != hipSuccess) return hip_fail(e, "grouping launch");
     // experts with <= 8 columns: matrix-vector kernel, one workgroup row per listed expert
     if (k <= kMvMaxK) {
-        e = w_up ? qmm::launch_mmvq_glu(type, (const uint8_t *)w, (const uint8_t *)w_up, rows, k, xq, 0, y, &cm, n_exp, s)
-                 : qmm::launch_mmvq(type, (const uint8_t *)w, rows, k, xq, 0, y, nullptr, &cm, n_exp, s);
+        e = w_up ? qmm::launch_mmvq_glu(type, (const uint8_t *)w, (const uint8_t *)w_up, rows, k, xq, 0, y, &cm, n_exp, o, s)
+                 : qmm::launch_mmvq(type, (const uint8_t *)w, rows, k, xq, 0, y, nullptr, &cm, n_exp, o, s);
         if (e != hipSuccess) return hip_fail(e, "expert matrix-vector launch");
     }
     // the rest: tiled kernel over the device-built column-tile list
@@ -655,7 +707,7 @@ qmm_status qmm_matmul_id_grouping_layout(int type, int64_t n_exp, int64_t k, int
     out[1] = (int64_t)L.bounds_off;
     out[2] = (int64_t)L.tstart_off;
     out[3] = (int64_t)L.small_off;
-    out[4] = id_tile_j(type, n_tok * top_k, n_exp);
+    out[4] = id_tile_j(type, n_tok * top_k, n_exp, load_ovr());
     out[5] = k <= kMvMaxK ? kSmallMax : 0;
     return QMM_OK;
 }

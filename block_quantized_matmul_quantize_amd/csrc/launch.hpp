@@ -5,6 +5,17 @@
 
 namespace qmm {
 
+// Plan overrides (qmm_set_override), read once at the start of a call so that every decision of
+// that call (workspace layout, regime, kernels) sees the same values; 0 = automatic throughout.
+struct Ovr {
+    int path = 0;        // 1 matrix-vector, 2 tiled
+    int streamk = 0;     // 1 off, 2 on
+    int tile_j = 0;      // 32, 64, 128
+    int mv_steps = 0;    // register-streamed matrix-vector kernel: 256-value steps per wave (1, 2, 4)
+    int mv_kernel = 0;   // 1 register-streamed, 2 LDS-staged, 3 dot4
+    int fuse_cols = 0;   // most columns the LDS-staged kernel quantizes itself (1..8)
+};
+
 hipError_t launch_quantize_q8_1(const float *x, int64_t n_rows, int64_t k, uint8_t *y, hipStream_t s);
 
 // Tiled-kernel activation layout: for each 256-value step kb and activation row r, the 8 blocks'
@@ -36,14 +47,14 @@ struct ColMap {
 
 // Matrix-vector kernel: n <= 8 columns (dense) or the small experts (expert mode, grid.y = n_exp).
 hipError_t launch_mmvq(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n,
-                       float *y, int32_t *dbg, const ColMap *cm, int64_t n_exp, hipStream_t s);
+                       float *y, int32_t *dbg, const ColMap *cm, int64_t n_exp, const Ovr &o, hipStream_t s);
 
 // Gate/up fusion, matrix-vector: y = silu(W_gate x) * (W_up x) for n <= 8 dense q8_1 columns (cm
 // null) or the small experts (cm set, grid.y = n_exp); the LDS-staged kernel where both matrices
 // meet its rules, else the register-streamed one.
-int mmvq_glu_f32_choice(int type, const void *wg, const void *wu, int64_t k, const float *x, int64_t n);
+int mmvq_glu_f32_choice(int type, const void *wg, const void *wu, int64_t k, const float *x, int64_t n, const Ovr &o);
 hipError_t launch_mmvq_glu(int type, const uint8_t *wg, const uint8_t *wu, int64_t rows, int64_t k, const uint8_t *xq,
-                           int64_t n, float *y, const ColMap *cm, int64_t n_exp, hipStream_t s);
+                           int64_t n, float *y, const ColMap *cm, int64_t n_exp, const Ovr &o, hipStream_t s);
 
 // The same on the dot4 kernel for 1..3 dense fp32 columns (quantized inside); Q4_K and Q8_0 under
 // mmvq_dot4_supported's alignment rules for both matrices.
@@ -58,27 +69,19 @@ hipError_t launch_mmvq_stream_glu(int type, const uint8_t *wg, const uint8_t *wu
 
 // fp32-input matrix-vector product with the q8_1 quantization done inside the dot4 or the
 // LDS-staged kernel (no separate quantize launch): dense calls either kernel would take.
-bool mmvq_fused_applies(int type, const void *w, int64_t k, const float *x, int64_t n);
 // Kernel launch_mmvq takes for q8_1 input: 3 dot4, 2 LDS-staged MFMA, 1 register-streamed, 0 none
 // (a forced kernel that cannot serve the call); host logic only.
-int mmvq_kernel_choice(int type, const void *w, int64_t k, const void *xq, int64_t n, const ColMap *cm);
+int mmvq_kernel_choice(int type, const void *w, int64_t k, const void *xq, int64_t n, const ColMap *cm, const Ovr &o);
 // Kernel launch_mmvq_fused takes for fp32 input: 3 dot4, 2 LDS-staged MFMA, 0 not fused.
-int mmvq_fused_choice(int type, const void *w, int64_t k, const float *x, int64_t n);
-// Tuning: most columns the LDS-staged kernel quantizes itself (0 = automatic).
-void set_mmvq_fuse_cols(int cols);
-hipError_t launch_mmvq_fused(int type, const uint8_t *w, int64_t rows, int64_t k, const float *x, int64_t n, float *y,
-                             hipStream_t s);
+int mmvq_fused_choice(int type, const void *w, int64_t k, const float *x, int64_t n, const Ovr &o);
+// Launches the kernel mmvq_fused_choice names (`choice`, non-zero).
+hipError_t launch_mmvq_fused(int choice, int type, const uint8_t *w, int64_t rows, int64_t k, const float *x, int64_t n,
+                             float *y, hipStream_t s);
 hipError_t launch_mmvq_dot4_f32(int type, const uint8_t *w, int64_t rows, int64_t k, const float *x, int64_t n,
                                 float *y, hipStream_t s);
 hipError_t launch_mmvq_stream_f32(int type, const uint8_t *w, int64_t rows, int64_t k, const float *x, int64_t n,
                                   float *y, hipStream_t s);
 
-// Tuning: 256-value steps per wave of the register-streamed matrix-vector kernel (0 = automatic).
-void set_mmvq_steps_per_wave(int spw);
-// Matrix-vector kernel choice: 0 automatic (dot4 for few columns, else LDS-staged MFMA, where
-// supported), 1 register-streamed, 2 LDS-staged MFMA only, 3 dot4 only (launch_mmvq fails where
-// the forced kernel is unsupported).
-void set_mmvq_kernel(int which);
 // LDS-streamed matrix-vector kernel (mmvq_stream.hip): 16-byte aligned weights, activations and
 // rows, K a multiple of 256.
 bool mmvq_stream_supported(int type, const void *w, int64_t k, const void *xq, const ColMap *cm);

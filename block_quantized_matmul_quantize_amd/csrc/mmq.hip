@@ -100,14 +100,14 @@ template <int T, int J> constexpr bool kDoubleBuffer = kK45<T> && J == 128;
 template <int T, int J> constexpr int kSmemBytes = (kDoubleBuffer<T, J> ? 2 : 1) * Smem<T, J>::BYTES;
 
 // ---------------------------------------------------------------------------------------------
-// Activation tile: J columns of the step's 8 q8_1 blocks.  Thread tid owns (column, block) pairs
-// i = tid + NT*it: column i/8, block i%8.  TILED: the tiled layout (launch.hpp), where the 8
-// consecutive threads of a column read its 256 code bytes and 8 (d, s) pairs with aligned loads;
-// otherwise canonical 36-byte blocks (the debug export reads those).  acol always names a valid
-// activation row (tile columns past the end repeat a valid one and are never written out), so the
-// loads need no predicate; RAGGED (Q8_0, K a multiple of 32 only): blocks past K read as zero.
+// Activation tile: J columns of the step's 8 q8_1 blocks, read from the tiled layout (launch.hpp).
+// Thread tid owns (column, block) pairs i = tid + NT*it: column i/8, block i%8; the 8 consecutive
+// threads of a column read its 256 code bytes and 8 (d, s) pairs with aligned loads.  acol always
+// names a valid activation row (tile columns past the end repeat a valid one and are never written
+// out), so the loads need no predicate; RAGGED (Q8_0 / Q4_0, K a multiple of 32 only): blocks past
+// K read as zero.
 // ---------------------------------------------------------------------------------------------
-template <int J, bool TILED, bool RAGGED> struct ActFetch {
+template <int J, bool RAGGED> struct ActFetch {
     static constexpr int NT = Cfg<J>::NT, N = J * 8 / NT;
     uint32_t ds[N];   // fp16 d | fp16 s << 16
     u32x4 c0[N], c1[N];
@@ -124,18 +124,11 @@ template <int J, bool TILED, bool RAGGED> struct ActFetch {
                 c1[it] = c0[it];
             }
             if (!RAGGED || b < nb32) {
-                if constexpr (TILED) {
-                    const int64_t slot = kb * act_rows + acol[it];
-                    const uint8_t *src = xq + slot * 256 + 32 * blk;
-                    c0[it] = *(const u32x4 *)src;
-                    c1[it] = *(const u32x4 *)(src + 16);
-                    ds[it] = ((const uint32_t *)(xq + ((nb32 + 7) / 8) * act_rows * 256))[slot * 8 + blk];
-                } else {
-                    const uint8_t *src = xq + (acol[it] * nb32 + b) * kQ8_1Bytes;
-                    ds[it] = *(const uint32_t *)src;
-                    c0[it] = ld16(src + 4);
-                    c1[it] = ld16(src + 20);
-                }
+                const int64_t slot = kb * act_rows + acol[it];
+                const uint8_t *src = xq + slot * 256 + 32 * blk;
+                c0[it] = *(const u32x4 *)src;
+                c1[it] = *(const u32x4 *)(src + 16);
+                ds[it] = ((const uint32_t *)(xq + ((nb32 + 7) / 8) * act_rows * 256))[slot * 8 + blk];
             }
         }
     }
@@ -468,10 +461,14 @@ template <int NT> struct WFetch<kQ6_K, NT> : std::conditional<(NT >= 512), WFetc
 // Q4_K tile time).  The tile loop builds the seed once and makes it opaque, so that it stays in
 // registers instead of being rebuilt every step.  Q8_0 would qualify too but its tiles run out of
 // registers with the 16 seed registers; Q6_K's scale-folded dots can exceed the range.
-template <int T, bool DBG> constexpr bool kSeeded = !DBG && kK45<T>;   // Q5_K: |D| <= 32*31*127 too
+template <int T> constexpr bool kSeeded = kK45<T>;   // Q5_K: |D| <= 32*31*127 too
 constexpr int32_t kBiasBits = 0x4B400000;
 constexpr float kBias = 12582912.0f;   // 1.5 * 2^23
 
+// DBG (the integer-dot export) runs the same loads, LDS layout, MFMAs and seeded accumulators; it
+// differs only where an integer dot would be folded into the fp32 accumulators: there it stores
+// the exact integer the production fold consumes (the seeded value minus the seed for Q4_K /
+// Q5_K, the scale-folded 128*D_hi + D_lo for Q6_K, D for Q8_0 / Q4_0).
 template <int T, int J, bool DBG>
 __device__ __forceinline__ void tile_step(const uint8_t *sm, f32x16 (&acc)[Cfg<J>::NCB], const i32x16 &cinit,
                                           int64_t kb, int64_t nb32, int32_t *dbg, int64_t rows, int64_t n, int64_t r0,
@@ -488,6 +485,13 @@ __device__ __forceinline__ void tile_step(const uint8_t *sm, f32x16 (&acc)[Cfg<J
     const int colw = JW * cw + (lane & 31);   // + 32*cb
     const i32x16 zero = {};
     const f32x16 fzero = {};
+
+    // Debug export of the integer dot v of element e of column block cb, sub-block sb.
+    auto export_dot = [&](int cb, int sb, int e, int32_t v) {
+        const int64_t col = c0 + colw + 32 * cb;
+        const int64_t row = r0 + 32 * rw + 4 * h + 8 * (e >> 2) + (e & 3);
+        if (row < rows && col < n) dbg[(col * rows + row) * nb32 + kb * 8 + sb] = v;
+    };
 
     // Per-element scales of sub-block sb: the outer product of this wave's 32 row scales and its
     // columns' d_a.  Two 32-column blocks come from one two-block v_mfma_f32_32x32x1_f32 (block b
@@ -507,24 +511,22 @@ __device__ __forceinline__ void tile_step(const uint8_t *sm, f32x16 (&acc)[Cfg<J
             S[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(h ? 0.f : wsr, da, fzero, 0, 0, 0);
         }
     };
-    // D of block (sb, cb) folded into the accumulators with its scales (or exported raw)
-    constexpr bool BIAS = kSeeded<T, DBG>;
+    // D of block (sb, cb) folded into the accumulators with its scales (or exported)
     auto fix = [&](int cb, int sb, const i32x16 &D, const f32x16 &S) {
-        const int bcol = colw + 32 * cb;
-        if (DBG) {
-            const int64_t col = c0 + bcol;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int64_t row = r0 + 32 * rw + 4 * h + 8 * (e >> 2) + (e & 3);
-                if (row < rows && col < n) dbg[(col * rows + row) * nb32 + kb * 8 + sb] = D[e];
-            }
-        } else if constexpr (BIAS) {
+        if constexpr (kSeeded<T>) {
             const f32x16 Df = __builtin_bit_cast(f32x16, D);
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[cb][e] = fmaf(Df[e] - kBias, S[e], acc[cb][e]);
+            for (int e = 0; e < 16; ++e) {
+                const float dv = Df[e] - kBias;   // exact: |D| < 2^22
+                if constexpr (DBG) export_dot(cb, sb, e, (int32_t)dv);
+                else acc[cb][e] = fmaf(dv, S[e], acc[cb][e]);
+            }
         } else {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[cb][e] = fmaf((float)D[e], S[e], acc[cb][e]);
+            for (int e = 0; e < 16; ++e) {
+                if constexpr (DBG) export_dot(cb, sb, e, D[e]);
+                else acc[cb][e] = fmaf((float)D[e], S[e], acc[cb][e]);
+            }
         }
     };
 
@@ -549,7 +551,7 @@ __device__ __forceinline__ void tile_step(const uint8_t *sm, f32x16 (&acc)[Cfg<J
                 aop.w |= ((qh.w >> sb) & 0x01010101u) << 4;
             }
             f32x16 S[NCB];
-            if (!DBG) scales(sb, sWs[sb * kTI + arow], S);
+            if constexpr (!DBG) scales(sb, sWs[sb * kTI + arow], S);
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
                 const u32x4 b = *(const u32x4 *)(sA + (colw + 32 * cb) * kLd + 32 * sb + koff);
@@ -563,27 +565,11 @@ __device__ __forceinline__ void tile_step(const uint8_t *sm, f32x16 (&acc)[Cfg<J
             if (kb * 8 + j >= nb32) break;   // ragged last step (workgroup-uniform)
             const u32x4 a = *(const u32x4 *)(sW + arow * kLd + 32 * j + koff);
             f32x16 S[NCB];
-            if (!DBG) scales(j, sWs[j * kTI + arow], S);
+            if constexpr (!DBG) scales(j, sWs[j * kTI + arow], S);
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
                 const u32x4 b = *(const u32x4 *)(sA + (colw + 32 * cb) * kLd + 32 * j + koff);
                 fix(cb, j, mfma32x32x32(a, b, cinit), S[cb]);
-            }
-        }
-    } else if constexpr (DBG) {
-        const int8_t *sW = (const int8_t *)(sm + L::W_OFF);
-#pragma unroll 1
-        for (int j = 0; j < 8; ++j) {
-            const u32x4 a = *(const u32x4 *)(sW + arow * kLd + 32 * j + koff);
-            const u32x4 a_hi = *(const u32x4 *)(sW + kTI * kLd + arow * kLd + 32 * j + koff);
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) {
-                const u32x4 b = *(const u32x4 *)(sA + (colw + 32 * cb) * kLd + 32 * j + koff);
-                i32x16 D = mfma32x32x32(a, b, zero);
-                const i32x16 Dh = mfma32x32x32(a_hi, b, zero);
-#pragma unroll
-                for (int e = 0; e < 16; ++e) D[e] = (Dh[e] << 7) + D[e];
-                fix(cb, j, D, f32x16{});
             }
         }
     } else {
@@ -606,17 +592,23 @@ __device__ __forceinline__ void tile_step(const uint8_t *sm, f32x16 (&acc)[Cfg<J
                 const i32x16 D = mfma32x32x32(a, b, zero);
                 const i32x16 Dh = mfma32x32x32(a_hi, b, zero);
 #pragma unroll
-                for (int e = 0; e < 16; ++e) Tc[cb][e] = fmaf((float)((Dh[e] << 7) + D[e]), da, Tc[cb][e]);
+                for (int e = 0; e < 16; ++e) {
+                    const int32_t v = (Dh[e] << 7) + D[e];   // sc0*D0 + sc1*D1
+                    if constexpr (DBG) export_dot(cb, j, e, v);
+                    else Tc[cb][e] = fmaf((float)v, da, Tc[cb][e]);
+                }
             }
         }
-        // row scales of the lane's elements: rows 32*rw + 8*q + 4*h + (0..3), q = e/4
+        if constexpr (!DBG) {
+            // row scales of the lane's elements: rows 32*rw + 8*q + 4*h + (0..3), q = e/4
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const f32x4 dr = *(const f32x4 *)(sWs + 32 * rw + 8 * q + 4 * h);
+            for (int q = 0; q < 4; ++q) {
+                const f32x4 dr = *(const f32x4 *)(sWs + 32 * rw + 8 * q + 4 * h);
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb)
+                for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) acc[cb][4 * q + i] = fmaf(dr[i], Tc[cb][4 * q + i], acc[cb][4 * q + i]);
+                    for (int i = 0; i < 4; ++i) acc[cb][4 * q + i] = fmaf(dr[i], Tc[cb][4 * q + i], acc[cb][4 * q + i]);
+            }
         }
     }
 }
@@ -657,13 +649,13 @@ __device__ __forceinline__ void run_tile(uint8_t *sm, f32x16 (&acc)[Cfg<J>::NCB]
                                          int64_t c0, int64_t act_rows) {
     constexpr bool DB = kDoubleBuffer<T, J>;
     i32x16 cinit = {};
-    if constexpr (kSeeded<T, DBG>) {
+    if constexpr (kSeeded<T>) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) cinit[e] = kBiasBits;
         asm volatile("" : "+v"(cinit));
     }
     WFetch<T, Cfg<J>::NT> wf;
-    ActFetch<J, !DBG, kB32<T>> af;
+    ActFetch<J, kB32<T>> af;
     wf.fetch(wr, kb0, nb32);
     af.fetch(xq, nb32, kb0, acol, act_rows);
     uint8_t *const buf0 = sm, *const buf1 = sm + (DB ? Smem<T, J>::BYTES : 0);
@@ -707,7 +699,7 @@ __device__ __forceinline__ void run_tile(uint8_t *sm, f32x16 (&acc)[Cfg<J>::NCB]
     }
     for (int64_t kb = kb0; kb < kb1; ++kb) {
         const uint8_t *cur = enter(kb);
-        if constexpr (kK45<T> && !DBG) q4k_min_term<T, J>(cur, acc);
+        if constexpr (kK45<T> && !DBG) q4k_min_term<T, J>(cur, acc);   // acc only
         tile_step<T, J, DBG>(cur, acc, cinit, kb, nb32, dbg, wr.rows, n, wr.r0, c0);
     }
 }
@@ -995,12 +987,9 @@ static hipError_t launch_mmq_t(const uint8_t *w, int64_t rows, int64_t k, const 
     MmqArgs a{p.ntiles, p.n_ct, p.k_iters, p.units, p.partials, p.stream_k ? 1 : 0};
     constexpr int smem = kSmemBytes<T, J>;
     auto kern = mmq_kernel<T, J, DBG>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    // once per process (a function-local static is initialised exactly once, thread-safely)
+    static const hipError_t attr_err = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    if (attr_err != hipSuccess) return attr_err;
     hipLaunchKernelGGL(kern, dim3((unsigned)p.units), dim3(Cfg<J>::NT), smem, s, w, rows, k, xq, n, y, dbg, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || DBG || !p.stream_k) return e;
@@ -1037,12 +1026,9 @@ static hipError_t launch_mmq_glu_t(const uint8_t *wg, const uint8_t *wu, int64_t
                                    int64_t n, float *y, hipStream_t s) {
     constexpr int smem = kSmemBytes<T, J>;
     auto kern = mmq_glu_kernel<T, J>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    // once per process (a function-local static is initialised exactly once, thread-safely)
+    static const hipError_t attr_err = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    if (attr_err != hipSuccess) return attr_err;
     const int64_t n_ct = (n + J - 1) / J;
     const int64_t ntiles = ((rows + kTI / 2 - 1) / (kTI / 2)) * n_ct;
     hipLaunchKernelGGL(kern, dim3((unsigned)ntiles), dim3(Cfg<J>::NT), smem, s, wg, wu, rows, k, xq, n, y, ntiles, n_ct);
@@ -1071,12 +1057,9 @@ static hipError_t launch_mmq_id_t(const uint8_t *w, const uint8_t *w2, int64_t r
                                   float *y, const ColMap &cm, int32_t n_exp, int64_t max_ct, hipStream_t s) {
     constexpr int smem = kSmemBytes<T, J>;
     auto kern = mmq_id_kernel<T, J, GLU>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    // once per process (a function-local static is initialised exactly once, thread-safely)
+    static const hipError_t attr_err = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    if (attr_err != hipSuccess) return attr_err;
     if (max_ct <= 0) return hipSuccess;
     constexpr int64_t TR = GLU ? kTI / 2 : kTI;   // outputs per row tile
     dim3 grid((unsigned)((rows + TR - 1) / TR), (unsigned)max_ct);

@@ -472,8 +472,6 @@ __global__ __launch_bounds__(64 * mv_max_waves(SPW)) void mmvq_kernel(const uint
         }
 }
 
-static int g_mv_spw = 0;   // 0: automatic
-
 template <int T, int SPW, bool DBG, bool EXPERT, bool GLU = false>
 static hipError_t launch_mmvq_spw(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y,
                                   int32_t *dbg, const ColMap &c, int64_t n_exp, hipStream_t s,
@@ -485,13 +483,10 @@ static hipError_t launch_mmvq_spw(const uint8_t *w, int64_t rows, int64_t k, con
     constexpr int RW = GLU ? kMvRows / 2 : kMvRows;   // outputs per workgroup
     dim3 grid((unsigned)((rows + RW - 1) / RW), EXPERT ? (unsigned)n_exp : 1u);
     const size_t smem = (size_t)(k / 32) * 8 * sizeof(float2) + (size_t)nw * 128 * sizeof(float);
-    static bool attr = false;
-    if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void *)mmvq_kernel<T, SPW, DBG, EXPERT, GLU>,
+    // once per process (a function-local static is initialised exactly once, thread-safely)
+    static const hipError_t attr_err = hipFuncSetAttribute((const void *)mmvq_kernel<T, SPW, DBG, EXPERT, GLU>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        if (e != hipSuccess) return e;
-        attr = true;
-    }
+    if (attr_err != hipSuccess) return attr_err;
     hipLaunchKernelGGL((mmvq_kernel<T, SPW, DBG, EXPERT, GLU>), grid, dim3(64 * (unsigned)nw), smem, s, w, w2, rows, k,
                        xq, n, y, dbg, c);
     return hipGetLastError();
@@ -499,21 +494,13 @@ static hipError_t launch_mmvq_spw(const uint8_t *w, int64_t rows, int64_t k, con
 
 template <int T, bool DBG, bool EXPERT>
 static hipError_t launch_mmvq_t(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y,
-                                int32_t *dbg, const ColMap *cm, int64_t n_exp, hipStream_t s) {
+                                int32_t *dbg, const ColMap *cm, int64_t n_exp, int spw, hipStream_t s) {
     ColMap c = cm ? *cm : ColMap{};
-    int spw = g_mv_spw;
     if (spw == 0) spw = 2;
     if (spw == 1) return launch_mmvq_spw<T, 1, DBG, EXPERT>(w, rows, k, xq, n, y, dbg, c, n_exp, s);
     if (spw == 4) return launch_mmvq_spw<T, 4, DBG, EXPERT>(w, rows, k, xq, n, y, dbg, c, n_exp, s);
     return launch_mmvq_spw<T, 2, DBG, EXPERT>(w, rows, k, xq, n, y, dbg, c, n_exp, s);
 }
-
-void set_mmvq_steps_per_wave(int spw) { g_mv_spw = spw; }
-
-// 0: automatic, 1: this file's register-streamed kernel, 2: LDS-staged MFMA kernel, 3: dot4 kernel
-static int g_mv_kernel = 0;
-
-void set_mmvq_kernel(int which) { g_mv_kernel = which; }
 
 // Largest column count the automatic choice sends to the dot4 kernel, per type: measured at
 // 4096 x 4096 (fp32 input, graph-replayed calls), dot4 is ~0.1 us faster than the LDS-staged
@@ -522,13 +509,10 @@ static int dot4_auto_cols(int type) {
     return type == kQ4_K || type == kQ5_K || type == kQ8_0 || type == kQ4_0 ? 1 : 0;
 }
 
-static int g_fuse_cols = 0;   // 0: automatic (5)
-
-void set_mmvq_fuse_cols(int cols) { g_fuse_cols = cols; }
-
-// Which fused kernel serves an fp32-input call: 3 dot4, 2 LDS-staged MFMA, 0 none.
-static int fused_kernel(int type, const void *w, int64_t k, const float *x, int64_t n) {
-    const int kc = g_mv_kernel;
+// Which fused kernel serves an fp32-input call: 3 dot4, 2 LDS-staged MFMA, 0 none.  Override
+// o.mv_kernel: 0 automatic, 1 register-streamed (never fused), 2 LDS-staged only, 3 dot4 only.
+static int fused_kernel(int type, const void *w, int64_t k, const float *x, int64_t n, const Ovr &o) {
+    const int kc = o.mv_kernel;
     if (n < 1 || (uintptr_t)x % 16 != 0) return 0;
     if (kc == 0 || kc == 3) {
         const int lim = kc == 3 ? mmvq_dot4_max_cols() : dot4_auto_cols(type);
@@ -539,26 +523,22 @@ static int fused_kernel(int type, const void *w, int64_t k, const float *x, int6
     // quantizes all of x, so the cost grows with n while a separate quantize launch costs a
     // fixed ~2-3 us.  Measured at 4096 x 4096 (graph-replayed calls), fused is faster for every
     // n <= 8 and type: 1.9-2.4 us at n = 1, 0.3-0.7 us at n = 8.
-    const int lim = g_fuse_cols > 0 ? g_fuse_cols : 8;
+    const int lim = o.fuse_cols > 0 ? o.fuse_cols : 8;
     if ((kc == 0 || kc == 2) && n <= lim && mmvq_stream_supported(type, w, k, x, nullptr)) return 2;
     return 0;
 }
 
-bool mmvq_fused_applies(int type, const void *w, int64_t k, const float *x, int64_t n) {
-    return fused_kernel(type, w, k, x, n) != 0;
-}
-
-hipError_t launch_mmvq_fused(int type, const uint8_t *w, int64_t rows, int64_t k, const float *x, int64_t n, float *y,
-                             hipStream_t s) {
-    switch (fused_kernel(type, w, k, x, n)) {
+hipError_t launch_mmvq_fused(int choice, int type, const uint8_t *w, int64_t rows, int64_t k, const float *x, int64_t n,
+                             float *y, hipStream_t s) {
+    switch (choice) {
         case 3: return launch_mmvq_dot4_f32(type, w, rows, k, x, n, y, s);
         case 2: return launch_mmvq_stream_f32(type, w, rows, k, x, n, y, s);
         default: return hipErrorInvalidValue;
     }
 }
 
-int mmvq_kernel_choice(int type, const void *w, int64_t k, const void *xq, int64_t n, const ColMap *cm) {
-    const int kc = g_mv_kernel;
+int mmvq_kernel_choice(int type, const void *w, int64_t k, const void *xq, int64_t n, const ColMap *cm, const Ovr &o) {
+    const int kc = o.mv_kernel;
     if (kc == 3 || kc == 0) {
         const int lim = kc == 3 ? mmvq_dot4_max_cols() : dot4_auto_cols(type);
         if (!cm && n <= lim && mmvq_dot4_supported(type, w, k, xq, cm)) return 3;
@@ -569,13 +549,13 @@ int mmvq_kernel_choice(int type, const void *w, int64_t k, const void *xq, int64
     return 1;
 }
 
-int mmvq_fused_choice(int type, const void *w, int64_t k, const float *x, int64_t n) {
-    return fused_kernel(type, w, k, x, n);
+int mmvq_fused_choice(int type, const void *w, int64_t k, const float *x, int64_t n, const Ovr &o) {
+    return fused_kernel(type, w, k, x, n, o);
 }
 
 hipError_t launch_mmvq(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y,
-                       int32_t *dbg, const ColMap *cm, int64_t n_exp, hipStream_t s) {
-    switch (mmvq_kernel_choice(type, w, k, xq, n, cm)) {
+                       int32_t *dbg, const ColMap *cm, int64_t n_exp, const Ovr &o, hipStream_t s) {
+    switch (mmvq_kernel_choice(type, w, k, xq, n, cm, o)) {
         case 3: return launch_mmvq_dot4(type, w, rows, k, xq, n, y, dbg, cm, n_exp, (int)n, s);
         case 2: return launch_mmvq_stream(type, w, rows, k, xq, n, y, dbg, cm, n_exp, s);
         case 1: break;
@@ -585,9 +565,9 @@ hipError_t launch_mmvq(int type, const uint8_t *w, int64_t rows, int64_t k, cons
     const bool d = dbg != nullptr;
 #define QMM_MV(TT)                                                                                       \
     if (type == TT) {                                                                                  \
-        if (d) return launch_mmvq_t<TT, true, false>(w, rows, k, xq, n, y, dbg, cm, n_exp, s); \
-        if (expert) return launch_mmvq_t<TT, false, true>(w, rows, k, xq, n, y, dbg, cm, n_exp, s); \
-        return launch_mmvq_t<TT, false, false>(w, rows, k, xq, n, y, dbg, cm, n_exp, s);   \
+        if (d) return launch_mmvq_t<TT, true, false>(w, rows, k, xq, n, y, dbg, cm, n_exp, o.mv_steps, s); \
+        if (expert) return launch_mmvq_t<TT, false, true>(w, rows, k, xq, n, y, dbg, cm, n_exp, o.mv_steps, s); \
+        return launch_mmvq_t<TT, false, false>(w, rows, k, xq, n, y, dbg, cm, n_exp, o.mv_steps, s);   \
     }
     QMM_MV(kQ4_K)
     QMM_MV(kQ5_K)
@@ -606,8 +586,8 @@ namespace qmm {
 // matrices meet its alignment rules (and no override forces the register-streamed one), else the
 // register-streamed kernel.
 hipError_t launch_mmvq_glu(int type, const uint8_t *wg, const uint8_t *wu, int64_t rows, int64_t k, const uint8_t *xq,
-                           int64_t n, float *y, const ColMap *cm, int64_t n_exp, hipStream_t s) {
-    if (g_mv_kernel != 1 && g_mv_kernel != 3 && mmvq_stream_supported(type, wg, k, xq, cm) &&
+                           int64_t n, float *y, const ColMap *cm, int64_t n_exp, const Ovr &o, hipStream_t s) {
+    if (o.mv_kernel != 1 && o.mv_kernel != 3 && mmvq_stream_supported(type, wg, k, xq, cm) &&
         mmvq_stream_supported(type, wu, k, xq, cm))
         return launch_mmvq_stream_glu(type, wg, wu, rows, k, xq, false, n, y, cm, n_exp, s);
     const ColMap c = cm ? *cm : ColMap{};
@@ -628,8 +608,8 @@ hipError_t launch_mmvq_glu(int type, const uint8_t *wg, const uint8_t *wu, int64
 // Kernel for a dense fp32-input gate/up call of n <= 8 columns, as fused_kernel decides for one
 // matrix, with both matrices checked: 3 dot4, 2 LDS-staged (both quantize x themselves), 0 none
 // (quantize first, then launch_mmvq_glu).
-int mmvq_glu_f32_choice(int type, const void *wg, const void *wu, int64_t k, const float *x, int64_t n) {
-    const int a = fused_kernel(type, wg, k, x, n), b = fused_kernel(type, wu, k, x, n);
+int mmvq_glu_f32_choice(int type, const void *wg, const void *wu, int64_t k, const float *x, int64_t n, const Ovr &o) {
+    const int a = fused_kernel(type, wg, k, x, n, o), b = fused_kernel(type, wu, k, x, n, o);
     return a == b ? a : 0;
 }
 

@@ -331,13 +331,10 @@ hipError_t launch_nc(const uint8_t *w, int64_t rows, int64_t k, const void *xq, 
     a.r = (int32_t)(nsteps % nw);
     a.n = (int32_t)n;
     const size_t smem = (size_t)NC * a.nb * 40 + (size_t)nw * 16 * NC * sizeof(float);
-    static bool attr = false;
-    if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void *)mmvq_dot4_kernel<T, NC, DBG, EXPERT, F32, GLU>,
+    // once per process (a function-local static is initialised exactly once, thread-safely)
+    static const hipError_t attr_err = hipFuncSetAttribute((const void *)mmvq_dot4_kernel<T, NC, DBG, EXPERT, F32, GLU>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        if (e != hipSuccess) return e;
-        attr = true;
-    }
+    if (attr_err != hipSuccess) return attr_err;
     constexpr int RW = GLU ? kRows / 2 : kRows;   // outputs per workgroup
     dim3 grid((unsigned)((rows + RW - 1) / RW), EXPERT ? (unsigned)n_exp : 1u);
     hipLaunchKernelGGL((mmvq_dot4_kernel<T, NC, DBG, EXPERT, F32, GLU>), grid, dim3(64 * (unsigned)nw), smem, s, w, w2,

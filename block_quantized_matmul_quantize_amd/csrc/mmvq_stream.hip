@@ -569,13 +569,10 @@ hipError_t launch_t(const uint8_t *w, int64_t rows, int64_t k, const void *xq, i
     a.q = (int32_t)(nsteps / nw);
     a.r = (int32_t)(nsteps % nw);
     a.n = (int32_t)n;
-    static bool attr = false;
-    if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void *)mmvq_stream_kernel<T, DBG, EXPERT, F32, GLU>,
+    // once per process (a function-local static is initialised exactly once, thread-safely)
+    static const hipError_t attr_err = hipFuncSetAttribute((const void *)mmvq_stream_kernel<T, DBG, EXPERT, F32, GLU>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-        if (e != hipSuccess) return e;
-        attr = true;
-    }
+    if (attr_err != hipSuccess) return attr_err;
     constexpr int RW = GLU ? kRows / 2 : kRows;
     dim3 grid((unsigned)((rows + RW - 1) / RW), EXPERT ? (unsigned)n_exp : 1u);
     hipLaunchKernelGGL((mmvq_stream_kernel<T, DBG, EXPERT, F32, GLU>), grid, dim3(64 * (unsigned)nw), smem, s, w, w2, xq,

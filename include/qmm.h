@@ -172,16 +172,23 @@ qmm_status qmm_matmul_id_glu(int type, const void *w_gate, const void *w_up, int
                              float *y, void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
- * Test hook: the integer sub-block dots from the production kernels' own integer accumulators
- * ([MMQ] "write-back": the integer part is exact).  path: 1 = matrix-vector kernel,
- * 2 = tiled MFMA kernel.  d_out: int32 [n][rows][per] with
- *   per = k/32 for Q4_K and Q8_0 (D_b),
+ * Test hook: the integer sub-block dots from the production kernels ([MMQ] "write-back": the
+ * integer part is exact).  path: 1 = matrix-vector kernel, 2 = tiled MFMA kernel.  The call runs
+ * the plan a qmm_matmul_q8_1 of this shape takes under the current overrides, with the path
+ * forced: the same kernel, activation layout, LDS layout, MFMAs and accumulator seeding
+ * (stream-K split included on the tiled path), and only where a kernel folds an integer dot into
+ * its fp32 result does it store that integer to d_out instead (y is not written).
+ * d_out: int32 [n][rows][per] (device, 4-byte aligned) with
+ *   per = k/32 for Q4_K, Q5_K, Q8_0, Q4_0 (D_b),
  *   Q6_K path 1: per = k/16 (D per 16-value sub-block),
  *   Q6_K path 2: per = k/32, the scale-folded integer sc_{2b}*D_{2b} + sc_{2b+1}*D_{2b+1}.
- * Path 1 requires n <= 8.
+ * xq: n * k/32 q8_1 blocks (4-byte aligned).  Path 1 requires n <= 8.
+ * qmm_debug_subdots_workspace: bytes of device workspace (256-byte aligned) the call needs; 0
+ *   means none (ws may be NULL), also for invalid arguments.
  * ------------------------------------------------------------------------------------------- */
+size_t qmm_debug_subdots_workspace(int type, int64_t rows, int64_t k, int64_t n, int path);
 qmm_status qmm_debug_subdots(int type, const void *w, int64_t rows, int64_t k, const void *xq,
-                             int64_t n, int path, int32_t *d_out, void *stream);
+                             int64_t n, int path, int32_t *d_out, void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
  * Which matrix-vector kernel a dense call would launch ([MMQ] "shape criteria": n <= 8 takes the
@@ -197,7 +204,9 @@ qmm_status qmm_matvec_kernel(int type, const void *w, int64_t k, const void *x, 
                              int32_t *out);
 
 /* ---------------------------------------------------------------------------------------------
- * Plan overrides for tests and tuning (process-wide; 0 = automatic).
+ * Plan overrides for tests and tuning (process-wide; 0 = automatic).  Every other entry point
+ * reads the overrides once when it starts, so a concurrent change never splits one call's
+ * workspace layout from its plan; this is the only entry point that writes process-wide state.
  *   QMM_OVR_PATH:     1 force matrix-vector (only when n <= 8), 2 force tiled MFMA.
  *   QMM_OVR_STREAMK:  1 force off, 2 force on (tiled path).
  *   QMM_OVR_TILE_J:   tile width in columns (32, 64 or 128).
@@ -236,6 +245,8 @@ typedef struct {
     int64_t k_iters;         /* K steps per tile (one super-block of 256 values per step) */
     int64_t units;           /* stream-K work units launched (== ntiles without stream-K) */
     int32_t fixup;           /* 1 if a fixup pass is needed */
+    uint64_t ws_bytes;       /* workspace qmm_matmul needs under this plan (from the same reading
+                                of the overrides as the rest of the plan) */
 } qmm_plan;
 
 qmm_status qmm_plan_dense(int type, int64_t rows, int64_t k, int64_t n, int32_t nsm, qmm_plan *out);

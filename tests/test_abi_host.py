@@ -138,9 +138,12 @@ def test_argument_validation_without_gpu():
     # bad x_per_tok / top_k
     assert L.qmm_matmul_id(qmm.Q4_K, null, 4, 16, 256, null, 3, null, 8, 2, null, null, 0, null) == -1
     assert L.qmm_matmul_id(qmm.Q4_K, null, 4, 16, 256, null, 1, null, 8, 0, null, null, 0, null) == -1
-    # debug export: bad path
-    assert L.qmm_debug_subdots(qmm.Q4_K, null, 16, 256, null, 1, 3, null, null) == -1
-    assert L.qmm_debug_subdots(qmm.Q4_K, null, 16, 256, null, 9, 1, null, null) == -1
+    # debug export: bad path, too many columns for the matrix-vector kernel, workspace too small
+    one = ctypes.c_void_p(4096)   # a non-null address, never dereferenced: the calls fail first
+    assert L.qmm_debug_subdots(qmm.Q4_K, null, 16, 256, null, 1, 3, null, null, 0, null) == -1
+    assert L.qmm_debug_subdots(qmm.Q4_K, null, 16, 256, null, 9, 1, null, null, 0, null) == -1
+    assert qmm.debug_subdots_workspace(qmm.Q4_K, 16, 256, 9, qmm.PATH_TILED) > 0
+    assert L.qmm_debug_subdots(qmm.Q4_K, one, 16, 256, one, 9, 2, one, null, 0, null) == -4
 
 
 def test_glu_argument_validation_without_gpu():
@@ -257,4 +260,94 @@ def test_expert_tile_width_follows_typical_columns_per_expert(qtype, n_exp, n_to
     try:
         assert qmm.matmul_id_layout(qtype, n_exp, 2048, n_tok, top_k, 1)[4] == 32
     finally:
+        qmm.set_override(qmm.OVR_TILE_J, 0)
+
+
+def test_wrappers_refuse_undersized_tensors_without_gpu():
+    """The C ABI receives bare pointers, so the binding checks that every weight, activation and
+    output tensor holds the bytes its shape needs before any pointer reaches the library (CPU
+    tensors here: the size checks come before the device check, nothing is launched)."""
+    import torch
+    rows, k = 32, 512
+    wb = qmm.weight_bytes(qmm.Q4_K, rows, k)
+    assert wb == rows * 2 * 144
+    w_ok, w_small = torch.zeros(wb, dtype=torch.uint8), torch.zeros(wb - 1, dtype=torch.uint8)
+    x = torch.zeros((3, k), dtype=torch.float32)
+    with pytest.raises(ValueError, match="w holds"):
+        qmm.matmul(w_small, qmm.Q4_K, rows, k, x)
+    with pytest.raises(ValueError, match="out holds"):
+        qmm.matmul(w_ok, qmm.Q4_K, rows, k, x, out=torch.zeros((3, rows - 1), dtype=torch.float32))
+    with pytest.raises(ValueError, match="w holds"):
+        qmm.matmul_f16act(w_small, qmm.Q4_K, rows, k, x)
+    with pytest.raises(ValueError, match="w holds"):
+        qmm.matmul_q8_1(w_small, qmm.Q4_K, rows, k, torch.zeros(3 * 16 * 36, dtype=torch.uint8), 3)
+    with pytest.raises(ValueError, match="w_gate holds"):
+        qmm.matmul_glu(w_small, w_small, qmm.Q4_K, rows, k, x)
+    ids = torch.zeros((3, 2), dtype=torch.int32)
+    with pytest.raises(ValueError, match="w holds"):
+        qmm.matmul_id(torch.zeros(4 * wb - 1, dtype=torch.uint8), qmm.Q4_K, 4, rows, k, x, ids)
+    with pytest.raises(ValueError, match="out holds"):
+        qmm.matmul_id(torch.zeros(4 * wb, dtype=torch.uint8), qmm.Q4_K, 4, rows, k, x, ids,
+                      out=torch.zeros((3, 2, rows - 1), dtype=torch.float32))
+    with pytest.raises(ValueError, match="w_gate holds"):
+        qmm.matmul_id_glu(w_ok, w_ok, qmm.Q4_K, 4, rows, k, x, ids)
+    with pytest.raises(ValueError, match="out holds"):
+        qmm.quantize_q8_1(x, out=torch.zeros(3 * 16 * 36 - 1, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="not a positive multiple"):
+        qmm.weight_bytes(qmm.Q6_K, rows, 300)
+    # correctly sized CPU tensors pass every size check and stop at the device check
+    with pytest.raises(ValueError, match="device tensor"):
+        qmm.matmul(w_ok, qmm.Q4_K, rows, k, x)
+
+
+def test_plan_and_workspace_come_from_one_reading_of_the_overrides():
+    """Writers flip the path and tile-width overrides while readers plan calls: every plan is one
+    of the two consistent (regime, tile width, workspace) combinations, never a mixture -- the
+    workspace layout and the regime of a call are derived from the same snapshot."""
+    import threading
+    rows, k, n = 4096, 4096, 4
+    mv_ws = qmm.matmul_workspace(qmm.Q4_K, rows, k, n)
+    legal = set()
+    try:
+        for path in (0, 2):
+            for tj in (0, 32, 64, 128):
+                qmm.set_override(qmm.OVR_PATH, path)
+                qmm.set_override(qmm.OVR_TILE_J, tj)
+                p = qmm.plan_dense(qmm.Q4_K, rows, k, n)
+                legal.add((p["regime"], p["tile_j"], p["ntiles"], p["ws_bytes"]))
+        qmm.set_override(qmm.OVR_PATH, 0)
+        qmm.set_override(qmm.OVR_TILE_J, 0)
+        assert (1, 8, 256, mv_ws) in legal and len(legal) == 4   # tile width 0 and 32 coincide
+        stop = threading.Event()
+        seen, errors = [], []
+
+        def writer(i):
+            j = 0
+            while not stop.is_set():
+                qmm.set_override(qmm.OVR_PATH, (0, 2)[(i + j) % 2])
+                qmm.set_override(qmm.OVR_TILE_J, (0, 32, 64, 128)[(i * 3 + j) % 4])
+                j += 1
+
+        def reader():
+            try:
+                for _ in range(3000):
+                    p = qmm.plan_dense(qmm.Q4_K, rows, k, n)
+                    seen.append((p["regime"], p["tile_j"], p["ntiles"], p["ws_bytes"]))
+            except Exception as e:   # noqa: BLE001 -- reported below
+                errors.append(e)
+
+        ws = [threading.Thread(target=writer, args=(i,)) for i in range(2)]
+        rs = [threading.Thread(target=reader) for _ in range(4)]
+        for t in ws + rs:
+            t.start()
+        for t in rs:
+            t.join()
+        stop.set()
+        for t in ws:
+            t.join()
+        assert not errors, errors
+        assert set(seen) <= legal
+        assert len(seen) == 4 * 3000
+    finally:
+        qmm.set_override(qmm.OVR_PATH, 0)
         qmm.set_override(qmm.OVR_TILE_J, 0)

@@ -41,14 +41,39 @@ def test_encoder_bit_exact(n, k, seed):
     assert np.all(np.abs(s.cpu().numpy().astype(np.float64) - rs) <= 2.0 ** -19 * absum)
 
 
-def _check(qtype, rows, k, n, seed, wide=False):
+def _binade_x(n, k, seed):
+    """Column c: every 32-value block at its own power-of-two scale 2^(s_c + 5*(b mod 3)), s_c from
+    -60 to +60 over the columns.  Inside a column the blocks span 2^10, so each block's share of a
+    dot is at least ~2^-10 of the largest: a block unscaled by a neighbour's exponent (off by 2^5 or
+    2^10) moves the result by far more than the per-block bound below allows."""
+    rng = np.random.default_rng(seed)
+    nb = k // 32
+    s_c = np.linspace(-60, 60, n).round().astype(int)
+    e = s_c[:, None] + 5 * (np.arange(nb)[None, :] % 3)
+    return (rng.standard_normal((n, k)) * np.exp2(e).repeat(32, axis=1)).astype(np.float32)
+
+
+def _check(qtype, rows, k, n, seed, x=None, per_block=False):
+    """Products within 1e-4 of the oracle, normalised by ||w_r|| * ||x_n|| or (per_block) by the
+    tighter sum over 32-value blocks b of ||w_r,b|| * ||x_n,b||, which scores every block against
+    its own magnitude rather than the column's largest."""
     g_w, g_x = synth.rngs(seed, 2)
     w = synth.gen_weights(qtype, rows, k, g_w)
-    x = _wide_x(n, k, seed) if wide else synth.gen_activations(n, k, g_x)
+    if x is None:
+        x = synth.gen_activations(n, k, g_x)
+    n = x.shape[0]
     y = qmm.matmul_f16act(to_dev(w), qtype, rows, k, to_dev(x)).cpu().numpy()
     ref = oracle.matmul_f16act(qtype, w, rows, k, x)
-    assert_close(y, ref, row_norms(qtype, w, rows, k), np.linalg.norm(x.astype(np.float64), axis=1),
-                 what=f"{TNAME[qtype]} {rows}x{k} n={n}")
+    what = f"{TNAME[qtype]} {rows}x{k} n={n}"
+    if not per_block:
+        assert_close(y, ref, row_norms(qtype, w, rows, k), np.linalg.norm(x.astype(np.float64), axis=1), what=what)
+        return
+    W = oracle.dequantize(qtype, w, rows, k).reshape(rows, k // 32, 32)
+    X = x.astype(np.float64).reshape(n, k // 32, 32)
+    denom = np.einsum("rb,nb->nr", np.linalg.norm(W, axis=2), np.linalg.norm(X, axis=2))
+    assert np.all(np.isfinite(y)), what
+    err = np.abs(y.astype(np.float64) - ref) / np.where(denom > 0, denom, 1.0)
+    assert err.max() <= 1e-4, f"{what}: max per-block normalised error {err.max():.3e}"
 
 
 @pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
@@ -62,10 +87,15 @@ def test_f16act_small_ragged(qtype, n):
 
 @pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
 def test_f16act_wide_range_activations(qtype):
-    _check(qtype, 40, 512, 3, 800 + qtype, wide=True)
+    _check(qtype, 40, 512, 3, 800 + qtype, x=_wide_x(3, 512, 800 + qtype), per_block=True)
 
 
-@pytest.mark.parametrize("qtype", [qmm.Q4_K, qmm.Q6_K, qmm.Q4_0])
+@pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
+def test_f16act_per_block_exponents_across_binades(qtype):
+    _check(qtype, 40, 2048, 8, 850 + qtype, x=_binade_x(8, 2048, 850 + qtype), per_block=True)
+
+
+@pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
 @pytest.mark.parametrize("n", [1, 8])
 def test_f16act_full_size(qtype, n):
     _check(qtype, 4096, 4096, n, 900 + 10 * qtype + n)

@@ -5,7 +5,8 @@ Bars (both sides take every integer decision in the same precision):
   * q8_1 bytes (codes, fp16 d and s): bit-exact.
   * integer sub-block dots from the production kernels' own accumulators: bit-exact.
   * fp32 outputs: |Y_gpu - Y_oracle| <= 1e-4 * ||w_r|| * ||x_n|| (gpu_util.assert_close).
-Full-size workloads are checked on sampled outputs the oracle computes one by one.
+Full-size prefill and MoE workloads are checked on 256 whole output rows (every column of each),
+the oracle running on just those weight rows.
 """
 import numpy as np
 import pytest
@@ -111,12 +112,8 @@ def test_subdots_matvec_bit_exact(qtype, n):
     assert np.array_equal(got, exp), np.argwhere(got != exp)[:5]
 
 
-@pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
-@pytest.mark.parametrize("n", [3, 40])
-def test_subdots_tiled_bit_exact(qtype, n):
-    k = 352 if qtype == qmm.Q8_0 else 512
-    rows = 200                                     # not a multiple of the 128-row tile
-    w, x = _case(qtype, rows, k, n, 300 + n)
+def _tiled_subdots_check(qtype, rows, k, n, seed):
+    w, x = _case(qtype, rows, k, n, seed)
     xq = oracle.quantize_q8_1(x)
     got = qmm.debug_subdots(to_dev(w), qtype, rows, k, to_dev(xq), n, qmm.PATH_TILED).cpu().numpy()
     if qtype == qmm.Q6_K:
@@ -124,6 +121,46 @@ def test_subdots_tiled_bit_exact(qtype, n):
     else:
         exp = oracle.subdots(qtype, w, rows, k, xq, n)
     assert np.array_equal(got, exp), np.argwhere(got != exp)[:5]
+
+
+@pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
+@pytest.mark.parametrize("n", [3, 40])
+def test_subdots_tiled_bit_exact(qtype, n):
+    """The tiled kernel's integer dots from its production instantiation: the tiled activation
+    layout written by the relayout pass, the seeded integer accumulator (Q4_K, Q5_K) and the
+    scale-folded hi/lo planes (Q6_K); only the epilogue stores the integer instead of folding it."""
+    _tiled_subdots_check(qtype, 200, 352 if qtype == qmm.Q8_0 else 512, n, 300 + n)
+
+
+@pytest.mark.parametrize("J", [32, 64, 128])
+@pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
+def test_subdots_tiled_stream_k_and_tile_widths(qtype, J):
+    """The production plan with stream-K forced on: units start and end inside tiles, so each
+    tile's steps come from several units; every tile width."""
+    qmm.set_override(qmm.OVR_STREAMK, 2)
+    qmm.set_override(qmm.OVR_TILE_J, J)
+    rows, k, n = 300, (2080 if qtype == qmm.Q8_0 else 2048), 70
+    p = qmm.plan_dense(qtype, rows, k, n)
+    assert p["stream_k"] == 1 and p["tile_j"] == J
+    _tiled_subdots_check(qtype, rows, k, n, 310 + J)
+
+
+def test_subdots_tiled_extreme_codes():
+    """Integer dots at the edges of the seeded accumulator's range: Q4_K / Q5_K codes all at their
+    maximum against q8_1 codes of +-127 (|D| = 32 * 31 * 127 for Q5_K, below 2^22)."""
+    rows, k, n = 130, 512, 33
+    # one sign per 32-value block, alternating over blocks and columns: every q8_1 code is +-127
+    blk = np.arange(k)[None, :] // 32 + np.arange(n)[:, None]
+    x = np.where(blk % 2 == 0, 1.0, -1.0).astype(np.float32)
+    xq = oracle.quantize_q8_1(x)
+    for qtype in (qmm.Q4_K, qmm.Q5_K):
+        w = synth.gen_weights(qtype, rows, k, np.random.default_rng(320))
+        blocks = w.reshape(rows, k // 256, qmm.BLOCK_BYTES[qtype])
+        blocks[:, :, 16:] = 0xFF                      # every low nibble and (Q5_K) fifth bit set
+        got = qmm.debug_subdots(to_dev(w), qtype, rows, k, to_dev(xq), n, qmm.PATH_TILED).cpu().numpy()
+        exp = oracle.subdots(qtype, w, rows, k, xq, n)
+        assert np.abs(exp).max() == (31 if qtype == qmm.Q5_K else 15) * 32 * 127
+        assert np.array_equal(got, exp)
 
 
 # ---------------------------------------------------------------------------------------------
@@ -337,29 +374,26 @@ def test_wrong_dtype_rejected():
 # ---------------------------------------------------------------------------------------------
 # Full-size prefill shapes: sampled outputs
 # ---------------------------------------------------------------------------------------------
-def _sampled_check(y, qtype, w, rows, k, xq, n, rng, count=1536, what=""):
-    cols = rng.integers(0, n, count)
-    rws = rng.integers(0, rows, count)
-    ref = oracle.matmul_q8_1_at(qtype, w, rows, k, xq, n, cols, rws)
-    got = y[cols, rws]
+def _whole_rows_check(y, qtype, w, rows, k, xq, n, rng, nrows=256, what=""):
+    """nrows distinct output rows, every column of each, against the oracle run on exactly those
+    weight rows (rows always include the first and the last, the edges of the tile grid)."""
+    sel = np.unique(np.concatenate([[0, rows - 1], rng.choice(rows, nrows, replace=False)]))
     rb = oracle.row_bytes(qtype, k)
-    w2 = w.reshape(rows, rb)
-    wn = np.linalg.norm(oracle.dequantize(qtype, w2[rws], count, k), axis=1)
-    X, _, _ = oracle.dequantize_q8_1(xq[cols], count, k)
-    xn = np.linalg.norm(X, axis=1)
-    err = np.abs(got.astype(np.float64) - ref) / (wn * xn)
-    assert np.all(np.isfinite(got))
-    assert err.max() <= 1e-4, f"{what}: max normalised error {err.max():.3e}"
-    return float(err.max())
+    wsub = np.ascontiguousarray(w.reshape(rows, rb)[sel])
+    ref = oracle.matmul_q8_1(qtype, wsub, len(sel), k, xq, n)
+    return assert_close(np.ascontiguousarray(y[:, sel]), ref, row_norms(qtype, wsub, len(sel), k),
+                        col_norms(xq, n, k), what=what)
 
 
 @pytest.mark.parametrize("case", synth.PREFILL_CASES, ids=lambda c: c["name"])
-def test_prefill_workloads_sampled(case):
+def test_prefill_workloads_whole_rows(case):
+    """The prefill projections at full size in the launch configuration the bench times (fp32
+    input, automatic plan: stream-K at 512 tokens, whole tiles at 2048)."""
     w, x = synth.make_dense(case)
     qtype, rows, k, n = case["qtype"], case["rows"], case["k"], case["n"]
     y = qmm.matmul(to_dev(w), qtype, rows, k, to_dev(x)).cpu().numpy()
     xq = oracle.quantize_q8_1(x)
-    _sampled_check(y, qtype, w, rows, k, xq, n, np.random.default_rng(7), what=case["name"])
+    _whole_rows_check(y, qtype, w, rows, k, xq, n, np.random.default_rng(7), what=case["name"])
 
 
 def test_streamk_on_off_agree_and_rerun_is_bitwise():
@@ -405,8 +439,9 @@ def test_few_columns_beyond_matvec_k_limit(qtype):
 @pytest.mark.parametrize("J", [32, 64, 128])
 def test_q4k_min_term_large_dmin(J):
     """Q4_K min coefficients -dmin*m near and beyond the fp16 range: rows 64..127 with dmin = 1000
-    (|dmin*m| up to 63000, still fp16) and rows 128..159 with dmin = 60000 (beyond: that wave's
-    min term takes the fp32 path); every output against the oracle."""
+    (|dmin*m| up to 63000) and rows 128..159 with dmin = 60000 (up to 3.8e6, far beyond fp16).  The
+    tiled kernel's min term splits -dmin*m exactly into three bf16 pieces, which keep fp32's
+    exponent range, so no coefficient can overflow; every output against the oracle."""
     rows, k, n = 256, 512, 70
     w, x = _case(qmm.Q4_K, rows, k, n, 1600 + J)
     blocks = w.reshape(rows, k // 256, 144)
@@ -446,28 +481,27 @@ def test_tile_widths(J):
 # ---------------------------------------------------------------------------------------------
 # Expert-indexed product
 # ---------------------------------------------------------------------------------------------
-def _moe_ref_sampled(case, w, x, ids, y, rng, count=1024):
+def _moe_whole_rows(case, w, x, ids, y, rng, nrows=256):
+    """nrows distinct output rows of every (token, slot) pair: the oracle's expert product on the
+    same rows of every expert, compared element by element."""
     qtype, rows, k, n_exp = case["qtype"], case["rows"], case["k"], case["n_exp"]
     n_tok, top_k = ids.shape
     xpt = case["x_per_tok"]
+    sel = np.unique(np.concatenate([[0, rows - 1], rng.choice(rows, nrows, replace=False)]))
     rb = oracle.row_bytes(qtype, k)
-    wm = w.reshape(n_exp, rows * rb)
+    wsub = np.ascontiguousarray(w.reshape(n_exp, rows, rb)[:, sel])
+    ref, bad = oracle.matmul_id(qtype, wsub, n_exp, len(sel), k, x, xpt, ids)
+    assert bad == 0
     xq = oracle.quantize_q8_1(x)
-    pairs = rng.integers(0, n_tok * top_k, count)
-    rws = rng.integers(0, rows, count)
-    worst = 0.0
-    for e in np.unique(ids.reshape(-1)[pairs]):
-        sel = np.nonzero(ids.reshape(-1)[pairs] == e)[0]
-        p = pairs[sel]
-        arow = (p // top_k) * xpt + (p % top_k if xpt > 1 else 0)
-        ref = oracle.matmul_q8_1_at(qtype, wm[e], rows, k, xq, xq.shape[0], arow, rws[sel])
-        got = y.reshape(n_tok * top_k, rows)[p, rws[sel]]
-        wn = np.linalg.norm(oracle.dequantize(qtype, wm[e].reshape(rows, rb)[rws[sel]], len(sel), k), axis=1)
-        X, _, _ = oracle.dequantize_q8_1(xq[arow], len(sel), k)
-        err = np.abs(got.astype(np.float64) - ref) / (wn * np.linalg.norm(X, axis=1))
-        worst = max(worst, float(err.max()))
-    assert worst <= 1e-4, f"max normalised error {worst:.3e}"
-    return worst
+    wn = row_norms(qtype, wsub, n_exp * len(sel), k).reshape(n_exp, len(sel))
+    xn = col_norms(xq, xq.shape[0], k)
+    got = y[:, :, sel]
+    arow = np.arange(n_tok)[:, None] * xpt + (np.arange(top_k)[None, :] if xpt > 1 else 0)
+    denom = wn[ids] * xn[arow][:, :, None]
+    assert np.all(np.isfinite(got))
+    err = np.abs(got.astype(np.float64) - ref.astype(np.float64)) / denom
+    assert err.max() <= 1e-4, f"max normalised error {err.max():.3e} at {np.unravel_index(np.argmax(err), err.shape)}"
+    return float(err.max())
 
 
 @pytest.mark.parametrize("case", synth.MOE_CASES, ids=lambda c: c["name"])
@@ -489,7 +523,7 @@ def test_moe_workloads(case):
                 a = t * case["x_per_tok"] + (s if case["x_per_tok"] > 1 else 0)
                 assert_close(y[t, s][None], ref[t, s][None], wn_all[ids[t, s]], xn_all[a:a + 1], what=f"pair {t},{s}")
     else:
-        _moe_ref_sampled(case, w, x, ids, y, np.random.default_rng(11))
+        _moe_whole_rows(case, w, x, ids, y, np.random.default_rng(11))
 
 
 def test_moe_invalid_ids_and_per_slot_activations():
