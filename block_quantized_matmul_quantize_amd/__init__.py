@@ -214,6 +214,13 @@ def _need_size(t, nbytes, name):
         raise ValueError(f"{name} holds {have} bytes, the call needs {nbytes}")
 
 
+def _need_weights(t, qtype, rows, k, name, n_mat=1):
+    """Size check of a weight tensor; an unknown type or a k the type cannot take is left to the
+    library, which reports it as QMM_ERR_TYPE / QMM_ERR_SHAPE (QmmError)."""
+    if qtype in BLOCK_VALUES and k > 0 and k % BLOCK_VALUES[qtype] == 0 and rows > 0:
+        _need_size(t, n_mat * weight_bytes(qtype, rows, k), name)
+
+
 def _workspace(nbytes, device):
     torch = _torch()
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
@@ -243,7 +250,7 @@ def matmul(w, qtype, rows, k, x, out=None, ws=None):
     if x.dim() != 2 or x.shape[1] != k:
         raise ValueError(f"x must be [n, {k}]")
     n = x.shape[0]
-    _need_size(w, weight_bytes(qtype, rows, k), "w")
+    _need_weights(w, qtype, rows, k, "w")
     if out is None:
         out = torch.empty((n, rows), dtype=torch.float32, device=x.device)
     py = _need(out, torch.float32, "out")
@@ -285,7 +292,7 @@ def matmul_f16act(w, qtype, rows, k, x, out=None, ws=None):
     if x.dim() != 2 or x.shape[1] != k:
         raise ValueError(f"x must be [n, {k}]")
     n = x.shape[0]
-    _need_size(w, weight_bytes(qtype, rows, k), "w")
+    _need_weights(w, qtype, rows, k, "w")
     if out is None:
         out = torch.empty((n, rows), dtype=torch.float32, device=x.device)
     py = _need(out, torch.float32, "out")
@@ -304,7 +311,7 @@ def matmul_q8_1(w, qtype, rows, k, xq, n, out=None, ws=None):
     px = _need(xq, torch.uint8, "xq")
     if xq.numel() != n * (k // 32) * Q8_1_BYTES:
         raise ValueError("xq has the wrong number of bytes")
-    _need_size(w, weight_bytes(qtype, rows, k), "w")
+    _need_weights(w, qtype, rows, k, "w")
     if out is None:
         out = torch.empty((n, rows), dtype=torch.float32, device=xq.device)
     py = _need(out, torch.float32, "out")
@@ -329,7 +336,7 @@ def matmul_id(w, qtype, n_exp, rows, k, x, ids, x_per_tok=1, out=None, ws=None):
     n_tok, top_k = ids.shape
     if x.shape != (n_tok * x_per_tok, k):
         raise ValueError(f"x must be [{n_tok * x_per_tok}, {k}]")
-    _need_size(w, n_exp * weight_bytes(qtype, rows, k), "w")
+    _need_weights(w, qtype, rows, k, "w", n_exp)
     if out is None:
         out = torch.zeros((n_tok, top_k, rows), dtype=torch.float32, device=x.device)
     py = _need(out, torch.float32, "out")
@@ -350,7 +357,7 @@ def matmul_glu(w_gate, w_up, qtype, rows, k, x, out=None, ws=None):
     pu = _need(w_up, torch.uint8, "w_up")
     if w_gate.numel() != w_up.numel():
         raise ValueError("w_gate and w_up must have the same size")
-    _need_size(w_gate, weight_bytes(qtype, rows, k), "w_gate")
+    _need_weights(w_gate, qtype, rows, k, "w_gate")
     px = _need(x, torch.float32, "x")
     if x.dim() != 2 or x.shape[1] != k:
         raise ValueError(f"x must be [n, {k}]")
@@ -375,7 +382,7 @@ def matmul_id_glu(w_gate, w_up, qtype, n_exp, rows, k, x, ids, out=None, ws=None
     pu = _need(w_up, torch.uint8, "w_up")
     if w_gate.numel() != w_up.numel():
         raise ValueError("w_gate and w_up must have the same size")
-    _need_size(w_gate, n_exp * weight_bytes(qtype, rows, k), "w_gate")
+    _need_weights(w_gate, qtype, rows, k, "w_gate", n_exp)
     px = _need(x, torch.float32, "x")
     pi = _need(ids, torch.int32, "ids")
     if ids.dim() != 2:
@@ -435,7 +442,7 @@ def debug_subdots(w, qtype, rows, k, xq, n, path):
     torch = _torch()
     pw = _need(w, torch.uint8, "w")
     px = _need(xq, torch.uint8, "xq")
-    _need_size(w, weight_bytes(qtype, rows, k), "w")
+    _need_weights(w, qtype, rows, k, "w")
     _need_size(xq, n * (k // 32) * Q8_1_BYTES, "xq")
     per = k // 16 if (qtype == Q6_K and path == PATH_MATVEC) else k // 32
     out = torch.zeros((n, rows, per), dtype=torch.int32, device=xq.device)
