@@ -61,6 +61,7 @@ _sig("qmm_encode_f16act", _i32, _vp, _i64, _i64, _vp, _vp, _vp, _vp)
 _sig("qmm_matmul_f16act_workspace", _sz, _i64, _i64)
 _sig("qmm_matmul_f16act", _i32, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _sz, _vp)
 _sig("qmm_matmul", _i32, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _sz, _vp)
+_sig("qmm_matmul_noalloc", _i32, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _vp)
 _sig("qmm_matmul_q8_1_workspace", _sz, _i32, _i64, _i64, _i64)
 _sig("qmm_matmul_q8_1", _i32, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _sz, _vp)
 _sig("qmm_matmul_id_workspace", _sz, _i32, _i64, _i64, _i64, _i64, _i64, _i64)
@@ -260,6 +261,25 @@ def matmul(w, qtype, rows, k, x, out=None, ws=None):
         ws = _workspace(nbytes, x.device)
     _on_device(w=w, x=x, out=out, ws=ws)
     _check(_L.qmm_matmul(qtype, pw, rows, k, px, n, py, ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream()))
+    return out
+
+
+def matmul_noalloc(w, qtype, rows, k, x, out=None):
+    """matmul without a workspace argument: the library's own per-GPU scratch buffer holds it (the
+    call allocates nothing itself, apart from `out` when it is not given)."""
+    torch = _torch()
+    pw = _need(w, torch.uint8, "w")
+    px = _need(x, torch.float32, "x")
+    if x.dim() != 2 or x.shape[1] != k:
+        raise ValueError(f"x must be [n, {k}]")
+    n = x.shape[0]
+    _need_weights(w, qtype, rows, k, "w")
+    if out is None:
+        out = torch.empty((n, rows), dtype=torch.float32, device=x.device)
+    py = _need(out, torch.float32, "out")
+    _need_size(out, n * rows * 4, "out")
+    _on_device(w=w, x=x, out=out)
+    _check(_L.qmm_matmul_noalloc(qtype, pw, rows, k, px, n, py, _stream()))
     return out
 
 

@@ -16,7 +16,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libqmm.so")
-SOURCES = ["quantize.hip", "mmvq.hip", "mmvq_stream.hip", "mmvq_dot4.hip", "mmq.hip", "moe.hip", "f16act.hip", "api.cpp"]
+SOURCES = ["quantize.hip", "mmvq.hip", "mmvq_stream.hip", "mmvq_dot4.hip", "mmq.hip", "moe.hip", "f16act.hip",
+           "noalloc.hip", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

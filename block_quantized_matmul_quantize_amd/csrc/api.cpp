@@ -275,6 +275,22 @@ DenseWs dense_layout(int type, int64_t rows, int64_t k, int64_t n, bool with_xq,
     return L;
 }
 
+// The workspace a qmm_matmul of this shape uses under plan p exactly (qmm_matmul's own layout
+// reserves stream-K slots for any plan, so that one size serves every override): the q8_1 copy on
+// the matrix-vector path, the tiled activations and p's stream-K slots on the tiled path.
+DenseWs dense_layout_exact(int64_t k, int64_t n, const qmm_plan &p) {
+    DenseWs L{};
+    size_t off = 0;
+    L.xq_off = off;
+    if (p.regime == 1) off = align_up(off + (size_t)(n * (k / 32) * 36), 256);
+    L.tiled_off = off;
+    if (p.regime == 2) off = align_up(off + qmm::q8_1_tiled_bytes(n, k), 256);
+    L.part_off = off;
+    if (p.regime == 2 && p.stream_k) off = align_up(off + (size_t)p.units * 2 * kTI * p.tile_j * 4, 256);
+    L.total = off;
+    return L;
+}
+
 // xq: canonical q8_1 blocks, or (x_tiled) activations already in the tiled layout.  The plan,
 // the workspace layout L and the kernel choices all come from the one override snapshot o.  dbg
 // set: the integer-dot export of the planned kernel (the tiled kernel in its production plan,
@@ -724,3 +740,32 @@ qmm_status qmm_matmul_id_invalid_count(const void *ws, int64_t *out, void *strea
 }
 
 }  // extern "C"
+
+// ----------------------------------------------------------------------------------------------
+// Hooks for the allocation-free dense entry point (noalloc.hip), which owns its scratch memory.
+// ----------------------------------------------------------------------------------------------
+namespace qmm {
+
+Ovr load_overrides() { return load_ovr(); }
+
+qmm_status report(qmm_status st, const char *msg) { return fail(st, "%s", msg); }
+
+qmm_status matmul_exact_check(int type, const void *w, int64_t rows, int64_t k, const float *x, int64_t n,
+                              const float *y, const Ovr &o, size_t *need) {
+    qmm_status st = check_plan_args(type, rows, k, n, o);
+    if (st) return st;
+    if ((st = check_ptrs_dense(w, x, y, n))) return st;
+    *need = 0;
+    if (n == 0) return QMM_OK;
+    if (((uintptr_t)x) & 15) return fail(QMM_ERR_ARG, "x must be 16-byte aligned");
+    *need = dense_layout_exact(k, n, plan_dense_impl(type, rows, k, n, device_cus(), o)).total;
+    return QMM_OK;
+}
+
+qmm_status matmul_exact_run(int type, const void *w, int64_t rows, int64_t k, const float *x, int64_t n, float *y,
+                            uint8_t *ws, const Ovr &o, hipStream_t s) {
+    const DenseWs L = dense_layout_exact(k, n, plan_dense_impl(type, rows, k, n, device_cus(), o));
+    return dense_f32(type, w, rows, k, x, n, y, ws, L, o, s);
+}
+
+}  // namespace qmm

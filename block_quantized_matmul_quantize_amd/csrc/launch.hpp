@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/qmm.h"
+
 namespace qmm {
 
 // Plan overrides (qmm_set_override), read once at the start of a call so that every decision of
@@ -125,5 +127,17 @@ hipError_t launch_f16act_encode(const float *x, int64_t n, int64_t k, uint16_t *
                                 hipStream_t s);
 hipError_t launch_mmvq_f16act(int type, const uint8_t *w, int64_t rows, int64_t k, const uint16_t *y16,
                               const int32_t *e, const float *bsum, int64_t n, float *out, hipStream_t s);
+
+// Dense fp32-input product with a workspace sized exactly to its plan (api.cpp), for the
+// allocation-free entry point (noalloc.hip).  o: one reading of the overrides for the whole call.
+Ovr load_overrides();
+// Sets the calling thread's qmm_last_error message and returns st.
+qmm_status report(qmm_status st, const char *msg);
+// qmm_matmul's argument checks; *need = the workspace bytes the call's plan uses (0 for n == 0).
+qmm_status matmul_exact_check(int type, const void *w, int64_t rows, int64_t k, const float *x, int64_t n,
+                              const float *y, const Ovr &o, size_t *need);
+// The product itself, with ws holding at least matmul_exact_check's bytes.
+qmm_status matmul_exact_run(int type, const void *w, int64_t rows, int64_t k, const float *x, int64_t n, float *y,
+                            uint8_t *ws, const Ovr &o, hipStream_t s);
 
 }  // namespace qmm

@@ -93,6 +93,23 @@ qmm_status qmm_matmul_q8_1(int type, const void *w, int64_t rows, int64_t k, con
                            int64_t n, float *y, void *ws, size_t ws_bytes, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Allocation-free dense product, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The same product, plan,
+ * kernels and argument checks as qmm_matmul, but the workspace is a buffer the library owns: a
+ * static device array of QMM_NOALLOC_SCRATCH_BYTES on each GPU the library runs on (held until the
+ * process ends), of which a call uses exactly what its plan needs.  The call itself allocates
+ * nothing; its first call with a given device current looks up that device's buffer address.
+ * A call whose plan needs more than QMM_NOALLOC_SCRATCH_BYTES returns QMM_ERR_WORKSPACE before
+ * anything is launched (e.g. 4096 x 14336 Q6_K at 512 columns needs ~42 MB and fits; 65536
+ * columns of k = 14336 do not).  Calls share their GPU's buffer: calls that overlap on one GPU
+ * (different streams, different threads without ordering) race and must be serialised by the
+ * caller, e.g. by issuing them on one stream.  No part of the buffer needs clearing between calls.
+ * ------------------------------------------------------------------------------------------- */
+#define QMM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+qmm_status qmm_matmul_noalloc(int type, const void *w, int64_t rows, int64_t k, const float *x, int64_t n,
+                              float *y, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Expert-indexed product (MoE mul_mat_id; [MMQ] "MoE dispatch", "expert bounds", "MoE skew").
  * w: n_exp weight matrices [rows][k] back to back (ggml [k, rows, n_exp]).
  * ids: int32 [n_tok][top_k] expert ids (ggml [n_expert_used, n_tokens]).

@@ -115,6 +115,14 @@ int main() {
     }
     int64_t cnt = 0;
     EXPECT(qmm_matmul_id_invalid_count(WS, &cnt, nullptr) == QMM_ERR_HIP);
+    // allocation-free entry point: too large for its scratch (host check), argument errors, and a
+    // call that fits -- its scratch lookup fails without a device
+    EXPECT(qmm_matmul_noalloc(QMM_Q6_K, W, 4096, 14336, (const float *)X, 65536, (float *)Y, nullptr) ==
+           QMM_ERR_WORKSPACE);
+    EXPECT(qmm_matmul_noalloc(11, W, 4096, 256, (const float *)X, 4, (float *)Y, nullptr) == QMM_ERR_TYPE);
+    EXPECT(qmm_matmul_noalloc(QMM_Q4_K, W, 4096, 4096, (const float *)X, 0, (float *)Y, nullptr) == QMM_OK);
+    for (int64_t n : {3, 512})
+        EXPECT(qmm_matmul_noalloc(QMM_Q4_K, W, 4096, 4096, (const float *)X, n, (float *)Y, nullptr) == QMM_ERR_HIP);
 
     // overrides written while other threads plan
     std::atomic<bool> stop{false};

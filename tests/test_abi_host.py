@@ -351,3 +351,15 @@ def test_plan_and_workspace_come_from_one_reading_of_the_overrides():
     finally:
         qmm.set_override(qmm.OVR_PATH, 0)
         qmm.set_override(qmm.OVR_TILE_J, 0)
+
+
+def test_noalloc_entry_refuses_calls_beyond_its_scratch_without_gpu():
+    """The allocation-free entry point checks its plan's workspace against its fixed scratch size on
+    the host, before any device call (fake addresses here: nothing is launched or looked up)."""
+    L = qmm.lib()
+    w, x, y = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000), ctypes.c_void_p(0x300000)
+    assert L.qmm_matmul_noalloc(qmm.Q6_K, w, 4096, 14336, x, 65536, y, None) == -4
+    assert b"allocation-free" in L.qmm_last_error()
+    assert L.qmm_matmul_noalloc(11, w, 4096, 256, x, 4, y, None) == -2
+    assert L.qmm_matmul_noalloc(qmm.Q4_K, w, 4096, 4096, ctypes.c_void_p(0x200004), 4, y, None) == -1
+    assert L.qmm_matmul_noalloc(qmm.Q4_K, w, 4096, 4096, x, 0, y, None) == 0
