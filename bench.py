@@ -8,22 +8,32 @@ divided by the step time.  Weights rotate over several distinct copies (> 512 MB
 256 MB Infinity Cache cannot serve them; the cache-warm rate is reported separately.
 
 Also in the same JSON line:
-  roofline      for the dominant kernel (the matrix-vector kernel): per case, a HIP graph of
-                back-to-back launches over the weight rotations is replayed between two HIP
-                events on the launch stream; peak = 8 TB/s HBM.  traffic comes from the committed
-                rocprofv3 FETCH_SIZE/WRITE_SIZE summary when it matches the current sources.
-  cpu_baseline  the oracle (plain C, all host threads) on whole steps of the same workload.
+  roofline      for the dominant kernel (the matrix-vector kernel): per case, the weights rotate over
+                copies totalling > 512 MB, a HIP graph holds one launch per copy, and every replay
+                is timed by HIP events on the launch stream (median / p10 / p90 per launch);
+                peak = 8 TB/s HBM.  probe: the loads-only streaming read (libqmm_probe) of the same
+                rotated weight bytes, and at the 66 MB fused gate/up decode size; frac_of_probe =
+                probe time / kernel time.  traffic comes from the committed rocprofv3
+                FETCH_SIZE/WRITE_SIZE summary when it matches the current kernel sources.
+  cpu_baseline  the oracle (plain C, all host threads) on whole steps of the same workload; the
+                host CPU model; one-thread figures on the small dense workload and one step.
   f16act_matvec  per-call timing (encoder + kernel) of the fp16-activation mode on the step's shapes
   extra_types_matvec  per-launch timing of the same matrix-vector shapes in Q5_K and Q4_0 (not
                 part of the step).
-  secondary     int8 TOPS and % of the 5.0 POP/s int8 MFMA peak for the prefill and MoE shapes, and
-                for the gate/up products fused with SwiGLU (decode: also GB/s of the two matrices).
+  secondary     for the prefill and MoE shapes and the gate/up products fused with SwiGLU: per-call
+                median / p10 / p90, int8 TOPS as a fraction of the 5.0 POP/s datasheet peak and of
+                the int8 MFMA probe, % of roofline (max of bytes / 8 TB/s and ops / 5 POP/s over
+                the time); weights rotated over > 512 MB, MoE also with resident weights (warm).
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-secondary]
        python bench.py --secondary-only [--calib-copy]   only the prefill / MoE shapes (profiling)
 
 Profile summaries (no GPU; read the SQLite databases rocprofv3 writes under -d DIR):
   python bench.py --summarize-trace DIR          per-kernel durations of a --kernel-trace run
+  python bench.py --summarize-counters DIR       per-kernel, per-launch-shape averages of the
+                 counters of a --pmc run, with the matrix-pipe busy fraction
+                 (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * SIMDs)), vector-ALU activity
+                 (SQ_ACTIVE_INST_VALU / SQ_BUSY_CU_CYCLES) and int8 MFMA ops (MOPS_I8 * 512)
   python bench.py --summarize-pmc FDIR WDIR [--write-traffic]
                  per-kernel FETCH_SIZE / WRITE_SIZE of two --pmc runs of `bench.py --calib-copy`,
                  scaled to bytes by the 256 MiB device copy (tiled and grouping kernels get one
@@ -47,9 +57,30 @@ HBM_PEAK_GBPS = 8000.0
 INT8_PEAK_TOPS = 5000.0
 
 
-# Sources the matrix-vector kernels are built and chosen from: a change to any of them drops the
-# stored counter traffic; changes elsewhere (tiled kernels, planner) do not affect those kernels.
-MV_SOURCES = ["common.hpp", "launch.hpp", "q8_1.hpp", "mmvq.hip", "mmvq_stream.hip", "mmvq_dot4.hip"]
+# Sources of the matrix-vector kernels themselves: a change to any of them drops the stored counter
+# traffic; changes elsewhere (tiled kernels, planner, shared headers of declarations) do not
+# change those kernels' memory traffic.
+MV_SOURCES = ["q8_1.hpp", "mv_cols.hpp", "mmvq.hip", "mmvq_stream.hip", "mmvq_dot4.hip"]
+
+
+def probe_lib():
+    """The measurement probes (include/qmm_probe.h), loaded after torch like libqmm."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "block_quantized_matmul_quantize_amd", "libqmm_probe.so"))
+    lib.qmm_probe_read.restype = ctypes.c_int
+    lib.qmm_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_void_p]
+    lib.qmm_probe_mfma_i8.restype = ctypes.c_int
+    lib.qmm_probe_mfma_i8.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    return lib
+
+
+PROBE_WGS, PROBE_THREADS = 2048, 256   # the read probe's launch shape (the fastest of those measured)
+
+
+def pct(vals, q):
+    import numpy as np
+    return round(float(np.percentile(np.asarray(vals), q)), 3)
 
 
 def source_hash():
@@ -87,11 +118,19 @@ def main():
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run one 256 MiB device copy (known bytes) to scale profiler counters")
     ap.add_argument("--summarize-trace", metavar="DIR")
+    ap.add_argument("--summarize-counters", metavar="DIR")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--write-traffic", action="store_true")
+    ap.add_argument("--cpu-single", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.cpu_single:
+        cpu_single_thread()
+        return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
         return
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, write=args.write_traffic)
@@ -193,45 +232,90 @@ def main():
     # The matrix-vector kernel as the step launches it.  qmm.matvec_kernel names it per case and
     # says whether it quantizes the fp32 input itself: then qmm.matmul is exactly one launch of it
     # (reading fp32 activations); otherwise qmm.matmul_q8_1 on the pre-quantized activations is
-    # one launch of it (the step adds one quantize launch).  Per case, a graph of back-to-back
-    # launches over the R weight rotations is replayed between two HIP events on the stream the
-    # graph runs on; duration = elapsed / launches.
+    # one launch of it (the step adds one quantize launch).  Per case, the weights rotate over
+    # copies totalling > 512 MB (whole rows rolled on the device), a HIP graph holds one launch per
+    # copy back to back, and each of `reps` replays is timed by two HIP events on the stream the
+    # graph runs on: duration per launch = replay time / copies; median, p10 and p90 over replays.
+    # The loads-only probe (libqmm_probe) reads the same rotated weight bytes in the same way.
+    plib = probe_lib()
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device=dev)
+
+    def replay_samples(g, per, reps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in ev:
+            a.record()
+            g.replay()
+            b.record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) * 1e3 / per for a, b in ev]
+
+    def rotations(w0, row_bytes, target=600e6):
+        n = max(2, int(np.ceil(target / w0.numel())))
+        flat = w0.reshape(-1)
+        return [torch.roll(flat, r * row_bytes) for r in range(n)]
+
+    def probe_us(bufs, reps):
+        def launch():
+            st = torch.cuda.current_stream().cuda_stream
+            for wb in bufs:
+                assert plib.qmm_probe_read(wb.data_ptr(), wb.numel(), sink.data_ptr(), PROBE_WGS, PROBE_THREADS, st) == 0
+        return replay_samples(capture(launch), len(bufs), reps)
+
     per_case = []
-    tot_bytes = tot_us = 0.0
-    nrep = max(4, args.steps // 10)
+    tot_bytes = tot_us = tot_probe_us = 0.0
+    reps = max(20, args.steps)
     for i, c in enumerate(cases):
         kid, fused = qmm.matvec_kernel(c["qtype"], W[0][i], c["k"], X[i], c["n"], x_fp32=True)
+        rot = rotations(W[0][i], (c["k"] // BV[c["qtype"]]) * BB[c["qtype"]])
         if fused:
-            call = lambda r, i=i, c=c: qmm.matmul(W[r][i], c["qtype"], c["rows"], c["k"], X[i], out=Y[i], ws=WS[i])
+            call = lambda r, i=i, c=c: qmm.matmul(rot[r], c["qtype"], c["rows"], c["k"], X[i], out=Y[i], ws=WS[i])
         else:
-            call = lambda r, i=i, c=c: qmm.matmul_q8_1(W[r][i], c["qtype"], c["rows"], c["k"], XQ[i], c["n"],
+            call = lambda r, i=i, c=c: qmm.matmul_q8_1(rot[r], c["qtype"], c["rows"], c["k"], XQ[i], c["n"],
                                                        out=Y[i])
-        g = capture(lambda: [call(r) for _ in range(4) for r in range(R)])
-        g.replay()
-        us = run(nrep, lambda s: g.replay()) * 1e3 / (4 * R)
+        g = capture(lambda: [call(r) for r in range(len(rot))])
+        smp = replay_samples(g, len(rot), reps)
+        us = pct(smp, 50)
+        pus = pct(probe_us(rot, reps), 50)
         b = launch_bytes(c["qtype"], c["rows"], c["k"], c["n"], BB, BV, fused)
+        wb = rot[0].numel()
         per_case.append({"case": c["name"], "kernel": qmm.MV_KERNEL_NAMES.get(kid, "?") + (" (fp32 in)" if fused else ""),
-                         "us": round(us, 3), "bytes": b, "GBps": round(b / us / 1e3, 1),
-                         "frac": round(b / us / 1e3 / HBM_PEAK_GBPS, 4)})
+                         "us": us, "us_p10": pct(smp, 10), "us_p90": pct(smp, 90), "bytes": b,
+                         "GBps": round(b / us / 1e3, 1), "frac": round(b / us / 1e3 / HBM_PEAK_GBPS, 4),
+                         "probe_us": pus, "probe_GBps": round(wb / pus / 1e3, 1),
+                         "frac_of_probe": round(pus / us, 4), "weight_copies": len(rot)})
         tot_bytes += b
         tot_us += us
+        tot_probe_us += pus
+        del g, rot
     achieved = tot_bytes / tot_us / 1e3
     for pc in per_case:
-        log(f"[bench]   {pc['case']:24s} {pc['kernel']:30s} {pc['us']:8.3f} us  {pc['GBps']:8.1f} GB/s")
+        log(f"[bench]   {pc['case']:24s} {pc['kernel']:30s} {pc['us']:8.3f} us (p10 {pc['us_p10']:.3f} p90 "
+            f"{pc['us_p90']:.3f})  {pc['GBps']:8.1f} GB/s; loads-only probe {pc['probe_us']:.3f} us")
+    # the probe at the fused gate/up decode size: two Q4_K 14336 x 4096 matrices (66 MB)
+    big = torch.zeros(2 * 14336 * 16 * 144, dtype=torch.uint8, device=dev)
+    big_rot = rotations(big, 16 * 144)
+    probe_66 = pct(probe_us(big_rot, max(10, reps // 4)), 50)
+    del big, big_rot
+    probe = {"kernel": "qmm_probe_read (streaming 16-byte loads, %d x %d threads)" % (PROBE_WGS, PROBE_THREADS),
+             "avg_launch_us": round(tot_probe_us / len(cases), 3),
+             "GBps_at_step_sizes": round(sum(pc["probe_GBps"] * pc["probe_us"] for pc in per_case) / tot_probe_us, 1),
+             "us_66MB": probe_66, "GBps_66MB": round(2 * 14336 * 16 * 144 / probe_66 / 1e3, 1)}
+    log(f"[bench] loads-only probe: {probe}")
 
     # Q5_K and Q4_0, types beyond the headline workload: the same per-launch timing (not in the step)
     q5_cases = []
     for i, c in enumerate(synth.EXTRA_MMVQ_CASES):
-        w5 = [torch.from_numpy(synth.gen_weights(c["qtype"], c["rows"], c["k"], synth.rngs(3000 * r + i, 1)[0])).to(dev)
-              for r in range(R)]
+        w5 = rotations(torch.from_numpy(synth.gen_weights(c["qtype"], c["rows"], c["k"], synth.rngs(3000 + i, 1)[0])).to(dev),
+                       (c["k"] // BV[c["qtype"]]) * BB[c["qtype"]])
         x5 = torch.from_numpy(synth.gen_activations(c["n"], c["k"], synth.rngs(70 + i, 1)[0])).to(dev)
         y5 = torch.empty((c["n"], c["rows"]), dtype=torch.float32, device=dev)
         ws5 = qmm._workspace(qmm.matmul_workspace(c["qtype"], c["rows"], c["k"], c["n"]), dev)
         kid, fused = qmm.matvec_kernel(c["qtype"], w5[0], c["k"], x5, c["n"], x_fp32=True)
         g = capture(lambda: [qmm.matmul(w5[r], c["qtype"], c["rows"], c["k"], x5, out=y5, ws=ws5)
-                             for _ in range(4) for r in range(R)])
-        g.replay()
-        us = run(nrep, lambda s: g.replay()) * 1e3 / (4 * R)
+                             for r in range(len(w5))])
+        us = pct(replay_samples(g, len(w5), max(10, reps // 4)), 50)
         b = launch_bytes(c["qtype"], c["rows"], c["k"], c["n"], BB, BV, fused)
         # one call = one launch where the kernel quantizes x itself, else quantize + kernel
         q5_cases.append({"case": c["name"], "launches_per_call": 1 if fused else 2,
@@ -243,15 +327,14 @@ def main():
     # fp16-activation mode (encoder + wave-per-row kernel: two launches per call) on the step's shapes
     f16_cases = []
     for i, c in enumerate(synth.MMVQ_CASES):
-        wf = [torch.from_numpy(synth.gen_weights(c["qtype"], c["rows"], c["k"], synth.rngs(5000 * r + i, 1)[0])).to(dev)
-              for r in range(R)]
+        wf = rotations(torch.from_numpy(synth.gen_weights(c["qtype"], c["rows"], c["k"], synth.rngs(5000 + i, 1)[0])).to(dev),
+                       (c["k"] // BV[c["qtype"]]) * BB[c["qtype"]])
         xf = torch.from_numpy(synth.gen_activations(c["n"], c["k"], synth.rngs(90 + i, 1)[0])).to(dev)
         yf = torch.empty((c["n"], c["rows"]), dtype=torch.float32, device=dev)
         wsf = qmm._workspace(qmm.matmul_f16act_workspace(c["k"], c["n"]), dev)
         g = capture(lambda: [qmm.matmul_f16act(wf[r], c["qtype"], c["rows"], c["k"], xf, out=yf, ws=wsf)
-                             for _ in range(4) for r in range(R)])
-        g.replay()
-        us = run(nrep, lambda s: g.replay()) * 1e3 / (4 * R)
+                             for r in range(len(wf))])
+        us = pct(replay_samples(g, len(wf), max(10, reps // 4)), 50)
         b = launch_bytes(c["qtype"], c["rows"], c["k"], c["n"], BB, BV, True)
         f16_cases.append({"case": c["name"], "launches_per_call": 2, "us": round(us, 3),
                           "GBps": round(b / us / 1e3, 1), "frac": round(b / us / 1e3 / HBM_PEAK_GBPS, 4)})
@@ -271,7 +354,8 @@ def main():
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "algorithmic_bytes_per_launch_avg": round(tot_bytes / len(cases), 1),
-                "avg_launch_us": round(tot_us / len(cases), 3), "per_case": per_case}
+                "avg_launch_us": round(tot_us / len(cases), 3),
+                "probe": probe, "frac_of_probe": round(tot_probe_us / tot_us, 4), "per_case": per_case}
 
     # ---------------------------------------------------------------- secondary: prefill / MoE
     secondary = None
@@ -331,6 +415,28 @@ def summarize_trace(d):
     for n, ds in sorted(by.items(), key=lambda kv: -sum(kv[1])):
         print(f"{n[:66]:66s} {len(ds):6d} {sum(ds) / len(ds):9.3f} {statistics.median(ds):9.3f} "
               f"{min(ds):9.3f} {max(ds):9.3f} {sum(ds) / 1e3:9.3f}")
+
+
+def summarize_counters(d, simds=1024):
+    import statistics
+    con = _rocpd(d)
+    rows = con.execute("select kernel_name, grid_size, counter_name, value from counters_collection").fetchall()
+    by = {}
+    for name, grid, cname, value in rows:
+        by.setdefault((_short(name), grid), {}).setdefault(cname, []).append(value)
+    names = sorted({c for v in by.values() for c in v})
+    print("| kernel | grid (threads) | dispatches | " + " | ".join(names) + " | MFMA busy | VALU active | int8 ops |")
+    print("|---|---|---|" + "---|" * len(names) + "---|---|---|")
+    for (k, grid), cs in sorted(by.items()):
+        avg = {c: statistics.mean(v) for c, v in cs.items()}
+        disp = max(len(v) for v in cs.values())
+        mfma = avg.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) / (avg.get("GRBM_GUI_ACTIVE", 0) * simds) \
+            if avg.get("GRBM_GUI_ACTIVE") else None
+        valu = avg.get("SQ_ACTIVE_INST_VALU", 0) / avg["SQ_BUSY_CU_CYCLES"] if avg.get("SQ_BUSY_CU_CYCLES") else None
+        ops = avg.get("SQ_INSTS_VALU_MFMA_MOPS_I8", 0) * 512
+        fmt = lambda v: "-" if v is None else f"{100 * v:.1f} %"
+        print(f"| `{k[:60]}` | {grid} | {disp} | " + " | ".join(f"{avg.get(c, 0):.4g}" for c in names) +
+              f" | {fmt(mfma)} | {fmt(valu)} | {ops:.4g} |")
 
 
 def summarize_pmc(fdir, wdir, write=False):
@@ -395,89 +501,135 @@ def summarize_pmc(fdir, wdir, write=False):
             f.write("\n")
 
 
-def run_secondary(torch, np, qmm, synth, dev, log):
-    """Prefill and MoE shapes: int8 TOPS = 2*rows*k*columns / kernel-sequence time."""
-    res = []
-    reps = 8
-
-    def timed(fn, warm):
-        # every rotated weight copy is touched before timing (first touches of a fresh buffer run
-        # ~10 % slower), so the timed calls see weights streamed from HBM at steady state
-        for r in range(warm):
-            fn(r)
+def mfma_probe_tops(torch, dev, log):
+    """Attainable int8 matrix-core rate: the MFMA probe on 4 / 8 / 16 waves per compute unit, best of
+    the three (TOPS)."""
+    plib = probe_lib()
+    sink = torch.zeros(16, dtype=torch.int32, device=dev)
+    ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+    best = 0.0
+    iters = 2000
+    for wpc in (4, 8, 16):
+        wgs = ncu * wpc // 4
+        st = torch.cuda.current_stream().cuda_stream
+        assert plib.qmm_probe_mfma_i8(iters, wgs, sink.data_ptr(), st) == 0
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
-        for r in range(reps):
-            fn(r)
+        for _ in range(3):
+            assert plib.qmm_probe_mfma_i8(iters, wgs, sink.data_ptr(), st) == 0
         b.record()
         torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps * 1e3   # us
+        us = a.elapsed_time(b) * 1e3 / 3
+        tops = 2.0 * 32 * 32 * 32 * 4 * iters * wgs * 4 / us / 1e6
+        best = max(best, tops)
+    log(f"[bench] int8 MFMA probe: {best:.1f} TOPS")
+    return best
+
+
+def run_secondary(torch, np, qmm, synth, dev, log):
+    """Prefill and MoE shapes: int8 TOPS = 2*rows*k*columns / call time, as a fraction of the 5.0
+    POP/s datasheet peak and of the MFMA probe; % of roofline = max(bytes / 8 TB/s, ops / 5 POP/s) /
+    time with bytes = weights + q8_1 activations + fp32 outputs.  Each call is timed by two HIP
+    events (median, p10, p90 over the calls); weights rotate over copies totalling > 512 MB so
+    the 256 MB Infinity Cache cannot hold them (the MoE shapes also with one resident copy,
+    labelled warm)."""
+    res = []
+    mfma_tops = mfma_probe_tops(torch, dev, log)
+
+    def timed(fn, ncopies, calls):
+        # every rotated weight copy is touched before timing (first touches of a fresh buffer run
+        # ~10 % slower), so the timed calls see weights streamed from HBM at steady state
+        for r in range(ncopies):
+            fn(r)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+        for r, (a, b) in enumerate(ev):
+            a.record()
+            fn(r)
+            b.record()
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) * 1e3 for a, b in ev]   # us
+
+    def entry(name, smp, ops, nbytes, **extra):
+        us = pct(smp, 50)
+        tops = ops / us / 1e6
+        roof = max(nbytes / (HBM_PEAK_GBPS * 1e3), ops / (INT8_PEAK_TOPS * 1e6)) / us
+        e = {"case": name, "us": us, "us_p10": pct(smp, 10), "us_p90": pct(smp, 90), "TOPS": round(tops, 1),
+             "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4), "frac_of_mfma_probe": round(tops / mfma_tops, 4),
+             "frac_roofline": round(roof, 4), "bytes": int(nbytes)}
+        e.update(extra)
+        log(f"[bench] {name:40s} {us:9.1f} us {tops:8.1f} TOPS  {100 * roof:5.1f} % of roofline "
+            f"{' '.join(f'{k}={v}' for k, v in extra.items())}")
+        res.append(e)
+
+    def copies(w, target=600e6):
+        n = max(1, int(np.ceil(target / w.nbytes)))
+        base = torch.from_numpy(w).to(dev).reshape(-1)
+        rb = w.shape[-1] if w.ndim == 2 else 1
+        return [torch.roll(base, r * rb) for r in range(n)]
 
     for c in synth.PREFILL_CASES + synth.EXTRA_PREFILL_CASES:
         w, x = synth.make_dense(c)
-        nrot = max(1, int(np.ceil(512e6 / w.nbytes)))
-        ws_ = [torch.from_numpy(w).to(dev)] + [torch.roll(torch.from_numpy(w).to(dev), 1, 0) for _ in range(min(nrot, 8) - 1)]
+        ws_ = copies(w)
         xd = torch.from_numpy(x).to(dev)
         y = torch.empty((c["n"], c["rows"]), dtype=torch.float32, device=dev)
         wsb = qmm._workspace(qmm.matmul_workspace(c["qtype"], c["rows"], c["k"], c["n"]), dev)
-        us = timed(lambda r: qmm.matmul(ws_[r % len(ws_)], c["qtype"], c["rows"], c["k"], xd, out=y, ws=wsb),
-                   warm=2 * len(ws_))
+        smp = timed(lambda r: qmm.matmul(ws_[r % len(ws_)], c["qtype"], c["rows"], c["k"], xd, out=y, ws=wsb),
+                    len(ws_), max(20, 2 * len(ws_)))
         ops = 2.0 * c["rows"] * c["k"] * c["n"]
-        tops = ops / us / 1e6
-        res.append({"case": c["name"], "us": round(us, 1), "TOPS": round(tops, 1),
-                    "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4)})
-        log(f"[bench] {c['name']:36s} {us:9.1f} us {tops:8.1f} TOPS")
+        nbytes = w.nbytes + c["n"] * (c["k"] // 32) * 36 + c["n"] * c["rows"] * 4
+        entry(c["name"], smp, ops, nbytes, weight_copies=len(ws_))
         del ws_
     for c in synth.MOE_CASES[:3]:
         w, x, ids = synth.make_moe(c)
-        wd = torch.from_numpy(w).to(dev)
         xd, idd = torch.from_numpy(x).to(dev), torch.from_numpy(ids).to(dev)
         out = torch.empty((c["n_tok"], c["top_k"], c["rows"]), dtype=torch.float32, device=dev)
         wsb = qmm._workspace(qmm.matmul_id_workspace(c["qtype"], c["n_exp"], c["rows"], c["k"], c["n_tok"],
                                                      c["top_k"], c["x_per_tok"]), dev)
-        us = timed(lambda r: qmm.matmul_id(wd, c["qtype"], c["n_exp"], c["rows"], c["k"], xd, idd,
-                                           x_per_tok=c["x_per_tok"], out=out, ws=wsb), warm=8)
         ops = 2.0 * c["rows"] * c["k"] * c["n_tok"] * c["top_k"]
-        tops = ops / us / 1e6
-        res.append({"case": c["name"], "us": round(us, 1), "TOPS": round(tops, 1),
-                    "frac_int8_peak": round(tops / INT8_PEAK_TOPS, 4), "cache": "weights resident (warm)"})
-        log(f"[bench] {c['name']:36s} {us:9.1f} us {tops:8.1f} TOPS")
-        del wd
+        nx = c["n_tok"] * c["x_per_tok"]
+        nbytes = w.nbytes + nx * (c["k"] // 32) * 36 + c["n_tok"] * c["top_k"] * c["rows"] * 4
+        for cache in ("cold", "warm"):
+            wd = copies(w) if cache == "cold" else [torch.from_numpy(w).to(dev).reshape(-1)]
+            smp = timed(lambda r: qmm.matmul_id(wd[r % len(wd)], c["qtype"], c["n_exp"], c["rows"], c["k"], xd, idd,
+                                                x_per_tok=c["x_per_tok"], out=out, ws=wsb), max(8, len(wd)),
+                        max(20, 2 * len(wd)))
+            entry(c["name"], smp, ops, nbytes, cache="weights rotated over %d copies (%.0f MB)" % (
+                len(wd), len(wd) * w.nbytes / 1e6) if cache == "cold" else "weights resident (warm)")
+            del wd
     # gate/up products fused with SwiGLU (one call for both matrices)
     for c in synth.GLU_CASES:
         wg, wu, x, ids = synth.make_glu(c)
         xd = torch.from_numpy(x).to(dev)
         if c["kind"] == "dense":
-            nrot = max(1, min(8, int(np.ceil(512e6 / (2 * wg.nbytes)))))
-            gs = [torch.roll(torch.from_numpy(wg).to(dev), r, 0) for r in range(nrot)]
-            us_ = [torch.roll(torch.from_numpy(wu).to(dev), r, 0) for r in range(nrot)]
+            gs, us_ = copies(wg, 300e6), copies(wu, 300e6)
+            nrot = len(gs)
             y = torch.empty((c["n"], c["rows"]), dtype=torch.float32, device=dev)
             wsb = qmm._workspace(qmm.matmul_glu_workspace(c["qtype"], c["rows"], c["k"], c["n"]), dev)
-            us = timed(lambda r: qmm.matmul_glu(gs[r % nrot], us_[r % nrot], c["qtype"], c["rows"], c["k"], xd,
-                                                out=y, ws=wsb), warm=2 * nrot)
+            smp = timed(lambda r: qmm.matmul_glu(gs[r % nrot], us_[r % nrot], c["qtype"], c["rows"], c["k"], xd,
+                                                 out=y, ws=wsb), nrot, max(20, 2 * nrot))
             cols = c["n"]
             del gs, us_
+            extra = {}
+            if c["n"] <= 8:
+                gbs = 2.0 * wg.nbytes / pct(smp, 50) / 1e3
+                extra = {"GBps_weights": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBPS, 4)}
+            nbytes = 2 * wg.nbytes + cols * (c["k"] // 32) * 36 + cols * c["rows"] * 4
         else:
             wgd, wud = torch.from_numpy(wg).to(dev), torch.from_numpy(wu).to(dev)
             idd = torch.from_numpy(ids).to(dev)
             out = torch.empty((c["n_tok"], c["top_k"], c["rows"]), dtype=torch.float32, device=dev)
             wsb = qmm._workspace(qmm.matmul_id_glu_workspace(c["qtype"], c["n_exp"], c["rows"], c["k"], c["n_tok"],
                                                              c["top_k"]), dev)
-            us = timed(lambda r: qmm.matmul_id_glu(wgd, wud, c["qtype"], c["n_exp"], c["rows"], c["k"], xd, idd,
-                                                   out=out, ws=wsb), warm=8)
+            smp = timed(lambda r: qmm.matmul_id_glu(wgd, wud, c["qtype"], c["n_exp"], c["rows"], c["k"], xd, idd,
+                                                    out=out, ws=wsb), 8, 20)
             cols = c["n_tok"] * c["top_k"]
             del wgd, wud
-        ops = 2.0 * 2 * c["rows"] * c["k"] * cols
-        entry = {"case": c["name"], "us": round(us, 1), "TOPS": round(ops / us / 1e6, 1),
-                 "frac_int8_peak": round(ops / us / 1e6 / INT8_PEAK_TOPS, 4)}
-        if c["kind"] == "dense" and c["n"] <= 8:
-            gbs = 2.0 * wg.nbytes / us / 1e3
-            entry["GBps_weights"] = round(gbs, 1)
-            entry["frac_hbm"] = round(gbs / HBM_PEAK_GBPS, 4)
-        res.append(entry)
-        log(f"[bench] {c['name']:36s} {us:9.1f} us {ops / us / 1e6:8.1f} TOPS")
-    return res
+            extra = {"cache": "weights resident (warm)"}
+            nbytes = 2 * wg.nbytes + c["n_tok"] * (c["k"] // 32) * 36 + cols * c["rows"] * 4
+        entry(c["name"], smp, 2.0 * 2 * c["rows"] * c["k"] * cols, nbytes, **extra)
+    return {"mfma_probe_TOPS": round(mfma_tops, 1), "cases": res}
 
 
 def run_cpu_baseline(np, synth, cases, BB, BV, seconds, log):
@@ -501,9 +653,59 @@ def run_cpu_baseline(np, synth, cases, BB, BV, seconds, log):
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     gbps = step_bytes * nsteps / dt / 1e9
     log(f"[bench] cpu oracle: {nsteps} steps in {dt:.2f} s -> {gbps:.3f} GB/s on {cores} threads")
+    # one thread, in a child process (the OpenMP thread count is fixed when the oracle loads)
+    import subprocess
+    single = None
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-single"], capture_output=True, text=True,
+                       env=dict(os.environ, OMP_NUM_THREADS="1"), timeout=600)
+    if r.returncode == 0 and r.stdout.strip():
+        single = json.loads(r.stdout.strip().splitlines()[-1])
+        log(f"[bench] cpu oracle, one thread: {single}")
     return {"value": round(gbps, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"{nsteps} whole steps of the same 12-call workload ({dt:.1f} s), weights from rotation 0",
-            "ms_per_step": round(dt / nsteps * 1e3, 2)}
+            "ms_per_step": round(dt / nsteps * 1e3, 2), "cpu_model": cpu_model(), "host_threads": os.cpu_count(),
+            "single_thread": single}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_single_thread():
+    """The oracle on one thread (OMP_NUM_THREADS=1 set by the parent): the small dense workload
+    (Q4_K 512 x 1024 x 16 tokens) and one whole matrix-vector step (the 12 calls); ms and GB/s."""
+    import numpy as np  # noqa: F401
+    import oracle
+    import synth
+    BB = {2: 18, 8: 34, 12: 144, 13: 176, 14: 210}
+    BV = {2: 32, 8: 32, 12: 256, 13: 256, 14: 256}
+    c = synth.DENSE_SMALL
+    w, x = synth.make_dense(c)
+    t0 = time.perf_counter()
+    reps = 20
+    for _ in range(reps):
+        oracle.matmul(c["qtype"], w, c["rows"], c["k"], x)
+    small_ms = (time.perf_counter() - t0) * 1e3 / reps
+    small_b = algo_bytes(c["qtype"], c["rows"], c["k"], c["n"], BB, BV)
+    data = []
+    for i, cc in enumerate(synth.MMVQ_CASES):
+        data.append((cc, synth.gen_weights(cc["qtype"], cc["rows"], cc["k"], synth.rngs(i, 1)[0]),
+                     synth.gen_activations(cc["n"], cc["k"], synth.rngs(7 + i, 1)[0])))
+    t0 = time.perf_counter()
+    for cc, ww, xx in data:
+        oracle.matmul(cc["qtype"], ww, cc["rows"], cc["k"], xx)
+    step_ms = (time.perf_counter() - t0) * 1e3
+    step_b = sum(algo_bytes(cc["qtype"], cc["rows"], cc["k"], cc["n"], BB, BV) for cc, _, _ in data)
+    print(json.dumps({"threads": 1, "dense_small_ms": round(small_ms, 3),
+                      "dense_small_GBps": round(small_b / small_ms / 1e6, 4),
+                      "matvec_step_ms": round(step_ms, 1), "matvec_step_GBps": round(step_b / step_ms / 1e6, 4)}))
 
 
 if __name__ == "__main__":

@@ -26,6 +26,20 @@ def test_library_exports_every_header_symbol():
         assert hasattr(qmm.lib(), s)
 
 
+def test_probe_library_exports_its_header():
+    """The benchmark's measurement probes (include/qmm_probe.h) live in their own library."""
+    import os
+    import re
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    with open(os.path.join(root, "include", "qmm_probe.h")) as f:
+        declared = sorted(set(re.findall(r"\b(qmm_[a-z0-9_]+)\s*\(", f.read())))
+    assert declared == ["qmm_probe_mfma_i8", "qmm_probe_read"]
+    lib = os.path.join(os.path.dirname(qmm.LIB_PATH), "libqmm_probe.so")
+    out = subprocess.run(["nm", "-D", "--defined-only", lib], capture_output=True, text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert set(declared) <= exported
+
+
 def test_version_string():
     assert "gfx950" in qmm.version()
 
