@@ -69,6 +69,14 @@ def lib():
         L.oracle_f16act_encode.restype = i32
         L.oracle_matmul_f16act.argtypes = [i32, vp, i64, i64, vp, i64, vp]
         L.oracle_matmul_f16act.restype = i32
+        L.oracle_panel_bytes.argtypes = [i32, i64, i64]
+        L.oracle_panel_bytes.restype = i64
+        L.oracle_panel_offset.argtypes = [i32, i32, i32]
+        L.oracle_panel_offset.restype = i64
+        L.oracle_repack_panels.argtypes = [i32, vp, i64, i64, vp]
+        L.oracle_repack_panels.restype = i32
+        L.oracle_dequantize_panels.argtypes = [i32, vp, i64, i64, vp]
+        L.oracle_dequantize_panels.restype = i32
         _lib = L
     return _lib
 
@@ -247,3 +255,34 @@ def matmul_f16act(qtype, w, rows, k, x):
     if lib().oracle_matmul_f16act(qtype, _ptr(w), rows, k, _ptr(x), n, _ptr(y)):
         raise ValueError("oracle_matmul_f16act: bad arguments")
     return y
+
+
+def panel_bytes(qtype, rows, k):
+    """Bytes of the panel layout of a [rows, k] matrix (-1: type or shape not supported)."""
+    return int(lib().oracle_panel_bytes(qtype, rows, k))
+
+
+def panel_offset(qtype, i, o):
+    """Offset inside a panel of byte o of row i's 256-value step (-1: out of range)."""
+    return int(lib().oracle_panel_offset(qtype, i, o))
+
+
+def repack_panels(qtype, w, rows, k):
+    """Original blocks [rows, row_bytes] -> panel layout (uint8, flat)."""
+    w = _c(w, np.uint8)
+    nb = panel_bytes(qtype, rows, k)
+    if nb < 0:
+        raise ValueError("repack_panels: type or shape not supported")
+    out = np.zeros(nb, dtype=np.uint8)
+    if lib().oracle_repack_panels(qtype, _ptr(w), rows, k, _ptr(out)):
+        raise ValueError("oracle_repack_panels: bad arguments")
+    return out
+
+
+def dequantize_panels(qtype, wp, rows, k):
+    """Panel layout -> fp64 values [rows, k]."""
+    wp = _c(wp, np.uint8)
+    out = np.zeros((rows, k), dtype=np.float64)
+    if lib().oracle_dequantize_panels(qtype, _ptr(wp), rows, k, _ptr(out)):
+        raise ValueError("oracle_dequantize_panels: bad arguments")
+    return out

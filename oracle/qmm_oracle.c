@@ -636,3 +636,106 @@ int oracle_matmul_f16act(int type, const uint8_t *w, int64_t rows, int64_t k, co
     free(wr);
     return rc;
 }
+
+/* ---------------------------------------------------------------------------------------------
+ * Panel layout: a one-time repack of a weight matrix ("QTensor and QMatMul" page, section on the
+ * 8-column Q4K repack: the blocks of adjacent rows at the same position are interleaved once, on
+ * first use, into a layout the product reads faster; the original blocks are kept).  This
+ * library's layout takes 16 rows and one 256-value step at a time and splits codes from scales:
+ *
+ *   k % 256 == 0.  G = ceil(rows / 16) row groups, S = k / 256 steps, B = bytes of 256 values in
+ *   the original layout (Q4_K 144, Q5_K 176, Q6_K 210, Q8_0 272, Q4_0 144), P = 16 * B.
+ *   Panel (g, s) -- rows 16g..16g+15, values 256s..256s+255 -- is the P bytes at (g*S + s) * P.
+ *   Inside a panel, slab j is the 256 bytes at 256*j: one 16-byte piece for each of the 16 rows,
+ *   row i's piece at 256*j + 16*i.  Slabs per type (byte ranges of the row's step in the
+ *   original layout):
+ *     Q4_K  slabs 0-7: qs[16j, 16j+16);   slab 8: header {d, dmin, scales[12]}
+ *     Q5_K  slabs 0-1: qh[16j, +16);      slabs 2-9: qs[16(j-2), +16);  slab 10: header
+ *     Q6_K  slabs 0-7: ql[16j, +16);      slabs 8-11: qh[16(j-8), +16); slab 12: scales[16];
+ *           then 32 bytes: fp16 d of row i at 3328 + 2i
+ *     Q8_0  slab j (0-15): qs[16(j%2), +16) of block j/2 of the step;  slab 16: the 8 blocks'
+ *           fp16 d, block b at byte 2b of the row's piece
+ *     Q4_0  slab j (0-7): qs[16] (nibbles) of block j;  slab 8: the 8 blocks' fp16 d as Q8_0
+ *   Rows of the last group past `rows` are zero bytes.  Every byte of the original is copied
+ *   unchanged (no value is re-encoded), so decoding a panel gives the original values.
+ * ------------------------------------------------------------------------------------------- */
+static int panel_step_bytes(int type) {
+    if (type == ORC_Q4_K || type == ORC_Q4_0) return 144;
+    if (type == ORC_Q5_K) return 176;
+    if (type == ORC_Q6_K) return 210;
+    if (type == ORC_Q8_0) return 272;
+    return 0;
+}
+
+/* Offset inside a panel of byte o (0 <= o < B) of row i's step (original layout). */
+static int64_t panel_offset(int type, int i, int o) {
+    switch (type) {
+        case ORC_Q4_K:
+            if (o < 16) return 8 * 256 + 16 * i + o;
+            return (o - 16) / 16 * 256 + 16 * i + (o - 16) % 16;
+        case ORC_Q5_K:
+            if (o < 16) return 10 * 256 + 16 * i + o;
+            if (o < 48) return (o - 16) / 16 * 256 + 16 * i + (o - 16) % 16;
+            return (2 + (o - 48) / 16) * 256 + 16 * i + (o - 48) % 16;
+        case ORC_Q6_K:
+            if (o < 128) return o / 16 * 256 + 16 * i + o % 16;
+            if (o < 192) return (8 + (o - 128) / 16) * 256 + 16 * i + (o - 128) % 16;
+            if (o < 208) return 12 * 256 + 16 * i + (o - 192);
+            return 13 * 256 + 2 * i + (o - 208);
+        case ORC_Q8_0: {
+            const int b = o / 34, q = o % 34;
+            if (q < 2) return 16 * 256 + 16 * i + 2 * b + q;
+            return (2 * b + (q - 2) / 16) * 256 + 16 * i + (q - 2) % 16;
+        }
+        case ORC_Q4_0: {
+            const int b = o / 18, q = o % 18;
+            if (q < 2) return 8 * 256 + 16 * i + 2 * b + q;
+            return b * 256 + 16 * i + (q - 2);
+        }
+        default:
+            return -1;
+    }
+}
+
+int64_t oracle_panel_bytes(int type, int64_t rows, int64_t k) {
+    const int B = panel_step_bytes(type);
+    if (B == 0 || rows < 1 || k < 256 || k % 256) return -1;
+    return (rows + 15) / 16 * (k / 256) * 16 * B;
+}
+
+/* Offset inside a panel of byte o of row i's step: exposed for the layout pins. */
+int64_t oracle_panel_offset(int type, int i, int o) {
+    const int B = panel_step_bytes(type);
+    if (B == 0 || i < 0 || i > 15 || o < 0 || o >= B) return -1;
+    return panel_offset(type, i, o);
+}
+
+/* Original layout w [rows][k] -> panel layout out (oracle_panel_bytes bytes). */
+int oracle_repack_panels(int type, const uint8_t *w, int64_t rows, int64_t k, uint8_t *out) {
+    const int64_t total = oracle_panel_bytes(type, rows, k);
+    if (total < 0) return ORC_ERR;
+    const int64_t B = panel_step_bytes(type), S = k / 256, P = 16 * B, rb = oracle_row_bytes(type, k);
+    memset(out, 0, (size_t)total);
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t s = 0; s < S; ++s)
+            for (int o = 0; o < B; ++o)
+                out[(r / 16 * S + s) * P + panel_offset(type, (int)(r % 16), o)] = w[r * rb + s * B + o];
+    return ORC_OK;
+}
+
+/* Panel layout -> fp64 values [rows][k]: each row's steps are read back from their panel
+ * positions into the original byte order and decoded with the definitions above. */
+int oracle_dequantize_panels(int type, const uint8_t *wp, int64_t rows, int64_t k, double *out) {
+    if (oracle_panel_bytes(type, rows, k) < 0) return ORC_ERR;
+    const int64_t B = panel_step_bytes(type), S = k / 256, P = 16 * B, rb = oracle_row_bytes(type, k);
+    uint8_t *row = (uint8_t *)malloc((size_t)rb);
+    if (!row) return ORC_ERR;
+    int rc = ORC_OK;
+    for (int64_t r = 0; r < rows && !rc; ++r) {
+        for (int64_t s = 0; s < S; ++s)
+            for (int o = 0; o < B; ++o) row[s * B + o] = wp[(r / 16 * S + s) * P + panel_offset(type, (int)(r % 16), o)];
+        rc = oracle_dequantize(type, row, 1, k, out + r * k);
+    }
+    free(row);
+    return rc;
+}
