@@ -31,9 +31,8 @@ Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu] [--no-seco
 Profile summaries (no GPU; read the SQLite databases rocprofv3 writes under -d DIR):
   python bench.py --summarize-trace DIR          per-kernel durations of a --kernel-trace run
   python bench.py --summarize-counters DIR       per-kernel, per-launch-shape averages of the
-                 counters of a --pmc run, with the matrix-pipe busy fraction
-                 (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * SIMDs)), vector-ALU activity
-                 (SQ_ACTIVE_INST_VALU / SQ_BUSY_CU_CYCLES) and int8 MFMA ops (MOPS_I8 * 512)
+                 counters of a --pmc run, with rocprofv3's derived MfmaUtil and VALUBusy and the
+                 int8 MFMA ops (MOPS_I8 * 512)
   python bench.py --summarize-pmc FDIR WDIR [--write-traffic]
                  per-kernel FETCH_SIZE / WRITE_SIZE of two --pmc runs of `bench.py --calib-copy`,
                  scaled to bytes by the 256 MiB device copy (tiled and grouping kernels get one
@@ -417,7 +416,12 @@ def summarize_trace(d):
               f"{min(ds):9.3f} {max(ds):9.3f} {sum(ds) / 1e3:9.3f}")
 
 
-def summarize_counters(d, simds=1024):
+def summarize_counters(d, cus=256, simds=1024, xcds=8, clock_ghz=2.4):
+    """Per kernel and launch shape: the average of each counter over the dispatches, and rocprofv3's
+    derived metrics MfmaUtil = sum(SQ_VALU_MFMA_BUSY_CYCLES) / (max(GRBM_GUI_ACTIVE) * SIMDs) and
+    VALUBusy = sum(SQ_ACTIVE_INST_VALU) / CUs / max(GRBM_GUI_ACTIVE).  The database holds counters
+    summed over their instances; GRBM_GUI_ACTIVE is counted once per XCD, so its max over the 8 XCDs
+    (all busy for the whole dispatch) is the stored sum / 8."""
     import statistics
     con = _rocpd(d)
     rows = con.execute("select kernel_name, grid_size, counter_name, value from counters_collection").fetchall()
@@ -425,18 +429,20 @@ def summarize_counters(d, simds=1024):
     for name, grid, cname, value in rows:
         by.setdefault((_short(name), grid), {}).setdefault(cname, []).append(value)
     names = sorted({c for v in by.values() for c in v})
-    print("| kernel | grid (threads) | dispatches | " + " | ".join(names) + " | MFMA busy | VALU active | int8 ops |")
-    print("|---|---|---|" + "---|" * len(names) + "---|---|---|")
+    print("| kernel | grid (threads) | dispatches | " + " | ".join(names) +
+          " | busy us | MfmaUtil | VALUBusy | int8 ops |")
+    print("|---|---|---|" + "---|" * len(names) + "---|---|---|---|")
     for (k, grid), cs in sorted(by.items()):
         avg = {c: statistics.mean(v) for c, v in cs.items()}
         disp = max(len(v) for v in cs.values())
-        mfma = avg.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) / (avg.get("GRBM_GUI_ACTIVE", 0) * simds) \
-            if avg.get("GRBM_GUI_ACTIVE") else None
-        valu = avg.get("SQ_ACTIVE_INST_VALU", 0) / avg["SQ_BUSY_CU_CYCLES"] if avg.get("SQ_BUSY_CU_CYCLES") else None
+        gui = avg.get("GRBM_GUI_ACTIVE", 0) / xcds
+        mfma = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * simds) if gui and "SQ_VALU_MFMA_BUSY_CYCLES" in avg else None
+        valu = avg["SQ_ACTIVE_INST_VALU"] / cus / gui if gui and "SQ_ACTIVE_INST_VALU" in avg else None
         ops = avg.get("SQ_INSTS_VALU_MFMA_MOPS_I8", 0) * 512
         fmt = lambda v: "-" if v is None else f"{100 * v:.1f} %"
+        busy = f"{gui / (clock_ghz * 1e3):.1f}" if gui else "-"
         print(f"| `{k[:60]}` | {grid} | {disp} | " + " | ".join(f"{avg.get(c, 0):.4g}" for c in names) +
-              f" | {fmt(mfma)} | {fmt(valu)} | {ops:.4g} |")
+              f" | {busy} | {fmt(mfma)} | {fmt(valu)} | {ops:.4g} |")
 
 
 def summarize_pmc(fdir, wdir, write=False):

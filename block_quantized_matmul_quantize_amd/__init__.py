@@ -62,6 +62,10 @@ _sig("qmm_matmul_f16act_workspace", _sz, _i64, _i64)
 _sig("qmm_matmul_f16act", _i32, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _sz, _vp)
 _sig("qmm_matmul", _i32, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _sz, _vp)
 _sig("qmm_matmul_noalloc", _i32, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _vp)
+_sig("qmm_repack_bytes", ctypes.c_uint64, _i32, _i64, _i64)
+_sig("qmm_repack", _i32, _i32, _vp, _i64, _i64, _vp, ctypes.c_uint64, _vp)
+_sig("qmm_matmul_packed_workspace", _sz, _i32, _i64, _i64, _i64)
+_sig("qmm_matmul_packed", _i32, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _sz, _vp)
 _sig("qmm_matmul_q8_1_workspace", _sz, _i32, _i64, _i64, _i64)
 _sig("qmm_matmul_q8_1", _i32, _i32, _vp, _i64, _i64, _vp, _i64, _vp, _vp, _sz, _vp)
 _sig("qmm_matmul_id_workspace", _sz, _i32, _i64, _i64, _i64, _i64, _i64, _i64)
@@ -261,6 +265,53 @@ def matmul(w, qtype, rows, k, x, out=None, ws=None):
         ws = _workspace(nbytes, x.device)
     _on_device(w=w, x=x, out=out, ws=ws)
     _check(_L.qmm_matmul(qtype, pw, rows, k, px, n, py, ctypes.c_void_p(ws.data_ptr()), ws.numel(), _stream()))
+    return out
+
+
+def repack_bytes(qtype, rows, k):
+    """Bytes of the panel layout of a [rows, k] matrix (0: type or shape not supported)."""
+    return int(_L.qmm_repack_bytes(qtype, rows, k))
+
+
+def repack(w, qtype, rows, k, out=None):
+    """One-time repack of original blocks w into the panel layout (uint8 tensor on w's device)."""
+    torch = _torch()
+    pw = _need(w, torch.uint8, "w")
+    _need_weights(w, qtype, rows, k, "w")
+    nb = repack_bytes(qtype, rows, k)
+    if out is None:
+        out = torch.empty(max(nb, 16), dtype=torch.uint8, device=w.device)
+    pp = _need(out, torch.uint8, "out")
+    _on_device(w=w, out=out)
+    _check(_L.qmm_repack(qtype, pw, rows, k, pp, out.numel(), _stream()))
+    return out
+
+
+def matmul_packed_workspace(qtype, rows, k, n):
+    return int(_L.qmm_matmul_packed_workspace(qtype, rows, k, n))
+
+
+def matmul_packed(wp, qtype, rows, k, x, out=None, ws=None):
+    """matmul with the weights in the panel layout (from repack)."""
+    torch = _torch()
+    pw = _need(wp, torch.uint8, "wp")
+    px = _need(x, torch.float32, "x")
+    if x.dim() != 2 or x.shape[1] != k:
+        raise ValueError(f"x must be [n, {k}]")
+    n = x.shape[0]
+    need = repack_bytes(qtype, rows, k)
+    if need:
+        _need_size(wp, need, "wp")
+    if out is None:
+        out = torch.empty((n, rows), dtype=torch.float32, device=x.device)
+    py = _need(out, torch.float32, "out")
+    _need_size(out, n * rows * 4, "out")
+    nbytes = matmul_packed_workspace(qtype, rows, k, n)
+    if ws is None:
+        ws = _workspace(nbytes, x.device)
+    _on_device(wp=wp, x=x, out=out, ws=ws)
+    _check(_L.qmm_matmul_packed(qtype, pw, rows, k, px, n, py, ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                                _stream()))
     return out
 
 

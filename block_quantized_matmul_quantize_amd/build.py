@@ -18,7 +18,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libqmm.so")
 PROBE_LIB = os.path.join(HERE, "libqmm_probe.so")   # measurement probes for bench.py (include/qmm_probe.h)
 SOURCES = ["quantize.hip", "mmvq.hip", "mmvq_stream.hip", "mmvq_dot4.hip", "mmq.hip", "moe.hip", "f16act.hip",
-           "noalloc.hip", "api.cpp"]
+           "noalloc.hip", "repack.hip", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -297,12 +297,12 @@ DenseWs dense_layout_exact(int64_t k, int64_t n, const qmm_plan &p) {
 // stream-K included, with only its epilogue changed; y is not written).
 qmm_status run_dense(int type, const void *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y,
                      uint8_t *ws, const DenseWs &L, int32_t *dbg, const qmm::Ovr &o, hipStream_t s,
-                     bool x_tiled = false) {
+                     bool x_tiled = false, bool packed = false) {
     hipError_t e;
     const qmm_plan p = plan_dense_impl(type, rows, k, n, device_cus(), o);
     const bool tiled_ws = L.tiled_off != L.part_off;   // the layout reserved the tiled copy
     if (p.regime == 1) {
-        if (x_tiled) return fail(QMM_ERR_ARG, "internal: tiled activations on the matrix-vector path");
+        if (x_tiled || packed) return fail(QMM_ERR_ARG, "internal: tiled activations or panel weights on the matrix-vector path");
         e = qmm::launch_mmvq(type, (const uint8_t *)w, rows, k, xq, n, y, dbg, nullptr, 0, o, s);
         if (e != hipSuccess) return hip_fail(e, "matrix-vector kernel launch");
         return QMM_OK;
@@ -316,6 +316,7 @@ qmm_status run_dense(int type, const void *w, int64_t rows, int64_t k, const uin
     ml.units = p.units;
     ml.stream_k = p.stream_k != 0;
     ml.partials = (float *)(ws + L.part_off);
+    ml.packed = packed;
     if (ml.stream_k && (size_t)(L.part_off + (size_t)ml.units * 2 * kTI * p.tile_j * 4) > L.total)
         return fail(QMM_ERR_WORKSPACE, "internal: stream-K partials exceed the workspace");
     const uint8_t *xa = xq;
@@ -490,6 +491,77 @@ qmm_status qmm_matmul_q8_1(int type, const void *w, int64_t rows, int64_t k, con
         return fail(QMM_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", ws_bytes, L.total);
     if (((uintptr_t)ws) & 255) return fail(QMM_ERR_ARG, "workspace must be 256-byte aligned");
     return run_dense(type, w, rows, k, (const uint8_t *)xq, n, y, (uint8_t *)ws, L, nullptr, o, (hipStream_t)stream);
+}
+
+// ----------------------------------------------------------------------------------------------
+// Panel layout: one-time weight repack and the dense product that reads it
+// ----------------------------------------------------------------------------------------------
+namespace {
+
+qmm_status check_panel_shape(int type, int64_t rows, int64_t k) {
+    if (block_values(type) == 0)
+        return fail(QMM_ERR_TYPE, "unsupported weight type %d (supported: Q4_0=2, Q8_0=8, Q4_K=12, Q5_K=13, Q6_K=14)", type);
+    if (rows <= 0) return fail(QMM_ERR_ARG, "rows must be >= 1 (got %lld)", (long long)rows);
+    if (k <= 0 || k % 256 != 0)
+        return fail(QMM_ERR_SHAPE, "the panel layout needs k a positive multiple of 256 (got %lld)", (long long)k);
+    if (k > kMaxK) return fail(QMM_ERR_SHAPE, "k=%lld exceeds the supported maximum %lld", (long long)k, (long long)kMaxK);
+    if (rows > (1ll << 31)) return fail(QMM_ERR_SHAPE, "rows too large");
+    return QMM_OK;
+}
+
+}  // namespace
+
+uint64_t qmm_repack_bytes(int type, int64_t rows, int64_t k) {
+    if (block_values(type) == 0 || rows <= 0 || rows > (1ll << 31) || k <= 0 || k % 256 != 0 || k > kMaxK) return 0;
+    return (uint64_t)qmm::panel_bytes(type, rows, k);
+}
+
+qmm_status qmm_repack(int type, const void *w, int64_t rows, int64_t k, void *wp, uint64_t wp_bytes, void *stream) {
+    qmm_status st = check_panel_shape(type, rows, k);
+    if (st) return st;
+    if (!w || !wp) return fail(QMM_ERR_ARG, "null w or wp");
+    if (((uintptr_t)w) & 1) return fail(QMM_ERR_ARG, "w must be 2-byte aligned");
+    if (((uintptr_t)wp) & 15) return fail(QMM_ERR_ARG, "wp must be 16-byte aligned");
+    const uint64_t need = (uint64_t)qmm::panel_bytes(type, rows, k);
+    if (wp_bytes < need)
+        return fail(QMM_ERR_ARG, "wp holds %llu bytes, the panel layout needs %llu", (unsigned long long)wp_bytes,
+                    (unsigned long long)need);
+    hipError_t e = qmm::launch_repack_panels(type, (const uint8_t *)w, rows, k, (uint8_t *)wp, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "repack launch");
+    return QMM_OK;
+}
+
+size_t qmm_matmul_packed_workspace(int type, int64_t rows, int64_t k, int64_t n) {
+    if (check_common(type, rows, k, n) || k % 256 != 0) return 0;
+    return dense_layout(type, rows, k, n, false, load_ovr()).total;
+}
+
+qmm_status qmm_matmul_packed(int type, const void *wp, int64_t rows, int64_t k, const float *x, int64_t n, float *y,
+                             void *ws, size_t ws_bytes, void *stream) {
+    const qmm::Ovr o = load_ovr();
+    qmm_status st = check_panel_shape(type, rows, k);
+    if (st) return st;
+    if ((st = check_plan_args(type, rows, k, n, o))) return st;
+    if ((st = check_ptrs_dense(wp, x, y, n))) return st;
+    if (n == 0) return QMM_OK;
+    if (((uintptr_t)wp) & 15) return fail(QMM_ERR_ARG, "wp must be 16-byte aligned");
+    if (((uintptr_t)x) & 15) return fail(QMM_ERR_ARG, "x must be 16-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    const qmm_plan p = plan_dense_impl(type, rows, k, n, device_cus(), o);
+    if (p.regime == 1) {
+        // few columns: the LDS-staged kernel quantizes x itself and parks each panel as it is
+        hipError_t e = qmm::launch_mmvq_stream_panel_f32(type, (const uint8_t *)wp, rows, k, x, n, y, s);
+        if (e != hipSuccess) return hip_fail(e, "panel matrix-vector kernel launch");
+        return QMM_OK;
+    }
+    const DenseWs L = dense_layout(type, rows, k, n, false, o);
+    if (L.total > 0 && (!ws || ws_bytes < L.total))
+        return fail(QMM_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", ws_bytes, L.total);
+    if (((uintptr_t)ws) & 255) return fail(QMM_ERR_ARG, "workspace must be 256-byte aligned");
+    uint8_t *wsb = (uint8_t *)ws;
+    hipError_t e = qmm::launch_quantize_q8_1_tiled(x, n, k, wsb + L.tiled_off, nullptr, s);
+    if (e != hipSuccess) return hip_fail(e, "quantize launch");
+    return run_dense(type, wp, rows, k, wsb + L.tiled_off, n, y, wsb, L, nullptr, o, s, true, true);
 }
 
 // ----------------------------------------------------------------------------------------------

@@ -105,6 +105,7 @@ struct MmqLaunch {
     int64_t units;       // workgroups (== ntiles unless stream-K)
     bool stream_k;
     float *partials;     // [units][2][128*tile_j] when stream_k
+    bool packed = false; // w in the panel layout (repack.hip), k % 256 == 0
 };
 hipError_t launch_mmq(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n,
                       float *y, int32_t *dbg, const MmqLaunch &plan, hipStream_t s);
@@ -121,6 +122,15 @@ hipError_t launch_mmq_id(int type, const uint8_t *w, const uint8_t *w_up, int64_
 hipError_t launch_moe_group(const int32_t *ids, int64_t pairs, int32_t n_exp, int32_t tile_j,
                             int32_t small_max, int32_t *sorted, int32_t *bounds, int32_t *tile_start,
                             int32_t *small, int32_t *invalid, hipStream_t s);
+
+// Panel layout (repack.hip): bytes of the layout for a [rows][k] matrix (-1: type or shape not
+// supported), and the one-time repack of the original blocks w into wp (16-byte aligned).
+int64_t panel_bytes(int type, int64_t rows, int64_t k);
+hipError_t launch_repack_panels(int type, const uint8_t *w, int64_t rows, int64_t k, uint8_t *wp, hipStream_t s);
+// Dense products reading panel-layout weights: n <= 8 fp32 columns (the LDS-staged kernel, which
+// quantizes x itself; x 16-byte aligned), and the tiled kernel (plan.packed set).
+hipError_t launch_mmvq_stream_panel_f32(int type, const uint8_t *wp, int64_t rows, int64_t k, const float *x, int64_t n,
+                                        float *y, hipStream_t s);
 
 // fp16-activation mode (f16act.hip)
 hipError_t launch_f16act_encode(const float *x, int64_t n, int64_t k, uint16_t *y16, int32_t *e, float *bsum,

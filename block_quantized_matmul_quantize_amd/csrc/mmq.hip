@@ -172,6 +172,49 @@ template <bool GLU> struct WRows {
         r = r < rows ? r : rows - 1;
         return w0 + (GLU ? (int64_t)((t >> 3) & 1) * d01 : 0) + r * row_bytes;
     }
+    // Byte o of tile row t's 256-value step kb (o counts from the step's first byte in the row).
+    template <int T> __device__ __forceinline__ const uint8_t *at(int t, int64_t kb, int o) const {
+        return row(t) + kb * (kSuper / Fmt<T>::QK * Fmt<T>::BYTES) + o;
+    }
+};
+
+// ---------------------------------------------------------------------------------------------
+// Weight rows in the panel layout (repack.hip): rows 16g..16g+15 x values 256s..256s+255 are the
+// 16*B contiguous bytes of panel (g, s) at (g*nsteps + s) * 16*B; slab j (256 bytes at 256*j)
+// holds a 16-byte piece per row.  panel_off maps byte o of a row's step in the original layout to
+// its panel offset for row i of the group; every fetch below reads a run that stays inside one
+// piece (or, for the fp16 scales, one 2-byte unit), so the run is contiguous in both layouts.
+// ---------------------------------------------------------------------------------------------
+template <int T> __device__ __forceinline__ int panel_off(int o, int i) {
+    if constexpr (T == kQ4_K) {
+        return o < 16 ? 8 * 256 + 16 * i + o : ((o - 16) >> 4) * 256 + 16 * i + ((o - 16) & 15);
+    } else if constexpr (T == kQ5_K) {
+        return o < 16 ? 10 * 256 + 16 * i + o
+               : o < 48 ? ((o - 16) >> 4) * 256 + 16 * i + ((o - 16) & 15)
+                        : (2 + ((o - 48) >> 4)) * 256 + 16 * i + ((o - 48) & 15);
+    } else if constexpr (T == kQ6_K) {
+        return o < 192 ? (o >> 4) * 256 + 16 * i + (o & 15)   // ql: slabs 0-7, qh: slabs 8-11
+               : o < 208 ? 12 * 256 + 16 * i + (o - 192)
+                         : 13 * 256 + 2 * i + (o - 208);
+    } else if constexpr (T == kQ8_0) {
+        const int b = o / 34, q = o - 34 * b;
+        return q < 2 ? 16 * 256 + 16 * i + 2 * b + q : (2 * b + ((q - 2) >> 4)) * 256 + 16 * i + ((q - 2) & 15);
+    } else {   // Q4_0
+        const int b = o / 18, q = o - 18 * b;
+        return q < 2 ? 8 * 256 + 16 * i + 2 * b + q : b * 256 + 16 * i + (q - 2);
+    }
+}
+
+struct WPanels {
+    const uint8_t *w;
+    int64_t group_bytes;   // nsteps * panel bytes: one row group's panels
+    int64_t r0, rows;
+    template <int T> __device__ __forceinline__ const uint8_t *at(int t, int64_t kb, int o) const {
+        int64_t r = r0 + t;
+        r = r < rows ? r : rows - 1;   // rows past the end repeat the last row (never written out)
+        return w + (r >> 4) * group_bytes + kb * (16 * (kSuper / Fmt<T>::QK * Fmt<T>::BYTES)) +
+               panel_off<T>(o, (int)(r & 15));
+    }
 };
 
 // ---------------------------------------------------------------------------------------------
@@ -193,13 +236,13 @@ template <int T, int NT> struct WFetchK45 {
 #pragma unroll
         for (int it = 0; it < N; ++it) {
             const int i = tid + NT * it;
-            q[it] = ld16(wr.row(i >> 3) + kb * BB + QS + 16 * (i & 7));
+            q[it] = ld16(wr.template at<T>(i >> 3, kb, QS + 16 * (i & 7)));
         }
-        if (tid < kTI) h = ld16(wr.row(tid) + kb * BB);
+        if (tid < kTI) h = ld16(wr.template at<T>(tid, kb, 0));
 #pragma unroll
         for (int it = 0; it < NH; ++it) {
             const int i = tid + NT * it;
-            if (i < 256) qh[it] = ld16(wr.row(i >> 1) + kb * BB + 16 + 16 * (i & 1));
+            if (i < 256) qh[it] = ld16(wr.template at<T>(i >> 1, kb, 16 + 16 * (i & 1)));
         }
     }
     template <int J, class WR>
@@ -268,14 +311,15 @@ template <int NT> struct WFetch<kQ8_0, NT> {
 #pragma unroll
         for (int it = 0; it < NQ; ++it) {
             const int i = tid + NT * it;
-            const int64_t b = kb * 8 + ((i >> 1) & 7);
-            q[it] = b < nb32 ? ld16(wr.row(i >> 4) + b * 34 + 2 + 16 * (i & 1)) : u32x4{0u, 0u, 0u, 0u};
+            const int bs = (i >> 1) & 7;   // block within the step
+            const int64_t b = kb * 8 + bs;
+            q[it] = b < nb32 ? ld16(wr.template at<kQ8_0>(i >> 4, kb, 34 * bs + 2 + 16 * (i & 1))) : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int it = 0; it < ND; ++it) {
             const int i = tid + NT * it;
             const int64_t b = kb * 8 + (i & 7);
-            d[it] = b < nb32 ? ld2(wr.row(i >> 3) + b * 34) : (uint16_t)0;
+            d[it] = b < nb32 ? ld2(wr.template at<kQ8_0>(i >> 3, kb, 34 * (i & 7))) : (uint16_t)0;
         }
     }
     template <int J, class WR>
@@ -310,9 +354,8 @@ template <int NT> struct WFetch<kQ4_0, NT> {
         for (int it = 0; it < N; ++it) {
             const int i = tid + NT * it;   // (row i/8, block i%8)
             const int64_t b = kb * 8 + (i & 7);
-            const uint8_t *blk = wr.row(i >> 3) + b * 18;
-            q[it] = b < nb32 ? ld16(blk + 2) : u32x4{0u, 0u, 0u, 0u};
-            d[it] = b < nb32 ? ld2(blk) : (uint16_t)0;
+            q[it] = b < nb32 ? ld16(wr.template at<kQ4_0>(i >> 3, kb, 18 * (i & 7) + 2)) : u32x4{0u, 0u, 0u, 0u};
+            d[it] = b < nb32 ? ld2(wr.template at<kQ4_0>(i >> 3, kb, 18 * (i & 7))) : (uint16_t)0;
         }
     }
     // nibble - 8 as int8, four bytes at a time: (n + 120) has bit 7 set iff n >= 8, so flipping
@@ -369,11 +412,10 @@ template <int NT> struct WFetchQ6Direct {
             const int r = i >> 4, G = i & 15;
             uint32_t lo_w[4], hi_w[4];
             {
-                const uint8_t *blk = wr.row(r) + kb * 210;
                 const int hh = G >> 3, gq = (G & 7) >> 1, l0 = 16 * (G & 1);
-                const u32x4 ql = ld16(blk + 64 * hh + 32 * (gq & 1) + l0);
-                const u32x4 qh = ld16(blk + 128 + 32 * hh + l0);
-                const int sc = (int)(int8_t)blk[192 + G];
+                const u32x4 ql = ld16(wr.template at<kQ6_K>(r, kb, 64 * hh + 32 * (gq & 1) + l0));
+                const u32x4 qh = ld16(wr.template at<kQ6_K>(r, kb, 128 + 32 * hh + l0));
+                const int sc = (int)(int8_t)*wr.template at<kQ6_K>(r, kb, 192 + G);
                 const s16x2 sc2 = {(short)sc, (short)sc}, off2 = {(short)(-32 * sc), (short)(-32 * sc)};
                 const int nsh = gq < 2 ? 0 : 4, tsh = 2 * gq;
                 const uint32_t qlw[4] = {ql.x, ql.y, ql.z, ql.w}, qhw[4] = {qh.x, qh.y, qh.z, qh.w};
@@ -388,7 +430,7 @@ template <int NT> struct WFetchQ6Direct {
         }
         if (tid < kTI) {
             float *sWs = (float *)(sm + Smem<kQ6_K, J>::WS_OFF);
-            sWs[tid] = h2f(ld2(wr.row(tid) + kb * 210 + 208));
+            sWs[tid] = h2f(ld2(wr.template at<kQ6_K>(tid, kb, 208)));
         }
     }
 };
@@ -406,12 +448,11 @@ template <int NT> struct WFetchQ6Reg {
     __device__ __forceinline__ void fetch(const WR &wr, int64_t kb, int64_t) {
         const int u = threadIdx.x;
         const int r = u >> 2, hh = (u >> 1) & 1, l0 = 16 * (u & 1);
-        const uint8_t *blk = wr.row(r) + kb * 210;
-        ql0 = ld16(blk + 64 * hh + l0);
-        ql1 = ld16(blk + 64 * hh + 32 + l0);
-        qh = ld16(blk + 128 + 32 * hh + l0);
-        sc = ld16(blk + 192);
-        d = (u & 3) == 0 ? ld2(blk + 208) : (uint16_t)0;
+        ql0 = ld16(wr.template at<kQ6_K>(r, kb, 64 * hh + l0));
+        ql1 = ld16(wr.template at<kQ6_K>(r, kb, 64 * hh + 32 + l0));
+        qh = ld16(wr.template at<kQ6_K>(r, kb, 128 + 32 * hh + l0));
+        sc = ld16(wr.template at<kQ6_K>(r, kb, 192));
+        d = (u & 3) == 0 ? ld2(wr.template at<kQ6_K>(r, kb, 208)) : (uint16_t)0;
     }
     template <int J, class WR>
     __device__ __forceinline__ void store(uint8_t *sm, const WR &, int64_t, int64_t) const {
@@ -750,7 +791,8 @@ __device__ __forceinline__ void store_tile_glu(const f32x16 (&acc)[Cfg<J>::NCB],
 // ---------------------------------------------------------------------------------------------
 // Dense kernel: persistent over the unit's (tile, step) range.
 // ---------------------------------------------------------------------------------------------
-template <int T, int J, bool DBG>
+// PK: w in the panel layout (repack.hip).
+template <int T, int J, bool DBG, bool PK = false>
 __global__ __launch_bounds__(Cfg<J>::NT, 2) void mmq_kernel(const uint8_t *__restrict__ w, int64_t rows, int64_t k,
                                                          const uint8_t *__restrict__ xq, int64_t n,
                                                          float *__restrict__ y, int32_t *__restrict__ dbg,
@@ -784,8 +826,13 @@ __global__ __launch_bounds__(Cfg<J>::NT, 2) void mmq_kernel(const uint8_t *__res
 #pragma unroll
         for (int cb = 0; cb < Cfg<J>::NCB; ++cb) acc[cb] = f32x16{};
 
-        const WRows<false> wr{w, w, row_bytes, r0, rows};
-        run_tile<T, J, DBG>(sm, acc, wr, kb0, kb1, nb32, xq, acol, dbg, n, c0, n);
+        if constexpr (PK) {
+            const WPanels wr{w, args.k_iters * 16 * (kSuper / Fmt<T>::QK * Fmt<T>::BYTES), r0, rows};
+            run_tile<T, J, DBG>(sm, acc, wr, kb0, kb1, nb32, xq, acol, dbg, n, c0, n);
+        } else {
+            const WRows<false> wr{w, w, row_bytes, r0, rows};
+            run_tile<T, J, DBG>(sm, acc, wr, kb0, kb1, nb32, xq, acol, dbg, n, c0, n);
+        }
 
         if (!DBG) {
             const bool whole = kb0 == 0 && kb1 == args.k_iters;
@@ -981,12 +1028,12 @@ __global__ __launch_bounds__(Cfg<J>::NT, 2) void mmq_id_kernel(const uint8_t *__
 // ---------------------------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------------------------
-template <int T, int J, bool DBG>
+template <int T, int J, bool DBG, bool PK = false>
 static hipError_t launch_mmq_t(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y,
                                int32_t *dbg, const MmqLaunch &p, hipStream_t s) {
     MmqArgs a{p.ntiles, p.n_ct, p.k_iters, p.units, p.partials, p.stream_k ? 1 : 0};
     constexpr int smem = kSmemBytes<T, J>;
-    auto kern = mmq_kernel<T, J, DBG>;
+    auto kern = mmq_kernel<T, J, DBG, PK>;
     // once per process (a function-local static is initialised exactly once, thread-safely)
     static const hipError_t attr_err = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (attr_err != hipSuccess) return attr_err;
@@ -997,21 +1044,23 @@ static hipError_t launch_mmq_t(const uint8_t *w, int64_t rows, int64_t k, const 
     return hipGetLastError();
 }
 
-template <int T, bool DBG>
+template <int T, bool DBG, bool PK = false>
 static hipError_t launch_mmq_j(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y,
                                int32_t *dbg, const MmqLaunch &p, hipStream_t s) {
-    if (p.tile_j == 32) return launch_mmq_t<T, 32, DBG>(w, rows, k, xq, n, y, dbg, p, s);
-    if (p.tile_j == 64) return launch_mmq_t<T, 64, DBG>(w, rows, k, xq, n, y, dbg, p, s);
-    if (p.tile_j == 128) return launch_mmq_t<T, 128, DBG>(w, rows, k, xq, n, y, dbg, p, s);
+    if (p.tile_j == 32) return launch_mmq_t<T, 32, DBG, PK>(w, rows, k, xq, n, y, dbg, p, s);
+    if (p.tile_j == 64) return launch_mmq_t<T, 64, DBG, PK>(w, rows, k, xq, n, y, dbg, p, s);
+    if (p.tile_j == 128) return launch_mmq_t<T, 128, DBG, PK>(w, rows, k, xq, n, y, dbg, p, s);
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_mmq(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y,
                       int32_t *dbg, const MmqLaunch &p, hipStream_t s) {
     const bool d = dbg != nullptr;
+    if (p.packed && d) return hipErrorInvalidValue;   // no integer-dot export from panel weights
 #define QMM_MQ(TT)                                                                                    \
-    if (type == TT) return d ? launch_mmq_j<TT, true>(w, rows, k, xq, n, y, dbg, p, s)    \
-                             : launch_mmq_j<TT, false>(w, rows, k, xq, n, y, dbg, p, s);
+    if (type == TT) return p.packed ? launch_mmq_j<TT, false, true>(w, rows, k, xq, n, y, dbg, p, s)   \
+                           : d ? launch_mmq_j<TT, true>(w, rows, k, xq, n, y, dbg, p, s)               \
+                               : launch_mmq_j<TT, false>(w, rows, k, xq, n, y, dbg, p, s);
     QMM_MQ(kQ4_K)
     QMM_MQ(kQ5_K)
     QMM_MQ(kQ6_K)

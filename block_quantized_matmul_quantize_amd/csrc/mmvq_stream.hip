@@ -62,8 +62,18 @@ template <> struct Geo<kQ8_0> { static constexpr int PPR = 0, STEP = 272, RSTR =
 // Q4_0 (18-byte blocks {d, 16 nibble bytes}): loaded as 36-byte block pairs, parked as Q8_0's codes.
 template <> struct Geo<kQ4_0> { static constexpr int PPR = 0, STEP = 144, RSTR = 272, WD = 16 * 8 * 4; };
 
-template <int T> struct Stage {
-    static constexpr int WB = kRows * Geo<T>::RSTR + Geo<T>::WD;   // weights (+ Q8_0 scales)
+// Panel layout (repack.hip): the bytes of 16 rows x 256 values, parked in LDS as they are.
+// B: bytes of 256 values of a row (a panel is 16 * B bytes, B pieces).  HDR: the slab after the
+// code slabs (the K-quant header, the Q8_0 / Q4_0 fp16 scales); QS: the first qs slab (Q5_K's
+// qh comes first).
+template <int T> struct PanelGeo {
+    static constexpr int B = T == kQ5_K ? 176 : T == kQ6_K ? 210 : T == kQ8_0 ? 272 : 144;
+    static constexpr int HDR = B / 16 - 1, QS = T == kQ5_K ? 2 : 0;
+};
+
+template <int T, bool PK = false> struct Stage {
+    // weights (+ Q8_0 scales); panel layout: the panel itself (16 * B bytes)
+    static constexpr int WB = PK ? 16 * PanelGeo<T>::B : kRows * Geo<T>::RSTR + Geo<T>::WD;
     static constexpr int AB = 8 * 256;                             // activation codes: [column][block][32]
     static constexpr int FB = 64 * 8;                              // fp32 (d, s): [block][column]
     static constexpr int BYTES = WB + AB + FB;
@@ -109,12 +119,16 @@ struct MvArgs {
     int32_t n;            // dense column count
 };
 
-template <int T, bool DBG, bool EXPERT, bool F32, bool GLU>
+// PK: w is in the panel layout (repack.hip): workgroup b reads panels (b, s), each 16 * B
+// contiguous bytes fetched by lane-consecutive 16-byte loads and parked in LDS unchanged; the
+// operand reads below then address slabs (256 bytes, one 16-byte piece per row).
+template <int T, bool DBG, bool EXPERT, bool F32, bool GLU, bool PK = false>
 __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__restrict__ w, const uint8_t *__restrict__ w2,
                                                           const void *__restrict__ xin,
                                                           float *__restrict__ y, int32_t *__restrict__ dbg,
                                                           MvArgs P, ColMap cm) {
-    using S = Stage<T>;
+    static_assert(!PK || !(GLU || EXPERT || DBG), "the panel layout serves the dense product");
+    using S = Stage<T, PK>;
     constexpr int PPR = Geo<T>::PPR, RSTR = Geo<T>::RSTR, WB = S::WB, SB = S::BYTES;
     constexpr int A0 = WB, F0 = WB + S::AB;   // activation codes and (d, s) table within a stage
     constexpr int NCG = (T == kQ6_K) ? 2 : 1;
@@ -132,7 +146,8 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
     constexpr int RW = GLU ? kRows / 2 : kRows;   // outputs per workgroup
     const int64_t row0 = (int64_t)blockIdx.x * RW;
     const int rmax = (int)((rows - row0) < RW ? (rows - row0) : RW) - 1;   // last live output row of the group
-    const uint8_t *wg = mc.wbase + row0 * (int64_t)row_bytes;
+    constexpr int PB = 16 * PanelGeo<T>::B;   // panel bytes
+    const uint8_t *wg = PK ? w + (int64_t)blockIdx.x * P.nsteps * PB : mc.wbase + row0 * (int64_t)row_bytes;
     const uint8_t *wg2 = GLU ? mc.wbase2 + row0 * (int64_t)row_bytes : wg;   // up rows (GLU)
     uint8_t *zero = smem + (size_t)wave * (kHead + SB);   // zero block (off-diagonal A lanes)
     uint8_t *st = zero + kHead;                            // this wave's stage
@@ -161,8 +176,16 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
 
     u32x4 wv[4];
     uint32_t wv4 = 0;
+    // panel layout: load i covers pieces 64i..64i+63 of the panel; the last covers PLAST of them
+    constexpr int PN = (PanelGeo<T>::B + 63) / 64, PLAST = PanelGeo<T>::B - 64 * (PN - 1);
+    u32x4 pv[PK ? PN : 1];
     auto load_w = [&](int s) __attribute__((always_inline)) {
-        if constexpr (T == kQ8_0) {
+        if constexpr (PK) {
+            const uint8_t *src = wg + (uint32_t)(s * PB) + 16 * lane;
+#pragma unroll
+            for (int i = 0; i < PN; ++i)
+                if (i < PN - 1 || lane < PLAST) pv[i] = *(const u32x4 *)(src + 1024 * i);
+        } else if constexpr (T == kQ8_0) {
             const uint8_t *src = wg8 + (uint32_t)(s * 272) + wofs8;
 #pragma unroll
             for (int i = 0; i < 4; ++i) wv[i] = *(const u32x4_a4 *)(src + 16 * i);
@@ -272,7 +295,11 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
                 if (i < nic) *(u32x4 *)(st + acdst[i]) = av[i];
             *(float2 *)(st + asdst) = make_float2(h2f((uint16_t)(ads & 0xFFFF)), h2f((uint16_t)(ads >> 16)));
         }
-        if constexpr (kK45<T>) {
+        if constexpr (PK) {
+#pragma unroll
+            for (int i = 0; i < PN; ++i)
+                if (i < PN - 1 || lane < PLAST) *(u32x4 *)(st + 1024 * i + 16 * lane) = pv[i];
+        } else if constexpr (kK45<T>) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) *(u32x4 *)(st + pofs[i]) = wv[i];
         } else if constexpr (T == kQ6_K) {
@@ -394,9 +421,12 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
         if constexpr (kK45<T>) {
             constexpr int QS = T == kQ5_K ? 32 : 0;   // Q5_K: qs after qh[32]
             const uint8_t *wr = st + wrow;
-            const u32x4 hdr = lds16(wr);
-            const u32x4 src1 = lds16(wr + QS + 16 * (g ? g : 4));
-            const u32x4 src2 = lds16(wr + QS + 16 * (g ? 4 + g : 8));
+            // this lane's qs pieces: (g + 3) % 4 and 4 + (g + 3) % 4 of the row's eight
+            const int qa = (g + 3) & 3;
+            const u32x4 hdr = PK ? lds16(st + 256 * PanelGeo<T>::HDR + 16 * r16) : lds16(wr);
+            const u32x4 src1 = PK ? lds16(st + 256 * (PanelGeo<T>::QS + qa) + 16 * r16) : lds16(wr + QS + 16 + 16 * qa);
+            const u32x4 src2 = PK ? lds16(st + 256 * (PanelGeo<T>::QS + 4 + qa) + 16 * r16)
+                                  : lds16(wr + QS + 16 + 16 * (4 + qa));
             const int sel = g >> 1;
             const float d = h2f((uint16_t)(hdr.x & 0xFFFF));
             const float dmin = h2f((uint16_t)(hdr.x >> 16));
@@ -408,7 +438,7 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
             if constexpr (T == kQ5_K) {
                 // fifth bits: this lane's bytes are values 16*half.. of sub-blocks
                 // 2*group + (j&1) + 4*(j>>1); bit (sub-block) of qh bytes 16*half..
-                const u32x4 qh = lds16(wr + 16 + 16 * q4_half(g));
+                const u32x4 qh = PK ? lds16(st + 256 * q4_half(g) + 16 * r16) : lds16(wr + 16 + 16 * q4_half(g));
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int sbb = 2 * q4_group(g) + (j & 1) + 4 * (j >> 1);
@@ -442,12 +472,15 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
             }
         } else if constexpr (T == kQ6_K) {
             const uint8_t *wr = st + wrow;
-            const u32x4 ql0 = lds16(wr + 16 * g);
-            const u32x4 ql1 = lds16(wr + 64 + 16 * g);
-            const u32x4 qh0 = lds16(wr + 128 + 16 * (g & 1));   // qh of half 0 for this lane's l range
-            const u32x4 qh1 = lds16(wr + 160 + 16 * (g & 1));   // half 1
-            const u32x4 scv = lds16(wr + 192);
-            const float d = h2f(*(const uint16_t *)(wr + 208));
+            // original super-block bytes / panel slabs: ql pieces g and 4+g, qh pieces (g&1) and
+            // 2+(g&1), the 16 scales, d
+            const uint8_t *pr = st + 16 * r16;
+            const u32x4 ql0 = PK ? lds16(pr + 256 * g) : lds16(wr + 16 * g);
+            const u32x4 ql1 = PK ? lds16(pr + 256 * (4 + g)) : lds16(wr + 64 + 16 * g);
+            const u32x4 qh0 = PK ? lds16(pr + 256 * (8 + (g & 1))) : lds16(wr + 128 + 16 * (g & 1));   // half 0
+            const u32x4 qh1 = PK ? lds16(pr + 256 * (10 + (g & 1))) : lds16(wr + 160 + 16 * (g & 1));  // half 1
+            const u32x4 scv = PK ? lds16(pr + 256 * 12) : lds16(wr + 192);
+            const float d = h2f(PK ? *(const uint16_t *)(st + 13 * 256 + 2 * r16) : *(const uint16_t *)(wr + 208));
             const u32x4 neg32 = {0xE0E0E0E0u, 0xE0E0E0E0u, 0xE0E0E0E0u, 0xE0E0E0E0u};
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
@@ -488,10 +521,23 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
         } else {
             const uint8_t *wr = st + wrow;
             const float *wd = (const float *)(st + kRows * RSTR) + 8 * r16;
+            const uint16_t *wdh = (const uint16_t *)(st + 256 * PanelGeo<T>::HDR + 16 * r16);   // panel: fp16 d
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
                 const int blk = 2 * p + (g >> 1);
-                const u32x4 q = lds16(wr + 64 * p + 16 * g);
+                u32x4 q;
+                if constexpr (PK && T == kQ4_0) {
+                    // block blk's 16 nibble bytes; this lane's half (g & 1) of its 32 values as
+                    // int8 nibble - 8: (n + 120) ^ 0x80 per byte
+                    const u32x4 nb = lds16(st + 256 * blk + 16 * r16);
+                    const uint32_t sh = 4 * (g & 1);
+                    auto c4 = [sh](uint32_t v) { return (((v >> sh) & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u; };
+                    q = u32x4{c4(nb.x), c4(nb.y), c4(nb.z), c4(nb.w)};
+                } else if constexpr (PK) {
+                    q = lds16(st + 256 * (4 * p + g) + 16 * r16);
+                } else {
+                    q = lds16(wr + 64 * p + 16 * g);
+                }
                 const i32x4 D = mfma16x16x64(aop(0, p), q, zero4);
                 if (DBG) {
 #pragma unroll
@@ -500,7 +546,7 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
                         if (dbg_row && c < ncols) dbg_row[(int64_t)c * dbg_ld + s * 8 + blk] = D[e];
                     }
                 } else {
-                    const float ws = wd[blk];
+                    const float ws = PK ? h2f(wdh[blk]) : wd[blk];
                     const f32x4 t0 = *(const f32x4 *)(ftab + blk * 8 + 4 * (g & 1));
                     const f32x4 t1 = *(const f32x4 *)(ftab + blk * 8 + 4 * (g & 1) + 2);
                     acc[0][0] = fmaf((float)D[0], ws * t0.x, acc[0][0]);
@@ -555,12 +601,12 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
     if (c < ncols && row0 + rr < rows) y[mc.pair(c) * rows + row0 + rr] = GLU ? v / (1.0f + expf(-v)) * u : v;
 }
 
-template <int T, bool DBG, bool EXPERT, bool F32 = false, bool GLU = false>
+template <int T, bool DBG, bool EXPERT, bool F32 = false, bool GLU = false, bool PK = false>
 hipError_t launch_t(const uint8_t *w, int64_t rows, int64_t k, const void *xq, int64_t n, float *y,
                     int32_t *dbg, const ColMap &c, int64_t n_exp, hipStream_t s, const uint8_t *w2 = nullptr) {
     const int64_t nsteps = k / kSuper;
     const int nw = (int)(nsteps < 16 ? nsteps : 16);
-    const size_t smem = (size_t)nw * (kHead + Stage<T>::BYTES);
+    const size_t smem = (size_t)nw * (kHead + Stage<T, PK>::BYTES);
     MvArgs a;
     a.rows = rows;
     a.row_bytes = (uint32_t)((k / Fmt<T>::QK) * Fmt<T>::BYTES);
@@ -570,13 +616,13 @@ hipError_t launch_t(const uint8_t *w, int64_t rows, int64_t k, const void *xq, i
     a.r = (int32_t)(nsteps % nw);
     a.n = (int32_t)n;
     // once per process (a function-local static is initialised exactly once, thread-safely)
-    static const hipError_t attr_err = hipFuncSetAttribute((const void *)mmvq_stream_kernel<T, DBG, EXPERT, F32, GLU>,
+    static const hipError_t attr_err = hipFuncSetAttribute((const void *)mmvq_stream_kernel<T, DBG, EXPERT, F32, GLU, PK>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (attr_err != hipSuccess) return attr_err;
     constexpr int RW = GLU ? kRows / 2 : kRows;
     dim3 grid((unsigned)((rows + RW - 1) / RW), EXPERT ? (unsigned)n_exp : 1u);
-    hipLaunchKernelGGL((mmvq_stream_kernel<T, DBG, EXPERT, F32, GLU>), grid, dim3(64 * (unsigned)nw), smem, s, w, w2, xq,
-                       y, dbg, a, c);
+    hipLaunchKernelGGL((mmvq_stream_kernel<T, DBG, EXPERT, F32, GLU, PK>), grid, dim3(64 * (unsigned)nw), smem, s, w, w2,
+                       xq, y, dbg, a, c);
     return hipGetLastError();
 }
 
@@ -613,6 +659,20 @@ hipError_t launch_mmvq_stream_f32(int type, const uint8_t *w, int64_t rows, int6
     if (type == kQ6_K) return launch_t<kQ6_K, false, false, true>(w, rows, k, x, n, y, nullptr, c, 0, s);
     if (type == kQ8_0) return launch_t<kQ8_0, false, false, true>(w, rows, k, x, n, y, nullptr, c, 0, s);
     if (type == kQ4_0) return launch_t<kQ4_0, false, false, true>(w, rows, k, x, n, y, nullptr, c, 0, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_mmvq_stream_panel_f32(int type, const uint8_t *wp, int64_t rows, int64_t k, const float *x, int64_t n,
+                                        float *y, hipStream_t s) {
+    const ColMap c{};
+#define QMM_SP(TT) \
+    if (type == TT) return launch_t<TT, false, false, true, false, true>(wp, rows, k, x, n, y, nullptr, c, 0, s);
+    QMM_SP(kQ4_K)
+    QMM_SP(kQ5_K)
+    QMM_SP(kQ6_K)
+    QMM_SP(kQ8_0)
+    QMM_SP(kQ4_0)
+#undef QMM_SP
     return hipErrorInvalidValue;
 }
 

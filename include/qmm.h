@@ -110,6 +110,47 @@ qmm_status qmm_matmul_noalloc(int type, const void *w, int64_t rows, int64_t k, 
                               float *y, void *stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Panel layout: a one-time weight repack ([QMM] "Q4K 8-column repack": the blocks of adjacent
+ * rows are interleaved once, on first use, into a layout the product reads faster, and the
+ * original blocks are kept, so the weights then take twice the memory).  Here the caller repacks
+ * explicitly and owns both buffers; the library keeps no state.
+ *
+ * Layout (k % 256 == 0): G = ceil(rows/16) row groups, S = k/256 steps, B = bytes of 256 values
+ * of a row in the original layout (Q4_K 144, Q5_K 176, Q6_K 210, Q8_0 272, Q4_0 144), P = 16*B.
+ * Panel (g, s) -- rows 16g..16g+15, values 256s..256s+255 -- is the P bytes at (g*S + s)*P.  In a
+ * panel, slab j is the 256 bytes at 256*j, holding one 16-byte piece per row (row i at 16*i):
+ *   Q4_K  slabs 0-7: qs[16j, +16);    slab 8: the header {d, dmin, scales[12]}
+ *   Q5_K  slabs 0-1: qh[16j, +16);    slabs 2-9: qs[16(j-2), +16);   slab 10: the header
+ *   Q6_K  slabs 0-7: ql[16j, +16);    slabs 8-11: qh[16(j-8), +16);  slab 12: scales[16];
+ *         then 32 bytes: the fp16 d of row i at 3328 + 2i
+ *   Q8_0  slab j (0-15): qs[16(j%2), +16) of block j/2 of the step; slab 16: the 8 fp16 d
+ *         (block b at byte 2b of the row's piece)
+ *   Q4_0  slab j (0-7): qs[16] (nibbles) of block j;  slab 8: the 8 fp16 d as for Q8_0
+ * Rows of the last group past `rows` are zero.  Bytes are copied unchanged, so the values, and the
+ * products below, are those of the original blocks; the total is the original size plus the
+ * padding rows.  Each panel is contiguous and 16-byte aligned, so a kernel fetches it with
+ * coalesced 16-byte loads and parks it in LDS as it is (no per-call byte shuffling of the 210- and
+ * 34-byte blocks), and a slab read in the int8 MFMA operand layout is 256 consecutive LDS bytes.
+ *
+ * qmm_repack_bytes: bytes of the panel layout of a [rows][k] matrix of `type`; 0 for an
+ *   unsupported type or shape (k not a positive multiple of 256, rows < 1, k > 1<<20).
+ * qmm_repack: w (original blocks, 2-byte aligned) -> wp (device, 16-byte aligned, at least
+ *   qmm_repack_bytes bytes; QMM_ERR_ARG if smaller).  Asynchronous on `stream`; w is only read.
+ * qmm_matmul_packed: the dense product of qmm_matmul with wp in the panel layout.  n <= 8 runs the
+ *   LDS-staged matrix-vector kernel, which quantizes x itself (no workspace); more columns run the
+ *   tiled kernel with qmm_matmul's plan (J, stream-K) and the qmm_matmul_packed_workspace bytes
+ *   (256-byte aligned).  x fp32 [n][k], 16-byte aligned; y fp32 [n][rows].  Results equal
+ *   qmm_matmul's on the original blocks up to fp32 summation order (the same kernels' arithmetic).
+ *   QMM_ERR_SHAPE for k % 256 != 0; QMM_ERR_TYPE for an unsupported type.
+ * ------------------------------------------------------------------------------------------- */
+uint64_t qmm_repack_bytes(int type, int64_t rows, int64_t k);
+qmm_status qmm_repack(int type, const void *w, int64_t rows, int64_t k, void *wp, uint64_t wp_bytes,
+                      void *stream);
+size_t qmm_matmul_packed_workspace(int type, int64_t rows, int64_t k, int64_t n);
+qmm_status qmm_matmul_packed(int type, const void *wp, int64_t rows, int64_t k, const float *x, int64_t n,
+                             float *y, void *ws, size_t ws_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Expert-indexed product (MoE mul_mat_id; [MMQ] "MoE dispatch", "expert bounds", "MoE skew").
  * w: n_exp weight matrices [rows][k] back to back (ggml [k, rows, n_exp]).
  * ids: int32 [n_tok][top_k] expert ids (ggml [n_expert_used, n_tokens]).

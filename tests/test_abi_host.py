@@ -377,3 +377,28 @@ def test_noalloc_entry_refuses_calls_beyond_its_scratch_without_gpu():
     assert L.qmm_matmul_noalloc(11, w, 4096, 256, x, 4, y, None) == -2
     assert L.qmm_matmul_noalloc(qmm.Q4_K, w, 4096, 4096, ctypes.c_void_p(0x200004), 4, y, None) == -1
     assert L.qmm_matmul_noalloc(qmm.Q4_K, w, 4096, 4096, x, 0, y, None) == 0
+
+
+def test_panel_entry_points_check_arguments_without_gpu():
+    """The panel-layout calls refuse bad shapes, types and pointers on the host, before any launch;
+    their sizes follow the layout (the original bytes of whole 16-row groups)."""
+    L = qmm.lib()
+    assert qmm.repack_bytes(qmm.Q4_K, 4096, 4096) == 4096 * 4096 // 256 * 144
+    assert qmm.repack_bytes(qmm.Q6_K, 17, 512) == 2 * 2 * 16 * 210          # 2 row groups x 2 steps
+    assert qmm.repack_bytes(qmm.Q8_0, 16, 96) == 0                           # k % 256 != 0
+    assert qmm.repack_bytes(3, 16, 256) == 0                                 # unsupported type
+    assert qmm.repack_bytes(qmm.Q4_K, 0, 256) == 0
+    assert L.qmm_repack(qmm.Q4_K, None, 16, 256, None, 0, None) == -1       # null pointers
+    assert L.qmm_repack(qmm.Q8_0, 2, 16, 96, 16, 1 << 20, None) == -3       # k % 256 != 0
+    assert L.qmm_repack(7, 2, 16, 256, 16, 1 << 20, None) == -2             # type
+    assert L.qmm_repack(qmm.Q4_K, 2, 16, 256, 24, 1 << 20, None) == -1      # wp not 16-byte aligned
+    assert L.qmm_repack(qmm.Q4_K, 2, 16, 256, 32, 100, None) == -1          # wp too small
+    assert L.qmm_matmul_packed(qmm.Q4_K, 32, 16, 320, 16, 1, 16, None, 0, None) == -3
+    assert L.qmm_matmul_packed(qmm.Q4_K, 24, 16, 256, 16, 1, 16, None, 0, None) == -1   # wp alignment
+    assert L.qmm_matmul_packed(qmm.Q4_K, 32, 16, 256, 16, 0, 16, None, 0, None) == 0    # n = 0: no-op
+    # the tiled path needs the same workspace as qmm_matmul_q8_1 (tiled activations + partials);
+    # up to 8 columns none
+    assert qmm.matmul_packed_workspace(qmm.Q4_K, 4096, 4096, 8) == 0
+    assert qmm.matmul_packed_workspace(qmm.Q4_K, 4096, 4096, 512) == \
+        L.qmm_matmul_q8_1_workspace(qmm.Q4_K, 4096, 4096, 512)
+    assert L.qmm_matmul_packed(qmm.Q4_K, 32, 4096, 4096, 16, 512, 16, 256, 256, None) == -4   # workspace
