@@ -20,6 +20,8 @@ Also in the same JSON line:
   f16act_matvec  per-call timing (encoder + kernel) of the fp16-activation mode on the step's shapes
   extra_types_matvec  per-launch timing of the same matrix-vector shapes in Q5_K and Q4_0 (not
                 part of the step).
+  panel_layout  the step's shapes read from the panel layout (qmm_repack / qmm_matmul_packed), and
+                the repack's first-call versus steady-state cost at 8192 x 4096 Q4_K, one column.
   secondary     for the prefill and MoE shapes and the gate/up products fused with SwiGLU: per-call
                 median / p10 / p90, int8 TOPS as a fraction of the 5.0 POP/s datasheet peak and of
                 the int8 MFMA probe, % of roofline (max of bytes / 8 TB/s and ops / 5 POP/s over
@@ -266,7 +268,7 @@ def main():
     tot_bytes = tot_us = tot_probe_us = 0.0
     reps = max(20, args.steps)
     for i, c in enumerate(cases):
-        kid, fused = qmm.matvec_kernel(c["qtype"], W[0][i], c["k"], X[i], c["n"], x_fp32=True)
+        kid, fused = qmm.matvec_kernel(c["qtype"], W[0][i], c["rows"], c["k"], X[i], c["n"], x_fp32=True)
         rot = rotations(W[0][i], (c["k"] // BV[c["qtype"]]) * BB[c["qtype"]])
         if fused:
             call = lambda r, i=i, c=c: qmm.matmul(rot[r], c["qtype"], c["rows"], c["k"], X[i], out=Y[i], ws=WS[i])
@@ -311,7 +313,7 @@ def main():
         x5 = torch.from_numpy(synth.gen_activations(c["n"], c["k"], synth.rngs(70 + i, 1)[0])).to(dev)
         y5 = torch.empty((c["n"], c["rows"]), dtype=torch.float32, device=dev)
         ws5 = qmm._workspace(qmm.matmul_workspace(c["qtype"], c["rows"], c["k"], c["n"]), dev)
-        kid, fused = qmm.matvec_kernel(c["qtype"], w5[0], c["k"], x5, c["n"], x_fp32=True)
+        kid, fused = qmm.matvec_kernel(c["qtype"], w5[0], c["rows"], c["k"], x5, c["n"], x_fp32=True)
         g = capture(lambda: [qmm.matmul(w5[r], c["qtype"], c["rows"], c["k"], x5, out=y5, ws=ws5)
                              for r in range(len(w5))])
         us = pct(replay_samples(g, len(w5), max(10, reps // 4)), 50)
@@ -339,6 +341,47 @@ def main():
                           "GBps": round(b / us / 1e3, 1), "frac": round(b / us / 1e3 / HBM_PEAK_GBPS, 4)})
         log(f"[bench]   f16act {c['name']:24s} {us:8.3f} us  {b / us / 1e3:8.1f} GB/s")
         del wf
+
+    # Panel layout (one-time repack, qmm_repack): the step's shapes from panels, timed like the
+    # per-case figures above (weights rotated by whole row groups over > 512 MB, graph-replayed),
+    # and the first-call versus steady-state cost at 8192 x 4096 Q4_K, one column.
+    panel_cases = []
+    for i, c in enumerate(cases):
+        wp0 = qmm.repack(W[0][i], c["qtype"], c["rows"], c["k"])
+        rotp = rotations(wp0, wp0.numel() // ((c["rows"] + 15) // 16))
+        wsp = qmm._workspace(qmm.matmul_packed_workspace(c["qtype"], c["rows"], c["k"], c["n"]), dev)
+        g = capture(lambda: [qmm.matmul_packed(rotp[r], c["qtype"], c["rows"], c["k"], X[i], out=Y[i], ws=wsp)
+                             for r in range(len(rotp))])
+        us = pct(replay_samples(g, len(rotp), max(10, reps // 4)), 50)
+        b = launch_bytes(c["qtype"], c["rows"], c["k"], c["n"], BB, BV, True)
+        panel_cases.append({"case": c["name"], "us": round(us, 3), "GBps": round(b / us / 1e3, 1),
+                            "frac": round(b / us / 1e3 / HBM_PEAK_GBPS, 4), "original_layout_us": per_case[i]["us"]})
+        log(f"[bench]   panels {c['name']:24s} {us:8.3f} us  {b / us / 1e3:8.1f} GB/s "
+            f"(original layout {per_case[i]['us']:.3f} us)")
+        del g, rotp, wp0
+    fc = dict(qtype=qmm.Q4_K, rows=8192, k=4096, n=1)
+    wfc = rotations(torch.from_numpy(synth.gen_weights(fc["qtype"], fc["rows"], fc["k"], synth.rngs(6000, 1)[0])).to(dev),
+                    (fc["k"] // 256) * 144)
+    xfc = torch.from_numpy(synth.gen_activations(1, fc["k"], synth.rngs(6001, 1)[0])).to(dev)
+    yfc = torch.empty((1, fc["rows"]), dtype=torch.float32, device=dev)
+    nbp = qmm.repack_bytes(fc["qtype"], fc["rows"], fc["k"])
+    wpfc = [torch.empty(nbp, dtype=torch.uint8, device=dev) for _ in wfc]
+    wsfc = qmm._workspace(qmm.matmul_workspace(fc["qtype"], fc["rows"], fc["k"], 1), dev)
+    wspfc = qmm._workspace(qmm.matmul_packed_workspace(fc["qtype"], fc["rows"], fc["k"], 1), dev)
+    rep = lambda r: qmm.repack(wfc[r], fc["qtype"], fc["rows"], fc["k"], out=wpfc[r])
+    prod = lambda r: qmm.matmul_packed(wpfc[r], fc["qtype"], fc["rows"], fc["k"], xfc, out=yfc, ws=wspfc)
+    nfc = len(wfc)
+    t_rep = pct(replay_samples(capture(lambda: [rep(r) for r in range(nfc)]), nfc, 10), 50)
+    t_first = pct(replay_samples(capture(lambda: [(rep(r), prod(r)) for r in range(nfc)]), nfc, 10), 50)
+    t_steady = pct(replay_samples(capture(lambda: [prod(r) for r in range(nfc)]), nfc, 10), 50)
+    t_orig = pct(replay_samples(capture(lambda: [qmm.matmul(wfc[r], fc["qtype"], fc["rows"], fc["k"], xfc, out=yfc,
+                                                            ws=wsfc) for r in range(nfc)]), nfc, 10), 50)
+    first_call = {"case": "q4_K 8192x4096 N=1", "repack_us": round(t_rep, 3), "first_call_us": round(t_first, 3),
+                  "steady_us": round(t_steady, 3), "original_layout_us": round(t_orig, 3),
+                  "repacked_bytes": nbp, "original_bytes": wfc[0].numel()}
+    log(f"[bench] panel layout first call vs steady state: {first_call}")
+    del wfc, wpfc
+    panel_layout = {"matvec": panel_cases, "first_call": first_call}
 
     traffic = None
     tpath = os.path.join(ROOT, "profiles", "mmvq_traffic.json")
@@ -381,6 +424,7 @@ def main():
         "cpu_baseline": cpu,
         "secondary": secondary,
         "extra_types_matvec": q5_cases,
+        "panel_layout": panel_layout,
         "f16act_matvec": f16_cases,
     }
     print(json.dumps(out), flush=True)

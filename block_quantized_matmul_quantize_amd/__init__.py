@@ -83,7 +83,7 @@ _sig("qmm_plan_dense", _i32, _i32, _i64, _i64, _i64, ctypes.c_int32, ctypes.POIN
 _sig("qmm_tile_efficiency", ctypes.c_int32, _i64, ctypes.c_int32)
 _sig("qmm_select_tile_j", ctypes.c_int32, _i64)
 _sig("qmm_streamk_unit_start", _i64, _i64, _i64, _i64, _i64)
-_sig("qmm_matvec_kernel", _i32, _i32, _vp, _i64, _vp, _i64, _i32, ctypes.POINTER(_i32))
+_sig("qmm_matvec_kernel", _i32, _i32, _vp, _i64, _i64, _vp, _i64, _i32, ctypes.POINTER(_i32))
 
 
 class QmmError(RuntimeError):
@@ -140,14 +140,14 @@ def streamk_unit_start(u, units, ntiles, k_iters):
 MV_KERNEL_NAMES = {1: "mmvq_kernel", 2: "mmvq_stream_kernel", 3: "mmvq_dot4_kernel"}
 
 
-def matvec_kernel(qtype, w_ptr, k, x_ptr, n, x_fp32=True):
+def matvec_kernel(qtype, w_ptr, rows, k, x_ptr, n, x_fp32=True):
     """(kernel id, fused) a dense call would launch: 0 tiled path, 1 register-streamed, 2
     LDS-staged MFMA, 3 dot4; fused = the kernel quantizes the fp32 activations itself.  Takes
     raw addresses (ints) or tensors; only their alignment matters."""
     w_ptr = w_ptr.data_ptr() if hasattr(w_ptr, "data_ptr") else int(w_ptr)
     x_ptr = x_ptr.data_ptr() if hasattr(x_ptr, "data_ptr") else int(x_ptr)
     out = _i32(0)
-    _check(_L.qmm_matvec_kernel(qtype, w_ptr, k, x_ptr, n, 1 if x_fp32 else 0, ctypes.byref(out)))
+    _check(_L.qmm_matvec_kernel(qtype, w_ptr, rows, k, x_ptr, n, 1 if x_fp32 else 0, ctypes.byref(out)))
     return out.value & 15, bool(out.value & 16)
 
 

@@ -343,7 +343,7 @@ qmm_status dense_f32(int type, const void *w, int64_t rows, int64_t k, const flo
                      uint8_t *wsb, const DenseWs &L, const qmm::Ovr &o, hipStream_t s) {
     const qmm_plan p = plan_dense_impl(type, rows, k, n, device_cus(), o);
     if (p.regime == 1) {
-        const int fc = qmm::mmvq_fused_choice(type, w, k, x, n, o);
+        const int fc = qmm::mmvq_fused_choice(type, w, rows, k, x, n, o);
         if (fc) {
             // few columns: the dot4 or LDS-staged kernel quantizes the activations itself (the same
             // q8_1 bytes as the quantize kernel below), one launch instead of two
@@ -455,10 +455,10 @@ qmm_status qmm_matmul(int type, const void *w, int64_t rows, int64_t k, const fl
     return dense_f32(type, w, rows, k, x, n, y, (uint8_t *)ws, L, o, (hipStream_t)stream);
 }
 
-qmm_status qmm_matvec_kernel(int type, const void *w, int64_t k, const void *x, int64_t n, int32_t x_fp32,
-                             int32_t *out) {
+qmm_status qmm_matvec_kernel(int type, const void *w, int64_t rows, int64_t k, const void *x, int64_t n,
+                             int32_t x_fp32, int32_t *out) {
     const qmm::Ovr o = load_ovr();
-    qmm_status st = check_common(type, 1, k, n);
+    qmm_status st = check_common(type, rows, k, n);
     if (st) return st;
     if (!out) return fail(QMM_ERR_ARG, "null out");
     if (n < 1 || n > 8 || k > kMvMaxK || o.path == 2) {
@@ -467,14 +467,14 @@ qmm_status qmm_matvec_kernel(int type, const void *w, int64_t k, const void *x, 
     }
     if (x_fp32) {
         if (((uintptr_t)x) & 15) return fail(QMM_ERR_ARG, "x must be 16-byte aligned");
-        const int f = qmm::mmvq_fused_choice(type, w, k, (const float *)x, n, o);
+        const int f = qmm::mmvq_fused_choice(type, w, rows, k, (const float *)x, n, o);
         if (f) {
             *out = f + 16;
             return QMM_OK;
         }
         x = (const void *)(uintptr_t)256;   // the q8_1 copy sits at the 256-byte aligned workspace start
     }
-    *out = qmm::mmvq_kernel_choice(type, w, k, x, n, nullptr, o);
+    *out = qmm::mmvq_kernel_choice(type, w, rows, k, x, n, nullptr, o);
     return QMM_OK;
 }
 
@@ -603,7 +603,7 @@ qmm_status qmm_matmul_glu(int type, const void *w_gate, const void *w_up, int64_
     hipError_t e;
     if (glu_matvec(n, k, o)) {
         // the dot4 or LDS-staged kernel quantizing x itself (one launch), as for one matrix
-        const int kc = qmm::mmvq_glu_f32_choice(type, wg, wu, k, x, n, o);
+        const int kc = qmm::mmvq_glu_f32_choice(type, wg, wu, rows, k, x, n, o);
         if (kc == 3 || kc == 2) {
             e = kc == 3 ? qmm::launch_mmvq_dot4_glu_f32(type, wg, wu, rows, k, x, n, y, s)
                         : qmm::launch_mmvq_stream_glu(type, wg, wu, rows, k, x, true, n, y, nullptr, 0, s);

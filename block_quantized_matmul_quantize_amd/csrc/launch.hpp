@@ -54,7 +54,8 @@ hipError_t launch_mmvq(int type, const uint8_t *w, int64_t rows, int64_t k, cons
 // Gate/up fusion, matrix-vector: y = silu(W_gate x) * (W_up x) for n <= 8 dense q8_1 columns (cm
 // null) or the small experts (cm set, grid.y = n_exp); the LDS-staged kernel where both matrices
 // meet its rules, else the register-streamed one.
-int mmvq_glu_f32_choice(int type, const void *wg, const void *wu, int64_t k, const float *x, int64_t n, const Ovr &o);
+int mmvq_glu_f32_choice(int type, const void *wg, const void *wu, int64_t rows, int64_t k, const float *x, int64_t n,
+                        const Ovr &o);
 hipError_t launch_mmvq_glu(int type, const uint8_t *wg, const uint8_t *wu, int64_t rows, int64_t k, const uint8_t *xq,
                            int64_t n, float *y, const ColMap *cm, int64_t n_exp, const Ovr &o, hipStream_t s);
 
@@ -73,9 +74,10 @@ hipError_t launch_mmvq_stream_glu(int type, const uint8_t *wg, const uint8_t *wu
 // LDS-staged kernel (no separate quantize launch): dense calls either kernel would take.
 // Kernel launch_mmvq takes for q8_1 input: 3 dot4, 2 LDS-staged MFMA, 1 register-streamed, 0 none
 // (a forced kernel that cannot serve the call); host logic only.
-int mmvq_kernel_choice(int type, const void *w, int64_t k, const void *xq, int64_t n, const ColMap *cm, const Ovr &o);
+int mmvq_kernel_choice(int type, const void *w, int64_t rows, int64_t k, const void *xq, int64_t n, const ColMap *cm,
+                       const Ovr &o);
 // Kernel launch_mmvq_fused takes for fp32 input: 3 dot4, 2 LDS-staged MFMA, 0 not fused.
-int mmvq_fused_choice(int type, const void *w, int64_t k, const float *x, int64_t n, const Ovr &o);
+int mmvq_fused_choice(int type, const void *w, int64_t rows, int64_t k, const float *x, int64_t n, const Ovr &o);
 // Launches the kernel mmvq_fused_choice names (`choice`, non-zero).
 hipError_t launch_mmvq_fused(int choice, int type, const uint8_t *w, int64_t rows, int64_t k, const float *x, int64_t n,
                              float *y, hipStream_t s);

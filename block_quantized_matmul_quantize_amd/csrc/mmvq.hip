@@ -502,20 +502,24 @@ static hipError_t launch_mmvq_t(const uint8_t *w, int64_t rows, int64_t k, const
     return launch_mmvq_spw<T, 2, DBG, EXPERT>(w, rows, k, xq, n, y, dbg, c, n_exp, s);
 }
 
-// Largest column count the automatic choice sends to the dot4 kernel, per type: measured at
-// 4096 x 4096 (fp32 input, graph-replayed calls), dot4 is ~0.1 us faster than the LDS-staged
-// kernel at one column and 0.8-1.4 us slower at two or three.
-static int dot4_auto_cols(int type) {
-    return type == kQ4_K || type == kQ5_K || type == kQ8_0 || type == kQ4_0 ? 1 : 0;
+// Largest column count the automatic choice sends to the dot4 kernel, per type and weight rows:
+// one column from 8192 rows on, none below.  Measured with the weights rotated over > 512 MB
+// (graph-replayed calls, fp32 input, Q4_K, one column): at 4096 x 4096 the LDS-staged kernel takes
+// 5.2 us and dot4 5.7; at 14336 x 4096 dot4 takes 11.8 us and the LDS-staged kernel 15.3, at
+// 57344 x 4096 34 and 53 (its 16-row workgroups each quantize all of x and run one step per wave,
+// while dot4's waves stream many rows).  At two or three columns dot4 is 0.8-1.4 us slower.
+constexpr int64_t kDot4MinRows = 8192;
+static int dot4_auto_cols(int type, int64_t rows) {
+    return rows >= kDot4MinRows && (type == kQ4_K || type == kQ5_K || type == kQ8_0 || type == kQ4_0) ? 1 : 0;
 }
 
 // Which fused kernel serves an fp32-input call: 3 dot4, 2 LDS-staged MFMA, 0 none.  Override
 // o.mv_kernel: 0 automatic, 1 register-streamed (never fused), 2 LDS-staged only, 3 dot4 only.
-static int fused_kernel(int type, const void *w, int64_t k, const float *x, int64_t n, const Ovr &o) {
+static int fused_kernel(int type, const void *w, int64_t rows, int64_t k, const float *x, int64_t n, const Ovr &o) {
     const int kc = o.mv_kernel;
     if (n < 1 || (uintptr_t)x % 16 != 0) return 0;
     if (kc == 0 || kc == 3) {
-        const int lim = kc == 3 ? mmvq_dot4_max_cols() : dot4_auto_cols(type);
+        const int lim = kc == 3 ? mmvq_dot4_max_cols() : dot4_auto_cols(type, rows);
         if (n <= lim && mmvq_dot4_supported(type, w, k, x, nullptr)) return 3;
         if (kc == 3) return 0;
     }
@@ -537,10 +541,11 @@ hipError_t launch_mmvq_fused(int choice, int type, const uint8_t *w, int64_t row
     }
 }
 
-int mmvq_kernel_choice(int type, const void *w, int64_t k, const void *xq, int64_t n, const ColMap *cm, const Ovr &o) {
+int mmvq_kernel_choice(int type, const void *w, int64_t rows, int64_t k, const void *xq, int64_t n, const ColMap *cm,
+                       const Ovr &o) {
     const int kc = o.mv_kernel;
     if (kc == 3 || kc == 0) {
-        const int lim = kc == 3 ? mmvq_dot4_max_cols() : dot4_auto_cols(type);
+        const int lim = kc == 3 ? mmvq_dot4_max_cols() : dot4_auto_cols(type, rows);
         if (!cm && n <= lim && mmvq_dot4_supported(type, w, k, xq, cm)) return 3;
         if (kc == 3) return 0;
     }
@@ -549,13 +554,13 @@ int mmvq_kernel_choice(int type, const void *w, int64_t k, const void *xq, int64
     return 1;
 }
 
-int mmvq_fused_choice(int type, const void *w, int64_t k, const float *x, int64_t n, const Ovr &o) {
-    return fused_kernel(type, w, k, x, n, o);
+int mmvq_fused_choice(int type, const void *w, int64_t rows, int64_t k, const float *x, int64_t n, const Ovr &o) {
+    return fused_kernel(type, w, rows, k, x, n, o);
 }
 
 hipError_t launch_mmvq(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y,
                        int32_t *dbg, const ColMap *cm, int64_t n_exp, const Ovr &o, hipStream_t s) {
-    switch (mmvq_kernel_choice(type, w, k, xq, n, cm, o)) {
+    switch (mmvq_kernel_choice(type, w, rows, k, xq, n, cm, o)) {
         case 3: return launch_mmvq_dot4(type, w, rows, k, xq, n, y, dbg, cm, n_exp, (int)n, s);
         case 2: return launch_mmvq_stream(type, w, rows, k, xq, n, y, dbg, cm, n_exp, s);
         case 1: break;
@@ -607,9 +612,10 @@ hipError_t launch_mmvq_glu(int type, const uint8_t *wg, const uint8_t *wu, int64
 
 // Kernel for a dense fp32-input gate/up call of n <= 8 columns, as fused_kernel decides for one
 // matrix, with both matrices checked: 3 dot4, 2 LDS-staged (both quantize x themselves), 0 none
-// (quantize first, then launch_mmvq_glu).
-int mmvq_glu_f32_choice(int type, const void *wg, const void *wu, int64_t k, const float *x, int64_t n, const Ovr &o) {
-    const int a = fused_kernel(type, wg, k, x, n, o), b = fused_kernel(type, wu, k, x, n, o);
+// (quantize first, then launch_mmvq_glu).  The kernel streams both matrices: 2 * rows weight rows.
+int mmvq_glu_f32_choice(int type, const void *wg, const void *wu, int64_t rows, int64_t k, const float *x, int64_t n,
+                        const Ovr &o) {
+    const int a = fused_kernel(type, wg, 2 * rows, k, x, n, o), b = fused_kernel(type, wu, 2 * rows, k, x, n, o);
     return a == b ? a : 0;
 }
 

@@ -252,14 +252,15 @@ qmm_status qmm_debug_subdots(int type, const void *w, int64_t rows, int64_t k, c
  * Which matrix-vector kernel a dense call would launch ([MMQ] "shape criteria": n <= 8 takes the
  * matrix-vector regime), under the current overrides; host logic only, nothing is launched and
  * no GPU is needed.  x_fp32 = 1 asks about qmm_matmul with fp32 activations x, 0 about
- * qmm_matmul_q8_1 with q8_1 activations x; only the alignment of w and x is looked at.
+ * qmm_matmul_q8_1 with q8_1 activations x; only the alignment of w and x, and the sizes, are looked
+ * at (one column of 8192 or more rows takes the dot4 kernel, fewer rows the LDS-staged one).
  * *out: 0 the call takes the tiled path (n > 8 or forced), 1 register-streamed, 2 LDS-staged
  * MFMA, 3 dot4; plus 16 when that kernel quantizes the fp32 activations itself (one launch, no
  * quantize kernel).  Errors: QMM_ERR_TYPE / QMM_ERR_SHAPE as for qmm_matmul, QMM_ERR_ARG for a
  * null out or an fp32 x that is not 16-byte aligned.
  * ------------------------------------------------------------------------------------------- */
-qmm_status qmm_matvec_kernel(int type, const void *w, int64_t k, const void *x, int64_t n, int32_t x_fp32,
-                             int32_t *out);
+qmm_status qmm_matvec_kernel(int type, const void *w, int64_t rows, int64_t k, const void *x, int64_t n,
+                             int32_t x_fp32, int32_t *out);
 
 /* ---------------------------------------------------------------------------------------------
  * Plan overrides for tests and tuning (process-wide; 0 = automatic).  Every other entry point

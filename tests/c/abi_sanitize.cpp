@@ -79,7 +79,7 @@ int main() {
                 (void)qmm_matmul_glu_workspace(t, 4096, k, n);
                 (void)qmm_debug_subdots_workspace(t, 100, k, n, 2);
                 int32_t kid = -1;
-                if (n >= 1) EXPECT(qmm_matvec_kernel(t, W, k, X, n, 1, &kid) == QMM_OK);
+                if (n >= 1) EXPECT(qmm_matvec_kernel(t, W, 4096, k, X, n, 1, &kid) == QMM_OK);
                 int64_t lay[6];
                 EXPECT(qmm_matmul_id_grouping_layout(t, 128, k, n, 8, 1, lay) == QMM_OK);
                 (void)qmm_matmul_id_workspace(t, 128, 768, k, n, 8, 8);

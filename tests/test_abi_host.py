@@ -197,31 +197,28 @@ def test_workspace_sizes_monotone():
 
 
 MV_AUTO = [
-    # (type, n, expected (kernel, fused)) for aligned weights and fp32 activations, K = 4096:
-    # dot4 for Q4_K, Q5_K, Q8_0 and Q4_0 at n = 1, else the LDS-staged kernel; both quantize the fp32 input
-    # themselves at every n <= 8.
-    (qmm.Q4_K, 1, (3, True)),
-    *[(qmm.Q4_K, n, (2, True)) for n in range(2, 9)],
-    *[(qmm.Q6_K, n, (2, True)) for n in range(1, 9)],
-    (qmm.Q8_0, 1, (3, True)),
-    (qmm.Q5_K, 1, (3, True)),
-    *[(qmm.Q5_K, n, (2, True)) for n in range(2, 9)],
-    *[(qmm.Q8_0, n, (2, True)) for n in range(2, 9)],
-    (qmm.Q4_0, 1, (3, True)),
-    *[(qmm.Q4_0, n, (2, True)) for n in range(2, 9)],
-    *[(t, 9, (0, False)) for t in (qmm.Q4_K, qmm.Q5_K, qmm.Q6_K, qmm.Q8_0, qmm.Q4_0)],
+    # (type, rows, n, expected (kernel, fused)) for aligned weights and fp32 activations, K = 4096:
+    # dot4 for Q4_K, Q5_K, Q8_0 and Q4_0 at n = 1 from 8192 rows on, else the LDS-staged kernel; both
+    # quantize the fp32 input themselves at every n <= 8.
+    *[(t, 4096, n, (2, True)) for t in (qmm.Q4_K, qmm.Q5_K, qmm.Q6_K, qmm.Q8_0, qmm.Q4_0) for n in range(1, 9)],
+    *[(t, 8192, 1, (3, True)) for t in (qmm.Q4_K, qmm.Q5_K, qmm.Q8_0, qmm.Q4_0)],
+    (qmm.Q4_K, 8191, 1, (2, True)),
+    (qmm.Q6_K, 14336, 1, (2, True)),
+    *[(t, 14336, 2, (2, True)) for t in (qmm.Q4_K, qmm.Q8_0)],
+    *[(t, 4096, 9, (0, False)) for t in (qmm.Q4_K, qmm.Q5_K, qmm.Q6_K, qmm.Q8_0, qmm.Q4_0)],
 ]
 
 
-@pytest.mark.parametrize("qtype,n,expect", MV_AUTO)
-def test_matvec_kernel_automatic_choice(qtype, n, expect):
-    assert qmm.matvec_kernel(qtype, 0x10000, 4096, 0x20000, n, x_fp32=True) == expect
+@pytest.mark.parametrize("qtype,rows,n,expect", MV_AUTO)
+def test_matvec_kernel_automatic_choice(qtype, rows, n, expect):
+    assert qmm.matvec_kernel(qtype, 0x10000, rows, 4096, 0x20000, n, x_fp32=True) == expect
 
 
 def test_matvec_kernel_choice_follows_alignment_and_overrides():
-    mk = qmm.matvec_kernel
+    mk = lambda t, w, k, x, n, rows=8192, **kw: qmm.matvec_kernel(t, w, rows, k, x, n, **kw)
     # q8_1 input: 4-byte alignment serves both dot4 and the LDS-staged kernel, 2-byte neither
     assert mk(qmm.Q4_K, 0x10000, 4096, 0x20004, 1, x_fp32=False) == (3, False)
+    assert mk(qmm.Q4_K, 0x10000, 4096, 0x20004, 1, rows=4096, x_fp32=False) == (2, False)
     assert mk(qmm.Q4_K, 0x10000, 4096, 0x20004, 5, x_fp32=False) == (2, False)
     assert mk(qmm.Q4_K, 0x10000, 4096, 0x20002, 1, x_fp32=False) == (1, False)
     assert mk(qmm.Q6_K, 0x10000, 4096, 0x20002, 5, x_fp32=False) == (1, False)
@@ -242,6 +239,8 @@ def test_matvec_kernel_choice_follows_alignment_and_overrides():
         assert mk(qmm.Q4_K, 0x10000, 4096, 0x20000, 1) == (1, False)
         qmm.set_override(qmm.OVR_MV_KERNEL, 2)
         assert mk(qmm.Q4_K, 0x10000, 4096, 0x20000, 1) == (2, True)
+        qmm.set_override(qmm.OVR_MV_KERNEL, 3)
+        assert mk(qmm.Q4_K, 0x10000, 4096, 0x20000, 1, rows=16) == (3, True)
         qmm.set_override(qmm.OVR_MV_KERNEL, 0)
         qmm.set_override(qmm.OVR_FUSE_COLS, 2)
         assert mk(qmm.Q6_K, 0x10000, 4096, 0x20000, 3) == (2, False)

@@ -266,7 +266,7 @@ def test_matvec_lds_kernel_at_minimum_alignment(qtype, woff):
         w, x = _case(qtype, rows, k, n, 560 + n)
         xq = oracle.quantize_q8_1(x)
         wd, xd = _at_offset(w, woff), _at_offset(xq, 4)
-        assert qmm.matvec_kernel(qtype, wd, k, xd, n, x_fp32=False) == (2, False)
+        assert qmm.matvec_kernel(qtype, wd, rows, k, xd, n, x_fp32=False) == (2, False)
         y = qmm.matmul_q8_1(wd, qtype, rows, k, xd, n).cpu().numpy()
         ref = oracle.matmul_q8_1(qtype, w, rows, k, xq, n)
         assert_close(y, ref, row_norms(qtype, w, rows, k), col_norms(xq, n, k), what=f"{TNAME[qtype]} n={n}")
@@ -286,11 +286,16 @@ def test_forced_matvec_kernel_refuses_unsupported_call(kernel, qtype, k, n):
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("kernel", [0, 2], ids=["auto", "lds"])
-@pytest.mark.parametrize("qtype,n", [(qmm.Q4_K, 1), (qmm.Q4_K, 2), (qmm.Q8_0, 1), (qmm.Q8_0, 2), (qmm.Q8_0, 3),
-                                     (qmm.Q4_K, 3), (qmm.Q4_K, 5), (qmm.Q4_K, 8), (qmm.Q8_0, 4), (qmm.Q8_0, 8),
-                                     (qmm.Q6_K, 1), (qmm.Q6_K, 2), (qmm.Q6_K, 3), (qmm.Q6_K, 8),
-                                     (qmm.Q5_K, 1), (qmm.Q5_K, 2), (qmm.Q5_K, 8)])
+FUSED_SHAPES = [(qmm.Q4_K, 1), (qmm.Q4_K, 2), (qmm.Q8_0, 1), (qmm.Q8_0, 2), (qmm.Q8_0, 3),
+                (qmm.Q4_K, 3), (qmm.Q4_K, 5), (qmm.Q4_K, 8), (qmm.Q8_0, 4), (qmm.Q8_0, 8),
+                (qmm.Q6_K, 1), (qmm.Q6_K, 2), (qmm.Q6_K, 3), (qmm.Q6_K, 8),
+                (qmm.Q5_K, 1), (qmm.Q5_K, 2), (qmm.Q5_K, 8)]
+# automatic choice and the LDS-staged kernel everywhere; dot4 where it serves (not Q6_K, <= 3 columns)
+FUSED_CASES = [(t, n, kern) for kern in (0, 2, 3) for t, n in FUSED_SHAPES if kern != 3 or (t != qmm.Q6_K and n <= 3)]
+
+
+@pytest.mark.parametrize("qtype,n,kernel", FUSED_CASES,
+                         ids=[f"{TNAME[t]}-n{n}-{('auto', '', 'lds', 'dot4')[kern]}" for t, n, kern in FUSED_CASES])
 def test_fused_quantize_matches_separate_quantize_bitwise(qtype, n, kernel):
     """fp32 input to the matrix-vector path with fusion forced for every column count: the dot4 or
     LDS-staged kernel quantizes the activations itself; the output equals

@@ -60,8 +60,8 @@ def test_oracle_under_address_and_ub_sanitizers(tmp_path):
 
 @pytest.mark.skipif(not (os.path.exists(HIPCC) and os.path.exists(CLANG)), reason="ROCm toolchain not installed")
 def test_abi_host_code_under_address_and_ub_sanitizers(tmp_path):
-    srcs = ["api.cpp", "quantize.hip", "mmvq.hip", "mmvq_stream.hip", "mmvq_dot4.hip", "mmq.hip", "moe.hip",
-            "f16act.hip", "noalloc.hip"]
+    from block_quantized_matmul_quantize_amd.build import SOURCES
+    srcs = list(SOURCES)   # every translation unit of libqmm
 
     def compile_one(name):
         obj = str(tmp_path / (os.path.splitext(name)[0] + ".o"))
