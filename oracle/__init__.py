@@ -15,12 +15,14 @@ from . import build as _build
 
 Q4_0 = 2
 Q8_0 = 8
+Q3_K = 11
 Q4_K = 12
 Q5_K = 13
 Q6_K = 14
+IQ4_XS = 23
 
-BLOCK_VALUES = {Q4_0: 32, Q8_0: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256}
-BLOCK_BYTES = {Q4_0: 18, Q8_0: 34, Q4_K: 144, Q5_K: 176, Q6_K: 210}
+BLOCK_VALUES = {Q4_0: 32, Q8_0: 32, Q3_K: 256, Q4_K: 256, Q5_K: 256, Q6_K: 256, IQ4_XS: 256}
+BLOCK_BYTES = {Q4_0: 18, Q8_0: 34, Q3_K: 110, Q4_K: 144, Q5_K: 176, Q6_K: 210, IQ4_XS: 136}
 Q8_1_BYTES = 36
 
 _lib = None

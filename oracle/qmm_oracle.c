@@ -22,6 +22,13 @@
  *  - Q4_0 weights: value = d*(q - 8), 4-bit q, fp16 d per 32 values (named with the other types on
  *    the MMQ page, whose tile-size table gives it only qs and one scale; the byte layout is GGUF's
  *    block_q4_0: low nibbles of qs[0..15] are values 0..15, high nibbles values 16..31).
+ *  - Q3_K weights: value = d * (sc - 32) * (q - 4), a 3-bit code q and an unsigned 6-bit scale per
+ *    16 values; the GP100 patch page ("How", step 3) names the type and its -4 code offset; the
+ *    byte layout and the 6-bit scale packing are GGUF's block_q3_K.
+ *  - IQ4_XS weights: value = d * (ls - 32) * cb[q], a 4-bit index q into a fixed 16-entry
+ *    non-linear codebook cb and an unsigned 6-bit scale ls per 32 values; the GP100 page ("How",
+ *    step 3) names the type and its codebook; the byte layout and the codebook are GGUF's
+ *    block_iq4_xs and its 4-bit non-linear table.
  *  - fp16-activation mode ("GP100 MMVQ" page, "How" step 1 and the accuracy paragraph under the
  *    results table): per 32 values of a column a power-of-two prescale 2^e, e the largest integer
  *    with max|x| * 2^e < 2^15 (e = 0 for an all-zero block), the values rounded once to fp16, and
@@ -41,6 +48,15 @@
  *    q8_1 {d, s, qs[32]} (36 B); fp16 is little-endian IEEE binary16.  q5_K {d, dmin, scales[12],
  *    qh[32], qs[128]} (176 B): the low 4 bits of value v as in Q4_K, the fifth bit is bit v/32 of
  *    qh[v % 32].
+ *  - q3_K {hmask[32], qs[64], scales[12], d} (110 B): value v, h = v/128, j = (v%128)/32,
+ *    l = v%32: low 2 bits = bits 2j..2j+1 of qs[32h + l], third bit = bit 4h + j of hmask[l];
+ *    16 6-bit scales from the 12 bytes s: scale i (i < 4) = (s[i] & 15) | ((s[8+i] & 3) << 4),
+ *    4+i: (s[4+i] & 15) | (((s[8+i] >> 2) & 3) << 4), 8+i: (s[i] >> 4) | (((s[8+i] >> 4) & 3) << 4),
+ *    12+i: (s[4+i] >> 4) | (((s[8+i] >> 6) & 3) << 4); scale t serves values 16t..16t+15.
+ *  - iq4_xs {d, scales_h (u16), scales_l[4], qs[128]} (136 B): sub-block b (32 values) has
+ *    ls = ((scales_l[b/2] >> 4(b%2)) & 15) | (((scales_h >> 2b) & 3) << 4); its values i < 16 take
+ *    the low nibble of qs[16b + i], values 16 + i the high nibble; codebook -127 -104 -83 -65 -49
+ *    -35 -22 -10 1 13 25 38 53 69 89 113 (the format's table: parity unpinned, no page prints it).
  *  - Q4_K 6-bit scale/min unpacking (the page's description is garbled) follows GGUF:
  *    j < 4: sc = s[j] & 63, m = s[j+4] & 63;
  *    j >= 4: sc = (s[j+4] & 15) | ((s[j-4] >> 6) << 4), m = (s[j+4] >> 4) | ((s[j] >> 6) << 4).
@@ -58,9 +74,11 @@
 
 #define ORC_Q4_0 2
 #define ORC_Q8_0 8
+#define ORC_Q3_K 11
 #define ORC_Q4_K 12
 #define ORC_Q5_K 13
 #define ORC_Q6_K 14
+#define ORC_IQ4_XS 23
 
 #define ORC_OK 0
 #define ORC_ERR -1
@@ -242,6 +260,40 @@ static void decode_q4_0(const uint8_t *blk, double *d, int code[32]) {
     }
 }
 
+/* Q3_K, 110 bytes per 256 values: code[v] = 3-bit value - 4 in [-4, 3], sc[v/16] = 6-bit scale - 32. */
+static void decode_q3_K(const uint8_t *blk, double *d, int sc[16], int code[256]) {
+    const uint8_t *hmask = blk, *qs = blk + 32, *s = blk + 96;
+    *d = oracle_half_to_double(rd16(blk + 108));
+    for (int i = 0; i < 4; ++i) {
+        sc[i] = ((s[i] & 15) | ((s[8 + i] & 3) << 4)) - 32;
+        sc[4 + i] = ((s[4 + i] & 15) | (((s[8 + i] >> 2) & 3) << 4)) - 32;
+        sc[8 + i] = ((s[i] >> 4) | (((s[8 + i] >> 4) & 3) << 4)) - 32;
+        sc[12 + i] = ((s[4 + i] >> 4) | (((s[8 + i] >> 6) & 3) << 4)) - 32;
+    }
+    for (int v = 0; v < 256; ++v) {
+        const int h = v / 128, j = (v % 128) / 32, l = v % 32;
+        const int low = (qs[32 * h + l] >> (2 * j)) & 3;
+        const int top = (hmask[l] >> (4 * h + j)) & 1;
+        code[v] = low + 4 * top - 4;
+    }
+}
+
+/* IQ4_XS, 136 bytes per 256 values: code[v] = codebook entry of its 4-bit index, sc[v/32] = 6-bit
+ * scale - 32. */
+static const int iq4_codebook[16] = {-127, -104, -83, -65, -49, -35, -22, -10, 1, 13, 25, 38, 53, 69, 89, 113};
+static void decode_iq4_xs(const uint8_t *blk, double *d, int sc[8], int code[256]) {
+    *d = oracle_half_to_double(rd16(blk + 0));
+    const int sh = rd16(blk + 2);
+    const uint8_t *sl = blk + 4, *qs = blk + 8;
+    for (int b = 0; b < 8; ++b) {
+        sc[b] = (((sl[b / 2] >> (4 * (b % 2))) & 15) | (((sh >> (2 * b)) & 3) << 4)) - 32;
+        for (int i = 0; i < 16; ++i) {
+            code[32 * b + i] = iq4_codebook[qs[16 * b + i] & 15];
+            code[32 * b + 16 + i] = iq4_codebook[qs[16 * b + i] >> 4];
+        }
+    }
+}
+
 static void decode_q8_1(const uint8_t *blk, double *d, double *s, int code[32]) {
     *d = oracle_half_to_double(rd16(blk + 0));
     *s = oracle_half_to_double(rd16(blk + 2));
@@ -249,7 +301,7 @@ static void decode_q8_1(const uint8_t *blk, double *d, double *s, int code[32]) 
 }
 
 static int type_block_values(int type) {
-    if (type == ORC_Q4_K || type == ORC_Q5_K || type == ORC_Q6_K) return 256;
+    if (type == ORC_Q4_K || type == ORC_Q5_K || type == ORC_Q6_K || type == ORC_Q3_K || type == ORC_IQ4_XS) return 256;
     if (type == ORC_Q8_0 || type == ORC_Q4_0) return 32;
     return 0;
 }
@@ -259,6 +311,8 @@ static int type_block_bytes(int type) {
     if (type == ORC_Q6_K) return 210;
     if (type == ORC_Q8_0) return 34;
     if (type == ORC_Q4_0) return 18;
+    if (type == ORC_Q3_K) return 110;
+    if (type == ORC_IQ4_XS) return 136;
     return 0;
 }
 
@@ -268,9 +322,9 @@ int64_t oracle_row_bytes(int type, int64_t k) {
     return (k / bv) * type_block_bytes(type);
 }
 
-/* Number of integer sub-block dots per (row, column): Q6_K has 16-value sub-blocks. */
+/* Number of integer sub-block dots per (row, column): Q6_K and Q3_K have 16-value sub-blocks. */
 int64_t oracle_subdots_per_row(int type, int64_t k) {
-    if (type == ORC_Q6_K) return k / 16;
+    if (type == ORC_Q6_K || type == ORC_Q3_K) return k / 16;
     return k / 32;
 }
 
@@ -290,10 +344,15 @@ int oracle_dequantize(int type, const uint8_t *w, int64_t rows, int64_t k, doubl
                 if (type == ORC_Q4_K) decode_q4_K(p, &d, &dmin, sc, m, code);
                 else decode_q5_K(p, &d, &dmin, sc, m, code);
                 for (int v = 0; v < 256; ++v) o[v] = d * sc[v / 32] * code[v] - dmin * m[v / 32];
-            } else if (type == ORC_Q6_K) {
+            } else if (type == ORC_Q6_K || type == ORC_Q3_K) {
                 double d; int sc[16], code[256];
-                decode_q6_K(p, &d, sc, code);
+                if (type == ORC_Q6_K) decode_q6_K(p, &d, sc, code);
+                else decode_q3_K(p, &d, sc, code);
                 for (int v = 0; v < 256; ++v) o[v] = d * sc[v / 16] * code[v];
+            } else if (type == ORC_IQ4_XS) {
+                double d; int sc[8], code[256];
+                decode_iq4_xs(p, &d, sc, code);
+                for (int v = 0; v < 256; ++v) o[v] = d * sc[v / 32] * code[v];
             } else {
                 double d; int code[32];
                 if (type == ORC_Q8_0) decode_q8_0(p, &d, code);
@@ -371,10 +430,11 @@ static float dot_row_col(int type, const uint8_t *wrow, int64_t k, const act_t *
                 acc += d * sc[j] * da[b] * (double)Db - dmin * m[j] * sa[b];
             }
         }
-    } else if (type == ORC_Q6_K) {
+    } else if (type == ORC_Q6_K || type == ORC_Q3_K) {
         for (int64_t sb = 0; sb < k / 256; ++sb) {
             double d; int sc[16], code[256];
-            decode_q6_K(wrow + sb * 210, &d, sc, code);
+            if (type == ORC_Q6_K) decode_q6_K(wrow + sb * 210, &d, sc, code);
+            else decode_q3_K(wrow + sb * 110, &d, sc, code);
             for (int j = 0; j < 8; ++j) {           /* one q8_1 block = two 16-value sub-blocks */
                 int64_t b = sb * 8 + j;
                 int32_t D0 = 0, D1 = 0;
@@ -382,6 +442,18 @@ static float dot_row_col(int type, const uint8_t *wrow, int64_t k, const act_t *
                 for (int i = 16; i < 32; ++i) D1 += code[32 * j + i] * qa[b * 32 + i];
                 if (D) { D[2 * b] = D0; D[2 * b + 1] = D1; }
                 acc += d * da[b] * ((double)sc[2 * j] * D0 + (double)sc[2 * j + 1] * D1);
+            }
+        }
+    } else if (type == ORC_IQ4_XS) {   /* one scale per 32-value sub-block */
+        for (int64_t sb = 0; sb < k / 256; ++sb) {
+            double d; int sc[8], code[256];
+            decode_iq4_xs(wrow + sb * 136, &d, sc, code);
+            for (int j = 0; j < 8; ++j) {
+                int64_t b = sb * 8 + j;
+                int32_t Db = 0;
+                for (int i = 0; i < 32; ++i) Db += code[32 * j + i] * qa[b * 32 + i];
+                if (D) D[b] = Db;
+                acc += d * sc[j] * da[b] * (double)Db;
             }
         }
     } else { /* Q8_0, Q4_0: one scale per 32-value block */

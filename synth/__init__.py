@@ -12,6 +12,10 @@ Value distributions (the workload descriptions give Q4_K's; the rest are the pla
   * Q6_K super-block (210 B): uniform random ql (128 B) and qh (64 B); int8 scales ~ U{-32..31};
     fp16 d ~ U(0.001, 0.02).
   * Q8_0 block (34 B): fp16 d ~ U(0.001, 0.02); int8 codes ~ U{-127..127}.
+  * Q3_K super-block (110 B): uniform random hmask (32 B), qs (64 B) and 6-bit-packed scales
+    (12 B); fp16 d ~ U(0.001, 0.02).
+  * IQ4_XS super-block (136 B): fp16 d ~ U(0.001, 0.02); uniform random scale bits (2 + 4 B) and
+    4-bit codebook indices (128 B).
   * Activations: N(0, 1) fp32.
   * MoE routing: expert e has probability proportional to (e + 1)^-s; each token draws top_k
     distinct experts by successive sampling without replacement.
@@ -24,9 +28,11 @@ Q4_0 = 2
 Q4_K = 12
 Q5_K = 13
 Q6_K = 14
-TYPE_NAMES = {Q4_0: "q4_0", Q8_0: "q8_0", Q4_K: "q4_K", Q5_K: "q5_K", Q6_K: "q6_K"}
-BLOCK_VALUES = {Q4_0: 32, Q8_0: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256}
-BLOCK_BYTES = {Q4_0: 18, Q8_0: 34, Q4_K: 144, Q5_K: 176, Q6_K: 210}
+Q3_K = 11
+IQ4_XS = 23
+TYPE_NAMES = {Q4_0: "q4_0", Q8_0: "q8_0", Q4_K: "q4_K", Q5_K: "q5_K", Q6_K: "q6_K", Q3_K: "q3_K", IQ4_XS: "iq4_xs"}
+BLOCK_VALUES = {Q4_0: 32, Q8_0: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256, Q3_K: 256, IQ4_XS: 256}
+BLOCK_BYTES = {Q4_0: 18, Q8_0: 34, Q4_K: 144, Q5_K: 176, Q6_K: 210, Q3_K: 110, IQ4_XS: 136}
 
 
 def rngs(seed, n):
@@ -57,6 +63,10 @@ def gen_weights(qtype, rows, k, rng):
     elif qtype == Q8_0:
         blk[:, 0:2] = _fp16_bytes(rng.uniform(0.001, 0.02, size=nb))
         blk[:, 2:34] = rng.integers(-127, 128, size=(nb, 32)).astype(np.int8).view(np.uint8)
+    elif qtype == Q3_K:
+        blk[:, 108:110] = _fp16_bytes(rng.uniform(0.001, 0.02, size=nb))
+    elif qtype == IQ4_XS:
+        blk[:, 0:2] = _fp16_bytes(rng.uniform(0.001, 0.02, size=nb))
     else:
         raise ValueError(qtype)
     return blk.reshape(rows, (k // qk) * bb)

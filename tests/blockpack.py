@@ -11,6 +11,8 @@ sub-blocks, and the Q6_K ql/qh bit composition):
   q6_K: ql[128] @0, qh[64] @128, int8 scales[16] @192, d f16 @208
   q8_0: d f16 @0, int8 qs[32] @2
   q4_0: d f16 @0, qs[16] @2 (low nibble of qs[i] = value i, high nibble = value i + 16; code q - 8)
+  q3_K, iq4_xs: below, beside their encoders (the GP100 patch page names both types, Q3_K's -4
+  code offset and IQ4_XS's codebook; the layouts are GGUF's)
 """
 import numpy as np
 
@@ -175,6 +177,10 @@ def weight_codes(qtype, fields):
         return np.concatenate([f[1] for f in fields]).astype(np.int64) - 8
     if qtype == 14:
         return np.concatenate([f[2] for f in fields]).astype(np.int64) - 32
+    if qtype == 11:
+        return np.concatenate([f[2] for f in fields]).astype(np.int64) - 4
+    if qtype == 23:
+        return np.array(IQ4_CODEBOOK, dtype=np.int64)[np.concatenate([f[2] for f in fields])]
     return np.concatenate([f[1] for f in fields]).astype(np.int64)
 
 
@@ -189,3 +195,76 @@ def q8_1_scales(xq_row):
     d = blk[:, 0:2].copy().view(np.float16).reshape(-1).astype(np.float64)
     s = blk[:, 2:4].copy().view(np.float16).reshape(-1).astype(np.float64)
     return d, s
+
+
+# q3_K: hmask[32] @0, qs[64] @32, 12 bytes of packed 6-bit scales @96, d f16 @108.  Value v sits in
+# half h = v // 128, shift group j = (v % 128) // 32, lane l = v % 32: its low two bits are bits
+# 2j, 2j+1 of qs[32h + l] and its third bit is bit 4h + j of hmask[l].  Scale t (values 16t..):
+# its low nibble in byte t % 8 (t < 8: low nibble; t >= 8: high nibble; bytes 0-3 for t % 8 < 4,
+# 4-7 otherwise), its top two bits in byte 8 + t % 4 at bit 2 * (t // 4).
+def pack_q3_K(d, sc6, q):
+    """sc6: 16 ints in [0,63] (stored scales, value = sc6 - 32); q: 256 ints in [0,7] (stored
+    3-bit codes, value = q - 4).  Returns 110 bytes."""
+    sc6 = [int(v) for v in sc6]
+    q = [int(v) for v in q]
+    assert len(sc6) == 16 and len(q) == 256
+    assert all(0 <= v < 64 for v in sc6) and all(0 <= v < 8 for v in q)
+    b = np.zeros(110, dtype=np.uint8)
+    for v in range(256):
+        h, j, l = v // 128, (v % 128) // 32, v % 32
+        b[32 + 32 * h + l] |= (q[v] & 3) << (2 * j)
+        b[l] |= (q[v] >> 2) << (4 * h + j)
+    for t in range(16):
+        low, top = sc6[t] & 15, sc6[t] >> 4
+        byte = t % 8
+        b[96 + byte] |= low if t < 8 else low << 4
+        b[96 + 8 + t % 4] |= top << (2 * (t // 4))
+    _put16(b, 108, f16_bits(d))
+    return b
+
+
+# iq4_xs: d f16 @0, scales_h u16 @2 (bits 2b, 2b+1: top bits of sub-block b's scale), scales_l[4]
+# @4 (sub-block b's low nibble in byte b // 2, low nibble for even b), qs[128] @8 (sub-block b:
+# bytes 16b..16b+15, low nibble of byte i = index of value i, high nibble = value 16 + i).
+def pack_iq4_xs(d, ls, idx):
+    """ls: 8 ints in [0,63] (stored scales, value = ls - 32); idx: 256 codebook indices in [0,15]."""
+    ls = [int(v) for v in ls]
+    idx = [int(v) for v in idx]
+    assert len(ls) == 8 and len(idx) == 256
+    assert all(0 <= v < 64 for v in ls) and all(0 <= v < 16 for v in idx)
+    b = np.zeros(136, dtype=np.uint8)
+    _put16(b, 0, f16_bits(d))
+    sh = 0
+    for sb in range(8):
+        sh |= (ls[sb] >> 4) << (2 * sb)
+        b[4 + sb // 2] |= (ls[sb] & 15) << (4 * (sb % 2))
+        for i in range(16):
+            b[8 + 16 * sb + i] = idx[32 * sb + i] | (idx[32 * sb + 16 + i] << 4)
+    _put16(b, 2, sh)
+    return b
+
+
+# The IQ4_XS codebook (the format's fixed 16-entry table; no page prints its values).
+IQ4_CODEBOOK = [-127, -104, -83, -65, -49, -35, -22, -10, 1, 13, 25, 38, 53, 69, 89, 113]
+
+
+def random_q3_K_row(rng, k):
+    blocks, fields = [], []
+    for _ in range(k // 256):
+        d = f16_value(rng.uniform(0.001, 0.02))
+        sc6 = rng.integers(0, 64, 16)
+        q = rng.integers(0, 8, 256)
+        blocks.append(pack_q3_K(d, sc6, q))
+        fields.append((d, sc6, q))
+    return np.concatenate(blocks), fields
+
+
+def random_iq4_xs_row(rng, k):
+    blocks, fields = [], []
+    for _ in range(k // 256):
+        d = f16_value(rng.uniform(0.001, 0.02))
+        ls = rng.integers(0, 64, 8)
+        idx = rng.integers(0, 16, 256)
+        blocks.append(pack_iq4_xs(d, ls, idx))
+        fields.append((d, ls, idx))
+    return np.concatenate(blocks), fields

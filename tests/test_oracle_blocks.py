@@ -223,3 +223,105 @@ def test_bad_arguments_rejected():
         oracle.dequantize(oracle.Q4_K, np.zeros(144, np.uint8), 1, 100)
     with pytest.raises(ValueError):
         oracle.dequantize(99, np.zeros(144, np.uint8), 1, 256)
+
+
+# ---------------------------------------------------------------------------------------------
+# Q3_K (GP100 patch page, "How" step 3: the type's codes carry a -4 offset; layout GGUF's)
+# ---------------------------------------------------------------------------------------------
+from blockpack import IQ4_CODEBOOK, pack_iq4_xs, pack_q3_K  # noqa: E402
+
+
+def test_q3_K_encoder_roundtrip_random():
+    rng = np.random.default_rng(31)
+    for _ in range(50):
+        d = f16_value(rng.uniform(-2, 2))
+        sc6 = rng.integers(0, 64, 16)
+        q = rng.integers(0, 8, 256)
+        w = oracle.dequantize(oracle.Q3_K, pack_q3_K(d, sc6, q), 1, 256)[0]
+        assert np.array_equal(w, d * np.repeat(sc6 - 32, 16) * (q - 4))
+
+
+@pytest.mark.parametrize("v", list(range(0, 256, 7)) + [31, 32, 127, 128, 255])
+def test_q3_K_one_hot_position(v):
+    q = np.full(256, 4); q[v] = 7                 # code +3 at v, zero everywhere else
+    w = oracle.dequantize(oracle.Q3_K, pack_q3_K(1.0, np.full(16, 33), q), 1, 256)[0]
+    assert np.nonzero(w)[0].tolist() == [v] and w[v] == 3.0
+
+
+@pytest.mark.parametrize("t", range(16))
+def test_q3_K_single_scale(t):
+    sc6 = np.full(16, 32); sc6[t] = 32 + 5        # scale 5 on sub-block t, 0 elsewhere
+    w = oracle.dequantize(oracle.Q3_K, pack_q3_K(1.0, sc6, np.full(256, 5)), 1, 256)[0]
+    assert np.nonzero(w)[0].tolist() == list(range(16 * t, 16 * t + 16))
+    assert np.all(w[16 * t:16 * t + 16] == 5.0)
+
+
+def test_q3_K_hand_placed_bits():
+    """Bytes set by hand from the layout statement (not by the encoder): hmask[5] = 0x10 is the
+    third bit of value 128 + 5 (h = 1, j = 0); qs[32 + 7] = 0x30 puts low bits 3 on value
+    128 + 2*32 + 7 = 199 (h = 1, j = 2); scale bytes: s[2] = 0x0F and s[10] = 0x03 give scale 2 the
+    stored value 63, s[8 + 1] = 0x40 puts top bits 01 on scale 13 (= 4 + 1 + 8), whose low nibble is the
+    high nibble of s[5]; all other stored codes 0 (value -4) and scales 0 (value -32)."""
+    b = np.zeros(110, dtype=np.uint8)
+    b[5] = 0x10
+    b[32 + 32 + 7] = 0x30
+    b[96 + 2] = 0x0F
+    b[96 + 10] = 0x03
+    b[96 + 9] = 0x40
+    b[96 + 5] = 0x20
+    b[108], b[109] = 0x00, 0x3C                   # d = 1.0
+    w = oracle.dequantize(oracle.Q3_K, b, 1, 256)[0]
+    sc = np.full(16, -32); sc[2] = 63 - 32; sc[13] = (0x2 | (1 << 4)) - 32
+    code = np.full(256, -4); code[133] = 4 - 4; code[199] = 3 - 4
+    assert np.array_equal(w, np.repeat(sc, 16) * code)
+
+
+# ---------------------------------------------------------------------------------------------
+# IQ4_XS (GP100 patch page, "How" step 3: a non-linear 4-bit codebook; layout GGUF's).  The
+# codebook's 16 values are the format's table: no page prints them, so they are unpinned beyond
+# the properties below; the index and scale placement is pinned.
+# ---------------------------------------------------------------------------------------------
+def _iq4_code_of(idx):
+    w = oracle.dequantize(oracle.IQ4_XS, pack_iq4_xs(1.0, np.full(8, 33), np.full(256, idx)), 1, 256)[0]
+    assert np.all(w == w[0])
+    return w[0]
+
+
+def test_iq4_xs_codebook_properties():
+    cb = [_iq4_code_of(i) for i in range(16)]
+    assert cb == [float(v) for v in IQ4_CODEBOOK]
+    assert all(a < b for a, b in zip(cb, cb[1:]))              # strictly increasing
+    assert cb[0] == -127 and max(abs(v) for v in cb) == 127    # within int8, symmetric extreme
+
+
+def test_iq4_xs_encoder_roundtrip_random():
+    rng = np.random.default_rng(32)
+    for _ in range(50):
+        d = f16_value(rng.uniform(-2, 2))
+        ls = rng.integers(0, 64, 8)
+        idx = rng.integers(0, 16, 256)
+        w = oracle.dequantize(oracle.IQ4_XS, pack_iq4_xs(d, ls, idx), 1, 256)[0]
+        assert np.array_equal(w, d * np.repeat(ls - 32, 32) * np.array(IQ4_CODEBOOK)[idx])
+
+
+@pytest.mark.parametrize("v", list(range(0, 256, 9)) + [15, 16, 31, 32, 255])
+def test_iq4_xs_one_hot_position(v):
+    idx = np.full(256, 8); idx[v] = 15            # codebook entry 8 (= 1) everywhere, entry 15 at v
+    w = oracle.dequantize(oracle.IQ4_XS, pack_iq4_xs(1.0, np.full(8, 33), idx), 1, 256)[0]
+    assert np.nonzero(w != 1.0)[0].tolist() == [v] and w[v] == IQ4_CODEBOOK[15]
+
+
+def test_iq4_xs_hand_placed_bits():
+    """Bytes set by hand: scales_h = 0x8000 gives sub-block 7 top scale bits 10; scales_l[3] =
+    0x50 its low nibble 5 (odd sub-block: high nibble) -> stored 37, scale 5; every other
+    sub-block stores 0 (scale -32).  qs[8 + 16*7 + 3] = 0xF0: value 32*7 + 16 + 3 = 243 takes
+    index 15, every other index 0."""
+    b = np.zeros(136, dtype=np.uint8)
+    b[0], b[1] = 0x00, 0x3C                       # d = 1.0
+    b[2], b[3] = 0x00, 0x80
+    b[4 + 3] = 0x50
+    b[8 + 16 * 7 + 3] = 0xF0
+    w = oracle.dequantize(oracle.IQ4_XS, b, 1, 256)[0]
+    sc = np.full(8, -32); sc[7] = 37 - 32
+    code = np.full(256, IQ4_CODEBOOK[0]); code[243] = IQ4_CODEBOOK[15]
+    assert np.array_equal(w, np.repeat(sc, 32) * code)

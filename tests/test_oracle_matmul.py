@@ -11,11 +11,14 @@ import pytest
 import oracle
 import synth
 from blockpack import (pack_q4_K, random_q4_0_row, random_q4_K_row, random_q5_K_row, random_q6_K_row, random_q8_0_row,
+                       random_q3_K_row, random_iq4_xs_row,
                        weight_codes,
                        q8_1_codes, q8_1_scales)
 
 ROWGEN = {oracle.Q4_K: random_q4_K_row, oracle.Q5_K: random_q5_K_row, oracle.Q6_K: random_q6_K_row,
-          oracle.Q8_0: random_q8_0_row, oracle.Q4_0: random_q4_0_row}
+          oracle.Q8_0: random_q8_0_row, oracle.Q4_0: random_q4_0_row, oracle.Q3_K: random_q3_K_row,
+          oracle.IQ4_XS: random_iq4_xs_row}
+ALL_TYPES = [oracle.Q4_K, oracle.Q5_K, oracle.Q6_K, oracle.Q8_0, oracle.Q4_0, oracle.Q3_K, oracle.IQ4_XS]
 
 
 def _rows(qtype, rows, k, rng):
@@ -23,7 +26,7 @@ def _rows(qtype, rows, k, rng):
     return np.stack(data), list(fields)
 
 
-@pytest.mark.parametrize("qtype", [oracle.Q4_K, oracle.Q5_K, oracle.Q6_K, oracle.Q8_0, oracle.Q4_0])
+@pytest.mark.parametrize("qtype", ALL_TYPES)
 def test_subdots_brute_force(qtype):
     """Integer dots from the encoder's own codes and the q8_1 bytes, summed in Python ints."""
     rng = np.random.default_rng(20)
@@ -32,7 +35,7 @@ def test_subdots_brute_force(qtype):
     x = rng.standard_normal((n, k)).astype(np.float32)
     xq = oracle.quantize_q8_1(x)
     D = oracle.subdots(qtype, w, rows, k, xq, n)
-    sub = 16 if qtype == oracle.Q6_K else 32
+    sub = 16 if qtype in (oracle.Q6_K, oracle.Q3_K) else 32
     assert D.shape == (n, rows, k // sub)
     for c in range(n):
         qa = q8_1_codes(xq[c])
@@ -58,7 +61,7 @@ def _min_correction(qtype, fields, xq_row):
     return corr
 
 
-@pytest.mark.parametrize("qtype", [oracle.Q4_K, oracle.Q5_K, oracle.Q6_K, oracle.Q8_0, oracle.Q4_0])
+@pytest.mark.parametrize("qtype", ALL_TYPES)
 @pytest.mark.parametrize("shape", [(7, 256, 3), (16, 1024, 5), (3, 512, 17)])
 def test_matches_fp64_dequantize_then_multiply(qtype, shape):
     """Y equals the fp64 product of the dequantized weights and dequantized q8_1 activations
