@@ -49,7 +49,7 @@ static void *xmalloc(size_t n) {
     return p;
 }
 
-static const int kTypes[] = {2, 8, 12, 13, 14};   /* Q4_0, Q8_0, Q4_K, Q5_K, Q6_K */
+static const int kTypes[] = {2, 8, 11, 12, 13, 14, 23};   /* Q4_0, Q8_0, Q3_K, Q4_K, Q5_K, Q6_K, IQ4_XS */
 
 /* random block bytes with every fp16 field a finite value in [0.001, 0.02] */
 static void fill_weights(int type, uint8_t *w, int64_t rows, int64_t k) {
@@ -62,6 +62,7 @@ static void fill_weights(int type, uint8_t *w, int64_t rows, int64_t k) {
         uint16_t d = oracle_float_to_half(0.001f + 0.019f * (float)(rnd() % 1000) / 1000.0f);
         uint16_t m = oracle_float_to_half(0.001f + 0.019f * (float)(rnd() % 1000) / 1000.0f);
         if (type == 14) { memcpy(p + 208, &d, 2); }
+        else if (type == 11) { memcpy(p + 108, &d, 2); }
         else { memcpy(p, &d, 2); if (type == 12 || type == 13) memcpy(p + 2, &m, 2); }
     }
 }
@@ -138,7 +139,7 @@ int main(void) {
     /* argument errors are reported, not acted on */
     float yv[4];
     if (oracle_matmul_q8_1(12, NULL, 1, 100, NULL, 1, yv) == 0) return 1;
-    if (oracle_matmul_q8_1(11, NULL, 1, 256, NULL, 1, yv) == 0) return 1;
+    if (oracle_matmul_q8_1(3, NULL, 1, 256, NULL, 1, yv) == 0) return 1;   /* unsupported type */
     printf("ok\n");
     return 0;
 }
