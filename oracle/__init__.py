@@ -59,6 +59,8 @@ def lib():
         L.oracle_subdots.restype = i32
         L.oracle_subdots_q6_K_folded.argtypes = [vp, i64, i64, vp, i64, vp]
         L.oracle_subdots_q6_K_folded.restype = i32
+        L.oracle_subdots_q3_K_folded.argtypes = [vp, i64, i64, vp, i64, vp]
+        L.oracle_subdots_q3_K_folded.restype = i32
         L.oracle_matmul.argtypes = [i32, vp, i64, i64, vp, i64, vp]
         L.oracle_matmul.restype = i32
         L.oracle_matmul_id.argtypes = [i32, vp, i64, i64, i64, vp, i64, vp, i64, i64, vp, vp]
@@ -175,6 +177,17 @@ def subdots_q6_K_folded(w, rows, k, xq, n):
     rc = lib().oracle_subdots_q6_K_folded(_ptr(w), rows, k, _ptr(xq), n, _ptr(F))
     if rc:
         raise ValueError("oracle_subdots_q6_K_folded: bad arguments")
+    return F
+
+
+def subdots_q3_K_folded(w, rows, k, xq, n):
+    """Q3_K: sc0*D0 + sc1*D1 per 32-value block (sc = 6-bit scale - 32), int32 [n, rows, k/32]."""
+    w = _c(w, np.uint8)
+    xq = _c(xq, np.uint8)
+    F = np.zeros((n, rows, k // 32), dtype=np.int32)
+    rc = lib().oracle_subdots_q3_K_folded(_ptr(w), rows, k, _ptr(xq), n, _ptr(F))
+    if rc:
+        raise ValueError("oracle_subdots_q3_K_folded: bad arguments")
     return F
 
 

@@ -551,6 +551,35 @@ int oracle_subdots_q6_K_folded(const uint8_t *w, int64_t rows, int64_t k, const 
     return ORC_OK;
 }
 
+/* Q3_K: the same folding with its scales (6-bit value - 32): sc[2b]*D[2b] + sc[2b+1]*D[2b+1]
+ * per 32-value q8_1 block, D over the codes q - 4 (GP100 patch page, "How" step 3).
+ * Output int32 [n][rows][k/32]. */
+int oracle_subdots_q3_K_folded(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n,
+                               int32_t *F) {
+    if (check_args(ORC_Q3_K, rows, k, n)) return ORC_ERR;
+    int64_t rb = oracle_row_bytes(ORC_Q3_K, k);
+    int64_t nb = k / 32;
+    int32_t *D = (int32_t *)malloc(sizeof(int32_t) * (size_t)(k / 16) + 4);
+    act_t a;
+    if (act_decode(&a, xq, n, k)) { act_free(&a); free(D); return ORC_ERR; }
+    for (int64_t c = 0; c < n; ++c)
+        for (int64_t r = 0; r < rows; ++r) {
+            const uint8_t *wrow = w + r * rb;
+            (void)dot_row_col(ORC_Q3_K, wrow, k, &a, c, D);
+            for (int64_t sb = 0; sb < k / 256; ++sb) {
+                double d; int sc[16], code[256];
+                decode_q3_K(wrow + sb * 110, &d, sc, code);
+                for (int j = 0; j < 8; ++j) {
+                    const int64_t b = sb * 8 + j;
+                    F[(c * rows + r) * nb + b] = sc[2 * j] * D[2 * b] + sc[2 * j + 1] * D[2 * b + 1];
+                }
+            }
+        }
+    act_free(&a);
+    free(D);
+    return ORC_OK;
+}
+
 /* fp32 activations -> q8_1 -> Y. */
 int oracle_matmul(int type, const uint8_t *w, int64_t rows, int64_t k, const float *x, int64_t n,
                   float *y) {

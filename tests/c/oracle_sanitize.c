@@ -22,6 +22,7 @@ int oracle_matmul_q8_1_at(int type, const uint8_t *w, int64_t rows, int64_t k, c
                           const int64_t *cols, const int64_t *rws, int64_t count, float *out);
 int oracle_subdots(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, int32_t *D);
 int oracle_subdots_q6_K_folded(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, int32_t *F);
+int oracle_subdots_q3_K_folded(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, int32_t *F);
 int oracle_matmul(int type, const uint8_t *w, int64_t rows, int64_t k, const float *x, int64_t n, float *y);
 int oracle_matmul_id(int type, const uint8_t *w, int64_t n_exp, int64_t rows, int64_t k, const float *x,
                      int64_t x_per_tok, const int32_t *ids, int64_t n_tok, int64_t top_k, float *y,
@@ -93,9 +94,9 @@ static int run_type(int type, int64_t rows, int64_t k, int64_t n) {
     if (n && oracle_matmul_q8_1_at(type, w, rows, k, xq, n, cols, rws, cnt, at)) return 1;
     int32_t *D = xmalloc(sizeof(int32_t) * (size_t)(n * rows * oracle_subdots_per_row(type, k)));
     if (oracle_subdots(type, w, rows, k, xq, n, D)) return 1;
-    if (type == 14) {
+    if (type == 14 || type == 11) {
         int32_t *F = xmalloc(sizeof(int32_t) * (size_t)(n * rows * nb));
-        if (oracle_subdots_q6_K_folded(w, rows, k, xq, n, F)) return 1;
+        if ((type == 14 ? oracle_subdots_q6_K_folded : oracle_subdots_q3_K_folded)(w, rows, k, xq, n, F)) return 1;
         free(F);
     }
     uint16_t *y16 = xmalloc(sizeof(uint16_t) * (size_t)(n * k));

@@ -179,3 +179,21 @@ def test_q6_K_folded_subdots_brute_force():
             for b in range(k // 32):
                 expect = sum(int(sc[v // 16]) * int(qw[v]) * int(qa[v]) for v in range(32 * b, 32 * b + 32))
                 assert F[c, r, b] == expect
+
+
+def test_q3_K_folded_subdots_brute_force():
+    """(sc[2b]-32)*D[2b] + (sc[2b+1]-32)*D[2b+1] per q8_1 block, D over the codes q - 4, from the
+    encoder's own scales and codes (GP100 page, "How" step 3: the -4 offset)."""
+    rng = np.random.default_rng(71)
+    rows, k, n = 4, 512, 2
+    w, fields = _rows(oracle.Q3_K, rows, k, rng)
+    xq = oracle.quantize_q8_1(rng.standard_normal((n, k)).astype(np.float32))
+    F = oracle.subdots_q3_K_folded(w, rows, k, xq, n)
+    for c in range(n):
+        qa = q8_1_codes(xq[c])
+        for r in range(rows):
+            qw = weight_codes(oracle.Q3_K, fields[r])
+            sc = np.concatenate([f[1] for f in fields[r]]) - 32
+            for b in range(k // 32):
+                expect = sum(int(sc[v // 16]) * int(qw[v]) * int(qa[v]) for v in range(32 * b, 32 * b + 32))
+                assert F[c, r, b] == expect
