@@ -1,4 +1,5 @@
-"""Python binding of libqmm: GGUF block-quantized (Q4_K / Q6_K / Q8_0) x q8_1 matmul on MI355X.
+"""Python binding of libqmm: GGUF block-quantized (Q4_K / Q5_K / Q6_K / Q8_0 / Q4_0 / Q3_K / IQ4_XS) x q8_1
+matmul on MI355X.
 
 Thin ctypes marshalling over the C ABI declared in include/qmm.h; every computation runs in the
 library's HIP kernels.  Function names follow the C entry points without the ``qmm_`` prefix.
@@ -18,8 +19,10 @@ Q8_0 = 8
 Q4_K = 12
 Q5_K = 13
 Q6_K = 14
-BLOCK_VALUES = {Q4_0: 32, Q8_0: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256}
-BLOCK_BYTES = {Q4_0: 18, Q8_0: 34, Q4_K: 144, Q5_K: 176, Q6_K: 210}
+Q3_K = 11
+IQ4_XS = 23
+BLOCK_VALUES = {Q4_0: 32, Q8_0: 32, Q4_K: 256, Q5_K: 256, Q6_K: 256, Q3_K: 256, IQ4_XS: 256}
+BLOCK_BYTES = {Q4_0: 18, Q8_0: 34, Q4_K: 144, Q5_K: 176, Q6_K: 210, Q3_K: 110, IQ4_XS: 136}
 Q8_1_BYTES = 36
 
 OVR_PATH, OVR_STREAMK, OVR_TILE_J, OVR_MV_STEPS, OVR_MV_KERNEL, OVR_FUSE_COLS = 1, 2, 3, 4, 5, 6
@@ -515,7 +518,7 @@ def debug_subdots(w, qtype, rows, k, xq, n, path):
     px = _need(xq, torch.uint8, "xq")
     _need_weights(w, qtype, rows, k, "w")
     _need_size(xq, n * (k // 32) * Q8_1_BYTES, "xq")
-    per = k // 16 if (qtype == Q6_K and path == PATH_MATVEC) else k // 32
+    per = k // 16 if (qtype in (Q6_K, Q3_K) and path == PATH_MATVEC) else k // 32
     out = torch.zeros((n, rows, per), dtype=torch.int32, device=xq.device)
     ws = _workspace(debug_subdots_workspace(qtype, rows, k, n, path), xq.device)
     _on_device(w=w, xq=xq, out=out, ws=ws)

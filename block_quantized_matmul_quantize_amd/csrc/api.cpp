@@ -56,7 +56,7 @@ constexpr int kSmallMax = 8;           // experts with <= 8 columns use the matr
 
 int block_values(int type) {
     switch (type) {
-        case QMM_Q4_K: case QMM_Q5_K: case QMM_Q6_K: return 256;
+        case QMM_Q4_K: case QMM_Q5_K: case QMM_Q6_K: case QMM_Q3_K: case QMM_IQ4_XS: return 256;
         case QMM_Q8_0: case QMM_Q4_0: return 32;
         default: return 0;
     }
@@ -68,6 +68,8 @@ int block_bytes(int type) {
         case QMM_Q6_K: return 210;
         case QMM_Q8_0: return 34;
         case QMM_Q4_0: return 18;
+        case QMM_Q3_K: return 110;
+        case QMM_IQ4_XS: return 136;
         default: return 0;
     }
 }
@@ -90,7 +92,9 @@ int device_cus() {
 
 qmm_status check_common(int type, int64_t rows, int64_t k, int64_t n) {
     const int qk = block_values(type);
-    if (qk == 0) return fail(QMM_ERR_TYPE, "unsupported weight type %d (supported: Q4_0=2, Q8_0=8, Q4_K=12, Q5_K=13, Q6_K=14)", type);
+    if (qk == 0)
+        return fail(QMM_ERR_TYPE, "unsupported weight type %d (supported: Q4_0=2, Q8_0=8, Q3_K=11, Q4_K=12, Q5_K=13, "
+                    "Q6_K=14, IQ4_XS=23)", type);
     if (rows <= 0) return fail(QMM_ERR_ARG, "rows must be >= 1 (got %lld)", (long long)rows);
     if (n < 0) return fail(QMM_ERR_ARG, "n must be >= 0 (got %lld)", (long long)n);
     if (k <= 0 || k % qk != 0) return fail(QMM_ERR_SHAPE, "k=%lld is not a positive multiple of the block size %d", (long long)k, qk);
@@ -105,7 +109,7 @@ qmm_status check_common(int type, int64_t rows, int64_t k, int64_t n) {
 int mmq_smem(int type, int J) {
     const bool k45 = type == QMM_Q4_K || type == QMM_Q5_K;
     const int wt = k45 ? kTI * 144 + (type == QMM_Q5_K ? kTI * 32 : 0)   // packed qs (+ Q5_K qh)
-                       : (type == QMM_Q6_K ? 2 * kTI * 272 : kTI * 272);
+                       : (type == QMM_Q6_K || type == QMM_Q3_K ? 2 * kTI * 272 : kTI * 272);
     const int wm = k45 ? kTI * 48 + 8 * J * 4 : 0;   // bf16 pieces of the mins and of s
     const int one = wt + 8 * kTI * 4 + wm + J * 272 + 8 * (J + 4) * 8;
     return k45 && J == 128 ? 2 * one : one;   // Q4_K / Q5_K 8-wave tiles: two step buffers
@@ -498,8 +502,12 @@ qmm_status qmm_matmul_q8_1(int type, const void *w, int64_t rows, int64_t k, con
 // ----------------------------------------------------------------------------------------------
 namespace {
 
+bool panel_type(int type) {
+    return type == QMM_Q4_K || type == QMM_Q5_K || type == QMM_Q6_K || type == QMM_Q8_0 || type == QMM_Q4_0;
+}
+
 qmm_status check_panel_shape(int type, int64_t rows, int64_t k) {
-    if (block_values(type) == 0)
+    if (!panel_type(type))
         return fail(QMM_ERR_TYPE, "unsupported weight type %d (supported: Q4_0=2, Q8_0=8, Q4_K=12, Q5_K=13, Q6_K=14)", type);
     if (rows <= 0) return fail(QMM_ERR_ARG, "rows must be >= 1 (got %lld)", (long long)rows);
     if (k <= 0 || k % 256 != 0)
@@ -512,7 +520,7 @@ qmm_status check_panel_shape(int type, int64_t rows, int64_t k) {
 }  // namespace
 
 uint64_t qmm_repack_bytes(int type, int64_t rows, int64_t k) {
-    if (block_values(type) == 0 || rows <= 0 || rows > (1ll << 31) || k <= 0 || k % 256 != 0 || k > kMaxK) return 0;
+    if (!panel_type(type) || rows <= 0 || rows > (1ll << 31) || k <= 0 || k % 256 != 0 || k > kMaxK) return 0;
     return (uint64_t)qmm::panel_bytes(type, rows, k);
 }
 
@@ -532,7 +540,7 @@ qmm_status qmm_repack(int type, const void *w, int64_t rows, int64_t k, void *wp
 }
 
 size_t qmm_matmul_packed_workspace(int type, int64_t rows, int64_t k, int64_t n) {
-    if (check_common(type, rows, k, n) || k % 256 != 0) return 0;
+    if (check_common(type, rows, k, n) || k % 256 != 0 || !panel_type(type)) return 0;
     return dense_layout(type, rows, k, n, false, load_ovr()).total;
 }
 
@@ -686,9 +694,9 @@ int id_tile_j(int type, int64_t pairs, int64_t n_exp, const qmm::Ovr &o) {
     // mean for many (a handful of hot experts then hold most columns; on the Zipf MoE shapes the
     // median expert has 0.7x the mean with 8 experts, 0.4x with 128), then the smallest tile that
     // covers it.  Measured: 8 experts x 128 mean columns 128-column tiles best, 128 experts x 128
-    // mean 64-column tiles best.  Q6_K keeps 128: its 4-wave tiles hold the unpacked planes and
-    // run one workgroup per CU.
-    if (type == QMM_Q6_K) return 128;
+    // mean 64-column tiles best.  Q6_K (and Q3_K, parked the same way) keeps 128: its 4-wave tiles
+    // hold the unpacked planes and run one workgroup per CU.
+    if (type == QMM_Q6_K || type == QMM_Q3_K) return 128;
     const int64_t mean = pairs / (n_exp > 0 ? n_exp : 1);
     const int64_t typical = n_exp > 16 ? mean / 2 : mean;
     return typical > 64 ? 128 : (typical > 32 ? 64 : 32);

@@ -8,9 +8,11 @@ namespace qmm {
 
 constexpr int kQ4_0 = 2;
 constexpr int kQ8_0 = 8;
+constexpr int kQ3_K = 11;
 constexpr int kQ4_K = 12;
 constexpr int kQ5_K = 13;
 constexpr int kQ6_K = 14;
+constexpr int kIQ4_XS = 23;
 
 // GGUF block geometry.
 template <int T> struct Fmt;
@@ -19,6 +21,29 @@ template <> struct Fmt<kQ5_K> { static constexpr int QK = 256, BYTES = 176; };
 template <> struct Fmt<kQ6_K> { static constexpr int QK = 256, BYTES = 210; };
 template <> struct Fmt<kQ8_0> { static constexpr int QK = 32, BYTES = 34; };
 template <> struct Fmt<kQ4_0> { static constexpr int QK = 32, BYTES = 18; };
+template <> struct Fmt<kQ3_K> { static constexpr int QK = 256, BYTES = 110; };
+template <> struct Fmt<kIQ4_XS> { static constexpr int QK = 256, BYTES = 136; };
+
+// Types whose scale changes every 16 values (Q6_K, Q3_K): their integer dots are per 16-value
+// sub-block.
+template <int T> constexpr bool kSub16 = T == kQ6_K || T == kQ3_K;
+
+// IQ4_XS: the format's 16-entry non-linear codebook (GP100 patch page, "How" step 3, names the
+// codebook; the values are GGUF's table), as int8 bytes in four dwords for a v_perm lookup.
+constexpr int8_t kIq4Codebook[16] = {-127, -104, -83, -65, -49, -35, -22, -10, 1, 13, 25, 38, 53, 69, 89, 113};
+constexpr uint32_t iq4_table_dword(int i) {
+    return (uint32_t)(uint8_t)kIq4Codebook[4 * i] | ((uint32_t)(uint8_t)kIq4Codebook[4 * i + 1] << 8) |
+           ((uint32_t)(uint8_t)kIq4Codebook[4 * i + 2] << 16) | ((uint32_t)(uint8_t)kIq4Codebook[4 * i + 3] << 24);
+}
+// Four 4-bit indices (one per byte, values 0..15) -> their four int8 codebook entries: v_perm picks
+// entries 0-7 and 8-15 by the low three bits, bit 3 chooses between the two.
+__device__ __forceinline__ uint32_t iq4_lookup4(uint32_t idx) {
+    const uint32_t sel = idx & 0x07070707u;
+    const uint32_t lo = __builtin_amdgcn_perm(iq4_table_dword(1), iq4_table_dword(0), sel);
+    const uint32_t hi = __builtin_amdgcn_perm(iq4_table_dword(3), iq4_table_dword(2), sel);
+    const uint32_t mask = ((idx >> 3) & 0x01010101u) * 0xFFu;
+    return (hi & mask) | (lo & ~mask);
+}
 
 constexpr int kQ8_1Bytes = 36;       // {fp16 d, fp16 s, int8 q[32]}
 constexpr int kSuper = 256;          // K values per planning step (one K-quant super-block)

@@ -75,13 +75,19 @@ template <int J> struct Cfg {
 // Q4_K and Q5_K share the super-block header, the scale/min packing and the fixup (the MMQ page
 // pairs them in its "Q4_K load" section); Q5_K adds a fifth code bit per value.
 template <int T> constexpr bool kK45 = T == kQ4_K || T == kQ5_K;
-// Q8_0 and Q4_0: one fp16 scale per 32-value block; parked alike (int8 codes + fp32 d).
-template <int T> constexpr bool kB32 = T == kQ8_0 || T == kQ4_0;
+// Q8_0, Q4_0 and IQ4_XS: one scale per 32-value block; parked alike (int8 codes + fp32 scale).
+template <int T> constexpr bool kB32 = T == kQ8_0 || T == kQ4_0 || T == kIQ4_XS;
+// Q6_K and Q3_K: a scale per 16 values, folded into the codes at park time (two int8 planes).
+template <int T> constexpr bool kQ6like = T == kQ6_K || T == kQ3_K;
+// Types whose K need only be a multiple of 32 (the last step may be partial).
+template <int T> constexpr bool kRaggedK = T == kQ8_0 || T == kQ4_0;
+// Types the panel layout (repack.hip) serves.
+template <int T> constexpr bool kPanel = T == kQ4_K || T == kQ5_K || T == kQ6_K || T == kQ8_0 || T == kQ4_0;
 
 // LDS layout of one step.
 template <int T, int J> struct Smem {
     static constexpr int W_BYTES = kK45<T> ? kTI * kLd4 + (T == kQ5_K ? kTI * 32 : 0)   // qs (+ Q5_K qh)
-                                          : (T == kQ6_K ? 2 * kTI * kLd : kTI * kLd);
+                                          : (kQ6like<T> ? 2 * kTI * kLd : kTI * kLd);
     static constexpr int W_OFF = 0;
     static constexpr int QH_OFF = kTI * kLd4;                                     // Q5_K qh [128][32]
     static constexpr int WS_OFF = W_OFF + W_BYTES;                               // float [8][128]
@@ -199,7 +205,8 @@ template <int T> __device__ __forceinline__ int panel_off(int o, int i) {
     } else if constexpr (T == kQ8_0) {
         const int b = o / 34, q = o - 34 * b;
         return q < 2 ? 16 * 256 + 16 * i + 2 * b + q : (2 * b + ((q - 2) >> 4)) * 256 + 16 * i + ((q - 2) & 15);
-    } else {   // Q4_0
+    } else {
+        static_assert(T == kQ4_0, "the panel layout serves Q4_K, Q5_K, Q6_K, Q8_0 and Q4_0");
         const int b = o / 18, q = o - 18 * b;
         return q < 2 ? 8 * 256 + 16 * i + 2 * b + q : b * 256 + 16 * i + (q - 2);
     }
@@ -488,6 +495,88 @@ template <int NT> struct WFetchQ6Reg {
 
 template <int NT> struct WFetch<kQ6_K, NT> : std::conditional<(NT >= 512), WFetchQ6Reg<NT>, WFetchQ6Direct<NT>>::type {};
 
+// Q3_K (GP100 patch page, "How" step 3: 3-bit codes with a -4 offset; a 6-bit scale - 32 per 16
+// values): parked like Q6_K, v = (sc - 32) * (q - 4) in [-124, 128] split into the two planes, the
+// fp16 d per row in the scale slot.  Unit (row, 16-value group G), unpacked straight from HBM at
+// park time: values 16G.. sit in half h = G/8, bit pair j = (G%8)/2, bytes l = 16(G&1)..: low bits
+// 2j.. of qs[32h + l], third bit 4h + j of hmask[l]; scale G: low nibble in byte G%8 of the 12
+// scale bytes (G < 8: low nibble, else high), top two bits at bit 2(G/4) of byte 8 + G%4.
+template <int NT> struct WFetchQ3 {
+    template <class WR>
+    __device__ __forceinline__ void fetch(const WR &, int64_t, int64_t) {}
+    template <int J, class WR>
+    __device__ __forceinline__ void store(uint8_t *sm, const WR &wr, int64_t kb, int64_t) const {
+        const int tid = threadIdx.x;
+        int8_t *sLo = (int8_t *)(sm + Smem<kQ3_K, J>::W_OFF);
+        int8_t *sHi = sLo + kTI * kLd;
+#pragma unroll 2
+        for (int it = 0; it < 2048 / NT; ++it) {
+            const int i = tid + NT * it;               // (row, 16-value group G): 128 x 16
+            const int r = i >> 4, G = i & 15;
+            const int h = G >> 3, j = (G & 7) >> 1, l0 = 16 * (G & 1);
+            const u32x4 qs = ld16(wr.template at<kQ3_K>(r, kb, 32 + 32 * h + l0));
+            const u32x4 hm = ld16(wr.template at<kQ3_K>(r, kb, l0));
+            const uint32_t lb = *wr.template at<kQ3_K>(r, kb, 96 + (G & 7));
+            const uint32_t tb = *wr.template at<kQ3_K>(r, kb, 104 + (G & 3));
+            const int sc = (int)((G < 8 ? (lb & 15u) : (lb >> 4)) | (((tb >> (2 * (G >> 2))) & 3u) << 4)) - 32;
+            const s16x2 sc2 = {(short)sc, (short)sc}, off2 = {(short)(-4 * sc), (short)(-4 * sc)};
+            const uint32_t qw[4] = {qs.x, qs.y, qs.z, qs.w}, hw[4] = {hm.x, hm.y, hm.z, hm.w};
+            uint32_t lo_w[4], hi_w[4];
+#pragma unroll
+            for (int dd = 0; dd < 4; ++dd) {
+                const uint32_t code3 = ((qw[dd] >> (2 * j)) & 0x03030303u) | (((hw[dd] >> (4 * h + j)) & 0x01010101u) << 2);
+                q6_split4(code3, sc2, off2, lo_w[dd], hi_w[dd]);
+            }
+            *(u32x4 *)(sLo + r * kLd + 16 * G) = u32x4{lo_w[0], lo_w[1], lo_w[2], lo_w[3]};
+            *(u32x4 *)(sHi + r * kLd + 16 * G) = u32x4{hi_w[0], hi_w[1], hi_w[2], hi_w[3]};
+        }
+        if (tid < kTI) {
+            float *sWs = (float *)(sm + Smem<kQ3_K, J>::WS_OFF);
+            sWs[tid] = h2f(ld2(wr.template at<kQ3_K>(tid, kb, 108)));
+        }
+    }
+};
+template <int NT> struct WFetch<kQ3_K, NT> : WFetchQ3<NT> {};
+
+// IQ4_XS (GP100 patch page, "How" step 3: a 4-bit codebook index and a 6-bit scale - 32 per 32
+// values): unit (row, sub-block b) -- the 16 index bytes qs[16b..] (low nibbles: values 0-15,
+// high: 16-31), mapped through the codebook to int8 codes and parked as Q8_0's; the fp32 scale
+// d * (ls - 32) with ls from nibble b&1 of scales_l[b/2] and bits 2b.. of scales_h.
+template <int NT> struct WFetch<kIQ4_XS, NT> {
+    static constexpr int N = 1024 / NT;
+    u32x4 q[N];
+    uint32_t h0[N], h1[N];
+    template <class WR>
+    __device__ __forceinline__ void fetch(const WR &wr, int64_t kb, int64_t) {
+        const int tid = threadIdx.x;
+#pragma unroll
+        for (int it = 0; it < N; ++it) {
+            const int i = tid + NT * it;   // (row i/8, sub-block i%8)
+            q[it] = ld16(wr.template at<kIQ4_XS>(i >> 3, kb, 8 + 16 * (i & 7)));
+            h0[it] = ld4(wr.template at<kIQ4_XS>(i >> 3, kb, 0));
+            h1[it] = ld4(wr.template at<kIQ4_XS>(i >> 3, kb, 4));
+        }
+    }
+    template <int J, class WR>
+    __device__ __forceinline__ void store(uint8_t *sm, const WR &, int64_t, int64_t) const {
+        const int tid = threadIdx.x;
+        uint8_t *sW = sm + Smem<kIQ4_XS, J>::W_OFF;
+        float *sWs = (float *)(sm + Smem<kIQ4_XS, J>::WS_OFF);
+#pragma unroll
+        for (int it = 0; it < N; ++it) {
+            const int i = tid + NT * it, b = i & 7;
+            uint8_t *dst = sW + (i >> 3) * kLd + 32 * b;
+            const u32x4 v = q[it];
+            *(u32x4 *)dst = u32x4{iq4_lookup4(v.x & 0x0F0F0F0Fu), iq4_lookup4(v.y & 0x0F0F0F0Fu),
+                                  iq4_lookup4(v.z & 0x0F0F0F0Fu), iq4_lookup4(v.w & 0x0F0F0F0Fu)};
+            *(u32x4 *)(dst + 16) = u32x4{iq4_lookup4((v.x >> 4) & 0x0F0F0F0Fu), iq4_lookup4((v.y >> 4) & 0x0F0F0F0Fu),
+                                         iq4_lookup4((v.z >> 4) & 0x0F0F0F0Fu), iq4_lookup4((v.w >> 4) & 0x0F0F0F0Fu)};
+            const int ls = (int)(((h1[it] >> (8 * (b >> 1) + 4 * (b & 1))) & 15u) | (((h0[it] >> (16 + 2 * b)) & 3u) << 4));
+            sWs[b * kTI + (i >> 3)] = h2f((uint16_t)(h0[it] & 0xFFFF)) * (float)(ls - 32);
+        }
+    }
+};
+
 // ---------------------------------------------------------------------------------------------
 // One 256-value step of MFMAs + fixups for this wave's 32 rows x JW columns.  Wave wid: row wave
 // rw = wid % 4 (rows 32*rw..), column wave cw = wid / 4 (columns JW*cw..).  Accumulator block cb,
@@ -696,7 +785,7 @@ __device__ __forceinline__ void run_tile(uint8_t *sm, f32x16 (&acc)[Cfg<J>::NCB]
         asm volatile("" : "+v"(cinit));
     }
     WFetch<T, Cfg<J>::NT> wf;
-    ActFetch<J, kB32<T>> af;
+    ActFetch<J, kRaggedK<T>> af;
     wf.fetch(wr, kb0, nb32);
     af.fetch(xq, nb32, kb0, acol, act_rows);
     uint8_t *const buf0 = sm, *const buf1 = sm + (DB ? Smem<T, J>::BYTES : 0);
@@ -1053,19 +1142,30 @@ static hipError_t launch_mmq_j(const uint8_t *w, int64_t rows, int64_t k, const 
     return hipErrorInvalidValue;
 }
 
+template <int T>
+static hipError_t launch_mmq_panels(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y,
+                                    const MmqLaunch &p, hipStream_t s) {
+    if constexpr (kPanel<T>) return launch_mmq_j<T, false, true>(w, rows, k, xq, n, y, nullptr, p, s);
+    else return hipErrorInvalidValue;
+}
+
 hipError_t launch_mmq(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y,
                       int32_t *dbg, const MmqLaunch &p, hipStream_t s) {
     const bool d = dbg != nullptr;
     if (p.packed && d) return hipErrorInvalidValue;   // no integer-dot export from panel weights
 #define QMM_MQ(TT)                                                                                    \
-    if (type == TT) return p.packed ? launch_mmq_j<TT, false, true>(w, rows, k, xq, n, y, dbg, p, s)   \
-                           : d ? launch_mmq_j<TT, true>(w, rows, k, xq, n, y, dbg, p, s)               \
-                               : launch_mmq_j<TT, false>(w, rows, k, xq, n, y, dbg, p, s);
+    if (type == TT) {                                                                                 \
+        if (p.packed) return launch_mmq_panels<TT>(w, rows, k, xq, n, y, p, s);                       \
+        return d ? launch_mmq_j<TT, true>(w, rows, k, xq, n, y, dbg, p, s)                           \
+                 : launch_mmq_j<TT, false>(w, rows, k, xq, n, y, dbg, p, s);                          \
+    }
     QMM_MQ(kQ4_K)
     QMM_MQ(kQ5_K)
     QMM_MQ(kQ6_K)
     QMM_MQ(kQ8_0)
     QMM_MQ(kQ4_0)
+    QMM_MQ(kQ3_K)
+    QMM_MQ(kIQ4_XS)
 #undef QMM_MQ
     return hipErrorInvalidValue;
 }
@@ -1097,6 +1197,8 @@ hipError_t launch_mmq_glu(int type, const uint8_t *wg, const uint8_t *wu, int64_
     QMM_MG(kQ6_K)
     QMM_MG(kQ8_0)
     QMM_MG(kQ4_0)
+    QMM_MG(kQ3_K)
+    QMM_MG(kIQ4_XS)
 #undef QMM_MG
     return hipErrorInvalidValue;
 }
@@ -1138,6 +1240,8 @@ hipError_t launch_mmq_id(int type, const uint8_t *w, const uint8_t *w_up, int64_
     QMM_MQI(kQ6_K)
     QMM_MQI(kQ8_0)
     QMM_MQI(kQ4_0)
+    QMM_MQI(kQ3_K)
+    QMM_MQI(kIQ4_XS)
 #undef QMM_MQI
     return hipErrorInvalidValue;
 }

@@ -332,6 +332,154 @@ template <int T> struct MvStepB32 {
 template <> struct MvStep<kQ8_0> : MvStepB32<kQ8_0> {};
 template <> struct MvStep<kQ4_0> : MvStepB32<kQ4_0> {};
 
+// ------------------------------------------------------------------------------------------
+// Q3_K: 110-byte super-block = {hmask[32], qs[64], 12 bytes of 6-bit scales, d}; value
+// d * (sc - 32) * (q - 4) with a 3-bit q and one scale per 16 values (GP100 patch page, "How"
+// step 3: the -4 offset).  Value v = 64p + 16g + i (MFMA p, lane group g, the 16-value sub-block
+// t = 4p + g, as for Q6_K): half h = p/2, bit pair j = 2(p&1) + g/2, byte l = 16(g&1) + i; its
+// low two bits are bits 2j.. of qs[32h + l], its third bit is bit 4h + j of hmask[l].  So lane g
+// of a row loads hmask[16(g&1)..], qs[16(g&1)..] and qs[32 + 16(g&1)..] once per step.  Scale t:
+// low nibble in byte 4(p&1) + g (p < 2: low nibble, else high), top two bits at bit 2p of byte
+// 8 + g.  D = sum q*q_a - 4*sum q_a: a second MFMA against a constant -4 operand.
+// ------------------------------------------------------------------------------------------
+template <> struct MvStep<kQ3_K> {
+    static constexpr int NCG = 2;
+    static constexpr int BYTES = 110;
+    u32x4 hm, qs0, qs1;
+    uint32_t s0, s1, s2, dbits;
+    u32x4 a[2][4];
+
+    __device__ static void lane_setup(MvLane &L, int m) { MvStep<kQ6_K>::lane_setup(L, m); }
+    __device__ static bool a_diag(int g, int m) { return g == (m >> 2); }
+    __device__ static int a_col(int m, int cg) { return (m & 3) + 4 * cg; }
+
+    __device__ __forceinline__ void load(const uint8_t *wg, const MvLane &L, int64_t step) {
+        const uint8_t *blk = wg + L.wrow_off + step * BYTES;
+        hm = ld16(blk + 16 * (L.g & 1));
+        qs0 = ld16(blk + 32 + 16 * (L.g & 1));
+        qs1 = ld16(blk + 64 + 16 * (L.g & 1));
+        s0 = ld4(blk + 96);
+        s1 = ld4(blk + 100);
+        s2 = ld4(blk + 104);
+        dbits = ld2(blk + 108);
+#pragma unroll
+        for (int cg = 0; cg < 2; ++cg)
+#pragma unroll
+            for (int p = 0; p < 4; ++p) a[cg][p] = ld16(L.abase[cg] + step * L.astride[cg] + L.aoff[cg][p]);
+    }
+
+    template <bool DBG>
+    __device__ __forceinline__ void compute(int64_t step, const MvLane &L, const float2 *sTab, float (&acc)[NCG][4],
+                                            int32_t *dbg_row, int64_t dbg_ld, int ncols) const {
+        const int g = L.g;
+        const float d = h2f((uint16_t)dbits);
+        const u32x4 neg4 = {0xFCFCFCFCu, 0xFCFCFCFCu, 0xFCFCFCFCu, 0xFCFCFCFCu};
+        const i32x4 zero = {0, 0, 0, 0};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const u32x4 Q = (p >> 1) ? qs1 : qs0;
+            const int j = 2 * (p & 1) + (g >> 1), hb = 4 * (p >> 1) + j;
+            u32x4 b;   // stored 3-bit codes (0..7)
+            b.x = ((Q.x >> (2 * j)) & 0x03030303u) | (((hm.x >> hb) & 0x01010101u) << 2);
+            b.y = ((Q.y >> (2 * j)) & 0x03030303u) | (((hm.y >> hb) & 0x01010101u) << 2);
+            b.z = ((Q.z >> (2 * j)) & 0x03030303u) | (((hm.z >> hb) & 0x01010101u) << 2);
+            b.w = ((Q.w >> (2 * j)) & 0x03030303u) | (((hm.w >> hb) & 0x01010101u) << 2);
+            const uint32_t lb = (((p & 1) ? s1 : s0) >> (8 * g)) & 0xFFu;
+            const int sc6 = (int)((p < 2 ? (lb & 15u) : (lb >> 4)) | (((s2 >> (8 * g + 2 * p)) & 3u) << 4));
+            const float ws = d * (float)(sc6 - 32);               // scale of sub-block 4p+g
+            const int64_t blk = step * 8 + 2 * p + (g >> 1);   // q8_1 block of this lane's sub-block
+#pragma unroll
+            for (int cg = 0; cg < NCG; ++cg) {
+                if (cg * 4 >= ncols) break;
+                i32x4 D = mfma16x16x64(a[cg][p], b, zero);
+                D = mfma16x16x64(a[cg][p], neg4, D);           // - 4 * sum(q_a) over the sub-block
+                if (DBG) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int c = 4 * cg + e;
+                        if (dbg_row && c < ncols) dbg_row[(int64_t)c * dbg_ld + step * 16 + 4 * p + g] = D[e];
+                    }
+                } else {
+                    const f32x4 t0 = *(const f32x4 *)(sTab + blk * 8 + 4 * cg);
+                    const f32x4 t1 = *(const f32x4 *)(sTab + blk * 8 + 4 * cg + 2);
+                    acc[cg][0] += (float)D[0] * (ws * t0.x);
+                    acc[cg][1] += (float)D[1] * (ws * t0.z);
+                    acc[cg][2] += (float)D[2] * (ws * t1.x);
+                    acc[cg][3] += (float)D[3] * (ws * t1.z);
+                }
+            }
+        }
+    }
+};
+
+// ------------------------------------------------------------------------------------------
+// IQ4_XS: 136-byte super-block = {d, scales_h (16 bits), scales_l[4], qs[128]}; value
+// d * (ls - 32) * cb[q] with a 4-bit codebook index q and one 6-bit scale ls per 32 values
+// (GP100 patch page, "How" step 3).  The lane roles are Q8_0's: MFMA p covers sub-blocks 2p (lane
+// groups 0, 1) and 2p+1 (2, 3); lane g takes half g&1 of sub-block b = 2p + g/2 -- the low
+// (values 0-15) or high nibbles (16-31) of qs[16b..16b+15] -- mapped through the codebook to
+// int8.  ls of sub-block b: nibble b&1 of scales_l[b/2], top two bits at bit 2b of scales_h.
+// ------------------------------------------------------------------------------------------
+template <> struct MvStep<kIQ4_XS> {
+    static constexpr int NCG = 1;
+    static constexpr int BYTES = 136;
+    uint32_t h0, h1;   // {d, scales_h}, scales_l
+    u32x4 q[4];
+    u32x4 a[4];
+
+    __device__ static void lane_setup(MvLane &L, int m) {
+        const int sel = m >> 3;
+        for (int p = 0; p < 4; ++p) L.aoff[0][p] = (uint32_t)((2 * p + sel) * kQ8_1Bytes + 4 + 16 * (L.g & 1));
+    }
+    __device__ static bool a_diag(int g, int m) { return (g >> 1) == (m >> 3); }
+    __device__ static int a_col(int m, int) { return m & 7; }
+
+    __device__ __forceinline__ void load(const uint8_t *wg, const MvLane &L, int64_t step) {
+        const uint8_t *blk = wg + L.wrow_off + step * BYTES;
+        h0 = ld4(blk);
+        h1 = ld4(blk + 4);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            q[p] = ld16(blk + 8 + 16 * (2 * p + (L.g >> 1)));
+            a[p] = ld16(L.abase[0] + step * L.astride[0] + L.aoff[0][p]);
+        }
+    }
+
+    template <bool DBG>
+    __device__ __forceinline__ void compute(int64_t step, const MvLane &L, const float2 *sTab, float (&acc)[NCG][4],
+                                            int32_t *dbg_row, int64_t dbg_ld, int ncols) const {
+        const int g = L.g;
+        const float d = h2f((uint16_t)(h0 & 0xFFFF));
+        const uint32_t sh = h0 >> 16;
+        const int nsh = 4 * (g & 1);
+        const i32x4 zero = {0, 0, 0, 0};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int b = 2 * p + (g >> 1);
+            const u32x4 c = {iq4_lookup4((q[p].x >> nsh) & 0x0F0F0F0Fu), iq4_lookup4((q[p].y >> nsh) & 0x0F0F0F0Fu),
+                             iq4_lookup4((q[p].z >> nsh) & 0x0F0F0F0Fu), iq4_lookup4((q[p].w >> nsh) & 0x0F0F0F0Fu)};
+            const i32x4 D = mfma16x16x64(a[p], c, zero);
+            const int64_t blk = step * 8 + b;
+            if (DBG) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int cc = 4 * (g & 1) + e;
+                    if (dbg_row && cc < ncols) dbg_row[(int64_t)cc * dbg_ld + blk] = D[e];
+                }
+            } else {
+                const int ls = (int)(((h1 >> (8 * (b >> 1) + 4 * (b & 1))) & 15u) | (((sh >> (2 * b)) & 3u) << 4));
+                const float ws = d * (float)(ls - 32);
+                const f32x4 t0 = *(const f32x4 *)(sTab + blk * 8 + 4 * (g & 1));
+                const f32x4 t1 = *(const f32x4 *)(sTab + blk * 8 + 4 * (g & 1) + 2);
+                acc[0][0] += (float)D[0] * (ws * t0.x);
+                acc[0][1] += (float)D[1] * (ws * t0.z);
+                acc[0][2] += (float)D[2] * (ws * t1.x);
+                acc[0][3] += (float)D[3] * (ws * t1.z);
+            }
+        }
+    }
+};
+
 constexpr int mv_max_waves(int spw) { return spw == 1 ? 16 : spw == 2 ? 8 : 4; }
 
 template <int T, int SPW, bool DBG, bool EXPERT, bool GLU>
@@ -407,7 +555,7 @@ __global__ __launch_bounds__(64 * mv_max_waves(SPW)) void mmvq_kernel(const uint
     int32_t *dbg_row = nullptr;
     int64_t dbg_ld = 0;
     if (DBG && row < rows) {
-        const int64_t per = (T == kQ6_K) ? k / 16 : nb;
+        const int64_t per = kSub16<T> ? k / 16 : nb;
         dbg_ld = rows * per;
         dbg_row = dbg + row * per;
     }
@@ -443,13 +591,13 @@ __global__ __launch_bounds__(64 * mv_max_waves(SPW)) void mmvq_kernel(const uint
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             float v = acc[cg][e];
-            if (T == kQ6_K) v += __shfl_xor(v, 16);
+            if (kSub16<T>) v += __shfl_xor(v, 16);
             v += __shfl_xor(v, 32);
             acc[cg][e] = v;
         }
     // Lanes holding the wave's values: Q4_K/Q8_0 g in {0,1} (columns 4g..4g+3), Q6_K g == 0
     // (columns 4cg..4cg+3); 128 floats per wave.
-    const bool holder = (T == kQ6_K) ? (L.g == 0) : (L.g < 2);
+    const bool holder = kSub16<T> ? (L.g == 0) : (L.g < 2);
     if (holder) {
 #pragma unroll
         for (int cg = 0; cg < NCG; ++cg)
@@ -467,7 +615,7 @@ __global__ __launch_bounds__(64 * mv_max_waves(SPW)) void mmvq_kernel(const uint
                 v += sRed[wv * 128 + lane * (4 * NCG) + cg * 4 + e];
                 if (GLU) u += sRed[wv * 128 + (lane + 8) * (4 * NCG) + cg * 4 + e];   // the up row
             }
-            const int c = (T == kQ6_K) ? 4 * cg + e : 4 * L.g + e;
+            const int c = kSub16<T> ? 4 * cg + e : 4 * L.g + e;
             if (c < ncols) y[mc.pair(c) * rows + row] = GLU ? v / (1.0f + expf(-v)) * u : v;
         }
 }
@@ -579,6 +727,8 @@ hipError_t launch_mmvq(int type, const uint8_t *w, int64_t rows, int64_t k, cons
     QMM_MV(kQ6_K)
     QMM_MV(kQ8_0)
     QMM_MV(kQ4_0)
+    QMM_MV(kQ3_K)
+    QMM_MV(kIQ4_XS)
 #undef QMM_MV
     return hipErrorInvalidValue;
 }
@@ -606,6 +756,8 @@ hipError_t launch_mmvq_glu(int type, const uint8_t *wg, const uint8_t *wu, int64
     QMM_MVG(kQ6_K)
     QMM_MVG(kQ8_0)
     QMM_MVG(kQ4_0)
+    QMM_MVG(kQ3_K)
+    QMM_MVG(kIQ4_XS)
 #undef QMM_MVG
     return hipErrorInvalidValue;
 }

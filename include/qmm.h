@@ -1,6 +1,6 @@
 /*
- * qmm.h -- C ABI of libqmm: GGUF block-quantized weights (Q4_K, Q6_K, Q8_0) times fp32
- * activations quantized to q8_1, on AMD Instinct MI355X (gfx950).
+ * qmm.h -- C ABI of libqmm: GGUF block-quantized weights (Q4_K, Q5_K, Q6_K, Q8_0, Q4_0, Q3_K,
+ * IQ4_XS) times fp32 activations quantized to q8_1, on AMD Instinct MI355X (gfx950).
  *
  * Sources (the web pages this library implements):
  *  [MMQ]   "llama.cpp source walkthrough (15): quantized GEMM -- MMQ" (pinghaoyang.com.cn)
@@ -17,8 +17,11 @@
  *    back to back, rows back to back ([QMM] "QTensor": the last dimension must be a multiple of
  *    the block size and a block never spans rows).  QK = 256 for Q4_K/Q6_K, 32 for Q8_0.  Block
  *    bytes: Q4_K 144 {fp16 d, fp16 dmin, 12 B packed 6-bit scales/mins, 128 B nibbles};
- *    Q6_K 210 {128 B ql, 64 B qh, 16 int8 scales, fp16 d}; Q8_0 34 {fp16 d, 32 int8}.  Only
- *    2-byte alignment of w is required.
+ *    Q6_K 210 {128 B ql, 64 B qh, 16 int8 scales, fp16 d}; Q8_0 34 {fp16 d, 32 int8}; Q5_K 176 and
+ *    Q4_0 18 as GGUF's.  Q3_K 110 {32 B hmask, 64 B qs, 12 B of 6-bit scales, fp16 d} and IQ4_XS
+ *    136 {fp16 d, 16-bit scales_h, 4 B scales_l, 128 B of 4-bit codebook indices} ([GP100] "How"
+ *    step 3 names both, Q3_K's -4 code offset and IQ4_XS's codebook; the layouts and the codebook
+ *    are GGUF's).  Only 2-byte alignment of w is required.
  *  - Activations x are fp32 row-major [n][k] (token-major, [QMM] "QMatMul": input [..., k]),
  *    16-byte aligned (the kernels read 8 values per lane as two 16-byte loads); QMM_ERR_ARG
  *    otherwise.  Outputs y are fp32 row-major [n][rows] (output [..., n]), 4-byte aligned.
@@ -31,6 +34,8 @@
  *      Q4_K  y += d*sc_b*d_b*D_b - dmin*m_b*s_b
  *      Q6_K  y += d*d_b*(sc_{2b}*D_{2b} + sc_{2b+1}*D_{2b+1})   (16-value sub-blocks)
  *      Q8_0  y += dw_b*d_b*D_b
+ *      Q3_K  as Q6_K with sc = 6-bit scale - 32 and codes q - 4 (q 3-bit)
+ *      IQ4_XS y += d*(ls_b - 32)*d_b*D_b, D_b over the codebook values of the indices
  *    summed in fp32 in an order that depends on the chosen kernel (several fp32 results are
  *    correct; see qmm_set_override).  For a fixed plan the result is bitwise reproducible.
  *  - Errors: a status code; qmm_last_error() returns a message for the calling thread.
@@ -54,7 +59,9 @@ typedef enum {
     QMM_ERR_HIP = -5         /* a HIP call failed (message in qmm_last_error) */
 } qmm_status;
 
-typedef enum { QMM_Q4_0 = 2, QMM_Q8_0 = 8, QMM_Q4_K = 12, QMM_Q5_K = 13, QMM_Q6_K = 14 } qmm_type; /* GGUF type ids */
+typedef enum {
+    QMM_Q4_0 = 2, QMM_Q8_0 = 8, QMM_Q3_K = 11, QMM_Q4_K = 12, QMM_Q5_K = 13, QMM_Q6_K = 14, QMM_IQ4_XS = 23
+} qmm_type; /* GGUF type ids */
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char *qmm_last_error(void);
@@ -238,8 +245,10 @@ qmm_status qmm_matmul_id_glu(int type, const void *w_gate, const void *w_up, int
  * its fp32 result does it store that integer to d_out instead (y is not written).
  * d_out: int32 [n][rows][per] (device, 4-byte aligned) with
  *   per = k/32 for Q4_K, Q5_K, Q8_0, Q4_0 (D_b),
- *   Q6_K path 1: per = k/16 (D per 16-value sub-block),
- *   Q6_K path 2: per = k/32, the scale-folded integer sc_{2b}*D_{2b} + sc_{2b+1}*D_{2b+1}.
+ *   per = k/32 for IQ4_XS (D_b over the codebook values),
+ *   Q6_K and Q3_K path 1: per = k/16 (D per 16-value sub-block),
+ *   Q6_K and Q3_K path 2: per = k/32, the scale-folded integer sc_{2b}*D_{2b} + sc_{2b+1}*D_{2b+1}
+ *   (Q3_K: sc = 6-bit scale - 32).
  * xq: n * k/32 q8_1 blocks (4-byte aligned).  Path 1 requires n <= 8.
  * qmm_debug_subdots_workspace: bytes of device workspace (256-byte aligned) the call needs; 0
  *   means none (ws may be NULL), also for invalid arguments.

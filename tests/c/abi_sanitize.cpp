@@ -38,7 +38,7 @@ int main() {
     const int32_t *IDS = static_cast<const int32_t *>(fake(0x500000));
 
     // argument errors
-    EXPECT(qmm_matmul(11, W, 16, 256, (const float *)X, 1, (float *)Y, WS, 1 << 30, nullptr) == QMM_ERR_TYPE);
+    EXPECT(qmm_matmul(3, W, 16, 256, (const float *)X, 1, (float *)Y, WS, 1 << 30, nullptr) == QMM_ERR_TYPE);
     EXPECT(qmm_matmul(QMM_Q4_K, W, 16, 100, (const float *)X, 1, (float *)Y, WS, 1 << 30, nullptr) == QMM_ERR_SHAPE);
     EXPECT(qmm_matmul(QMM_Q4_K, W, 0, 256, (const float *)X, 1, (float *)Y, WS, 1 << 30, nullptr) == QMM_ERR_ARG);
     EXPECT(qmm_matmul(QMM_Q4_K, W, 16, 256, (const float *)X, -1, (float *)Y, WS, 1 << 30, nullptr) == QMM_ERR_ARG);
@@ -119,7 +119,7 @@ int main() {
     // call that fits -- its scratch lookup fails without a device
     EXPECT(qmm_matmul_noalloc(QMM_Q6_K, W, 4096, 14336, (const float *)X, 65536, (float *)Y, nullptr) ==
            QMM_ERR_WORKSPACE);
-    EXPECT(qmm_matmul_noalloc(11, W, 4096, 256, (const float *)X, 4, (float *)Y, nullptr) == QMM_ERR_TYPE);
+    EXPECT(qmm_matmul_noalloc(3, W, 4096, 256, (const float *)X, 4, (float *)Y, nullptr) == QMM_ERR_TYPE);
     EXPECT(qmm_matmul_noalloc(QMM_Q4_K, W, 4096, 4096, (const float *)X, 0, (float *)Y, nullptr) == QMM_OK);
     for (int64_t n : {3, 512})
         EXPECT(qmm_matmul_noalloc(QMM_Q4_K, W, 4096, 4096, (const float *)X, n, (float *)Y, nullptr) == QMM_ERR_HIP);

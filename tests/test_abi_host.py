@@ -136,7 +136,7 @@ def test_argument_validation_without_gpu():
     L = qmm.lib()
     null = ctypes.c_void_p(0)
     # unsupported type
-    assert L.qmm_matmul(11, null, 16, 256, null, 1, null, null, 0, null) == -2
+    assert L.qmm_matmul(3, null, 16, 256, null, 1, null, null, 0, null) == -2
     assert b"unsupported" in L.qmm_last_error()
     # k not a multiple of the block size
     assert L.qmm_matmul(qmm.Q4_K, null, 16, 100, null, 1, null, null, 0, null) == -3
@@ -164,7 +164,7 @@ def test_glu_argument_validation_without_gpu():
     L = qmm.lib()
     null = ctypes.c_void_p(0)
     one = ctypes.c_void_p(4096)   # a non-null address, never dereferenced: the calls fail first
-    assert L.qmm_matmul_glu(11, null, null, 16, 256, null, 1, null, null, 0, null) == -2
+    assert L.qmm_matmul_glu(3, null, null, 16, 256, null, 1, null, null, 0, null) == -2
     assert L.qmm_matmul_glu(qmm.Q4_K, null, null, 16, 100, null, 1, null, null, 0, null) == -3
     assert L.qmm_matmul_glu(qmm.Q4_K, null, null, 16, 256, null, 0, null, null, 0, null) == 0
     # null up matrix with columns to compute
@@ -191,7 +191,7 @@ def test_workspace_sizes_monotone():
     assert qmm.matmul_workspace(qmm.Q4_K, 4096, 4096, 1) >= 4096 // 32 * 36
     # the tiled path reserves stream-K partial slots
     assert qmm.matmul_q8_1_workspace(qmm.Q6_K, 4096, 14336, 512) >= 256 * 2 * 128 * 128 * 4
-    assert qmm.matmul_workspace(11, 16, 256, 1) == 0
+    assert qmm.matmul_workspace(3, 16, 256, 1) == 0
     assert qmm.matmul_id_workspace(qmm.Q4_K, 8, 14336, 4096, 512, 2, 1) > 512 * 128 * 36
     assert qmm.matmul_id_workspace(qmm.Q4_K, 8, 14336, 4096, 512, 2, 3) == 0
 
@@ -373,7 +373,7 @@ def test_noalloc_entry_refuses_calls_beyond_its_scratch_without_gpu():
     w, x, y = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000), ctypes.c_void_p(0x300000)
     assert L.qmm_matmul_noalloc(qmm.Q6_K, w, 4096, 14336, x, 65536, y, None) == -4
     assert b"allocation-free" in L.qmm_last_error()
-    assert L.qmm_matmul_noalloc(11, w, 4096, 256, x, 4, y, None) == -2
+    assert L.qmm_matmul_noalloc(3, w, 4096, 256, x, 4, y, None) == -2
     assert L.qmm_matmul_noalloc(qmm.Q4_K, w, 4096, 4096, ctypes.c_void_p(0x200004), 4, y, None) == -1
     assert L.qmm_matmul_noalloc(qmm.Q4_K, w, 4096, 4096, x, 0, y, None) == 0
 

@@ -123,11 +123,11 @@ def test_f16act_more_accurate_than_q8_1_on_device():
 
 
 @pytest.mark.parametrize("qtype,rows,k,n,off", [(qmm.Q4_K, 16, 256, 9, 0),      # more than 8 columns
-                                                (11, 16, 256, 1, 0),           # unsupported type
+                                                (3, 16, 256, 1, 0),            # unsupported type
                                                 (qmm.Q4_K, 16, 288, 1, 0),     # K not a multiple of 256
                                                 (qmm.Q4_K, 16, 256, 1, 2)])    # weights not 16-byte aligned
 def test_f16act_refusals(qtype, rows, k, n, off):
-    wt = qtype if qtype != 11 else qmm.Q4_K
+    wt = qtype if qtype != 3 else qmm.Q4_K
     kk = k if k % 256 == 0 else 512
     w = to_dev(np.zeros(off + oracle.row_bytes(wt, kk) * rows + 64, np.uint8))[off:]
     with pytest.raises(qmm.QmmError):
