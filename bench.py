@@ -18,7 +18,7 @@ Also in the same JSON line:
   cpu_baseline  the oracle (plain C, all host threads) on whole steps of the same workload; the
                 host CPU model; one-thread figures on the small dense workload and one step.
   f16act_matvec  per-call timing (encoder + kernel) of the fp16-activation mode on the step's shapes
-  extra_types_matvec  per-launch timing of the same matrix-vector shapes in Q5_K and Q4_0 (not
+  extra_types_matvec  per-launch timing of the same matrix-vector shapes in Q5_K, Q4_0, Q3_K and IQ4_XS (not
                 part of the step).
   panel_layout  the step's shapes read from the panel layout (qmm_repack / qmm_matmul_packed), and
                 the repack's first-call versus steady-state cost at 8192 x 4096 Q4_K, one column.

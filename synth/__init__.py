@@ -117,11 +117,12 @@ MOE_CASES = [
 ]
 
 
-# Q5_K and Q4_0 (beyond the headline types): the matrix-vector shapes and one prefill shape each.
+# Q5_K, Q4_0, Q3_K and IQ4_XS (beyond the headline types): the matrix-vector shapes and one prefill
+# shape each.
 EXTRA_MMVQ_CASES = [dict(name=f"{TYPE_NAMES[t]} 4096x4096 N={n}", qtype=t, rows=4096, k=4096, n=n)
-                    for t in (Q5_K, Q4_0) for n in (1, 2, 5, 8)]
-EXTRA_PREFILL_CASES = [dict(name="ffn up q5_K 14336x4096 T=512", qtype=Q5_K, rows=14336, k=4096, n=512),
-                       dict(name="ffn up q4_0 14336x4096 T=512", qtype=Q4_0, rows=14336, k=4096, n=512)]
+                    for t in (Q5_K, Q4_0, Q3_K, IQ4_XS) for n in (1, 2, 5, 8)]
+EXTRA_PREFILL_CASES = [dict(name=f"ffn up {TYPE_NAMES[t]} 14336x4096 T=512", qtype=t, rows=14336, k=4096, n=512)
+                       for t in (Q5_K, Q4_0, Q3_K, IQ4_XS)]
 
 # Gate/up products fused with SwiGLU: two matrices of `rows` rows each.
 GLU_CASES = [
