@@ -2,7 +2,10 @@
 // of the expert-sorted column list, built on the GPU so that nothing is read back; "MoE skew":
 // sorting by expert makes each expert's columns contiguous).
 //
-// One workgroup runs a stable counting sort of the (token, slot) pairs by expert id:
+// One workgroup runs a counting sort of the (token, slot) pairs by expert id.  Up to 2304 experts
+// the slots come from per-wave LDS atomics (moe_group_wave_kernel, below: each expert's segment
+// holds exactly its pairs, in an order not fixed within a wave's share); for more experts, a
+// stable sort from per-thread counts:
 //   1. thread t counts its contiguous chunk of pairs per expert into an LDS table cnt[e][t]
 //      (ids read in batches of independent loads, counted with LDS atomics on its own column);
 //   2. thread t owns the experts [t*ce, t*ce + ce): it sums their rows, a block scan over the
@@ -224,9 +227,163 @@ __global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(const int32_t 
     }
 }
 
+// ---------------------------------------------------------------------------------------------
+// The grouping for up to kWaveMaxExperts experts, with LDS atomics instead of per-thread rows.
+// 16 waves; wave w owns the contiguous pairs [w*chunk, (w+1)*chunk) and counts them per expert
+// into its own row hist[w][e] (LDS atomics: lanes of a wave with the same expert serialise on one
+// address).  The rows are scanned expert-major -- expert e's segment start plus the counts of
+// waves w' < w -- and each wave walks its pairs again, taking each pair's slot with an atomic
+// increment of hist[w][e].  Each expert's segment then holds exactly its pairs, the pairs of
+// wave w before those of wave w + 1 (ascending blocks of pair indices), but the order among one
+// wave's pairs of an expert is the order the atomics were served in, which need not be the same
+// from run to run.  Any order is correct: every column of an expert is computed on its own, with
+// the same arithmetic whatever its place in the segment, so the products are bitwise the same.
+// Per pair this is one load and one LDS atomic per pass (the earlier per-thread form spent most
+// of its time in serial row scans of an n_exp x 256 table on one compute unit).
+// ---------------------------------------------------------------------------------------------
+constexpr int kWaveGroupWaves = 16;
+constexpr int kWaveMaxExperts = kGroupTableInts / kWaveGroupWaves;   // 2304
+constexpr int kWaveGroupBatches = 16;                                // 64-id batches loaded together
+
+// Exclusive scan of one value per thread over the 1024-thread workgroup: lane prefix by shuffles,
+// then the 16 wave totals (wsum, 16 ints of LDS).
+__device__ __forceinline__ int32_t wave_block_excl_scan(int32_t v, int32_t *wsum, int32_t *total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int32_t x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int32_t y = __shfl_up(x, d);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    int32_t pre = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < kWaveGroupWaves; ++i) {
+        const int32_t sv = wsum[i];
+        pre += i < wave ? sv : 0;
+        tot += sv;
+    }
+    __syncthreads();   // wsum is reused by the next scan
+    *total = tot;
+    return pre + x - v;
+}
+
+__global__ __launch_bounds__(64 * kWaveGroupWaves) void moe_group_wave_kernel(
+    const int32_t *__restrict__ ids, int64_t pairs, int32_t n_exp, int32_t tile_j, int32_t small_max,
+    int32_t *__restrict__ sorted, int32_t *__restrict__ bounds, int32_t *__restrict__ tile_start,
+    int32_t *__restrict__ small, int32_t *__restrict__ invalid) {
+    __shared__ __align__(16) int32_t hist[kGroupTableInts];   // [wave][expert]
+    __shared__ int32_t wsum[kWaveGroupWaves];
+    __shared__ int32_t bad_sh;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    constexpr int NT = 64 * kWaveGroupWaves;
+    const int64_t chunk = ((pairs + kWaveGroupWaves - 1) / kWaveGroupWaves + 63) & ~(int64_t)63;
+    const int64_t lo = (int64_t)wave * chunk < pairs ? (int64_t)wave * chunk : pairs;
+    const int64_t hi = lo + chunk < pairs ? lo + chunk : pairs;
+    int32_t *my = hist + wave * n_exp;
+
+    if (t == 0) bad_sh = 0;
+    for (int i = t; i < kWaveGroupWaves * n_exp; i += NT) hist[i] = 0;
+    __syncthreads();
+
+    // The wave's ids, kWaveGroupBatches batches of 64 at a time, every load issued before the
+    // first is used (one memory latency per group, not per batch).
+    auto load_group = [&](int64_t g0, int32_t (&ev)[kWaveGroupBatches]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int b = 0; b < kWaveGroupBatches; ++b) {
+            const int64_t p = g0 + 64 * b + lane;
+            ev[b] = p < hi ? ids[p] : -1;
+        }
+    };
+
+    // pass 1: per-wave counts
+    int bad = 0;
+    for (int64_t g0 = lo; g0 < hi; g0 += 64 * kWaveGroupBatches) {
+        int32_t ev[kWaveGroupBatches];
+        load_group(g0, ev);
+#pragma unroll
+        for (int b = 0; b < kWaveGroupBatches; ++b) {
+            const int32_t e = ev[b];
+            if ((uint32_t)e < (uint32_t)n_exp) atomicAdd(&my[e], 1);
+            else bad += g0 + 64 * b + lane < hi ? 1 : 0;
+        }
+    }
+    if (bad) atomicAdd(&bad_sh, bad);
+    __syncthreads();
+
+    // scan: thread t owns the experts [t*ce, t*ce + ce) (contiguous, so the workgroup scan of the
+    // per-thread totals orders them); hist[w][e] becomes the first position of wave w's pairs of e
+    const int ce = (n_exp + NT - 1) / NT;
+    const int e0 = t * ce < n_exp ? t * ce : n_exp, e1 = e0 + ce < n_exp ? e0 + ce : n_exp;
+    int32_t mine = 0;
+    for (int e = e0; e < e1; ++e) {
+        int32_t c = 0;
+#pragma unroll
+        for (int w = 0; w < kWaveGroupWaves; ++w) c += hist[w * n_exp + e];
+        mine += c;
+    }
+    int32_t total = 0;
+    int32_t run = wave_block_excl_scan(mine, wsum, &total);
+    int32_t my_tiles = 0, my_small = 0;
+    for (int e = e0; e < e1; ++e) {
+        bounds[e] = run;
+        int32_t r = run;
+#pragma unroll
+        for (int w = 0; w < kWaveGroupWaves; ++w) {
+            const int32_t v = hist[w * n_exp + e];
+            hist[w * n_exp + e] = r;
+            r += v;
+        }
+        const int32_t c = r - run;
+        run = r;
+        // count of tiles, or -1 for an expert the matrix-vector kernel takes (prefixes below)
+        const int32_t nt = c > small_max ? (c + tile_j - 1) / tile_j : (c > 0 ? -1 : 0);
+        tile_start[e] = nt;
+        my_tiles += nt > 0 ? nt : 0;
+        my_small += nt < 0 ? 1 : 0;
+    }
+    int32_t tiles_total = 0, small_total = 0;
+    int32_t trun = wave_block_excl_scan(my_tiles, wsum, &tiles_total);
+    int32_t srun = wave_block_excl_scan(my_small, wsum, &small_total);
+    for (int e = e0; e < e1; ++e) {
+        const int32_t nt = tile_start[e];
+        if (nt < 0) small[srun++] = e;
+        tile_start[e] = trun;
+        trun += nt > 0 ? nt : 0;
+    }
+    for (int i = small_total + t; i < n_exp; i += NT) small[i] = -1;
+    if (t == 0) {
+        bounds[n_exp] = total;
+        tile_start[n_exp] = tiles_total;
+        invalid[0] = bad_sh;
+    }
+    __syncthreads();
+
+    // pass 2: each pair takes the next slot of its wave's range for its expert
+    for (int64_t g0 = lo; g0 < hi; g0 += 64 * kWaveGroupBatches) {
+        int32_t ev[kWaveGroupBatches];
+        load_group(g0, ev);
+        int32_t pos[kWaveGroupBatches];
+#pragma unroll
+        for (int b = 0; b < kWaveGroupBatches; ++b) {
+            const int32_t e = ev[b];
+            pos[b] = (uint32_t)e < (uint32_t)n_exp ? atomicAdd(&my[e], 1) : -1;
+        }
+#pragma unroll
+        for (int b = 0; b < kWaveGroupBatches; ++b)
+            if (pos[b] >= 0) sorted[pos[b]] = (int32_t)(g0 + 64 * b + lane);
+    }
+}
+
 hipError_t launch_moe_group(const int32_t *ids, int64_t pairs, int32_t n_exp, int32_t tile_j, int32_t small_max,
                             int32_t *sorted, int32_t *bounds, int32_t *tile_start, int32_t *small, int32_t *invalid,
                             hipStream_t s) {
+    if (n_exp >= 1 && n_exp <= kWaveMaxExperts) {
+        hipLaunchKernelGGL(moe_group_wave_kernel, dim3(1), dim3(64 * kWaveGroupWaves), 0, s, ids, pairs, n_exp,
+                           tile_j, small_max, sorted, bounds, tile_start, small, invalid);
+        return hipGetLastError();
+    }
     int32_t nthr = kGroupThreads;
     while (nthr > 1 && (int64_t)group_row_stride(nthr) * n_exp > kGroupTableInts) nthr >>= 1;
     if ((int64_t)group_row_stride(nthr) * n_exp > kGroupTableInts) return hipErrorInvalidValue;
