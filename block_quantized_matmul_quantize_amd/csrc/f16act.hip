@@ -7,7 +7,7 @@
 // subnormals too); y = fp16(x * 2^e) with one round to nearest even; the block sum of the y in
 // fp32.
 //
-// Product: one wave per weight row, lane l takes the row's 32-value blocks l, l+64, ...  Each
+// Product (below): lane l of a row's wave takes the row's 32-value blocks l, l+64, ...  Each
 // block's weights are an affine map of small unsigned integer codes u: value = A*u + B (Q4_K /
 // Q5_K: A = d*sc, B = -dmin*m; Q8_0: u = q + 128, B = -128 d; Q4_0: B = -8 d; Q6_K per 16 values:
 // u = 6-bit code, B = -32 A).  The codes become exact fp16 integers (bit pattern 0x6400 | u is
@@ -154,50 +154,96 @@ __device__ __forceinline__ void decode(const uint8_t *row, int jg, Blk &o) {
     for (int i = 0; i < 8; ++i) bytes_to_h2(c[i], o.u[2 * i], o.u[2 * i + 1]);
 }
 
+// Product: a workgroup of 16 waves (Q6_K: 8, whose two scales per block need more registers than
+// 16 waves per compute unit leave) owns one weight row per wave and walks K in chunks of 64
+// blocks (2048 values).  Each chunk's fp16 activations of all columns, with their exponents and
+// block sums, are parked in LDS once per workgroup (64 + 16 bytes per block and column, so the 16
+// lanes of a row read group hit distinct banks) and serve the workgroup's 16 rows: the columns are
+// read from L2 once per 16 rows instead of once per row.  Within a chunk lane l takes block l of
+// every row of its wave, so a lane still accumulates its blocks l, l + 64, ... in order and the
+// 64 lanes of a row are summed with the same lane exchanges.
+template <int T> constexpr int kF16Rows = T == kQ6_K ? 8 : 16;   // rows (= waves) per workgroup
+constexpr int kF16RowsPerWave = 1;
+constexpr int kF16Chunk = 64;          // 32-value blocks per K chunk
+constexpr int kF16YStride = 80;        // LDS bytes per (column, block): 32 fp16 + 16 pad
+
 template <int T>
-__global__ __launch_bounds__(256) void mmvq_f16act_kernel(const uint8_t *__restrict__ w, int64_t rows,
-                                                          int64_t row_bytes, int64_t k,
-                                                          const uint16_t *__restrict__ y16,
-                                                          const int32_t *__restrict__ e,
-                                                          const float *__restrict__ bsum, int n,
-                                                          float *__restrict__ out) {
-    const int lane = threadIdx.x & 63;
-    const int64_t r = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    if (r >= rows) return;   // whole wave; no barrier below
-    const uint8_t *row = w + r * row_bytes;
+__global__ __launch_bounds__(64 * kF16Rows<T>) void mmvq_f16act_kernel(const uint8_t *__restrict__ w, int64_t rows,
+                                                                  int64_t row_bytes, int64_t k,
+                                                                  const uint16_t *__restrict__ y16,
+                                                                  const int32_t *__restrict__ e,
+                                                                  const float *__restrict__ bsum, int n,
+                                                                  float *__restrict__ out) {
+    __shared__ __align__(16) uint8_t ys[8 * kF16Chunk * kF16YStride];
+    __shared__ int32_t es[8 * kF16Chunk];
+    __shared__ float bs[8 * kF16Chunk];
+    constexpr int kF16Threads = 64 * kF16Rows<T>;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t rbase = (int64_t)blockIdx.x * kF16Rows<T> + wave * kF16RowsPerWave;
     const int nb = (int)(k >> 5);
-    float acc[8];
+    float acc[kF16RowsPerWave][8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) acc[c] = 0.f;
-    for (int jg = lane; jg < nb; jg += 64) {
-        Blk b;
-        decode<T>(row, jg, b);
+    for (int rr = 0; rr < kF16RowsPerWave; ++rr)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-            if (c >= n) break;
-            const u32x4 *yv = (const u32x4 *)(y16 + (int64_t)c * k + 32 * jg);
-            const u32x4 yy[4] = {yv[0], yv[1], yv[2], yv[3]};
-            const int eb = e[(int64_t)c * nb + jg];
-            float t;
-            if constexpr (T == kQ6_K) {
-                const h2v one = {(_Float16)1.0f, (_Float16)1.0f};
-                const h2v ones[16] = {one, one, one, one, one, one, one, one, one, one, one, one, one, one, one, one};
-                const float s0 = dot16(ones, yy, 0), s1 = dot16(ones, yy, 8);
-                t = b.A0 * dot16(b.u, yy, 0) + b.B0 * s0 + (b.A1 * dot16(b.u, yy, 8) + b.B1 * s1);
-            } else {
-                const float p = dot16(b.u, yy, 0) + dot16(b.u, yy, 8);
-                t = b.A0 * p + b.B0 * bsum[(int64_t)c * nb + jg];
+        for (int c = 0; c < 8; ++c) acc[rr][c] = 0.f;
+
+    for (int jb0 = 0; jb0 < nb; jb0 += kF16Chunk) {
+        const int cnt = nb - jb0 < kF16Chunk ? nb - jb0 : kF16Chunk;
+        __syncthreads();   // the previous chunk's LDS reads are done
+        // 16-byte pieces (column c, block b, quarter q) of the chunk
+        for (int p = tid; p < n * cnt * 4; p += kF16Threads) {
+            const int c = p / (cnt * 4), rem = p - c * cnt * 4, b = rem >> 2, q = rem & 3;
+            *(u32x4 *)(ys + (c * kF16Chunk + b) * kF16YStride + 16 * q) =
+                *(const u32x4 *)(y16 + (int64_t)c * k + (int64_t)(jb0 + b) * 32 + 8 * q);
+        }
+        for (int p = tid; p < n * cnt; p += kF16Threads) {
+            const int c = p / cnt, b = p - c * cnt;
+            es[c * kF16Chunk + b] = e[(int64_t)c * nb + jb0 + b];
+            bs[c * kF16Chunk + b] = bsum[(int64_t)c * nb + jb0 + b];
+        }
+        __syncthreads();
+        if (lane >= cnt) continue;   // the last chunk may be partial (no barrier until the next chunk)
+        const int jg = jb0 + lane;
+#pragma unroll
+        for (int rr = 0; rr < kF16RowsPerWave; ++rr) {
+            const int64_t r = rbase + rr;
+            if (r >= rows) break;   // wave-uniform
+            Blk b;
+            decode<T>(w + r * row_bytes, jg, b);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                if (c >= n) break;
+                const uint8_t *yp = ys + (c * kF16Chunk + lane) * kF16YStride;
+                const u32x4 yy[4] = {*(const u32x4 *)yp, *(const u32x4 *)(yp + 16), *(const u32x4 *)(yp + 32),
+                                     *(const u32x4 *)(yp + 48)};
+                const int eb = es[c * kF16Chunk + lane];
+                float t;
+                if constexpr (T == kQ6_K) {
+                    // the two 16-value halves' sums of y (the offset term of each half's scale)
+                    const h2v one = {(_Float16)1.0f, (_Float16)1.0f};
+                    const h2v ones[16] = {one, one, one, one, one, one, one, one, one, one, one, one, one, one, one, one};
+                    const float s0 = dot16(ones, yy, 0), s1 = dot16(ones, yy, 8);
+                    t = b.A0 * dot16(b.u, yy, 0) + b.B0 * s0 + (b.A1 * dot16(b.u, yy, 8) + b.B1 * s1);
+                } else {
+                    const float pp = dot16(b.u, yy, 0) + dot16(b.u, yy, 8);
+                    t = b.A0 * pp + b.B0 * bs[c * kF16Chunk + lane];
+                }
+                acc[rr][c] += ldexpf(t, -eb);
             }
-            acc[c] += ldexpf(t, -eb);
         }
     }
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        if (c >= n) break;
-        float v = acc[c];
+    for (int rr = 0; rr < kF16RowsPerWave; ++rr) {
+        const int64_t r = rbase + rr;
+        if (r >= rows) break;
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
-        if (lane == 0) out[(int64_t)c * rows + r] = v;
+        for (int c = 0; c < 8; ++c) {
+            if (c >= n) break;
+            float v = acc[rr][c];
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
+            if (lane == 0) out[(int64_t)c * rows + r] = v;
+        }
     }
 }
 
@@ -205,8 +251,9 @@ template <int T>
 hipError_t launch_t(const uint8_t *w, int64_t rows, int64_t k, const uint16_t *y16, const int32_t *e,
                     const float *bsum, int64_t n, float *out, hipStream_t s) {
     const int64_t row_bytes = k / Fmt<T>::QK * Fmt<T>::BYTES;
-    hipLaunchKernelGGL(mmvq_f16act_kernel<T>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, w, rows, row_bytes,
-                       k, y16, e, bsum, (int)n, out);
+    hipLaunchKernelGGL(mmvq_f16act_kernel<T>, dim3((unsigned)((rows + kF16Rows<T> - 1) / kF16Rows<T>)),
+                       dim3(64 * kF16Rows<T>), 0, s, w,
+                       rows, row_bytes, k, y16, e, bsum, (int)n, out);
     return hipGetLastError();
 }
 

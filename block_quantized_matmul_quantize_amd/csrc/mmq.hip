@@ -666,7 +666,7 @@ __device__ __forceinline__ void tile_step(const uint8_t *sm, f32x16 (&acc)[Cfg<J
         // l of sub-block sb
         u32x4 qh = {0u, 0u, 0u, 0u};
         if constexpr (T == kQ5_K) qh = *(const u32x4 *)(sm + L::QH_OFF + arow * 32 + koff);
-#pragma unroll 1
+#pragma unroll 2
         for (int sb = 0; sb < 8; ++sb) {
             // qs bytes 32*(sb/2)+16h .. +15: low nibbles = values 16h.. of the even sub-block of
             // the pair, high nibbles = of the odd one
@@ -690,7 +690,7 @@ __device__ __forceinline__ void tile_step(const uint8_t *sm, f32x16 (&acc)[Cfg<J
         }
     } else if constexpr (kB32<T>) {
         const int8_t *sW = (const int8_t *)(sm + L::W_OFF);
-#pragma unroll 1
+#pragma unroll 2
         for (int j = 0; j < 8; ++j) {
             if (kb * 8 + j >= nb32) break;   // ragged last step (workgroup-uniform)
             const u32x4 a = *(const u32x4 *)(sW + arow * kLd + 32 * j + koff);
@@ -711,7 +711,7 @@ __device__ __forceinline__ void tile_step(const uint8_t *sm, f32x16 (&acc)[Cfg<J
         f32x16 Tc[NCB];
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) Tc[cb] = fzero;
-#pragma unroll 1
+#pragma unroll 2
         for (int j = 0; j < 8; ++j) {
             const u32x4 a = *(const u32x4 *)(sW + arow * kLd + 32 * j + koff);
             const u32x4 a_hi = *(const u32x4 *)(sW + kTI * kLd + arow * kLd + 32 * j + koff);
