@@ -56,6 +56,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0
 INT8_PEAK_TOPS = 5000.0
+STEP_ROWS = 4096   # weight rows of every matrix-vector call of the step (synth.MMVQ_CASES)
 
 
 # Sources of the matrix-vector kernels themselves: a change to any of them drops the stored counter
@@ -514,18 +515,37 @@ def summarize_pmc(fdir, wdir, write=False):
     print(f"calibration: {COPY_BYTES >> 20} MiB device copy -> FETCH_SIZE x{fs:.3f}, WRITE_SIZE x{ws:.3f}")
     print("| kernel | dispatches | FETCH_SIZE KiB/dispatch (raw) | WRITE_SIZE KiB/dispatch (raw) | HBM bytes/dispatch (scaled) |")
     print("|---|---|---|---|---|")
-    mv_tot = mv_cnt = 0
     for k in sorted(F, key=lambda k: -statistics.mean(F[k])):
         f = statistics.mean(F[k])
         w = statistics.mean(Wr.get(k, [0.0]))
         b = f * 1024 * fs + w * 1024 * ws
         print(f"| `{k}` | {len(F[k])} | {f:.1f} | {w:.1f} | {b / 1e6:.3f} MB |")
-        # the step's launches: the headline types (8, 12, 14), not the extra types' timing
-        if "mmvq" in k and re.search(r"<(8|12|14),", k):
-            mv_tot += b * len(F[k])
-            mv_cnt += len(F[k])
-    # tiled and grouping kernels: one line per launch shape (grid size), as the shapes differ
     FG, WG = by_grid(fdir), by_grid(wdir)
+    # The step's launches: the headline types (8, 12, 14) in the forms the step takes (fp32 input,
+    # no fusion, original layout) at its 4096 rows (16 rows per 1024-thread workgroup); not the
+    # extra types, the fp16-activation mode, the panel layout or the 8192-row comparison.
+    step_kernel = re.compile(r"^qmm::mmvq_(stream_kernel<(8|12|14), false, false, true, false, false>"
+                             r"|dot4_kernel<(8|12|14), \d, false, false, true, false>)$")
+    # Each case of a type runs the same number of launches, so a kernel's share of its type's
+    # dispatches counts the cases it served; the figure is the mean over the step's cases, as the
+    # algorithmic bytes per launch are.
+    groups = {}
+    for (k, grid), fv in FG.items():
+        m = step_kernel.match(k)
+        if m and grid == (STEP_ROWS // 16) * 1024:
+            b = statistics.mean(fv) * 1024 * fs + statistics.mean(WG.get((k, grid), [0.0])) * 1024 * ws
+            groups[k] = (int(m.group(2) or m.group(3)), len(fv), b)
+    import synth
+    ncases = {t: sum(c["qtype"] == t for c in synth.MMVQ_CASES) for t in {c["qtype"] for c in synth.MMVQ_CASES}}
+    per_type = {}
+    for t, cnt, _ in groups.values():
+        per_type[t] = per_type.get(t, 0) + cnt
+    mv_tot = mv_cnt = 0.0
+    for t, cnt, b in groups.values():
+        cases = ncases[t] * cnt / per_type[t]
+        mv_tot += b * cases
+        mv_cnt += cases
+    # tiled and grouping kernels: one line per launch shape (grid size), as the shapes differ
     tiled = sorted(k for k in FG if "mmq" in k[0] or "moe_group" in k[0] or "fixup" in k[0])
     if tiled:
         print()
@@ -540,7 +560,8 @@ def summarize_pmc(fdir, wdir, write=False):
             raise SystemExit("no matrix-vector kernel dispatches in the counter runs")
         return
     avg = mv_tot / mv_cnt
-    print(f"matrix-vector kernels: {mv_cnt} dispatches, average HBM bytes per dispatch {avg / 1e6:.3f} MB")
+    print(f"matrix-vector kernels of the step: {sum(g[1] for g in groups.values())} dispatches, "
+          f"{mv_cnt:.0f} cases, mean over the cases of HBM bytes per launch {avg / 1e6:.3f} MB")
     if write:
         with open(os.path.join(ROOT, "profiles", "mmvq_traffic.json"), "w") as f:
             json.dump({"kernel": "matrix-vector kernels as the step launches them (12 cases)",

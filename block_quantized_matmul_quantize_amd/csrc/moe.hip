@@ -230,43 +230,54 @@ __global__ __launch_bounds__(kGroupThreads) void moe_group_kernel(const int32_t 
 // ---------------------------------------------------------------------------------------------
 // The grouping for up to kWaveMaxExperts experts, with LDS atomics instead of per-thread rows.
 // 16 waves; wave w owns the contiguous pairs [w*chunk, (w+1)*chunk) and counts them per expert
-// into its own row hist[w][e] (LDS atomics: lanes of a wave with the same expert serialise on one
-// address).  The rows are scanned expert-major -- expert e's segment start plus the counts of
-// waves w' < w -- and each wave walks its pairs again, taking each pair's slot with an atomic
-// increment of hist[w][e].  Each expert's segment then holds exactly its pairs, the pairs of
-// wave w before those of wave w + 1 (ascending blocks of pair indices), but the order among one
-// wave's pairs of an expert is the order the atomics were served in, which need not be the same
-// from run to run.  Any order is correct: every column of an expert is computed on its own, with
-// the same arithmetic whatever its place in the segment, so the products are bitwise the same.
-// Per pair this is one load and one LDS atomic per pass (the earlier per-thread form spent most
-// of its time in serial row scans of an n_exp x 256 table on one compute unit).
+// into its own row hist[w][e] with LDS atomics (lanes of a wave with the same expert serialise on
+// one address); the value an atomic returns is the pair's rank among wave w's pairs of expert e.
+// The rows are scanned expert-major -- expert e's segment start plus the counts of waves w' < w --
+// so a pair's slot is hist[w][e] + its rank.  Chunks of up to 1024 pairs (every call up to 16384
+// pairs) keep their ids and ranks in registers, so the ids are read once and each pair costs one
+// atomic; longer chunks read their ids again and take slots with a second atomic per pair.  Each
+// expert's segment holds exactly its pairs, the pairs of wave w before those of wave w + 1
+// (ascending blocks of pair indices), but the order among one wave's pairs of an expert is the
+// order the atomics were served in, which need not be the same from run to run.  Any order is
+// correct: every column of an expert is computed on its own, with the same arithmetic whatever
+// its place in the segment, so the products are bitwise the same.  (The earlier per-thread form
+// spent most of its time in serial row scans of an n_exp x 256 table on one compute unit.)
 // ---------------------------------------------------------------------------------------------
 constexpr int kWaveGroupWaves = 16;
 constexpr int kWaveMaxExperts = kGroupTableInts / kWaveGroupWaves;   // 2304
 constexpr int kWaveGroupBatches = 16;                                // 64-id batches loaded together
 
-// Exclusive scan of one value per thread over the 1024-thread workgroup: lane prefix by shuffles,
-// then the 16 wave totals (wsum, 16 ints of LDS).
-__device__ __forceinline__ int32_t wave_block_excl_scan(int32_t v, int32_t *wsum, int32_t *total) {
+// Exclusive scans of three values per thread over the 1024-thread workgroup in one pass: lane
+// prefixes by shuffles, then the 16 wave totals of each (wsum, 3 x 16 ints of LDS).  v[i] becomes
+// the thread's exclusive prefix, tot[i] the workgroup total.
+__device__ __forceinline__ void wave_block_excl_scan3(int32_t (&v)[3], int32_t *wsum, int32_t (&tot)[3]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int32_t x = v;
+    int32_t x[3] = {v[0], v[1], v[2]};
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
-        const int32_t y = __shfl_up(x, d);
-        if (lane >= d) x += y;
-    }
-    if (lane == 63) wsum[wave] = x;
-    __syncthreads();
-    int32_t pre = 0, tot = 0;
 #pragma unroll
-    for (int i = 0; i < kWaveGroupWaves; ++i) {
-        const int32_t sv = wsum[i];
-        pre += i < wave ? sv : 0;
-        tot += sv;
+        for (int i = 0; i < 3; ++i) {
+            const int32_t y = __shfl_up(x[i], d);
+            if (lane >= d) x[i] += y;
+        }
     }
-    __syncthreads();   // wsum is reused by the next scan
-    *total = tot;
-    return pre + x - v;
+    if (lane == 63) {
+#pragma unroll
+        for (int i = 0; i < 3; ++i) wsum[i * kWaveGroupWaves + wave] = x[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        int32_t pre = 0, t = 0;
+#pragma unroll
+        for (int w = 0; w < kWaveGroupWaves; ++w) {
+            const int32_t sv = wsum[i * kWaveGroupWaves + w];
+            pre += w < wave ? sv : 0;
+            t += sv;
+        }
+        tot[i] = t;
+        v[i] = pre + x[i] - v[i];
+    }
 }
 
 __global__ __launch_bounds__(64 * kWaveGroupWaves) void moe_group_wave_kernel(
@@ -274,7 +285,7 @@ __global__ __launch_bounds__(64 * kWaveGroupWaves) void moe_group_wave_kernel(
     int32_t *__restrict__ sorted, int32_t *__restrict__ bounds, int32_t *__restrict__ tile_start,
     int32_t *__restrict__ small, int32_t *__restrict__ invalid) {
     __shared__ __align__(16) int32_t hist[kGroupTableInts];   // [wave][expert]
-    __shared__ int32_t wsum[kWaveGroupWaves];
+    __shared__ int32_t wsum[3 * kWaveGroupWaves];
     __shared__ int32_t bad_sh;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     constexpr int NT = 64 * kWaveGroupWaves;
@@ -282,10 +293,8 @@ __global__ __launch_bounds__(64 * kWaveGroupWaves) void moe_group_wave_kernel(
     const int64_t lo = (int64_t)wave * chunk < pairs ? (int64_t)wave * chunk : pairs;
     const int64_t hi = lo + chunk < pairs ? lo + chunk : pairs;
     int32_t *my = hist + wave * n_exp;
-
-    if (t == 0) bad_sh = 0;
-    for (int i = t; i < kWaveGroupWaves * n_exp; i += NT) hist[i] = 0;
-    __syncthreads();
+    // chunk is uniform over the waves, so every wave takes the same branch below
+    const bool keep = chunk <= 64 * kWaveGroupBatches;
 
     // The wave's ids, kWaveGroupBatches batches of 64 at a time, every load issued before the
     // first is used (one memory latency per group, not per batch).
@@ -297,15 +306,21 @@ __global__ __launch_bounds__(64 * kWaveGroupWaves) void moe_group_wave_kernel(
         }
     };
 
-    // pass 1: per-wave counts
+    // The first group's loads go out before the table is cleared.
+    int32_t ev[kWaveGroupBatches], rank[kWaveGroupBatches];
+    load_group(lo, ev);
+    if (t == 0) bad_sh = 0;
+    for (int i = t; i < kWaveGroupWaves * n_exp; i += NT) hist[i] = 0;
+    __syncthreads();
+
+    // pass 1: per-wave counts (and, for a kept chunk, each pair's rank)
     int bad = 0;
     for (int64_t g0 = lo; g0 < hi; g0 += 64 * kWaveGroupBatches) {
-        int32_t ev[kWaveGroupBatches];
-        load_group(g0, ev);
+        if (g0 != lo) load_group(g0, ev);
 #pragma unroll
         for (int b = 0; b < kWaveGroupBatches; ++b) {
             const int32_t e = ev[b];
-            if ((uint32_t)e < (uint32_t)n_exp) atomicAdd(&my[e], 1);
+            if ((uint32_t)e < (uint32_t)n_exp) rank[b] = atomicAdd(&my[e], 1);
             else bad += g0 + 64 * b + lane < hi ? 1 : 0;
         }
     }
@@ -316,18 +331,22 @@ __global__ __launch_bounds__(64 * kWaveGroupWaves) void moe_group_wave_kernel(
     // per-thread totals orders them); hist[w][e] becomes the first position of wave w's pairs of e
     const int ce = (n_exp + NT - 1) / NT;
     const int e0 = t * ce < n_exp ? t * ce : n_exp, e1 = e0 + ce < n_exp ? e0 + ce : n_exp;
-    int32_t mine = 0;
+    // per thread: pairs, column tiles, and matrix-vector (small) experts of its experts
+    int32_t acc[3] = {0, 0, 0};
     for (int e = e0; e < e1; ++e) {
         int32_t c = 0;
 #pragma unroll
         for (int w = 0; w < kWaveGroupWaves; ++w) c += hist[w * n_exp + e];
-        mine += c;
+        acc[0] += c;
+        acc[1] += c > small_max ? (c + tile_j - 1) / tile_j : 0;
+        acc[2] += c > 0 && c <= small_max ? 1 : 0;
     }
-    int32_t total = 0;
-    int32_t run = wave_block_excl_scan(mine, wsum, &total);
-    int32_t my_tiles = 0, my_small = 0;
+    int32_t tot[3];
+    wave_block_excl_scan3(acc, wsum, tot);
+    int32_t run = acc[0], trun = acc[1], srun = acc[2];
     for (int e = e0; e < e1; ++e) {
         bounds[e] = run;
+        tile_start[e] = trun;
         int32_t r = run;
 #pragma unroll
         for (int w = 0; w < kWaveGroupWaves; ++w) {
@@ -337,32 +356,45 @@ __global__ __launch_bounds__(64 * kWaveGroupWaves) void moe_group_wave_kernel(
         }
         const int32_t c = r - run;
         run = r;
-        // count of tiles, or -1 for an expert the matrix-vector kernel takes (prefixes below)
-        const int32_t nt = c > small_max ? (c + tile_j - 1) / tile_j : (c > 0 ? -1 : 0);
-        tile_start[e] = nt;
-        my_tiles += nt > 0 ? nt : 0;
-        my_small += nt < 0 ? 1 : 0;
+        if (c > small_max) trun += (c + tile_j - 1) / tile_j;
+        else if (c > 0) small[srun++] = e;
     }
-    int32_t tiles_total = 0, small_total = 0;
-    int32_t trun = wave_block_excl_scan(my_tiles, wsum, &tiles_total);
-    int32_t srun = wave_block_excl_scan(my_small, wsum, &small_total);
-    for (int e = e0; e < e1; ++e) {
-        const int32_t nt = tile_start[e];
-        if (nt < 0) small[srun++] = e;
-        tile_start[e] = trun;
-        trun += nt > 0 ? nt : 0;
-    }
-    for (int i = small_total + t; i < n_exp; i += NT) small[i] = -1;
+    for (int i = tot[2] + t; i < n_exp; i += NT) small[i] = -1;
     if (t == 0) {
-        bounds[n_exp] = total;
-        tile_start[n_exp] = tiles_total;
+        bounds[n_exp] = tot[0];
+        tile_start[n_exp] = tot[1];
         invalid[0] = bad_sh;
     }
     __syncthreads();
 
-    // pass 2: each pair takes the next slot of its wave's range for its expert
+    // pass 2: each pair's slot.  A kept chunk whose whole sorted list fits in LDS beside the table
+    // is placed there first and then written out with contiguous 16-byte stores: scattered 4-byte
+    // stores from the one compute unit cost more than all the rest of the kernel.
+    if (keep) {
+        const int soff = (kWaveGroupWaves * n_exp + 3) & ~3;   // 16-byte aligned staging area
+        if (soff + pairs <= kGroupTableInts) {
+            int32_t *stage = hist + soff;
+#pragma unroll
+            for (int b = 0; b < kWaveGroupBatches; ++b) {
+                const int32_t e = ev[b];
+                if ((uint32_t)e < (uint32_t)n_exp) stage[my[e] + rank[b]] = (int32_t)(lo + 64 * b + lane);
+            }
+            __syncthreads();
+            const int32_t n = tot[0], n4 = n >> 2;
+            const u32x4 *s4 = (const u32x4 *)stage;
+            u32x4 *d4 = (u32x4 *)sorted;   // sorted is 256-byte aligned (workspace layout)
+            for (int i = t; i < n4; i += NT) d4[i] = s4[i];
+            for (int i = 4 * n4 + t; i < n; i += NT) sorted[i] = stage[i];
+        } else {
+#pragma unroll
+            for (int b = 0; b < kWaveGroupBatches; ++b) {
+                const int32_t e = ev[b];
+                if ((uint32_t)e < (uint32_t)n_exp) sorted[my[e] + rank[b]] = (int32_t)(lo + 64 * b + lane);
+            }
+        }
+        return;
+    }
     for (int64_t g0 = lo; g0 < hi; g0 += 64 * kWaveGroupBatches) {
-        int32_t ev[kWaveGroupBatches];
         load_group(g0, ev);
         int32_t pos[kWaveGroupBatches];
 #pragma unroll

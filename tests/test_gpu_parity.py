@@ -610,6 +610,7 @@ def _grouping_ref(ids, n_exp, tile_j, small_max):
 @pytest.mark.parametrize("n_exp,n_tok,top_k,zipf", [(8, 512, 2, 1.1), (128, 2048, 8, 1.0), (6, 37, 3, 0.0),
                                                      (1000, 333, 4, 0.8), (5000, 50, 2, 0.0),
                                                      (128, 5000, 8, 1.0),    # many batches per wave
+                                                     (128, 2049, 8, 1.0),    # just past ids kept in registers
                                                      (1, 100, 1, 0.0),       # one expert: no id bits
                                                      (2304, 700, 4, 0.5),    # the most the wave ranking takes
                                                      (2305, 700, 4, 0.5),    # the per-thread counting beyond
