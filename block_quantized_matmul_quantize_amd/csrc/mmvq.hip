@@ -656,8 +656,11 @@ static hipError_t launch_mmvq_t(const uint8_t *w, int64_t rows, int64_t k, const
 // 5.2 us and dot4 5.7; at 14336 x 4096 dot4 takes 11.8 us and the LDS-staged kernel 15.3, at
 // 57344 x 4096 34 and 53 (its 16-row workgroups each quantize all of x and run one step per wave,
 // while dot4's waves stream many rows).  At two or three columns dot4 is 0.8-1.4 us slower.
+// Q3_K and IQ4_XS, which the LDS-staged kernel does not serve, take dot4 up to three columns at
+// any row count: their alternative is a separate quantize launch and the register-streamed kernel.
 constexpr int64_t kDot4MinRows = 8192;
 static int dot4_auto_cols(int type, int64_t rows) {
+    if (type == kQ3_K || type == kIQ4_XS) return 3;
     return rows >= kDot4MinRows && (type == kQ4_K || type == kQ5_K || type == kQ8_0 || type == kQ4_0) ? 1 : 0;
 }
 

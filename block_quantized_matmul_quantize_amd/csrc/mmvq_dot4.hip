@@ -9,7 +9,10 @@
 // sub-blocks 2g and 2g+1 -- for Q4_K the 32 qs bytes 32g..32g+31 (low nibbles sub-block 2g, high
 // nibbles 2g+1; Q5_K: the same qs bytes 32 further on, plus all 32 qh bytes, whose bits 2g and
 // // 2g+1 are the fifth bits of the two sub-blocks), for Q8_0 the two 34-byte blocks, for Q4_0 the two
-// 18-byte blocks (nibbles turned into int8 codes minus 8 in registers).  Consecutive lanes of a row
+// 18-byte blocks (nibbles turned into int8 codes minus 8 in registers), for Q3_K the 32 qs bytes
+// 32(g/2).. (2-bit codes of two 32-value rows j, shifts 2j) with all 32 hmask bytes (their third
+// bits) and the 12 scale bytes, for IQ4_XS the 32 qs bytes of sub-blocks 2g and 2g+1 (4-bit
+// codebook indices, looked up in registers).  Consecutive lanes of a row
 // read consecutive bytes, so each quarter-wave load touches one or two cache lines.  The columns' q8_1 codes and
 // fp32 (d, s) are staged once per workgroup in LDS -- read from q8_1 blocks, or, for fp32 input,
 // quantized on the spot with the same arithmetic as the standalone quantize kernel (q8_1.hpp),
@@ -17,11 +20,14 @@
 // broadcast).  Next step's weights load while this step computes.
 //   Q4_K, Q5_K  acc += D(2g)*(d*sc)*d_a - (dmin*m)*s_a   (+ the same for sub-block 2g+1)
 //   Q8_0, Q4_0  acc += D*d_w*d_a                   (both blocks)
+//   IQ4_XS      acc += D*(d*(ls-32))*d_a            (both blocks)
+//   Q3_K        acc += ((sc-32)*D_lo + (sc'-32)*D_hi)*d*d_a   (two 16-value sub-blocks per q8_1 block,
+//               D over the codes minus 4; the GP100 patch page, "How" step 3, names the offset)
 // The four quarters of a row are summed with lane shuffles, the waves in LDS in a fixed order.
 // GLU (gate/up fusion, the MMQ page's fusion passage): rows 0-7 of the workgroup are 8 gate rows,
 // rows 8-15 the same 8 rows of the up matrix, and the write-back applies silu(gate) * up.
 // Requirements (checked by the host): K a multiple of 256; Q4_K / Q5_K weights and rows 16-byte
-// aligned, Q8_0 / Q4_0 4-byte aligned; activations 4-byte aligned.
+// aligned, Q8_0 / Q4_0 4-byte aligned, Q3_K / IQ4_XS 2-byte aligned; activations 4-byte aligned.
 #include "common.hpp"
 #include "launch.hpp"
 #include "mv_cols.hpp"
@@ -89,11 +95,39 @@ template <> struct W4<kQ4_0> {
         v4 = *(const uint32_t *)(p + 32);
     }
 };
+template <> struct W4<kQ3_K> {
+    u32x4 hm0, hm1, q0, q1;   // hmask[0..31]; qs[32h..32h+31], h = g/2 (values 128h + 32j + l, j = 2(g&1), +1)
+    uint32_t s0, s1, s2, dbits;   // the 12 scale bytes, d
+    __device__ __forceinline__ void load(const uint8_t *base, uint32_t off, int g) {
+        const uint8_t *p = base + off;
+        hm0 = ld16(p);
+        hm1 = ld16(p + 16);
+        q0 = ld16(p + 32 + 32 * (g >> 1));
+        q1 = ld16(p + 48 + 32 * (g >> 1));
+        s0 = ld4(p + 96);
+        s1 = ld4(p + 100);
+        s2 = ld4(p + 104);
+        dbits = ld2(p + 108);
+    }
+};
+template <> struct W4<kIQ4_XS> {
+    uint32_t h0, h1;   // {d, scales_h}, scales_l
+    u32x4 qa, qb;      // qs of sub-blocks 2g and 2g+1 (16 bytes each: low nibbles values 0-15, high 16-31)
+    __device__ __forceinline__ void load(const uint8_t *base, uint32_t off, int g) {
+        const uint8_t *p = base + off;
+        h0 = ld4(p);
+        h1 = ld4(p + 4);
+        qa = ld16(p + 8 + 32 * g);
+        qb = ld16(p + 24 + 32 * g);
+    }
+};
 template <int T> struct StepBytes;
 template <> struct StepBytes<kQ4_K> { static constexpr int V = 144; };
 template <> struct StepBytes<kQ5_K> { static constexpr int V = 176; };
 template <> struct StepBytes<kQ8_0> { static constexpr int V = 272; };
 template <> struct StepBytes<kQ4_0> { static constexpr int V = 144; };
+template <> struct StepBytes<kQ3_K> { static constexpr int V = 110; };
+template <> struct StepBytes<kIQ4_XS> { static constexpr int V = 136; };
 
 template <int T, int NC, bool DBG, bool EXPERT, bool F32, bool GLU>
 __global__ __launch_bounds__(1024) void mmvq_dot4_kernel(const uint8_t *__restrict__ w, const uint8_t *__restrict__ w2,
@@ -167,9 +201,10 @@ __global__ __launch_bounds__(1024) void mmvq_dot4_kernel(const uint8_t *__restri
     for (int c = 0; c < NC; ++c) acc[c] = 0.f;
     int32_t *dbg_row = nullptr;
     int64_t dbg_ld = 0;
+    constexpr int DS = kSub16<T> ? 2 : 1;   // exported dots per 32 values (Q3_K: one per 16)
     if (DBG && row0 + r < rows) {
-        dbg_ld = rows * (int64_t)nb;
-        dbg_row = dbg + (row0 + r) * (int64_t)nb;
+        dbg_ld = rows * (int64_t)nb * DS;
+        dbg_row = dbg + (row0 + r) * (int64_t)nb * DS;
     }
 
     for (int it = 0; it < my_steps; ++it) {
@@ -230,6 +265,92 @@ __global__ __launch_bounds__(1024) void mmvq_dot4_kernel(const uint8_t *__restri
                     a = fmaf(-wm0, f.y, a);
                     a = fmaf((float)D1, ws1 * f.z, a);
                     a = fmaf(-wm1, f.w, a);
+                    acc[c] = a;
+                }
+            }
+        } else if constexpr (T == kQ3_K) {
+            // quarter g: h = g/2, j = 2(g&1) + jj for the q8_1 blocks b0 + jj (jj = 0, 1); value
+            // 128h + 32j + l takes bits 2j of qs[32h + l] and bit 4h + j of hmask[l], minus 4
+            // ((c + 124) ^ 128 per byte: c - 4 as int8, no carry between bytes).  Sub-block t =
+            // 4g + 2jj + (l >= 16): low 4 scale bits in nibble h of scale byte 4(g&1) + 2jj + (l >= 16),
+            // top 2 bits at 2g of byte 8 + 2jj + (l >= 16).
+            const int h = g >> 1;
+            const float d = h2f((uint16_t)x.dbits);
+            const uint32_t sl = (g & 1) ? x.s1 : x.s0;
+            const uint32_t qv[8] = {x.q0.x, x.q0.y, x.q0.z, x.q0.w, x.q1.x, x.q1.y, x.q1.z, x.q1.w};
+            const uint32_t hv[8] = {x.hm0.x, x.hm0.y, x.hm0.z, x.hm0.w, x.hm1.x, x.hm1.y, x.hm1.z, x.hm1.w};
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const int j = 2 * (g & 1) + jj, hb = 4 * h + j;
+                uint32_t cv[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    cv[i] = ((((qv[i] >> (2 * j)) & 0x03030303u) | (((hv[i] >> hb) & 0x01010101u) << 2)) + 0x7C7C7C7Cu) ^
+                            0x80808080u;
+                int sc[2];
+#pragma unroll
+                for (int lh = 0; lh < 2; ++lh) {
+                    const int bsel = 8 * (2 * jj + lh);
+                    sc[lh] = (int)(((sl >> (bsel + 4 * h)) & 15u) | (((x.s2 >> (bsel + 2 * g)) & 3u) << 4)) - 32;
+                }
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    if (c >= ncols) break;
+                    const uint8_t *ab = acodes + ((size_t)c * nb + b0 + jj) * 32;
+                    const u32x4 a0 = *(const u32x4 *)ab, a1 = *(const u32x4 *)(ab + 16);
+                    int Dl = 0, Dh = 0;
+                    Dl = dot4(cv[0], a0.x, Dl); Dl = dot4(cv[1], a0.y, Dl); Dl = dot4(cv[2], a0.z, Dl); Dl = dot4(cv[3], a0.w, Dl);
+                    Dh = dot4(cv[4], a1.x, Dh); Dh = dot4(cv[5], a1.y, Dh); Dh = dot4(cv[6], a1.z, Dh); Dh = dot4(cv[7], a1.w, Dh);
+                    if (DBG) {
+                        if (dbg_row) {
+                            dbg_row[(int64_t)c * dbg_ld + 2 * (b0 + jj)] = Dl;
+                            dbg_row[(int64_t)c * dbg_ld + 2 * (b0 + jj) + 1] = Dh;
+                        }
+                    } else {
+                        // (sc_lo D_lo + sc_hi D_hi) is exact in int32 (|D| <= 16 * 4 * 127) and in fp32
+                        const float da = aft[(size_t)c * nb + b0 + jj].x;
+                        acc[c] = fmaf((float)(sc[0] * Dl + sc[1] * Dh), d * da, acc[c]);
+                    }
+                }
+            }
+        } else if constexpr (T == kIQ4_XS) {
+            // sub-blocks 2g (qa) and 2g+1 (qb) = q8_1 blocks b0, b0 + 1; low nibbles are values
+            // 0-15, high nibbles 16-31, each an index into the codebook; 6-bit scale of sub-block b:
+            // nibble b&1 of scales_l byte b/2 (= g), top bits at 2b of scales_h, minus 32
+            const float d = h2f((uint16_t)(x.h0 & 0xFFFF));
+            const uint32_t sh = x.h0 >> 16, sl = x.h1 >> (8 * g);
+            const float ws0 = d * (float)((int)((sl & 15u) | (((sh >> (4 * g)) & 3u) << 4)) - 32);
+            const float ws1 = d * (float)((int)(((sl >> 4) & 15u) | (((sh >> (4 * g + 2)) & 3u) << 4)) - 32);
+            const uint32_t av[4] = {x.qa.x, x.qa.y, x.qa.z, x.qa.w}, bv[4] = {x.qb.x, x.qb.y, x.qb.z, x.qb.w};
+            uint32_t q0[8], q1[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                q0[i] = iq4_lookup4(av[i] & 0x0F0F0F0Fu);
+                q0[4 + i] = iq4_lookup4((av[i] >> 4) & 0x0F0F0F0Fu);
+                q1[i] = iq4_lookup4(bv[i] & 0x0F0F0F0Fu);
+                q1[4 + i] = iq4_lookup4((bv[i] >> 4) & 0x0F0F0F0Fu);
+            }
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                if (c >= ncols) break;
+                const uint8_t *ab = acodes + ((size_t)c * nb + b0) * 32;
+                const u32x4 a0 = *(const u32x4 *)ab, a1 = *(const u32x4 *)(ab + 16);
+                const u32x4 a2 = *(const u32x4 *)(ab + 32), a3 = *(const u32x4 *)(ab + 48);
+                int D0 = 0, D1 = 0;
+                D0 = dot4(q0[0], a0.x, D0); D0 = dot4(q0[1], a0.y, D0); D0 = dot4(q0[2], a0.z, D0); D0 = dot4(q0[3], a0.w, D0);
+                D0 = dot4(q0[4], a1.x, D0); D0 = dot4(q0[5], a1.y, D0); D0 = dot4(q0[6], a1.z, D0); D0 = dot4(q0[7], a1.w, D0);
+                D1 = dot4(q1[0], a2.x, D1); D1 = dot4(q1[1], a2.y, D1); D1 = dot4(q1[2], a2.z, D1); D1 = dot4(q1[3], a2.w, D1);
+                D1 = dot4(q1[4], a3.x, D1); D1 = dot4(q1[5], a3.y, D1); D1 = dot4(q1[6], a3.z, D1); D1 = dot4(q1[7], a3.w, D1);
+                if (DBG) {
+                    if (dbg_row) {
+                        dbg_row[(int64_t)c * dbg_ld + b0] = D0;
+                        dbg_row[(int64_t)c * dbg_ld + b0 + 1] = D1;
+                    }
+                } else {
+                    const f32x4 f = *(const f32x4 *)(aft + (size_t)c * nb + b0);   // d0, s0, d1, s1
+                    float a = acc[c];
+                    a = fmaf((float)D0, ws0 * f.x, a);
+                    a = fmaf((float)D1, ws1 * f.z, a);
                     acc[c] = a;
                 }
             }
@@ -364,10 +485,14 @@ hipError_t dispatch(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq
 int mmvq_dot4_max_cols() { return 3; }
 
 bool mmvq_dot4_supported(int type, const void *w, int64_t k, const void *xq, const ColMap *cm) {
-    if (type != kQ4_K && type != kQ5_K && type != kQ8_0 && type != kQ4_0) return false;
+    if (type != kQ4_K && type != kQ5_K && type != kQ8_0 && type != kQ4_0 && type != kQ3_K && type != kIQ4_XS)
+        return false;
     if (k % kSuper != 0 || k < kSuper || k > 32768) return false;
-    const int64_t row_bytes = type == kQ8_0 ? k / 32 * 34 : type == kQ4_0 ? k / 32 * 18 : k / 256 * (type == kQ5_K ? 176 : 144);
-    const int align = type == kQ8_0 || type == kQ4_0 ? 4 : 16;
+    const int64_t row_bytes = type == kQ8_0   ? k / 32 * 34
+                              : type == kQ4_0 ? k / 32 * 18
+                                              : k / 256 * (type == kQ5_K ? 176 : type == kQ3_K ? 110 : type == kIQ4_XS ? 136 : 144);
+    // Q3_K and IQ4_XS read every piece with 2-byte-aligned loads
+    const int align = type == kQ8_0 || type == kQ4_0 ? 4 : type == kQ3_K || type == kIQ4_XS ? 2 : 16;
     if (row_bytes % align != 0 || (uintptr_t)w % align != 0) return false;
     if ((uintptr_t)xq % 4 != 0) return false;
     if (cm && cm->w_expert_stride % align != 0) return false;
@@ -380,6 +505,8 @@ hipError_t launch_mmvq_dot4(int type, const uint8_t *w, int64_t rows, int64_t k,
     if (type == kQ5_K) return dispatch<kQ5_K>(w, rows, k, xq, n, y, dbg, cm, n_exp, max_cols, s);
     if (type == kQ8_0) return dispatch<kQ8_0>(w, rows, k, xq, n, y, dbg, cm, n_exp, max_cols, s);
     if (type == kQ4_0) return dispatch<kQ4_0>(w, rows, k, xq, n, y, dbg, cm, n_exp, max_cols, s);
+    if (type == kQ3_K) return dispatch<kQ3_K>(w, rows, k, xq, n, y, dbg, cm, n_exp, max_cols, s);
+    if (type == kIQ4_XS) return dispatch<kIQ4_XS>(w, rows, k, xq, n, y, dbg, cm, n_exp, max_cols, s);
     return hipErrorInvalidValue;
 }
 
@@ -396,6 +523,8 @@ hipError_t launch_mmvq_dot4_f32(int type, const uint8_t *w, int64_t rows, int64_
     QMM_D4F(kQ5_K)
     QMM_D4F(kQ8_0)
     QMM_D4F(kQ4_0)
+    QMM_D4F(kQ3_K)
+    QMM_D4F(kIQ4_XS)
 #undef QMM_D4F
     return hipErrorInvalidValue;
 }
@@ -413,6 +542,8 @@ hipError_t launch_mmvq_dot4_glu_f32(int type, const uint8_t *wg, const uint8_t *
     QMM_D4G(kQ5_K)
     QMM_D4G(kQ8_0)
     QMM_D4G(kQ4_0)
+    QMM_D4G(kQ3_K)
+    QMM_D4G(kIQ4_XS)
 #undef QMM_D4G
     return hipErrorInvalidValue;
 }

@@ -206,6 +206,9 @@ MV_AUTO = [
     (qmm.Q6_K, 14336, 1, (2, True)),
     *[(t, 14336, 2, (2, True)) for t in (qmm.Q4_K, qmm.Q8_0)],
     *[(t, 4096, 9, (0, False)) for t in (qmm.Q4_K, qmm.Q5_K, qmm.Q6_K, qmm.Q8_0, qmm.Q4_0)],
+    # Q3_K and IQ4_XS: dot4 up to three columns at any row count, then quantize + register-streamed
+    *[(t, r, n, (3, True)) for t in (qmm.Q3_K, qmm.IQ4_XS) for r in (16, 4096, 14336) for n in (1, 2, 3)],
+    *[(t, 4096, n, (1, False)) for t in (qmm.Q3_K, qmm.IQ4_XS) for n in (4, 8)],
 ]
 
 
@@ -230,6 +233,10 @@ def test_matvec_kernel_choice_follows_alignment_and_overrides():
     assert mk(qmm.Q8_0, 0x10004, 4096, 0x20000, 5, x_fp32=True) == (2, True)
     assert mk(qmm.Q8_0, 0x10002, 4096, 0x20000, 6, x_fp32=True) == (1, False)
     assert mk(qmm.Q6_K, 0x10004, 4096, 0x20000, 6, x_fp32=True) == (1, False)
+    # Q3_K / IQ4_XS: dot4 reads any 2-byte aligned rows
+    assert mk(qmm.Q3_K, 0x10002, 4096, 0x20000, 2, x_fp32=True) == (3, True)
+    assert mk(qmm.IQ4_XS, 0x10002, 4096, 0x20002, 3, x_fp32=False) == (1, False)
+    assert mk(qmm.IQ4_XS, 0x10002, 4096, 0x20004, 3, x_fp32=False) == (3, False)
     # K not a multiple of 256 (Q8_0 allows multiples of 32): register-streamed
     assert mk(qmm.Q8_0, 0x10000, 4128, 0x20000, 2, x_fp32=True) == (1, False)
     with pytest.raises(qmm.QmmError):

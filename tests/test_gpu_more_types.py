@@ -1,8 +1,9 @@
 """GPU parity for Q3_K and IQ4_XS (the GP100 patch page, "How" step 3: Q3_K's 3-bit codes carry a
 -4 offset, IQ4_XS maps 4-bit indices through a codebook; both have 6-bit scales minus 32).  They
-run on the register-streamed matrix-vector kernel (any 2-byte aligned rows) and the tiled kernel
-(Q3_K parked like Q6_K as scale-folded planes, IQ4_XS like Q8_0 as int8 codes plus a scale per
-32 values), dense, expert-indexed and gate/up-fused.  Bars as everywhere: integer dots from the
+run on the dot4 matrix-vector kernel (one to three columns, activations quantized in the kernel),
+the register-streamed matrix-vector kernel (any column count up to 8, any 2-byte aligned rows) and
+the tiled kernel (Q3_K parked like Q6_K as scale-folded planes, IQ4_XS like Q8_0 as int8 codes
+plus a scale per 32 values), dense, expert-indexed and gate/up-fused.  Bars as everywhere: integer dots from the
 production kernels bit-exact, fp32 outputs within gpu_util.assert_close's normalised bound.
 """
 import numpy as np
@@ -51,6 +52,7 @@ def test_subdots_matvec_bit_exact(qtype, n, spw):
     """Integer dots of the register-streamed kernel (Q3_K per 16 values, IQ4_XS per 32) at every
     steps-per-wave setting; 40 rows (ragged last row group), 1792 values = 7 steps (odd: rows are
     only 2-byte aligned for Q3_K)."""
+    qmm.set_override(qmm.OVR_MV_KERNEL, 1)
     qmm.set_override(qmm.OVR_MV_STEPS, spw)
     rows, k = 40, 1792
     w, x = _case(qtype, rows, k, n, 2000 + n)
@@ -58,6 +60,39 @@ def test_subdots_matvec_bit_exact(qtype, n, spw):
     got = qmm.debug_subdots(to_dev(w), qtype, rows, k, to_dev(xq), n, qmm.PATH_MATVEC).cpu().numpy()
     exp = oracle.subdots(qtype, w, rows, k, xq, n)
     assert np.array_equal(got, exp), np.argwhere(got != exp)[:5]
+
+
+@pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
+@pytest.mark.parametrize("n", [1, 2, 3])
+def test_subdots_dot4_bit_exact(qtype, n):
+    """Integer dots of the dot4 kernel (Q3_K per 16 values over the codes minus 4, IQ4_XS per 32
+    over the codebook values): 40 rows, 7 steps, rows 2-byte aligned for Q3_K."""
+    qmm.set_override(qmm.OVR_MV_KERNEL, 3)
+    rows, k = 40, 1792
+    w, x = _case(qtype, rows, k, n, 2050 + n)
+    xq = oracle.quantize_q8_1(x)
+    got = qmm.debug_subdots(to_dev(w), qtype, rows, k, to_dev(xq), n, qmm.PATH_MATVEC).cpu().numpy()
+    exp = oracle.subdots(qtype, w, rows, k, xq, n)
+    assert np.array_equal(got, exp), np.argwhere(got != exp)[:5]
+
+
+@pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
+@pytest.mark.parametrize("n", [1, 2, 3])
+def test_dot4_fp32_and_q8_1_inputs(qtype, n):
+    """The dot4 kernel from fp32 activations (quantized in the kernel) and from q8_1 blocks, on
+    ragged rows with K = 7 steps: every output within the bound, and both inputs give the same
+    outputs bit for bit (the in-kernel quantization writes the same codes)."""
+    qmm.set_override(qmm.OVR_MV_KERNEL, 3)
+    rows, k = 333, 1792
+    w, x = _case(qtype, rows, k, n, 2060 + n)
+    wd, xd = to_dev(w), to_dev(x)
+    assert qmm.matvec_kernel(qtype, wd, rows, k, xd, n) == (3, True)
+    y = qmm.matmul(wd, qtype, rows, k, xd).cpu().numpy()
+    xq = oracle.quantize_q8_1(x)
+    ref = oracle.matmul_q8_1(qtype, w, rows, k, xq, n)
+    assert_close(y, ref, row_norms(qtype, w, rows, k), col_norms(xq, n, k), what=f"{TNAME[qtype]} dot4 n={n}")
+    yq = qmm.matmul_q8_1(wd, qtype, rows, k, to_dev(xq), n).cpu().numpy()
+    assert np.array_equal(y, yq)
 
 
 @pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
@@ -89,12 +124,12 @@ def test_subdots_extreme_codes():
     blk[:, :, 2:4] = 0xFF
     blk[:, :, 4:8] = 0xFF
     for qtype, w in ((qmm.Q3_K, w3), (qmm.IQ4_XS, wi)):
-        for path in (qmm.PATH_MATVEC, qmm.PATH_TILED):
-            nn = 8 if path == qmm.PATH_MATVEC else n
+        # matrix-vector: 8 columns (register-streamed) and 3 (dot4); tiled: all 40
+        for path, nn in ((qmm.PATH_MATVEC, 8), (qmm.PATH_MATVEC, 3), (qmm.PATH_TILED, n)):
             got = qmm.debug_subdots(to_dev(w), qtype, rows, k, to_dev(xq[:nn]), nn, path).cpu().numpy()
             exp = (oracle.subdots(qtype, w, rows, k, xq[:nn], nn) if path == qmm.PATH_MATVEC
                    else _folded(qtype, w, rows, k, xq[:nn], nn))
-            assert np.array_equal(got, exp), (qtype, path)
+            assert np.array_equal(got, exp), (qtype, path, nn)
 
 
 def _full_check(qtype, rows, k, n, seed, what):
