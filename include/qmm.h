@@ -262,7 +262,8 @@ qmm_status qmm_debug_subdots(int type, const void *w, int64_t rows, int64_t k, c
  * matrix-vector regime), under the current overrides; host logic only, nothing is launched and
  * no GPU is needed.  x_fp32 = 1 asks about qmm_matmul with fp32 activations x, 0 about
  * qmm_matmul_q8_1 with q8_1 activations x; only the alignment of w and x, and the sizes, are looked
- * at (one column of 8192 or more rows takes the dot4 kernel, fewer rows the LDS-staged one).
+ * at (one column of 8192 or more rows takes the dot4 kernel, fewer rows the LDS-staged one;
+ * Q3_K and IQ4_XS take dot4 for one to three columns at any row count).
  * *out: 0 the call takes the tiled path (n > 8 or forced), 1 register-streamed, 2 LDS-staged
  * MFMA, 3 dot4; plus 16 when that kernel quantizes the fp32 activations itself (one launch, no
  * quantize kernel).  Errors: QMM_ERR_TYPE / QMM_ERR_SHAPE as for qmm_matmul, QMM_ERR_ARG for a
@@ -281,11 +282,13 @@ qmm_status qmm_matvec_kernel(int type, const void *w, int64_t rows, int64_t k, c
  *   QMM_OVR_MV_STEPS: 256-value steps per wave in the register-streamed matrix-vector kernel
  *                     (1, 2 or 4).
  *   QMM_OVR_MV_KERNEL: matrix-vector kernel: 1 register-streamed (any input), 2 LDS-staged
- *                     MFMA only, 3 dot4 only (up to 3 columns, Q4_K and Q8_0); calls the forced
- *                     kernel cannot serve fail with QMM_ERR_HIP.  The automatic choice takes the
- *                     dot4 kernel for Q4_K and Q8_0 with n = 1, else the LDS-staged kernel, when
- *                     K is a multiple of 256 and the weights are aligned (Q4_K, Q6_K: 16 bytes,
- *                     rows too; Q8_0: 4) and q8_1 activations 4-byte aligned; otherwise the
+ *                     MFMA only (Q4_0, Q8_0, Q4_K, Q5_K, Q6_K), 3 dot4 only (up to 3 columns;
+ *                     Q4_0, Q8_0, Q3_K, Q4_K, Q5_K, IQ4_XS); calls the forced kernel cannot serve
+ *                     fail with QMM_ERR_HIP.  The automatic choice takes the dot4 kernel for one
+ *                     column of 8192 or more rows (Q3_K, IQ4_XS: up to three columns at any
+ *                     rows), else the LDS-staged kernel, when K is a multiple of 256 and the
+ *                     weights are aligned (Q4_K, Q5_K, Q6_K: 16 bytes, rows too; Q8_0, Q4_0: 4;
+ *                     Q3_K, IQ4_XS: 2) and q8_1 activations 4-byte aligned; otherwise the
  *                     register-streamed kernel.
  *   QMM_OVR_FUSE_COLS: qmm_matmul only: most columns (1..8) for which the LDS-staged kernel
  *                     quantizes the fp32 activations itself instead of a separate quantize
