@@ -743,8 +743,6 @@ qmm_status run_id(int type, const void *w, const void *w_up, int64_t n_exp, int6
     const int64_t nx = n_tok * x_per_tok;
     const int64_t pairs = n_tok * top_k;
     uint8_t *xq = wsb + L.xq_off, *xt = wsb + L.tiled_off;
-    hipError_t e = qmm::launch_quantize_q8_1_tiled(x, nx, k, xt, xq, s);   // both layouts, one launch
-    if (e != hipSuccess) return hip_fail(e, "quantize launch");
     const int tile_j = id_tile_j(type, pairs, n_exp, o);
     qmm::ColMap cm{};
     cm.sorted = (const int32_t *)(wsb + L.sorted_off);
@@ -757,9 +755,20 @@ qmm_status run_id(int type, const void *w, const void *w_up, int64_t n_exp, int6
     cm.w_expert_stride = rows * (k / block_values(type)) * block_bytes(type);
     cm.act_rows = nx;
     const int small_max = k <= kMvMaxK ? kSmallMax : 0;
-    e = qmm::launch_moe_group(ids, pairs, (int32_t)n_exp, tile_j, small_max, (int32_t *)cm.sorted,
-                              (int32_t *)cm.bounds, (int32_t *)cm.tile_start, (int32_t *)cm.small, invalid, s);
-    if (e != hipSuccess) return hip_fail(e, "grouping launch");
+    hipError_t e;
+    if (qmm::moe_prologue_fused((int32_t)n_exp)) {
+        // grouping and the activations' quantization (both layouts) in one launch
+        e = qmm::launch_moe_prologue(ids, pairs, (int32_t)n_exp, tile_j, small_max, (int32_t *)cm.sorted,
+                                     (int32_t *)cm.bounds, (int32_t *)cm.tile_start, (int32_t *)cm.small, invalid, x,
+                                     nx, k, xt, xq, device_cus(), s);
+        if (e != hipSuccess) return hip_fail(e, "grouping and quantize launch");
+    } else {
+        e = qmm::launch_quantize_q8_1_tiled(x, nx, k, xt, xq, s);   // both layouts, one launch
+        if (e != hipSuccess) return hip_fail(e, "quantize launch");
+        e = qmm::launch_moe_group(ids, pairs, (int32_t)n_exp, tile_j, small_max, (int32_t *)cm.sorted,
+                                  (int32_t *)cm.bounds, (int32_t *)cm.tile_start, (int32_t *)cm.small, invalid, s);
+        if (e != hipSuccess) return hip_fail(e, "grouping launch");
+    }
     // experts with <= 8 columns: matrix-vector kernel, one workgroup row per listed expert
     if (k <= kMvMaxK) {
         e = w_up ? qmm::launch_mmvq_glu(type, (const uint8_t *)w, (const uint8_t *)w_up, rows, k, xq, 0, y, &cm, n_exp, o, s)

@@ -124,6 +124,13 @@ hipError_t launch_mmq_id(int type, const uint8_t *w, const uint8_t *w_up, int64_
 hipError_t launch_moe_group(const int32_t *ids, int64_t pairs, int32_t n_exp, int32_t tile_j,
                             int32_t small_max, int32_t *sorted, int32_t *bounds, int32_t *tile_start,
                             int32_t *small, int32_t *invalid, hipStream_t s);
+// Grouping + activation quantization (tiled and canonical layouts) in one launch, for n_exp up to
+// the per-wave grouping's limit (moe_prologue_fused); cus: compute units of the device.
+bool moe_prologue_fused(int32_t n_exp);
+hipError_t launch_moe_prologue(const int32_t *ids, int64_t pairs, int32_t n_exp, int32_t tile_j, int32_t small_max,
+                               int32_t *sorted, int32_t *bounds, int32_t *tile_start, int32_t *small, int32_t *invalid,
+                               const float *x, int64_t n_rows, int64_t k, uint8_t *tiled, uint8_t *canon,
+                               int32_t cus, hipStream_t s);
 
 // Panel layout (repack.hip): bytes of the layout for a [rows][k] matrix (-1: type or shape not
 // supported), and the one-time repack of the original blocks w into wp (16-byte aligned).

@@ -2,7 +2,9 @@
 // of the expert-sorted column list, built on the GPU so that nothing is read back; "MoE skew":
 // sorting by expert makes each expert's columns contiguous).
 //
-// One workgroup runs a counting sort of the (token, slot) pairs by expert id.  Up to 2304 experts
+// One workgroup runs a counting sort of the (token, slot) pairs by expert id; up to 2304 experts it
+// shares its launch with the quantization of the activations (moe_prologue_kernel, below), which
+// the other workgroups do meanwhile.  Up to 2304 experts
 // the slots come from per-wave LDS atomics (moe_group_wave_kernel, below: each expert's segment
 // holds exactly its pairs, in an order not fixed within a wave's share); for more experts, a
 // stable sort from per-thread counts:
@@ -23,6 +25,7 @@
 // in invalid[0].  No step loops over all experts or all threads in one thread.
 #include "common.hpp"
 #include "launch.hpp"
+#include "q8_1.hpp"
 
 namespace qmm {
 
@@ -280,13 +283,12 @@ __device__ __forceinline__ void wave_block_excl_scan3(int32_t (&v)[3], int32_t *
     }
 }
 
-__global__ __launch_bounds__(64 * kWaveGroupWaves) void moe_group_wave_kernel(
-    const int32_t *__restrict__ ids, int64_t pairs, int32_t n_exp, int32_t tile_j, int32_t small_max,
-    int32_t *__restrict__ sorted, int32_t *__restrict__ bounds, int32_t *__restrict__ tile_start,
-    int32_t *__restrict__ small, int32_t *__restrict__ invalid) {
-    __shared__ __align__(16) int32_t hist[kGroupTableInts];   // [wave][expert]
-    __shared__ int32_t wsum[3 * kWaveGroupWaves];
-    __shared__ int32_t bad_sh;
+// The grouping itself, run by one 1024-thread workgroup; hist / wsum / bad_sh are its LDS.
+__device__ __forceinline__ void moe_group_wave(const int32_t *__restrict__ ids, int64_t pairs, int32_t n_exp,
+                                               int32_t tile_j, int32_t small_max, int32_t *__restrict__ sorted,
+                                               int32_t *__restrict__ bounds, int32_t *__restrict__ tile_start,
+                                               int32_t *__restrict__ small, int32_t *__restrict__ invalid,
+                                               int32_t *hist, int32_t *wsum, int32_t &bad_sh) {
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     constexpr int NT = 64 * kWaveGroupWaves;
     const int64_t chunk = ((pairs + kWaveGroupWaves - 1) / kWaveGroupWaves + 63) & ~(int64_t)63;
@@ -408,6 +410,53 @@ __global__ __launch_bounds__(64 * kWaveGroupWaves) void moe_group_wave_kernel(
     }
 }
 
+__global__ __launch_bounds__(64 * kWaveGroupWaves) void moe_group_wave_kernel(
+    const int32_t *__restrict__ ids, int64_t pairs, int32_t n_exp, int32_t tile_j, int32_t small_max,
+    int32_t *__restrict__ sorted, int32_t *__restrict__ bounds, int32_t *__restrict__ tile_start,
+    int32_t *__restrict__ small, int32_t *__restrict__ invalid) {
+    __shared__ __align__(16) int32_t hist[kGroupTableInts];   // [wave][expert]
+    __shared__ int32_t wsum[3 * kWaveGroupWaves];
+    __shared__ int32_t bad_sh;
+    moe_group_wave(ids, pairs, n_exp, tile_j, small_max, sorted, bounds, tile_start, small, invalid, hist, wsum, bad_sh);
+}
+
+// The expert call's prologue in one launch: workgroup 0 groups the pairs (moe_group_wave), the
+// others quantize the fp32 activation rows into the tiled and the canonical q8_1 layouts with the
+// arithmetic of quantize_q8_1_tiled_kernel (q8_1.hpp), a 4-lane group per 32-value block, striding
+// over the blocks.  The two jobs are independent, so the grouping's latency -- one compute unit
+// working through a chain of loads, LDS atomics, scans and barriers -- hides under the
+// quantization instead of adding to it.
+__global__ __launch_bounds__(64 * kWaveGroupWaves) void moe_prologue_kernel(
+    const int32_t *__restrict__ ids, int64_t pairs, int32_t n_exp, int32_t tile_j, int32_t small_max,
+    int32_t *__restrict__ sorted, int32_t *__restrict__ bounds, int32_t *__restrict__ tile_start,
+    int32_t *__restrict__ small, int32_t *__restrict__ invalid, const float *__restrict__ x, int64_t n_rows,
+    int64_t k, uint8_t *__restrict__ tiled, uint8_t *__restrict__ canon) {
+    __shared__ __align__(16) int32_t hist[kGroupTableInts];
+    __shared__ int32_t wsum[3 * kWaveGroupWaves];
+    __shared__ int32_t bad_sh;
+    if (blockIdx.x == 0) {
+        moe_group_wave(ids, pairs, n_exp, tile_j, small_max, sorted, bounds, tile_start, small, invalid, hist, wsum,
+                       bad_sh);
+        return;
+    }
+    const int64_t nb = k / 32;
+    const int64_t total = n_rows * nb * 4;   // a multiple of 4: the 4 lanes of a block loop together
+    const int64_t stride = (int64_t)(gridDim.x - 1) * blockDim.x;
+    for (int64_t gid = (int64_t)(blockIdx.x - 1) * blockDim.x + threadIdx.x; gid < total; gid += stride) {
+        const int64_t blk = gid >> 2;
+        const int sub = (int)(gid & 3);
+        const int64_t row = blk / nb, bi = blk - row * nb;
+        const float *src = x + row * k + bi * 32 + 8 * sub;
+        const Q81Lane4 q = quantize_q8_1_lane4(*(const float4 *)src, *(const float4 *)(src + 4));
+        const int64_t slot = (bi >> 3) * n_rows + row;   // (step, row)
+        *(u32x2 *)(tiled + slot * 256 + 32 * (bi & 7) + 8 * sub) = u32x2{q.c0, q.c1};
+        if (sub == 0) ((uint32_t *)(tiled + (size_t)((nb + 7) / 8) * n_rows * 256))[slot * 8 + (bi & 7)] = q.ds;
+        uint8_t *yb = canon + blk * kQ8_1Bytes;
+        *(u32x2_a4 *)(yb + 4 + 8 * sub) = u32x2{q.c0, q.c1};
+        if (sub == 0) *(uint32_t *)yb = q.ds;
+    }
+}
+
 hipError_t launch_moe_group(const int32_t *ids, int64_t pairs, int32_t n_exp, int32_t tile_j, int32_t small_max,
                             int32_t *sorted, int32_t *bounds, int32_t *tile_start, int32_t *small, int32_t *invalid,
                             hipStream_t s) {
@@ -421,6 +470,25 @@ hipError_t launch_moe_group(const int32_t *ids, int64_t pairs, int32_t n_exp, in
     if ((int64_t)group_row_stride(nthr) * n_exp > kGroupTableInts) return hipErrorInvalidValue;
     hipLaunchKernelGGL(moe_group_kernel, dim3(1), dim3(kGroupThreads), 0, s, ids, pairs, n_exp, nthr, tile_j,
                        small_max, sorted, bounds, tile_start, small, invalid);
+    return hipGetLastError();
+}
+
+bool moe_prologue_fused(int32_t n_exp) { return n_exp >= 1 && n_exp <= kWaveMaxExperts; }
+
+hipError_t launch_moe_prologue(const int32_t *ids, int64_t pairs, int32_t n_exp, int32_t tile_j, int32_t small_max,
+                               int32_t *sorted, int32_t *bounds, int32_t *tile_start, int32_t *small, int32_t *invalid,
+                               const float *x, int64_t n_rows, int64_t k, uint8_t *tiled, uint8_t *canon,
+                               int32_t cus, hipStream_t s) {
+    if (!moe_prologue_fused(n_exp)) return hipErrorInvalidValue;
+    // one quantizing workgroup per remaining compute unit (each holds the grouping's LDS, so one
+    // workgroup per compute unit), at most one per 1024 threads of work
+    const int64_t work = n_rows * (k / 32) * 4;
+    int64_t q = (work + 64 * kWaveGroupWaves - 1) / (64 * kWaveGroupWaves);
+    const int64_t qmax = cus > 1 ? cus - 1 : 1;
+    if (q > qmax) q = qmax;
+    if (q < 1) q = 1;
+    hipLaunchKernelGGL(moe_prologue_kernel, dim3((unsigned)(1 + q)), dim3(64 * kWaveGroupWaves), 0, s, ids, pairs,
+                       n_exp, tile_j, small_max, sorted, bounds, tile_start, small, invalid, x, n_rows, k, tiled, canon);
     return hipGetLastError();
 }
 
