@@ -14,6 +14,29 @@
 
 #include "launch.hpp"
 
+namespace qmm {
+
+namespace {
+int g_nsm_cache[64];
+std::mutex g_nsm_mu;
+}  // namespace
+
+int device_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    std::lock_guard<std::mutex> lk(g_nsm_mu);
+    if (g_nsm_cache[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+        g_nsm_cache[dev] = v;
+    }
+    return g_nsm_cache[dev];
+}
+
+}  // namespace qmm
+
+using qmm::device_cus;
+
 namespace {
 
 thread_local std::string g_err;
@@ -75,20 +98,6 @@ int block_bytes(int type) {
 }
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
-
-int g_nsm_cache[64];
-std::mutex g_nsm_mu;
-int device_cus() {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    std::lock_guard<std::mutex> lk(g_nsm_mu);
-    if (g_nsm_cache[dev] == 0) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-        g_nsm_cache[dev] = v;
-    }
-    return g_nsm_cache[dev];
-}
 
 qmm_status check_common(int type, int64_t rows, int64_t k, int64_t n) {
     const int qk = block_values(type);
@@ -754,6 +763,7 @@ qmm_status run_id(int type, const void *w, const void *w_up, int64_t n_exp, int6
     cm.n_exp = (int32_t)n_exp;
     cm.w_expert_stride = rows * (k / block_values(type)) * block_bytes(type);
     cm.act_rows = nx;
+    cm.pairs = pairs;
     const int small_max = k <= kMvMaxK ? kSmallMax : 0;
     hipError_t e;
     if (qmm::moe_prologue_fused((int32_t)n_exp)) {

@@ -45,6 +45,7 @@ struct ColMap {
     int32_t n_exp;
     int64_t w_expert_stride;   // bytes between expert matrices
     int64_t act_rows;          // activation rows (n_tok * x_per_tok): row count of the tiled layout
+    int64_t pairs;             // (token, slot) pairs of the call
 };
 
 // Matrix-vector kernel: n <= 8 columns (dense) or the small experts (expert mode, grid.y = n_exp).
@@ -93,6 +94,7 @@ hipError_t launch_mmvq_stream(int type, const uint8_t *w, int64_t rows, int64_t 
                               float *y, int32_t *dbg, const ColMap *cm, int64_t n_exp, hipStream_t s);
 // dot4 matrix-vector kernel (mmvq_dot4.hip) for 1..mmvq_dot4_max_cols() dense columns: Q4_K and
 // Q8_0, K a multiple of 256.
+int device_cus();   // compute units of the current device, looked up once per device (api.cpp)
 int mmvq_dot4_max_cols();
 bool mmvq_dot4_supported(int type, const void *w, int64_t k, const void *xq, const ColMap *cm);
 hipError_t launch_mmvq_dot4(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n,

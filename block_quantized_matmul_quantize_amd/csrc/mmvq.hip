@@ -483,17 +483,17 @@ template <> struct MvStep<kIQ4_XS> {
 constexpr int mv_max_waves(int spw) { return spw == 1 ? 16 : spw == 2 ? 8 : 4; }
 
 template <int T, int SPW, bool DBG, bool EXPERT, bool GLU>
-__global__ __launch_bounds__(64 * mv_max_waves(SPW)) void mmvq_kernel(const uint8_t *__restrict__ w,
-                                                    const uint8_t *__restrict__ w2, int64_t rows, int64_t k,
-                                                    const uint8_t *__restrict__ xq, int64_t n, float *__restrict__ y,
-                                                    int32_t *__restrict__ dbg, ColMap cm) {
+// Returns false (workgroup-uniform) when expert slot ey holds no expert, true otherwise.
+__device__ __forceinline__ bool mmvq_body(const uint8_t *__restrict__ w, const uint8_t *__restrict__ w2, int64_t rows,
+                                          int64_t k, const uint8_t *__restrict__ xq, int64_t n, float *__restrict__ y,
+                                          int32_t *__restrict__ dbg, const ColMap &cm, int ey) {
     static_assert(!(GLU && DBG), "no debug export of the fused form");
     extern __shared__ __align__(16) uint8_t mv_smem[];
     using S = MvStep<T>;
     constexpr int NCG = S::NCG;
 
     MvCols mc;
-    if (!mv_resolve(mc, w, n, cm, EXPERT, GLU ? w2 : nullptr)) return;   // workgroup-uniform
+    if (!mv_resolve(mc, w, n, cm, EXPERT, GLU ? w2 : nullptr, ey)) return false;   // workgroup-uniform
     const int ncols = mc.ncols;
 
     const int lane = threadIdx.x & 63;
@@ -582,7 +582,7 @@ __global__ __launch_bounds__(64 * mv_max_waves(SPW)) void mmvq_kernel(const uint
             }
         }
     }
-    if (DBG) return;
+    if (DBG) return true;
 
     // Combine the sub-block slots held by lane groups: Q4_K/Q8_0 lanes g and g^2 (the two halves
     // of the block diagonal), Q6_K lanes g = 0..3 (the four 16-value sub-blocks).
@@ -605,7 +605,7 @@ __global__ __launch_bounds__(64 * mv_max_waves(SPW)) void mmvq_kernel(const uint
             for (int e = 0; e < 4; ++e) sRed[wave * 128 + lane * (4 * NCG) + cg * 4 + e] = acc[cg][e];
     }
     __syncthreads();
-    if (wave != 0 || !holder || row >= rows || (GLU && L.r16 >= 8)) return;
+    if (wave != 0 || !holder || row >= rows || (GLU && L.r16 >= 8)) return true;
 #pragma unroll
     for (int cg = 0; cg < NCG; ++cg)
 #pragma unroll
@@ -618,6 +618,31 @@ __global__ __launch_bounds__(64 * mv_max_waves(SPW)) void mmvq_kernel(const uint
             const int c = kSub16<T> ? 4 * cg + e : 4 * L.g + e;
             if (c < ncols) y[mc.pair(c) * rows + row] = GLU ? v / (1.0f + expf(-v)) * u : v;
         }
+    return true;
+}
+
+// Dense: one row group per workgroup.  Expert mode: grid row blockIdx.y takes the listed small
+// experts blockIdx.y, blockIdx.y + gridDim.y, ... until the compacted list ends (see
+// mmvq_stream_kernel).
+template <int T, int SPW, bool DBG, bool EXPERT, bool GLU>
+__global__ __launch_bounds__(64 * mv_max_waves(SPW)) void mmvq_kernel(const uint8_t *__restrict__ w,
+                                                    const uint8_t *__restrict__ w2, int64_t rows, int64_t k,
+                                                    const uint8_t *__restrict__ xq, int64_t n, float *__restrict__ y,
+                                                    int32_t *__restrict__ dbg, ColMap cm) {
+    if constexpr (!EXPERT) {
+        mmvq_body<T, SPW, DBG, EXPERT, GLU>(w, w2, rows, k, xq, n, y, dbg, cm, -1);
+    } else {
+        if (gridDim.y == (unsigned)cm.n_exp) {   // one expert slot per grid row: no loop
+            mmvq_body<T, SPW, DBG, EXPERT, GLU>(w, w2, rows, k, xq, n, y, dbg, cm, (int)blockIdx.y);
+            return;
+        }
+        for (int ey = blockIdx.y;;) {
+            if (!mmvq_body<T, SPW, DBG, EXPERT, GLU>(w, w2, rows, k, xq, n, y, dbg, cm, ey)) break;
+            ey += gridDim.y;
+            if (ey >= cm.n_exp) break;
+            __syncthreads();   // the next expert reuses the LDS
+        }
+    }
 }
 
 template <int T, int SPW, bool DBG, bool EXPERT, bool GLU = false>
@@ -629,7 +654,8 @@ static hipError_t launch_mmvq_spw(const uint8_t *w, int64_t rows, int64_t k, con
     if (nw > mv_max_waves(SPW)) nw = mv_max_waves(SPW);
     if (nw < 1) nw = 1;
     constexpr int RW = GLU ? kMvRows / 2 : kMvRows;   // outputs per workgroup
-    dim3 grid((unsigned)((rows + RW - 1) / RW), EXPERT ? (unsigned)n_exp : 1u);
+    const int64_t groups = (rows + RW - 1) / RW;
+    dim3 grid((unsigned)groups, EXPERT ? (unsigned)mv_expert_slots(groups, n_exp, c.pairs) : 1u);
     const size_t smem = (size_t)(k / 32) * 8 * sizeof(float2) + (size_t)nw * 128 * sizeof(float);
     // once per process (a function-local static is initialised exactly once, thread-safely)
     static const hipError_t attr_err = hipFuncSetAttribute((const void *)mmvq_kernel<T, SPW, DBG, EXPERT, GLU>,

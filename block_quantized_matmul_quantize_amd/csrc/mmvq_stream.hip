@@ -122,11 +122,11 @@ struct MvArgs {
 // PK: w is in the panel layout (repack.hip): workgroup b reads panels (b, s), each 16 * B
 // contiguous bytes fetched by lane-consecutive 16-byte loads and parked in LDS unchanged; the
 // operand reads below then address slabs (256 bytes, one 16-byte piece per row).
-template <int T, bool DBG, bool EXPERT, bool F32, bool GLU, bool PK = false>
-__global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__restrict__ w, const uint8_t *__restrict__ w2,
-                                                          const void *__restrict__ xin,
-                                                          float *__restrict__ y, int32_t *__restrict__ dbg,
-                                                          MvArgs P, ColMap cm) {
+template <int T, bool DBG, bool EXPERT, bool F32, bool GLU, bool PK>
+// Returns false (workgroup-uniform) when expert slot ey holds no expert, true otherwise.
+__device__ __forceinline__ bool mmvq_stream_body(const uint8_t *__restrict__ w, const uint8_t *__restrict__ w2,
+                                                 const void *__restrict__ xin, float *__restrict__ y,
+                                                 int32_t *__restrict__ dbg, const MvArgs &P, const ColMap &cm, int ey) {
     static_assert(!PK || !(GLU || EXPERT || DBG), "the panel layout serves the dense product");
     using S = Stage<T, PK>;
     constexpr int PPR = Geo<T>::PPR, RSTR = Geo<T>::RSTR, WB = S::WB, SB = S::BYTES;
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
 
     MvCols mc;
     static_assert(!(GLU && DBG), "no debug export of the fused form");
-    if (!mv_resolve(mc, w, P.n, cm, EXPERT, GLU ? w2 : nullptr)) return;   // workgroup-uniform
+    if (!mv_resolve(mc, w, P.n, cm, EXPERT, GLU ? w2 : nullptr, ey)) return false;   // workgroup-uniform
     const int ncols = mc.ncols;                           // >= 1
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -558,7 +558,7 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
         }
 
     }
-    if (DBG) return;
+    if (DBG) return true;
 
     // Combine the sub-block slots held by lane groups: Q4_K/Q8_0 lanes g and g^2 (the two halves
     // of the block diagonal), Q6_K lanes g = 0..3 (the four 16-value sub-blocks).
@@ -583,22 +583,49 @@ __global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__rest
             for (int e = 0; e < 4; ++e) red[lane * (4 * NCG) + cg * 4 + e] = acc[cg][e];
     }
     __syncthreads();
-    // 128 threads each sum one (row, column) over the waves, all loads in flight at once.
-    const int t = threadIdx.x;
-    if (t >= 128) return;
-    int rr, c;
-    if (T == kQ6_K) { rr = t >> 3; c = t & 7; }
-    else { rr = (t >> 2) & 15; c = 4 * (t >> 6) + (t & 3); }
-    if (GLU && rr >= 8) return;
-    // GLU: the up value of (rr, c) sits at row rr + 8: index t + 64 (Q6_K) or t + 32
-    constexpr int kUp = T == kQ6_K ? 64 : 32;
-    float v = 0.f, u = 0.f;
-    for (int wv = 0; wv < nwaves; ++wv) {
-        const float *rb = (const float *)(smem + (size_t)wv * (kHead + SB) + kHead);
-        v += rb[t];
-        if (GLU) u += rb[t + kUp];
+    // Each of the 128 (row, column) sums over the waves is one thread's, all loads in flight at
+    // once; a one-wave workgroup (K = 256) takes two per thread.
+    for (int t = threadIdx.x; t < 128; t += blockDim.x) {
+        int rr, c;
+        if (T == kQ6_K) { rr = t >> 3; c = t & 7; }
+        else { rr = (t >> 2) & 15; c = 4 * (t >> 6) + (t & 3); }
+        if (GLU && rr >= 8) continue;
+        // GLU: the up value of (rr, c) sits at row rr + 8: index t + 64 (Q6_K) or t + 32
+        constexpr int kUp = T == kQ6_K ? 64 : 32;
+        float v = 0.f, u = 0.f;
+        for (int wv = 0; wv < nwaves; ++wv) {
+            const float *rb = (const float *)(smem + (size_t)wv * (kHead + SB) + kHead);
+            v += rb[t];
+            if (GLU) u += rb[t + kUp];
+        }
+        if (c < ncols && row0 + rr < rows) y[mc.pair(c) * rows + row0 + rr] = GLU ? v / (1.0f + expf(-v)) * u : v;
     }
-    if (c < ncols && row0 + rr < rows) y[mc.pair(c) * rows + row0 + rr] = GLU ? v / (1.0f + expf(-v)) * u : v;
+    return true;
+}
+
+// Dense: one row group per workgroup.  Expert mode: the workgroups of grid row blockIdx.y take the
+// listed small experts blockIdx.y, blockIdx.y + gridDim.y, ... until the list ends (it is compacted,
+// -1 after the last), so the launch holds a few workgroups per row group rather than one per
+// expert, most of which would find no expert to run.
+template <int T, bool DBG, bool EXPERT, bool F32, bool GLU, bool PK = false>
+__global__ __launch_bounds__(1024) void mmvq_stream_kernel(const uint8_t *__restrict__ w, const uint8_t *__restrict__ w2,
+                                                          const void *__restrict__ xin,
+                                                          float *__restrict__ y, int32_t *__restrict__ dbg,
+                                                          MvArgs P, ColMap cm) {
+    if constexpr (!EXPERT) {
+        mmvq_stream_body<T, DBG, EXPERT, F32, GLU, PK>(w, w2, xin, y, dbg, P, cm, -1);
+    } else {
+        if (gridDim.y == (unsigned)cm.n_exp) {   // one expert slot per grid row: no loop
+            mmvq_stream_body<T, DBG, EXPERT, F32, GLU, PK>(w, w2, xin, y, dbg, P, cm, (int)blockIdx.y);
+            return;
+        }
+        for (int ey = blockIdx.y;;) {
+            if (!mmvq_stream_body<T, DBG, EXPERT, F32, GLU, PK>(w, w2, xin, y, dbg, P, cm, ey)) break;
+            ey += gridDim.y;
+            if (ey >= cm.n_exp) break;
+            __syncthreads();   // the next expert reuses the LDS stages
+        }
+    }
 }
 
 template <int T, bool DBG, bool EXPERT, bool F32 = false, bool GLU = false, bool PK = false>
@@ -620,7 +647,8 @@ hipError_t launch_t(const uint8_t *w, int64_t rows, int64_t k, const void *xq, i
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (attr_err != hipSuccess) return attr_err;
     constexpr int RW = GLU ? kRows / 2 : kRows;
-    dim3 grid((unsigned)((rows + RW - 1) / RW), EXPERT ? (unsigned)n_exp : 1u);
+    const int64_t groups = (rows + RW - 1) / RW;
+    dim3 grid((unsigned)groups, EXPERT ? (unsigned)mv_expert_slots(groups, n_exp, c.pairs) : 1u);
     hipLaunchKernelGGL((mmvq_stream_kernel<T, DBG, EXPERT, F32, GLU, PK>), grid, dim3(64 * (unsigned)nw), smem, s, w, w2,
                        xq, y, dbg, a, c);
     return hipGetLastError();

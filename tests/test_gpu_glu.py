@@ -101,6 +101,13 @@ def test_glu_matvec_kernels(qtype, n, kernel):
     _check_dense(qtype, 229, 1024, n, 1200 + 10 * n + kernel, f"{TNAME[qtype]} n={n} kernel={kernel}")
 
 
+@pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
+@pytest.mark.parametrize("n", [1, 5, 8])
+def test_glu_single_step_k(qtype, n):
+    """K = 256 (one wave per matrix-vector workgroup): gate and up sums of every column."""
+    _check_dense(qtype, 100, 256, n, 1260 + n, f"{TNAME[qtype]} k=256 n={n}")
+
+
 def test_glu_dense_tiled_path_for_few_columns():
     qmm.set_override(qmm.OVR_PATH, 2)
     _check_dense(qmm.Q4_K, 136, 768, 5, 990, "q4_K n=5 tiled")

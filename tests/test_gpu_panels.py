@@ -64,6 +64,13 @@ def test_packed_dense_ragged(qtype, n):
 
 
 @pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
+@pytest.mark.parametrize("n", [1, 5, 8])
+def test_packed_single_step_k(qtype, n):
+    """K = 256: one panel per row group, one wave per matrix-vector workgroup."""
+    _check_packed(qtype, 77, 256, n, 960 + n, f"{TNAME[qtype]} packed 77x256 n={n}")
+
+
+@pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
 @pytest.mark.parametrize("n", [1, 8])
 def test_packed_matvec_full_size(qtype, n):
     _check_packed(qtype, 4096, 4096, n, 970 + n, f"{TNAME[qtype]} packed 4096^2 n={n}")

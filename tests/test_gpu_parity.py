@@ -200,6 +200,14 @@ def test_dense_single_block_k(qtype):
 
 
 @pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
+@pytest.mark.parametrize("n", range(1, 9))
+def test_single_step_k_every_column_count(qtype, n):
+    """K = 256: the LDS-staged kernel runs one wave per workgroup, so its 128 (row, column) sums
+    over the waves fall two to a thread; every column count it serves, every output."""
+    _full_check(qtype, 77, 256, n, 1180 + n, f"{TNAME[qtype]} k=256 n={n}")
+
+
+@pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
 @pytest.mark.parametrize("n", [1, 2, 5, 8])
 def test_matvec_workload_full(qtype, n):
     """The matrix-vector workload at full size: 4096 x 4096, every output compared."""
@@ -583,6 +591,41 @@ def test_moe_small_experts_both_kernels(qtype, kernel):
         for s in range(top_k):
             a = t * top_k + s
             assert_close(y[t, s][None], ref[t, s][None], wn_all[ids[t, s]], xn_all[a:a + 1], what=f"pair {t},{s}")
+
+
+@pytest.mark.parametrize("kernel", [1, 2], ids=MV_KNAME.get)
+@pytest.mark.parametrize("qtype", [qmm.Q4_K, qmm.Q6_K, qmm.Q8_0], ids=TNAME.get)
+def test_moe_small_experts_strided_workgroups(qtype, kernel):
+    """Dense routing with a few small experts: more than 16 pairs per expert on average, so the
+    matrix-vector launch holds a few grid rows (about four workgroups per compute unit over the
+    2048 rows' 128 row groups: 8 rows on 256 compute units) and each row walks the small-expert
+    list with that stride, two experts for some workgroups.  Experts 0-3 take 54 pairs each,
+    experts 4-15 seven each (small); every output against the oracle, the tiled experts' too.
+    K = 256 (one wave per workgroup) except for Q6_K in the LDS-staged kernel, which needs
+    16-byte aligned rows (K a multiple of 2048)."""
+    qmm.set_override(qmm.OVR_MV_KERNEL, kernel)
+    rng = np.random.default_rng(1150 + qtype + kernel)
+    n_exp, rows, n_tok, top_k = 16, 2048, 150, 2
+    k = 2048 if qtype == qmm.Q6_K and kernel == 2 else 256
+    ids = np.zeros((n_tok, top_k), dtype=np.int32)
+    for t in range(n_tok):
+        ids[t, 0] = t % 4
+        ids[t, 1] = 4 + t % 12 if t < 84 else (t + 1) % 4
+    counts = np.bincount(ids.reshape(-1), minlength=n_exp)
+    assert counts[4:].max() <= 8 and ids.size > 16 * n_exp
+    w = synth.gen_weights(qtype, n_exp * rows, k, rng)
+    x = rng.standard_normal((n_tok, k)).astype(np.float32)
+    y, ws = qmm.matmul_id(to_dev(w), qtype, n_exp, rows, k, to_dev(x), to_dev(ids), x_per_tok=1)
+    assert qmm.matmul_id_invalid_count(ws) == 0
+    y = y.cpu().numpy()
+    ref, bad = oracle.matmul_id(qtype, w, n_exp, rows, k, x, 1, ids)
+    assert bad == 0
+    xq = oracle.quantize_q8_1(x)
+    wn_all = row_norms(qtype, w, n_exp * rows, k).reshape(n_exp, rows)
+    xn_all = col_norms(xq, n_tok, k)
+    for t in range(n_tok):
+        for s in range(top_k):
+            assert_close(y[t, s][None], ref[t, s][None], wn_all[ids[t, s]], xn_all[t:t + 1], what=f"pair {t},{s}")
 
 
 def _grouping_ref(ids, n_exp, tile_j, small_max):
