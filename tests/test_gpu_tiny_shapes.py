@@ -1,9 +1,10 @@
 """Small and degenerate shapes through every matrix-vector kernel and mode: one to three 256-value
 steps (one-, two- and three-wave workgroups), one and seventeen rows (a single ragged row group),
 every column count a kernel serves, the fp16-activation mode down to one 32-value block, the
-panel layout at one panel per row group, and the fused gate/up form.  Every output against the
-oracle within the normalised bound (the MMQ page, "shape criteria": n <= 8 runs the
-matrix-vector regime at any K)."""
+panel layout at one panel per row group, the fused gate/up form; the tiled kernel at one or two
+steps, one or 129 rows, every tile width, stream-K on and off; experts at one step.  Every output
+against the oracle within the normalised bound (the MMQ page, "shape criteria": n <= 8 runs the
+matrix-vector regime at any K, more columns the tiled one)."""
 import numpy as np
 import pytest
 import torch
@@ -25,11 +26,16 @@ SERVES = {1: set(TYPES), 2: {qmm.Q4_K, qmm.Q5_K, qmm.Q8_0, qmm.Q4_0, qmm.Q6_K},
           3: {qmm.Q4_K, qmm.Q5_K, qmm.Q8_0, qmm.Q4_0, qmm.Q3_K, qmm.IQ4_XS}}
 
 
+_KEYS = (qmm.OVR_PATH, qmm.OVR_STREAMK, qmm.OVR_TILE_J, qmm.OVR_MV_KERNEL)
+
+
 @pytest.fixture(autouse=True)
 def _clean_overrides():
-    qmm.set_override(qmm.OVR_MV_KERNEL, 0)
+    for key in _KEYS:
+        qmm.set_override(key, 0)
     yield
-    qmm.set_override(qmm.OVR_MV_KERNEL, 0)
+    for key in _KEYS:
+        qmm.set_override(key, 0)
 
 
 def _case(qtype, rows, k, n, seed):
@@ -99,3 +105,42 @@ def test_glu_one_step(qtype, kernel):
     qmm.set_override(qmm.OVR_MV_KERNEL, kernel)
     for n in ((1, 2, 3) if kernel == 3 else (1, 5, 8)):
         _check_glu(qtype, 9, 256, n, 3300 + n, f"{TNAME[qtype]} glu kernel={kernel} n={n}")
+
+
+@pytest.mark.parametrize("J", [32, 64, 128])
+@pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
+def test_tiled_few_steps_and_rows(qtype, J):
+    """The tiled kernel on one to two 256-value steps (Q8_0 / Q4_0 also a ragged 288), one and
+    129 rows (a single ragged row tile, and one full tile plus one row), 9 to 130 columns, with
+    stream-K forced on and off."""
+    qmm.set_override(qmm.OVR_PATH, 2)
+    qmm.set_override(qmm.OVR_TILE_J, J)
+    ks = (256, 512, 288) if qtype in (qmm.Q8_0, qmm.Q4_0) else (256, 512)
+    for k in ks:
+        for rows in (1, 129):
+            for n, sk in ((9, 1), (33, 2), (130, 2)):
+                qmm.set_override(qmm.OVR_STREAMK, sk)
+                _check(qtype, rows, k, n, 3400 + k + rows + n, f"{TNAME[qtype]} tiled J={J} {rows}x{k} n={n} sk={sk}")
+
+
+@pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
+def test_experts_one_step(qtype):
+    """Expert-indexed product at K = 256: three experts, one with 40 columns (tiled), one with 3
+    (matrix-vector), one with none; 17 rows; top-1 routing."""
+    rng = np.random.default_rng(3500 + qtype)
+    n_exp, rows, k, n_tok, top_k = 3, 17, 256, 43, 1
+    ids = np.zeros((n_tok, top_k), dtype=np.int32)
+    ids[:40, 0] = 0
+    ids[40:, 0] = 2
+    w = synth.gen_weights(qtype, n_exp * rows, k, rng)
+    x = rng.standard_normal((n_tok, k)).astype(np.float32)
+    y, ws = qmm.matmul_id(to_dev(w), qtype, n_exp, rows, k, to_dev(x), to_dev(ids), x_per_tok=1)
+    assert qmm.matmul_id_invalid_count(ws) == 0
+    y = y.cpu().numpy()
+    ref, bad = oracle.matmul_id(qtype, w, n_exp, rows, k, x, 1, ids)
+    assert bad == 0
+    xq = oracle.quantize_q8_1(x)
+    wn = row_norms(qtype, w, n_exp * rows, k).reshape(n_exp, rows)
+    xn = col_norms(xq, n_tok, k)
+    for t in range(n_tok):
+        assert_close(y[t, 0][None], ref[t, 0][None], wn[ids[t, 0]], xn[t:t + 1], what=f"{TNAME[qtype]} token {t}")
