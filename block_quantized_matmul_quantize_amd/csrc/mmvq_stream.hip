@@ -72,8 +72,9 @@ template <int T> struct PanelGeo {
 };
 
 template <int T, bool PK = false> struct Stage {
-    // weights (+ Q8_0 scales); panel layout: the panel itself (16 * B bytes)
-    static constexpr int WB = PK ? 16 * PanelGeo<T>::B : kRows * Geo<T>::RSTR + Geo<T>::WD;
+    // weights (+ Q8_0 scales); panel layout: no weights are parked, the space holds the
+    // cross-wave partial sums at the end (up to 2 KB)
+    static constexpr int WB = PK ? 2048 : kRows * Geo<T>::RSTR + Geo<T>::WD;
     static constexpr int AB = 8 * 256;                             // activation codes: [column][block][32]
     static constexpr int FB = 64 * 8;                              // fp32 (d, s): [block][column]
     static constexpr int BYTES = WB + AB + FB;
@@ -119,9 +120,10 @@ struct MvArgs {
     int32_t n;            // dense column count
 };
 
-// PK: w is in the panel layout (repack.hip): workgroup b reads panels (b, s), each 16 * B
-// contiguous bytes fetched by lane-consecutive 16-byte loads and parked in LDS unchanged; the
-// operand reads below then address slabs (256 bytes, one 16-byte piece per row).
+// PK: w is in the panel layout (repack.hip): workgroup b reads panels (b, s).  A slab (256
+// bytes, one 16-byte piece per row) is exactly a 16-row MFMA operand slice, so each lane loads the
+// pieces its operands need straight into registers -- 16 lanes read 256 contiguous bytes -- and
+// only the activations go through LDS (measured 3-5 % faster than parking the panel in LDS).
 template <int T, bool DBG, bool EXPERT, bool F32, bool GLU, bool PK>
 // Returns false (workgroup-uniform) when expert slot ey holds no expert, true otherwise.
 __device__ __forceinline__ bool mmvq_stream_body(const uint8_t *__restrict__ w, const uint8_t *__restrict__ w2,
@@ -176,15 +178,34 @@ __device__ __forceinline__ bool mmvq_stream_body(const uint8_t *__restrict__ w, 
 
     u32x4 wv[4];
     uint32_t wv4 = 0;
-    // panel layout: load i covers pieces 64i..64i+63 of the panel; the last covers PLAST of them
-    constexpr int PN = (PanelGeo<T>::B + 63) / 64, PLAST = PanelGeo<T>::B - 64 * (PN - 1);
-    u32x4 pv[PK ? PN : 1];
+    // panel layout: the pieces this lane's MFMA operands need, straight into registers (slab j,
+    // row r16 at 256 j + 16 r16 of the panel)
+    u32x4 pw[PK ? 5 : 1];
+    uint16_t pwd = 0;
     auto load_w = [&](int s) __attribute__((always_inline)) {
         if constexpr (PK) {
-            const uint8_t *src = wg + (uint32_t)(s * PB) + 16 * lane;
+            const uint8_t *src = wg + (uint32_t)(s * PB) + 16 * (lane & 15);
+            const int gg = lane >> 4;
+            if constexpr (kK45<T>) {
+                constexpr int QS = PanelGeo<T>::QS, HDR = PanelGeo<T>::HDR;
+                const int qa = (gg + 3) & 3;
+                pw[0] = *(const u32x4 *)(src + 256 * HDR);
+                pw[1] = *(const u32x4 *)(src + 256 * (QS + qa));
+                pw[2] = *(const u32x4 *)(src + 256 * (QS + 4 + qa));
+                if constexpr (T == kQ5_K) pw[3] = *(const u32x4 *)(src + 256 * q4_half(gg));
+            } else if constexpr (T == kQ6_K) {
+                pw[0] = *(const u32x4 *)(src + 256 * gg);
+                pw[1] = *(const u32x4 *)(src + 256 * (4 + gg));
+                pw[2] = *(const u32x4 *)(src + 256 * (8 + (gg & 1)));
+                pw[3] = *(const u32x4 *)(src + 256 * (10 + (gg & 1)));
+                pw[4] = *(const u32x4 *)(src + 256 * 12);
+                pwd = *(const uint16_t *)(wg + (uint32_t)(s * PB) + 13 * 256 + 2 * (lane & 15));
+            } else {
 #pragma unroll
-            for (int i = 0; i < PN; ++i)
-                if (i < PN - 1 || lane < PLAST) pv[i] = *(const u32x4 *)(src + 1024 * i);
+                for (int p = 0; p < 4; ++p)
+                    pw[p] = *(const u32x4 *)(src + 256 * (T == kQ4_0 ? 2 * p + (gg >> 1) : 4 * p + gg));
+                pw[4] = *(const u32x4 *)(src + 256 * PanelGeo<T>::HDR);
+            }
         } else if constexpr (T == kQ8_0) {
             const uint8_t *src = wg8 + (uint32_t)(s * 272) + wofs8;
 #pragma unroll
@@ -296,9 +317,7 @@ __device__ __forceinline__ bool mmvq_stream_body(const uint8_t *__restrict__ w, 
             *(float2 *)(st + asdst) = make_float2(h2f((uint16_t)(ads & 0xFFFF)), h2f((uint16_t)(ads >> 16)));
         }
         if constexpr (PK) {
-#pragma unroll
-            for (int i = 0; i < PN; ++i)
-                if (i < PN - 1 || lane < PLAST) *(u32x4 *)(st + 1024 * i + 16 * lane) = pv[i];
+            // weights stay in registers (pw)
         } else if constexpr (kK45<T>) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) *(u32x4 *)(st + pofs[i]) = wv[i];
@@ -423,10 +442,9 @@ __device__ __forceinline__ bool mmvq_stream_body(const uint8_t *__restrict__ w, 
             const uint8_t *wr = st + wrow;
             // this lane's qs pieces: (g + 3) % 4 and 4 + (g + 3) % 4 of the row's eight
             const int qa = (g + 3) & 3;
-            const u32x4 hdr = PK ? lds16(st + 256 * PanelGeo<T>::HDR + 16 * r16) : lds16(wr);
-            const u32x4 src1 = PK ? lds16(st + 256 * (PanelGeo<T>::QS + qa) + 16 * r16) : lds16(wr + QS + 16 + 16 * qa);
-            const u32x4 src2 = PK ? lds16(st + 256 * (PanelGeo<T>::QS + 4 + qa) + 16 * r16)
-                                  : lds16(wr + QS + 16 + 16 * (4 + qa));
+            const u32x4 hdr = PK ? pw[0] : lds16(wr);
+            const u32x4 src1 = PK ? pw[1] : lds16(wr + QS + 16 + 16 * qa);
+            const u32x4 src2 = PK ? pw[2] : lds16(wr + QS + 16 + 16 * (4 + qa));
             const int sel = g >> 1;
             const float d = h2f((uint16_t)(hdr.x & 0xFFFF));
             const float dmin = h2f((uint16_t)(hdr.x >> 16));
@@ -438,7 +456,7 @@ __device__ __forceinline__ bool mmvq_stream_body(const uint8_t *__restrict__ w, 
             if constexpr (T == kQ5_K) {
                 // fifth bits: this lane's bytes are values 16*half.. of sub-blocks
                 // 2*group + (j&1) + 4*(j>>1); bit (sub-block) of qh bytes 16*half..
-                const u32x4 qh = PK ? lds16(st + 256 * q4_half(g) + 16 * r16) : lds16(wr + 16 + 16 * q4_half(g));
+                const u32x4 qh = PK ? pw[PK ? 3 : 0] : lds16(wr + 16 + 16 * q4_half(g));
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int sbb = 2 * q4_group(g) + (j & 1) + 4 * (j >> 1);
@@ -475,12 +493,12 @@ __device__ __forceinline__ bool mmvq_stream_body(const uint8_t *__restrict__ w, 
             // original super-block bytes / panel slabs: ql pieces g and 4+g, qh pieces (g&1) and
             // 2+(g&1), the 16 scales, d
             const uint8_t *pr = st + 16 * r16;
-            const u32x4 ql0 = PK ? lds16(pr + 256 * g) : lds16(wr + 16 * g);
-            const u32x4 ql1 = PK ? lds16(pr + 256 * (4 + g)) : lds16(wr + 64 + 16 * g);
-            const u32x4 qh0 = PK ? lds16(pr + 256 * (8 + (g & 1))) : lds16(wr + 128 + 16 * (g & 1));   // half 0
-            const u32x4 qh1 = PK ? lds16(pr + 256 * (10 + (g & 1))) : lds16(wr + 160 + 16 * (g & 1));  // half 1
-            const u32x4 scv = PK ? lds16(pr + 256 * 12) : lds16(wr + 192);
-            const float d = h2f(PK ? *(const uint16_t *)(st + 13 * 256 + 2 * r16) : *(const uint16_t *)(wr + 208));
+            const u32x4 ql0 = PK ? pw[0] : lds16(wr + 16 * g);
+            const u32x4 ql1 = PK ? pw[PK ? 1 : 0] : lds16(wr + 64 + 16 * g);
+            const u32x4 qh0 = PK ? pw[PK ? 2 : 0] : lds16(wr + 128 + 16 * (g & 1));   // half 0
+            const u32x4 qh1 = PK ? pw[PK ? 3 : 0] : lds16(wr + 160 + 16 * (g & 1));  // half 1
+            const u32x4 scv = PK ? pw[PK ? 4 : 0] : lds16(wr + 192);
+            const float d = h2f(PK ? pwd : *(const uint16_t *)(wr + 208));
             const u32x4 neg32 = {0xE0E0E0E0u, 0xE0E0E0E0u, 0xE0E0E0E0u, 0xE0E0E0E0u};
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
@@ -521,7 +539,7 @@ __device__ __forceinline__ bool mmvq_stream_body(const uint8_t *__restrict__ w, 
         } else {
             const uint8_t *wr = st + wrow;
             const float *wd = (const float *)(st + kRows * RSTR) + 8 * r16;
-            const uint16_t *wdh = (const uint16_t *)(st + 256 * PanelGeo<T>::HDR + 16 * r16);   // panel: fp16 d
+            const uint32_t wdw[4] = {pw[PK ? 4 : 0].x, pw[PK ? 4 : 0].y, pw[PK ? 4 : 0].z, pw[PK ? 4 : 0].w};   // panel: fp16 d
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
                 const int blk = 2 * p + (g >> 1);
@@ -529,12 +547,12 @@ __device__ __forceinline__ bool mmvq_stream_body(const uint8_t *__restrict__ w, 
                 if constexpr (PK && T == kQ4_0) {
                     // block blk's 16 nibble bytes; this lane's half (g & 1) of its 32 values as
                     // int8 nibble - 8: (n + 120) ^ 0x80 per byte
-                    const u32x4 nb = lds16(st + 256 * blk + 16 * r16);
+                    const u32x4 nb = pw[p];
                     const uint32_t sh = 4 * (g & 1);
                     auto c4 = [sh](uint32_t v) { return (((v >> sh) & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u; };
                     q = u32x4{c4(nb.x), c4(nb.y), c4(nb.z), c4(nb.w)};
                 } else if constexpr (PK) {
-                    q = lds16(st + 256 * (4 * p + g) + 16 * r16);
+                    q = pw[p];
                 } else {
                     q = lds16(wr + 64 * p + 16 * g);
                 }
@@ -546,7 +564,7 @@ __device__ __forceinline__ bool mmvq_stream_body(const uint8_t *__restrict__ w, 
                         if (dbg_row && c < ncols) dbg_row[(int64_t)c * dbg_ld + s * 8 + blk] = D[e];
                     }
                 } else {
-                    const float ws = PK ? h2f(wdh[blk]) : wd[blk];
+                    const float ws = PK ? h2f((uint16_t)(wdw[blk >> 1] >> (16 * (blk & 1)))) : wd[blk];
                     const f32x4 t0 = *(const f32x4 *)(ftab + blk * 8 + 4 * (g & 1));
                     const f32x4 t1 = *(const f32x4 *)(ftab + blk * 8 + 4 * (g & 1) + 2);
                     acc[0][0] = fmaf((float)D[0], ws * t0.x, acc[0][0]);
