@@ -180,8 +180,10 @@ qmm_status qmm_matmul_id(int type, const void *w, int64_t n_exp, int64_t rows, i
 qmm_status qmm_matmul_id_invalid_count(const void *ws, int64_t *out, void *stream);
 /* Test hook (host logic only, no GPU call): where the expert grouping of a qmm_matmul_id call of
  * this shape lives in its workspace, so a test can check it ([MMQ] "expert bounds").  out[6]:
- * byte offsets of sorted (int32 [pairs]: pair indices t*top_k+slot grouped by expert, ascending
- * inside an expert), bounds (int32 [n_exp+1]: segment starts, bounds[n_exp] = valid pairs),
+ * byte offsets of sorted (int32 [pairs]: pair indices t*top_k+slot grouped by expert; inside an
+ * expert's segment the order is not fixed up to 2304 experts -- slots come from LDS atomics --
+ * and ascending beyond; no output depends on it), bounds (int32 [n_exp+1]: segment starts,
+ * bounds[n_exp] = valid pairs),
  * tile_start (int32 [n_exp+1]: prefix of tiled-kernel column tiles), small (int32 [n_exp]:
  * experts with 1..small_max columns in ascending order, then -1), then the column-tile width
  * and small_max the call uses.  Returns QMM_ERR_ARG for a bad shape. */
