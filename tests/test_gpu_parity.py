@@ -629,8 +629,9 @@ def test_moe_small_experts_strided_workgroups(qtype, kernel):
 
 
 def _grouping_ref(ids, n_exp, tile_j, small_max):
-    """Stable counting sort of the (token, slot) pairs by expert, as the expert-bounds passage
-    describes it: each expert's pairs contiguous and in ascending pair order."""
+    """Host counting sort of the (token, slot) pairs by expert (the expert-bounds passage: each
+    expert's pairs contiguous); stable, so each segment is in ascending pair order, against which
+    the device's segments are compared as sets."""
     flat = ids.reshape(-1).astype(np.int64)
     valid = (flat >= 0) & (flat < n_exp)
     p = np.nonzero(valid)[0]
