@@ -536,7 +536,59 @@ template <int NT> struct WFetchQ3 {
         }
     }
 };
-template <int NT> struct WFetch<kQ3_K, NT> : WFetchQ3<NT> {};
+// Q3_K with 8-wave tiles (J = 128), as Q6_K's: thread u owns row u/4 and the four 16-value groups
+// G = 8h + 2j + half with h = (u/2)%2, half = u%2, j = 0..3 -- all four read the same 16 qs
+// bytes 32h + 16 half.. (bit pairs j) and the same 16 hmask bytes 16 half.. (bits 4h + j) -- so it
+// prefetches those two pieces, the 12 scale bytes and (one thread per row) d in the previous step,
+// and unpacks them from registers at park time.
+template <int NT> struct WFetchQ3Reg {
+    static_assert(NT == 512, "one (row, half, group-parity) unit per thread");
+    u32x4 qs, hm;
+    uint32_t s0, s1, s2;
+    uint16_t d;
+    template <class WR>
+    __device__ __forceinline__ void fetch(const WR &wr, int64_t kb, int64_t) {
+        const int u = threadIdx.x;
+        const int r = u >> 2, h = (u >> 1) & 1, l0 = 16 * (u & 1);
+        qs = ld16(wr.template at<kQ3_K>(r, kb, 32 + 32 * h + l0));
+        hm = ld16(wr.template at<kQ3_K>(r, kb, l0));
+        s0 = ld4(wr.template at<kQ3_K>(r, kb, 96));
+        s1 = ld4(wr.template at<kQ3_K>(r, kb, 100));
+        s2 = ld4(wr.template at<kQ3_K>(r, kb, 104));
+        d = (u & 3) == 0 ? ld2(wr.template at<kQ3_K>(r, kb, 108)) : (uint16_t)0;
+    }
+    template <int J, class WR>
+    __device__ __forceinline__ void store(uint8_t *sm, const WR &, int64_t, int64_t) const {
+        const int u = threadIdx.x;
+        const int r = u >> 2, h = (u >> 1) & 1, half = u & 1;
+        int8_t *sLo = (int8_t *)(sm + Smem<kQ3_K, J>::W_OFF);
+        int8_t *sHi = sLo + kTI * kLd;
+        const uint32_t qw[4] = {qs.x, qs.y, qs.z, qs.w}, hw[4] = {hm.x, hm.y, hm.z, hm.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int G = 8 * h + 2 * j + half, t = 2 * j + half;   // t = G % 8
+            // low nibble of scale G in byte G%8 (nibble G/8 = h), top bits at 2(G/4) of byte 8 + G%4
+            const uint32_t lb = ((t < 4 ? s0 : s1) >> (8 * (t & 3) + 4 * h)) & 15u;
+            const uint32_t tb = (s2 >> (8 * (t & 3) + 2 * (2 * h + (j >> 1)))) & 3u;
+            const int sc = (int)(lb | (tb << 4)) - 32;
+            const s16x2 sc2 = {(short)sc, (short)sc}, off2 = {(short)(-4 * sc), (short)(-4 * sc)};
+            uint32_t lo_w[4], hi_w[4];
+#pragma unroll
+            for (int dd = 0; dd < 4; ++dd) {
+                const uint32_t code3 = ((qw[dd] >> (2 * j)) & 0x03030303u) | (((hw[dd] >> (4 * h + j)) & 0x01010101u) << 2);
+                q6_split4(code3, sc2, off2, lo_w[dd], hi_w[dd]);
+            }
+            *(u32x4 *)(sLo + r * kLd + 16 * G) = u32x4{lo_w[0], lo_w[1], lo_w[2], lo_w[3]};
+            *(u32x4 *)(sHi + r * kLd + 16 * G) = u32x4{hi_w[0], hi_w[1], hi_w[2], hi_w[3]};
+        }
+        if ((u & 3) == 0) {
+            float *sWs = (float *)(sm + Smem<kQ3_K, J>::WS_OFF);
+            sWs[r] = h2f(d);
+        }
+    }
+};
+
+template <int NT> struct WFetch<kQ3_K, NT> : std::conditional<(NT >= 512), WFetchQ3Reg<NT>, WFetchQ3<NT>>::type {};
 
 // IQ4_XS (GP100 patch page, "How" step 3: a 4-bit codebook index and a 6-bit scale - 32 per 32
 // values): unit (row, sub-block b) -- the 16 index bytes qs[16b..] (low nibbles: values 0-15,
