@@ -20,10 +20,10 @@ struct Ovr {
 
 hipError_t launch_quantize_q8_1(const float *x, int64_t n_rows, int64_t k, uint8_t *y, hipStream_t s);
 
-// Tiled-kernel activation layout: for each 256-value step kb and activation row r, the 8 blocks'
-// codes as 256 contiguous bytes at (kb * n_rows + r) * 256, then (after all steps' codes) the 8
-// blocks' fp16 (d, s) pairs at (kb * n_rows + r) * 32 -- every load of the tiled kernel aligned.
-inline size_t q8_1_tiled_bytes(int64_t n_rows, int64_t k) { return (size_t)((k / 32 + 7) / 8) * n_rows * 288; }
+// Tiled-kernel activation layout (tiled_act.hpp): for each 256-value step kb and activation row r,
+// the 8 blocks' codes (256 bytes), fp32 d (32 bytes) and s parts (32 bytes), each kind in a table
+// of its own indexed by kb * n_rows + r.
+inline size_t q8_1_tiled_bytes(int64_t n_rows, int64_t k) { return (size_t)((k / 32 + 7) / 8) * n_rows * 320; }
 // fp32 rows -> tiled layout (and, if canon is not null, the canonical q8_1 blocks as well)
 hipError_t launch_quantize_q8_1_tiled(const float *x, int64_t n_rows, int64_t k, uint8_t *tiled, uint8_t *canon,
                                       hipStream_t s);

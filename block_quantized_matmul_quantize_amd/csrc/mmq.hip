@@ -84,80 +84,140 @@ template <int T> constexpr bool kRaggedK = T == kQ8_0 || T == kQ4_0;
 // Types the panel layout (repack.hip) serves.
 template <int T> constexpr bool kPanel = T == kQ4_K || T == kQ5_K || T == kQ6_K || T == kQ8_0 || T == kQ4_0;
 
-// LDS layout of one step.
+// LDS layout of one step: a weight part and an activation part, each in buffers of its own.
 template <int T, int J> struct Smem {
+    // weight part (offsets from a weight buffer)
     static constexpr int W_BYTES = kK45<T> ? kTI * kLd4 + (T == kQ5_K ? kTI * 32 : 0)   // qs (+ Q5_K qh)
                                           : (kQ6like<T> ? 2 * kTI * kLd : kTI * kLd);
     static constexpr int W_OFF = 0;
     static constexpr int QH_OFF = kTI * kLd4;                                     // Q5_K qh [128][32]
     static constexpr int WS_OFF = W_OFF + W_BYTES;                               // float [8][128]
     static constexpr int WM_OFF = WS_OFF + 8 * kTI * 4;                          // Q4_K: bf16 pieces of -dmin*m,
-    static constexpr int A_OFF = WM_OFF + (kK45<T> ? kTI * 48 : 0);             // [128][half][piece][4]; int8 [J][kLd]
-    static constexpr int XS = J + 4;                                             // (d, s) row stride: the
-    static constexpr int X_OFF = A_OFF + J * kLd;                                // float2 [8][XS] (8 blocks of a
-    static constexpr int XB_OFF = X_OFF + 8 * XS * 8;                            // column land in 2-way banks)
-                                                                                 // then bf16 pieces of s [J][8] (Q4_K)
-    static constexpr int BYTES = XB_OFF + (kK45<T> ? 8 * J * 4 : 0);
+    static constexpr int W_PART = WM_OFF + (kK45<T> ? kTI * 48 : 0);            // [128][half][piece][4]
+    // activation part (offsets from an activation buffer), an image of the tiled layout's records
+    // (tiled_act.hpp): codes [J][kLd] (a column's 256 codes and 16 bytes of padding, so that the
+    // rows of a B-operand read fall in distinct banks); d [8][J] fp32; s parts [J][8] (K-quants
+    // with a min term)
+    static constexpr int A_OFF = 0;
+    static constexpr int X_OFF = A_OFF + J * kLd;
+    static constexpr int XB_OFF = X_OFF + 8 * J * 4;
+    static constexpr int A_PART = XB_OFF + (kK45<T> ? 8 * J * 4 : 0);
 };
 
-// Two LDS step buffers where they fit beside the occupancy the tile runs at: Q4_K 8-wave tiles
-// (one workgroup per CU either way, 2 x 68 KB).
+// Two LDS weight buffers where they fit beside the occupancy the tile runs at: K-quant 8-wave
+// tiles (one workgroup per CU either way).  The activation part is always double-buffered.
 template <int T, int J> constexpr bool kDoubleBuffer = kK45<T> && J == 128;
-template <int T, int J> constexpr int kSmemBytes = (kDoubleBuffer<T, J> ? 2 : 1) * Smem<T, J>::BYTES;
+template <int T, int J> constexpr int kSmemBytes = (kDoubleBuffer<T, J> ? 2 : 1) * Smem<T, J>::W_PART + 2 * Smem<T, J>::A_PART;
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 // ---------------------------------------------------------------------------------------------
-// Activation tile: J columns of the step's 8 q8_1 blocks, read from the tiled layout (launch.hpp).
-// Thread tid owns (column, block) pairs i = tid + NT*it: column i/8, block i%8; the 8 consecutive
-// threads of a column read its 256 code bytes and 8 (d, s) pairs with aligned loads.  acol always
-// names a valid activation row (tile columns past the end repeat a valid one and are never written
-// out), so the loads need no predicate; RAGGED (Q8_0 / Q4_0, K a multiple of 32 only): blocks past
-// K read as zero.
+// Activation tile: J columns of a step, copied from the tiled layout (tiled_act.hpp) into an
+// activation buffer with direct global-to-LDS loads -- no registers, no vector ALU work and no
+// LDS stores of the waves.  One wave instruction fills 64 consecutive LDS slots of 16 (or 4)
+// bytes, lane l slot l, from sources the lane picks: code slot q is part q % 17 of column q / 17
+// (parts 0-15 the column's 16-byte chunks, part 16 its padding, loaded with chunk 15 again); d
+// slot x is block x / J of column x % J; s-part slot q is half q % 2 of column q / 2.  Each lane
+// keeps the byte offsets of its slots' records (fixed for a tile: the step only moves the uniform
+// table bases).  colrow(c) names the activation row of tile column c, always a valid row (columns
+// past the end repeat one and are never written out).
 // ---------------------------------------------------------------------------------------------
-template <int J, bool RAGGED> struct ActFetch {
-    static constexpr int NT = Cfg<J>::NT, N = J * 8 / NT;
-    uint32_t ds[N];   // fp16 d | fp16 s << 16
-    u32x4 c0[N], c1[N];
-    __device__ __forceinline__ void fetch(const uint8_t *xq, int64_t nb32, int64_t kb, const int64_t (&acol)[N],
-                                          int64_t act_rows) {
-        const int tid = threadIdx.x;
+template <int T, int J> struct ActDirect {
+    static constexpr int NT = Cfg<J>::NT, NW = NT / 64;
+    static constexpr int NSLOT = J * 17;                      // code slots
+    static constexpr int NI = (NSLOT + 63) / 64;              // code instructions (the last one partial for J = 32)
+    static constexpr int NA = (NI + NW - 1) / NW;             // code instructions per wave, at most
+    static constexpr int NX = J * 8 / 64 / NW;                // d slots (4 B) per lane
+    static constexpr int NBW = kK45<T> ? J * 2 / 64 : 0;      // waves with one s-part instruction
+    static_assert(NX * 64 * NW == J * 8 && NBW <= NW && kLd == 272, "activation slots");
+    uint32_t ao[NA], xo[NX], bo;
+    template <class CR> __device__ __forceinline__ void init(const CR &colrow) {
+        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-        for (int it = 0; it < N; ++it) {
-            const int blk = (tid + NT * it) & 7;
-            const int64_t b = kb * 8 + blk;
-            if (RAGGED) {
-                ds[it] = 0u;
-                c0[it] = u32x4{0u, 0u, 0u, 0u};
-                c1[it] = c0[it];
-            }
-            if (!RAGGED || b < nb32) {
-                const int64_t slot = kb * act_rows + acol[it];
-                const uint8_t *src = xq + slot * 256 + 32 * blk;
-                c0[it] = *(const u32x4 *)src;
-                c1[it] = *(const u32x4 *)(src + 16);
-                ds[it] = ((const uint32_t *)(xq + ((nb32 + 7) / 8) * act_rows * 256))[slot * 8 + blk];
-            }
+        for (int m = 0; m < NA; ++m) {
+            const int q = 64 * (w + NW * m) + lane;
+            const int c = q / 17, part = q - 17 * c;
+            ao[m] = q < NSLOT ? (uint32_t)colrow(c) * 256u + 16u * (uint32_t)(part < 16 ? part : 15) : 0u;
+        }
+#pragma unroll
+        for (int m = 0; m < NX; ++m) {
+            const int x = 64 * (w + NW * m) + lane, blk = x / J, c = x - blk * J;
+            xo[m] = (uint32_t)colrow(c) * 32u + 4u * (uint32_t)blk;
+        }
+        bo = 0u;
+        if constexpr (NBW > 0) {
+            const int q = 64 * (w < NBW ? w : 0) + lane;
+            bo = (uint32_t)colrow(q >> 1) * 32u + 16u * (uint32_t)(q & 1);
         }
     }
-    template <int T>
-    __device__ __forceinline__ void store(uint8_t *sm) const {
-        const int tid = threadIdx.x;
-        int8_t *sA = (int8_t *)(sm + Smem<T, J>::A_OFF);
-        float2 *sX = (float2 *)(sm + Smem<T, J>::X_OFF);
+    // Step kb into the activation buffer at xsm (act_rows rows, nsteps steps in the layout).
+    __device__ __forceinline__ void issue(uint8_t *xsm, const uint8_t *xq, int64_t kb, int64_t act_rows,
+                                          int64_t nsteps) const {
+        using L = Smem<T, J>;
+        const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+        const int64_t cells = nsteps * act_rows, cell0 = kb * act_rows;
+        const uint8_t *codes = xq + cell0 * 256, *dtab = xq + cells * 256 + cell0 * 32;
 #pragma unroll
-        for (int it = 0; it < N; ++it) {
-            const int i = tid + NT * it;
-            const int col = i >> 3, blk = i & 7;
-            *(u32x4 *)(sA + col * kLd + 32 * blk) = c0[it];
-            *(u32x4 *)(sA + col * kLd + 32 * blk + 16) = c1[it];
-            sX[blk * Smem<T, J>::XS + col] = make_float2(h2f((uint16_t)(ds[it] & 0xFFFF)), h2f((uint16_t)(ds[it] >> 16)));
-            if constexpr (kK45<T>) {   // s = t1 + t2 exactly in bf16: the B operand of the min term
-                const float sf = h2f((uint16_t)(ds[it] >> 16));
-                const uint32_t t1 = bf16_bits(sf);
-                ((uint32_t *)(sm + Smem<T, J>::XB_OFF))[col * 8 + blk] = t1 | (bf16_bits(sf - bf16_val(t1)) << 16);
+        for (int m = 0; m < NA; ++m) {
+            const int j = w + NW * m;
+            if (j < NI && 64 * j + lane < NSLOT)   // wave-uniform but for the partial last instruction
+                __builtin_amdgcn_global_load_lds((const void *)(codes + ao[m]), (lds_void *)(xsm + L::A_OFF + 1024 * j),
+                                                 16, 0, 0);
+        }
+#pragma unroll
+        for (int m = 0; m < NX; ++m)
+            __builtin_amdgcn_global_load_lds((const void *)(dtab + xo[m]), (lds_void *)(xsm + L::X_OFF + 256 * (w + NW * m)),
+                                             4, 0, 0);
+        if constexpr (NBW > 0) {
+            if (w < NBW) {
+                const uint8_t *ptab = xq + cells * 288 + cell0 * 32;
+                __builtin_amdgcn_global_load_lds((const void *)(ptab + bo), (lds_void *)(xsm + L::XB_OFF + 1024 * w), 16, 0, 0);
             }
         }
     }
 };
+
+// The same tile through registers, for the Q4_K / Q5_K kernels: fetched ahead and stored by the
+// waves in one burst, where direct loads (landing while a step computes) measured slower.  Thread
+// tid owns (column, block) pairs i = tid + NT*it: column i/8, block i%8.
+template <int T, int J> struct ActRegs {
+    static constexpr int NT = Cfg<J>::NT, N = J * 8 / NT;
+    uint32_t po[N];       // byte offset of the pair's column record in each table (times 1, 8 or 32)
+    u32x4 c0[N], c1[N];   // the block's 32 codes
+    float d[N];
+    uint32_t sp[N];       // s parts
+    template <class CR> __device__ __forceinline__ void init(const CR &colrow) {
+#pragma unroll
+        for (int it = 0; it < N; ++it) po[it] = (uint32_t)colrow((threadIdx.x + NT * it) >> 3);
+    }
+    __device__ __forceinline__ void fetch(const uint8_t *xq, int64_t kb, int64_t act_rows, int64_t nsteps) {
+        const int64_t cells = nsteps * act_rows, cell0 = kb * act_rows;
+#pragma unroll
+        for (int it = 0; it < N; ++it) {
+            const int blk = (threadIdx.x + NT * it) & 7;
+            const uint8_t *src = xq + (cell0 + po[it]) * 256 + 32 * blk;
+            c0[it] = *(const u32x4 *)src;
+            c1[it] = *(const u32x4 *)(src + 16);
+            d[it] = ((const float *)(xq + cells * 256))[(cell0 + po[it]) * 8 + blk];
+            if constexpr (kK45<T>) sp[it] = ((const uint32_t *)(xq + cells * 288))[(cell0 + po[it]) * 8 + blk];
+        }
+    }
+    __device__ __forceinline__ void store(uint8_t *xsm) const {
+        using L = Smem<T, J>;
+#pragma unroll
+        for (int it = 0; it < N; ++it) {
+            const int i = threadIdx.x + NT * it, col = i >> 3, blk = i & 7;
+            uint8_t *cbase = xsm + L::A_OFF + col * kLd + 32 * blk;
+            *(u32x4 *)cbase = c0[it];
+            *(u32x4 *)(cbase + 16) = c1[it];
+            ((float *)(xsm + L::X_OFF))[blk * J + col] = d[it];
+            if constexpr (kK45<T>) ((uint32_t *)(xsm + L::XB_OFF))[col * 8 + blk] = sp[it];
+        }
+    }
+};
+
+// Waits until this wave's direct loads (and every earlier global load) have landed.
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // ---------------------------------------------------------------------------------------------
 // Weight rows of a tile.  Plain: tile row t is matrix row r0 + t.  GLU (gate/up fusion, the MMQ
@@ -653,16 +713,17 @@ constexpr float kBias = 12582912.0f;   // 1.5 * 2^23
 // the exact integer the production fold consumes (the seeded value minus the seed for Q4_K /
 // Q5_K, the scale-folded 128*D_hi + D_lo for Q6_K, D for Q8_0 / Q4_0).
 template <int T, int J, bool DBG>
-__device__ __forceinline__ void tile_step(const uint8_t *sm, f32x16 (&acc)[Cfg<J>::NCB], const i32x16 &cinit,
+__device__ __forceinline__ void tile_step(const uint8_t *wsm, const uint8_t *xsm, f32x16 (&acc)[Cfg<J>::NCB],
+                                          const i32x16 &cinit,
                                           int64_t kb, int64_t nb32, int32_t *dbg, int64_t rows, int64_t n, int64_t r0,
                                           int64_t c0) {
     using L = Smem<T, J>;
     constexpr int NCB = Cfg<J>::NCB, JW = Cfg<J>::JW;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int rw = wid & 3, cw = wid >> 2;
-    const int8_t *sA = (const int8_t *)(sm + L::A_OFF);
-    const float *sWs = (const float *)(sm + L::WS_OFF);
-    const float2 *sX = (const float2 *)(sm + L::X_OFF);
+    const int8_t *sA = (const int8_t *)(xsm + L::A_OFF);
+    const float *sWs = (const float *)(wsm + L::WS_OFF);
+    const float *sX = (const float *)(xsm + L::X_OFF);
     const int arow = 32 * rw + (lane & 31);
     const int h = lane >> 5, koff = 16 * h;
     const int colw = JW * cw + (lane & 31);   // + 32*cb
@@ -682,7 +743,7 @@ __device__ __forceinline__ void tile_step(const uint8_t *sm, f32x16 (&acc)[Cfg<J
     // columns); a single block from v_mfma_f32_32x32x2_f32 with the second K slot zero.
     auto scales = [&](int sb, float wsr, f32x16 (&S)[NCB]) {
         if constexpr (NCB == 2) {
-            const float da = sX[sb * L::XS + JW * cw + 32 * h + (lane & 31)].x;
+            const float da = sX[sb * J + JW * cw + 32 * h + (lane & 31)];
             const f32x32 S2 = __builtin_amdgcn_mfma_f32_32x32x1f32(wsr, da, f32x32{}, 0, 0, 0);
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
@@ -690,7 +751,7 @@ __device__ __forceinline__ void tile_step(const uint8_t *sm, f32x16 (&acc)[Cfg<J
                 S[1][e] = S2[16 + e];
             }
         } else {
-            const float da = h ? 0.f : sX[sb * L::XS + colw].x;
+            const float da = h ? 0.f : sX[sb * J + colw];
             S[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(h ? 0.f : wsr, da, fzero, 0, 0, 0);
         }
     };
@@ -713,12 +774,45 @@ __device__ __forceinline__ void tile_step(const uint8_t *sm, f32x16 (&acc)[Cfg<J
         }
     };
 
+    // Seeded tiles: per 32-value block, t = D * d_a by one multiply-add on the seeded value
+    // ((1.5 * 2^23 + D) * d_a - 1.5 * 2^23 * d_a, the second product exact: d_a has 11 significant
+    // bits), then acc += t * w[row] -- the lane's 16 row scales are read from LDS and its column's
+    // d_a is one scalar, so no scale-product MFMA is needed.
+    auto seeded_fold = [&](int sb, const u32x4 &aop) __attribute__((always_inline)) {
+        f32x4 wr[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) wr[q] = *(const f32x4 *)(sWs + sb * kTI + 32 * rw + 8 * q + 4 * h);
+        auto fold = [&](int cb, const i32x16 &D) __attribute__((always_inline)) {
+            const float da = sX[sb * J + colw + 32 * cb];
+            const float nb = -kBias * da;
+            const f32x16 Df = __builtin_bit_cast(f32x16, D);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[cb][e] = fmaf(fmaf(Df[e], da, nb), wr[e >> 2][e & 3], acc[cb][e]);
+        };
+        auto bop = [&](int cb) __attribute__((always_inline)) {
+            return *(const u32x4 *)(sA + (colw + 32 * cb) * kLd + 32 * sb + koff);
+        };
+        if constexpr (T != kQ5_K && J == 128) {
+            // every column block's MFMA is issued before the first fold, so the matrix pipe works
+            // while the vector ALU folds (8-wave tiles; Q5_K's fifth bits and the 4-wave tiles'
+            // other state leave no registers for it)
+            i32x16 Ds[NCB];
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) Ds[cb] = mfma32x32x32(aop, bop(cb), cinit);
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) fold(cb, Ds[cb]);
+        } else {
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) fold(cb, mfma32x32x32(aop, bop(cb), cinit));
+        }
+    };
+
     if constexpr (kK45<T>) {
-        const uint8_t *sW = sm + L::W_OFF;
+        const uint8_t *sW = wsm + L::W_OFF;
         // Q5_K: qh bytes 16h..16h+15 of the lane's row; bit sb of byte l is the fifth bit of value
         // l of sub-block sb
         u32x4 qh = {0u, 0u, 0u, 0u};
-        if constexpr (T == kQ5_K) qh = *(const u32x4 *)(sm + L::QH_OFF + arow * 32 + koff);
+        if constexpr (T == kQ5_K) qh = *(const u32x4 *)(wsm + L::QH_OFF + arow * 32 + koff);
 #pragma unroll 2
         for (int sb = 0; sb < 8; ++sb) {
             // qs bytes 32*(sb/2)+16h .. +15: low nibbles = values 16h.. of the even sub-block of
@@ -733,26 +827,33 @@ __device__ __forceinline__ void tile_step(const uint8_t *sm, f32x16 (&acc)[Cfg<J
                 aop.z |= ((qh.z >> sb) & 0x01010101u) << 4;
                 aop.w |= ((qh.w >> sb) & 0x01010101u) << 4;
             }
-            f32x16 S[NCB];
-            if constexpr (!DBG) scales(sb, sWs[sb * kTI + arow], S);
+            if constexpr (!DBG) {
+                seeded_fold(sb, aop);
+            } else {
+                f32x16 S[NCB];
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) {
-                const u32x4 b = *(const u32x4 *)(sA + (colw + 32 * cb) * kLd + 32 * sb + koff);
-                fix(cb, sb, mfma32x32x32(aop, b, cinit), S[cb]);
+                for (int cb = 0; cb < NCB; ++cb) {
+                    const u32x4 b = *(const u32x4 *)(sA + (colw + 32 * cb) * kLd + 32 * sb + koff);
+                    fix(cb, sb, mfma32x32x32(aop, b, cinit), S[cb]);
+                }
             }
         }
     } else if constexpr (kB32<T>) {
-        const int8_t *sW = (const int8_t *)(sm + L::W_OFF);
+        const int8_t *sW = (const int8_t *)(wsm + L::W_OFF);
 #pragma unroll 2
         for (int j = 0; j < 8; ++j) {
             if (kb * 8 + j >= nb32) break;   // ragged last step (workgroup-uniform)
             const u32x4 a = *(const u32x4 *)(sW + arow * kLd + 32 * j + koff);
-            f32x16 S[NCB];
-            if constexpr (!DBG) scales(j, sWs[j * kTI + arow], S);
+            if constexpr (!DBG && kSeeded<T, J>) {
+                seeded_fold(j, a);
+            } else {
+                f32x16 S[NCB];
+                if constexpr (!DBG) scales(j, sWs[j * kTI + arow], S);
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) {
-                const u32x4 b = *(const u32x4 *)(sA + (colw + 32 * cb) * kLd + 32 * j + koff);
-                fix(cb, j, mfma32x32x32(a, b, cinit), S[cb]);
+                for (int cb = 0; cb < NCB; ++cb) {
+                    const u32x4 b = *(const u32x4 *)(sA + (colw + 32 * cb) * kLd + 32 * j + koff);
+                    fix(cb, j, mfma32x32x32(a, b, cinit), S[cb]);
+                }
             }
         }
     } else {
@@ -760,7 +861,7 @@ __device__ __forceinline__ void tile_step(const uint8_t *sm, f32x16 (&acc)[Cfg<J
         // element of a lane is in the lane's column, so the per-element scale factors as
         // d[row] * d_a[col]: T += D * d_a with d_a a per-lane scalar, then acc += d[row] * T once
         // per step (no scale-product MFMAs).
-        const int8_t *sW = (const int8_t *)(sm + L::W_OFF);
+        const int8_t *sW = (const int8_t *)(wsm + L::W_OFF);
         f32x16 Tc[NCB];
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) Tc[cb] = fzero;
@@ -771,7 +872,7 @@ __device__ __forceinline__ void tile_step(const uint8_t *sm, f32x16 (&acc)[Cfg<J
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb) {
                 const u32x4 b = *(const u32x4 *)(sA + (colw + 32 * cb) * kLd + 32 * j + koff);
-                const float da = sX[j * L::XS + colw + 32 * cb].x;
+                const float da = sX[j * J + colw + 32 * cb];
                 const i32x16 D = mfma32x32x32(a, b, zero);
                 const i32x16 Dh = mfma32x32x32(a_hi, b, zero);
 #pragma unroll
@@ -802,15 +903,15 @@ __device__ __forceinline__ void tile_step(const uint8_t *sm, f32x16 (&acc)[Cfg<J
 // and three K = 16 MFMAs per column block sum them -- MFMA m, lane (row, h), slots 2q and 2q+1
 // hold p_m of sub-block 4h+q against t1 and t2 of the same sub-block.
 template <int T, int J>
-__device__ __forceinline__ void q4k_min_term(const uint8_t *sm, f32x16 (&acc)[Cfg<J>::NCB]) {
+__device__ __forceinline__ void q4k_min_term(const uint8_t *wsm, const uint8_t *xsm, f32x16 (&acc)[Cfg<J>::NCB]) {
     using L = Smem<T, J>;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int rw = wid & 3, cw = wid >> 2, h = lane >> 5;
     const int arow = 32 * rw + (lane & 31), colw = Cfg<J>::JW * cw + (lane & 31);
-    const uint8_t *wp = sm + L::WM_OFF + arow * 48 + 24 * h;
+    const uint8_t *wp = wsm + L::WM_OFF + arow * 48 + 24 * h;
     u32x4 bs[Cfg<J>::NCB];
 #pragma unroll
-    for (int cb = 0; cb < Cfg<J>::NCB; ++cb) bs[cb] = *(const u32x4 *)(sm + L::XB_OFF + (colw + 32 * cb) * 32 + 16 * h);
+    for (int cb = 0; cb < Cfg<J>::NCB; ++cb) bs[cb] = *(const u32x4 *)(xsm + L::XB_OFF + (colw + 32 * cb) * 32 + 16 * h);
 #pragma unroll
     for (int m = 0; m < 3; ++m) {
         const u32x2 p = *(const u32x2 *)(wp + 8 * m);
@@ -824,12 +925,19 @@ __device__ __forceinline__ void q4k_min_term(const uint8_t *sm, f32x16 (&acc)[Cf
 }
 
 // One tile's steps [kb0, kb1), software-pipelined: the loads of a later step are in flight while
-// a step computes.
-template <int T, int J, bool DBG, class WR>
+// a step computes.  Two weight buffers (kDoubleBuffer): weights and activations are fetched into
+// registers two steps ahead and step kb+1 is parked while step kb computes, so a step needs one
+// barrier (it publishes the parked step and retires the buffers computed before).  One weight
+// buffer: step kb's weights (fetched a step ahead) are parked between two barriers; the
+// activations of Q6_K, Q3_K and the 32-value types, double-buffered, come by direct loads issued
+// before step kb computes and awaited (each wave its own, then the first barrier) before step
+// kb+1, those of Q4_K / Q5_K through registers like the weights (measured faster for them).  A
+// barrier waits for every load the wave has in flight, so no load is issued just before one.
+template <int T, int J, bool DBG, class WR, class CR>
 __device__ __forceinline__ void run_tile(uint8_t *sm, f32x16 (&acc)[Cfg<J>::NCB], const WR &wr, int64_t kb0,
-                                         int64_t kb1, int64_t nb32, const uint8_t *xq,
-                                         const int64_t (&acol)[J * 8 / Cfg<J>::NT], int32_t *dbg, int64_t n,
-                                         int64_t c0, int64_t act_rows) {
+                                         int64_t kb1, int64_t nb32, const uint8_t *xq, const CR &colrow,
+                                         int32_t *dbg, int64_t n, int64_t c0, int64_t act_rows) {
+    using L = Smem<T, J>;
     constexpr bool DB = kDoubleBuffer<T, J>;
     i32x16 cinit = {};
     if constexpr (kSeeded<T, J>) {
@@ -837,53 +945,76 @@ __device__ __forceinline__ void run_tile(uint8_t *sm, f32x16 (&acc)[Cfg<J>::NCB]
         for (int e = 0; e < 16; ++e) cinit[e] = kBiasBits;
         asm volatile("" : "+v"(cinit));
     }
+    const int64_t nsteps = (nb32 + 7) / 8;
+    uint8_t *const wb0 = sm, *const wb1 = sm + (DB ? L::W_PART : 0);
+    uint8_t *const xb0 = sm + (DB ? 2 : 1) * L::W_PART, *const xb1 = xb0 + L::A_PART;
     WFetch<T, Cfg<J>::NT> wf;
-    ActFetch<J, kRaggedK<T>> af;
-    wf.fetch(wr, kb0, nb32);
-    af.fetch(xq, nb32, kb0, acol, act_rows);
-    uint8_t *const buf0 = sm, *const buf1 = sm + (DB ? Smem<T, J>::BYTES : 0);
-    // Publishes step kb in LDS and returns its buffer.  Two buffers: step kb computes from one
-    // while step kb+1 is parked in the other, so a step needs one barrier (it publishes the parked
-    // step and retires the buffer computed before) and the fetch of step kb+2 flies during step
-    // kb.  One buffer: step kb is parked between two barriers, then step kb+1 is fetched.
-    auto enter = [&](int64_t kb) -> const uint8_t * {
-        if constexpr (DB) {
-            uint8_t *cur = ((kb - kb0) & 1) ? buf1 : buf0, *nxt = ((kb - kb0) & 1) ? buf0 : buf1;
-            __syncthreads();
+    if constexpr (DB) {
+        ActRegs<T, J> ar;
+        ar.init(colrow);
+        wf.fetch(wr, kb0, nb32);
+        ar.fetch(xq, kb0, act_rows, nsteps);
+        __syncthreads();   // the previous tile's reads of every buffer are done
+        wf.template store<J>(wb0, wr, kb0, nb32);
+        ar.store(xb0);
+        if (kb0 + 1 < kb1) {
+            wf.fetch(wr, kb0 + 1, nb32);
+            ar.fetch(xq, kb0 + 1, act_rows, nsteps);
+        }
+        for (int64_t kb = kb0; kb < kb1; ++kb) {
+            const bool odd = (kb - kb0) & 1;
+            __syncthreads();   // publishes step kb; step kb-1 is retired
             if (kb + 1 < kb1) {
-                wf.template store<J>(nxt, wr, kb + 1, nb32);
-                af.template store<T>(nxt);
+                wf.template store<J>(odd ? wb0 : wb1, wr, kb + 1, nb32);
+                ar.store(odd ? xb0 : xb1);
                 if (kb + 2 < kb1) {
                     wf.fetch(wr, kb + 2, nb32);
-                    af.fetch(xq, nb32, kb + 2, acol, act_rows);
+                    ar.fetch(xq, kb + 2, act_rows, nsteps);
                 }
             }
-            return cur;
-        } else {
-            __syncthreads();   // the previous step's LDS reads are done
-            wf.template store<J>(sm, wr, kb, nb32);
-            af.template store<T>(sm);
+            const uint8_t *wcur = odd ? wb1 : wb0, *xcur = odd ? xb1 : xb0;
+            if constexpr (kK45<T> && !DBG) q4k_min_term<T, J>(wcur, xcur, acc);   // acc only
+            tile_step<T, J, DBG>(wcur, xcur, acc, cinit, kb, nb32, dbg, wr.rows, n, wr.r0, c0);
+        }
+    } else if constexpr (kK45<T>) {
+        // one weight buffer, activations through registers: step kb parked between two barriers
+        ActRegs<T, J> ar;
+        ar.init(colrow);
+        wf.fetch(wr, kb0, nb32);
+        ar.fetch(xq, kb0, act_rows, nsteps);
+        for (int64_t kb = kb0; kb < kb1; ++kb) {
+            __syncthreads();   // the previous step's (or tile's) LDS reads are done
+            wf.template store<J>(wb0, wr, kb, nb32);
+            ar.store(xb0);
             __syncthreads();
             if (kb + 1 < kb1) {
                 wf.fetch(wr, kb + 1, nb32);
-                af.fetch(xq, nb32, kb + 1, acol, act_rows);
+                ar.fetch(xq, kb + 1, act_rows, nsteps);
             }
-            return sm;
+            if constexpr (!DBG) q4k_min_term<T, J>(wb0, xb0, acc);   // acc only
+            tile_step<T, J, DBG>(wb0, xb0, acc, cinit, kb, nb32, dbg, wr.rows, n, wr.r0, c0);
         }
-    };
-    if constexpr (DB) {
-        __syncthreads();   // the previous tile's reads of both buffers are done
-        wf.template store<J>(buf0, wr, kb0, nb32);
-        af.template store<T>(buf0);
-        if (kb0 + 1 < kb1) {
-            wf.fetch(wr, kb0 + 1, nb32);
-            af.fetch(xq, nb32, kb0 + 1, acol, act_rows);
+    } else {
+        ActDirect<T, J> ad;
+        ad.init(colrow);
+        __syncthreads();   // the previous tile's reads of every buffer are done
+        ad.issue(xb0, xq, kb0, act_rows, nsteps);
+        wf.fetch(wr, kb0, nb32);
+        for (int64_t kb = kb0; kb < kb1; ++kb) {
+            const bool odd = (kb - kb0) & 1;
+            uint8_t *const xcur = odd ? xb1 : xb0, *const xnxt = odd ? xb0 : xb1;
+            wait_loads();      // this wave's direct loads of step kb (and the weights fetched since) landed
+            __syncthreads();   // ... every wave's: step kb's activations are in LDS; step kb-1 is retired
+            wf.template store<J>(wb0, wr, kb, nb32);
+            __syncthreads();   // step kb's weights are parked (a barrier waits for every load in flight,
+                               // so the next step's loads are issued after it)
+            if (kb + 1 < kb1) {
+                ad.issue(xnxt, xq, kb + 1, act_rows, nsteps);
+                wf.fetch(wr, kb + 1, nb32);
+            }
+            if constexpr (kK45<T> && !DBG) q4k_min_term<T, J>(wb0, xcur, acc);   // acc only
+            tile_step<T, J, DBG>(wb0, xcur, acc, cinit, kb, nb32, dbg, wr.rows, n, wr.r0, c0);
         }
-    }
-    for (int64_t kb = kb0; kb < kb1; ++kb) {
-        const uint8_t *cur = enter(kb);
-        if constexpr (kK45<T> && !DBG) q4k_min_term<T, J>(cur, acc);   // acc only
-        tile_step<T, J, DBG>(cur, acc, cinit, kb, nb32, dbg, wr.rows, n, wr.r0, c0);
     }
 }
 
@@ -940,7 +1071,6 @@ __global__ __launch_bounds__(Cfg<J>::NT, 2) void mmq_kernel(const uint8_t *__res
                                                          float *__restrict__ y, int32_t *__restrict__ dbg,
                                                          MmqArgs args) {
     extern __shared__ __align__(16) uint8_t sm[];
-    constexpr int NA = J * 8 / Cfg<J>::NT, NT = Cfg<J>::NT;
     const int64_t nb32 = k / 32;
     const int64_t row_bytes = (k / Fmt<T>::QK) * Fmt<T>::BYTES;
     const int64_t u = xcd_remap(blockIdx.x, args.units);
@@ -948,7 +1078,6 @@ __global__ __launch_bounds__(Cfg<J>::NT, 2) void mmq_kernel(const uint8_t *__res
     int64_t pos = (u * W) / args.units;
     const int64_t end = ((u + 1) * W) / args.units;
     const int64_t first = pos;
-    const int tid = threadIdx.x;
 
     while (pos < end) {
         const int64_t t = pos / args.k_iters;
@@ -958,22 +1087,18 @@ __global__ __launch_bounds__(Cfg<J>::NT, 2) void mmq_kernel(const uint8_t *__res
         tile_coords(t, args.ntiles, args.n_ct, rt, ct);
         const int64_t r0 = rt * kTI, c0 = ct * J;
 
-        int64_t acol[NA];
-#pragma unroll
-        for (int it = 0; it < NA; ++it) {
-            const int64_t c = c0 + ((tid + NT * it) >> 3);
-            acol[it] = c < n ? c : n - 1;   // columns past the end repeat the last (not written)
-        }
+        // columns past the end repeat the last (never written out)
+        auto colrow = [&](int c) -> int64_t { return c0 + c < n ? c0 + c : n - 1; };
         f32x16 acc[Cfg<J>::NCB];
 #pragma unroll
         for (int cb = 0; cb < Cfg<J>::NCB; ++cb) acc[cb] = f32x16{};
 
         if constexpr (PK) {
             const WPanels wr{w, args.k_iters * 16 * (kSuper / Fmt<T>::QK * Fmt<T>::BYTES), r0, rows};
-            run_tile<T, J, DBG>(sm, acc, wr, kb0, kb1, nb32, xq, acol, dbg, n, c0, n);
+            run_tile<T, J, DBG>(sm, acc, wr, kb0, kb1, nb32, xq, colrow, dbg, n, c0, n);
         } else {
             const WRows<false> wr{w, w, row_bytes, r0, rows};
-            run_tile<T, J, DBG>(sm, acc, wr, kb0, kb1, nb32, xq, acol, dbg, n, c0, n);
+            run_tile<T, J, DBG>(sm, acc, wr, kb0, kb1, nb32, xq, colrow, dbg, n, c0, n);
         }
 
         if (!DBG) {
@@ -997,24 +1122,18 @@ __global__ __launch_bounds__(Cfg<J>::NT, 2) void mmq_glu_kernel(const uint8_t *_
                                                              const uint8_t *__restrict__ xq, int64_t n,
                                                              float *__restrict__ y, int64_t ntiles, int64_t n_ct) {
     extern __shared__ __align__(16) uint8_t sm[];
-    constexpr int NA = J * 8 / Cfg<J>::NT, NT = Cfg<J>::NT;
     const int64_t nb32 = k / 32;
     const int64_t row_bytes = (k / Fmt<T>::QK) * Fmt<T>::BYTES;
     const int64_t t = xcd_remap(blockIdx.x, ntiles);
     int64_t rt, ct;
     tile_coords(t, ntiles, n_ct, rt, ct);
     const int64_t r0 = rt * (kTI / 2), c0 = ct * J;
-    int64_t acol[NA];
-#pragma unroll
-    for (int it = 0; it < NA; ++it) {
-        const int64_t c = c0 + ((threadIdx.x + NT * it) >> 3);
-        acol[it] = c < n ? c : n - 1;
-    }
+    auto colrow = [&](int c) -> int64_t { return c0 + c < n ? c0 + c : n - 1; };
     f32x16 acc[Cfg<J>::NCB];
 #pragma unroll
     for (int cb = 0; cb < Cfg<J>::NCB; ++cb) acc[cb] = f32x16{};
     const WRows<true> wr{wg, wu, row_bytes, r0, rows};
-    run_tile<T, J, false>(sm, acc, wr, 0, (k + kSuper - 1) / kSuper, nb32, xq, acol, nullptr, n, c0, n);
+    run_tile<T, J, false>(sm, acc, wr, 0, (k + kSuper - 1) / kSuper, nb32, xq, colrow, nullptr, n, c0, n);
     store_tile_glu<J>(acc, y + c0 * rows + r0, rows, rows - r0, n - c0);
 }
 
@@ -1096,7 +1215,6 @@ __global__ __launch_bounds__(Cfg<J>::NT, 2) void mmq_id_kernel(const uint8_t *__
                                                             const uint8_t *__restrict__ xq, float *__restrict__ y,
                                                             ColMap cm, int32_t n_exp) {
     extern __shared__ __align__(16) uint8_t sm[];
-    constexpr int NA = J * 8 / Cfg<J>::NT, NT = Cfg<J>::NT;
     // The grid is sized for the most column tiles the call can have; the valid ones are
     // tile_start[n_exp] (device).  Valid (row tile, column tile) pairs are numbered in the dense
     // kernel's banded order and dealt out in contiguous ranges per XCD (hardware workgroup b runs
@@ -1130,12 +1248,8 @@ __global__ __launch_bounds__(Cfg<J>::NT, 2) void mmq_id_kernel(const uint8_t *__
         const int64_t t = pr / cm.top_k, s = pr - t * cm.top_k;
         return t * cm.x_per_tok + (cm.x_per_tok > 1 ? s : 0);
     };
-    int64_t acol[NA];
-#pragma unroll
-    for (int it = 0; it < NA; ++it) {
-        const int64_t c = c0 + ((tid + NT * it) >> 3);
-        acol[it] = arow_of(c < cnt ? c : cnt - 1);   // past the end: the last column (not written)
-    }
+    // past the end: the last column (never written out)
+    auto colrow = [&](int c) -> int64_t { return arow_of(c0 + c < cnt ? c0 + c : cnt - 1); };
     f32x16 acc[Cfg<J>::NCB];
 #pragma unroll
     for (int cb = 0; cb < Cfg<J>::NCB; ++cb) acc[cb] = f32x16{};
@@ -1143,7 +1257,7 @@ __global__ __launch_bounds__(Cfg<J>::NT, 2) void mmq_id_kernel(const uint8_t *__
     const int64_t k_iters = (k + kSuper - 1) / kSuper;
     const WRows<GLU> wr{w + (int64_t)e * cm.w_expert_stride, GLU ? w2 + (int64_t)e * cm.w_expert_stride : nullptr,
                         row_bytes, r0, rows};
-    run_tile<T, J, false>(sm, acc, wr, 0, k_iters, nb32, xq, acol, nullptr, cnt, c0, cm.act_rows);
+    run_tile<T, J, false>(sm, acc, wr, 0, k_iters, nb32, xq, colrow, nullptr, cnt, c0, cm.act_rows);
     const int rw = wid & 3, cw = wid >> 2;
 #pragma unroll
     for (int cb = 0; cb < Cfg<J>::NCB; ++cb) {

@@ -26,6 +26,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "q8_1.hpp"
+#include "tiled_act.hpp"
 
 namespace qmm {
 
@@ -448,9 +449,7 @@ __global__ __launch_bounds__(64 * kWaveGroupWaves) void moe_prologue_kernel(
         const int64_t row = blk / nb, bi = blk - row * nb;
         const float *src = x + row * k + bi * 32 + 8 * sub;
         const Q81Lane4 q = quantize_q8_1_lane4(*(const float4 *)src, *(const float4 *)(src + 4));
-        const int64_t slot = (bi >> 3) * n_rows + row;   // (step, row)
-        *(u32x2 *)(tiled + slot * 256 + 32 * (bi & 7) + 8 * sub) = u32x2{q.c0, q.c1};
-        if (sub == 0) ((uint32_t *)(tiled + (size_t)((nb + 7) / 8) * n_rows * 256))[slot * 8 + (bi & 7)] = q.ds;
+        tiled_act_put(tiled, (nb + 7) / 8, n_rows, row, bi, sub, q.c0, q.c1, q.ds);
         uint8_t *yb = canon + blk * kQ8_1Bytes;
         *(u32x2_a4 *)(yb + 4 + 8 * sub) = u32x2{q.c0, q.c1};
         if (sub == 0) *(uint32_t *)yb = q.ds;

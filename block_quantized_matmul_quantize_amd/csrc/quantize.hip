@@ -4,6 +4,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "q8_1.hpp"
+#include "tiled_act.hpp"
 
 namespace qmm {
 
@@ -29,8 +30,8 @@ __global__ __launch_bounds__(256) void quantize_q8_1_kernel(const float *__restr
     if (sub == 0) *(uint32_t *)yb = q.ds;
 }
 
-// Same quantization, written in the tiled kernel's layout (codes of a 256-value step contiguous
-// per row, the fp16 (d, s) pairs in a table after all codes), optionally also as canonical blocks.
+// Same quantization, written in the tiled kernel's layout (tiled_act.hpp), optionally also as
+// canonical blocks.
 __global__ __launch_bounds__(256) void quantize_q8_1_tiled_kernel(const float *__restrict__ x, int64_t n_rows,
                                                                   int64_t k, uint8_t *__restrict__ tiled,
                                                                   uint8_t *__restrict__ canon) {
@@ -51,9 +52,7 @@ __global__ __launch_bounds__(256) void quantize_q8_1_tiled_kernel(const float *_
     }
     const Q81Lane4 q = quantize_q8_1_lane4(a, b);
     if (!live) return;
-    const int64_t slot = (bi >> 3) * n_rows + row;   // (step, row)
-    *(u32x2 *)(tiled + slot * 256 + 32 * (bi & 7) + 8 * sub) = u32x2{q.c0, q.c1};
-    if (sub == 0) ((uint32_t *)(tiled + (size_t)((nb + 7) / 8) * n_rows * 256))[slot * 8 + (bi & 7)] = q.ds;
+    tiled_act_put(tiled, (nb + 7) / 8, n_rows, row, bi, sub, q.c0, q.c1, q.ds);
     if (canon) {
         uint8_t *yb = canon + blk * kQ8_1Bytes;
         *(u32x2_a4 *)(yb + 4 + 8 * sub) = u32x2{q.c0, q.c1};
@@ -71,9 +70,8 @@ __global__ __launch_bounds__(256) void relayout_q8_1_tiled_kernel(const uint8_t 
     if (blk >= n_rows * nb) return;
     const int64_t row = blk / nb, bi = blk - row * nb;
     const uint8_t *src = xq + blk * kQ8_1Bytes;
-    const int64_t slot = (bi >> 3) * n_rows + row;
-    *(u32x2 *)(tiled + slot * 256 + 32 * (bi & 7) + 8 * sub) = *(const u32x2_a4 *)(src + 4 + 8 * sub);
-    if (sub == 0) ((uint32_t *)(tiled + (size_t)((nb + 7) / 8) * n_rows * 256))[slot * 8 + (bi & 7)] = *(const uint32_t *)src;
+    const u32x2 c = *(const u32x2_a4 *)(src + 4 + 8 * sub);
+    tiled_act_put(tiled, (nb + 7) / 8, n_rows, row, bi, sub, c.x, c.y, *(const uint32_t *)src);
 }
 
 // Plain fill kernel (used instead of a memset so that the call sequence stays capturable).
