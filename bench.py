@@ -502,8 +502,9 @@ def summarize_pmc(fdir, wdir, write=False):
 
     def by_grid(d):
         out = {}
-        for name, value, grid in _rocpd(d).execute("select kernel_name, value, grid_size from counters_collection"):
-            out.setdefault((_short(name), grid), []).append(value)
+        for name, value, grid, wg in _rocpd(d).execute(
+                "select kernel_name, value, grid_size, workgroup_size from counters_collection"):
+            out.setdefault((_short(name), grid, wg), []).append(value)
         return out
 
     F, Wr = load(fdir), load(wdir)
@@ -522,18 +523,19 @@ def summarize_pmc(fdir, wdir, write=False):
         print(f"| `{k}` | {len(F[k])} | {f:.1f} | {w:.1f} | {b / 1e6:.3f} MB |")
     FG, WG = by_grid(fdir), by_grid(wdir)
     # The step's launches: the headline types (8, 12, 14) in the forms the step takes (fp32 input,
-    # no fusion, original layout) at its 4096 rows (16 rows per 1024-thread workgroup); not the
-    # extra types, the fp16-activation mode, the panel layout or the 8192-row comparison.
+    # no fusion, original layout) at its 4096 rows, i.e. 256 workgroups of 16 rows (dot4 picks its
+    # workgroup size per launch, so the workgroup count, not the grid, identifies the shape); not
+    # the extra types, the fp16-activation mode, the panel layout or the larger-row comparisons.
     step_kernel = re.compile(r"^qmm::mmvq_(stream_kernel<(8|12|14), false, false, true, false, false>"
                              r"|dot4_kernel<(8|12|14), \d, false, false, true, false>)$")
     # Each case of a type runs the same number of launches, so a kernel's share of its type's
     # dispatches counts the cases it served; the figure is the mean over the step's cases, as the
     # algorithmic bytes per launch are.
     groups = {}
-    for (k, grid), fv in FG.items():
+    for (k, grid, wg), fv in FG.items():
         m = step_kernel.match(k)
-        if m and grid == (STEP_ROWS // 16) * 1024:
-            b = statistics.mean(fv) * 1024 * fs + statistics.mean(WG.get((k, grid), [0.0])) * 1024 * ws
+        if m and wg and grid // wg == STEP_ROWS // 16:
+            b = statistics.mean(fv) * 1024 * fs + statistics.mean(WG.get((k, grid, wg), [0.0])) * 1024 * ws
             groups[k] = (int(m.group(2) or m.group(3)), len(fv), b)
     import synth
     ncases = {t: sum(c["qtype"] == t for c in synth.MMVQ_CASES) for t in {c["qtype"] for c in synth.MMVQ_CASES}}

@@ -677,17 +677,23 @@ static hipError_t launch_mmvq_t(const uint8_t *w, int64_t rows, int64_t k, const
 }
 
 // Largest column count the automatic choice sends to the dot4 kernel, per type and weight rows:
-// one column from 8192 rows on, none below.  Measured with the weights rotated over > 512 MB
-// (graph-replayed calls, fp32 input, Q4_K, one column): at 4096 x 4096 the LDS-staged kernel takes
-// 5.2 us and dot4 5.7; at 14336 x 4096 dot4 takes 11.8 us and the LDS-staged kernel 15.3, at
-// 57344 x 4096 34 and 53 (its 16-row workgroups each quantize all of x and run one step per wave,
-// while dot4's waves stream many rows).  At two or three columns dot4 is 0.8-1.4 us slower.
+// up to three columns from 8192 rows on (Q8_0: one column from 8192 rows, three from 12288), none
+// below.  Measured with the weights rotated over > 512 MB (graph-replayed calls, fp32 input, K =
+// 4096, the LDS-staged kernel against dot4 at 1 / 2 / 3 columns): Q4_K 4096 rows 5.1 / 5.3 / 6.1
+// against 5.3 / 6.1 / 6.8 us, 8192 rows 8.7 / 9.0 / 10.4 against 6.7 / 8.6 / 9.7, 14336 rows
+// 15.3 / 15.8 / 18.8 against 9.8 / 12.1 / 14.5 (the LDS-staged kernel's 16-row workgroups each
+// quantize all of x and run one step per wave, while dot4's 4-8-wave workgroups share a compute
+// unit and stream several steps per wave); Q5_K and Q4_0 alike; Q8_0 8192 rows 10.7 / 10.9 /
+// 11.8 against 9.3 / 11.7 / 12.9, 14336 rows 18.9 / 19.3 / 20.8 against 14.9 / 17.3 / 18.3.
 // Q3_K and IQ4_XS, which the LDS-staged kernel does not serve, take dot4 up to three columns at
 // any row count: their alternative is a separate quantize launch and the register-streamed kernel.
 constexpr int64_t kDot4MinRows = 8192;
+constexpr int64_t kDot4Q8MultiRows = 12288;
 static int dot4_auto_cols(int type, int64_t rows) {
     if (type == kQ3_K || type == kIQ4_XS) return 3;
-    return rows >= kDot4MinRows && (type == kQ4_K || type == kQ5_K || type == kQ8_0 || type == kQ4_0) ? 1 : 0;
+    if (rows < kDot4MinRows) return 0;
+    if (type == kQ8_0) return rows >= kDot4Q8MultiRows ? 3 : 1;
+    return type == kQ4_K || type == kQ5_K || type == kQ4_0 ? 3 : 0;
 }
 
 // Which fused kernel serves an fp32-input call: 3 dot4, 2 LDS-staged MFMA, 0 none.  Override

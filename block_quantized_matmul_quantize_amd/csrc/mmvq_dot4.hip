@@ -4,7 +4,8 @@
 //
 // With one to three columns a block-diagonal MFMA would spend most of its per-result fp32 fixups
 // on empty columns, so this kernel works on the vector ALU and does exactly the useful work.
-// A workgroup owns 16 weight rows; wave w takes the 256-value steps w, w+W, ... (up to 16 waves).
+// A workgroup owns 16 weight rows; wave w takes the 256-value steps w, w+W, ... (W = 4, 8 or 16
+// waves, chosen at launch).
 // Lane 4r+g holds row r and the quarter g of the step: values 64g..64g+63, i.e. the two 32-value
 // sub-blocks 2g and 2g+1 -- for Q4_K the 32 qs bytes 32g..32g+31 (low nibbles sub-block 2g, high
 // nibbles 2g+1; Q5_K: the same qs bytes 32 further on, plus all 32 qh bytes, whose bits 2g and
@@ -442,7 +443,16 @@ template <int T, int NC, bool DBG, bool EXPERT, bool F32 = false, bool GLU = fal
 hipError_t launch_nc(const uint8_t *w, int64_t rows, int64_t k, const void *xq, int64_t n, float *y, int32_t *dbg,
                      const ColMap &cm, int64_t n_exp, hipStream_t s, const uint8_t *w2 = nullptr) {
     const int64_t nsteps = k / kSuper;
-    const int nw = (int)(nsteps < 16 ? nsteps : 16);
+    constexpr int RW = GLU ? kRows / 2 : kRows;   // outputs per workgroup
+    const int64_t wgs = (rows + RW - 1) / RW * (EXPERT ? n_exp : 1);
+    // Waves per workgroup (each takes steps w, w+W, ... with the next step's weights in flight):
+    // 8 by default, 4 for two or three columns once there are two workgroups per compute unit,
+    // 16 for one-column Q8_0 (its 4-byte pieces want the most loads in flight per workgroup).
+    // Fewer waves per workgroup let more workgroups share a compute unit, so one workgroup's
+    // staging and quantization overlaps another's weight loads (Q4_K 14336x4096 at 1 / 3 columns
+    // 11.5 -> 9.9 / 21.8 -> 14.7 us against 16 waves).
+    int nw = T == kQ8_0 && NC == 1 ? 16 : NC >= 2 && wgs >= 2 * (int64_t)device_cus() ? 4 : 8;
+    if (nw > nsteps) nw = (int)nsteps;
     D4Args a;
     a.rows = rows;
     a.row_bytes = (uint32_t)((k / Fmt<T>::QK) * Fmt<T>::BYTES);
@@ -456,7 +466,6 @@ hipError_t launch_nc(const uint8_t *w, int64_t rows, int64_t k, const void *xq, 
     static const hipError_t attr_err = hipFuncSetAttribute((const void *)mmvq_dot4_kernel<T, NC, DBG, EXPERT, F32, GLU>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (attr_err != hipSuccess) return attr_err;
-    constexpr int RW = GLU ? kRows / 2 : kRows;   // outputs per workgroup
     dim3 grid((unsigned)((rows + RW - 1) / RW), EXPERT ? (unsigned)n_exp : 1u);
     hipLaunchKernelGGL((mmvq_dot4_kernel<T, NC, DBG, EXPERT, F32, GLU>), grid, dim3(64 * (unsigned)nw), smem, s, w, w2,
                        xq, y, dbg, a, cm);

@@ -198,13 +198,18 @@ def test_workspace_sizes_monotone():
 
 MV_AUTO = [
     # (type, rows, n, expected (kernel, fused)) for aligned weights and fp32 activations, K = 4096:
-    # dot4 for Q4_K, Q5_K, Q8_0 and Q4_0 at n = 1 from 8192 rows on, else the LDS-staged kernel; both
-    # quantize the fp32 input themselves at every n <= 8.
+    # dot4 for Q4_K, Q5_K and Q4_0 at n <= 3 from 8192 rows on (Q8_0: n = 1 from 8192 rows, n <= 3
+    # from 12288), else the LDS-staged kernel; both quantize the fp32 input themselves at every
+    # n <= 8.
     *[(t, 4096, n, (2, True)) for t in (qmm.Q4_K, qmm.Q5_K, qmm.Q6_K, qmm.Q8_0, qmm.Q4_0) for n in range(1, 9)],
     *[(t, 8192, 1, (3, True)) for t in (qmm.Q4_K, qmm.Q5_K, qmm.Q8_0, qmm.Q4_0)],
+    *[(t, 8192, n, (3, True)) for t in (qmm.Q4_K, qmm.Q5_K, qmm.Q4_0) for n in (2, 3)],
+    *[(t, 8192, 4, (2, True)) for t in (qmm.Q4_K, qmm.Q5_K, qmm.Q8_0, qmm.Q4_0)],
+    *[(qmm.Q8_0, r, n, (2, True)) for r in (8192, 12287) for n in (2, 3)],
+    *[(qmm.Q8_0, r, n, (3, True)) for r in (12288, 14336) for n in (2, 3)],
     (qmm.Q4_K, 8191, 1, (2, True)),
     (qmm.Q6_K, 14336, 1, (2, True)),
-    *[(t, 14336, 2, (2, True)) for t in (qmm.Q4_K, qmm.Q8_0)],
+    *[(t, 14336, 2, (3, True)) for t in (qmm.Q4_K, qmm.Q8_0)],
     *[(t, 4096, 9, (0, False)) for t in (qmm.Q4_K, qmm.Q5_K, qmm.Q6_K, qmm.Q8_0, qmm.Q4_0)],
     # Q3_K and IQ4_XS: dot4 up to three columns at any row count, then quantize + register-streamed
     *[(t, r, n, (3, True)) for t in (qmm.Q3_K, qmm.IQ4_XS) for r in (16, 4096, 14336) for n in (1, 2, 3)],

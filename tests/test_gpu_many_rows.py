@@ -62,15 +62,16 @@ def test_dot4_many_row_groups_q8_1_input(qtype):
 
 @pytest.mark.parametrize("qtype", [qmm.Q4_K, qmm.Q8_0], ids=TNAME.get)
 def test_automatic_choice_at_many_rows(qtype):
-    """One column at 8192 rows and more takes the dot4 kernel by itself."""
-    rows, k = 16389, 1024
-    w, x = _case(qtype, rows, k, 1, 1420)
-    wd, xd = to_dev(w), to_dev(x)
-    assert qmm.matvec_kernel(qtype, wd, rows, k, xd, 1)[0] == 3
-    y = qmm.matmul(wd, qtype, rows, k, xd).cpu().numpy()
-    xq = oracle.quantize_q8_1(x)
-    ref = oracle.matmul_q8_1(qtype, w, rows, k, xq, 1)
-    assert_close(y, ref, row_norms(qtype, w, rows, k), col_norms(xq, 1, k), what=f"{TNAME[qtype]} auto")
+    """One column at 8192 rows and more takes the dot4 kernel by itself; so do three columns at
+    12288 rows and more (there in workgroups of 4 waves, each wave streaming 4 of the 16 steps)."""
+    for rows, k, n in ((16389, 1024, 1), (16389, 4096, 3)):
+        w, x = _case(qtype, rows, k, n, 1420 + n)
+        wd, xd = to_dev(w), to_dev(x)
+        assert qmm.matvec_kernel(qtype, wd, rows, k, xd, n)[0] == 3
+        y = qmm.matmul(wd, qtype, rows, k, xd).cpu().numpy()
+        xq = oracle.quantize_q8_1(x)
+        ref = oracle.matmul_q8_1(qtype, w, rows, k, xq, n)
+        assert_close(y, ref, row_norms(qtype, w, rows, k), col_norms(xq, n, k), what=f"{TNAME[qtype]} auto n={n}")
 
 
 @pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
