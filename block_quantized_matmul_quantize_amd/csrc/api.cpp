@@ -241,7 +241,8 @@ qmm_status check_plan_args(int type, int64_t rows, int64_t k, int64_t n, const q
 }
 
 struct DenseWs {
-    size_t xq_off, tiled_off, part_off, total;
+    size_t xq_off, tiled_off, part_off, cnt_off, total;
+    int64_t cnt_n;   // stream-K split-tile counters at cnt_off (zeroed by the activation launch)
 };
 DenseWs dense_layout(int type, int64_t rows, int64_t k, int64_t n, bool with_xq, const qmm::Ovr &o);
 
@@ -277,12 +278,17 @@ DenseWs dense_layout(int type, int64_t rows, int64_t k, int64_t n, bool with_xq,
     L.tiled_off = off;
     if (tiled) off = align_up(off + qmm::q8_1_tiled_bytes(n, k), 256);
     L.part_off = off;
+    L.cnt_off = off;
     if (tiled) {
-        // stream-K partial slots: at most (compute units x 2 resident) units x 2 slots x 128 x 128
+        // stream-K partial slots: at most (compute units x 2 resident) units x 2 slots x 128 x 128,
+        // then one counter per tile of the most tiles any tile width gives
         const int64_t nsm = device_cus();
         const int64_t ntiles_max = ((rows + kTI - 1) / kTI) * ((n + 31) / 32);
         const int64_t units = std::min<int64_t>(2 * nsm, ntiles_max * ((k + 255) / 256));
         off = align_up(off + (size_t)(units * 2 * kTI * 128 * 4), 256);
+        L.cnt_off = off;
+        L.cnt_n = ntiles_max;
+        off = align_up(off + (size_t)ntiles_max * 4, 256);
     }
     L.total = off;
     return L;
@@ -299,7 +305,13 @@ DenseWs dense_layout_exact(int64_t k, int64_t n, const qmm_plan &p) {
     L.tiled_off = off;
     if (p.regime == 2) off = align_up(off + qmm::q8_1_tiled_bytes(n, k), 256);
     L.part_off = off;
-    if (p.regime == 2 && p.stream_k) off = align_up(off + (size_t)p.units * 2 * kTI * p.tile_j * 4, 256);
+    L.cnt_off = off;
+    if (p.regime == 2 && p.stream_k) {
+        off = align_up(off + (size_t)p.units * 2 * kTI * p.tile_j * 4, 256);
+        L.cnt_off = off;
+        L.cnt_n = p.ntiles;
+        off = align_up(off + (size_t)p.ntiles * 4, 256);
+    }
     L.total = off;
     return L;
 }
@@ -329,12 +341,14 @@ qmm_status run_dense(int type, const void *w, int64_t rows, int64_t k, const uin
     ml.units = p.units;
     ml.stream_k = p.stream_k != 0;
     ml.partials = (float *)(ws + L.part_off);
+    ml.counters = (int32_t *)(ws + L.cnt_off);
     ml.packed = packed;
-    if (ml.stream_k && (size_t)(L.part_off + (size_t)ml.units * 2 * kTI * p.tile_j * 4) > L.total)
-        return fail(QMM_ERR_WORKSPACE, "internal: stream-K partials exceed the workspace");
+    if (ml.stream_k && ((size_t)(L.part_off + (size_t)ml.units * 2 * kTI * p.tile_j * 4) > L.cnt_off ||
+                        L.cnt_n < p.ntiles))
+        return fail(QMM_ERR_WORKSPACE, "internal: stream-K partials or counters exceed the workspace");
     const uint8_t *xa = xq;
     if (!x_tiled) {
-        e = qmm::launch_relayout_q8_1_tiled(xq, n, k, ws + L.tiled_off, s);
+        e = qmm::launch_relayout_q8_1_tiled(xq, n, k, ws + L.tiled_off, s, (int32_t *)(ws + L.cnt_off), L.cnt_n);
         if (e != hipSuccess) return hip_fail(e, "relayout launch");
         xa = ws + L.tiled_off;
     }
@@ -368,8 +382,9 @@ qmm_status dense_f32(int type, const void *w, int64_t rows, int64_t k, const flo
         if (e != hipSuccess) return hip_fail(e, "quantize launch");
         return run_dense(type, w, rows, k, wsb + L.xq_off, n, y, wsb, L, nullptr, o, s);
     }
-    // tiled path: quantize straight into the tiled kernel's layout
-    hipError_t e = qmm::launch_quantize_q8_1_tiled(x, n, k, wsb + L.tiled_off, nullptr, s);
+    // tiled path: quantize straight into the tiled kernel's layout (and zero the stream-K counters)
+    hipError_t e = qmm::launch_quantize_q8_1_tiled(x, n, k, wsb + L.tiled_off, nullptr, s, (int32_t *)(wsb + L.cnt_off),
+                                                   L.cnt_n);
     if (e != hipSuccess) return hip_fail(e, "quantize launch");
     return run_dense(type, w, rows, k, wsb + L.tiled_off, n, y, wsb, L, nullptr, o, s, true);
 }
@@ -576,7 +591,8 @@ qmm_status qmm_matmul_packed(int type, const void *wp, int64_t rows, int64_t k, 
         return fail(QMM_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", ws_bytes, L.total);
     if (((uintptr_t)ws) & 255) return fail(QMM_ERR_ARG, "workspace must be 256-byte aligned");
     uint8_t *wsb = (uint8_t *)ws;
-    hipError_t e = qmm::launch_quantize_q8_1_tiled(x, n, k, wsb + L.tiled_off, nullptr, s);
+    hipError_t e = qmm::launch_quantize_q8_1_tiled(x, n, k, wsb + L.tiled_off, nullptr, s, (int32_t *)(wsb + L.cnt_off),
+                                                   L.cnt_n);
     if (e != hipSuccess) return hip_fail(e, "quantize launch");
     return run_dense(type, wp, rows, k, wsb + L.tiled_off, n, y, wsb, L, nullptr, o, s, true, true);
 }

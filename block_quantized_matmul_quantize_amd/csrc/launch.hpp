@@ -24,11 +24,13 @@ hipError_t launch_quantize_q8_1(const float *x, int64_t n_rows, int64_t k, uint8
 // the 8 blocks' codes (256 bytes), fp32 d (32 bytes) and s parts (32 bytes), each kind in a table
 // of its own indexed by kb * n_rows + r.
 inline size_t q8_1_tiled_bytes(int64_t n_rows, int64_t k) { return (size_t)((k / 32 + 7) / 8) * n_rows * 320; }
-// fp32 rows -> tiled layout (and, if canon is not null, the canonical q8_1 blocks as well)
+// fp32 rows -> tiled layout (and, if canon is not null, the canonical q8_1 blocks as well); the
+// same launch sets the nzero words at zero to 0 (the tiled kernel's stream-K counters)
 hipError_t launch_quantize_q8_1_tiled(const float *x, int64_t n_rows, int64_t k, uint8_t *tiled, uint8_t *canon,
-                                      hipStream_t s);
-// canonical q8_1 blocks -> tiled layout
-hipError_t launch_relayout_q8_1_tiled(const uint8_t *xq, int64_t n_rows, int64_t k, uint8_t *tiled, hipStream_t s);
+                                      hipStream_t s, int32_t *zero = nullptr, int64_t nzero = 0);
+// canonical q8_1 blocks -> tiled layout (zero / nzero as above)
+hipError_t launch_relayout_q8_1_tiled(const uint8_t *xq, int64_t n_rows, int64_t k, uint8_t *tiled, hipStream_t s,
+                                      int32_t *zero = nullptr, int64_t nzero = 0);
 hipError_t launch_fill_u32(uint32_t *p, int64_t n, uint32_t v, hipStream_t s);
 
 // Column map for the matrix-vector and tiled kernels.  Dense: column j reads activation row j
@@ -109,6 +111,7 @@ struct MmqLaunch {
     int64_t units;       // workgroups (== ntiles unless stream-K)
     bool stream_k;
     float *partials;     // [units][2][128*tile_j] when stream_k
+    int32_t *counters;   // [ntiles] split-tile arrival counters when stream_k, zero at launch
     bool packed = false; // w in the panel layout (repack.hip), k % 256 == 0
 };
 hipError_t launch_mmq(int type, const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n,

@@ -22,11 +22,16 @@
 // v = sc*(q-32) lies in [-4064, 4096] and is split as v = 128*hi + lo with lo in [0,127] and hi
 // in [-32, 32]; two MFMAs give D_hi and D_lo and sc0*D0 + sc1*D1 = 128*D_hi + D_lo exactly.
 //
-// Work split: `units` workgroups share ntiles*k_iters (tile, step) items; unit u owns
-// [u*W/units, (u+1)*W/units).  A unit that covers a whole tile writes it to y; a partial tile
-// goes to the unit's slot (0: its first tile, 1: its last) and the fixup kernel adds the slots
-// of a split tile in ascending unit order (deterministic, no atomics).  Without stream-K,
-// units == ntiles and every unit is exactly one tile.  Tiles are numbered in bands of 8 row
+// Work split: `units` workgroups; the first dp_tiles = floor(ntiles/units)*units tiles go whole,
+// unit u taking tiles u, u + units, ... (data-parallel rounds), and the units share the remaining
+// tiles' W = (ntiles - dp_tiles)*k_iters (tile, step) items, unit u owning [u*W/units,
+// (u+1)*W/units) (stream-K).  A unit that covers a whole tile writes it to y; a partial tile goes
+// to the unit's slot (0: its first tile, 1: its last), and the last covering unit to finish --
+// an atomic counter per split tile tells -- adds the slots in ascending unit order and writes the
+// tile (finish_split: deterministic, no unit waits for another, no separate fixup launch).
+// Splitting only the remainder keeps the partial round trip to the tiles that need it (at 448
+// tiles on 256 units: 192 split tiles instead of nearly all 448).  Without stream-K, units ==
+// ntiles and every unit is exactly one tile.  Tiles are numbered in bands of 8 row
 // tiles walked column by column (tile_coords), units are contiguous per XCD.
 #include <type_traits>
 
@@ -46,8 +51,10 @@ constexpr int kLd4 = 144;       // LDS bytes per row of packed Q4_K qs (128 + 16
 
 struct MmqArgs {
     int64_t ntiles, n_ct, k_iters, units;
-    float *partials;
+    float *partials;            // [units][2] slots of 128 x J floats
+    int32_t *counters;          // [ntiles - dp_tiles] arrivals per split tile, zero when a call starts
     int32_t write_partials;     // stream-K active
+    int64_t dp_tiles;           // tiles 0..dp_tiles-1 go whole, one per unit per round (data-parallel)
 };
 
 // Tile order: bands of kBand row tiles, each walked column by column, so that consecutive tiles
@@ -1061,6 +1068,68 @@ __device__ __forceinline__ void store_tile_glu(const f32x16 (&acc)[Cfg<J>::NCB],
     }
 }
 
+// Stream-K unit owning item i of the W stream-K items: the largest u with floor(u*W/units) <= i.
+__device__ __forceinline__ int64_t unit_of(int64_t i, int64_t W, int64_t units) {
+    const int64_t u = ((i + 1) * units - 1) / W;
+    return u < units - 1 ? u : units - 1;
+}
+
+// Epilogue of a unit's piece of a split tile (stream-K tile ts, the unit's partial slot `slot`).
+// Every covering unit stores its accumulators to its slot (in register order: element e of column
+// block cb of thread tid at (cb*16 + e)*NT + tid, so the stores and loads are coalesced) and counts
+// itself in; the unit that arrives last adds the covering units' partials in ascending unit order
+// -- its own from registers -- and writes the tile to y.  The slots are written through to memory
+// and read past the caches (system-scope accesses), and each thread waits for its stores to
+// complete before the unit counts in, so no cache-wide fence is needed (a device-scope fence
+// writes back and invalidates a whole L2, which measured twice as slow).  The order of the sum
+// does not depend on which unit arrives last (deterministic, bitwise reruns), and no unit waits
+// for another.
+template <int J>
+__device__ __forceinline__ void finish_split(const f32x16 (&acc)[Cfg<J>::NCB], const MmqArgs &args, int64_t u,
+                                             int64_t ts, int64_t slot, float *y, int64_t rows, int64_t n,
+                                             int64_t r0, int64_t c0) {
+    constexpr int NT = Cfg<J>::NT, NCB = Cfg<J>::NCB;
+    const int tid = threadIdx.x;
+    const int64_t S = (int64_t)kTI * J;
+    float *mine = args.partials + slot * S;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            __hip_atomic_store(mine + (cb * 16 + e) * NT + tid, acc[cb][e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's slot stores have completed
+    // covering units: u0..u1, those with an empty range (fewer items than units) excepted
+    const int64_t W = (args.ntiles - args.dp_tiles) * args.k_iters, U = args.units, K = args.k_iters;
+    const int64_t u0 = unit_of(ts * K, W, U), u1 = unit_of((ts + 1) * K - 1, W, U);
+    __shared__ int32_t last;
+    __syncthreads();
+    if (tid == 0) {
+        int32_t cover = 0;
+        for (int64_t v = u0; v <= u1; ++v) cover += ((v + 1) * W) / U != (v * W) / U;
+        last = atomicAdd(args.counters + ts, 1) == cover - 1;
+    }
+    __syncthreads();
+    if (!last) return;   // workgroup-uniform: the other units' slots were complete before they counted in
+    f32x16 tot[NCB];
+    bool started = false;
+    for (int64_t v = u0; v <= u1; ++v) {
+        const int64_t start = (v * W) / U;
+        if (((v + 1) * W) / U == start) continue;   // empty range: not a covering unit
+        const float *src = args.partials + (2 * v + (start / K == ts ? 0 : 1)) * S;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float p = v == u ? acc[cb][e]
+                                       : __hip_atomic_load(src + (cb * 16 + e) * NT + tid, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_SYSTEM);
+                tot[cb][e] = started ? tot[cb][e] + p : p;
+            }
+        started = true;
+    }
+    store_tile<J>(tot, y + c0 * rows + r0, rows, rows - r0, n - c0);
+}
+
 // ---------------------------------------------------------------------------------------------
 // Dense kernel: persistent over the unit's (tile, step) range.
 // ---------------------------------------------------------------------------------------------
@@ -1074,15 +1143,31 @@ __global__ __launch_bounds__(Cfg<J>::NT, 2) void mmq_kernel(const uint8_t *__res
     const int64_t nb32 = k / 32;
     const int64_t row_bytes = (k / Fmt<T>::QK) * Fmt<T>::BYTES;
     const int64_t u = xcd_remap(blockIdx.x, args.units);
-    const int64_t W = args.ntiles * args.k_iters;
+    // Data-parallel rounds first (tiles u, u + units, ... below dp_tiles, each whole), then the
+    // unit's stream-K range over the remaining tiles' (tile, step) items.
+    const int64_t W = (args.ntiles - args.dp_tiles) * args.k_iters;
+    int64_t tdp = u;
     int64_t pos = (u * W) / args.units;
     const int64_t end = ((u + 1) * W) / args.units;
     const int64_t first = pos;
 
-    while (pos < end) {
-        const int64_t t = pos / args.k_iters;
-        const int64_t kb0 = pos - t * args.k_iters;
-        const int64_t kb1 = (kb0 + (end - pos) < args.k_iters) ? kb0 + (end - pos) : args.k_iters;
+    for (;;) {
+        int64_t t, kb0, kb1, ts = 0, slot = -1;   // slot < 0: the tile is whole here (or stream-K is off)
+        if (tdp < args.dp_tiles) {
+            t = tdp;
+            kb0 = 0;
+            kb1 = args.k_iters;
+            tdp += args.units;
+        } else if (pos < end) {
+            ts = pos / args.k_iters;
+            t = args.dp_tiles + ts;
+            kb0 = pos - ts * args.k_iters;
+            kb1 = (kb0 + (end - pos) < args.k_iters) ? kb0 + (end - pos) : args.k_iters;
+            if (args.write_partials && !(kb0 == 0 && kb1 == args.k_iters)) slot = 2 * u + (pos == first ? 0 : 1);
+            pos += kb1 - kb0;
+        } else {
+            break;
+        }
         int64_t rt, ct;
         tile_coords(t, args.ntiles, args.n_ct, rt, ct);
         const int64_t r0 = rt * kTI, c0 = ct * J;
@@ -1102,15 +1187,9 @@ __global__ __launch_bounds__(Cfg<J>::NT, 2) void mmq_kernel(const uint8_t *__res
         }
 
         if (!DBG) {
-            const bool whole = kb0 == 0 && kb1 == args.k_iters;
-            if (whole || !args.write_partials) {
-                store_tile<J>(acc, y + c0 * rows + r0, rows, rows - r0, n - c0);
-            } else {
-                const int64_t slot = 2 * u + (pos == first ? 0 : 1);
-                store_tile<J>(acc, args.partials + slot * (int64_t)kTI * J, kTI, kTI, J);
-            }
+            if (slot < 0) store_tile<J>(acc, y + c0 * rows + r0, rows, rows - r0, n - c0);
+            else finish_split<J>(acc, args, u, ts, slot, y, rows, n, r0, c0);
         }
-        pos += kb1 - kb0;
     }
 }
 
@@ -1138,73 +1217,6 @@ __global__ __launch_bounds__(Cfg<J>::NT, 2) void mmq_glu_kernel(const uint8_t *_
 }
 
 // Sum of the partial slots of every split tile, in ascending unit order.
-__device__ __forceinline__ int64_t unit_of(int64_t item, int64_t W, int64_t units) {
-    // largest u with floor(u*W/units) <= item
-    int64_t lo = 0, hi = units - 1;
-    while (lo < hi) {
-        const int64_t mid = (lo + hi + 1) / 2;
-        if ((mid * W) / units <= item) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-}
-
-template <int J>
-__global__ __launch_bounds__(256) void streamk_fixup_kernel(float *__restrict__ y, int64_t rows, int64_t n,
-                                                            MmqArgs args) {
-    const int64_t t = blockIdx.x;
-    const int64_t W = args.ntiles * args.k_iters;
-    const int64_t u0 = unit_of(t * args.k_iters, W, args.units);
-    const int64_t u1 = unit_of((t + 1) * args.k_iters - 1, W, args.units);
-    if (u0 == u1) return;                         // one unit covered the whole tile
-    int64_t rt, ct;
-    tile_coords(t, args.ntiles, args.n_ct, rt, ct);
-    const int64_t r0 = rt * kTI, c0 = ct * J;
-    // partial-slot offsets of the covering units, computed once (kSlots at a time)
-    constexpr int kSlots = 256;
-    __shared__ int64_t slot_off[kSlots];
-    for (int64_t ub = u0; ub <= u1; ub += kSlots) {
-        const int64_t m = u1 - ub + 1 < kSlots ? u1 - ub + 1 : kSlots;
-        __syncthreads();
-        if (threadIdx.x < m) {
-            const int64_t u = ub + threadIdx.x;
-            const int64_t first_tile = ((u * W) / args.units) / args.k_iters;
-            slot_off[threadIdx.x] = (2 * u + (first_tile == t ? 0 : 1)) * (int64_t)kTI * J;
-        }
-        __syncthreads();
-        // item it = threadIdx.x + 256*q: four consecutive rows of one column; the partials of all
-        // the thread's items are loaded together, one covering unit at a time
-        constexpr int PER = kTI * J / 4 / 256;
-        f32x4 v[PER];
-#pragma unroll
-        for (int q = 0; q < PER; ++q) {
-            v[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (ub != u0) {
-                const int it = threadIdx.x + 256 * q, c = (4 * it) / kTI, r = 4 * it - c * kTI;
-                if (c0 + c < n)
-                    for (int e = 0; e < 4 && r0 + r + e < rows; ++e) v[q][e] = y[(c0 + c) * rows + r0 + r + e];
-            }
-        }
-        for (int64_t j = 0; j < m; ++j) {
-            const float *src = args.partials + slot_off[j] + 4 * threadIdx.x;
-#pragma unroll
-            for (int q = 0; q < PER; ++q) v[q] += *(const f32x4 *)(src + 1024 * q);
-        }
-#pragma unroll
-        for (int q = 0; q < PER; ++q) {
-            const int it = threadIdx.x + 256 * q, c = (4 * it) / kTI, r = 4 * it - c * kTI;
-            if (c0 + c >= n) continue;
-            float *dst = y + (c0 + c) * rows + r0 + r;
-            if (r0 + r + 4 <= rows) {
-                dst[0] = v[q][0];
-                dst[1] = v[q][1];
-                dst[2] = v[q][2];
-                dst[3] = v[q][3];
-            } else {
-                for (int e = 0; r0 + r + e < rows; ++e) dst[e] = v[q][e];
-            }
-        }
-    }
-}
 
 // ---------------------------------------------------------------------------------------------
 // Expert kernel: one tile per workgroup, full K; grid (row tiles, column-tile slots).
@@ -1287,16 +1299,16 @@ __global__ __launch_bounds__(Cfg<J>::NT, 2) void mmq_id_kernel(const uint8_t *__
 template <int T, int J, bool DBG, bool PK = false>
 static hipError_t launch_mmq_t(const uint8_t *w, int64_t rows, int64_t k, const uint8_t *xq, int64_t n, float *y,
                                int32_t *dbg, const MmqLaunch &p, hipStream_t s) {
-    MmqArgs a{p.ntiles, p.n_ct, p.k_iters, p.units, p.partials, p.stream_k ? 1 : 0};
+    // whole rounds of tiles run data-parallel; stream-K splits only the remainder (without stream-K
+    // units == ntiles: one round)
+    const int64_t dp = p.units > 0 ? (p.ntiles / p.units) * p.units : 0;
+    MmqArgs a{p.ntiles, p.n_ct, p.k_iters, p.units, p.partials, p.counters, p.stream_k ? 1 : 0, dp};
     constexpr int smem = kSmemBytes<T, J>;
     auto kern = mmq_kernel<T, J, DBG, PK>;
     // once per process (a function-local static is initialised exactly once, thread-safely)
     static const hipError_t attr_err = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
     if (attr_err != hipSuccess) return attr_err;
     hipLaunchKernelGGL(kern, dim3((unsigned)p.units), dim3(Cfg<J>::NT), smem, s, w, rows, k, xq, n, y, dbg, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || DBG || !p.stream_k) return e;
-    hipLaunchKernelGGL(streamk_fixup_kernel<J>, dim3((unsigned)p.ntiles), dim3(256), 0, s, y, rows, n, a);
     return hipGetLastError();
 }
 

@@ -8,7 +8,8 @@
 // per device with hipGetSymbolAddress and kept in scratch_base[], and only that address is handed
 // to kernels.  The calls share the copy of their GPU, so two calls that overlap on one GPU race
 // (callers serialise them, e.g. on one stream).  Nothing in it has to start at zero: every byte a
-// call reads (q8_1 activations, stream-K partial slots) is written earlier in that same call.
+// call reads (q8_1 activations, stream-K partial slots and counters) is written earlier in that
+// same call (the counters by the activation quantization launch).
 #include <mutex>
 
 #include "common.hpp"

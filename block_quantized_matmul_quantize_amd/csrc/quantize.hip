@@ -1,6 +1,8 @@
 // q8_1 activation quantization kernel: one block of 32 values per 4 consecutive lanes, each lane
 // owning 8 values (two 16-byte loads, one 8-byte store of codes); the arithmetic and its readings
 // are in q8_1.hpp.
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "q8_1.hpp"
@@ -34,10 +36,12 @@ __global__ __launch_bounds__(256) void quantize_q8_1_kernel(const float *__restr
 // canonical blocks.
 __global__ __launch_bounds__(256) void quantize_q8_1_tiled_kernel(const float *__restrict__ x, int64_t n_rows,
                                                                   int64_t k, uint8_t *__restrict__ tiled,
-                                                                  uint8_t *__restrict__ canon) {
+                                                                  uint8_t *__restrict__ canon,
+                                                                  int32_t *__restrict__ zero, int64_t nzero) {
     const int64_t nb = k / 32;
     const int64_t total = n_rows * nb;
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (int64_t i = gid; i < nzero; i += (int64_t)gridDim.x * blockDim.x) zero[i] = 0;
     const int64_t blk = gid >> 2;
     const int sub = (int)(gid & 3);
     const bool live = blk < total;   // the whole 4-lane group shares this predicate
@@ -62,9 +66,11 @@ __global__ __launch_bounds__(256) void quantize_q8_1_tiled_kernel(const float *_
 
 // Canonical q8_1 blocks -> tiled layout: 4 threads per block, 8 code bytes each.
 __global__ __launch_bounds__(256) void relayout_q8_1_tiled_kernel(const uint8_t *__restrict__ xq, int64_t n_rows,
-                                                                  int64_t k, uint8_t *__restrict__ tiled) {
+                                                                  int64_t k, uint8_t *__restrict__ tiled,
+                                                                  int32_t *__restrict__ zero, int64_t nzero) {
     const int64_t nb = k / 32;
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (int64_t i = gid; i < nzero; i += (int64_t)gridDim.x * blockDim.x) zero[i] = 0;
     const int64_t blk = gid >> 2;
     const int sub = (int)(gid & 3);
     if (blk >= n_rows * nb) return;
@@ -90,19 +96,22 @@ hipError_t launch_quantize_q8_1(const float *x, int64_t n_rows, int64_t k, uint8
 }
 
 hipError_t launch_quantize_q8_1_tiled(const float *x, int64_t n_rows, int64_t k, uint8_t *tiled, uint8_t *canon,
-                                      hipStream_t s) {
+                                      hipStream_t s, int32_t *zero, int64_t nzero) {
     const int64_t threads = n_rows * (k / 32) * 4;
-    if (threads == 0) return hipSuccess;
-    hipLaunchKernelGGL(quantize_q8_1_tiled_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, x, n_rows, k,
-                       tiled, canon);
+    if (threads == 0 && nzero <= 0) return hipSuccess;
+    const int64_t blocks = (std::max<int64_t>(threads, nzero) + 255) / 256;
+    hipLaunchKernelGGL(quantize_q8_1_tiled_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, n_rows, k, tiled, canon,
+                       zero, nzero);
     return hipGetLastError();
 }
 
-hipError_t launch_relayout_q8_1_tiled(const uint8_t *xq, int64_t n_rows, int64_t k, uint8_t *tiled, hipStream_t s) {
+hipError_t launch_relayout_q8_1_tiled(const uint8_t *xq, int64_t n_rows, int64_t k, uint8_t *tiled, hipStream_t s,
+                                      int32_t *zero, int64_t nzero) {
     const int64_t threads = n_rows * (k / 32) * 4;
-    if (threads == 0) return hipSuccess;
-    hipLaunchKernelGGL(relayout_q8_1_tiled_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, xq, n_rows,
-                       k, tiled);
+    if (threads == 0 && nzero <= 0) return hipSuccess;
+    const int64_t blocks = (std::max<int64_t>(threads, nzero) + 255) / 256;
+    hipLaunchKernelGGL(relayout_q8_1_tiled_kernel, dim3((unsigned)blocks), dim3(256), 0, s, xq, n_rows, k, tiled,
+                       zero, nzero);
     return hipGetLastError();
 }
 

@@ -318,7 +318,8 @@ typedef struct {
     int32_t stream_k;        /* 1 if the stream-K split is used */
     int64_t k_iters;         /* K steps per tile (one super-block of 256 values per step) */
     int64_t units;           /* stream-K work units launched (== ntiles without stream-K) */
-    int32_t fixup;           /* 1 if a fixup pass is needed */
+    int32_t fixup;           /* 1 if some tiles are split across units (the last unit to finish
+                                such a tile adds the units' partials in unit order) */
     uint64_t ws_bytes;       /* workspace qmm_matmul needs under this plan (from the same reading
                                 of the overrides as the rest of the plan) */
 } qmm_plan;
@@ -329,7 +330,8 @@ int32_t qmm_tile_efficiency(int64_t ntiles, int32_t nsm);
 /* Column tile width minimising ceil(ncols / J) over the candidate widths (ties -> smaller J). */
 int32_t qmm_select_tile_j(int64_t ncols);
 /* Stream-K partition: first flattened work item of unit u, aligned down to a tile boundary's
- * K step; returns the start index in [0, nwork]. */
+ * K step; returns the start index in [0, nwork].  The tiled kernel applies it to the tiles left
+ * over after whole rounds of one tile per unit (ntiles - floor(ntiles/units)*units of them). */
 int64_t qmm_streamk_unit_start(int64_t u, int64_t units, int64_t ntiles, int64_t k_iters);
 
 #ifdef __cplusplus

@@ -427,6 +427,30 @@ def test_streamk_on_off_agree_and_rerun_is_bitwise():
     assert_close(y_sk.cpu().numpy(), ref, wn, xn, what="stream-K vs oracle")
 
 
+@pytest.mark.parametrize("qtype", [qmm.Q4_K, qmm.Q6_K, qmm.Q8_0], ids=TNAME.get)
+def test_streamk_remainder_after_whole_rounds(qtype):
+    """More tiles than units: 40 row tiles x 7 column tiles (the last with 2 live columns) = 280
+    tiles on the device's units (256 on this part).  Whole rounds of one tile per unit run
+    data-parallel and only the remaining tiles are split by stream-K; every output against the
+    oracle, bitwise reruns, and the same products with stream-K off."""
+    rows, k, n = 5120, 512, 770
+    p = qmm.plan_dense(qtype, rows, k, n)
+    assert p["tile_j"] == 128 and p["ntiles"] == 280 and p["stream_k"] == 1
+    if p["ntiles"] % p["units"] == 0 or p["units"] >= p["ntiles"]:
+        pytest.skip("this device's unit count leaves no remainder after whole rounds")
+    w, x = _case(qtype, rows, k, n, 1450 + qtype)
+    wd, xd = to_dev(w), to_dev(x)
+    y = qmm.matmul(wd, qtype, rows, k, xd)
+    assert torch.equal(y, qmm.matmul(wd, qtype, rows, k, xd))
+    xq = oracle.quantize_q8_1(x)
+    wn, xn = row_norms(qtype, w, rows, k), col_norms(xq, n, k)
+    ref = oracle.matmul_q8_1(qtype, w, rows, k, xq, n)
+    assert_close(y.cpu().numpy(), ref, wn, xn, what=f"{TNAME[qtype]} stream-K remainder")
+    qmm.set_override(qmm.OVR_STREAMK, 1)
+    y_dp = qmm.matmul(wd, qtype, rows, k, xd)
+    assert_close(y.cpu().numpy(), y_dp.cpu().numpy(), wn, xn, what="stream-K remainder vs whole tiles")
+
+
 @pytest.mark.parametrize("sk", [0, 1], ids=["streamk-auto", "streamk-off"])
 @pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
 def test_tile_bands_partial_band_ragged_tiles(qtype, sk):
