@@ -71,10 +71,18 @@ template <int T> struct PanelGeo {
     static constexpr int HDR = B / 16 - 1, QS = T == kQ5_K ? 2 : 0;
 };
 
-template <int T, bool PK = false> struct Stage {
-    // weights (+ Q8_0 scales); panel layout: no weights are parked, the space holds the
+// Weights loaded straight into the registers of the lanes whose MFMA operands they are, none
+// parked in LDS: the panel layout (every type it serves), and Q4_K in the original layout, whose
+// 144-byte super-blocks keep the header and every qs piece 16-byte aligned, so that lane (row r,
+// group g) reads the same three pieces the panel form hands it (the four lanes of a row read one
+// 64-byte run of its qs).  Measured 2-5 % faster at 4096 x 4096 than parking the rows in LDS;
+// Q5_K, a fourth piece per lane (qh), 0-6 % slower, so it keeps the parked rows.
+template <int T, bool PK> constexpr bool kRegW = PK || T == kQ4_K;
+
+template <int T, bool REG = false> struct Stage {
+    // weights (+ Q8_0 scales); weights in registers: none are parked, the space holds the
     // cross-wave partial sums at the end (up to 2 KB)
-    static constexpr int WB = PK ? 2048 : kRows * Geo<T>::RSTR + Geo<T>::WD;
+    static constexpr int WB = REG ? 2048 : kRows * Geo<T>::RSTR + Geo<T>::WD;
     static constexpr int AB = 8 * 256;                             // activation codes: [column][block][32]
     static constexpr int FB = 64 * 8;                              // fp32 (d, s): [block][column]
     static constexpr int BYTES = WB + AB + FB;
@@ -130,7 +138,8 @@ __device__ __forceinline__ bool mmvq_stream_body(const uint8_t *__restrict__ w, 
                                                  const void *__restrict__ xin, float *__restrict__ y,
                                                  int32_t *__restrict__ dbg, const MvArgs &P, const ColMap &cm, int ey) {
     static_assert(!PK || !(GLU || EXPERT || DBG), "the panel layout serves the dense product");
-    using S = Stage<T, PK>;
+    constexpr bool REG = kRegW<T, PK>, DR = REG && !PK;   // DR: Q4_K pieces from the original rows
+    using S = Stage<T, REG>;
     constexpr int PPR = Geo<T>::PPR, RSTR = Geo<T>::RSTR, WB = S::WB, SB = S::BYTES;
     constexpr int A0 = WB, F0 = WB + S::AB;   // activation codes and (d, s) table within a stage
     constexpr int NCG = (T == kQ6_K) ? 2 : 1;
@@ -175,12 +184,15 @@ __device__ __forceinline__ bool mmvq_stream_body(const uint8_t *__restrict__ w, 
     const int ro8 = GLU ? (r8 & 7) : r8;
     const uint32_t wofs8 = (uint32_t)(ro8 < rmax ? ro8 : rmax) * row_bytes + (T == kQ4_0 ? 36u : 68u) * p8;
     const uint8_t *wg8 = (GLU && r8 >= 8) ? wg2 : wg;
+    // DR: this lane's row (r16 = lane % 16; GLU: rows 8.. are the up rows)
+    const int rd = lane & 15, rdo = GLU ? (rd & 7) : rd;
+    const uint8_t *wrd = ((GLU && rd >= 8) ? wg2 : wg) + (uint32_t)(rdo < rmax ? rdo : rmax) * row_bytes;
 
     u32x4 wv[4];
     uint32_t wv4 = 0;
     // panel layout: the pieces this lane's MFMA operands need, straight into registers (slab j,
     // row r16 at 256 j + 16 r16 of the panel)
-    u32x4 pw[PK ? 5 : 1];
+    u32x4 pw[REG ? 5 : 1] = {};
     uint16_t pwd = 0;
     auto load_w = [&](int s) __attribute__((always_inline)) {
         if constexpr (PK) {
@@ -206,6 +218,14 @@ __device__ __forceinline__ bool mmvq_stream_body(const uint8_t *__restrict__ w, 
                     pw[p] = *(const u32x4 *)(src + 256 * (T == kQ4_0 ? 2 * p + (gg >> 1) : 4 * p + gg));
                 pw[4] = *(const u32x4 *)(src + 256 * PanelGeo<T>::HDR);
             }
+        } else if constexpr (DR) {
+            // super-block s of the row: header (d, dmin, scales) at 0, qs at 16
+            static_assert(T == kQ4_K, "original-layout pieces in registers: Q4_K");
+            const uint8_t *src = wrd + (uint32_t)(s * 144);
+            const int gd = lane >> 4, qa = (gd + 3) & 3;
+            pw[0] = *(const u32x4 *)src;
+            pw[1] = *(const u32x4 *)(src + 16 + 16 * qa);
+            pw[2] = *(const u32x4 *)(src + 16 + 16 * (4 + qa));
         } else if constexpr (T == kQ8_0) {
             const uint8_t *src = wg8 + (uint32_t)(s * 272) + wofs8;
 #pragma unroll
@@ -316,7 +336,7 @@ __device__ __forceinline__ bool mmvq_stream_body(const uint8_t *__restrict__ w, 
                 if (i < nic) *(u32x4 *)(st + acdst[i]) = av[i];
             *(float2 *)(st + asdst) = make_float2(h2f((uint16_t)(ads & 0xFFFF)), h2f((uint16_t)(ads >> 16)));
         }
-        if constexpr (PK) {
+        if constexpr (REG) {
             // weights stay in registers (pw)
         } else if constexpr (kK45<T>) {
 #pragma unroll
@@ -431,6 +451,14 @@ __device__ __forceinline__ bool mmvq_stream_body(const uint8_t *__restrict__ w, 
     for (int it = 0; it < my_steps; ++it) {
         const int s = wave + it * nwaves;
         park(s);
+        // weights in registers: step s's pieces, taken before the next step's loads refill pw
+        u32x4 pc[REG ? 5 : 1];
+        uint16_t pcd = 0;
+        if constexpr (REG) {
+#pragma unroll
+            for (int i = 0; i < 5; ++i) pc[i] = pw[i];
+            pcd = pwd;
+        }
         if (it + 1 < my_steps) {   // the next step's loads fly during this step's math
             load_a(s + nwaves);
             load_w(s + nwaves);
@@ -442,9 +470,9 @@ __device__ __forceinline__ bool mmvq_stream_body(const uint8_t *__restrict__ w, 
             const uint8_t *wr = st + wrow;
             // this lane's qs pieces: (g + 3) % 4 and 4 + (g + 3) % 4 of the row's eight
             const int qa = (g + 3) & 3;
-            const u32x4 hdr = PK ? pw[0] : lds16(wr);
-            const u32x4 src1 = PK ? pw[1] : lds16(wr + QS + 16 + 16 * qa);
-            const u32x4 src2 = PK ? pw[2] : lds16(wr + QS + 16 + 16 * (4 + qa));
+            const u32x4 hdr = REG ? pc[0] : lds16(wr);
+            const u32x4 src1 = REG ? pc[1] : lds16(wr + QS + 16 + 16 * qa);
+            const u32x4 src2 = REG ? pc[2] : lds16(wr + QS + 16 + 16 * (4 + qa));
             const int sel = g >> 1;
             const float d = h2f((uint16_t)(hdr.x & 0xFFFF));
             const float dmin = h2f((uint16_t)(hdr.x >> 16));
@@ -456,7 +484,7 @@ __device__ __forceinline__ bool mmvq_stream_body(const uint8_t *__restrict__ w, 
             if constexpr (T == kQ5_K) {
                 // fifth bits: this lane's bytes are values 16*half.. of sub-blocks
                 // 2*group + (j&1) + 4*(j>>1); bit (sub-block) of qh bytes 16*half..
-                const u32x4 qh = PK ? pw[PK ? 3 : 0] : lds16(wr + 16 + 16 * q4_half(g));
+                const u32x4 qh = REG ? pc[REG ? 3 : 0] : lds16(wr + 16 + 16 * q4_half(g));
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int sbb = 2 * q4_group(g) + (j & 1) + 4 * (j >> 1);
@@ -493,12 +521,12 @@ __device__ __forceinline__ bool mmvq_stream_body(const uint8_t *__restrict__ w, 
             // original super-block bytes / panel slabs: ql pieces g and 4+g, qh pieces (g&1) and
             // 2+(g&1), the 16 scales, d
             const uint8_t *pr = st + 16 * r16;
-            const u32x4 ql0 = PK ? pw[0] : lds16(wr + 16 * g);
-            const u32x4 ql1 = PK ? pw[PK ? 1 : 0] : lds16(wr + 64 + 16 * g);
-            const u32x4 qh0 = PK ? pw[PK ? 2 : 0] : lds16(wr + 128 + 16 * (g & 1));   // half 0
-            const u32x4 qh1 = PK ? pw[PK ? 3 : 0] : lds16(wr + 160 + 16 * (g & 1));  // half 1
-            const u32x4 scv = PK ? pw[PK ? 4 : 0] : lds16(wr + 192);
-            const float d = h2f(PK ? pwd : *(const uint16_t *)(wr + 208));
+            const u32x4 ql0 = PK ? pc[0] : lds16(wr + 16 * g);
+            const u32x4 ql1 = PK ? pc[PK ? 1 : 0] : lds16(wr + 64 + 16 * g);
+            const u32x4 qh0 = PK ? pc[PK ? 2 : 0] : lds16(wr + 128 + 16 * (g & 1));   // half 0
+            const u32x4 qh1 = PK ? pc[PK ? 3 : 0] : lds16(wr + 160 + 16 * (g & 1));  // half 1
+            const u32x4 scv = PK ? pc[PK ? 4 : 0] : lds16(wr + 192);
+            const float d = h2f(PK ? pcd : *(const uint16_t *)(wr + 208));
             const u32x4 neg32 = {0xE0E0E0E0u, 0xE0E0E0E0u, 0xE0E0E0E0u, 0xE0E0E0E0u};
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
@@ -539,7 +567,7 @@ __device__ __forceinline__ bool mmvq_stream_body(const uint8_t *__restrict__ w, 
         } else {
             const uint8_t *wr = st + wrow;
             const float *wd = (const float *)(st + kRows * RSTR) + 8 * r16;
-            const uint32_t wdw[4] = {pw[PK ? 4 : 0].x, pw[PK ? 4 : 0].y, pw[PK ? 4 : 0].z, pw[PK ? 4 : 0].w};   // panel: fp16 d
+            const uint32_t wdw[4] = {pc[PK ? 4 : 0].x, pc[PK ? 4 : 0].y, pc[PK ? 4 : 0].z, pc[PK ? 4 : 0].w};   // panel: fp16 d
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
                 const int blk = 2 * p + (g >> 1);
@@ -547,12 +575,12 @@ __device__ __forceinline__ bool mmvq_stream_body(const uint8_t *__restrict__ w, 
                 if constexpr (PK && T == kQ4_0) {
                     // block blk's 16 nibble bytes; this lane's half (g & 1) of its 32 values as
                     // int8 nibble - 8: (n + 120) ^ 0x80 per byte
-                    const u32x4 nb = pw[p];
+                    const u32x4 nb = pc[p];
                     const uint32_t sh = 4 * (g & 1);
                     auto c4 = [sh](uint32_t v) { return (((v >> sh) & 0x0F0F0F0Fu) + 0x78787878u) ^ 0x80808080u; };
                     q = u32x4{c4(nb.x), c4(nb.y), c4(nb.z), c4(nb.w)};
                 } else if constexpr (PK) {
-                    q = pw[p];
+                    q = pc[p];
                 } else {
                     q = lds16(wr + 64 * p + 16 * g);
                 }
@@ -651,7 +679,7 @@ hipError_t launch_t(const uint8_t *w, int64_t rows, int64_t k, const void *xq, i
                     int32_t *dbg, const ColMap &c, int64_t n_exp, hipStream_t s, const uint8_t *w2 = nullptr) {
     const int64_t nsteps = k / kSuper;
     const int nw = (int)(nsteps < 16 ? nsteps : 16);
-    const size_t smem = (size_t)nw * (kHead + Stage<T, PK>::BYTES);
+    const size_t smem = (size_t)nw * (kHead + Stage<T, kRegW<T, PK>>::BYTES);
     MvArgs a;
     a.rows = rows;
     a.row_bytes = (uint32_t)((k / Fmt<T>::QK) * Fmt<T>::BYTES);

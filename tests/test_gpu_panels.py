@@ -76,6 +76,15 @@ def test_packed_matvec_full_size(qtype, n):
     _check_packed(qtype, 4096, 4096, n, 970 + n, f"{TNAME[qtype]} packed 4096^2 n={n}")
 
 
+
+@pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
+@pytest.mark.parametrize("k", [4352, 14336])
+@pytest.mark.parametrize("n", [1, 5, 8])
+def test_packed_matvec_several_steps_per_wave(qtype, k, n):
+    """More than 16 steps (17 and 56): the waves of the matrix-vector kernel take several steps,
+    each computed from the panel pieces in its registers while the next step's pieces load."""
+    _check_packed(qtype, 40, k, n, 1300 + n + k % 97, f"{TNAME[qtype]} packed k={k} n={n}")
+
 @pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
 def test_packed_matches_original_layout_bitwise_matvec(qtype):
     """Same kernel, same arithmetic: the LDS-staged kernel reading panels gives exactly the bits it

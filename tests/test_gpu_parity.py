@@ -253,6 +253,21 @@ def test_matvec_kernel_variants(qtype, kernel):
     assert np.array_equal(got, oracle.subdots(qtype, w, 77, k, xq, nd))
 
 
+
+@pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
+@pytest.mark.parametrize("n", [1, 8])
+def test_matvec_lds_kernel_many_steps_per_wave(qtype, n):
+    """The LDS-staged kernel at K = 14336 (56 steps on 16 waves): every wave computes three or four
+    steps, each while the next step's loads are in flight, so a step must not read the registers
+    the next step's loads refill; fp32 outputs and the integer sub-block dots."""
+    qmm.set_override(qmm.OVR_MV_KERNEL, 2)
+    rows, k = 40, 14336
+    _full_check(qtype, rows, k, n, 590 + n, f"{TNAME[qtype]} lds k={k} n={n}")
+    w, x = _case(qtype, rows, k, n, 595 + n)
+    xq = oracle.quantize_q8_1(x)
+    got = qmm.debug_subdots(to_dev(w), qtype, rows, k, to_dev(xq), n, qmm.PATH_MATVEC).cpu().numpy()
+    assert np.array_equal(got, oracle.subdots(qtype, w, rows, k, xq, n))
+
 def _at_offset(a, off):
     """Device copy of numpy bytes whose data pointer sits `off` bytes past a 256-byte boundary."""
     buf = torch.zeros(a.nbytes + 512, dtype=torch.uint8, device=DEV)
