@@ -101,6 +101,17 @@ def test_glu_matvec_kernels(qtype, n, kernel):
     _check_dense(qtype, 229, 1024, n, 1200 + 10 * n + kernel, f"{TNAME[qtype]} n={n} kernel={kernel}")
 
 
+@pytest.mark.parametrize("kernel", [1, 2], ids=["regs", "lds"])
+@pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
+@pytest.mark.parametrize("n", [1, 8])
+def test_glu_matvec_several_steps_per_wave(qtype, n, kernel):
+    """More steps than waves (17; Q6_K 24, whose rows must stay 16-byte aligned for the LDS-staged
+    kernel): some waves compute a step while the next step's loads are in flight."""
+    qmm.set_override(qmm.OVR_MV_KERNEL, kernel)
+    k = 6144 if qtype == qmm.Q6_K else 4352
+    _check_dense(qtype, 45, k, n, 1280 + 10 * n + kernel, f"{TNAME[qtype]} k={k} n={n} kernel={kernel}")
+
+
 @pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
 @pytest.mark.parametrize("n", [1, 5, 8])
 def test_glu_single_step_k(qtype, n):

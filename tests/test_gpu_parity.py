@@ -607,14 +607,17 @@ def test_moe_invalid_ids_and_per_slot_activations():
                 assert_close(y[t, s][None], ref[t, s][None], wn_all[e], xn_all[a:a + 1], what=f"pair {t},{s}")
 
 
+@pytest.mark.parametrize("deep", [False, True], ids=["k2048", "k_past_16_steps"])
 @pytest.mark.parametrize("kernel", [1, 2], ids=MV_KNAME.get)
 @pytest.mark.parametrize("qtype", TYPES, ids=TNAME.get)
-def test_moe_small_experts_both_kernels(qtype, kernel):
+def test_moe_small_experts_both_kernels(qtype, kernel, deep):
     """Experts with at most 8 columns go to the matrix-vector kernel in expert mode; both kernels,
-    ragged rows, per-slot activations, every output against the oracle."""
+    ragged rows, per-slot activations, every output against the oracle; K = 2048, and K past 16
+    steps (some waves take two)."""
     qmm.set_override(qmm.OVR_MV_KERNEL, kernel)
-    rng = np.random.default_rng(1100 + qtype)
-    n_exp, rows, k, n_tok, top_k = 6, 77, 2048, 20, 2
+    rng = np.random.default_rng(1100 + qtype + (7 if deep else 0))
+    k = (6144 if qtype == qmm.Q6_K else 4352) if deep else 2048
+    n_exp, rows, n_tok, top_k = 6, 77, 20, 2
     w = synth.gen_weights(qtype, n_exp * rows, k, rng)
     x = rng.standard_normal((n_tok * top_k, k)).astype(np.float32)
     ids = np.stack([rng.choice(n_exp, top_k, replace=False) for _ in range(n_tok)]).astype(np.int32)
