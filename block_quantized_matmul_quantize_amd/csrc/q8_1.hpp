@@ -22,12 +22,14 @@ template <int CTRL> __device__ __forceinline__ float dpp_f(float v) {
 }
 constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E;
 
-// q = round-half-away(RN(x / d32)).  Fast path: t = x * rcp(d32) (hardware reciprocal, 1 ulp)
-// is within 2^-15 + 2^-17 of x / d32 for |x| <= amax, so rint(t) (nearest, ties to even) equals
-// the exact answer unless x / d32 lies within a few ulps of a half-integer -- which the
-// |t - rint(t)| > 0.5 - 2^-13 test catches (ties to even and ties away from zero differ only
-// there).  Those values, and blocks whose d32 is outside [2^-100, 2^100] (or not finite), take
-// the IEEE division, so the codes are always those of the plain definition.
+// q = round-half-away(RN(x / d32)).  Fast path: x * rcp(d32) (hardware reciprocal, 1 ulp) is
+// within E = 2^-15 + 2^-17 of x / d32 for |x| <= amax, so rounding it to the nearest integer gives
+// the exact answer unless the two lie on opposite sides of a half-integer (or x / d32 is one:
+// ties to even and ties away from zero differ only there), and then x * rcp(d32) is within E of
+// that half-integer.  One fma with 1.5 * 2^23 rounds x * rcp(d32) to an integer whose low byte is
+// the int8 code; a second gives the residual e = x * rcp(d32) - q, and |e| > 0.5 - 2^-14 (> 0.5 -
+// E) sends the lane to the IEEE division, as do blocks whose d32 is outside [2^-100, 2^100] (or
+// not finite), so the codes are always those of the plain definition.
 __device__ __forceinline__ int q81_round_div(float x, float d32) { return (int)roundf(x / d32); }
 
 __device__ __forceinline__ uint32_t pack4(int q0, int q1, int q2, int q3) {
@@ -66,16 +68,17 @@ __device__ __forceinline__ Q81Lane4 quantize_q8_1_lane4(float4 a, float4 b) {
         bool slow = !(d32 >= 0x1p-100f && d32 <= 0x1p100f);
         if (!slow) {
             const float r = __builtin_amdgcn_rcpf(d32);
+            constexpr float kRound = 12582912.0f;   // 1.5 * 2^23: sums in [2^23, 2^24) are integers
             int q[8];
             float dev = 0.0f;   // largest distance of a quotient from its nearest integer
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const float t = v[i] * r;
-                const float rt = rintf(t);
-                dev = fmaxf(dev, fabsf(t - rt));
-                q[i] = (int)rt;
+                const float m = fmaf(v[i], r, kRound);        // 1.5 * 2^23 + q, |q| <= 127: exact
+                const float e = fmaf(v[i], r, kRound - m);    // x * rcp(d32) - q, one rounding
+                dev = fmaxf(dev, fabsf(e));
+                q[i] = __float_as_int(m);                     // low byte: q (two's complement)
             }
-            slow = dev > 0.5f - 0x1p-13f;
+            slow = dev > 0.5f - 0x1p-14f;
             c0 = pack4(q[0], q[1], q[2], q[3]);
             c1 = pack4(q[4], q[5], q[6], q[7]);
         }
