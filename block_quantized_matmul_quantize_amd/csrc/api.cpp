@@ -218,9 +218,9 @@ qmm_plan plan_dense_impl(int type, int64_t rows, int64_t k, int64_t n, int32_t n
     const int occ = mmq_resident(type, p.tile_j);
     const int32_t slots = nsm * occ;
     p.efficiency_pct = qmm_tile_efficiency(p.ntiles, slots);
-    // stream-K pays a partial-tile round trip and a fixup pass: the MMQ page's "when not to use
-    // stream-K" threshold, tile efficiency below 90 % (measured here: at 87.5 % stream-K is ~5 %
-    // faster, at 100 % within noise)
+    // stream-K pays a partial-tile round trip through memory and the last unit's sum: the MMQ
+    // page's "when not to use stream-K" threshold, tile efficiency below 90 % (measured here: at
+    // 87.5 % the split remainder is ~3 % faster, at 50 % 1.7x, at 100 % the plan takes no split)
     bool use_sk = p.efficiency_pct < 90 && p.k_iters > 1;
     if (o.streamk == 1) use_sk = false;
     if (o.streamk == 2) use_sk = p.k_iters > 1 || p.ntiles > 1;
