@@ -715,15 +715,15 @@ IdWs id_layout(int64_t n_exp, int64_t k, int64_t n_tok, int64_t top_k, int64_t x
 int id_tile_j(int type, int64_t pairs, int64_t n_exp, const qmm::Ovr &o) {
     if (o.tile_j) return o.tile_j;
     // The MMQ page's "MoE skew": per-expert column counts are skewed, so the tile width follows
-    // the columns of a typical expert, not the call's total: the mean for a few experts, half the
-    // mean for many (a handful of hot experts then hold most columns; on the Zipf MoE shapes the
-    // median expert has 0.7x the mean with 8 experts, 0.4x with 128), then the smallest tile that
-    // covers it.  Measured: 8 experts x 128 mean columns 128-column tiles best, 128 experts x 128
-    // mean 64-column tiles best.  Q6_K (and Q3_K, parked the same way) keeps 128: its 4-wave tiles
-    // hold the unpacked planes and run one workgroup per CU.
+    // the columns of a typical expert, not the call's total: a quarter of the mean (on the Zipf
+    // MoE shapes the median expert has 0.7x the mean with 8 experts, 0.4x with 128, and the last
+    // tile of every expert is partly empty), then the smallest tile that covers it.  Measured on
+    // 8 experts and on 128 experts, both with 128 columns on average (Q4_K): 32-column tiles 3-5 %
+    // faster than 64 and 128.  Q6_K (and Q3_K, parked the same way) keeps 128: its 4-wave tiles
+    // hold the unpacked planes and run one workgroup per CU (32 columns: 2x slower).
     if (type == QMM_Q6_K || type == QMM_Q3_K) return 128;
     const int64_t mean = pairs / (n_exp > 0 ? n_exp : 1);
-    const int64_t typical = n_exp > 16 ? mean / 2 : mean;
+    const int64_t typical = mean / 4;
     return typical > 64 ? 128 : (typical > 32 ? 64 : 32);
 }
 
