@@ -266,7 +266,7 @@ qmm_status qmm_debug_subdots(int type, const void *w, int64_t rows, int64_t k, c
  * qmm_matmul_q8_1 with q8_1 activations x; only the alignment of w and x, and the sizes, are looked
  * at (one to three columns of 8192 or more rows take the dot4 kernel -- Q8_0: one column from
  * 8192 rows, two or three from 12288 -- fewer rows the LDS-staged one; Q3_K and IQ4_XS take dot4
- * for one to three columns at any row count).
+ * for one to three columns at any row count; Q6_K, which has no dot4 form, the LDS-staged one).
  * *out: 0 the call takes the tiled path (n > 8 or forced), 1 register-streamed, 2 LDS-staged
  * MFMA, 3 dot4; plus 16 when that kernel quantizes the fp32 activations itself (one launch, no
  * quantize kernel).  Errors: QMM_ERR_TYPE / QMM_ERR_SHAPE as for qmm_matmul, QMM_ERR_ARG for a
