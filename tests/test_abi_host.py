@@ -266,10 +266,11 @@ def test_matvec_kernel_choice_follows_alignment_and_overrides():
 
 @pytest.mark.parametrize("qtype,n_exp,n_tok,top_k,J", [
     (qmm.Q6_K, 128, 2048, 8, 128),     # Q6_K keeps 128-column tiles
-    (qmm.Q4_K, 128, 2048, 8, 64),      # many experts: typical = mean/2 = 64
-    (qmm.Q4_K, 8, 512, 2, 128),        # few experts: typical = mean = 128
-    (qmm.Q4_K, 16, 384, 2, 64),        # mean 48
-    (qmm.Q4_K, 32, 1024, 2, 32),       # mean 64, typical 32
+    (qmm.Q4_K, 128, 2048, 8, 32),      # mean 128, typical = mean/4 = 32
+    (qmm.Q4_K, 8, 512, 2, 32),         # mean 128, typical 32
+    (qmm.Q4_K, 16, 384, 2, 32),        # mean 48
+    (qmm.Q4_K, 8, 800, 2, 64),         # mean 200, typical 50
+    (qmm.Q4_K, 8, 1040, 2, 128),       # mean 260, typical 65
     (qmm.Q8_0, 64, 100, 4, 32),        # mean 6
     (qmm.Q4_K, 4, 1024, 2, 128),       # mean 512
 ])
