@@ -196,6 +196,17 @@ qmm_status qmm_set_override(int key, int value) {
 
 namespace {
 
+// Tile width of a dense tiled call: the fewest column tiles (qmm_select_tile_j), except where
+// that is one 64-column tile (33-64 columns), measured the slowest of the three widths there
+// (14336 x 4096 at 40-64 columns): Q6_K and Q3_K, whose planes are unpacked by half the threads
+// in the 4-wave tiles, take one 128-column tile (14-20 % faster), the other types two 32-column
+// tiles (5-12 % faster; Q8_0 ties with 128).
+int dense_tile_j(int type, int64_t n) {
+    const int32_t J = qmm_select_tile_j(n);
+    if (J != 64) return J;
+    return type == QMM_Q6_K || type == QMM_Q3_K ? 128 : 32;
+}
+
 // The planner under a given override snapshot (arguments already checked).
 qmm_plan plan_dense_impl(int type, int64_t rows, int64_t k, int64_t n, int32_t nsm, const qmm::Ovr &o) {
     qmm_plan p{};
@@ -212,7 +223,7 @@ qmm_plan plan_dense_impl(int type, int64_t rows, int64_t k, int64_t n, int32_t n
     }
     p.regime = 2;
     p.tile_i = kTI;
-    p.tile_j = o.tile_j ? o.tile_j : qmm_select_tile_j(n);
+    p.tile_j = o.tile_j ? o.tile_j : dense_tile_j(type, n);
     const int64_t n_ct = (n + p.tile_j - 1) / p.tile_j;
     p.ntiles = ((rows + kTI - 1) / kTI) * n_ct;
     const int occ = mmq_resident(type, p.tile_j);
