@@ -196,15 +196,16 @@ qmm_status qmm_set_override(int key, int value) {
 
 namespace {
 
-// Tile width of a dense tiled call: the fewest column tiles (qmm_select_tile_j), except where
-// that is one 64-column tile (33-64 columns), measured the slowest of the three widths there
-// (14336 x 4096 at 40-64 columns): Q6_K and Q3_K, whose planes are unpacked by half the threads
-// in the 4-wave tiles, take one 128-column tile (14-20 % faster), the other types two 32-column
-// tiles (5-12 % faster; Q8_0 ties with 128).
+// Tile width of a dense tiled call, plain or fused gate/up: the fewest column tiles
+// (qmm_select_tile_j), except where that is one 64-column tile (33-64 columns), measured the
+// slowest of the three widths there (14336 x 4096 at 40-64 columns): Q6_K and Q3_K, whose planes
+// are unpacked by half the threads in the 4-wave tiles, and Q8_0 take one 128-column tile (Q6_K /
+// Q3_K 14-20 % faster, 40 % in the fused form; Q8_0 1-2 %), the other types two 32-column tiles
+// (5-12 % faster).
 int dense_tile_j(int type, int64_t n) {
     const int32_t J = qmm_select_tile_j(n);
     if (J != 64) return J;
-    return type == QMM_Q6_K || type == QMM_Q3_K ? 128 : 32;
+    return type == QMM_Q6_K || type == QMM_Q3_K || type == QMM_Q8_0 ? 128 : 32;
 }
 
 // The planner under a given override snapshot (arguments already checked).
@@ -662,7 +663,7 @@ qmm_status qmm_matmul_glu(int type, const void *w_gate, const void *w_up, int64_
     }
     e = qmm::launch_quantize_q8_1_tiled(x, n, k, wsb, nullptr, s);
     if (e != hipSuccess) return hip_fail(e, "quantize launch");
-    const int tile_j = o.tile_j ? o.tile_j : qmm_select_tile_j(n);
+    const int tile_j = o.tile_j ? o.tile_j : dense_tile_j(type, n);
     e = qmm::launch_mmq_glu(type, wg, wu, rows, k, wsb, n, y, tile_j, s);
     if (e != hipSuccess) return hip_fail(e, "fused tiled kernel launch");
     return QMM_OK;

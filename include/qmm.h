@@ -305,8 +305,8 @@ qmm_status qmm_set_override(int key, int value);
 /* ---------------------------------------------------------------------------------------------
  * Host-side planner, exposed so its arithmetic can be tested without a GPU.
  * ([MMQ] "J runtime selection": smallest J with the fewest column tiles -- except that 33-64
- * columns take one 128-column tile for Q6_K / Q3_K and two 32-column tiles otherwise, the
- * 64-column tile measuring slowest there; "tile efficiency":
+ * columns take one 128-column tile for Q6_K / Q3_K / Q8_0 and two 32-column tiles otherwise, the
+ * 64-column tile measuring slowest there (plain and fused gate/up calls); "tile efficiency":
  * eff = floor(100 * ntiles / (nsm * ceil(ntiles / nsm))); "when not to use stream-K" and
  * "stream-K": nwork = ntiles * ceil(k_iters), units = min(nsm * occupancy, nwork), and unit u
  * owns the flattened (tile, k-iteration) range [u*W/units, (u+1)*W/units).)

@@ -72,13 +72,13 @@ def test_select_tile_j(ncols, J):
 
 
 @pytest.mark.parametrize("qtype,n,J", [
-    (qmm.Q4_K, 48, 32), (qmm.Q4_K, 64, 32), (qmm.Q8_0, 40, 32), (qmm.Q5_K, 33, 32),   # two 32-column tiles
-    (qmm.Q6_K, 48, 128), (qmm.Q3_K, 64, 128),                                           # one 128-column tile
+    (qmm.Q4_K, 48, 32), (qmm.Q4_K, 64, 32), (qmm.Q4_0, 40, 32), (qmm.Q5_K, 33, 32),   # two 32-column tiles
+    (qmm.Q6_K, 48, 128), (qmm.Q3_K, 64, 128), (qmm.Q8_0, 40, 128),                      # one 128-column tile
     (qmm.Q4_K, 32, 32), (qmm.Q6_K, 20, 32), (qmm.Q4_K, 65, 128), (qmm.Q6_K, 512, 128),  # fewest tiles
 ])
 def test_dense_tile_width_avoids_single_64_column_tile(qtype, n, J):
     """33-64 columns: the 64-column tile measured slowest, so the plan takes one 128-column tile
-    for Q6_K / Q3_K and two 32-column tiles for the other types; elsewhere the fewest tiles."""
+    for Q6_K / Q3_K / Q8_0 and two 32-column tiles for the other types; elsewhere the fewest."""
     p = qmm.plan_dense(qtype, 4096, 4096, n)
     assert p["regime"] == 2 and p["tile_j"] == J
 
